@@ -1,0 +1,296 @@
+/*
+ * Plain CPU oracle for the MXFP4 weight-streaming MoE layer and the dense
+ * MXFP4 linear layer.  TEST INFRASTRUCTURE ONLY: tests, the smoke check and
+ * the CPU-baseline leg of the benchmark load it; the product path never does.
+ * It shares no code, header, table or helper with the GPU library.
+ *
+ * Sources (the pages define the format; the remaining steps are the plainest
+ * reading of the layer they describe):
+ *   - "Zyphra Inference Wave 2" (aihot.news mirror), section "Quantization.":
+ *     MXFP4 = blocks of 32 values sharing one 8-bit power-of-two scale, each
+ *     value a 4-bit float with magnitude in {0, 0.5, 1, 1.5, 2, 3, 4, 6};
+ *     4.25 bits per value.
+ *   - same page, "Quantization" (serving) section: an MXFP4 expert runs the two
+ *     expert GEMMs and combines the results; only the routed experts are read.
+ *   - same page, section "Speculative decoding.": a step of T tokens reads each
+ *     needed weight once and applies it to every token of the step.
+ *   - "Bringing Ultra-Fast, Interactive LLM Inference to AMD Instinct MI355X
+ *     GPUs" (AMD ROCm blog), section "3. Low-Precision Data Types": 4-bit
+ *     values with one shared scale per 32.
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *   - E2M1 code c: sign = bit 3, bits 2..0 index the eight magnitudes in
+ *     ascending order; code 8 is -0.0.
+ *   - E8M0 byte s: value 2^(s-127); s = 0xFF is NaN; no zero, no infinity.
+ *   - Packing: codes of a row are K-contiguous, two per byte, element 2i in the
+ *     low nibble and 2i+1 in the high nibble; one scale byte per 32
+ *     consecutive K values of one output row.
+ *   - Weight tensors are row-major [rows = output features][K/2] bytes plus
+ *     scales [rows][K/32]; the gate_up tensor holds the I gate rows first,
+ *     then the I up rows.
+ *   - Router: the k largest logits (ties to the lower expert id), slots in
+ *     descending-logit order; gates are a softmax over the k selected logits.
+ *   - SwiGLU: h = silu(g) * u, silu(g) = g / (1 + exp(-g)); h is rounded once
+ *     to bf16 (round to nearest even).
+ *   - Accumulation: fp32, K ascending, each product rounded to fp32 first;
+ *     the combine sums the k gate-weighted fp32 down outputs in slot order and
+ *     rounds once to bf16.
+ *
+ * Build: gcc -O2 -std=c11 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC
+ * Contraction and fast-math are off so every fp32 operation is one IEEE
+ * rounding and results do not depend on the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORA_VERSION 1
+
+int ora_version(void) { return ORA_VERSION; }
+
+/* ---------------------------------------------------------------- format */
+
+/* E2M1 magnitudes, ascending ("Quantization." section of the Zyphra page). */
+static const double E2M1_MAG[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double ora_e2m1(int code) {
+  double m = E2M1_MAG[code & 7];
+  return (code & 8) ? -m : m; /* code 8 gives -0.0 */
+}
+
+/* E8M0 scale: an 8-bit power of two with bias 127; 0xFF encodes NaN. */
+double ora_e8m0(int s) {
+  if ((s & 0xFF) == 0xFF) return NAN;
+  return ldexp(1.0, (s & 0xFF) - 127);
+}
+
+/* Nibble i of a packed row: element 2j is the low nibble of byte j. */
+static int nibble(const uint8_t* row, int64_t i) {
+  uint8_t b = row[i >> 1];
+  return (i & 1) ? (b >> 4) : (b & 15);
+}
+
+/* Pack n 4-bit codes (n even) into n/2 bytes, element 2j in the low nibble. */
+void ora_pack_codes(const uint8_t* codes, int64_t n, uint8_t* packed) {
+  for (int64_t j = 0; j < n / 2; ++j)
+    packed[j] = (uint8_t)((codes[2 * j] & 15) | ((codes[2 * j + 1] & 15) << 4));
+}
+
+void ora_unpack_codes(const uint8_t* packed, int64_t n, uint8_t* codes) {
+  for (int64_t i = 0; i < n; ++i) codes[i] = (uint8_t)nibble(packed, i);
+}
+
+/* Exact weight value w[r,k] = e2m1(code) * 2^(s-127), in fp64 (exact: at most
+ * two significant bits, exponent within fp64 range). */
+static double weight(const uint8_t* w, const uint8_t* s, int64_t K, int64_t r, int64_t k) {
+  return ora_e2m1(nibble(w + r * (K / 2), k)) * ora_e8m0(s[r * (K / 32) + k / 32]);
+}
+
+/* Dequantize rows x K weights to fp64. */
+void ora_dequant_f64(const uint8_t* w, const uint8_t* s, int64_t rows, int64_t K, double* out) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t k = 0; k < K; ++k) out[r * K + k] = weight(w, s, K, r, k);
+}
+
+/* ------------------------------------------------------------ bf16 helpers */
+
+static double bf16_to_f64(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* Round a double to the nearest bf16 (ties to even), overflow to +-Inf, NaN
+ * kept.  bf16 = 1 sign, 8 exponent (bias 127), 7 stored fraction bits. */
+uint16_t ora_bf16_rne(double v) {
+  if (isnan(v)) return 0x7FC0;
+  if (isinf(v)) return v > 0 ? 0x7F80 : 0xFF80;
+  int neg = signbit(v) ? 1 : 0;
+  double a = fabs(v);
+  if (a == 0.0) return neg ? 0x8000 : 0x0000;
+  int e;
+  frexp(a, &e); /* a = m * 2^e, m in [0.5, 1) */
+  int qexp = e - 8;          /* 8 significant bits */
+  if (qexp < -133) qexp = -133; /* subnormal spacing 2^-133 */
+  double q = ldexp(1.0, qexp);
+  double n = nearbyint(a / q); /* exact division by a power of two; ties-to-even */
+  double r = n * q;
+  uint16_t bits;
+  if (r > 3.3895313892515355e38) { /* largest finite bf16, (2 - 2^-7) * 2^127 */
+    bits = 0x7F80;
+  } else {
+    float f = (float)r; /* exact: r has at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    bits = (uint16_t)(u >> 16);
+  }
+  return (uint16_t)(bits | (neg ? 0x8000 : 0));
+}
+
+/* ---------------------------------------------------------- dense linear */
+
+/* One fp32 dot product: acc = fl32(acc + fl32(x_k * w_k)), K ascending.
+ * Also returns sum_k |x_k * w_k| in fp64 (the scale of the acceptance bound). */
+static float dot_row(const uint16_t* x, const uint8_t* w, const uint8_t* s, int64_t K, int64_t r,
+                     double* abs_sum) {
+  float acc = 0.0f;
+  double as = 0.0;
+  for (int64_t k = 0; k < K; ++k) {
+    double xv = bf16_to_f64(x[k]);
+    double wv = weight(w, s, K, r, k);
+    double p = xv * wv; /* exact in fp64 */
+    float pf = (float)p;
+    acc = acc + pf;
+    as += fabs(p);
+  }
+  if (abs_sum) *abs_sum = as;
+  return acc;
+}
+
+/* y[t,n] = bf16(sum_k x[t,k] * w[n,k]).  x: bf16 bits [T,K]; w: [N,K/2];
+ * s: [N,K/32].  Outputs: y bf16 bits [T,N]; acc fp32 [T,N] (may be NULL);
+ * scale_d fp64 [T,N] = sum_k |x*w| (may be NULL). */
+void ora_mx_linear(const uint16_t* x, const uint8_t* w, const uint8_t* s, int64_t T, int64_t K,
+                   int64_t N, uint16_t* y, float* acc, double* scale_d, int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(static) collapse(2)
+#endif
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t n = 0; n < N; ++n) {
+      double as;
+      float a = dot_row(x + t * K, w, s, K, n, &as);
+      if (y) y[t * N + n] = ora_bf16_rne((double)a);
+      if (acc) acc[t * N + n] = a;
+      if (scale_d) scale_d[t * N + n] = as;
+    }
+}
+
+/* ---------------------------------------------------------------- routing */
+
+/* For each token: the k largest logits, ties to the lower expert id, slots in
+ * descending-logit order; gate_j = exp(l_j - l_0) / sum_i exp(l_i - l_0)
+ * evaluated in fp64 and stored as fp32.  Logits must be finite. */
+void ora_route(const float* logits, int64_t T, int64_t E, int64_t k, int32_t* ids, float* gates) {
+  char* taken = (char*)malloc((size_t)E);
+  for (int64_t t = 0; t < T; ++t) {
+    const float* l = logits + t * E;
+    memset(taken, 0, (size_t)E);
+    for (int64_t j = 0; j < k; ++j) {
+      int64_t best = -1;
+      for (int64_t e = 0; e < E; ++e) {
+        if (taken[e]) continue;
+        if (best < 0 || l[e] > l[best]) best = e; /* strict '>' keeps the lower id on ties */
+      }
+      taken[best] = 1;
+      ids[t * k + j] = (int32_t)best;
+    }
+    double m = (double)l[ids[t * k]];
+    double den = 0.0;
+    for (int64_t j = 0; j < k; ++j) den += exp((double)l[ids[t * k + j]] - m);
+    for (int64_t j = 0; j < k; ++j) gates[t * k + j] = (float)(exp((double)l[ids[t * k + j]] - m) / den);
+  }
+  free(taken);
+}
+
+/* ------------------------------------------------------------ expert sort */
+
+/* Counting sort of the T*k flat slots f = t*k + j by expert id: experts
+ * ascending, f ascending within an expert.  counts [E]; offsets [E+1]
+ * (exclusive prefix sums); sorted_slots [T*k]; active [E] = experts with at
+ * least one slot, ascending (entries past num_active are set to -1). */
+void ora_sort(const int32_t* ids, int64_t T, int64_t k, int64_t E, int32_t* counts, int32_t* offsets,
+              int32_t* sorted_slots, int32_t* active, int32_t* num_active) {
+  int64_t F = T * k;
+  for (int64_t e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t f = 0; f < F; ++f) counts[ids[f]] += 1;
+  offsets[0] = 0;
+  for (int64_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  int32_t* fill = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+  for (int64_t f = 0; f < F; ++f) {
+    int32_t e = ids[f];
+    sorted_slots[offsets[e] + fill[e]] = (int32_t)f;
+    fill[e] += 1;
+  }
+  free(fill);
+  int32_t na = 0;
+  for (int64_t e = 0; e < E; ++e)
+    if (counts[e] > 0) active[na++] = (int32_t)e;
+  for (int64_t e = na; e < E; ++e) active[e] = -1;
+  *num_active = na;
+}
+
+/* ------------------------------------------------------------- MoE layer */
+
+/* silu(g) * u in fp64 from the fp32 g and u. */
+static double swiglu(float g, float u) {
+  double gd = (double)g;
+  return gd / (1.0 + exp(-gd)) * (double)u;
+}
+
+/* MoE forward for the tokens listed in tok[0..ntok): for each token t and
+ * slot j (expert e = ids[t,j], gate = gates[t,j]):
+ *   g_n = sum_K x[t,K] Wgu[e][n,K],  u_n = sum_K x[t,K] Wgu[e][I+n,K]   (fp32)
+ *   h_n = bf16(silu(g_n) * u_n)                                         n < I
+ *   d_n = sum_i h_i Wd[e][n,i]                                          (fp32)
+ *   y[t,n] = bf16(sum_j fl32(gate_j * d_{j,n}))  j ascending, fp32.
+ * Shapes: x bf16 [T,H]; logits f32 [T,E]; Wgu [E,2I,H/2], Sgu [E,2I,H/32];
+ * Wd [E,H,I/2], Sd [E,H,I/32].  Outputs indexed by position in tok:
+ * y [ntok,H] bf16 bits; scale_m [ntok,H] = sum_j gate_j sum_i |h_i Wd[e][n,i]|
+ * (fp64, may be NULL); h [ntok*k, I] bf16 bits (may be NULL). */
+void ora_moe_tokens(const uint16_t* x, const float* logits, int64_t k, const uint8_t* wgu,
+                    const uint8_t* sgu, const uint8_t* wd, const uint8_t* sd, int64_t T, int64_t H,
+                    int64_t I, int64_t E, const int32_t* tok, int64_t ntok, uint16_t* y,
+                    double* scale_m, uint16_t* h_out, int nthreads) {
+  (void)T;
+  int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)(ntok * k));
+  float* gates = (float*)malloc(sizeof(float) * (size_t)(ntok * k));
+  for (int64_t i = 0; i < ntok; ++i) ora_route(logits + (int64_t)tok[i] * E, 1, E, k, ids + i * k, gates + i * k);
+
+  uint16_t* h = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(ntok * k * I));
+  const int64_t gu_rows = 2 * I;
+  const size_t gu_w = (size_t)gu_rows * (size_t)(H / 2), gu_s = (size_t)gu_rows * (size_t)(H / 32);
+  const size_t d_w = (size_t)H * (size_t)(I / 2), d_s = (size_t)H * (size_t)(I / 32);
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(static) collapse(2)
+#endif
+  for (int64_t p = 0; p < ntok * k; ++p)
+    for (int64_t n = 0; n < I; ++n) {
+      int64_t t = tok[p / k];
+      int64_t e = ids[p];
+      const uint8_t* W = wgu + (size_t)e * gu_w;
+      const uint8_t* S = sgu + (size_t)e * gu_s;
+      float g = dot_row(x + t * H, W, S, H, n, NULL);
+      float u = dot_row(x + t * H, W, S, H, I + n, NULL);
+      h[p * I + n] = ora_bf16_rne(swiglu(g, u));
+    }
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) collapse(2)
+#endif
+  for (int64_t i = 0; i < ntok; ++i)
+    for (int64_t n = 0; n < H; ++n) {
+      float acc = 0.0f;
+      double sm = 0.0;
+      for (int64_t j = 0; j < k; ++j) {
+        int64_t p = i * k + j;
+        int64_t e = ids[p];
+        double as;
+        float d = dot_row(h + p * I, wd + (size_t)e * d_w, sd + (size_t)e * d_s, I, n, &as);
+        float gd = (float)((double)gates[p] * (double)d);
+        acc = acc + gd;
+        sm += (double)gates[p] * as;
+      }
+      y[i * H + n] = ora_bf16_rne((double)acc);
+      if (scale_m) scale_m[i * H + n] = sm;
+    }
+  if (h_out) memcpy(h_out, h, sizeof(uint16_t) * (size_t)(ntok * k * I));
+  free(h);
+  free(gates);
+  free(ids);
+}
