@@ -1,0 +1,146 @@
+/*
+ * mxmoe -- MXFP4 weight-streaming MoE expert layer and dense MXFP4 linear layer for
+ * AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The operation (sources):
+ *   - MXFP4 ("Zyphra Inference Wave 2", section "Quantization."; the Open Compute
+ *     Project MX specification it names): blocks of 32 E2M1 4-bit values share one
+ *     E8M0 power-of-two scale; 4.25 bits per value.  E2M1 code c: sign = bit 3,
+ *     magnitude {0, 0.5, 1, 1.5, 2, 3, 4, 6}[c & 7].  E8M0 byte s: 2^(s-127), 0xFF = NaN.
+ *   - The MoE step ("Zyphra Inference Wave 2", sections "Speculative decoding." and
+ *     "Quantization"): a step of T tokens (requests x speculative positions) reads each
+ *     routed expert's weights once and applies them to every token routed to it; an
+ *     MXFP4 expert runs two expert GEMMs and a combine.
+ *   - Expert shapes of the pages' fused-MoE benchmarks (same page, Figure 10):
+ *     H = 7168, E = 256 or 384, top-k = 8.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers owned by the caller, unless stated otherwise.  The
+ *     library never allocates, never frees, never synchronizes, and keeps no state
+ *     between calls.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream); buffers must stay alive until that work completes.
+ *   - Tensors are dense row-major.  bf16 values are passed as their 16-bit patterns.
+ *   - MXFP4 weight layout: a matrix with R output rows and reduction length K is
+ *     codes [R][K/2] uint8 (element 2i in the low nibble of byte i) plus
+ *     scales [R][K/32] uint8 (one E8M0 byte per 32 consecutive K values of one row).
+ *   - Code and activation base pointers must be 16-byte aligned; scale pointers 8-byte
+ *     aligned.
+ *   - Return value: MX_OK (0) or a negative MX_ERR_* code.  All argument checks run on
+ *     the host before anything is enqueued; a failed check enqueues nothing.  Device
+ *     data (NaN, Inf) is not checked: NaN scales and NaN activations propagate.
+ */
+#ifndef MXMOE_H
+#define MXMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef MX_API
+#define MX_API __attribute__((visibility("default")))
+#endif
+
+enum mx_status {
+  MX_OK = 0,
+  MX_ERR_NULL = -1,      /* a required pointer is NULL */
+  MX_ERR_SHAPE = -2,     /* a size is out of range or not a required multiple */
+  MX_ERR_ALIGN = -3,     /* a pointer is not aligned as required */
+  MX_ERR_WORKSPACE = -4, /* workspace missing or smaller than moe_mxfp4_workspace_size */
+  MX_ERR_HIP = -5        /* the HIP runtime reported an error while enqueueing */
+};
+
+/* Limits checked by every call. */
+#define MX_MAX_TOKENS 256     /* T for the MoE calls */
+#define MX_MAX_EXPERTS 1024   /* E */
+#define MX_MAX_TOPK 32        /* top_k */
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+MX_API int mx_version(void);
+
+/* Static description of a status code; never NULL. */
+MX_API const char* mx_status_string(int status);
+
+/*
+ * Dense MXFP4 linear layer: y[t,n] = bf16_rne( sum_k x[t,k] * w[n,k] ), products exact,
+ * fp32 accumulation.
+ *   x       bf16 [T, K]
+ *   w_codes uint8 [N, K/2], w_scales uint8 [N, K/32]
+ *   y       bf16 [T, N]   (written)
+ *   T >= 1, N >= 1, K >= 32 and K % 32 == 0.
+ */
+MX_API int mx_linear(const uint16_t* x, const uint8_t* w_codes, const uint8_t* w_scales, uint16_t* y, int64_t T,
+              int64_t K, int64_t N, void* stream);
+
+/*
+ * Decode MXFP4 to bf16: out[r,k] = E2M1(code) * 2^(s-127), exact (NaN for s = 0xFF;
+ * +-Inf where the value exceeds the bf16 range, i.e. only for s >= 253).
+ *   w_codes uint8 [rows, K/2], w_scales uint8 [rows, K/32], out bf16 [rows, K].
+ *   rows >= 1, K >= 32, K % 32 == 0.
+ */
+MX_API int mxfp4_dequantize(const uint8_t* w_codes, const uint8_t* w_scales, int64_t rows, int64_t K, uint16_t* out,
+                     void* stream);
+
+/*
+ * Top-k routing with a softmax over the selected logits.  For each token t: the k
+ * largest logits[t,:] (ties go to the lower expert id), in descending-logit order;
+ * gates[t,j] = exp(l_j - l_0) / sum_i exp(l_i - l_0) in fp32.
+ *   logits fp32 [T, E] (must be finite), ids int32 [T, top_k], gates fp32 [T, top_k].
+ *   1 <= T <= MX_MAX_TOKENS, 1 <= top_k <= min(E, MX_MAX_TOPK), E <= MX_MAX_EXPERTS.
+ */
+MX_API int moe_route_topk(const float* logits, int64_t T, int64_t E, int64_t top_k, int32_t* ids, float* gates,
+                   void* stream);
+
+/*
+ * Counting sort of the T*top_k flat slots f = t*top_k + j by expert id ids[f]: experts
+ * ascending, f ascending within an expert (bit-exact, deterministic).
+ *   ids          int32 [T, top_k]; each row must hold top_k DISTINCT ids in [0, E)
+ *                (as moe_route_topk produces); other ids are skipped.
+ *   counts       int32 [E]       slots per expert
+ *   offsets      int32 [E + 1]   exclusive prefix sum of counts
+ *   sorted_slots int32 [T*top_k] flat slots in sorted order
+ *   active       int32 [E]       experts with counts > 0, ascending; -1 after the last
+ *   num_active   int32 [1]
+ */
+MX_API int moe_sort_by_expert(const int32_t* ids, int64_t T, int64_t top_k, int64_t E, int32_t* counts,
+                       int32_t* offsets, int32_t* sorted_slots, int32_t* active, int32_t* num_active,
+                       void* stream);
+
+/* Bytes of device workspace moe_mxfp4_forward needs for these sizes. */
+MX_API size_t moe_mxfp4_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k);
+
+/*
+ * MoE expert layer with MXFP4 weights and SwiGLU experts:
+ *   route:   ids, gates = moe_route_topk(router_logits, top_k)
+ *   gate_up: for slot (t, j) with expert e = ids[t,j]:
+ *              g_n = sum_c x[t,c] Wgu[e][n,c],  u_n = sum_c x[t,c] Wgu[e][I+n,c]    (fp32)
+ *              h_n = bf16_rne( silu(g_n) * u_n ),  silu(g) = g / (1 + exp(-g))    n < I
+ *   down:    d_n = sum_i h_i Wd[e][n,i]                                          (fp32)
+ *   combine: y[t,n] = bf16_rne( sum_j gates[t,j] * d_{t,j,n} )                    (fp32)
+ * Each routed expert's weights are read from HBM once per call, whatever the number of
+ * tokens routed to it; experts no token routes to are not read.
+ *   x             bf16 [T, H]
+ *   router_logits fp32 [T, E] (finite)
+ *   w_gate_up     uint8 [E, 2I, H/2]  (rows [0, I) gate, rows [I, 2I) up)
+ *   s_gate_up     uint8 [E, 2I, H/32]
+ *   w_down        uint8 [E, H, I/2]
+ *   s_down        uint8 [E, H, I/32]
+ *   y             bf16 [T, H]   (written)
+ *   workspace     device buffer of at least moe_mxfp4_workspace_size(T, H, I, E, top_k)
+ *                 bytes, 256-byte aligned; contents need no initialization and are
+ *                 overwritten.  Calls that share a workspace must not overlap in time.
+ *   1 <= T <= MX_MAX_TOKENS; 1 <= top_k <= min(E, MX_MAX_TOPK); E <= MX_MAX_EXPERTS;
+ *   H % 256 == 0; I % 256 == 0 (so both GEMMs stream whole 256-value segments).
+ */
+MX_API int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, int64_t top_k, const uint8_t* w_gate_up,
+                      const uint8_t* s_gate_up, const uint8_t* w_down, const uint8_t* s_down, uint16_t* y,
+                      int64_t T, int64_t H, int64_t I, int64_t E, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXMOE_H */

@@ -1,0 +1,213 @@
+"""Python binding of the mxmoe C ABI (include/mxmoe.h): MXFP4 weight-streaming MoE layer
+and dense MXFP4 linear layer for MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels of
+libmxmoe.so.  PyTorch provides device memory and the current stream.  If the library is
+not built, importing this package raises: there is no fallback path.
+
+bf16 tensors are passed as their bit patterns; MXFP4 weights are uint8 code tensors
+[..., rows, K/2] (element 2i in the low nibble) plus uint8 E8M0 scale tensors
+[..., rows, K/32].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmxmoe.so")
+
+MX_OK = 0
+MX_MAX_TOKENS = 256
+MX_MAX_EXPERTS = 1024
+MX_MAX_TOPK = 32
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m mxfp4_weight_moe_amd.build` (hipcc, gfx950) first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_lib.mx_version.restype = ctypes.c_int
+_lib.mx_status_string.restype = ctypes.c_char_p
+_lib.mx_status_string.argtypes = [ctypes.c_int]
+_lib.mx_linear.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P]
+_lib.mxfp4_dequantize.argtypes = [_P, _P, _I64, _I64, _P, _P]
+_lib.moe_route_topk.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P]
+_lib.moe_sort_by_expert.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P]
+_lib.moe_mxfp4_workspace_size.restype = ctypes.c_size_t
+_lib.moe_mxfp4_workspace_size.argtypes = [_I64, _I64, _I64, _I64, _I64]
+_lib.moe_mxfp4_forward.argtypes = [_P, _P, _I64, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]
+for _n in ("mx_linear", "mxfp4_dequantize", "moe_route_topk", "moe_sort_by_expert", "moe_mxfp4_forward"):
+    getattr(_lib, _n).restype = ctypes.c_int
+
+EXPORTED = ("mx_version", "mx_status_string", "mx_linear", "mxfp4_dequantize", "moe_route_topk",
+            "moe_sort_by_expert", "moe_mxfp4_workspace_size", "moe_mxfp4_forward")
+
+
+class MxError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call} failed: {status_string(status)} (status {status})")
+
+
+def version() -> int:
+    return _lib.mx_version()
+
+
+def status_string(status: int) -> str:
+    return _lib.mx_status_string(int(status)).decode()
+
+
+def raw():
+    """The ctypes handle of libmxmoe.so (for tests that call the C ABI directly)."""
+    return _lib
+
+
+def _ptr(t: torch.Tensor):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(t: torch.Tensor, name: str, dtype, ndim=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def _raise(status: int, call: str):
+    if status != MX_OK:
+        if status == -2:
+            raise ValueError(f"{call}: {status_string(status)}")
+        raise MxError(status, call)
+
+
+def mx_linear(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor,
+              out: torch.Tensor | None = None) -> torch.Tensor:
+    """y[T,N] = bf16(x[T,K] @ dequant(w)[N,K]^T), fp32 accumulation."""
+    _check(x, "x", torch.bfloat16, 2)
+    dev = x.device
+    _check(w_codes, "w_codes", torch.uint8, 2, dev)
+    _check(w_scales, "w_scales", torch.uint8, 2, dev)
+    T, K = x.shape
+    N = w_codes.shape[0]
+    if w_codes.shape != (N, K // 2) or w_scales.shape != (N, K // 32) or K % 32:
+        raise ValueError(f"weight shapes {tuple(w_codes.shape)}, {tuple(w_scales.shape)} do not match K={K}")
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, 2, dev)
+    if out.shape != (T, N):
+        raise ValueError("out has the wrong shape")
+    st = _lib.mx_linear(_ptr(x), _ptr(w_codes), _ptr(w_scales), _ptr(out), T, K, N, _stream(dev))
+    _raise(st, "mx_linear")
+    return out
+
+
+def mxfp4_dequantize(w_codes: torch.Tensor, w_scales: torch.Tensor) -> torch.Tensor:
+    """bf16 [rows, K] = E2M1(code) * 2^(s - 127), exact."""
+    _check(w_codes, "w_codes", torch.uint8)
+    dev = w_codes.device
+    _check(w_scales, "w_scales", torch.uint8, None, dev)
+    K = w_codes.shape[-1] * 2
+    rows = w_codes.numel() // (K // 2)
+    if w_scales.numel() != rows * (K // 32) or w_scales.shape[:-1] != w_codes.shape[:-1]:
+        raise ValueError("scale tensor does not match the code tensor")
+    out = torch.empty((*w_codes.shape[:-1], K), dtype=torch.bfloat16, device=dev)
+    st = _lib.mxfp4_dequantize(_ptr(w_codes), _ptr(w_scales), rows, K, _ptr(out), _stream(dev))
+    _raise(st, "mxfp4_dequantize")
+    return out
+
+
+def moe_route_topk(logits: torch.Tensor, top_k: int):
+    """(ids int32 [T,k], gates fp32 [T,k]): top-k logits (ties to lower id), softmax over them."""
+    _check(logits, "router_logits", torch.float32, 2)
+    dev = logits.device
+    T, E = logits.shape
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    gates = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    st = _lib.moe_route_topk(_ptr(logits), T, E, top_k, _ptr(ids), _ptr(gates), _stream(dev))
+    _raise(st, "moe_route_topk")
+    return ids, gates
+
+
+def moe_sort_by_expert(ids: torch.Tensor, num_experts: int) -> dict:
+    """Counting sort of the flat slots by expert (experts ascending, slot ascending)."""
+    _check(ids, "ids", torch.int32, 2)
+    dev = ids.device
+    T, k = ids.shape
+    E = int(num_experts)
+    out = dict(
+        counts=torch.empty(E, dtype=torch.int32, device=dev),
+        offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+        sorted_slots=torch.empty(T * k, dtype=torch.int32, device=dev),
+        active=torch.empty(E, dtype=torch.int32, device=dev),
+        num_active=torch.empty(1, dtype=torch.int32, device=dev),
+    )
+    st = _lib.moe_sort_by_expert(_ptr(ids), T, k, E, _ptr(out["counts"]), _ptr(out["offsets"]),
+                                 _ptr(out["sorted_slots"]), _ptr(out["active"]), _ptr(out["num_active"]),
+                                 _stream(dev))
+    _raise(st, "moe_sort_by_expert")
+    return out
+
+
+def workspace_size(T: int, H: int, I: int, E: int, top_k: int) -> int:
+    return int(_lib.moe_mxfp4_workspace_size(T, H, I, E, top_k))
+
+
+_ws_cache: dict = {}
+
+
+def workspace(T: int, H: int, I: int, E: int, top_k: int, device) -> torch.Tensor:
+    """A cached uint8 workspace tensor large enough for these sizes on `device`."""
+    need = workspace_size(T, H, I, E, top_k)
+    dev = torch.device(device)
+    buf = _ws_cache.get(dev)
+    if buf is None or buf.numel() < need:
+        buf = torch.empty(need, dtype=torch.uint8, device=dev)
+        _ws_cache[dev] = buf
+    return buf
+
+
+def moe_mxfp4_forward(x: torch.Tensor, router_logits: torch.Tensor, top_k: int, W_gate_up: torch.Tensor,
+                      S_gate_up: torch.Tensor, W_down: torch.Tensor, S_down: torch.Tensor,
+                      out: torch.Tensor | None = None, ws: torch.Tensor | None = None) -> torch.Tensor:
+    """y[T,H] of the MXFP4 SwiGLU MoE layer (see include/mxmoe.h for the definition)."""
+    _check(x, "x", torch.bfloat16, 2)
+    dev = x.device
+    _check(router_logits, "router_logits", torch.float32, 2, dev)
+    for t, n in ((W_gate_up, "W_gate_up"), (S_gate_up, "S_gate_up"), (W_down, "W_down"), (S_down, "S_down")):
+        _check(t, n, torch.uint8, 3, dev)
+    T, H = x.shape
+    E = router_logits.shape[1]
+    I = W_down.shape[2] * 2
+    if router_logits.shape[0] != T:
+        raise ValueError("router_logits must be [T, E]")
+    if (W_gate_up.shape != (E, 2 * I, H // 2) or S_gate_up.shape != (E, 2 * I, H // 32)
+            or W_down.shape != (E, H, I // 2) or S_down.shape != (E, H, I // 32)):
+        raise ValueError("expert weight shapes do not match [E, 2I, H/2], [E, 2I, H/32], [E, H, I/2], [E, H, I/32]")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, 2, dev)
+    if ws is None:
+        ws = workspace(T, H, I, E, top_k, dev)
+    _check(ws, "workspace", torch.uint8, 1, dev)
+    st = _lib.moe_mxfp4_forward(_ptr(x), _ptr(router_logits), top_k, _ptr(W_gate_up), _ptr(S_gate_up),
+                                _ptr(W_down), _ptr(S_down), _ptr(out), T, H, I, E, _ptr(ws), ws.numel(),
+                                _stream(dev))
+    _raise(st, "moe_mxfp4_forward")
+    return out

@@ -1,0 +1,147 @@
+// C-ABI entry points: host-side argument checks, workspace carving, kernel enqueue.
+// Every check runs before anything is enqueued; no call allocates or synchronizes.
+#include <atomic>
+#include <limits>
+
+#include "mx_internal.hpp"
+
+namespace mx {
+
+static constexpr size_t WS_ALIGN = 256;
+
+static size_t align_up(size_t v) { return (v + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN; }
+
+MoeWorkspace moe_workspace_carve(void* base, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
+  MoeWorkspace w{};
+  const size_t F = (size_t)(T * k);
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    char* p = base ? static_cast<char*>(base) + off : nullptr;
+    off += align_up(bytes);
+    return p;
+  };
+  w.ids = reinterpret_cast<int32_t*>(take(F * 4));
+  w.gates = reinterpret_cast<float*>(take(F * 4));
+  w.counts = reinterpret_cast<int32_t*>(take((size_t)E * 4));
+  w.offsets = reinterpret_cast<int32_t*>(take((size_t)(E + 1) * 4));
+  w.sorted_slots = reinterpret_cast<int32_t*>(take(F * 4));
+  w.active = reinterpret_cast<int32_t*>(take((size_t)E * 4));
+  w.num_active = reinterpret_cast<int32_t*>(take(4));
+  w.h = reinterpret_cast<uint16_t*>(take(F * (size_t)I * 2));
+  w.dpart = reinterpret_cast<float*>(take(F * (size_t)H * 4));
+  w.bytes = off;
+  return w;
+}
+
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+static constexpr int64_t INT_LIM = std::numeric_limits<int32_t>::max();
+
+static int check_moe_sizes(int64_t T, int64_t E, int64_t k) {
+  if (T < 1 || T > MX_MAX_TOKENS) return MX_ERR_SHAPE;
+  if (E < 1 || E > MX_MAX_EXPERTS) return MX_ERR_SHAPE;
+  if (k < 1 || k > MX_MAX_TOPK || k > E) return MX_ERR_SHAPE;
+  return MX_OK;
+}
+
+}  // namespace mx
+
+using namespace mx;
+
+extern "C" {
+
+int mx_version(void) { return 100; }
+
+const char* mx_status_string(int status) {
+  switch (status) {
+    case MX_OK: return "ok";
+    case MX_ERR_NULL: return "a required pointer is NULL";
+    case MX_ERR_SHAPE: return "a size is out of range or not a required multiple";
+    case MX_ERR_ALIGN: return "a pointer is not aligned as required";
+    case MX_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MX_ERR_HIP: return "the HIP runtime reported an error while enqueueing";
+    default: return "unknown status";
+  }
+}
+
+int mx_linear(const uint16_t* x, const uint8_t* w_codes, const uint8_t* w_scales, uint16_t* y, int64_t T, int64_t K,
+              int64_t N, void* stream) {
+  if (!x || !w_codes || !w_scales || !y) return MX_ERR_NULL;
+  if (T < 1 || N < 1 || K < 32 || K % 32 != 0) return MX_ERR_SHAPE;
+  if (T > INT_LIM || K > INT_LIM || N > INT_LIM || T * K > (int64_t)1 << 40 || N * K > (int64_t)1 << 42)
+    return MX_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(w_codes, 16) || !aligned(y, 8)) return MX_ERR_ALIGN;
+  if (K % 256 == 0 && !aligned(w_scales, 8)) return MX_ERR_ALIGN;  // 8-byte scale loads
+  return launch_mx_linear(x, w_codes, w_scales, y, (int)T, (int)K, (int)N, static_cast<hipStream_t>(stream));
+}
+
+int mxfp4_dequantize(const uint8_t* w_codes, const uint8_t* w_scales, int64_t rows, int64_t K, uint16_t* out,
+                     void* stream) {
+  if (!w_codes || !w_scales || !out) return MX_ERR_NULL;
+  if (rows < 1 || K < 32 || K % 32 != 0 || rows * (K / 32) > ((int64_t)1 << 38)) return MX_ERR_SHAPE;
+  if (!aligned(w_codes, 16) || !aligned(out, 16)) return MX_ERR_ALIGN;
+  return launch_dequant(w_codes, w_scales, rows, K, out, static_cast<hipStream_t>(stream));
+}
+
+int moe_route_topk(const float* logits, int64_t T, int64_t E, int64_t top_k, int32_t* ids, float* gates,
+                   void* stream) {
+  if (!logits || !ids || !gates) return MX_ERR_NULL;
+  const int st = check_moe_sizes(T, E, top_k);
+  if (st != MX_OK) return st;
+  if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(gates, 4)) return MX_ERR_ALIGN;
+  return launch_route(logits, (int)T, (int)E, (int)top_k, ids, gates, static_cast<hipStream_t>(stream));
+}
+
+int moe_sort_by_expert(const int32_t* ids, int64_t T, int64_t top_k, int64_t E, int32_t* counts, int32_t* offsets,
+                       int32_t* sorted_slots, int32_t* active, int32_t* num_active, void* stream) {
+  if (!ids || !counts || !offsets || !sorted_slots || !active || !num_active) return MX_ERR_NULL;
+  const int st = check_moe_sizes(T, E, top_k);
+  if (st != MX_OK) return st;
+  if (!aligned(ids, 4) || !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(sorted_slots, 4) ||
+      !aligned(active, 4) || !aligned(num_active, 4))
+    return MX_ERR_ALIGN;
+  return launch_sort(ids, (int)T, (int)top_k, (int)E, counts, offsets, sorted_slots, active, num_active,
+                     static_cast<hipStream_t>(stream));
+}
+
+size_t moe_mxfp4_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k) {
+  if (T < 1 || H < 1 || I < 1 || E < 1 || top_k < 1) return 0;
+  return moe_workspace_carve(nullptr, T, H, I, E, top_k).bytes;
+}
+
+int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, int64_t top_k, const uint8_t* w_gate_up,
+                      const uint8_t* s_gate_up, const uint8_t* w_down, const uint8_t* s_down, uint16_t* y, int64_t T,
+                      int64_t H, int64_t I, int64_t E, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !router_logits || !w_gate_up || !s_gate_up || !w_down || !s_down || !y) return MX_ERR_NULL;
+  int st = check_moe_sizes(T, E, top_k);
+  if (st != MX_OK) return st;
+  if (H < 256 || I < 256 || H % 256 != 0 || I % 256 != 0 || H > 65536 || I > 65536) return MX_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(w_gate_up, 16) || !aligned(w_down, 16) || !aligned(s_gate_up, 8) ||
+      !aligned(s_down, 8) || !aligned(y, 8) || !aligned(router_logits, 4))
+    return MX_ERR_ALIGN;
+  if (!workspace || !aligned(workspace, 256)) return MX_ERR_WORKSPACE;
+  const MoeWorkspace ws = moe_workspace_carve(workspace, T, H, I, E, top_k);
+  if (workspace_bytes < ws.bytes) return MX_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int t = (int)T, h = (int)H, i = (int)I, e = (int)E, k = (int)top_k;
+  if ((st = launch_route(router_logits, t, e, k, ws.ids, ws.gates, s)) != MX_OK) return st;
+  if ((st = launch_sort(ws.ids, t, k, e, ws.counts, ws.offsets, ws.sorted_slots, ws.active, ws.num_active, s)) != MX_OK)
+    return st;
+  if ((st = launch_gate_up(x, w_gate_up, s_gate_up, ws, t, h, i, e, k, s)) != MX_OK) return st;
+  if ((st = launch_down(w_down, s_down, ws, t, h, i, e, k, s)) != MX_OK) return st;
+  return launch_combine(ws, y, t, h, k, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// Host-side internals shared by the C-ABI translation units (not part of the public API).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/mxmoe.h"
+
+namespace mx {
+
+// Layout of the moe_mxfp4_forward workspace, carved in this order, 256-byte aligned.
+struct MoeWorkspace {
+  int32_t* ids;           // [T*k]
+  float* gates;           // [T*k]
+  int32_t* counts;        // [E]
+  int32_t* offsets;       // [E+1]
+  int32_t* sorted_slots;  // [T*k]
+  int32_t* active;        // [E]
+  int32_t* num_active;    // [1]
+  uint16_t* h;            // [T*k, I] bf16, rows in sorted-slot order
+  float* dpart;           // [T*k, H] fp32 gate-weighted down outputs, rows by flat slot
+  size_t bytes;
+};
+
+MoeWorkspace moe_workspace_carve(void* base, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k);
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int device_cu_count();
+
+// Kernel launchers (enqueue only; arguments already validated).
+int launch_mx_linear(const uint16_t* x, const uint8_t* w, const uint8_t* s, uint16_t* y, int T, int K, int N,
+                     hipStream_t stream);
+int launch_dequant(const uint8_t* w, const uint8_t* s, int64_t rows, int64_t K, uint16_t* out, hipStream_t stream);
+int launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* gates, hipStream_t stream);
+int launch_sort(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* sorted_slots,
+                int32_t* active, int32_t* num_active, hipStream_t stream);
+int launch_gate_up(const uint16_t* x, const uint8_t* wgu, const uint8_t* sgu, const MoeWorkspace& ws, int T, int H,
+                   int I, int E, int k, hipStream_t stream);
+int launch_down(const uint8_t* wd, const uint8_t* sd, const MoeWorkspace& ws, int T, int H, int I, int E, int k,
+                hipStream_t stream);
+int launch_combine(const MoeWorkspace& ws, uint16_t* y, int T, int H, int k, hipStream_t stream);
+
+}  // namespace mx

@@ -1,0 +1,140 @@
+// Dense MXFP4 linear layer (y = x W^T, W in MXFP4, x and y bf16, fp32 accumulation) and
+// the standalone MXFP4 -> bf16 decode.
+//
+// The dense layer is the MXFP4 projection the AMD megakernel blog applies to attention
+// projections and the LM head ("Bringing Ultra-Fast, Interactive LLM Inference to AMD
+// Instinct MI355X GPUs", section "3. Low-Precision Data Types"); here activations stay bf16.
+//
+// Work split: one workgroup per 16 output rows of W; its W waves split the K segments and
+// sum their partial tiles through LDS in a fixed order.  Activation rows are processed in
+// passes of up to 32 (two MFMA m-tiles).
+#include "mx_device.hpp"
+#include "mx_internal.hpp"
+
+namespace mx {
+
+template <int W, int MT, bool SBYTE>
+__device__ __forceinline__ void dense_pass(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
+                                           const uint8_t* __restrict__ s, uint16_t* __restrict__ y, int T, int K,
+                                           int N, int n0, int mp, uint8_t* slab, f32x4* red, int wave, int lane) {
+  constexpr int NS = 1;
+  constexpr int D = (MT == 1) ? 3 : 2;
+  StreamLanes<NS, MT> L;
+  lanes_init_lds(L, lane);
+  const int kb = K >> 1, ks = K >> 5;
+  for (int q = 0; q < 2; ++q) {
+    const int r = min(n0 + (lane >> 3) + 8 * q, N - 1);
+    L.w[0][q] = w + (size_t)r * kb + (lane & 7) * 16;
+  }
+  L.s[0] = s + (size_t)min(n0 + (lane & 15), N - 1) * ks;
+  for (int mt = 0; mt < MT; ++mt) {
+    const int t = mp + mt * 16 + (lane & 15);
+    L.x[mt] = (t < T) ? x + (size_t)t * K + 32 * (lane >> 4) : nullptr;
+  }
+  const int nseg = K / SEG_K;
+  const int nb_tail = (K % SEG_K) / 32;
+  const int sg0 = (int)((long)nseg * wave / W), sg1 = (int)((long)nseg * (wave + 1) / W);
+  f32x4 acc[MT][NS];
+  acc_zero(acc);
+  if (SBYTE) {
+    // Scale rows are not 8-byte aligned: every segment goes through the per-byte path.
+    Stage<NS, MT> st;
+    stage_zero_x(st);
+    for (int sg = sg0; sg < sg1; ++sg) {
+      stage_load_tail(st, L, sg, 8, lane);
+      stage_compute(st, L, slab, acc);
+    }
+    if (wave == W - 1 && nb_tail > 0) {
+      stage_load_tail(st, L, nseg, nb_tail, lane);
+      stage_compute(st, L, slab, acc);
+    }
+  } else {
+    stream_segments<NS, MT, D>(L, sg0, sg1, (wave == W - 1) ? nb_tail : 0, slab, acc, lane);
+  }
+  wg_reduce<NS, MT, W>(acc, red, wave, lane);
+  if (wave == 0) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int t = mp + mt * 16 + (lane & 15);
+      if (t >= T) continue;
+      const int n = n0 + 4 * (lane >> 4);
+      uint16_t o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = f32_to_bf16_rne(acc[mt][0][j]);
+      uint16_t* yp = y + (size_t)t * N + n;
+      if (n + 3 < N && (N & 3) == 0) {
+        *reinterpret_cast<u32x2*>(yp) = u32x2{(uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
+      } else {
+        for (int j = 0; j < 4; ++j)
+          if (n + j < N) yp[j] = o[j];
+      }
+    }
+  }
+}
+
+template <int W, bool SBYTE>
+__global__ void __launch_bounds__(W * 64) mx_linear_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
+                                                           const uint8_t* __restrict__ s, uint16_t* __restrict__ y,
+                                                           int T, int K, int N) {
+  __shared__ __attribute__((aligned(16))) uint8_t slabs[W][SLAB_BYTES];
+  __shared__ f32x4 red[(W > 1) ? W * 2 * 64 : 1];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n0 = blockIdx.x * SUB_ROWS;
+  for (int mp = 0; mp < T; mp += 32) {
+    if (T - mp > 16)
+      dense_pass<W, 2, SBYTE>(x, w, s, y, T, K, N, n0, mp, slabs[wave], red, wave, lane);
+    else
+      dense_pass<W, 1, SBYTE>(x, w, s, y, T, K, N, n0, mp, slabs[wave], red, wave, lane);
+  }
+}
+
+int launch_mx_linear(const uint16_t* x, const uint8_t* w, const uint8_t* s, uint16_t* y, int T, int K, int N,
+                     hipStream_t stream) {
+  const int items = (N + SUB_ROWS - 1) / SUB_ROWS;
+  const int nseg = K / SEG_K;
+  int W = 1;
+  while (W < 8 && 2 * W <= nseg && items * W < 2048) W *= 2;
+  const bool sbyte = (K % SEG_K) != 0;
+  dim3 grid(items), block(W * 64);
+#define MXL(WW, SB) hipLaunchKernelGGL((mx_linear_kernel<WW, SB>), grid, block, 0, stream, x, w, s, y, T, K, N)
+  if (sbyte) {
+    switch (W) {
+      case 1: MXL(1, true); break;
+      case 2: MXL(2, true); break;
+      case 4: MXL(4, true); break;
+      default: MXL(8, true); break;
+    }
+  } else {
+    switch (W) {
+      case 1: MXL(1, false); break;
+      case 2: MXL(2, false); break;
+      case 4: MXL(4, false); break;
+      default: MXL(8, false); break;
+    }
+  }
+#undef MXL
+  return hip_status(hipGetLastError());
+}
+
+// ------------------------------------------------------------------ decode
+
+// One thread per MX block: 16 code bytes + 1 scale byte -> 32 bf16 (64 bytes).
+__global__ void __launch_bounds__(256) mxfp4_dequant_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ s,
+                                                            int64_t nblocks, uint16_t* __restrict__ out) {
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nblocks) return;
+  const u32x4 codes = ld16(w + b * 16);
+  const float sc = e8m0_scale_operand(s[b]);
+  u32x4* o = reinterpret_cast<u32x4*>(out + b * 32);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) o[c] = __builtin_bit_cast(u32x4, decode8(codes[c], sc));
+}
+
+int launch_dequant(const uint8_t* w, const uint8_t* s, int64_t rows, int64_t K, uint16_t* out, hipStream_t stream) {
+  const int64_t nblocks = rows * (K / 32);  // blocks are contiguous in both tensors
+  const int64_t grid = (nblocks + 255) / 256;
+  hipLaunchKernelGGL(mxfp4_dequant_kernel, dim3((unsigned)grid), dim3(256), 0, stream, w, s, nblocks, out);
+  return hip_status(hipGetLastError());
+}
+
+}  // namespace mx

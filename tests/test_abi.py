@@ -1,0 +1,114 @@
+"""The C-ABI library loads without a GPU, exports exactly what include/mxmoe.h declares,
+and rejects bad arguments on the host before anything is enqueued.
+
+Every call here fails a host-side check, so no kernel is ever launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxmoe.h")
+
+m = pytest.importorskip("mxfp4_weight_moe_amd")
+
+MX_OK, MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_WORKSPACE, MX_ERR_HIP = 0, -1, -2, -3, -4, -5
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"MX_API\s+[\w\s\*]+?\b(\w+)\s*\(", src)))
+
+
+def test_exports_match_header():
+    decl = declared_functions()
+    assert decl == sorted(m.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", m.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = sorted(l.split()[-1] for l in out.splitlines() if " T " in l)
+    assert exported == decl
+    lib = m.raw()
+    for name in decl:
+        assert hasattr(lib, name)
+
+
+def test_header_compiles_as_c():
+    src = '#include "mxmoe.h"\nint main(void){return mx_version() > 0 ? 0 : 1;}\n'
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-I", os.path.dirname(HEADER), "-x", "c", "-"],
+                       input=src, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_status_strings():
+    for st in (MX_OK, MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_WORKSPACE, MX_ERR_HIP, 7):
+        assert isinstance(m.status_string(st), str) and m.status_string(st)
+    assert m.version() >= 100
+
+
+P = ctypes.c_void_p
+A = P(1 << 20)        # aligned fake pointer (never dereferenced: every call below fails a check)
+MIS = P((1 << 20) + 4)
+
+
+def test_mx_linear_rejects():
+    L = m.raw()
+    assert L.mx_linear(None, A, A, A, 1, 64, 16, None) == MX_ERR_NULL
+    assert L.mx_linear(A, A, A, A, 0, 64, 16, None) == MX_ERR_SHAPE
+    assert L.mx_linear(A, A, A, A, 1, 48, 16, None) == MX_ERR_SHAPE
+    assert L.mx_linear(A, A, A, A, 1, 0, 16, None) == MX_ERR_SHAPE
+    assert L.mx_linear(A, A, A, A, 1, 64, 0, None) == MX_ERR_SHAPE
+    assert L.mx_linear(MIS, A, A, A, 1, 64, 16, None) == MX_ERR_ALIGN
+    assert L.mx_linear(A, MIS, A, A, 1, 64, 16, None) == MX_ERR_ALIGN
+    assert L.mx_linear(A, A, MIS, A, 1, 256, 16, None) == MX_ERR_ALIGN
+    assert L.mx_linear(A, A, A, P((1 << 20) + 2), 1, 64, 16, None) == MX_ERR_ALIGN
+
+
+def test_dequant_rejects():
+    L = m.raw()
+    assert L.mxfp4_dequantize(None, A, 1, 32, A, None) == MX_ERR_NULL
+    assert L.mxfp4_dequantize(A, A, 0, 32, A, None) == MX_ERR_SHAPE
+    assert L.mxfp4_dequantize(A, A, 1, 33, A, None) == MX_ERR_SHAPE
+    assert L.mxfp4_dequantize(MIS, A, 1, 32, A, None) == MX_ERR_ALIGN
+
+
+def test_route_and_sort_reject():
+    L = m.raw()
+    assert L.moe_route_topk(None, 1, 8, 2, A, A, None) == MX_ERR_NULL
+    assert L.moe_route_topk(A, 0, 8, 2, A, A, None) == MX_ERR_SHAPE
+    assert L.moe_route_topk(A, 257, 8, 2, A, A, None) == MX_ERR_SHAPE
+    assert L.moe_route_topk(A, 1, 8, 9, A, A, None) == MX_ERR_SHAPE
+    assert L.moe_route_topk(A, 1, 1025, 2, A, A, None) == MX_ERR_SHAPE
+    assert L.moe_route_topk(A, 1, 64, 33, A, A, None) == MX_ERR_SHAPE
+    assert L.moe_route_topk(P((1 << 20) + 2), 1, 8, 2, A, A, None) == MX_ERR_ALIGN
+    assert L.moe_sort_by_expert(A, 1, 2, 8, A, A, A, A, None, None) == MX_ERR_NULL
+    assert L.moe_sort_by_expert(A, 1, 0, 8, A, A, A, A, A, None) == MX_ERR_SHAPE
+
+
+def test_forward_rejects():
+    L = m.raw()
+    ws = m.workspace_size(4, 512, 256, 8, 2)
+    assert ws > 0 and ws % 256 == 0
+
+    def fwd(x=A, lg=A, k=2, wgu=A, sgu=A, wd=A, sd=A, y=A, T=4, H=512, I=256, E=8, w=A, wb=ws):
+        return L.moe_mxfp4_forward(x, lg, k, wgu, sgu, wd, sd, y, T, H, I, E, w, wb, None)
+
+    assert fwd(x=None) == MX_ERR_NULL
+    assert fwd(sd=None) == MX_ERR_NULL
+    assert fwd(T=0) == MX_ERR_SHAPE
+    assert fwd(T=257) == MX_ERR_SHAPE
+    assert fwd(k=9) == MX_ERR_SHAPE
+    assert fwd(H=320) == MX_ERR_SHAPE
+    assert fwd(I=96) == MX_ERR_SHAPE
+    assert fwd(wgu=MIS) == MX_ERR_ALIGN
+    assert fwd(sgu=P((1 << 20) + 4)) == MX_ERR_ALIGN
+    assert fwd(w=None) == MX_ERR_WORKSPACE
+    assert fwd(w=P((1 << 20) + 128)) == MX_ERR_WORKSPACE
+    assert fwd(wb=ws - 1) == MX_ERR_WORKSPACE
+
+
+def test_workspace_size_grows_with_tokens():
+    a = m.workspace_size(1, 7168, 2048, 256, 8)
+    b = m.workspace_size(128, 7168, 2048, 384, 8)
+    assert 0 < a < b
+    assert m.workspace_size(0, 7168, 2048, 256, 8) == 0

@@ -1,0 +1,251 @@
+"""GPU parity: every stage of the HIP path against the CPU oracle on the same seeded inputs.
+
+All calls go through the C ABI of libmxmoe.so (via the thin Python binding).  Sizes run
+from tiny edge cases through several tiles with ragged tails to the full workload shapes
+(sampled tokens where the oracle would take too long).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from tests.gpu_helpers import (DENSE_REL, MOE_REL, bf16_to_f, check_bound, say, to_dev_bf16,
+                               to_host_bits)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    import mxfp4_weight_moe_amd  # noqa: F401  (fails loudly if the HIP library is missing)
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def mx(dev):
+    import mxfp4_weight_moe_amd
+    return mxfp4_weight_moe_amd
+
+
+# ------------------------------------------------------------------ decode
+
+def expected_decode_bits(w, s, rows, K):
+    v = oracle.dequant(w, s, rows, K)  # exact fp64
+    return torch.from_numpy(v).float().bfloat16().view(torch.int16).numpy().view(np.uint16)
+
+
+def test_dequant_all_codes_all_scales(dev, mx):
+    K = 512
+    w = np.tile(np.arange(256, dtype=np.uint8), (256, 1))   # row r: every byte value
+    s = np.repeat(np.arange(256, dtype=np.uint8)[:, None], K // 32, axis=1)  # row r: scale byte r
+    say("dequant all codes x all scales", w.shape)
+    out = mx.mxfp4_dequantize(torch.from_numpy(w).to(dev), torch.from_numpy(s).to(dev))
+    got = to_host_bits(out)
+    want = expected_decode_bits(w, s, 256, K)
+    nan_rows = np.isnan(bf16_to_f(want))
+    assert np.array_equal(np.isnan(bf16_to_f(got)), nan_rows)
+    assert np.array_equal(got[~nan_rows], want[~nan_rows])
+
+
+def test_dequant_random_large(dev, mx):
+    cfg = synthetic.LINEAR_CONFIGS["dense_t4"]
+    _, w, s = synthetic.linear_inputs(cfg)
+    say("dequant", w.shape)
+    out = mx.mxfp4_dequantize(torch.from_numpy(w).to(dev), torch.from_numpy(s).to(dev))
+    assert np.array_equal(to_host_bits(out), expected_decode_bits(w, s, cfg.N, cfg.K))
+
+
+# ------------------------------------------------------------------ dense linear
+
+def run_linear(dev, mx, x, w, s, T, K, N):
+    y = mx.mx_linear(to_dev_bf16(x, dev), torch.from_numpy(w).to(dev), torch.from_numpy(s).to(dev))
+    torch.cuda.synchronize()
+    return to_host_bits(y)
+
+
+@pytest.mark.parametrize("name", ["dense_t1", "dense_t4"])
+def test_mx_linear_configs(dev, mx, name):
+    cfg = synthetic.LINEAR_CONFIGS[name]
+    x, w, s = synthetic.linear_inputs(cfg)
+    say("mx_linear", name, cfg)
+    got = run_linear(dev, mx, x, w, s, cfg.T, cfg.K, cfg.N)
+    y, _, sd = oracle.mx_linear(x, w, s, cfg.T, cfg.K, cfg.N)
+    worst = check_bound(got, y, sd, DENSE_REL, name)
+    say(f"  worst ratio {worst:.3g}")
+
+
+ODD = [(1, 32, 16), (3, 64, 17), (2, 96, 40), (5, 288, 33), (16, 256, 16), (17, 512, 48), (31, 1024, 64),
+       (32, 800, 80), (33, 256, 32), (64, 2048, 128), (100, 256, 20), (7, 7168, 100), (4, 7200, 64)]
+
+
+@pytest.mark.parametrize("T,K,N", ODD)
+def test_mx_linear_odd_shapes(dev, mx, T, K, N):
+    cfg = synthetic.LinearConfig("odd", T=T, K=K, N=N, e_lo=-6, e_hi=2, seed=T * 7 + K + N)
+    x, w, s = synthetic.linear_inputs(cfg)
+    say("mx_linear odd", T, K, N)
+    got = run_linear(dev, mx, x, w, s, T, K, N)
+    y, _, sd = oracle.mx_linear(x, w, s, T, K, N)
+    check_bound(got, y, sd, DENSE_REL, f"odd {T},{K},{N}")
+
+
+def test_mx_linear_edge_values(dev, mx):
+    # subnormal-producing and overflowing scales, NaN scale, zero and one-hot activations
+    T, K, N = 3, 256, 32
+    cfg = synthetic.LinearConfig("edge", T=T, K=K, N=N, e_lo=-6, e_hi=0, seed=5)
+    x, w, s = synthetic.linear_inputs(cfg)
+    s = s.copy()
+    s[3, :] = 255       # NaN scales: whole output column NaN
+    s[4, 2] = 255       # one NaN block
+    s[5, :] = 250       # large weights, finite products
+    s[6, :] = 30        # tiny weights (~2^-97), normal in fp32
+    x = x.copy()
+    x[1, :] = 0         # zero row -> +0 outputs (except NaN columns)
+    x[2, :] = 0
+    x[2, 7] = 0x3F80    # one-hot row -> extracts weight column 7
+    say("mx_linear edge values")
+    got = run_linear(dev, mx, x, w, s, T, K, N)
+    y, _, sd = oracle.mx_linear(x, w, s, T, K, N)
+    check_bound(got, y, sd, DENSE_REL, "edge")
+    fin = ~np.isnan(bf16_to_f(y[2]))
+    assert np.array_equal(got[2][fin], y[2][fin])
+
+
+# ------------------------------------------------------------------ routing and sort
+
+ROUTE_CASES = [("moe_t4", None), ("moe_t32_zipf", None), ("moe_t128", None)]
+
+
+def route_logits(name):
+    return synthetic.router_logits(synthetic.MOE_CONFIGS[name])
+
+
+@pytest.mark.parametrize("name", ["moe_t4", "moe_t32_zipf", "moe_t128"])
+def test_route_matches_oracle(dev, mx, name):
+    cfg = synthetic.MOE_CONFIGS[name]
+    logits = synthetic.router_logits(cfg)
+    say("route", name, logits.shape)
+    ids, gates = mx.moe_route_topk(torch.from_numpy(logits).to(dev), cfg.k)
+    oids, ogates = oracle.route(logits, cfg.k)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    assert np.max(np.abs(gates.cpu().numpy().astype(np.float64) - ogates)) <= 1e-6
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (3, 7, 7), (5, 64, 3), (17, 1024, 32), (256, 256, 8), (2, 65, 4)])
+def test_route_edge_shapes_and_ties(dev, mx, T, E, k):
+    rng = np.random.default_rng(T + E + k)
+    logits = np.round(rng.standard_normal((T, E)), 1).astype(np.float32)  # many exact ties
+    logits[0, :] = 0.0                                                    # all tied
+    say("route ties", T, E, k)
+    ids, gates = mx.moe_route_topk(torch.from_numpy(logits).to(dev), k)
+    oids, ogates = oracle.route(logits, k)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    assert np.max(np.abs(gates.cpu().numpy().astype(np.float64) - ogates)) <= 1e-6
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 256, 8), (4, 256, 8), (32, 256, 8), (128, 384, 8), (256, 1024, 32),
+                                   (3, 4, 4), (9, 7, 2), (256, 8, 1)])
+def test_sort_matches_oracle(dev, mx, T, E, k):
+    rng = np.random.default_rng(T * 3 + E)
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    say("sort", T, E, k)
+    r = mx.moe_sort_by_expert(torch.from_numpy(ids).to(dev), E)
+    o = oracle.sort(ids, E)
+    for key in ("counts", "offsets", "sorted_slots", "active"):
+        assert np.array_equal(r[key].cpu().numpy(), o[key]), key
+    assert int(r["num_active"].item()) == o["num_active"]
+
+
+# ------------------------------------------------------------------ MoE layer
+
+def moe_device_inputs(cfg, dev, host=None):
+    """Inputs for a config: tiny configs drawn on the host, large ones on the device."""
+    if host is not None:
+        d = {k: torch.from_numpy(v).to(dev) for k, v in host.items() if k in ("wgu", "sgu", "wd", "sd")}
+        x, logits = host["x"], host["logits"]
+    else:
+        d = synthetic.moe_weights_device(cfg, dev)
+        x, logits = synthetic.moe_activations(cfg)
+    d["x"] = to_dev_bf16(x, dev)
+    d["logits"] = torch.from_numpy(logits).to(dev)
+    return d, x, logits
+
+
+def run_moe(mx, d, k):
+    y = mx.moe_mxfp4_forward(d["x"], d["logits"], k, d["wgu"], d["sgu"], d["wd"], d["sd"])
+    torch.cuda.synchronize()
+    return to_host_bits(y)
+
+
+def oracle_moe(cfg, x, logits, w_host, tokens=None):
+    y, sm, _ = oracle.moe_tokens(x, logits, cfg.k, w_host["wgu"], w_host["sgu"], w_host["wd"], w_host["sd"],
+                                 cfg.T, cfg.H, cfg.I, cfg.E, tokens=tokens)
+    return y, sm
+
+
+TINY = [
+    dict(T=1, H=256, I=256, E=4, k=1),
+    dict(T=3, H=256, I=256, E=4, k=2),
+    dict(T=5, H=512, I=256, E=8, k=3),
+    dict(T=17, H=256, I=512, E=4, k=2),    # 17 rows on some experts: two m-tiles
+    dict(T=40, H=256, I=256, E=4, k=4),    # every expert has 40 rows: passes of 32
+    dict(T=64, H=768, I=256, E=16, k=8),
+    dict(T=2, H=256, I=256, E=300, k=8),   # most experts inactive
+]
+
+
+@pytest.mark.parametrize("shape", TINY, ids=[f"T{s['T']}_H{s['H']}_I{s['I']}_E{s['E']}_k{s['k']}" for s in TINY])
+def test_moe_tiny_full_oracle(dev, mx, shape):
+    cfg = synthetic.MoEConfig("tiny", routing="normal", e_lo=-8, e_hi=-2, seed=shape["T"] + shape["E"], **shape)
+    host = synthetic.moe_inputs_host(cfg)
+    say("moe tiny", shape)
+    d, x, logits = moe_device_inputs(cfg, dev, host)
+    got = run_moe(mx, d, cfg.k)
+    y, sm = oracle_moe(cfg, x, logits, host)
+    worst = check_bound(got, y, sm, MOE_REL, f"tiny {shape}")
+    say(f"  worst ratio {worst:.3g}")
+
+
+FULL = [("moe_t4", None), ("moe_t32_zipf", [0, 5, 13, 31]), ("moe_t128", [0, 1, 64, 127])]
+
+
+@pytest.mark.parametrize("name,tokens", FULL, ids=[f[0] for f in FULL])
+def test_moe_full_size(dev, mx, name, tokens):
+    cfg = synthetic.MOE_CONFIGS[name]
+    say("moe full", name, "tokens", tokens)
+    d, x, logits = moe_device_inputs(cfg, dev)
+    got = run_moe(mx, d, cfg.k)
+    w_host = {k: d[k].cpu().numpy() for k in ("wgu", "sgu", "wd", "sd")}
+    tok = np.arange(cfg.T, dtype=np.int32) if tokens is None else np.array(tokens, np.int32)
+    y, sm = oracle_moe(cfg, x, logits, w_host, tokens=tok)
+    worst = check_bound(got[tok], y, sm, MOE_REL, name)
+    say(f"  worst ratio {worst:.3g}")
+
+
+def test_moe_small_scale_variant(dev, mx):
+    cfg = synthetic.small_scale_variant(synthetic.MOE_CONFIGS["moe_t4"])
+    say("moe small-scale variant")
+    d, x, logits = moe_device_inputs(cfg, dev)
+    got = run_moe(mx, d, cfg.k)
+    w_host = {k: d[k].cpu().numpy() for k in ("wgu", "sgu", "wd", "sd")}
+    y, sm = oracle_moe(cfg, x, logits, w_host)
+    worst = check_bound(got, y, sm, MOE_REL, "small-scale")
+    say(f"  worst ratio {worst:.3g}")
+
+
+def test_moe_deterministic_and_inactive_experts_unread(dev, mx):
+    cfg = synthetic.MoEConfig("det", T=8, H=512, I=256, E=32, k=4, routing="normal", e_lo=-8, e_hi=-2, seed=3)
+    host = synthetic.moe_inputs_host(cfg)
+    say("moe determinism / inactive NaN scales")
+    d, x, logits = moe_device_inputs(cfg, dev, host)
+    y1 = run_moe(mx, d, cfg.k)
+    y2 = run_moe(mx, d, cfg.k)
+    assert np.array_equal(y1, y2)
+    ids, _ = oracle.route(logits, cfg.k)
+    unused = sorted(set(range(cfg.E)) - set(ids.ravel().tolist()))
+    assert unused
+    for key in ("sgu", "sd"):
+        d[key][unused] = 255
+    y3 = run_moe(mx, d, cfg.k)
+    assert np.array_equal(y1, y3)
