@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Benchmark of the MXFP4 weight-streaming MoE layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload moe_t32_zipf] [--layers L]
+
+A step is one MoE layer forward (route, sort, gate_up + SwiGLU, down + combine) over one
+batch of T tokens.  Steps cycle over L distinct layers (own weights, own activations and
+routing), as a decode step walks a stack of MoE layers, so no step finds its expert
+weights in a cache: the 256 MB last-level cache is smaller than the active bytes of L-1
+layers.  Inputs are resident in HBM before timing.  The timed region replays one HIP
+graph holding the L layer forwards (moe_mxfp4_forward) K/L times, between two device
+synchronizations; K is rounded up to a multiple of L.
+
+Printed: one JSON line with the layer time (us), effective weight GB/s, a roofline entry
+for the dominant kernel (gate_up, timed with HIP events on its launch stream during a
+stage-by-stage pass) and the CPU oracle's time on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+METRIC = "µs per MXFP4 MoE layer and effective weight GB/s (% of 8 TB/s) at T=1..128"
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="moe_t32_zipf",
+                    help="moe_t4 | moe_t32_zipf | moe_t128 | moe_sweep_t<T>")
+    ap.add_argument("--layers", type=int, default=4, help="distinct layers cycled by the steps")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replay")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=32, help="tokens of the oracle's timed sample")
+    ap.add_argument("--stage-steps", type=int, default=None, help="steps of the per-kernel event pass (default K)")
+    ap.add_argument("--copy-mib", type=int, default=1024,
+                    help="size of the untimed reference copy (read + write) that calibrates HBM byte counters")
+    return ap.parse_args()
+
+
+def workload_config(name: str):
+    import synthetic
+    if name in synthetic.MOE_CONFIGS:
+        return synthetic.MOE_CONFIGS[name]
+    if name.startswith("moe_sweep_t"):
+        return synthetic.sweep_config(int(name[len("moe_sweep_t"):]))
+    raise SystemExit(f"unknown workload {name}")
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    import mxfp4_weight_moe_amd as mx  # raises if the HIP library is not built
+    import synthetic
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = workload_config(args.workload)
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    L = max(1, args.layers)
+
+    def log(*a):
+        print(*a, file=sys.stderr, flush=True)
+
+    log(f"[bench] workload {cfg.name}: T={T} H={H} I={I} E={E} k={k} routing={cfg.routing} layers={L}")
+    layers = []
+    for li in range(L):
+        w = synthetic.moe_weights_device(cfg, dev, layer=li)
+        x_bits, logits = synthetic.moe_activations(cfg, layer=li)
+        layers.append(dict(
+            w=w,
+            x=torch.from_numpy(x_bits.view(np.int16)).to(dev).view(torch.bfloat16),
+            logits=torch.from_numpy(logits).to(dev),
+            y=torch.empty((T, H), dtype=torch.bfloat16, device=dev),
+            x_bits=x_bits, logits_host=logits,
+        ))
+    ws = mx.workspace(T, H, I, E, k, dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident: {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
+
+    def forward(lay):
+        w = lay["w"]
+        mx.moe_mxfp4_forward(lay["x"], lay["logits"], k, w["wgu"], w["sgu"], w["wd"], w["sd"], out=lay["y"], ws=ws)
+
+    for i in range(max(1, args.warmup)):
+        forward(layers[i % L])
+    torch.cuda.synchronize()
+
+    # Untimed reference copy of a known size: under a counter profiler its FETCH_SIZE and
+    # WRITE_SIZE give the scale between the counters and bytes actually moved.
+    if args.copy_mib > 0:
+        src = torch.empty(args.copy_mib << 18, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    graph = None
+    if not args.eager:
+        # one graph holds the L layers back to back, as one decode step's graph would
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=side):
+                for lay in layers:
+                    forward(lay)
+        torch.cuda.current_stream(dev).wait_stream(side)
+        for _ in range(max(1, args.warmup // L)):
+            graph.replay()
+        torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- timed region
+    reps = max(1, -(-args.steps // L))
+    K = reps * L
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(reps):
+        if graph is not None:
+            graph.replay()
+        else:
+            for lay in layers:
+                forward(lay)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    log(f"[bench] timed {K} steps: {ms_per_step * 1e3:.1f} us/layer")
+
+    # ---------------------------------------------------------------- per-kernel pass (HIP events)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+    srt = dict(counts=torch.empty(E, dtype=torch.int32, device=dev),
+               offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+               sorted_slots=torch.empty(T * k, dtype=torch.int32, device=dev),
+               active=torch.empty(E, dtype=torch.int32, device=dev),
+               num_active=torch.empty(1, dtype=torch.int32, device=dev))
+    h = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    KS = args.stage_steps or K
+    names = ("route", "sort", "gate_up", "down_combine")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(KS)]
+    n_active = []
+    for i in range(KS):
+        lay = layers[i % L]
+        w = lay["w"]
+        e = evs[i]
+        e[0].record(stream)
+        mx.moe_route_topk(lay["logits"], k, ids=ids, gates=gates)
+        e[1].record(stream)
+        mx.moe_sort_by_expert(ids, E, out=srt)
+        e[2].record(stream)
+        mx.moe_gate_up_swiglu(lay["x"], w["wgu"], w["sgu"], srt, k, h=h)
+        e[3].record(stream)
+        mx.moe_down_combine(h, gates, w["wd"], w["sd"], srt, T, k, out=lay["y"], ws=ws)
+        e[4].record(stream)
+        if i < L:
+            n_active.append(srt["num_active"].clone())
+    torch.cuda.synchronize()
+    stage_ms = {n: [] for n in names}
+    for e in evs:
+        for j, n in enumerate(names):
+            stage_ms[n].append(e[j].elapsed_time(e[j + 1]))
+    n_active = [int(a.item()) for a in n_active]
+
+    # ---------------------------------------------------------------- bytes and roofline
+    gu_expert = 2 * I * H // 2 + 2 * I * H // 32          # gate_up codes + scales per expert
+    dn_expert = H * I // 2 + H * I // 32                  # down codes + scales per expert
+    act_bytes = T * H * 2 + T * E * 4 + T * H * 2         # x, router logits, y
+    layer_bytes = [na * (gu_expert + dn_expert) + act_bytes for na in n_active]
+    mean_layer_bytes = float(np.mean([layer_bytes[i % L] for i in range(K)]))
+    us_per_layer = ms_per_step * 1e3
+    eff_gbps = mean_layer_bytes / (us_per_layer * 1e-6) / 1e9
+    # gate_up per launch: its experts' codes + scales, x read once, h written
+    gu_bytes = [n_active[i % L] * gu_expert + T * H * 2 + T * k * I * 2 for i in range(KS)]
+    gu_ms = stage_ms["gate_up"]
+    gu_achieved = float(np.sum(gu_bytes) / (np.sum(gu_ms) * 1e-3) / 1e9)
+    roofline = {
+        "kernel": "moe_gate_up_kernel",
+        "bound": "hbm",
+        "achieved": round(gu_achieved, 1),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(gu_achieved / HBM_PEAK_GBPS, 4),
+        "traffic": None,
+        "avg_launch_us": round(float(np.mean(gu_ms)) * 1e3, 2),
+        "bytes_per_launch": int(np.mean(gu_bytes)),
+    }
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        lay = layers[0]
+        n = max(1, min(args.cpu_tokens, T))
+        toks = np.arange(n, dtype=np.int32)
+        w_host = {key: lay["w"][key].cpu().numpy() for key in ("wgu", "sgu", "wd", "sd")}
+        threads = oracle.default_threads()
+        log(f"[bench] oracle on {n} of {T} tokens, {threads} threads")
+        c0 = time.perf_counter()
+        oracle.moe_tokens(lay["x_bits"], lay["logits_host"], k, w_host["wgu"], w_host["sgu"], w_host["wd"],
+                          w_host["sd"], T, H, I, E, tokens=toks, nthreads=threads)
+        c1 = time.perf_counter()
+        cpu = {
+            "value": round((c1 - c0) * (T / n) * 1e6, 1),
+            "unit": "us/layer",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": f"layer 0, tokens 0..{n - 1} of {T} (all {k} routed experts each), full route+gate_up+down+combine; "
+                      f"time scaled by {T}/{n}; CPU: {cpu_model()}",
+            "seconds": round(c1 - c0, 2),
+        }
+        del w_host
+
+    out = {
+        "metric": METRIC,
+        "value": round(us_per_layer, 2),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name, "T": T, "H": H, "I": I, "E": E, "top_k": k, "routing": cfg.routing,
+            "weights": "MXFP4 (E2M1 codes, E8M0 scale per 32)", "accumulate": "fp32",
+            "layers_cycled": L, "timing": "eager launches" if args.eager else "HIP graph replay",
+        },
+        "effective_GBps": round(eff_gbps, 1),
+        "pct_of_8TBps": round(100 * eff_gbps / HBM_PEAK_GBPS, 2),
+        "active_experts": n_active,
+        "algorithmic_bytes_per_layer": int(mean_layer_bytes),
+        "stages_us": {n: round(float(np.mean(v)) * 1e3, 2) for n, v in stage_ms.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "env": {"GPU_MAX_HW_QUEUES": os.environ.get("GPU_MAX_HW_QUEUES"), "torch": torch.__version__,
+                "hip": getattr(torch.version, "hip", None)},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -108,6 +108,31 @@ MX_API int moe_sort_by_expert(const int32_t* ids, int64_t T, int64_t top_k, int6
                        int32_t* offsets, int32_t* sorted_slots, int32_t* active, int32_t* num_active,
                        void* stream);
 
+/*
+ * Stage hook: the gate_up GEMM with its SwiGLU epilogue, for every routed slot, from a
+ * moe_sort_by_expert result (counts, offsets, sorted_slots, active, num_active).  For the
+ * slot f = sorted_slots[p] routed to expert e (offsets[e] <= p < offsets[e+1]) of token
+ * t = f / top_k:  h[p, n] = bf16_rne( silu(g_n) * u_n ) with g, u as in moe_mxfp4_forward.
+ *   h  bf16 [T*top_k, I] (written; rows in sorted-slot order).  Other arguments and limits
+ *   as for moe_mxfp4_forward.  Each routed expert's gate_up weights are read once.
+ */
+MX_API int moe_gate_up_swiglu(const uint16_t* x, const uint8_t* w_gate_up, const uint8_t* s_gate_up,
+                              const int32_t* counts, const int32_t* offsets, const int32_t* sorted_slots,
+                              const int32_t* active, const int32_t* num_active, uint16_t* h, int64_t T, int64_t H,
+                              int64_t I, int64_t E, int64_t top_k, void* stream);
+
+/*
+ * Stage hook: the down GEMM with the gate-weighted combine, from gate_up's h and the sort
+ * result:  y[t, n] = bf16_rne( sum_j gates[t, j] * sum_i h[p(t,j), i] * Wd[e][n, i] ), where
+ * p(t, j) is the sorted position of slot t*top_k + j.  Uses `workspace` (at least
+ * moe_mxfp4_workspace_size bytes, 256-byte aligned) as scratch.
+ */
+MX_API int moe_down_combine(const uint16_t* h, const float* gates, const uint8_t* w_down, const uint8_t* s_down,
+                            const int32_t* counts, const int32_t* offsets, const int32_t* sorted_slots,
+                            const int32_t* active, const int32_t* num_active, uint16_t* y, int64_t T, int64_t H,
+                            int64_t I, int64_t E, int64_t top_k, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
 /* Bytes of device workspace moe_mxfp4_forward needs for these sizes. */
 MX_API size_t moe_mxfp4_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k);
 

@@ -38,14 +38,19 @@ _lib.mx_linear.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P]
 _lib.mxfp4_dequantize.argtypes = [_P, _P, _I64, _I64, _P, _P]
 _lib.moe_route_topk.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P]
 _lib.moe_sort_by_expert.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P]
+_lib.moe_gate_up_swiglu.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P]
+_lib.moe_down_combine.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P,
+                                  ctypes.c_size_t, _P]
 _lib.moe_mxfp4_workspace_size.restype = ctypes.c_size_t
 _lib.moe_mxfp4_workspace_size.argtypes = [_I64, _I64, _I64, _I64, _I64]
 _lib.moe_mxfp4_forward.argtypes = [_P, _P, _I64, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]
-for _n in ("mx_linear", "mxfp4_dequantize", "moe_route_topk", "moe_sort_by_expert", "moe_mxfp4_forward"):
+for _n in ("mx_linear", "mxfp4_dequantize", "moe_route_topk", "moe_sort_by_expert", "moe_gate_up_swiglu",
+           "moe_down_combine", "moe_mxfp4_forward"):
     getattr(_lib, _n).restype = ctypes.c_int
 
 EXPORTED = ("mx_version", "mx_status_string", "mx_linear", "mxfp4_dequantize", "moe_route_topk",
-            "moe_sort_by_expert", "moe_mxfp4_workspace_size", "moe_mxfp4_forward")
+            "moe_sort_by_expert", "moe_gate_up_swiglu", "moe_down_combine", "moe_mxfp4_workspace_size",
+            "moe_mxfp4_forward")
 
 
 class MxError(RuntimeError):
@@ -133,35 +138,101 @@ def mxfp4_dequantize(w_codes: torch.Tensor, w_scales: torch.Tensor) -> torch.Ten
     return out
 
 
-def moe_route_topk(logits: torch.Tensor, top_k: int):
+def moe_route_topk(logits: torch.Tensor, top_k: int, ids: torch.Tensor | None = None,
+                   gates: torch.Tensor | None = None):
     """(ids int32 [T,k], gates fp32 [T,k]): top-k logits (ties to lower id), softmax over them."""
     _check(logits, "router_logits", torch.float32, 2)
     dev = logits.device
     T, E = logits.shape
-    ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
-    gates = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    if ids is None:
+        ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    if gates is None:
+        gates = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    _check(ids, "ids", torch.int32, 2, dev)
+    _check(gates, "gates", torch.float32, 2, dev)
+    if ids.shape != (T, top_k) or gates.shape != (T, top_k):
+        raise ValueError("ids / gates must be [T, top_k]")
     st = _lib.moe_route_topk(_ptr(logits), T, E, top_k, _ptr(ids), _ptr(gates), _stream(dev))
     _raise(st, "moe_route_topk")
     return ids, gates
 
 
-def moe_sort_by_expert(ids: torch.Tensor, num_experts: int) -> dict:
+_SORT_KEYS = ("counts", "offsets", "sorted_slots", "active", "num_active")
+
+
+def _sort_ptrs(sort: dict, dev):
+    for key in _SORT_KEYS:
+        _check(sort[key], key, torch.int32, 1, dev)
+    return [_ptr(sort[key]) for key in _SORT_KEYS]
+
+
+def moe_sort_by_expert(ids: torch.Tensor, num_experts: int, out: dict | None = None) -> dict:
     """Counting sort of the flat slots by expert (experts ascending, slot ascending)."""
     _check(ids, "ids", torch.int32, 2)
     dev = ids.device
     T, k = ids.shape
     E = int(num_experts)
-    out = dict(
-        counts=torch.empty(E, dtype=torch.int32, device=dev),
-        offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
-        sorted_slots=torch.empty(T * k, dtype=torch.int32, device=dev),
-        active=torch.empty(E, dtype=torch.int32, device=dev),
-        num_active=torch.empty(1, dtype=torch.int32, device=dev),
-    )
+    if out is not None:
+        _sort_ptrs(out, dev)
+        if (out["counts"].numel() != E or out["offsets"].numel() != E + 1 or out["sorted_slots"].numel() != T * k
+                or out["active"].numel() != E or out["num_active"].numel() != 1):
+            raise ValueError("sort output tensors have the wrong sizes")
+    else:
+        out = dict(
+            counts=torch.empty(E, dtype=torch.int32, device=dev),
+            offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+            sorted_slots=torch.empty(T * k, dtype=torch.int32, device=dev),
+            active=torch.empty(E, dtype=torch.int32, device=dev),
+            num_active=torch.empty(1, dtype=torch.int32, device=dev),
+        )
     st = _lib.moe_sort_by_expert(_ptr(ids), T, k, E, _ptr(out["counts"]), _ptr(out["offsets"]),
                                  _ptr(out["sorted_slots"]), _ptr(out["active"]), _ptr(out["num_active"]),
                                  _stream(dev))
     _raise(st, "moe_sort_by_expert")
+    return out
+
+
+def moe_gate_up_swiglu(x: torch.Tensor, W_gate_up: torch.Tensor, S_gate_up: torch.Tensor, sort: dict, top_k: int,
+                       h: torch.Tensor | None = None) -> torch.Tensor:
+    """Stage hook: h [T*k, I] bf16 (rows in sorted-slot order) from a moe_sort_by_expert result."""
+    _check(x, "x", torch.bfloat16, 2)
+    dev = x.device
+    _check(W_gate_up, "W_gate_up", torch.uint8, 3, dev)
+    _check(S_gate_up, "S_gate_up", torch.uint8, 3, dev)
+    T, H = x.shape
+    E, two_i, _ = W_gate_up.shape
+    I = two_i // 2
+    if W_gate_up.shape != (E, 2 * I, H // 2) or S_gate_up.shape != (E, 2 * I, H // 32):
+        raise ValueError("W_gate_up / S_gate_up shapes do not match [E, 2I, H/2] / [E, 2I, H/32]")
+    if h is None:
+        h = torch.empty((T * top_k, I), dtype=torch.bfloat16, device=dev)
+    _check(h, "h", torch.bfloat16, 2, dev)
+    st = _lib.moe_gate_up_swiglu(_ptr(x), _ptr(W_gate_up), _ptr(S_gate_up), *_sort_ptrs(sort, dev), _ptr(h), T, H, I,
+                                 E, top_k, _stream(dev))
+    _raise(st, "moe_gate_up_swiglu")
+    return h
+
+
+def moe_down_combine(h: torch.Tensor, gates: torch.Tensor, W_down: torch.Tensor, S_down: torch.Tensor, sort: dict,
+                     T: int, top_k: int, out: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """Stage hook: y [T, H] bf16 from gate_up's h, the gates and the sort result."""
+    _check(h, "h", torch.bfloat16, 2)
+    dev = h.device
+    _check(gates, "gates", torch.float32, 2, dev)
+    _check(W_down, "W_down", torch.uint8, 3, dev)
+    _check(S_down, "S_down", torch.uint8, 3, dev)
+    E, H, half_i = W_down.shape
+    I = half_i * 2
+    if S_down.shape != (E, H, I // 32) or h.shape != (T * top_k, I) or gates.shape != (T, top_k):
+        raise ValueError("shapes do not match h [T*k, I], gates [T, k], W_down [E, H, I/2], S_down [E, H, I/32]")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, 2, dev)
+    if ws is None:
+        ws = workspace(T, H, I, E, top_k, dev)
+    st = _lib.moe_down_combine(_ptr(h), _ptr(gates), _ptr(W_down), _ptr(S_down), *_sort_ptrs(sort, dev), _ptr(out),
+                               T, H, I, E, top_k, _ptr(ws), ws.numel(), _stream(dev))
+    _raise(st, "moe_down_combine")
     return out
 
 

@@ -6,190 +6,249 @@
 // combine was slower for the MX formats.  So: two GEMM kernels with fused epilogues, no
 // float atomics.
 //
-//   gate_up: work item = (active expert, 16 intermediate columns).  One wavefront streams
-//            the 16 gate rows and the matching 16 up rows of that expert over all H, for
-//            every token row routed to the expert, then applies SwiGLU and rounds h to
-//            bf16.  h rows are stored in sorted-slot order, contiguous per expert.
-//   down:    work item = (active expert, 32 output columns); multiplies the expert's h rows
-//            by W_down and stores gate-weighted fp32 partial outputs per flat slot.
-//   combine: y[t,:] = bf16(sum_j partial[t*k + j,:]) with j ascending.
+//   gate_up: item = (row group of an active expert, 16 intermediate columns).  A wavefront
+//            streams the 16 gate rows and the 16 matching up rows over all H, then applies
+//            SwiGLU and rounds h to bf16.  h rows are stored in sorted-slot order.
+//   down:    item = (row group of an active expert, 32 output columns); stores the fp32
+//            down outputs per flat slot.
+//   combine: y[t,:] = bf16(sum_j fl32(gate[t,j] * d[t*k + j,:])), j ascending.
 //
-// Both GEMM kernels are persistent: a grid sized to the device loops over the work list,
-// whose length (number of active experts) is read on the device, so no host readback.
-#include "mx_device.hpp"
+// A row group is up to 16 of the expert's routed rows (one MFMA m-tile); experts with more
+// rows have several groups.  Items are ordered group-major, then expert, then column tile,
+// and dealt round-robin to a persistent grid of wavefronts sized to the device, which
+// stream them back to back (mx_stream.hpp).  The number of active experts is read on the
+// device, so there is no host readback.
 #include "mx_internal.hpp"
+#include "mx_stream.hpp"
 
 namespace mx {
 
-struct ExpertList {
-  const int32_t* counts;
-  const int32_t* offsets;
-  const int32_t* sorted_slots;
-  const int32_t* active;
-  const int32_t* num_active;
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+// Item metadata (sort outputs) is read through the scalar data path: the kernels never
+// write it, and scalar loads do not queue behind the wave's in-flight vector loads, so
+// setting up the next item does not drain the weight stream.
+typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
+
+__device__ __forceinline__ int ld_uniform(const int32_t* p, int i) { return ((cint_ptr)p)[i]; }
+
+// Flat slot of row `j` (< 16) of a group of `rows` rows starting at sorted position `base`,
+// as a per-lane value for lane row j = lane & 15 (-1 past the group).
+__device__ __forceinline__ int group_slot(const int32_t* sorted_slots, int base, int rows, int lane) {
+  const int j = lane & 15;
+  int v = -1;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    if (r < rows) {
+      const int s = ld_uniform(sorted_slots, base + r);
+      v = (j == r) ? s : v;
+    }
+  }
+  return v;
+}
+
+struct ItemIndex {
+  int a, tile, g;
 };
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+// item = (g * na + a) * ntile + tile
+__device__ __forceinline__ ItemIndex item_decode(int it, int ntile, int na) {
+  ItemIndex r;
+  const int q = it / ntile;
+  r.tile = it - q * ntile;
+  r.g = q / na;
+  r.a = q - r.g * na;
+  return r;
+}
 
 // ------------------------------------------------------------------ gate_up + SwiGLU
 
-template <int W, int MT>
-__device__ __forceinline__ void gate_up_pass(const uint16_t* __restrict__ x, const uint8_t* __restrict__ wexp,
-                                             const uint8_t* __restrict__ sexp, const ExpertList& el,
-                                             uint16_t* __restrict__ h, int H, int I, int k, int p, int row0, int R,
-                                             int mp, uint8_t* slab, f32x4* red, int wave, int lane) {
-  constexpr int NS = 2;
-  constexpr int D = (MT == 1) ? 3 : 2;
-  StreamLanes<NS, MT> L;
-  lanes_init_lds(L, lane);
-  const size_t kb = (size_t)H >> 1, ks = (size_t)H >> 5;
-  const int n0 = p * SUB_ROWS;
-  for (int q = 0; q < 2; ++q) {
-    const int r = n0 + (lane >> 3) + 8 * q;
-    L.w[0][q] = wexp + (size_t)r * kb + (lane & 7) * 16;        // gate rows
-    L.w[1][q] = wexp + (size_t)(I + r) * kb + (lane & 7) * 16;  // up rows
+struct GateUpPolicy {
+  static constexpr int NS = 2;
+  struct EpiState {
+    int hrow;   // h row of this group's first row
+    int rows;   // valid rows in the group
+    int n0;     // first intermediate column
+  };
+  __amdgpu_buffer_rsrc_t xrsrc;  // x [T, H] bf16
+  const uint8_t* wgu;
+  const uint8_t* sgu;
+  SortView sv;
+  uint16_t* h;
+  int H, I, k, nseg, n_items, ntile, na;
+  size_t e_codes, e_scales;
+
+  __device__ __forceinline__ bool valid(int it) const {
+    const ItemIndex ix = item_decode(it, ntile, na);
+    return ix.g * 16 < ld_uniform(sv.counts, ld_uniform(sv.active, ix.a));
   }
-  L.s[0] = sexp + (size_t)(n0 + (lane & 15)) * ks;
-  L.s[1] = sexp + (size_t)(I + n0 + (lane & 15)) * ks;
-  for (int mt = 0; mt < MT; ++mt) {
-    const int rr = mp + mt * 16 + (lane & 15);
-    if (rr < R) {
-      const int t = el.sorted_slots[row0 + rr] / k;
-      L.x[mt] = x + (size_t)t * H + 32 * (lane >> 4);
-    } else {
-      L.x[mt] = nullptr;
+  __device__ __forceinline__ void w_setup(int it, WCursor<NS>& c, int lane) const {
+    const ItemIndex ix = item_decode(it, ntile, na);
+    const int e = ld_uniform(sv.active, ix.a);
+    const uint8_t* we = wgu + (size_t)e * e_codes;
+    const uint8_t* se = sgu + (size_t)e * e_scales;
+    const size_t kb = (size_t)H >> 1, ks = (size_t)H >> 5;
+    const int n0 = ix.tile * SUB_ROWS;
+    for (int q = 0; q < 2; ++q) {
+      const int r = n0 + (lane >> 3) + 8 * q;
+      c.w[0][q] = we + (size_t)r * kb + (lane & 7) * 16;        // gate rows
+      c.w[1][q] = we + (size_t)(I + r) * kb + (lane & 7) * 16;  // up rows
+    }
+    c.s[0] = se + (size_t)(n0 + (lane & 15)) * ks;
+    c.s[1] = se + (size_t)(I + n0 + (lane & 15)) * ks;
+  }
+  __device__ __forceinline__ void x_setup(int it, XCursor& c, int lane) const {
+    const ItemIndex ix = item_decode(it, ntile, na);
+    const int e = ld_uniform(sv.active, ix.a);
+    const int rows = min(16, ld_uniform(sv.counts, e) - ix.g * 16);
+    const int f = group_slot(sv.sorted_slots, ld_uniform(sv.offsets, e) + ix.g * 16, rows, lane);
+    c.xoff = (f >= 0) ? ((f / k) * H + 32 * (lane >> 4)) * 2 : X_NONE;
+  }
+  __device__ __forceinline__ void c_setup(int it, EpiState& s, int) const {
+    const ItemIndex ix = item_decode(it, ntile, na);
+    const int e = ld_uniform(sv.active, ix.a);
+    s.hrow = ld_uniform(sv.offsets, e) + ix.g * 16;
+    s.rows = min(16, ld_uniform(sv.counts, e) - ix.g * 16);
+    s.n0 = ix.tile * SUB_ROWS;
+  }
+  __device__ __forceinline__ void epilogue(const EpiState& s, const f32x4 (&acc)[NS], int lane) const {
+    const int r = lane & 15;
+    if (r >= s.rows) return;
+    uint32_t o[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint16_t a = f32_to_bf16_rne(silu_mul(acc[0][2 * j], acc[1][2 * j]));
+      const uint16_t b = f32_to_bf16_rne(silu_mul(acc[0][2 * j + 1], acc[1][2 * j + 1]));
+      o[j] = (uint32_t)a | ((uint32_t)b << 16);
+    }
+    *reinterpret_cast<u32x2*>(h + (size_t)(s.hrow + r) * I + s.n0 + 4 * (lane >> 4)) = u32x2{o[0], o[1]};
+  }
+};
+
+// ------------------------------------------------------------------ down
+
+struct DownPolicy {
+  static constexpr int NS = 2;
+  struct EpiState {
+    int slot;  // flat slot of this lane's row, -1 if the row is past the group
+    int n0;    // first output column
+  };
+  __amdgpu_buffer_rsrc_t xrsrc;  // h [T*k, I] bf16
+  const uint8_t* wd;
+  const uint8_t* sd;
+  SortView sv;
+  float* dpart;
+  int H, I, nseg, n_items, ntile, na;
+  size_t e_codes, e_scales;
+
+  __device__ __forceinline__ bool valid(int it) const {
+    const ItemIndex ix = item_decode(it, ntile, na);
+    return ix.g * 16 < ld_uniform(sv.counts, ld_uniform(sv.active, ix.a));
+  }
+  __device__ __forceinline__ void w_setup(int it, WCursor<NS>& c, int lane) const {
+    const ItemIndex ix = item_decode(it, ntile, na);
+    const int e = ld_uniform(sv.active, ix.a);
+    const uint8_t* we = wd + (size_t)e * e_codes;
+    const uint8_t* se = sd + (size_t)e * e_scales;
+    const size_t kb = (size_t)I >> 1, ks = (size_t)I >> 5;
+    const int n0 = ix.tile * 32;
+    for (int i = 0; i < NS; ++i) {
+      for (int q = 0; q < 2; ++q) c.w[i][q] = we + (size_t)(n0 + 16 * i + (lane >> 3) + 8 * q) * kb + (lane & 7) * 16;
+      c.s[i] = se + (size_t)(n0 + 16 * i + (lane & 15)) * ks;
     }
   }
-  const int nseg = H / SEG_K;
-  const int sg0 = nseg * wave / W, sg1 = nseg * (wave + 1) / W;
-  f32x4 acc[MT][NS];
-  acc_zero(acc);
-  stream_segments<NS, MT, D>(L, sg0, sg1, 0, slab, acc, lane);
-  wg_reduce<NS, MT, W>(acc, red, wave, lane);
-  if (wave == 0) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int rr = mp + mt * 16 + (lane & 15);
-      if (rr >= R) continue;
-      uint32_t o[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const uint16_t a = f32_to_bf16_rne(silu_mul(acc[mt][0][2 * j], acc[mt][1][2 * j]));
-        const uint16_t b = f32_to_bf16_rne(silu_mul(acc[mt][0][2 * j + 1], acc[mt][1][2 * j + 1]));
-        o[j] = (uint32_t)a | ((uint32_t)b << 16);
-      }
-      *reinterpret_cast<u32x2*>(h + (size_t)(row0 + rr) * I + n0 + 4 * (lane >> 4)) = u32x2{o[0], o[1]};
-    }
+  __device__ __forceinline__ void x_setup(int it, XCursor& c, int lane) const {
+    const ItemIndex ix = item_decode(it, ntile, na);
+    const int e = ld_uniform(sv.active, ix.a);
+    const int rr = ix.g * 16 + (lane & 15);
+    c.xoff = (rr < ld_uniform(sv.counts, e)) ? ((ld_uniform(sv.offsets, e) + rr) * I + 32 * (lane >> 4)) * 2 : X_NONE;
   }
+  __device__ __forceinline__ void c_setup(int it, EpiState& s, int lane) const {
+    const ItemIndex ix = item_decode(it, ntile, na);
+    const int e = ld_uniform(sv.active, ix.a);
+    const int rows = min(16, ld_uniform(sv.counts, e) - ix.g * 16);
+    s.slot = group_slot(sv.sorted_slots, ld_uniform(sv.offsets, e) + ix.g * 16, rows, lane);
+    s.n0 = ix.tile * 32;
+  }
+  __device__ __forceinline__ void epilogue(const EpiState& s, const f32x4 (&acc)[NS], int lane) const {
+    if (s.slot < 0) return;
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+      *reinterpret_cast<f32x4*>(dpart + (size_t)s.slot * H + s.n0 + 16 * i + 4 * (lane >> 4)) = acc[i];
+  }
+};
+
+// ------------------------------------------------------------------ kernels
+
+constexpr int EXPERT_WAVES = 4;  // independent wavefronts per workgroup
+constexpr int GU_DW = 4, GU_DX = 2;
+constexpr int DN_DW = 4, DN_DX = 2;
+
+__global__ void __launch_bounds__(EXPERT_WAVES * 64) moe_gate_up_kernel(const uint16_t* __restrict__ x,
+                                                                        const uint8_t* __restrict__ wgu,
+                                                                        const uint8_t* __restrict__ sgu, SortView sv,
+                                                                        uint16_t* __restrict__ h, int T, int H, int I,
+                                                                        int k, int gmax) {
+  __shared__ __attribute__((aligned(16))) uint8_t slabs[EXPERT_WAVES][2 * SLAB_BYTES];
+  // wave index as a scalar, so every per-item quantity derived from it stays uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  GateUpPolicy p;
+  p.xrsrc = make_rsrc(x, (uint32_t)T * H * 2);
+  p.wgu = wgu;
+  p.sgu = sgu;
+  p.sv = sv;
+  p.h = h;
+  p.H = H;
+  p.I = I;
+  p.k = k;
+  p.nseg = H / SEG_K;
+  p.ntile = I / SUB_ROWS;
+  p.na = ld_uniform(sv.num_active, 0);
+  p.n_items = gmax * p.na * p.ntile;
+  p.e_codes = (size_t)2 * I * (H / 2);
+  p.e_scales = (size_t)2 * I * (H / 32);
+  stream_items<GateUpPolicy, GU_DW, GU_DX>(p, blockIdx.x * EXPERT_WAVES + wave, gridDim.x * EXPERT_WAVES, slabs[wave],
+                                           lane);
 }
 
-template <int W>
-__global__ void __launch_bounds__(W * 64) moe_gate_up_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ wgu,
-                                                             const uint8_t* __restrict__ sgu, ExpertList el,
-                                                             uint16_t* __restrict__ h, int H, int I, int k) {
-  __shared__ __attribute__((aligned(16))) uint8_t slabs[W][2 * SLAB_BYTES];
-  __shared__ f32x4 red[(W > 1) ? W * 2 * 2 * 64 : 1];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int npair = I / SUB_ROWS;
-  const int items = *el.num_active * npair;
-  const size_t e_codes = (size_t)2 * I * (H / 2), e_scales = (size_t)2 * I * (H / 32);
-  for (int it = blockIdx.x; it < items; it += gridDim.x) {
-    const int a = it / npair, p = it - a * npair;
-    const int e = el.active[a];
-    const int row0 = el.offsets[e], R = el.counts[e];
-    const uint8_t* wexp = wgu + (size_t)e * e_codes;
-    const uint8_t* sexp = sgu + (size_t)e * e_scales;
-    for (int mp = 0; mp < R; mp += 32) {
-      if (R - mp > 16)
-        gate_up_pass<W, 2>(x, wexp, sexp, el, h, H, I, k, p, row0, R, mp, slabs[wave], red, wave, lane);
-      else
-        gate_up_pass<W, 1>(x, wexp, sexp, el, h, H, I, k, p, row0, R, mp, slabs[wave], red, wave, lane);
-    }
-  }
+__global__ void __launch_bounds__(EXPERT_WAVES * 64) moe_down_kernel(const uint16_t* __restrict__ h,
+                                                                     const uint8_t* __restrict__ wd,
+                                                                     const uint8_t* __restrict__ sd, SortView sv,
+                                                                     float* __restrict__ dpart, int F, int H, int I,
+                                                                     int gmax) {
+  __shared__ __attribute__((aligned(16))) uint8_t slabs[EXPERT_WAVES][2 * SLAB_BYTES];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  DownPolicy p;
+  p.xrsrc = make_rsrc(h, (uint32_t)F * I * 2);
+  p.wd = wd;
+  p.sd = sd;
+  p.sv = sv;
+  p.dpart = dpart;
+  p.H = H;
+  p.I = I;
+  p.nseg = I / SEG_K;
+  p.ntile = H / 32;
+  p.na = ld_uniform(sv.num_active, 0);
+  p.n_items = gmax * p.na * p.ntile;
+  p.e_codes = (size_t)H * (I / 2);
+  p.e_scales = (size_t)H * (I / 32);
+  stream_items<DownPolicy, DN_DW, DN_DX>(p, blockIdx.x * EXPERT_WAVES + wave, gridDim.x * EXPERT_WAVES, slabs[wave],
+                                         lane);
 }
 
-// ------------------------------------------------------------------ down + gate weighting
-
-template <int W, int MT>
-__device__ __forceinline__ void down_pass(const uint16_t* __restrict__ h, const uint8_t* __restrict__ wexp,
-                                          const uint8_t* __restrict__ sexp, const ExpertList& el,
-                                          const float* __restrict__ gates, float* __restrict__ dpart, int H, int I,
-                                          int q32, int row0, int R, int mp, uint8_t* slab, f32x4* red, int wave,
-                                          int lane) {
-  constexpr int NS = 2;
-  constexpr int D = (MT == 1) ? 3 : 2;
-  StreamLanes<NS, MT> L;
-  lanes_init_lds(L, lane);
-  const size_t kb = (size_t)I >> 1, ks = (size_t)I >> 5;
-  const int n0 = q32 * 32;
-  for (int i = 0; i < NS; ++i) {
-    for (int q = 0; q < 2; ++q) L.w[i][q] = wexp + (size_t)(n0 + 16 * i + (lane >> 3) + 8 * q) * kb + (lane & 7) * 16;
-    L.s[i] = sexp + (size_t)(n0 + 16 * i + (lane & 15)) * ks;
-  }
-  for (int mt = 0; mt < MT; ++mt) {
-    const int rr = mp + mt * 16 + (lane & 15);
-    L.x[mt] = (rr < R) ? h + (size_t)(row0 + rr) * I + 32 * (lane >> 4) : nullptr;
-  }
-  const int nseg = I / SEG_K;
-  const int sg0 = nseg * wave / W, sg1 = nseg * (wave + 1) / W;
-  f32x4 acc[MT][NS];
-  acc_zero(acc);
-  stream_segments<NS, MT, D>(L, sg0, sg1, 0, slab, acc, lane);
-  wg_reduce<NS, MT, W>(acc, red, wave, lane);
-  if (wave == 0) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int rr = mp + mt * 16 + (lane & 15);
-      if (rr >= R) continue;
-      const int f = el.sorted_slots[row0 + rr];
-      const float g = gates[f];
-#pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        f32x4 v = acc[mt][i];
-        v = f32x4{g * v[0], g * v[1], g * v[2], g * v[3]};
-        *reinterpret_cast<f32x4*>(dpart + (size_t)f * H + n0 + 16 * i + 4 * (lane >> 4)) = v;
-      }
-    }
-  }
-}
-
-template <int W>
-__global__ void __launch_bounds__(W * 64) moe_down_kernel(const uint16_t* __restrict__ h, const uint8_t* __restrict__ wd,
-                                                          const uint8_t* __restrict__ sd, ExpertList el,
-                                                          const float* __restrict__ gates, float* __restrict__ dpart,
-                                                          int H, int I) {
-  __shared__ __attribute__((aligned(16))) uint8_t slabs[W][2 * SLAB_BYTES];
-  __shared__ f32x4 red[(W > 1) ? W * 2 * 2 * 64 : 1];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int ntile = H / 32;
-  const int items = *el.num_active * ntile;
-  const size_t e_codes = (size_t)H * (I / 2), e_scales = (size_t)H * (I / 32);
-  for (int it = blockIdx.x; it < items; it += gridDim.x) {
-    const int a = it / ntile, q32 = it - a * ntile;
-    const int e = el.active[a];
-    const int row0 = el.offsets[e], R = el.counts[e];
-    const uint8_t* wexp = wd + (size_t)e * e_codes;
-    const uint8_t* sexp = sd + (size_t)e * e_scales;
-    for (int mp = 0; mp < R; mp += 32) {
-      if (R - mp > 16)
-        down_pass<W, 2>(h, wexp, sexp, el, gates, dpart, H, I, q32, row0, R, mp, slabs[wave], red, wave, lane);
-      else
-        down_pass<W, 1>(h, wexp, sexp, el, gates, dpart, H, I, q32, row0, R, mp, slabs[wave], red, wave, lane);
-    }
-  }
-}
-
-// ------------------------------------------------------------------ combine
-
-// One thread per (token, 4 consecutive outputs): fp32 sum over the k slots, j ascending.
-__global__ void __launch_bounds__(256) moe_combine_kernel(const float* __restrict__ dpart, uint16_t* __restrict__ y, int T,
-                                                          int H, int k) {
+// One thread per (token, 4 consecutive outputs): fp32 sum of the gate-weighted slots, j ascending.
+__global__ void __launch_bounds__(256) moe_combine_kernel(const float* __restrict__ dpart, const float* __restrict__ gates,
+                                                          uint16_t* __restrict__ y, int T, int H, int k) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t per_t = H / 4;
   if (i >= (int64_t)T * per_t) return;
   const int64_t t = i / per_t, n = (i - t * per_t) * 4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) acc += *reinterpret_cast<const f32x4*>(dpart + (size_t)(t * k + j) * H + n);
+  for (int j = 0; j < k; ++j) {
+    const float g = gates[t * k + j];
+    const f32x4 d = *reinterpret_cast<const f32x4*>(dpart + (size_t)(t * k + j) * H + n);
+    acc += f32x4{g * d[0], g * d[1], g * d[2], g * d[3]};
+  }
   const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
   const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
   *reinterpret_cast<u32x2*>(y + t * H + n) = u32x2{lo, hi};
@@ -197,38 +256,49 @@ __global__ void __launch_bounds__(256) moe_combine_kernel(const float* __restric
 
 // ------------------------------------------------------------------ launchers
 
-static ExpertList expert_list(const MoeWorkspace& ws) {
-  return ExpertList{ws.counts, ws.offsets, ws.sorted_slots, ws.active, ws.num_active};
+template <class K>
+static int resident_wgs_per_cu(K kernel, int block) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, block, 0) != hipSuccess || n < 1) n = 1;
+  return n;
 }
 
-// Persistent grid: enough workgroups to cover every possible item when few experts can be
-// active, otherwise a fixed number of workgroups per compute unit.
-static int persistent_grid(int64_t max_items, int wgs_per_cu) {
+// Waves of the persistent grid: every wave must be resident at once, and no more waves
+// than items.
+static int expert_grid(int64_t max_items, int wgs_per_cu) {
   const int64_t cap = (int64_t)device_cu_count() * wgs_per_cu;
-  return (int)(max_items < cap ? max_items : cap);
+  const int64_t need = (max_items + EXPERT_WAVES - 1) / EXPERT_WAVES;
+  return (int)(need < cap ? need : cap);
 }
 
-int launch_gate_up(const uint16_t* x, const uint8_t* wgu, const uint8_t* sgu, const MoeWorkspace& ws, int T, int H,
-                   int I, int E, int k, hipStream_t stream) {
-  const int64_t max_active = (int64_t)T * k < E ? (int64_t)T * k : E;
-  const int grid = persistent_grid(max_active * (I / SUB_ROWS), 8);
-  hipLaunchKernelGGL((moe_gate_up_kernel<1>), dim3(grid), dim3(64), 0, stream, x, wgu, sgu, expert_list(ws), ws.h, H, I,
-                     k);
+static int64_t max_active(int T, int E, int k) { return (int64_t)T * k < E ? (int64_t)T * k : E; }
+static int row_groups(int T) { return (T + 15) / 16; }
+
+int launch_gate_up(const uint16_t* x, const uint8_t* wgu, const uint8_t* sgu, const SortView& sv, uint16_t* h, int T,
+                   int H, int I, int E, int k, hipStream_t stream) {
+  static const int occ = resident_wgs_per_cu(moe_gate_up_kernel, EXPERT_WAVES * 64);
+  const int gmax = row_groups(T);
+  const int grid = expert_grid((int64_t)gmax * max_active(T, E, k) * (I / SUB_ROWS), occ);
+  hipLaunchKernelGGL(moe_gate_up_kernel, dim3(grid), dim3(EXPERT_WAVES * 64), 0, stream, x, wgu, sgu, sv, h, T, H, I,
+                     k, gmax);
   return hip_status(hipGetLastError());
 }
 
-int launch_down(const uint8_t* wd, const uint8_t* sd, const MoeWorkspace& ws, int T, int H, int I, int E, int k,
-                hipStream_t stream) {
-  const int64_t max_active = (int64_t)T * k < E ? (int64_t)T * k : E;
-  const int grid = persistent_grid(max_active * (H / 32), 8);
-  hipLaunchKernelGGL((moe_down_kernel<1>), dim3(grid), dim3(64), 0, stream, ws.h, wd, sd, expert_list(ws), ws.gates,
-                     ws.dpart, H, I);
+int launch_down(const uint16_t* h, const float* gates, const uint8_t* wd, const uint8_t* sd, const SortView& sv,
+                float* dpart, int T, int H, int I, int E, int k, hipStream_t stream) {
+  (void)gates;  // applied by the combine
+  static const int occ = resident_wgs_per_cu(moe_down_kernel, EXPERT_WAVES * 64);
+  const int gmax = row_groups(T);
+  const int grid = expert_grid((int64_t)gmax * max_active(T, E, k) * (H / 32), occ);
+  hipLaunchKernelGGL(moe_down_kernel, dim3(grid), dim3(EXPERT_WAVES * 64), 0, stream, h, wd, sd, sv, dpart, T * k,
+                     H, I, gmax);
   return hip_status(hipGetLastError());
 }
 
-int launch_combine(const MoeWorkspace& ws, uint16_t* y, int T, int H, int k, hipStream_t stream) {
+int launch_combine(const float* dpart, const float* gates, uint16_t* y, int T, int H, int k, hipStream_t stream) {
   const int64_t n = (int64_t)T * (H / 4);
-  hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, ws.dpart, y, T, H, k);
+  hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, dpart, gates, y, T,
+                     H, k);
   return hip_status(hipGetLastError());
 }
 

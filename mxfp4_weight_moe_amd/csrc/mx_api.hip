@@ -56,6 +56,22 @@ static int check_moe_sizes(int64_t T, int64_t E, int64_t k) {
   return MX_OK;
 }
 
+static int check_expert_dims(int64_t H, int64_t I) {
+  if (H < 256 || I < 256 || H % 256 != 0 || I % 256 != 0 || H > 65536 || I > 65536) return MX_ERR_SHAPE;
+  return MX_OK;
+}
+
+static bool sort_view_ok(const int32_t* counts, const int32_t* offsets, const int32_t* sorted_slots,
+                         const int32_t* active, const int32_t* num_active) {
+  return counts && offsets && sorted_slots && active && num_active;
+}
+
+static bool sort_view_aligned(const int32_t* counts, const int32_t* offsets, const int32_t* sorted_slots,
+                              const int32_t* active, const int32_t* num_active) {
+  return aligned(counts, 4) && aligned(offsets, 4) && aligned(sorted_slots, 4) && aligned(active, 4) &&
+         aligned(num_active, 4);
+}
+
 }  // namespace mx
 
 using namespace mx;
@@ -116,6 +132,43 @@ int moe_sort_by_expert(const int32_t* ids, int64_t T, int64_t top_k, int64_t E, 
                      static_cast<hipStream_t>(stream));
 }
 
+int moe_gate_up_swiglu(const uint16_t* x, const uint8_t* w_gate_up, const uint8_t* s_gate_up, const int32_t* counts,
+                       const int32_t* offsets, const int32_t* sorted_slots, const int32_t* active,
+                       const int32_t* num_active, uint16_t* h, int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k,
+                       void* stream) {
+  if (!x || !w_gate_up || !s_gate_up || !h || !sort_view_ok(counts, offsets, sorted_slots, active, num_active))
+    return MX_ERR_NULL;
+  int st = check_moe_sizes(T, E, top_k);
+  if (st != MX_OK || (st = check_expert_dims(H, I)) != MX_OK) return st;
+  if (!aligned(x, 16) || !aligned(w_gate_up, 16) || !aligned(s_gate_up, 8) || !aligned(h, 8) ||
+      !sort_view_aligned(counts, offsets, sorted_slots, active, num_active))
+    return MX_ERR_ALIGN;
+  const SortView sv{counts, offsets, sorted_slots, active, num_active};
+  return launch_gate_up(x, w_gate_up, s_gate_up, sv, h, (int)T, (int)H, (int)I, (int)E, (int)top_k,
+                        static_cast<hipStream_t>(stream));
+}
+
+int moe_down_combine(const uint16_t* h, const float* gates, const uint8_t* w_down, const uint8_t* s_down,
+                     const int32_t* counts, const int32_t* offsets, const int32_t* sorted_slots, const int32_t* active,
+                     const int32_t* num_active, uint16_t* y, int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!h || !gates || !w_down || !s_down || !y || !sort_view_ok(counts, offsets, sorted_slots, active, num_active))
+    return MX_ERR_NULL;
+  int st = check_moe_sizes(T, E, top_k);
+  if (st != MX_OK || (st = check_expert_dims(H, I)) != MX_OK) return st;
+  if (!aligned(h, 16) || !aligned(gates, 4) || !aligned(w_down, 16) || !aligned(s_down, 8) || !aligned(y, 8) ||
+      !sort_view_aligned(counts, offsets, sorted_slots, active, num_active))
+    return MX_ERR_ALIGN;
+  if (!workspace || !aligned(workspace, 256)) return MX_ERR_WORKSPACE;
+  const MoeWorkspace ws = moe_workspace_carve(workspace, T, H, I, E, top_k);
+  if (workspace_bytes < ws.bytes) return MX_ERR_WORKSPACE;
+  const SortView sv{counts, offsets, sorted_slots, active, num_active};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = launch_down(h, gates, w_down, s_down, sv, ws.dpart, (int)T, (int)H, (int)I, (int)E, (int)top_k, s)) != MX_OK)
+    return st;
+  return launch_combine(ws.dpart, gates, y, (int)T, (int)H, (int)top_k, s);
+}
+
 size_t moe_mxfp4_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k) {
   if (T < 1 || H < 1 || I < 1 || E < 1 || top_k < 1) return 0;
   return moe_workspace_carve(nullptr, T, H, I, E, top_k).bytes;
@@ -127,7 +180,7 @@ int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, int64_t top
   if (!x || !router_logits || !w_gate_up || !s_gate_up || !w_down || !s_down || !y) return MX_ERR_NULL;
   int st = check_moe_sizes(T, E, top_k);
   if (st != MX_OK) return st;
-  if (H < 256 || I < 256 || H % 256 != 0 || I % 256 != 0 || H > 65536 || I > 65536) return MX_ERR_SHAPE;
+  if ((st = check_expert_dims(H, I)) != MX_OK) return st;
   if (!aligned(x, 16) || !aligned(w_gate_up, 16) || !aligned(w_down, 16) || !aligned(s_gate_up, 8) ||
       !aligned(s_down, 8) || !aligned(y, 8) || !aligned(router_logits, 4))
     return MX_ERR_ALIGN;
@@ -139,9 +192,10 @@ int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, int64_t top
   if ((st = launch_route(router_logits, t, e, k, ws.ids, ws.gates, s)) != MX_OK) return st;
   if ((st = launch_sort(ws.ids, t, k, e, ws.counts, ws.offsets, ws.sorted_slots, ws.active, ws.num_active, s)) != MX_OK)
     return st;
-  if ((st = launch_gate_up(x, w_gate_up, s_gate_up, ws, t, h, i, e, k, s)) != MX_OK) return st;
-  if ((st = launch_down(w_down, s_down, ws, t, h, i, e, k, s)) != MX_OK) return st;
-  return launch_combine(ws, y, t, h, k, s);
+  const SortView sv{ws.counts, ws.offsets, ws.sorted_slots, ws.active, ws.num_active};
+  if ((st = launch_gate_up(x, w_gate_up, s_gate_up, sv, ws.h, t, h, i, e, k, s)) != MX_OK) return st;
+  if ((st = launch_down(ws.h, ws.gates, w_down, s_down, sv, ws.dpart, t, h, i, e, k, s)) != MX_OK) return st;
+  return launch_combine(ws.dpart, ws.gates, y, t, h, k, s);
 }
 
 }  // extern "C"

@@ -18,11 +18,20 @@ struct MoeWorkspace {
   int32_t* active;        // [E]
   int32_t* num_active;    // [1]
   uint16_t* h;            // [T*k, I] bf16, rows in sorted-slot order
-  float* dpart;           // [T*k, H] fp32 gate-weighted down outputs, rows by flat slot
+  float* dpart;           // [T*k, H] fp32 down outputs, rows by flat slot
   size_t bytes;
 };
 
 MoeWorkspace moe_workspace_carve(void* base, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k);
+
+// The outputs of the token->expert sort, as the expert GEMM kernels read them.
+struct SortView {
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* sorted_slots;
+  const int32_t* active;
+  const int32_t* num_active;
+};
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
 
@@ -37,10 +46,10 @@ int launch_dequant(const uint8_t* w, const uint8_t* s, int64_t rows, int64_t K, 
 int launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* gates, hipStream_t stream);
 int launch_sort(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* sorted_slots,
                 int32_t* active, int32_t* num_active, hipStream_t stream);
-int launch_gate_up(const uint16_t* x, const uint8_t* wgu, const uint8_t* sgu, const MoeWorkspace& ws, int T, int H,
-                   int I, int E, int k, hipStream_t stream);
-int launch_down(const uint8_t* wd, const uint8_t* sd, const MoeWorkspace& ws, int T, int H, int I, int E, int k,
-                hipStream_t stream);
-int launch_combine(const MoeWorkspace& ws, uint16_t* y, int T, int H, int k, hipStream_t stream);
+int launch_gate_up(const uint16_t* x, const uint8_t* wgu, const uint8_t* sgu, const SortView& sv, uint16_t* h, int T,
+                   int H, int I, int E, int k, hipStream_t stream);
+int launch_down(const uint16_t* h, const float* gates, const uint8_t* wd, const uint8_t* sd, const SortView& sv,
+                float* dpart, int T, int H, int I, int E, int k, hipStream_t stream);
+int launch_combine(const float* dpart, const float* gates, uint16_t* y, int T, int H, int k, hipStream_t stream);
 
 }  // namespace mx
