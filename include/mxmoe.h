@@ -24,7 +24,7 @@
  *     codes [R][K/2] uint8 (element 2i in the low nibble of byte i) plus
  *     scales [R][K/32] uint8 (one E8M0 byte per 32 consecutive K values of one row).
  *   - Code and activation base pointers must be 16-byte aligned; scale pointers 8-byte
- *     aligned.
+ *     aligned for mx_linear and 16-byte aligned for the MoE calls.
  *   - Return value: MX_OK (0) or a negative MX_ERR_* code.  All argument checks run on
  *     the host before anything is enqueued; a failed check enqueues nothing.  Device
  *     data (NaN, Inf) is not checked: NaN scales and NaN activations propagate.
@@ -157,7 +157,7 @@ MX_API size_t moe_mxfp4_workspace_size(int64_t T, int64_t H, int64_t I, int64_t 
  *                 bytes, 256-byte aligned; contents need no initialization and are
  *                 overwritten.  Calls that share a workspace must not overlap in time.
  *   1 <= T <= MX_MAX_TOKENS; 1 <= top_k <= min(E, MX_MAX_TOPK); E <= MX_MAX_EXPERTS;
- *   H % 256 == 0; I % 256 == 0 (so both GEMMs stream whole 256-value segments).
+ *   H % 1024 == 0; I % 1024 == 0 (both GEMMs stream 1024 K values per step).
  */
 MX_API int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, int64_t top_k, const uint8_t* w_gate_up,
                       const uint8_t* s_gate_up, const uint8_t* w_down, const uint8_t* s_down, uint16_t* y,

@@ -6,16 +6,17 @@
 // combine was slower for the MX formats.  So: two GEMM kernels with fused epilogues, no
 // float atomics.
 //
-//   gate_up: item = (row group of an active expert, 16 intermediate columns).  A wavefront
-//            streams the 16 gate rows and the 16 matching up rows over all H, then applies
-//            SwiGLU and rounds h to bf16.  h rows are stored in sorted-slot order.
-//   down:    item = (row group of an active expert, 32 output columns); stores the fp32
-//            down outputs per flat slot.
+//   gate_up: item = (row group of an active expert, 64 intermediate columns).  Each of the
+//            4 wavefronts of a workgroup streams 16 gate rows and the 16 matching up rows
+//            over all H, then applies SwiGLU and rounds h to bf16.  h rows are stored in
+//            sorted-slot order.
+//   down:    item = (row group of an active expert, 128 output columns, 32 per wave);
+//            stores the fp32 down outputs per flat slot.
 //   combine: y[t,:] = bf16(sum_j fl32(gate[t,j] * d[t*k + j,:])), j ascending.
 //
 // A row group is up to 16 of the expert's routed rows (one MFMA m-tile); experts with more
 // rows have several groups.  Items are ordered group-major, then expert, then column tile,
-// and dealt round-robin to a persistent grid of wavefronts sized to the device, which
+// and dealt round-robin to a persistent grid of workgroups sized to the device, which
 // stream them back to back (mx_stream.hpp).  The number of active experts is read on the
 // device, so there is no host readback.
 #include "mx_internal.hpp"
@@ -48,47 +49,65 @@ __device__ __forceinline__ int group_slot(const int32_t* sorted_slots, int base,
 }
 
 struct ItemIndex {
-  int a, tile, g;
+  int a, quad, g;
 };
 
-// item = (g * na + a) * ntile + tile
-__device__ __forceinline__ ItemIndex item_decode(int it, int ntile, int na) {
+// item = (g * na + a) * nquad + quad
+__device__ __forceinline__ ItemIndex item_decode(int it, int nquad, int na) {
   ItemIndex r;
-  const int q = it / ntile;
-  r.tile = it - q * ntile;
+  const int q = it / nquad;
+  r.quad = it - q * nquad;
   r.g = q / na;
   r.a = q - r.g * na;
   return r;
 }
 
-// ------------------------------------------------------------------ gate_up + SwiGLU
-
-struct GateUpPolicy {
-  static constexpr int NS = 2;
-  struct EpiState {
-    int hrow;   // h row of this group's first row
-    int rows;   // valid rows in the group
-    int n0;     // first intermediate column
-  };
-  __amdgpu_buffer_rsrc_t xrsrc;  // x [T, H] bf16
-  const uint8_t* wgu;
-  const uint8_t* sgu;
+// Fields shared by both expert GEMMs: the work list over (row group, expert, tile quad).
+struct ExpertItems {
   SortView sv;
-  uint16_t* h;
-  int H, I, k, nseg, n_items, ntile, na;
-  size_t e_codes, e_scales;
+  int nseg, n_items, nquad, na;
 
   __device__ __forceinline__ bool valid(int it) const {
-    const ItemIndex ix = item_decode(it, ntile, na);
+    const ItemIndex ix = item_decode(it, nquad, na);
     return ix.g * 16 < ld_uniform(sv.counts, ld_uniform(sv.active, ix.a));
   }
-  __device__ __forceinline__ void w_setup(int it, WCursor<NS>& c, int lane) const {
-    const ItemIndex ix = item_decode(it, ntile, na);
-    const int e = ld_uniform(sv.active, ix.a);
-    const uint8_t* we = wgu + (size_t)e * e_codes;
-    const uint8_t* se = sgu + (size_t)e * e_scales;
+  __device__ __forceinline__ ItemInfo info(int it) const {
+    const ItemIndex ix = item_decode(it, nquad, na);
+    ItemInfo f;
+    f.e = ld_uniform(sv.active, ix.a);
+    f.rows = min(16, ld_uniform(sv.counts, f.e) - ix.g * 16);
+    f.row0 = ld_uniform(sv.offsets, f.e) + ix.g * 16;
+    f.tile0 = ix.quad * WG_WAVES;
+    // a whole number of 4-segment steps, at least one, at most 64 row-segments (32 KB)
+    f.cs = min(nseg, max(4, (64 / f.rows) & ~3));
+    return f;
+  }
+};
+
+// ------------------------------------------------------------------ gate_up + SwiGLU
+
+struct GateUpPolicy : ExpertItems {
+  static constexpr int NS = 2;
+  struct EpiState {
+    int hrow;  // h row of the group's first row
+    int rows;  // valid rows in the group
+    int n0;    // first intermediate column of this wave's tile
+  };
+  const uint16_t* xact;  // x [T, H]
+  const uint8_t* wgu;
+  const uint8_t* sgu;
+  uint16_t* h;
+  int H, I, k;
+  size_t e_codes, e_scales;
+
+  __device__ __forceinline__ int x_row_offset(const ItemInfo& f, int m) const {
+    return (ld_uniform(sv.sorted_slots, f.row0 + m) / k) * H;
+  }
+  __device__ __forceinline__ void w_setup(const ItemInfo& f, int wave, WCursor<NS>& c, int lane) const {
+    const uint8_t* we = wgu + (size_t)f.e * e_codes;
+    const uint8_t* se = sgu + (size_t)f.e * e_scales;
     const size_t kb = (size_t)H >> 1, ks = (size_t)H >> 5;
-    const int n0 = ix.tile * SUB_ROWS;
+    const int n0 = (f.tile0 + wave) * SUB_ROWS;
     for (int q = 0; q < 2; ++q) {
       const int r = n0 + (lane >> 3) + 8 * q;
       c.w[0][q] = we + (size_t)r * kb + (lane & 7) * 16;        // gate rows
@@ -97,19 +116,10 @@ struct GateUpPolicy {
     c.s[0] = se + (size_t)(n0 + (lane & 15)) * ks;
     c.s[1] = se + (size_t)(I + n0 + (lane & 15)) * ks;
   }
-  __device__ __forceinline__ void x_setup(int it, XCursor& c, int lane) const {
-    const ItemIndex ix = item_decode(it, ntile, na);
-    const int e = ld_uniform(sv.active, ix.a);
-    const int rows = min(16, ld_uniform(sv.counts, e) - ix.g * 16);
-    const int f = group_slot(sv.sorted_slots, ld_uniform(sv.offsets, e) + ix.g * 16, rows, lane);
-    c.xoff = (f >= 0) ? ((f / k) * H + 32 * (lane >> 4)) * 2 : X_NONE;
-  }
-  __device__ __forceinline__ void c_setup(int it, EpiState& s, int) const {
-    const ItemIndex ix = item_decode(it, ntile, na);
-    const int e = ld_uniform(sv.active, ix.a);
-    s.hrow = ld_uniform(sv.offsets, e) + ix.g * 16;
-    s.rows = min(16, ld_uniform(sv.counts, e) - ix.g * 16);
-    s.n0 = ix.tile * SUB_ROWS;
+  __device__ __forceinline__ void c_setup(const ItemInfo& f, int wave, EpiState& s, int) const {
+    s.hrow = f.row0;
+    s.rows = f.rows;
+    s.n0 = (f.tile0 + wave) * SUB_ROWS;
   }
   __device__ __forceinline__ void epilogue(const EpiState& s, const f32x4 (&acc)[NS], int lane) const {
     const int r = lane & 15;
@@ -127,48 +137,33 @@ struct GateUpPolicy {
 
 // ------------------------------------------------------------------ down
 
-struct DownPolicy {
+struct DownPolicy : ExpertItems {
   static constexpr int NS = 2;
   struct EpiState {
     int slot;  // flat slot of this lane's row, -1 if the row is past the group
-    int n0;    // first output column
+    int n0;    // first output column of this wave's tile
   };
-  __amdgpu_buffer_rsrc_t xrsrc;  // h [T*k, I] bf16
+  const uint16_t* xact;  // h [T*k, I], rows in sorted order
   const uint8_t* wd;
   const uint8_t* sd;
-  SortView sv;
   float* dpart;
-  int H, I, nseg, n_items, ntile, na;
+  int H, I;
   size_t e_codes, e_scales;
 
-  __device__ __forceinline__ bool valid(int it) const {
-    const ItemIndex ix = item_decode(it, ntile, na);
-    return ix.g * 16 < ld_uniform(sv.counts, ld_uniform(sv.active, ix.a));
-  }
-  __device__ __forceinline__ void w_setup(int it, WCursor<NS>& c, int lane) const {
-    const ItemIndex ix = item_decode(it, ntile, na);
-    const int e = ld_uniform(sv.active, ix.a);
-    const uint8_t* we = wd + (size_t)e * e_codes;
-    const uint8_t* se = sd + (size_t)e * e_scales;
+  __device__ __forceinline__ int x_row_offset(const ItemInfo& f, int m) const { return (f.row0 + m) * I; }
+  __device__ __forceinline__ void w_setup(const ItemInfo& f, int wave, WCursor<NS>& c, int lane) const {
+    const uint8_t* we = wd + (size_t)f.e * e_codes;
+    const uint8_t* se = sd + (size_t)f.e * e_scales;
     const size_t kb = (size_t)I >> 1, ks = (size_t)I >> 5;
-    const int n0 = ix.tile * 32;
+    const int n0 = (f.tile0 + wave) * 32;
     for (int i = 0; i < NS; ++i) {
       for (int q = 0; q < 2; ++q) c.w[i][q] = we + (size_t)(n0 + 16 * i + (lane >> 3) + 8 * q) * kb + (lane & 7) * 16;
       c.s[i] = se + (size_t)(n0 + 16 * i + (lane & 15)) * ks;
     }
   }
-  __device__ __forceinline__ void x_setup(int it, XCursor& c, int lane) const {
-    const ItemIndex ix = item_decode(it, ntile, na);
-    const int e = ld_uniform(sv.active, ix.a);
-    const int rr = ix.g * 16 + (lane & 15);
-    c.xoff = (rr < ld_uniform(sv.counts, e)) ? ((ld_uniform(sv.offsets, e) + rr) * I + 32 * (lane >> 4)) * 2 : X_NONE;
-  }
-  __device__ __forceinline__ void c_setup(int it, EpiState& s, int lane) const {
-    const ItemIndex ix = item_decode(it, ntile, na);
-    const int e = ld_uniform(sv.active, ix.a);
-    const int rows = min(16, ld_uniform(sv.counts, e) - ix.g * 16);
-    s.slot = group_slot(sv.sorted_slots, ld_uniform(sv.offsets, e) + ix.g * 16, rows, lane);
-    s.n0 = ix.tile * 32;
+  __device__ __forceinline__ void c_setup(const ItemInfo& f, int wave, EpiState& s, int lane) const {
+    s.slot = group_slot(sv.sorted_slots, f.row0, f.rows, lane);
+    s.n0 = (f.tile0 + wave) * 32;
   }
   __device__ __forceinline__ void epilogue(const EpiState& s, const f32x4 (&acc)[NS], int lane) const {
     if (s.slot < 0) return;
@@ -180,60 +175,64 @@ struct DownPolicy {
 
 // ------------------------------------------------------------------ kernels
 
-constexpr int EXPERT_WAVES = 4;  // independent wavefronts per workgroup
-constexpr int GU_DW = 4, GU_DX = 2;
-constexpr int DN_DW = 4, DN_DX = 2;
+constexpr int GU_SPS = 4, GU_DW = 1;  // gate_up: 28 segments per item at H = 7168
+constexpr int DN_SPS = 4, DN_DW = 1;  // down: 8 segments per item at I = 2048
 
-__global__ void __launch_bounds__(EXPERT_WAVES * 64) moe_gate_up_kernel(const uint16_t* __restrict__ x,
-                                                                        const uint8_t* __restrict__ wgu,
-                                                                        const uint8_t* __restrict__ sgu, SortView sv,
-                                                                        uint16_t* __restrict__ h, int T, int H, int I,
-                                                                        int k, int gmax) {
-  __shared__ __attribute__((aligned(16))) uint8_t slabs[EXPERT_WAVES][2 * SLAB_BYTES];
+__global__ void __launch_bounds__(WG_WAVES * 64) moe_gate_up_kernel(const uint16_t* __restrict__ x,
+                                                                    const uint8_t* __restrict__ wgu,
+                                                                    const uint8_t* __restrict__ sgu, SortView sv,
+                                                                    uint16_t* __restrict__ h, int H, int I, int k,
+                                                                    int gmax) {
+  __shared__ __attribute__((aligned(16))) uint8_t xbufs[2 * XCHUNK_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t slabs[WG_WAVES][SLAB_BYTES];
+  __shared__ uint32_t xctr[2];
+  if (threadIdx.x < 2) xctr[threadIdx.x] = 0u;
+  __syncthreads();
   // wave index as a scalar, so every per-item quantity derived from it stays uniform
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   GateUpPolicy p;
-  p.xrsrc = make_rsrc(x, (uint32_t)T * H * 2);
+  p.sv = sv;
+  p.nseg = H / SEG_K;
+  p.nquad = I / (SUB_ROWS * WG_WAVES);
+  p.na = ld_uniform(sv.num_active, 0);
+  p.n_items = gmax * p.na * p.nquad;
+  p.xact = x;
   p.wgu = wgu;
   p.sgu = sgu;
-  p.sv = sv;
   p.h = h;
   p.H = H;
   p.I = I;
   p.k = k;
-  p.nseg = H / SEG_K;
-  p.ntile = I / SUB_ROWS;
-  p.na = ld_uniform(sv.num_active, 0);
-  p.n_items = gmax * p.na * p.ntile;
   p.e_codes = (size_t)2 * I * (H / 2);
   p.e_scales = (size_t)2 * I * (H / 32);
-  stream_items<GateUpPolicy, GU_DW, GU_DX>(p, blockIdx.x * EXPERT_WAVES + wave, gridDim.x * EXPERT_WAVES, slabs[wave],
-                                           lane);
+  stream_items<GateUpPolicy, GU_SPS, GU_DW>(p, xbufs, xctr, slabs[wave], wave, lane);
 }
 
-__global__ void __launch_bounds__(EXPERT_WAVES * 64) moe_down_kernel(const uint16_t* __restrict__ h,
-                                                                     const uint8_t* __restrict__ wd,
-                                                                     const uint8_t* __restrict__ sd, SortView sv,
-                                                                     float* __restrict__ dpart, int F, int H, int I,
-                                                                     int gmax) {
-  __shared__ __attribute__((aligned(16))) uint8_t slabs[EXPERT_WAVES][2 * SLAB_BYTES];
+__global__ void __launch_bounds__(WG_WAVES * 64) moe_down_kernel(const uint16_t* __restrict__ h,
+                                                                 const uint8_t* __restrict__ wd,
+                                                                 const uint8_t* __restrict__ sd, SortView sv,
+                                                                 float* __restrict__ dpart, int H, int I, int gmax) {
+  __shared__ __attribute__((aligned(16))) uint8_t xbufs[2 * XCHUNK_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t slabs[WG_WAVES][SLAB_BYTES];
+  __shared__ uint32_t xctr[2];
+  if (threadIdx.x < 2) xctr[threadIdx.x] = 0u;
+  __syncthreads();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   DownPolicy p;
-  p.xrsrc = make_rsrc(h, (uint32_t)F * I * 2);
+  p.sv = sv;
+  p.nseg = I / SEG_K;
+  p.nquad = H / (32 * WG_WAVES);
+  p.na = ld_uniform(sv.num_active, 0);
+  p.n_items = gmax * p.na * p.nquad;
+  p.xact = h;
   p.wd = wd;
   p.sd = sd;
-  p.sv = sv;
   p.dpart = dpart;
   p.H = H;
   p.I = I;
-  p.nseg = I / SEG_K;
-  p.ntile = H / 32;
-  p.na = ld_uniform(sv.num_active, 0);
-  p.n_items = gmax * p.na * p.ntile;
   p.e_codes = (size_t)H * (I / 2);
   p.e_scales = (size_t)H * (I / 32);
-  stream_items<DownPolicy, DN_DW, DN_DX>(p, blockIdx.x * EXPERT_WAVES + wave, gridDim.x * EXPERT_WAVES, slabs[wave],
-                                         lane);
+  stream_items<DownPolicy, DN_SPS, DN_DW>(p, xbufs, xctr, slabs[wave], wave, lane);
 }
 
 // One thread per (token, 4 consecutive outputs): fp32 sum of the gate-weighted slots, j ascending.
@@ -263,12 +262,10 @@ static int resident_wgs_per_cu(K kernel, int block) {
   return n;
 }
 
-// Waves of the persistent grid: every wave must be resident at once, and no more waves
-// than items.
+// Persistent grid: all workgroups resident at once, and no more than there are items.
 static int expert_grid(int64_t max_items, int wgs_per_cu) {
   const int64_t cap = (int64_t)device_cu_count() * wgs_per_cu;
-  const int64_t need = (max_items + EXPERT_WAVES - 1) / EXPERT_WAVES;
-  return (int)(need < cap ? need : cap);
+  return (int)(max_items < cap ? max_items : cap);
 }
 
 static int64_t max_active(int T, int E, int k) { return (int64_t)T * k < E ? (int64_t)T * k : E; }
@@ -276,22 +273,21 @@ static int row_groups(int T) { return (T + 15) / 16; }
 
 int launch_gate_up(const uint16_t* x, const uint8_t* wgu, const uint8_t* sgu, const SortView& sv, uint16_t* h, int T,
                    int H, int I, int E, int k, hipStream_t stream) {
-  static const int occ = resident_wgs_per_cu(moe_gate_up_kernel, EXPERT_WAVES * 64);
+  static const int occ = resident_wgs_per_cu(moe_gate_up_kernel, WG_WAVES * 64);
   const int gmax = row_groups(T);
-  const int grid = expert_grid((int64_t)gmax * max_active(T, E, k) * (I / SUB_ROWS), occ);
-  hipLaunchKernelGGL(moe_gate_up_kernel, dim3(grid), dim3(EXPERT_WAVES * 64), 0, stream, x, wgu, sgu, sv, h, T, H, I,
-                     k, gmax);
+  const int grid = expert_grid((int64_t)gmax * max_active(T, E, k) * (I / (SUB_ROWS * WG_WAVES)), occ);
+  hipLaunchKernelGGL(moe_gate_up_kernel, dim3(grid), dim3(WG_WAVES * 64), 0, stream, x, wgu, sgu, sv, h, H, I, k,
+                     gmax);
   return hip_status(hipGetLastError());
 }
 
 int launch_down(const uint16_t* h, const float* gates, const uint8_t* wd, const uint8_t* sd, const SortView& sv,
                 float* dpart, int T, int H, int I, int E, int k, hipStream_t stream) {
   (void)gates;  // applied by the combine
-  static const int occ = resident_wgs_per_cu(moe_down_kernel, EXPERT_WAVES * 64);
+  static const int occ = resident_wgs_per_cu(moe_down_kernel, WG_WAVES * 64);
   const int gmax = row_groups(T);
-  const int grid = expert_grid((int64_t)gmax * max_active(T, E, k) * (H / 32), occ);
-  hipLaunchKernelGGL(moe_down_kernel, dim3(grid), dim3(EXPERT_WAVES * 64), 0, stream, h, wd, sd, sv, dpart, T * k,
-                     H, I, gmax);
+  const int grid = expert_grid((int64_t)gmax * max_active(T, E, k) * (H / (32 * WG_WAVES)), occ);
+  hipLaunchKernelGGL(moe_down_kernel, dim3(grid), dim3(WG_WAVES * 64), 0, stream, h, wd, sd, sv, dpart, H, I, gmax);
   return hip_status(hipGetLastError());
 }
 

@@ -56,8 +56,10 @@ static int check_moe_sizes(int64_t T, int64_t E, int64_t k) {
   return MX_OK;
 }
 
+// The expert kernels stream 1024 K values (four segments) per step and load the scales of
+// two segments as one 16-byte piece per row, so H and I must be multiples of 1024.
 static int check_expert_dims(int64_t H, int64_t I) {
-  if (H < 256 || I < 256 || H % 256 != 0 || I % 256 != 0 || H > 65536 || I > 65536) return MX_ERR_SHAPE;
+  if (H < 1024 || I < 1024 || H % 1024 != 0 || I % 1024 != 0 || H > 65536 || I > 65536) return MX_ERR_SHAPE;
   return MX_OK;
 }
 
@@ -140,7 +142,7 @@ int moe_gate_up_swiglu(const uint16_t* x, const uint8_t* w_gate_up, const uint8_
     return MX_ERR_NULL;
   int st = check_moe_sizes(T, E, top_k);
   if (st != MX_OK || (st = check_expert_dims(H, I)) != MX_OK) return st;
-  if (!aligned(x, 16) || !aligned(w_gate_up, 16) || !aligned(s_gate_up, 8) || !aligned(h, 8) ||
+  if (!aligned(x, 16) || !aligned(w_gate_up, 16) || !aligned(s_gate_up, 16) || !aligned(h, 8) ||
       !sort_view_aligned(counts, offsets, sorted_slots, active, num_active))
     return MX_ERR_ALIGN;
   const SortView sv{counts, offsets, sorted_slots, active, num_active};
@@ -156,7 +158,7 @@ int moe_down_combine(const uint16_t* h, const float* gates, const uint8_t* w_dow
     return MX_ERR_NULL;
   int st = check_moe_sizes(T, E, top_k);
   if (st != MX_OK || (st = check_expert_dims(H, I)) != MX_OK) return st;
-  if (!aligned(h, 16) || !aligned(gates, 4) || !aligned(w_down, 16) || !aligned(s_down, 8) || !aligned(y, 8) ||
+  if (!aligned(h, 16) || !aligned(gates, 4) || !aligned(w_down, 16) || !aligned(s_down, 16) || !aligned(y, 8) ||
       !sort_view_aligned(counts, offsets, sorted_slots, active, num_active))
     return MX_ERR_ALIGN;
   if (!workspace || !aligned(workspace, 256)) return MX_ERR_WORKSPACE;
@@ -181,8 +183,8 @@ int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, int64_t top
   int st = check_moe_sizes(T, E, top_k);
   if (st != MX_OK) return st;
   if ((st = check_expert_dims(H, I)) != MX_OK) return st;
-  if (!aligned(x, 16) || !aligned(w_gate_up, 16) || !aligned(w_down, 16) || !aligned(s_gate_up, 8) ||
-      !aligned(s_down, 8) || !aligned(y, 8) || !aligned(router_logits, 4))
+  if (!aligned(x, 16) || !aligned(w_gate_up, 16) || !aligned(w_down, 16) || !aligned(s_gate_up, 16) ||
+      !aligned(s_down, 16) || !aligned(y, 8) || !aligned(router_logits, 4))
     return MX_ERR_ALIGN;
   if (!workspace || !aligned(workspace, 256)) return MX_ERR_WORKSPACE;
   const MoeWorkspace ws = moe_workspace_carve(workspace, T, H, I, E, top_k);

@@ -87,10 +87,10 @@ def test_route_and_sort_reject():
 
 def test_forward_rejects():
     L = m.raw()
-    ws = m.workspace_size(4, 512, 256, 8, 2)
+    ws = m.workspace_size(4, 1024, 1024, 8, 2)
     assert ws > 0 and ws % 256 == 0
 
-    def fwd(x=A, lg=A, k=2, wgu=A, sgu=A, wd=A, sd=A, y=A, T=4, H=512, I=256, E=8, w=A, wb=ws):
+    def fwd(x=A, lg=A, k=2, wgu=A, sgu=A, wd=A, sd=A, y=A, T=4, H=1024, I=1024, E=8, w=A, wb=ws):
         return L.moe_mxfp4_forward(x, lg, k, wgu, sgu, wd, sd, y, T, H, I, E, w, wb, None)
 
     assert fwd(x=None) == MX_ERR_NULL
@@ -99,9 +99,12 @@ def test_forward_rejects():
     assert fwd(T=257) == MX_ERR_SHAPE
     assert fwd(k=9) == MX_ERR_SHAPE
     assert fwd(H=320) == MX_ERR_SHAPE
+    assert fwd(H=1536) == MX_ERR_SHAPE  # not a multiple of 1024
     assert fwd(I=96) == MX_ERR_SHAPE
+    assert fwd(I=512) == MX_ERR_SHAPE
     assert fwd(wgu=MIS) == MX_ERR_ALIGN
     assert fwd(sgu=P((1 << 20) + 4)) == MX_ERR_ALIGN
+    assert fwd(sd=P((1 << 20) + 8)) == MX_ERR_ALIGN
     assert fwd(w=None) == MX_ERR_WORKSPACE
     assert fwd(w=P((1 << 20) + 128)) == MX_ERR_WORKSPACE
     assert fwd(wb=ws - 1) == MX_ERR_WORKSPACE

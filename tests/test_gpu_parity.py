@@ -185,13 +185,15 @@ def oracle_moe(cfg, x, logits, w_host, tokens=None):
 
 
 TINY = [
-    dict(T=1, H=256, I=256, E=4, k=1),
-    dict(T=3, H=256, I=256, E=4, k=2),
-    dict(T=5, H=512, I=256, E=8, k=3),
-    dict(T=17, H=256, I=512, E=4, k=2),    # 17 rows on some experts: two m-tiles
-    dict(T=40, H=256, I=256, E=4, k=4),    # every expert has 40 rows: passes of 32
-    dict(T=64, H=768, I=256, E=16, k=8),
-    dict(T=2, H=256, I=256, E=300, k=8),   # most experts inactive
+    dict(T=1, H=1024, I=1024, E=4, k=1),
+    dict(T=3, H=1024, I=1024, E=4, k=2),
+    dict(T=5, H=2048, I=1024, E=8, k=3),
+    dict(T=17, H=1024, I=2048, E=4, k=2),   # 17 rows on some experts: two row groups
+    dict(T=40, H=1024, I=1024, E=4, k=4),   # every expert has 40 rows: three row groups
+    dict(T=64, H=3072, I=1024, E=16, k=8),
+    dict(T=2, H=1024, I=1024, E=300, k=8),  # most experts inactive
+    dict(T=33, H=1024, I=3072, E=2, k=1),   # 33 rows on one expert
+    dict(T=9, H=1024, I=1024, E=1, k=1),    # one expert, 9 rows: chunk of 4 segments
 ]
 
 
@@ -235,7 +237,7 @@ def test_moe_small_scale_variant(dev, mx):
 
 
 def test_moe_deterministic_and_inactive_experts_unread(dev, mx):
-    cfg = synthetic.MoEConfig("det", T=8, H=512, I=256, E=32, k=4, routing="normal", e_lo=-8, e_hi=-2, seed=3)
+    cfg = synthetic.MoEConfig("det", T=8, H=1024, I=1024, E=32, k=4, routing="normal", e_lo=-8, e_hi=-2, seed=3)
     host = synthetic.moe_inputs_host(cfg)
     say("moe determinism / inactive NaN scales")
     d, x, logits = moe_device_inputs(cfg, dev, host)
