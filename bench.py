@@ -12,12 +12,17 @@ graph holding the L layer forwards (moe_mxfp4_forward) K/L times, between two de
 synchronizations; K is rounded up to a multiple of L.
 
 Printed: one JSON line with the layer time (us), effective weight GB/s, a roofline entry
-for the dominant kernel (gate_up, timed with HIP events on its launch stream during a
-stage-by-stage pass) and the CPU oracle's time on a bounded sample of the same workload.
+for the dominant kernel (gate_up) and the CPU oracle's time on a bounded sample of the same
+workload.  The kernel's launch time comes from a second pass over the same K steps right
+after the timed region, issued as the four stage calls with a HIP event between them on
+the stream the kernels run on.  roofline.traffic is the kernel's HBM bytes per launch as
+measured by the committed counter summary under profiles/, and null when the workload
+differs or the kernel's sources changed since the counters were taken.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import platform
@@ -28,13 +33,20 @@ import numpy as np
 
 METRIC = "µs per MXFP4 MoE layer and effective weight GB/s (% of 8 TB/s) at T=1..128"
 HBM_PEAK_GBPS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+# sources (and build flags) the gate_up kernel is compiled from; the counter summary records
+# their hash, so measured traffic is only reported for the kernel it was measured on
+GATE_UP_SOURCES = ("mxfp4_weight_moe_amd/build.py", "mxfp4_weight_moe_amd/csrc/mx_device.hpp",
+                   "mxfp4_weight_moe_amd/csrc/mx_internal.hpp", "mxfp4_weight_moe_amd/csrc/mx_stream.hpp",
+                   "mxfp4_weight_moe_amd/csrc/moe_experts.hip")
+GATE_UP_COUNTERS = os.path.join(ROOT, "profiles", "moe_gate_up_kernel.moe_t32_zipf.hbm_counters.txt")
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="moe_t32_zipf",
                     help="moe_t4 | moe_t32_zipf | moe_t128 | moe_sweep_t<T>")
     ap.add_argument("--layers", type=int, default=4, help="distinct layers cycled by the steps")
@@ -67,6 +79,31 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
+def gate_up_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in GATE_UP_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per gate_up launch from the committed counter summary ("key: value" lines),
+    or None when the summary is absent, for another workload, or for other kernel sources."""
+    try:
+        with open(GATE_UP_COUNTERS) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith((" ", "#")))
+    except OSError:
+        return None
+    kv = {a.strip(): b.strip() for a, b in kv.items()}
+    if kv.get("workload") != workload or kv.get("kernel_sources_sha256") != gate_up_source_hash():
+        return None
+    try:
+        return int(kv["hbm_read_bytes_per_launch"]) + int(kv["hbm_write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -89,6 +126,7 @@ def main():
     def log(*a):
         print(*a, file=sys.stderr, flush=True)
 
+    # ---------------------------------------------------------------- set-up (all before timing)
     log(f"[bench] workload {cfg.name}: T={T} H={H} I={I} E={E} k={k} routing={cfg.routing} layers={L}")
     layers = []
     for li in range(L):
@@ -102,15 +140,42 @@ def main():
             x_bits=x_bits, logits_host=logits,
         ))
     ws = mx.workspace(T, H, I, E, k, dev)
-    torch.cuda.synchronize()
-    log(f"[bench] inputs resident: {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
+    # buffers of the stage-by-stage pass
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+    srt = dict(counts=torch.empty(E, dtype=torch.int32, device=dev),
+               offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+               sorted_slots=torch.empty(T * k, dtype=torch.int32, device=dev),
+               active=torch.empty(E, dtype=torch.int32, device=dev),
+               num_active=torch.empty(1, dtype=torch.int32, device=dev))
+    h = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
+    names = ("route", "sort", "gate_up", "down_combine")
+    n_active = []
+    for lay in layers:
+        mx.moe_route_topk(lay["logits"], k, ids=ids, gates=gates)
+        mx.moe_sort_by_expert(ids, E, out=srt)
+        n_active.append(int(srt["num_active"].item()))
+    log(f"[bench] inputs resident: {torch.cuda.memory_allocated() / 2**30:.1f} GiB; active experts {n_active}")
 
     def forward(lay):
         w = lay["w"]
         mx.moe_mxfp4_forward(lay["x"], lay["logits"], k, w["wgu"], w["sgu"], w["wd"], w["sd"], out=lay["y"], ws=ws)
 
-    for i in range(max(1, args.warmup)):
-        forward(layers[i % L])
+    def staged(i, e, stream):
+        lay = layers[i % L]
+        w = lay["w"]
+        e[0].record(stream)
+        mx.moe_route_topk(lay["logits"], k, ids=ids, gates=gates)
+        e[1].record(stream)
+        mx.moe_sort_by_expert(ids, E, out=srt)
+        e[2].record(stream)
+        mx.moe_gate_up_swiglu(lay["x"], w["wgu"], w["sgu"], srt, k, h=h)
+        e[3].record(stream)
+        mx.moe_down_combine(h, gates, w["wd"], w["sd"], srt, T, k, out=lay["y"], ws=ws)
+        e[4].record(stream)
+
+    for lay in layers:
+        forward(lay)
     torch.cuda.synchronize()
 
     # Untimed reference copy of a known size: under a counter profiler its FETCH_SIZE and
@@ -133,61 +198,46 @@ def main():
                 for lay in layers:
                     forward(lay)
         torch.cuda.current_stream(dev).wait_stream(side)
-        for _ in range(max(1, args.warmup // L)):
-            graph.replay()
         torch.cuda.synchronize()
 
-    # ---------------------------------------------------------------- timed region
+    def run_steps(n):  # n is a multiple of L
+        for _ in range(n // L):
+            if graph is not None:
+                graph.replay()
+            else:
+                for lay in layers:
+                    forward(lay)
+
+    # ---------------------------------------------------------------- warm-up and timed region
+    # Warm-up long enough for the clocks to settle: kernel times drift down over the
+    # first tens of milliseconds of back-to-back work after an idle GPU.
+    run_steps(L * max(1, -(-args.warmup // L)))
     reps = max(1, -(-args.steps // L))
     K = reps * L
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(reps):
-        if graph is not None:
-            graph.replay()
-        else:
-            for lay in layers:
-                forward(lay)
+    run_steps(K)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
     log(f"[bench] timed {K} steps: {ms_per_step * 1e3:.1f} us/layer")
 
     # ---------------------------------------------------------------- per-kernel pass (HIP events)
-    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-    gates = torch.empty((T, k), dtype=torch.float32, device=dev)
-    srt = dict(counts=torch.empty(E, dtype=torch.int32, device=dev),
-               offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
-               sorted_slots=torch.empty(T * k, dtype=torch.int32, device=dev),
-               active=torch.empty(E, dtype=torch.int32, device=dev),
-               num_active=torch.empty(1, dtype=torch.int32, device=dev))
-    h = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
+    # Right after the timed region, the same K layer forwards issued as the four stage calls
+    # (the kernels the forward launches), with a HIP event between stages recorded on the
+    # stream the kernels are launched on.  Launches are queued far faster than the GPU
+    # drains them, so the stream never runs dry and each event pair brackets one kernel.
     stream = torch.cuda.current_stream(dev)
     KS = args.stage_steps or K
-    names = ("route", "sort", "gate_up", "down_combine")
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(KS)]
-    n_active = []
     for i in range(KS):
-        lay = layers[i % L]
-        w = lay["w"]
-        e = evs[i]
-        e[0].record(stream)
-        mx.moe_route_topk(lay["logits"], k, ids=ids, gates=gates)
-        e[1].record(stream)
-        mx.moe_sort_by_expert(ids, E, out=srt)
-        e[2].record(stream)
-        mx.moe_gate_up_swiglu(lay["x"], w["wgu"], w["sgu"], srt, k, h=h)
-        e[3].record(stream)
-        mx.moe_down_combine(h, gates, w["wd"], w["sd"], srt, T, k, out=lay["y"], ws=ws)
-        e[4].record(stream)
-        if i < L:
-            n_active.append(srt["num_active"].clone())
+        staged(i, evs[i], stream)
     torch.cuda.synchronize()
     stage_ms = {n: [] for n in names}
     for e in evs:
         for j, n in enumerate(names):
             stage_ms[n].append(e[j].elapsed_time(e[j + 1]))
-    n_active = [int(a.item()) for a in n_active]
+    staged_us_per_layer = evs[0][0].elapsed_time(evs[-1][-1]) * 1e3 / KS
 
     # ---------------------------------------------------------------- bytes and roofline
     gu_expert = 2 * I * H // 2 + 2 * I * H // 32          # gate_up codes + scales per expert
@@ -208,8 +258,10 @@ def main():
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
         "frac": round(gu_achieved / HBM_PEAK_GBPS, 4),
-        "traffic": None,
+        "traffic": measured_traffic(cfg.name),
         "avg_launch_us": round(float(np.mean(gu_ms)) * 1e3, 2),
+        "launches": len(gu_ms),
+        "timing": "HIP events on the launch stream, one pair per launch, right after the timed region",
         "bytes_per_launch": int(np.mean(gu_bytes)),
     }
 
@@ -261,6 +313,7 @@ def main():
         "active_experts": n_active,
         "algorithmic_bytes_per_layer": int(mean_layer_bytes),
         "stages_us": {n: round(float(np.mean(v)) * 1e3, 2) for n, v in stage_ms.items()},
+        "staged_us_per_layer": round(staged_us_per_layer, 2),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "env": {"GPU_MAX_HW_QUEUES": os.environ.get("GPU_MAX_HW_QUEUES"), "torch": torch.__version__,
