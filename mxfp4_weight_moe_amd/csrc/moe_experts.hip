@@ -62,6 +62,15 @@ __device__ __forceinline__ ItemIndex item_decode(int it, int nquad, int na) {
   return r;
 }
 
+// Segments per weight step: an item's segments (H / 256 for gate_up, I / 256 for down)
+// must be a multiple of these, which the launchers check.  Activation chunks are a
+// multiple of both, so they end on steps of either kernel.
+constexpr int GU_SPS = 2;  // gate_up: 28 segments per item at H = 7168
+constexpr int DN_SPS = 2;  // down: 8 segments per item at I = 2048
+constexpr int CHUNK_ALIGN = GU_SPS > DN_SPS ? GU_SPS : DN_SPS;
+static_assert(CHUNK_ALIGN % GU_SPS == 0 && CHUNK_ALIGN % DN_SPS == 0, "chunks must end on steps");
+static_assert(SUB_ROWS * CHUNK_ALIGN <= XCHUNK_ROWSEGS, "a chunk must hold one step of a full row group");
+
 // Fields shared by both expert GEMMs: the work list over (row group, expert, tile quad).
 struct ExpertItems {
   SortView sv;
@@ -78,8 +87,7 @@ struct ExpertItems {
     f.rows = min(16, ld_uniform(sv.counts, f.e) - ix.g * 16);
     f.row0 = ld_uniform(sv.offsets, f.e) + ix.g * 16;
     f.tile0 = ix.quad * WG_WAVES;
-    // a whole number of 4-segment steps, at least one, at most 64 row-segments (32 KB)
-    f.cs = min(nseg, max(4, (64 / f.rows) & ~3));
+    f.cs = chunk_segments(f.rows, nseg, CHUNK_ALIGN);
     return f;
   }
 };
@@ -98,23 +106,29 @@ struct GateUpPolicy : ExpertItems {
   const uint8_t* sgu;
   uint16_t* h;
   int H, I, k;
+  uint32_t kinv;  // ceil(2^24 / k)
   size_t e_codes, e_scales;
 
+  // token = slot / k as (slot * ceil(2^24 / k)) >> 24, exact for slot < 8192 and k <= 32
+  static_assert(MX_MAX_TOKENS * MX_MAX_TOPK <= 8192 && MX_MAX_TOPK <= 32, "reciprocal range");
   __device__ __forceinline__ int x_row_offset(const ItemInfo& f, int m) const {
-    return (ld_uniform(sv.sorted_slots, f.row0 + m) / k) * H;
+    const uint32_t slot = (uint32_t)ld_uniform(sv.sorted_slots, f.row0 + m);
+    return (int)(((uint64_t)slot * kinv) >> 24) * H;
   }
   __device__ __forceinline__ void w_setup(const ItemInfo& f, int wave, WCursor<NS>& c, int lane) const {
     const uint8_t* we = wgu + (size_t)f.e * e_codes;
-    const uint8_t* se = sgu + (size_t)f.e * e_scales;
-    const size_t kb = (size_t)H >> 1, ks = (size_t)H >> 5;
+    const size_t kb = (size_t)H >> 1;
     const int n0 = (f.tile0 + wave) * SUB_ROWS;
     for (int q = 0; q < 2; ++q) {
       const int r = n0 + (lane >> 3) + 8 * q;
       c.w[0][q] = we + (size_t)r * kb + (lane & 7) * 16;        // gate rows
       c.w[1][q] = we + (size_t)(I + r) * kb + (lane & 7) * 16;  // up rows
     }
-    c.s[0] = se + (size_t)(n0 + (lane & 15)) * ks;
-    c.s[1] = se + (size_t)(I + n0 + (lane & 15)) * ks;
+  }
+  // subtile 0: gate row n0 + r; subtile 1: the matching up row I + n0 + r
+  __device__ __forceinline__ const uint8_t* scale_row(const ItemInfo& f, int wave, int i, int r) const {
+    const int n = (f.tile0 + wave) * SUB_ROWS + r + (i ? I : 0);
+    return sgu + (size_t)f.e * e_scales + (size_t)n * (H >> 5);
   }
   __device__ __forceinline__ void c_setup(const ItemInfo& f, int wave, EpiState& s, int) const {
     s.hrow = f.row0;
@@ -153,13 +167,15 @@ struct DownPolicy : ExpertItems {
   __device__ __forceinline__ int x_row_offset(const ItemInfo& f, int m) const { return (f.row0 + m) * I; }
   __device__ __forceinline__ void w_setup(const ItemInfo& f, int wave, WCursor<NS>& c, int lane) const {
     const uint8_t* we = wd + (size_t)f.e * e_codes;
-    const uint8_t* se = sd + (size_t)f.e * e_scales;
-    const size_t kb = (size_t)I >> 1, ks = (size_t)I >> 5;
+    const size_t kb = (size_t)I >> 1;
     const int n0 = (f.tile0 + wave) * 32;
-    for (int i = 0; i < NS; ++i) {
+    for (int i = 0; i < NS; ++i)
       for (int q = 0; q < 2; ++q) c.w[i][q] = we + (size_t)(n0 + 16 * i + (lane >> 3) + 8 * q) * kb + (lane & 7) * 16;
-      c.s[i] = se + (size_t)(n0 + 16 * i + (lane & 15)) * ks;
-    }
+  }
+  // subtile i: output rows n0 + 16 i .. n0 + 16 i + 15
+  __device__ __forceinline__ const uint8_t* scale_row(const ItemInfo& f, int wave, int i, int r) const {
+    const int n = (f.tile0 + wave) * 32 + SUB_ROWS * i + r;
+    return sd + (size_t)f.e * e_scales + (size_t)n * (I >> 5);
   }
   __device__ __forceinline__ void c_setup(const ItemInfo& f, int wave, EpiState& s, int lane) const {
     s.slot = group_slot(sv.sorted_slots, f.row0, f.rows, lane);
@@ -175,8 +191,7 @@ struct DownPolicy : ExpertItems {
 
 // ------------------------------------------------------------------ kernels
 
-constexpr int GU_SPS = 4, GU_DW = 1;  // gate_up: 28 segments per item at H = 7168
-constexpr int DN_SPS = 4, DN_DW = 1;  // down: 8 segments per item at I = 2048
+
 
 __global__ void __launch_bounds__(WG_WAVES * 64) moe_gate_up_kernel(const uint16_t* __restrict__ x,
                                                                     const uint8_t* __restrict__ wgu,
@@ -185,6 +200,7 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_gate_up_kernel(const uint16
                                                                     int gmax) {
   __shared__ __attribute__((aligned(16))) uint8_t xbufs[2 * XCHUNK_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t slabs[WG_WAVES][SLAB_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t sslabs[WG_WAVES][sslab_bytes<2>()];
   __shared__ uint32_t xctr[2];
   if (threadIdx.x < 2) xctr[threadIdx.x] = 0u;
   __syncthreads();
@@ -203,9 +219,11 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_gate_up_kernel(const uint16
   p.H = H;
   p.I = I;
   p.k = k;
+  p.kinv = ((1u << 24) + (uint32_t)k - 1u) / (uint32_t)k;
   p.e_codes = (size_t)2 * I * (H / 2);
   p.e_scales = (size_t)2 * I * (H / 32);
-  stream_items<GateUpPolicy, GU_SPS, GU_DW>(p, xbufs, xctr, slabs[wave], wave, lane);
+  static_assert(GateUpPolicy::NS == 2, "scale slab size");
+  stream_items<GateUpPolicy, GU_SPS>(p, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
 }
 
 __global__ void __launch_bounds__(WG_WAVES * 64) moe_down_kernel(const uint16_t* __restrict__ h,
@@ -214,6 +232,7 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_down_kernel(const uint16_t*
                                                                  float* __restrict__ dpart, int H, int I, int gmax) {
   __shared__ __attribute__((aligned(16))) uint8_t xbufs[2 * XCHUNK_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t slabs[WG_WAVES][SLAB_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t sslabs[WG_WAVES][sslab_bytes<2>()];
   __shared__ uint32_t xctr[2];
   if (threadIdx.x < 2) xctr[threadIdx.x] = 0u;
   __syncthreads();
@@ -232,7 +251,8 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_down_kernel(const uint16_t*
   p.I = I;
   p.e_codes = (size_t)H * (I / 2);
   p.e_scales = (size_t)H * (I / 32);
-  stream_items<DownPolicy, DN_SPS, DN_DW>(p, xbufs, xctr, slabs[wave], wave, lane);
+  static_assert(DownPolicy::NS == 2, "scale slab size");
+  stream_items<DownPolicy, DN_SPS>(p, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
 }
 
 // One thread per (token, 4 consecutive outputs): fp32 sum of the gate-weighted slots, j ascending.
@@ -273,6 +293,7 @@ static int row_groups(int T) { return (T + 15) / 16; }
 
 int launch_gate_up(const uint16_t* x, const uint8_t* wgu, const uint8_t* sgu, const SortView& sv, uint16_t* h, int T,
                    int H, int I, int E, int k, hipStream_t stream) {
+  if (H % (SEG_K * GU_SPS) != 0 || H % (SEG_K * SRUN) != 0 || I % (SUB_ROWS * WG_WAVES) != 0) return MX_ERR_SHAPE;
   static const int occ = resident_wgs_per_cu(moe_gate_up_kernel, WG_WAVES * 64);
   const int gmax = row_groups(T);
   const int grid = expert_grid((int64_t)gmax * max_active(T, E, k) * (I / (SUB_ROWS * WG_WAVES)), occ);
@@ -284,6 +305,7 @@ int launch_gate_up(const uint16_t* x, const uint8_t* wgu, const uint8_t* sgu, co
 int launch_down(const uint16_t* h, const float* gates, const uint8_t* wd, const uint8_t* sd, const SortView& sv,
                 float* dpart, int T, int H, int I, int E, int k, hipStream_t stream) {
   (void)gates;  // applied by the combine
+  if (I % (SEG_K * DN_SPS) != 0 || I % (SEG_K * SRUN) != 0 || H % (32 * WG_WAVES) != 0) return MX_ERR_SHAPE;
   static const int occ = resident_wgs_per_cu(moe_down_kernel, WG_WAVES * 64);
   const int gmax = row_groups(T);
   const int grid = expert_grid((int64_t)gmax * max_active(T, E, k) * (H / (32 * WG_WAVES)), occ);

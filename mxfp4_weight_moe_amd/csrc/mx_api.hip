@@ -56,8 +56,8 @@ static int check_moe_sizes(int64_t T, int64_t E, int64_t k) {
   return MX_OK;
 }
 
-// The expert kernels stream 1024 K values (four segments) per step and load the scales of
-// two segments as one 16-byte piece per row, so H and I must be multiples of 1024.
+// The expert kernels stage the weight scales 1024 K values (four 256-value segments) at a
+// time, so H and I must be multiples of 1024.
 static int check_expert_dims(int64_t H, int64_t I) {
   if (H < 1024 || I < 1024 || H % 1024 != 0 || I % 1024 != 0 || H > 65536 || I > 65536) return MX_ERR_SHAPE;
   return MX_OK;

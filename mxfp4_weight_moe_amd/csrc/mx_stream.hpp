@@ -5,53 +5,81 @@
 // activation slice.  A workgroup owns a strided subset of the items and walks them
 // back to back:
 //
-//   weights   each wave keeps its own register ring of DW steps; a step is SPS segments
-//             (a segment = 256 K values of NS x 16 rows), requested back to back so each
-//             row's SPS * 128 bytes hit one open DRAM page.  The ring runs across item
-//             boundaries, so there is no pipeline drain between items.
+//   weights   each wave keeps a register ring of one step: SPS segments (a segment = 256
+//             K values of NS x 16 rows).  A segment's registers are reloaded with the same
+//             segment of the next step as soon as they have been copied into the LDS
+//             transpose slab, so about one step of loads is always in flight while the
+//             wave computes.  The ring runs across item boundaries, so there is no
+//             pipeline drain between items.
+//   scales    staged per wave in LDS, one run of SRUN segments at a time: one coalesced
+//             16-byte load per lane brings the run's scales of all NS x 16 rows (lanes
+//             SLANES_PER_ROW apart cover one row), one step ahead of use, and each segment
+//             reads its row's 8 bytes back with one LDS load.  Loading 16 bytes of one row
+//             per lane and segment pair instead made the scale requests, not the bytes, cost
+//             a seventh of the kernel's time.
 //   acts      the activation rows of an item are staged in LDS, chunk by chunk, shared
 //             by the 4 waves.  A chunk holds CS segments of the item's R rows, with
-//             CS = 64 / R rounded down to a multiple of SPS (at least SPS), so a chunk is at
-//             most 32 KB, is loaded by XROUNDS rounds of 16-byte loads of the 256 threads,
-//             and ends on a step.  The loads of chunk i+1 are issued when chunk i starts and
-//             written to the other LDS buffer when it ends; LDS counters hand it over.
-//
-// Vector memory instructions per wave and segment: 2 * NS weight loads, NS / 2 scale loads
-// (16 bytes of one row = 2 segments) and on average 4 / CS activation loads; the MFMA
-// activation operand is read from LDS.  Issuing activation loads per wave and segment,
-// or one 8-byte scale load per row and segment, made the request count rather than the
-// bytes the limit.
+//             CS = XCHUNK_ROWSEGS / R rounded down to a multiple of SPS (at least SPS), so a
+//             chunk fits XCHUNK_BYTES, is loaded by XROUNDS rounds of 16-byte loads of
+//             the 256 threads, and ends on a step.  The loads of chunk i+1 are issued when
+//             chunk i starts and written to the other LDS buffer when it ends; LDS counters
+//             hand it over.
 //
 // Loads retire in issue order and every step issues the same weight loads (an exhausted
-// cursor re-reads its last segment), so the compiler's waits stay exact: a step waits
-// only for the segment it consumes.
+// cursor re-reads its last segment), so the compiler's waits stay exact: a segment waits
+// only for its own loads, issued one step earlier.
 #pragma once
 #include "mx_device.hpp"
 
 namespace mx {
 
 constexpr int WG_WAVES = 4;
+// sched_barrier mask: ALU, VALU, SALU, MFMA, all DS and transcendental instructions may be
+// scheduled across; vector memory instructions may not
+constexpr int SCHED_ALL_BUT_VMEM = 0x1 | 0x2 | 0x4 | 0x8 | 0x80 | 0x100 | 0x200 | 0x400;
 constexpr int XCHUNK_BYTES = 32768;  // one activation chunk: R rows x CS segments x 512 B
 constexpr int XPIECES = XCHUNK_BYTES / 16;
 constexpr int XROUNDS = XPIECES / (WG_WAVES * 64);
+constexpr int XCHUNK_ROWSEGS = XCHUNK_BYTES / (SEG_K * 2);  // row-segments a chunk holds
 
-// One step of the weight ring: SPS consecutive segments of the wave's NS subtiles, so each
-// row's SPS * 128 bytes are requested back to back (DRAM pages are opened once per step,
-// not once per segment), plus their scales: 16 bytes per row cover two segments.
+// Activation chunk length, in segments, for a group of `rows` rows: as many segments as fit,
+// a multiple of `align` (the weight step, so chunks end on steps), and at least one step.
+__host__ __device__ constexpr int chunk_segments(int rows, int nseg, int align) {
+  return (XCHUNK_ROWSEGS / rows / align * align) < align ? align
+         : ((XCHUNK_ROWSEGS / rows / align * align) < nseg ? XCHUNK_ROWSEGS / rows / align * align : nseg);
+}
+
+// Scale staging: runs of SRUN segments (an item's segment count must be a multiple).
+constexpr int SRUN = 4;
+constexpr int SRUN_ROW_BYTES = SRUN * SEG_SCALES;         // one row's scales of a run
+constexpr int SLANES_PER_ROW = SRUN_ROW_BYTES / 16;       // lanes loading one row
+constexpr int SROWS_PER_LOAD = 64 / SLANES_PER_ROW;       // rows one wave load covers
+template <int NS>
+constexpr int scale_loads() {
+  static_assert((NS * SUB_ROWS) % SROWS_PER_LOAD == 0, "whole scale loads per run");
+  return NS * SUB_ROWS / SROWS_PER_LOAD;
+}
+template <int NS>
+constexpr int sslab_bytes() {
+  return NS * SUB_ROWS * SRUN_ROW_BYTES;
+}
+
+// One step of the weight ring: SPS consecutive segments of the wave's NS subtiles.
 template <int NS, int SPS>
 struct WRing {
   u32x4 w[SPS][NS][2];
-  u32x4 s[NS][SPS / 2];
 };
 
 template <int NS>
 struct WCursor {
   int it;   // current item
-  int seg;  // first segment of the next step to load
-  const uint8_t* w[NS][2];
-  const uint8_t* s[NS];
+  int seg;  // first segment of the step the ring is reloaded with
+  const uint8_t* w[NS][2];                 // this lane's code bytes of segment 0 (2 rows)
+  const uint8_t* sr[scale_loads<NS>()];    // this lane's scale bytes of segment 0, per load
 };
 
+// Fill the ring with the step at cursor c, in the order the loop reloads it, so that the
+// compiler's waits on entry to the loop match its waits inside it.
 template <int NS, int SPS>
 __device__ __forceinline__ void wring_load(WRing<NS, SPS>& r, const WCursor<NS>& c) {
 #pragma unroll
@@ -62,11 +90,26 @@ __device__ __forceinline__ void wring_load(WRing<NS, SPS>& r, const WCursor<NS>&
       r.w[j][i][0] = ld_stream16(c.w[i][0] + wo);
       r.w[j][i][1] = ld_stream16(c.w[i][1] + wo);
     }
+    __builtin_amdgcn_sched_barrier(SCHED_ALL_BUT_VMEM);
   }
+}
+
+// Scales of the run starting at c.seg (a multiple of SRUN), one 16-byte load per lane and load.
+template <int NS>
+__device__ __forceinline__ void srun_load(u32x4 (&sreg)[scale_loads<NS>()], const WCursor<NS>& c) {
 #pragma unroll
-  for (int i = 0; i < NS; ++i)
+  for (int k = 0; k < scale_loads<NS>(); ++k) sreg[k] = ld16(c.sr[k] + (size_t)c.seg * SEG_SCALES);
+  __builtin_amdgcn_sched_barrier(SCHED_ALL_BUT_VMEM);
+}
+
+// The slab holds row rho = i * 16 + r of the run at rho * SRUN_ROW_BYTES; a load's 64 lanes
+// cover SROWS_PER_LOAD consecutive rows, so lane l of load k lands at k * 1024 + l * 16.
+template <int NS>
+__device__ __forceinline__ void srun_store(uint8_t* __restrict__ sslab, const u32x4 (&sreg)[scale_loads<NS>()],
+                                           int lane) {
 #pragma unroll
-    for (int q = 0; q < SPS / 2; ++q) r.s[i][q] = ld16(c.s[i] + (size_t)(c.seg + 2 * q) * SEG_SCALES);
+  for (int k = 0; k < scale_loads<NS>(); ++k)
+    *reinterpret_cast<u32x4*>(sslab + k * (64 * 16) + lane * 16) = sreg[k];
 }
 
 // What the kernels need of an item; all fields are uniform across the workgroup.
@@ -119,23 +162,32 @@ __device__ __forceinline__ void xready_wait(const uint32_t* ctr, uint32_t target
   __asm__ volatile("" ::: "memory");
 }
 
-// Issue the activation loads of chunk `ch` (XROUNDS rounds of one 16-byte load per
-// thread; threads past the chunk repeat its last piece).
+// Row-segment rs (< XCHUNK_ROWSEGS) of a chunk with R rows is segment rs / R, row rs % R.
+// The quotient is (rs * ceil(2^16 / R)) >> 16, exact for rs < 64 and R <= 16.
+static_assert(XCHUNK_ROWSEGS <= 64, "the reciprocal quotient is exact only below 64 row-segments");
+__device__ __forceinline__ uint32_t rows_reciprocal(int R) { return (65536u + (uint32_t)R - 1u) / (uint32_t)R; }
+
+// Issue the activation loads of chunk `ch`: XROUNDS rounds of one 16-byte piece per thread
+// (threads past the chunk repeat its last piece; skipping the unneeded rounds costs more
+// registers than the loads it saves).  Lane m < 16 holds row m's element offset, and each
+// thread fetches its row's offset from there with one cross-lane read.
 template <class P>
 __device__ __forceinline__ void xchunk_load(const P& p, const XChunk& ch, u32x4 (&xv)[XROUNDS], int tid) {
   const int R = ch.info.rows;
   const int npieces = R * ch.ns * 32;
-  int rowoff[16];  // element offset of each row of the group (uniform)
+  const uint32_t inv = rows_reciprocal(R);
+  int myoff = 0;  // lane (tid & 15)'s row offset
 #pragma unroll
-  for (int m = 0; m < 16; ++m) rowoff[m] = (m < R) ? p.x_row_offset(ch.info, m) : 0;
+  for (int m = 0; m < 16; ++m) {
+    const int off = (m < R) ? p.x_row_offset(ch.info, m) : 0;
+    myoff = ((tid & 15) == m) ? off : myoff;
+  }
 #pragma unroll
   for (int r = 0; r < XROUNDS; ++r) {
     const int q = min(r * (WG_WAVES * 64) + tid, npieces - 1);
     const int rs = q >> 5, pc = q & 31;
-    const int s = rs / R, m = rs - s * R;
-    int ro = 0;
-#pragma unroll
-    for (int mm = 0; mm < 16; ++mm) ro = (m == mm) ? rowoff[mm] : ro;
+    const int s = (int)(((uint32_t)rs * inv) >> 16), m = rs - s * R;
+    const int ro = __builtin_amdgcn_ds_bpermute(m << 2, myoff);
     xv[r] = ld16(p.xact + (size_t)ro + (size_t)(ch.c0 + s) * SEG_K + pc * 8);
   }
 }
@@ -144,21 +196,24 @@ __device__ __forceinline__ void xchunk_store(uint8_t* __restrict__ buf, const XC
                                              int tid) {
   const int R = ch.info.rows;
   const int npieces = R * ch.ns * 32;
+  const uint32_t inv = rows_reciprocal(R);
 #pragma unroll
   for (int r = 0; r < XROUNDS; ++r) {
     const int q = min(r * (WG_WAVES * 64) + tid, npieces - 1);
     const int rs = q >> 5, pc = q & 31;
-    const int s = rs / R, m = rs - s * R;
+    const int s = (int)(((uint32_t)rs * inv) >> 16), m = rs - s * R;
     *reinterpret_cast<u32x4*>(buf + xpiece_off(s, m, R, pc)) = xv[r];
   }
 }
 
 // Consume one segment: LDS transpose of the codes, decode, MFMA with activations from the
 // chunk buffer (xrow: this lane's row within the chunk; rows past R read row 0, whose
-// products land in output columns that are not stored).  sc2[i] holds the 8 scale bytes of
-// subtile i's row (lane & 15) for this segment.
+// products land in output columns that are not stored).  The scales come from the wave's
+// scale slab (segment u of the staged run).  Once the codes are in the slab, w is reloaded
+// with segment `nseg_next` of the cursor `c` (the same segment of the next step).
 template <int NS>
-__device__ __forceinline__ void segment_compute(const u32x4 (&w)[NS][2], const u32x2 (&sc2)[NS],
+__device__ __forceinline__ void segment_compute(u32x4 (&w)[NS][2], const uint8_t* __restrict__ sslab, int u,
+                                                const WCursor<NS>& c, int nseg_next,
                                                 const uint8_t* __restrict__ xbuf, int sl, int R, int xrow,
                                                 uint8_t* __restrict__ slab, const uint32_t (&lds_wr)[2],
                                                 const uint32_t (&lds_rd)[2], uint32_t sshift, int lane,
@@ -173,6 +228,20 @@ __device__ __forceinline__ void segment_compute(const u32x4 (&w)[NS][2], const u
     wc[i][0] = *reinterpret_cast<const u32x4*>(slab + lds_rd[0]);
     wc[i][1] = *reinterpret_cast<const u32x4*>(slab + lds_rd[1]);
   }
+  const size_t wo = (size_t)nseg_next * SEG_BYTES;
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    w[i][0] = ld_stream16(c.w[i][0] + wo);
+    w[i][1] = ld_stream16(c.w[i][1] + wo);
+  }
+  // Keep global loads in segment order (everything else may still move across), so the
+  // next step's waits are progressive: segment j waits only for the loads of segment j.
+  __builtin_amdgcn_sched_barrier(SCHED_ALL_BUT_VMEM);
+  // the 8 scale bytes of subtile i's row (lane & 15) for this segment
+  u32x2 sc2[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i)
+    sc2[i] = *reinterpret_cast<const u32x2*>(sslab + (i * SUB_ROWS + (lane & 15)) * SRUN_ROW_BYTES + u * SEG_SCALES);
   const int j = lane >> 4;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -180,11 +249,11 @@ __device__ __forceinline__ void segment_compute(const u32x4 (&w)[NS][2], const u
 #pragma unroll
     for (int i = 0; i < NS; ++i) sc[i] = e8m0_scale_operand((sc2[i][h] >> sshift) & 0xFFu);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c4 = 0; c4 < 4; ++c4) {
       const bf16x8 xb =
-          as_bf16x8(*reinterpret_cast<const u32x4*>(xbuf + xpiece_off(sl, xrow, R, (j + 4 * h) * 4 + c)));
+          as_bf16x8(*reinterpret_cast<const u32x4*>(xbuf + xpiece_off(sl, xrow, R, (j + 4 * h) * 4 + c4)));
 #pragma unroll
-      for (int i = 0; i < NS; ++i) acc[i] = mfma_bf16(decode8(wc[i][h][c], sc[i]), xb, acc[i]);
+      for (int i = 0; i < NS; ++i) acc[i] = mfma_bf16(decode8(wc[i][h][c4], sc[i]), xb, acc[i]);
     }
   }
 }
@@ -193,15 +262,20 @@ __device__ __forceinline__ void segment_compute(const u32x4 (&w)[NS][2], const u
 //   static constexpr int NS;   int nseg, n_items;   const uint16_t* xact;
 //   bool valid(int it);   ItemInfo info(int it);
 //   int x_row_offset(const ItemInfo&, int m)        -- element offset of activation row m
-//   void w_setup(const ItemInfo&, int wave, WCursor<NS>&, int lane)
+//   void w_setup(const ItemInfo&, int wave, WCursor<NS>&, int lane)   -- sets c.w
+//   const uint8_t* scale_row(const ItemInfo&, int wave, int i, int r) -- scales of row r of subtile i
 //   EpiState;  void c_setup(const ItemInfo&, int wave, EpiState&, int lane)
 //   void epilogue(const EpiState&, const f32x4 (&acc)[NS], int lane)
 // `xbufs` is 2 * XCHUNK_BYTES of LDS, `xctr` 2 zeroed LDS counters, `slab` this wave's
-// SLAB_BYTES of LDS.
-template <class P, int SPS, int DW>
+// SLAB_BYTES and `sslab` its sslab_bytes<NS>() of LDS.  nseg must be a multiple of SPS and
+// of SRUN (the launchers check it).
+template <class P, int SPS>
 __device__ __forceinline__ void stream_items(P& p, uint8_t* __restrict__ xbufs, uint32_t* xctr,
-                                             uint8_t* __restrict__ slab, int wave, int lane) {
+                                             uint8_t* __restrict__ slab, uint8_t* __restrict__ sslab, int wave,
+                                             int lane) {
   constexpr int NS = P::NS;
+  constexpr int SL = scale_loads<NS>();
+  static_assert(SRUN % SPS == 0, "scale runs end on steps");
   const int tid = wave * 64 + lane;
   const int wg = blockIdx.x, n_wg = gridDim.x;
   uint32_t lds_wr[2], lds_rd[2];
@@ -216,24 +290,31 @@ __device__ __forceinline__ void stream_items(P& p, uint8_t* __restrict__ xbufs, 
   const int first = next_valid(wg);
   if (first >= p.n_items) return;
 
-  // ---- weight cursor (per wave) and its ring
+  // ---- weight cursor (per wave): the step the ring is reloaded with.  Once the
+  // workgroup's items are exhausted it stays on the last step (re-read, never used).
   WCursor<NS> cw;
-  cw.it = first;
-  cw.seg = 0;
-  p.w_setup(p.info(first), wave, cw, lane);
+  auto cursor_setup = [&](int it) {
+    const ItemInfo f = p.info(it);
+    cw.it = it;
+    cw.seg = 0;
+    p.w_setup(f, wave, cw, lane);
+#pragma unroll
+    for (int k = 0; k < SL; ++k) {
+      const int rho = k * SROWS_PER_LOAD + lane / SLANES_PER_ROW;
+      cw.sr[k] = p.scale_row(f, wave, rho / SUB_ROWS, rho % SUB_ROWS) + (lane % SLANES_PER_ROW) * 16;
+    }
+  };
+  cursor_setup(first);
   auto advance_w = [&]() {
     if (cw.seg + SPS < p.nseg) {
       cw.seg += SPS;
     } else {
       const int nx = next_valid(cw.it + n_wg);
-      if (nx < p.n_items) {
-        cw.it = nx;
-        cw.seg = 0;
-        p.w_setup(p.info(nx), wave, cw, lane);
-      }
+      if (nx < p.n_items) cursor_setup(nx);
     }
   };
-  WRing<NS, SPS> rw[DW];
+  WRing<NS, SPS> rw;
+  u32x4 sreg[SL];  // scales of the next run, loaded one step ahead
 
   // ---- activation chunks (per workgroup): the first one is loaded before the loop
   auto chunk_of = [&](int it, int c0) {
@@ -257,23 +338,22 @@ __device__ __forceinline__ void stream_items(P& p, uint8_t* __restrict__ xbufs, 
   xchunk_load(p, cur, xv, tid);
   xchunk_store(xbufs, cur, xv, tid);
   xready_publish(&xctr[0]);
-  int xb = 0;          // LDS buffer holding `cur`
+  int xb = 0;                  // LDS buffer holding `cur`
   uint32_t gen[2] = {1u, 0u};  // chunks published so far into each buffer
   xready_wait(&xctr[0], WG_THREADS);
+  srun_load<NS>(sreg, cw);  // the first run's scales
   bool have_next;
   XChunk nxt = next_chunk(cur, have_next);
   if (have_next) xchunk_load(p, nxt, xv, tid);
-  // The weight ring is filled after the next chunk's activation loads, so on every path
-  // into the loop at least DW steps of weight loads follow them and the wait before
-  // their LDS store never drains the weight stream.
-#pragma unroll
-  for (int d = 0; d < DW; ++d) {
-    wring_load(rw[d], cw);
-    advance_w();
-  }
+  // The first weight step is requested after the next chunk's activation loads, so the
+  // wait before their LDS store never drains the weight stream.
+  wring_load(rw, cw);
+  advance_w();
+  srun_store<NS>(sslab, sreg, lane);
+  if (cw.seg % SRUN == 0) srun_load<NS>(sreg, cw);
 
   // ---- compute cursor
-  int cit = first, cseg = 0;
+  int cseg = 0;
   typename P::EpiState es;
   p.c_setup(cur.info, wave, es, lane);
   int xrow = ((lane & 15) < cur.info.rows) ? (lane & 15) : 0;
@@ -282,54 +362,44 @@ __device__ __forceinline__ void stream_items(P& p, uint8_t* __restrict__ xbufs, 
 #pragma unroll
   for (int i = 0; i < NS; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  while (cit < p.n_items) {
+  for (;;) {
+    // one step: SPS segments; each segment's ring slot is reloaded with the next step
 #pragma unroll
-    for (int u = 0; u < DW; ++u) {
-      if (cit < p.n_items) {
-#pragma unroll
-        for (int jj = 0; jj < SPS; ++jj) {
-          u32x2 sc2[NS];
-#pragma unroll
-          for (int i = 0; i < NS; ++i) {
-            const u32x4 q = rw[u].s[i][jj / 2];
-            sc2[i] = (jj & 1) ? u32x2{q[2], q[3]} : u32x2{q[0], q[1]};
-          }
-          segment_compute<NS>(rw[u].w[jj], sc2, xbufs + xb * XCHUNK_BYTES, cseg + jj - cur.c0, cur.info.rows, xrow,
-                              slab, lds_wr, lds_rd, sshift, lane, acc);
-        }
-        // Chunks and items end on step boundaries (their lengths are multiples of SPS), so
-        // this bookkeeping runs between steps, after which the next weight loads follow.
-        cseg += SPS;
-        if (cseg >= cur.c0 + cur.ns) {
-          // chunk done: publish this thread's pieces of the next chunk, wait for the rest
-          if (have_next) {
-            xchunk_store(xbufs + (xb ^ 1) * XCHUNK_BYTES, nxt, xv, tid);
-            xready_publish(&xctr[xb ^ 1]);
-            gen[xb ^ 1] += 1u;
-            xready_wait(&xctr[xb ^ 1], gen[xb ^ 1] * WG_THREADS);
-          }
-          if (cseg >= p.nseg) {
-            p.epilogue(es, acc, lane);
-#pragma unroll
-            for (int i = 0; i < NS; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-            cit = have_next ? nxt.it : p.n_items;
-            cseg = 0;
-          }
-          if (have_next) {
-            cur = nxt;
-            xb ^= 1;
-            if (cseg == 0) {
-              p.c_setup(cur.info, wave, es, lane);
-              xrow = ((lane & 15) < cur.info.rows) ? (lane & 15) : 0;
-            }
-            nxt = next_chunk(cur, have_next);
-            if (have_next) xchunk_load(p, nxt, xv, tid);
-          }
-        }
+    for (int jj = 0; jj < SPS; ++jj)
+      segment_compute<NS>(rw.w[jj], sslab, (cseg + jj) % SRUN, cw, cw.seg + jj, xbufs + xb * XCHUNK_BYTES,
+                          cseg + jj - cur.c0, cur.info.rows, xrow, slab, lds_wr, lds_rd, sshift, lane, acc);
+    advance_w();
+    // Chunks and items end on step boundaries (their lengths are multiples of SPS).
+    cseg += SPS;
+    if (cseg >= cur.c0 + cur.ns) {
+      // chunk done: publish this thread's pieces of the next chunk, wait for the rest
+      if (have_next) {
+        xchunk_store(xbufs + (xb ^ 1) * XCHUNK_BYTES, nxt, xv, tid);
+        xready_publish(&xctr[xb ^ 1]);
+        gen[xb ^ 1] += 1u;
+        xready_wait(&xctr[xb ^ 1], gen[xb ^ 1] * WG_THREADS);
       }
-      wring_load(rw[u], cw);
-      advance_w();
+      if (cseg >= p.nseg) {
+        p.epilogue(es, acc, lane);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (!have_next) break;
+        cseg = 0;
+      }
+      cur = nxt;
+      xb ^= 1;
+      if (cseg == 0) {
+        p.c_setup(cur.info, wave, es, lane);
+        xrow = ((lane & 15) < cur.info.rows) ? (lane & 15) : 0;
+      }
+      nxt = next_chunk(cur, have_next);
+      if (have_next) xchunk_load(p, nxt, xv, tid);
     }
+    // Scales: the next step starting a run finds its run in sreg (loaded when the weight
+    // cursor reached it, one step ago); the wave's own earlier slab reads precede this
+    // store in LDS order.  Then prefetch the run the cursor has just reached, if any.
+    if (cseg % SRUN == 0) srun_store<NS>(sslab, sreg, lane);
+    if (cw.seg % SRUN == 0) srun_load<NS>(sreg, cw);
   }
 }
 
