@@ -3,7 +3,7 @@
 
     python bench.py [--steps K] [--warmup W] [--workload moe_t32_zipf] [--layers L]
 
-A step is one MoE layer forward (route, sort, gate_up + SwiGLU, down + combine) over one
+A step is one MoE layer forward (route + sort, gate_up + SwiGLU, down + combine) over one
 batch of T tokens.  Steps cycle over L distinct layers (own weights, own activations and
 routing), as a decode step walks a stack of MoE layers, so no step finds its expert
 weights in a cache: the 256 MB last-level cache is smaller than the active bytes of L-1
@@ -14,7 +14,7 @@ synchronizations; K is rounded up to a multiple of L.
 Printed: one JSON line with the layer time (us), effective weight GB/s, a roofline entry
 for the dominant kernel (gate_up) and the CPU oracle's time on a bounded sample of the same
 workload.  The kernel's launch time comes from a second pass over the same K steps right
-after the timed region, issued as the four stage calls with a HIP event between them on
+after the timed region, issued as the three stage calls with a HIP event between them on
 the stream the kernels run on.  roofline.traffic is the kernel's HBM bytes per launch as
 measured by the committed counter summary under profiles/, and null when the workload
 differs or the kernel's sources changed since the counters were taken.
@@ -149,11 +149,10 @@ def main():
                active=torch.empty(E, dtype=torch.int32, device=dev),
                num_active=torch.empty(1, dtype=torch.int32, device=dev))
     h = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
-    names = ("route", "sort", "gate_up", "down_combine")
+    names = ("route_sort", "gate_up", "down_combine")
     n_active = []
     for lay in layers:
-        mx.moe_route_topk(lay["logits"], k, ids=ids, gates=gates)
-        mx.moe_sort_by_expert(ids, E, out=srt)
+        mx.moe_route_sort(lay["logits"], k, ids=ids, gates=gates, out=srt)
         n_active.append(int(srt["num_active"].item()))
     log(f"[bench] inputs resident: {torch.cuda.memory_allocated() / 2**30:.1f} GiB; active experts {n_active}")
 
@@ -165,14 +164,12 @@ def main():
         lay = layers[i % L]
         w = lay["w"]
         e[0].record(stream)
-        mx.moe_route_topk(lay["logits"], k, ids=ids, gates=gates)
+        mx.moe_route_sort(lay["logits"], k, ids=ids, gates=gates, out=srt)
         e[1].record(stream)
-        mx.moe_sort_by_expert(ids, E, out=srt)
-        e[2].record(stream)
         mx.moe_gate_up_swiglu(lay["x"], w["wgu"], w["sgu"], srt, k, h=h)
-        e[3].record(stream)
+        e[2].record(stream)
         mx.moe_down_combine(h, gates, w["wd"], w["sd"], srt, T, k, out=lay["y"], ws=ws)
-        e[4].record(stream)
+        e[3].record(stream)
 
     for lay in layers:
         forward(lay)
@@ -223,7 +220,7 @@ def main():
     log(f"[bench] timed {K} steps: {ms_per_step * 1e3:.1f} us/layer")
 
     # ---------------------------------------------------------------- per-kernel pass (HIP events)
-    # Right after the timed region, the same K layer forwards issued as the four stage calls
+    # Right after the timed region, the same K layer forwards issued as the three stage calls
     # (the kernels the forward launches), with a HIP event between stages recorded on the
     # stream the kernels are launched on.  Launches are queued far faster than the GPU
     # drains them, so the stream never runs dry and each event pair brackets one kernel.

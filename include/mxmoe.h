@@ -109,6 +109,15 @@ MX_API int moe_sort_by_expert(const int32_t* ids, int64_t T, int64_t top_k, int6
                        void* stream);
 
 /*
+ * moe_route_topk followed by moe_sort_by_expert of its ids (the first stage of
+ * moe_mxfp4_forward): one launch for T <= 16, two beyond.  Arguments, outputs and limits
+ * as for those two calls.
+ */
+MX_API int moe_route_sort(const float* logits, int64_t T, int64_t E, int64_t top_k, int32_t* ids, float* gates,
+                          int32_t* counts, int32_t* offsets, int32_t* sorted_slots, int32_t* active,
+                          int32_t* num_active, void* stream);
+
+/*
  * Stage hook: the gate_up GEMM with its SwiGLU epilogue, for every routed slot, from a
  * moe_sort_by_expert result (counts, offsets, sorted_slots, active, num_active).  For the
  * slot f = sorted_slots[p] routed to expert e (offsets[e] <= p < offsets[e+1]) of token

@@ -26,7 +26,7 @@ MX_MAX_TOPK = 32
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m mxfp4_weight_moe_amd.build` (hipcc, gfx950) first")
+        f"{LIB_PATH} is not built; run `python mxfp4_weight_moe_amd/build.py` (hipcc, gfx950) first")
 
 _lib = ctypes.CDLL(LIB_PATH)
 _P = ctypes.c_void_p
@@ -38,19 +38,20 @@ _lib.mx_linear.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P]
 _lib.mxfp4_dequantize.argtypes = [_P, _P, _I64, _I64, _P, _P]
 _lib.moe_route_topk.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P]
 _lib.moe_sort_by_expert.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P]
+_lib.moe_route_sort.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.moe_gate_up_swiglu.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P]
 _lib.moe_down_combine.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P,
                                   ctypes.c_size_t, _P]
 _lib.moe_mxfp4_workspace_size.restype = ctypes.c_size_t
 _lib.moe_mxfp4_workspace_size.argtypes = [_I64, _I64, _I64, _I64, _I64]
 _lib.moe_mxfp4_forward.argtypes = [_P, _P, _I64, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]
-for _n in ("mx_linear", "mxfp4_dequantize", "moe_route_topk", "moe_sort_by_expert", "moe_gate_up_swiglu",
-           "moe_down_combine", "moe_mxfp4_forward"):
+for _n in ("mx_linear", "mxfp4_dequantize", "moe_route_topk", "moe_sort_by_expert", "moe_route_sort",
+           "moe_gate_up_swiglu", "moe_down_combine", "moe_mxfp4_forward"):
     getattr(_lib, _n).restype = ctypes.c_int
 
 EXPORTED = ("mx_version", "mx_status_string", "mx_linear", "mxfp4_dequantize", "moe_route_topk",
-            "moe_sort_by_expert", "moe_gate_up_swiglu", "moe_down_combine", "moe_mxfp4_workspace_size",
-            "moe_mxfp4_forward")
+            "moe_sort_by_expert", "moe_route_sort", "moe_gate_up_swiglu", "moe_down_combine",
+            "moe_mxfp4_workspace_size", "moe_mxfp4_forward")
 
 
 class MxError(RuntimeError):
@@ -166,30 +167,55 @@ def _sort_ptrs(sort: dict, dev):
     return [_ptr(sort[key]) for key in _SORT_KEYS]
 
 
+def _sort_out(out: dict | None, T: int, k: int, E: int, dev) -> dict:
+    if out is not None:
+        _sort_ptrs(out, dev)
+        if (out["counts"].numel() != E or out["offsets"].numel() != E + 1 or out["sorted_slots"].numel() != T * k
+                or out["active"].numel() != E or out["num_active"].numel() != 1):
+            raise ValueError("sort output tensors have the wrong sizes")
+        return out
+    return dict(
+        counts=torch.empty(E, dtype=torch.int32, device=dev),
+        offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+        sorted_slots=torch.empty(T * k, dtype=torch.int32, device=dev),
+        active=torch.empty(E, dtype=torch.int32, device=dev),
+        num_active=torch.empty(1, dtype=torch.int32, device=dev),
+    )
+
+
 def moe_sort_by_expert(ids: torch.Tensor, num_experts: int, out: dict | None = None) -> dict:
     """Counting sort of the flat slots by expert (experts ascending, slot ascending)."""
     _check(ids, "ids", torch.int32, 2)
     dev = ids.device
     T, k = ids.shape
     E = int(num_experts)
-    if out is not None:
-        _sort_ptrs(out, dev)
-        if (out["counts"].numel() != E or out["offsets"].numel() != E + 1 or out["sorted_slots"].numel() != T * k
-                or out["active"].numel() != E or out["num_active"].numel() != 1):
-            raise ValueError("sort output tensors have the wrong sizes")
-    else:
-        out = dict(
-            counts=torch.empty(E, dtype=torch.int32, device=dev),
-            offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
-            sorted_slots=torch.empty(T * k, dtype=torch.int32, device=dev),
-            active=torch.empty(E, dtype=torch.int32, device=dev),
-            num_active=torch.empty(1, dtype=torch.int32, device=dev),
-        )
+    out = _sort_out(out, T, k, E, dev)
     st = _lib.moe_sort_by_expert(_ptr(ids), T, k, E, _ptr(out["counts"]), _ptr(out["offsets"]),
                                  _ptr(out["sorted_slots"]), _ptr(out["active"]), _ptr(out["num_active"]),
                                  _stream(dev))
     _raise(st, "moe_sort_by_expert")
     return out
+
+
+def moe_route_sort(logits: torch.Tensor, top_k: int, ids: torch.Tensor | None = None,
+                   gates: torch.Tensor | None = None, out: dict | None = None):
+    """moe_route_topk then moe_sort_by_expert in one launch: (ids, gates, sort dict)."""
+    _check(logits, "router_logits", torch.float32, 2)
+    dev = logits.device
+    T, E = logits.shape
+    if ids is None:
+        ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    if gates is None:
+        gates = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    _check(ids, "ids", torch.int32, 2, dev)
+    _check(gates, "gates", torch.float32, 2, dev)
+    if ids.shape != (T, top_k) or gates.shape != (T, top_k):
+        raise ValueError("ids / gates must be [T, top_k]")
+    out = _sort_out(out, T, top_k, E, dev)
+    st = _lib.moe_route_sort(_ptr(logits), T, E, top_k, _ptr(ids), _ptr(gates), *[_ptr(out[key]) for key in _SORT_KEYS],
+                             _stream(dev))
+    _raise(st, "moe_route_sort")
+    return ids, gates, out
 
 
 def moe_gate_up_swiglu(x: torch.Tensor, W_gate_up: torch.Tensor, S_gate_up: torch.Tensor, sort: dict, top_k: int,

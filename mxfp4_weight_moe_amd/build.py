@@ -1,6 +1,8 @@
 """Build the HIP library libmxmoe.so in-tree for gfx950 with hipcc.
 
-    python -m mxfp4_weight_moe_amd.build
+    python mxfp4_weight_moe_amd/build.py
+
+(run as a script: importing the package itself loads the library this builds)
 
 Each .hip source under csrc/ is compiled to an object in _build/, then linked into
 mxfp4_weight_moe_amd/libmxmoe.so.  Packed-fp32 instruction selection is disabled

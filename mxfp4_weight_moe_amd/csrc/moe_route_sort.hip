@@ -9,81 +9,145 @@
 // grouping the routed slots by expert lets each expert's weights be read once for all of
 // its rows.  The order is fixed (experts ascending, slot ascending), so the result is
 // bit-exact and independent of thread timing.
+//
+// For up to 16 tokens the layer forward runs both in one single-workgroup launch
+// (moe_route_sort_kernel); beyond that, and for the stage entry points, one kernel each.
 #include "mx_device.hpp"
 #include "mx_internal.hpp"
 
 namespace mx {
 
-constexpr int ROUTE_MAX_PER_LANE = MX_MAX_EXPERTS / 64;  // logits held per lane
-
-// (value, id) ordering of the router: larger value first, then lower id.
-__device__ __forceinline__ bool route_better(float v, int e, float bv, int be) {
-  return v > bv || (v == bv && e < be);
+// Order-preserving unsigned key of a float (larger float, larger key); -0 is first
+// normalised to +0 so that the two compare equal, as floats do.
+__device__ __forceinline__ uint32_t route_key(float v) {
+  const uint32_t b = __float_as_uint(v + 0.0f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float route_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
+// Router order as one unsigned 64-bit key: the value's key above the complement of the
+// expert id, so a larger value wins and, among equal values, the lower id.  0 (below every
+// valid key) marks an empty or already taken entry.
+__device__ __forceinline__ uint64_t route_key64(float v, int e) {
+  return ((uint64_t)route_key(v) << 32) | (uint64_t)(uint32_t)~e;
+}
+
+// a = max(a, a of the lane that DPP control CTRL selects); lanes of rows outside ROW_MASK
+// receive 0 and keep a.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void max64_dpp(uint64_t& a) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)a, CTRL, ROW_MASK, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(a >> 32), CTRL, ROW_MASK, 0xF, false);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  if (o > a) a = o;
+}
+
+// Sum over each row of 16 lanes (every lane of the row gets it).
+template <int CTRL>
+__device__ __forceinline__ float row_add_step(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+constexpr int DPP_QUAD_XOR1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
+constexpr int DPP_ROW_BCAST15 = 0x142;  // lane 15 of each row to the next row
+constexpr int DPP_ROW_BCAST31 = 0x143;  // lane 31 to rows 2 and 3
+
+// Maximum over the wavefront, returned uniform: within each row of 16 lanes by four
+// exchanges, then rows 0+1 into row 1 and 2+3 into row 3, then row 1 into row 3.
+__device__ __forceinline__ uint64_t wave_max64(uint64_t a) {
+  max64_dpp<DPP_QUAD_XOR1, 0xF>(a);
+  max64_dpp<DPP_QUAD_XOR2, 0xF>(a);
+  max64_dpp<DPP_ROW_HALF_MIRROR, 0xF>(a);
+  max64_dpp<DPP_ROW_MIRROR, 0xF>(a);
+  max64_dpp<DPP_ROW_BCAST15, 0xA>(a);
+  max64_dpp<DPP_ROW_BCAST31, 0xC>(a);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)a, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(a >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// One token's logits, lane l holding logits l, l + 64, ... (PER per lane, E <= 64 PER).
+// The loads are unconditional (indices past E re-read logit E-1, never used) so that they
+// are all in flight at once: the logits are not cache-resident after the weight stream.
+template <int PER>
+__device__ __forceinline__ void route_load(const float* __restrict__ l, int E, int lane, float (&v)[PER]) {
+#pragma unroll
+  for (int i = 0; i < PER; ++i) v[i] = l[min(lane + 64 * i, E - 1)];
+}
+
+// Top-k of one token by one wavefront, from its loaded logits.  Each of the k rounds takes
+// every lane's largest untaken key, reduces it over the wavefront with DPP exchanges and
+// marks the winner taken (its key becomes 0).  Lane j < k returns the j-th winner (slots in
+// descending logit order) and its softmax gate over the k winners.
+template <int PER>
+__device__ __forceinline__ void route_select(const float (&v)[PER], int E, int k, int lane, int& my_e,
+                                             float& my_gate) {
+  uint64_t key[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) key[i] = (lane + 64 * i < E) ? route_key64(v[i], lane + 64 * i) : 0ull;
+  uint32_t my_key = 0u;
+  my_e = 0;
+  for (int j = 0; j < k; ++j) {
+    uint64_t b = key[0];
+#pragma unroll
+    for (int i = 1; i < PER; ++i) b = key[i] > b ? key[i] : b;
+    const uint64_t w = wave_max64(b);
+    const int wi = (int)~(uint32_t)w;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) key[i] = (wi == lane + 64 * i) ? 0ull : key[i];
+    if (lane == j) {
+      my_key = (uint32_t)(w >> 32);
+      my_e = wi;
+    }
+  }
+  // softmax over the k winners, relative to the largest (slot 0)
+  const float m = route_value((uint32_t)__builtin_amdgcn_readlane((int)my_key, 0));
+  const float ex = (lane < k) ? expf(route_value(my_key) - m) : 0.f;
+  float s = row_add_step<DPP_QUAD_XOR1>(ex);
+  s = row_add_step<DPP_QUAD_XOR2>(s);
+  s = row_add_step<DPP_ROW_HALF_MIRROR>(s);
+  s = row_add_step<DPP_ROW_MIRROR>(s);
+  const float sum = (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 0)) +
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 16))) +
+                    (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 32)) +
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 48)));
+  my_gate = ex / sum;
+}
+
+// Logits per lane for E experts: 4, 8 or 16 (E <= MX_MAX_EXPERTS = 1024).
+static_assert(MX_MAX_EXPERTS <= 64 * 16, "at most 16 logits per lane");
+static int route_per(int E) { return E <= 256 ? 4 : (E <= 512 ? 8 : 16); }
+
 // One wavefront per token.
+template <int PER>
 __global__ void __launch_bounds__(256) moe_route_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                         int32_t* __restrict__ ids, float* __restrict__ gates) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const float* l = logits + (size_t)t * E;
-  const int per = (E + 63) >> 6;
-  float v[ROUTE_MAX_PER_LANE];
-  uint32_t taken = 0;
-#pragma unroll
-  for (int i = 0; i < ROUTE_MAX_PER_LANE; ++i) {
-    const int e = lane + 64 * i;
-    if (i < per && e < E) {
-      v[i] = l[e];
-    } else {
-      v[i] = 0.f;
-      taken |= 1u << i;
-    }
-  }
-  float my_v = 0.f;
-  int my_e = 0;
-  for (int j = 0; j < k; ++j) {
-    float bv = -__builtin_huge_valf();
-    int be = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < ROUTE_MAX_PER_LANE; ++i) {
-      if (i < per && !((taken >> i) & 1u)) {
-        const int e = lane + 64 * i;
-        if (route_better(v[i], e, bv, be)) {
-          bv = v[i];
-          be = e;
-        }
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oe = __shfl_xor(be, off);
-      if (route_better(ov, oe, bv, be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == j) {
-      my_v = bv;
-      my_e = be;
-    }
-  }
-  const float m = __shfl(my_v, 0);
-  const float ex = (lane < k) ? expf(my_v - m) : 0.f;
-  float sum = ex;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  float v[PER];
+  route_load<PER>(logits + (size_t)t * E, E, lane, v);
+  int e;
+  float g;
+  route_select<PER>(v, E, k, lane, e, g);
   if (lane < k) {
-    ids[(size_t)t * k + lane] = my_e;
-    gates[(size_t)t * k + lane] = ex / sum;
+    ids[(size_t)t * k + lane] = e;
+    gates[(size_t)t * k + lane] = g;
   }
 }
 
 int launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* gates, hipStream_t stream) {
-  hipLaunchKernelGGL(moe_route_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k, ids, gates);
+  const dim3 grid((T + 3) / 4), block(256);
+  switch (route_per(E)) {
+    case 4: hipLaunchKernelGGL(moe_route_kernel<4>, grid, block, 0, stream, logits, T, E, k, ids, gates); break;
+    case 8: hipLaunchKernelGGL(moe_route_kernel<8>, grid, block, 0, stream, logits, T, E, k, ids, gates); break;
+    default: hipLaunchKernelGGL(moe_route_kernel<16>, grid, block, 0, stream, logits, T, E, k, ids, gates); break;
+  }
   return hip_status(hipGetLastError());
 }
 
@@ -92,34 +156,31 @@ int launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* 
 constexpr int SORT_THREADS = 1024;
 constexpr int SORT_WORDS = MX_MAX_EXPERTS * (MX_MAX_TOKENS / 32);  // one bit per (expert, token)
 
-// Single workgroup.  A slot (t, j) routed to expert e sets bit t of expert e's token mask;
-// because a token's k experts are distinct, the rank of the slot among expert e's slots is
-// the number of set bits below t, which fixes a stable order without any ordering of
-// atomics.  Counts and the active list come from one packed block-wide scan.
-__global__ void __launch_bounds__(SORT_THREADS) moe_sort_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
-                                                                int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                                                int32_t* __restrict__ sorted_slots,
-                                                                int32_t* __restrict__ active,
-                                                                int32_t* __restrict__ num_active) {
-  __shared__ uint32_t bits[SORT_WORDS];
-  __shared__ int32_t s_off[MX_MAX_EXPERTS];
-  __shared__ int32_t s_wave[SORT_THREADS / 64];
+// LDS of the sort: a token mask per expert, each expert's offset and the scan's wave sums.
+struct SortShared {
+  uint32_t bits[SORT_WORDS];
+  int32_t off[MX_MAX_EXPERTS];
+  int32_t wave_sum[SORT_THREADS / 64];
+};
+
+// Counting sort from the token masks (bits must hold every routed (expert, token) pair).
+// A slot (t, j) routed to expert e sets bit t of expert e's mask; because a token's k
+// experts are distinct, the rank of the slot among expert e's slots is the number of set
+// bits below t, which fixes a stable order without any ordering of atomics.  Counts and
+// the active list come from one packed block-wide scan.  `ids` is read for the scatter
+// (global or LDS).  Must be called by all SORT_THREADS threads.
+__device__ __forceinline__ void sort_from_bits(SortShared& sh, const int32_t* ids, int T, int k, int E,
+                                               int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                               int32_t* __restrict__ sorted_slots, int32_t* __restrict__ active,
+                                               int32_t* __restrict__ num_active) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int words = (T + 31) >> 5;
   const int F = T * k;
-  for (int i = tid; i < E * words; i += SORT_THREADS) bits[i] = 0u;
-  __syncthreads();
-  for (int f = tid; f < F; f += SORT_THREADS) {
-    const int e = ids[f];
-    const int t = f / k;
-    if (e >= 0 && e < E) atomicOr(&bits[e * words + (t >> 5)], 1u << (t & 31));
-  }
-  __syncthreads();
   // per-expert count and active flag, packed as count | flag << 16 (count <= T < 2^16)
   const int e = tid;
   int cnt = 0;
   if (e < E)
-    for (int w = 0; w < words; ++w) cnt += __popc(bits[e * words + w]);
+    for (int w = 0; w < words; ++w) cnt += __popc(sh.bits[e * words + w]);
   const int packed = cnt | ((cnt > 0) ? (1 << 16) : 0);
   // block-wide exclusive scan of `packed` over e = 0..E-1 (E <= 1024 = blockDim)
   int incl = packed;
@@ -128,28 +189,28 @@ __global__ void __launch_bounds__(SORT_THREADS) moe_sort_kernel(const int32_t* _
     const int o = __shfl_up(incl, off);
     if (lane >= off) incl += o;
   }
-  if (lane == 63) s_wave[wave] = incl;
+  if (lane == 63) sh.wave_sum[wave] = incl;
   __syncthreads();
   if (wave == 0) {
-    int wv = (lane < SORT_THREADS / 64) ? s_wave[lane] : 0;
+    int wv = (lane < SORT_THREADS / 64) ? sh.wave_sum[lane] : 0;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int o = __shfl_up(wv, off);
       if (lane >= off) wv += o;
     }
-    if (lane < SORT_THREADS / 64) s_wave[lane] = wv;  // inclusive over waves
+    if (lane < SORT_THREADS / 64) sh.wave_sum[lane] = wv;  // inclusive over waves
   }
   __syncthreads();
-  const int excl = incl - packed + (wave > 0 ? s_wave[wave - 1] : 0);
+  const int excl = incl - packed + (wave > 0 ? sh.wave_sum[wave - 1] : 0);
   const int off_e = excl & 0xFFFF;
   const int act_pos = excl >> 16;
   if (e < E) {
-    s_off[e] = off_e;
+    sh.off[e] = off_e;
     counts[e] = cnt;
     offsets[e] = off_e;
     if (cnt > 0) active[act_pos] = e;
   }
-  const int total = s_wave[SORT_THREADS / 64 - 1];
+  const int total = sh.wave_sum[SORT_THREADS / 64 - 1];
   const int n_act = total >> 16;
   if (e < E && e >= n_act) active[e] = -1;
   if (tid == 0) {
@@ -161,17 +222,107 @@ __global__ void __launch_bounds__(SORT_THREADS) moe_sort_kernel(const int32_t* _
     const int ee = ids[f];
     if (ee < 0 || ee >= E) continue;
     const int t = f / k;
-    const uint32_t* b = bits + ee * words;
+    const uint32_t* b = sh.bits + ee * words;
     int rank = __popc(b[t >> 5] & ((1u << (t & 31)) - 1u));
     for (int w = 0; w < (t >> 5); ++w) rank += __popc(b[w]);
-    sorted_slots[s_off[ee] + rank] = f;
+    sorted_slots[sh.off[ee] + rank] = f;
   }
+}
+
+// Single workgroup: the token masks from the routed ids, then the counting sort.
+__global__ void __launch_bounds__(SORT_THREADS) moe_sort_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
+                                                                int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                                int32_t* __restrict__ sorted_slots,
+                                                                int32_t* __restrict__ active,
+                                                                int32_t* __restrict__ num_active) {
+  __shared__ SortShared sh;
+  const int tid = threadIdx.x;
+  const int words = (T + 31) >> 5;
+  const int F = T * k;
+  for (int i = tid; i < E * words; i += SORT_THREADS) sh.bits[i] = 0u;
+  __syncthreads();
+  for (int f = tid; f < F; f += SORT_THREADS) {
+    const int e = ids[f];
+    const int t = f / k;
+    if (e >= 0 && e < E) atomicOr(&sh.bits[e * words + (t >> 5)], 1u << (t & 31));
+  }
+  __syncthreads();
+  sort_from_bits(sh, ids, T, k, E, counts, offsets, sorted_slots, active, num_active);
 }
 
 int launch_sort(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* sorted_slots,
                 int32_t* active, int32_t* num_active, hipStream_t stream) {
   hipLaunchKernelGGL(moe_sort_kernel, dim3(1), dim3(SORT_THREADS), 0, stream, ids, T, k, E, counts, offsets,
                      sorted_slots, active, num_active);
+  return hip_status(hipGetLastError());
+}
+
+// ------------------------------------------------------------------ route + sort, one launch
+
+// Single workgroup of SORT_THREADS: wave w routes tokens w, w + 16, ... (loading the next
+// token's logits before routing the current one), writing ids and gates and setting the
+// token masks directly; the routed ids stay in LDS for the sort.
+template <int PER>
+__global__ void __launch_bounds__(SORT_THREADS) moe_route_sort_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids, float* __restrict__ gates,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slots,
+    int32_t* __restrict__ active, int32_t* __restrict__ num_active) {
+  __shared__ SortShared sh;
+  __shared__ int32_t s_ids[MX_MAX_TOKENS * MX_MAX_TOPK];
+  constexpr int NW = SORT_THREADS / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int words = (T + 31) >> 5;
+  float v[PER], vn[PER];
+  route_load<PER>(logits + (size_t)min(wave, T - 1) * E, E, lane, v);
+  for (int i = tid; i < E * words; i += SORT_THREADS) sh.bits[i] = 0u;
+  __syncthreads();
+  for (int t = wave; t < T; t += NW) {
+    // unconditional (the last row again past the end), so the waits stay exact
+    route_load<PER>(logits + (size_t)min(t + NW, T - 1) * E, E, lane, vn);
+    int e;
+    float g;
+    route_select<PER>(v, E, k, lane, e, g);
+    if (lane < k) {
+      ids[(size_t)t * k + lane] = e;
+      gates[(size_t)t * k + lane] = g;
+      s_ids[t * k + lane] = e;
+      atomicOr(&sh.bits[e * words + (t >> 5)], 1u << (t & 31));
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) v[i] = vn[i];
+  }
+  __syncthreads();
+  sort_from_bits(sh, s_ids, T, k, E, counts, offsets, sorted_slots, active, num_active);
+}
+
+// Up to this many tokens (one per wavefront of the workgroup) route and sort run as one
+// launch; beyond it the single workgroup's routing would take longer than the routing
+// kernel spread over T / 4 workgroups plus a separate sort launch.
+constexpr int ROUTE_SORT_FUSED_MAX_T = SORT_THREADS / 64;
+
+int launch_route_sort(const float* logits, int T, int E, int k, int32_t* ids, float* gates, int32_t* counts,
+                      int32_t* offsets, int32_t* sorted_slots, int32_t* active, int32_t* num_active,
+                      hipStream_t stream) {
+  if (T > ROUTE_SORT_FUSED_MAX_T) {
+    const int st = launch_route(logits, T, E, k, ids, gates, stream);
+    if (st != MX_OK) return st;
+    return launch_sort(ids, T, k, E, counts, offsets, sorted_slots, active, num_active, stream);
+  }
+  const dim3 grid(1), block(SORT_THREADS);
+  switch (route_per(E)) {
+    case 4:
+      hipLaunchKernelGGL(moe_route_sort_kernel<4>, grid, block, 0, stream, logits, T, E, k, ids, gates, counts,
+                         offsets, sorted_slots, active, num_active);
+      break;
+    case 8:
+      hipLaunchKernelGGL(moe_route_sort_kernel<8>, grid, block, 0, stream, logits, T, E, k, ids, gates, counts,
+                         offsets, sorted_slots, active, num_active);
+      break;
+    default:
+      hipLaunchKernelGGL(moe_route_sort_kernel<16>, grid, block, 0, stream, logits, T, E, k, ids, gates, counts,
+                         offsets, sorted_slots, active, num_active);
+      break;
+  }
   return hip_status(hipGetLastError());
 }
 

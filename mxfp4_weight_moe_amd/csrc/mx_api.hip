@@ -134,6 +134,19 @@ int moe_sort_by_expert(const int32_t* ids, int64_t T, int64_t top_k, int64_t E, 
                      static_cast<hipStream_t>(stream));
 }
 
+int moe_route_sort(const float* logits, int64_t T, int64_t E, int64_t top_k, int32_t* ids, float* gates,
+                   int32_t* counts, int32_t* offsets, int32_t* sorted_slots, int32_t* active, int32_t* num_active,
+                   void* stream) {
+  if (!logits || !ids || !gates || !counts || !offsets || !sorted_slots || !active || !num_active) return MX_ERR_NULL;
+  const int st = check_moe_sizes(T, E, top_k);
+  if (st != MX_OK) return st;
+  if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(gates, 4) || !aligned(counts, 4) || !aligned(offsets, 4) ||
+      !aligned(sorted_slots, 4) || !aligned(active, 4) || !aligned(num_active, 4))
+    return MX_ERR_ALIGN;
+  return launch_route_sort(logits, (int)T, (int)E, (int)top_k, ids, gates, counts, offsets, sorted_slots, active,
+                           num_active, static_cast<hipStream_t>(stream));
+}
+
 int moe_gate_up_swiglu(const uint16_t* x, const uint8_t* w_gate_up, const uint8_t* s_gate_up, const int32_t* counts,
                        const int32_t* offsets, const int32_t* sorted_slots, const int32_t* active,
                        const int32_t* num_active, uint16_t* h, int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k,
@@ -191,8 +204,8 @@ int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, int64_t top
   if (workspace_bytes < ws.bytes) return MX_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int t = (int)T, h = (int)H, i = (int)I, e = (int)E, k = (int)top_k;
-  if ((st = launch_route(router_logits, t, e, k, ws.ids, ws.gates, s)) != MX_OK) return st;
-  if ((st = launch_sort(ws.ids, t, k, e, ws.counts, ws.offsets, ws.sorted_slots, ws.active, ws.num_active, s)) != MX_OK)
+  if ((st = launch_route_sort(router_logits, t, e, k, ws.ids, ws.gates, ws.counts, ws.offsets, ws.sorted_slots,
+                              ws.active, ws.num_active, s)) != MX_OK)
     return st;
   const SortView sv{ws.counts, ws.offsets, ws.sorted_slots, ws.active, ws.num_active};
   if ((st = launch_gate_up(x, w_gate_up, s_gate_up, sv, ws.h, t, h, i, e, k, s)) != MX_OK) return st;

@@ -46,6 +46,10 @@ int launch_dequant(const uint8_t* w, const uint8_t* s, int64_t rows, int64_t K, 
 int launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* gates, hipStream_t stream);
 int launch_sort(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* sorted_slots,
                 int32_t* active, int32_t* num_active, hipStream_t stream);
+// route + sort in one single-workgroup launch (the layer forward's path)
+int launch_route_sort(const float* logits, int T, int E, int k, int32_t* ids, float* gates, int32_t* counts,
+                      int32_t* offsets, int32_t* sorted_slots, int32_t* active, int32_t* num_active,
+                      hipStream_t stream);
 int launch_gate_up(const uint16_t* x, const uint8_t* wgu, const uint8_t* sgu, const SortView& sv, uint16_t* h, int T,
                    int H, int I, int E, int k, hipStream_t stream);
 int launch_down(const uint16_t* h, const float* gates, const uint8_t* wd, const uint8_t* sd, const SortView& sv,

@@ -83,6 +83,10 @@ def test_route_and_sort_reject():
     assert L.moe_route_topk(P((1 << 20) + 2), 1, 8, 2, A, A, None) == MX_ERR_ALIGN
     assert L.moe_sort_by_expert(A, 1, 2, 8, A, A, A, A, None, None) == MX_ERR_NULL
     assert L.moe_sort_by_expert(A, 1, 0, 8, A, A, A, A, A, None) == MX_ERR_SHAPE
+    assert L.moe_route_sort(A, 1, 8, 2, A, A, A, A, A, A, None, None) == MX_ERR_NULL
+    assert L.moe_route_sort(A, 0, 8, 2, A, A, A, A, A, A, A, None) == MX_ERR_SHAPE
+    assert L.moe_route_sort(A, 1, 8, 9, A, A, A, A, A, A, A, None) == MX_ERR_SHAPE
+    assert L.moe_route_sort(P((1 << 20) + 2), 1, 8, 2, A, A, A, A, A, A, A, None) == MX_ERR_ALIGN
 
 
 def test_forward_rejects():

@@ -157,6 +157,35 @@ def test_sort_matches_oracle(dev, mx, T, E, k):
     assert int(r["num_active"].item()) == o["num_active"]
 
 
+# T <= 16 runs as one launch, larger T as the route and sort kernels: both paths, every
+# logits-per-lane class (E <= 256, <= 512, <= 1024) of the single launch
+ROUTE_SORT_CASES = [("moe_t4", 0), ("moe_t32_zipf", 0), ("moe_t128", 0), ("ties", 1), ("ties", 2), ("ties", 3),
+                    ("ties", 4), ("ties", 5)]
+
+
+@pytest.mark.parametrize("name,variant", ROUTE_SORT_CASES, ids=[f"{n}{v}" for n, v in ROUTE_SORT_CASES])
+def test_route_sort_matches_oracle(dev, mx, name, variant):
+    """The fused route + sort launch of the layer forward, bit-exact against the oracle's route then sort."""
+    if name != "ties":
+        cfg = synthetic.MOE_CONFIGS[name]
+        logits, k = synthetic.router_logits(cfg), cfg.k
+    else:
+        T, E, k = [(5, 64, 3), (256, 1024, 32), (40, 300, 8), (16, 1024, 32), (16, 300, 8)][variant - 1]
+        rng = np.random.default_rng(variant)
+        logits = np.round(rng.standard_normal((T, E)), 1).astype(np.float32)  # many exact ties
+        logits[0, :] = 0.0
+        logits[-1, ::2] = -0.0
+    say("route+sort", name, variant, logits.shape, k)
+    ids, gates, srt = mx.moe_route_sort(torch.from_numpy(logits).to(dev), k)
+    oids, ogates = oracle.route(logits, k)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    assert np.max(np.abs(gates.cpu().numpy().astype(np.float64) - ogates)) <= 1e-6
+    o = oracle.sort(oids, logits.shape[1])
+    for key in ("counts", "offsets", "sorted_slots", "active"):
+        assert np.array_equal(srt[key].cpu().numpy(), o[key]), key
+    assert int(srt["num_active"].item()) == o["num_active"]
+
+
 # ------------------------------------------------------------------ MoE layer
 
 def moe_device_inputs(cfg, dev, host=None):
@@ -251,3 +280,35 @@ def test_moe_deterministic_and_inactive_experts_unread(dev, mx):
         d[key][unused] = 255
     y3 = run_moe(mx, d, cfg.k)
     assert np.array_equal(y1, y3)
+
+
+def test_forward_with_tied_logits(dev, mx):
+    """The layer forward routes in its own fused kernel: exact ties (lower expert id wins)
+    and +0/-0 pairs must route as the oracle routes them."""
+    cfg = synthetic.MoEConfig("ties", T=6, H=1024, I=1024, E=16, k=4, routing="normal", e_lo=-8, e_hi=-2, seed=11)
+    host = synthetic.moe_inputs_host(cfg)
+    rng = np.random.default_rng(5)
+    logits = np.round(rng.standard_normal((cfg.T, cfg.E)), 0).astype(np.float32)  # values in a few integers
+    logits[0, :] = 0.0                    # every expert tied
+    logits[1, ::2] = -0.0                 # -0 ties +0
+    logits[1, 1::2] = 0.0
+    host["logits"] = logits
+    say("moe forward, tied logits")
+    d, x, lg = moe_device_inputs(cfg, dev, host)
+    got = run_moe(mx, d, cfg.k)
+    y, sm = oracle_moe(cfg, x, lg, host)
+    worst = check_bound(got, y, sm, MOE_REL, "tied logits")
+    say(f"  worst ratio {worst:.3g}")
+
+
+def test_forward_maximum_sizes(dev, mx):
+    """T = 256 tokens, E = 1024 experts, top-32: the largest routing the library accepts."""
+    cfg = synthetic.MoEConfig("max", T=256, H=1024, I=1024, E=1024, k=32, routing="normal", e_lo=-8, e_hi=-2, seed=2)
+    say("moe forward, T=256 E=1024 k=32")
+    d, x, logits = moe_device_inputs(cfg, dev)
+    got = run_moe(mx, d, cfg.k)
+    w_host = {k: d[k].cpu().numpy() for k in ("wgu", "sgu", "wd", "sd")}
+    tok = np.array([0, 1, 100, 254, 255], np.int32)
+    y, sm = oracle_moe(cfg, x, logits, w_host, tokens=tok)
+    worst = check_bound(got[tok], y, sm, MOE_REL, "maximum sizes")
+    say(f"  worst ratio {worst:.3g}")
