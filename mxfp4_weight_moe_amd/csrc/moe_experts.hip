@@ -6,12 +6,12 @@
 // combine was slower for the MX formats.  So: two GEMM kernels with fused epilogues, no
 // float atomics.
 //
-//   gate_up: item = (row group of an active expert, 64 intermediate columns).  Each of the
-//            4 wavefronts of a workgroup streams 16 gate rows and the 16 matching up rows
-//            over all H, then applies SwiGLU and rounds h to bf16.  h rows are stored in
-//            sorted-slot order.
-//   down:    item = (row group of an active expert, 128 output columns, 32 per wave);
-//            stores the fp32 down outputs per flat slot.
+//   gate_up: item = (row group of an active expert, 4 tiles of intermediate columns).
+//            Each of the 4 wavefronts of a workgroup streams the gate rows and the matching
+//            up rows of its tile (16 + 16, or 8 + 8 for half-width tiles) over all H, then
+//            applies SwiGLU and rounds h to bf16.  h rows are stored in sorted-slot order.
+//   down:    item = (row group of an active expert, 4 tiles of 32 output columns, or 16
+//            for half-width tiles); stores the fp32 down outputs per flat slot.
 //   combine: y[t,:] = bf16(sum_j fl32(gate[t,j] * d[t*k + j,:])), j ascending.
 //
 // A row group is up to 16 of the expert's routed rows (one MFMA m-tile); experts with more
@@ -94,8 +94,16 @@ struct ExpertItems {
 
 // ------------------------------------------------------------------ gate_up + SwiGLU
 
+// NS = 2: a wave's tile is 16 intermediate columns: subtile 0 = their 16 gate rows,
+//         subtile 1 = the 16 matching up rows.
+// NS = 1: a wave's tile is 8 intermediate columns: one subtile of their 8 gate rows
+//         (rows 0-7) and the 8 matching up rows (rows 8-15).  The MFMA result rows 8-15 sit
+//         in lanes 32-63, so one lane swap brings each up value beside its gate value.
+// Half-width tiles double the waves streaming a launch with few items (small T).
+template <int NS_>
 struct GateUpPolicy : ExpertItems {
-  static constexpr int NS = 2;
+  static constexpr int NS = NS_;
+  static constexpr int TILE = NS == 2 ? SUB_ROWS : SUB_ROWS / 2;  // intermediate columns per wave
   struct EpiState {
     int hrow;  // h row of the group's first row
     int rows;  // valid rows in the group
@@ -115,34 +123,49 @@ struct GateUpPolicy : ExpertItems {
     const uint32_t slot = (uint32_t)ld_uniform(sv.sorted_slots, f.row0 + m);
     return (int)(((uint64_t)slot * kinv) >> 24) * H;
   }
+  // weight row of row r (0..15) of subtile i of this wave's tile
+  __device__ __forceinline__ int wrow(const ItemInfo& f, int wave, int i, int r) const {
+    const int n0 = (f.tile0 + wave) * TILE;
+    if (NS == 2) return (i ? I : 0) + n0 + r;
+    return (r < 8) ? n0 + r : I + n0 + r - 8;
+  }
   __device__ __forceinline__ void w_setup(const ItemInfo& f, int wave, WCursor<NS>& c, int lane) const {
     const uint8_t* we = wgu + (size_t)f.e * e_codes;
     const size_t kb = (size_t)H >> 1;
-    const int n0 = (f.tile0 + wave) * SUB_ROWS;
-    for (int q = 0; q < 2; ++q) {
-      const int r = n0 + (lane >> 3) + 8 * q;
-      c.w[0][q] = we + (size_t)r * kb + (lane & 7) * 16;        // gate rows
-      c.w[1][q] = we + (size_t)(I + r) * kb + (lane & 7) * 16;  // up rows
-    }
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        c.w[i][q] = we + (size_t)wrow(f, wave, i, (lane >> 3) + 8 * q) * kb + (lane & 7) * 16;
   }
-  // subtile 0: gate row n0 + r; subtile 1: the matching up row I + n0 + r
   __device__ __forceinline__ const uint8_t* scale_row(const ItemInfo& f, int wave, int i, int r) const {
-    const int n = (f.tile0 + wave) * SUB_ROWS + r + (i ? I : 0);
-    return sgu + (size_t)f.e * e_scales + (size_t)n * (H >> 5);
+    return sgu + (size_t)f.e * e_scales + (size_t)wrow(f, wave, i, r) * (H >> 5);
   }
   __device__ __forceinline__ void c_setup(const ItemInfo& f, int wave, EpiState& s, int) const {
     s.hrow = f.row0;
     s.rows = f.rows;
-    s.n0 = (f.tile0 + wave) * SUB_ROWS;
+    s.n0 = (f.tile0 + wave) * TILE;
   }
+  // MFMA result: lane l holds rows 4 (l >> 4) + 0..3 of the tile for token row l & 15.
   __device__ __forceinline__ void epilogue(const EpiState& s, const f32x4 (&acc)[NS], int lane) const {
     const int r = lane & 15;
-    if (r >= s.rows) return;
+    float g[4], u[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      g[i] = acc[0][i];
+      if (NS == 2) {
+        u[i] = acc[1][i];
+      } else {
+        const uint32_t b = __float_as_uint(acc[0][i]);
+        u[i] = __uint_as_float(__builtin_amdgcn_permlane32_swap(b, b, false, false)[1]);  // lane l <- lane l + 32
+      }
+    }
+    if (r >= s.rows || (NS == 1 && lane >= 32)) return;
     uint32_t o[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const uint16_t a = f32_to_bf16_rne(silu_mul(acc[0][2 * j], acc[1][2 * j]));
-      const uint16_t b = f32_to_bf16_rne(silu_mul(acc[0][2 * j + 1], acc[1][2 * j + 1]));
+      const uint16_t a = f32_to_bf16_rne(silu_mul(g[2 * j], u[2 * j]));
+      const uint16_t b = f32_to_bf16_rne(silu_mul(g[2 * j + 1], u[2 * j + 1]));
       o[j] = (uint32_t)a | ((uint32_t)b << 16);
     }
     *reinterpret_cast<u32x2*>(h + (size_t)(s.hrow + r) * I + s.n0 + 4 * (lane >> 4)) = u32x2{o[0], o[1]};
@@ -151,8 +174,11 @@ struct GateUpPolicy : ExpertItems {
 
 // ------------------------------------------------------------------ down
 
+// A wave's tile is NS x 16 output columns (subtile i = columns n0 + 16 i ... + 15).
+template <int NS_>
 struct DownPolicy : ExpertItems {
-  static constexpr int NS = 2;
+  static constexpr int NS = NS_;
+  static constexpr int TILE = NS * SUB_ROWS;  // output columns per wave
   struct EpiState {
     int slot;  // flat slot of this lane's row, -1 if the row is past the group
     int n0;    // first output column of this wave's tile
@@ -168,18 +194,19 @@ struct DownPolicy : ExpertItems {
   __device__ __forceinline__ void w_setup(const ItemInfo& f, int wave, WCursor<NS>& c, int lane) const {
     const uint8_t* we = wd + (size_t)f.e * e_codes;
     const size_t kb = (size_t)I >> 1;
-    const int n0 = (f.tile0 + wave) * 32;
+    const int n0 = (f.tile0 + wave) * TILE;
+#pragma unroll
     for (int i = 0; i < NS; ++i)
+#pragma unroll
       for (int q = 0; q < 2; ++q) c.w[i][q] = we + (size_t)(n0 + 16 * i + (lane >> 3) + 8 * q) * kb + (lane & 7) * 16;
   }
-  // subtile i: output rows n0 + 16 i .. n0 + 16 i + 15
   __device__ __forceinline__ const uint8_t* scale_row(const ItemInfo& f, int wave, int i, int r) const {
-    const int n = (f.tile0 + wave) * 32 + SUB_ROWS * i + r;
+    const int n = (f.tile0 + wave) * TILE + SUB_ROWS * i + r;
     return sd + (size_t)f.e * e_scales + (size_t)n * (I >> 5);
   }
   __device__ __forceinline__ void c_setup(const ItemInfo& f, int wave, EpiState& s, int lane) const {
     s.slot = group_slot(sv.sorted_slots, f.row0, f.rows, lane);
-    s.n0 = (f.tile0 + wave) * 32;
+    s.n0 = (f.tile0 + wave) * TILE;
   }
   __device__ __forceinline__ void epilogue(const EpiState& s, const f32x4 (&acc)[NS], int lane) const {
     if (s.slot < 0) return;
@@ -191,8 +218,7 @@ struct DownPolicy : ExpertItems {
 
 // ------------------------------------------------------------------ kernels
 
-
-
+template <int NS>
 __global__ void __launch_bounds__(WG_WAVES * 64) moe_gate_up_kernel(const uint16_t* __restrict__ x,
                                                                     const uint8_t* __restrict__ wgu,
                                                                     const uint8_t* __restrict__ sgu, SortView sv,
@@ -200,16 +226,17 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_gate_up_kernel(const uint16
                                                                     int gmax) {
   __shared__ __attribute__((aligned(16))) uint8_t xbufs[2 * XCHUNK_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t slabs[WG_WAVES][SLAB_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t sslabs[WG_WAVES][sslab_bytes<2>()];
+  __shared__ __attribute__((aligned(16))) uint8_t sslabs[WG_WAVES][sslab_bytes<NS>()];
   __shared__ uint32_t xctr[2];
   if (threadIdx.x < 2) xctr[threadIdx.x] = 0u;
   __syncthreads();
   // wave index as a scalar, so every per-item quantity derived from it stays uniform
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  GateUpPolicy p;
+  using P = GateUpPolicy<NS>;
+  P p;
   p.sv = sv;
   p.nseg = H / SEG_K;
-  p.nquad = I / (SUB_ROWS * WG_WAVES);
+  p.nquad = I / (P::TILE * WG_WAVES);
   p.na = ld_uniform(sv.num_active, 0);
   p.n_items = gmax * p.na * p.nquad;
   p.xact = x;
@@ -222,25 +249,26 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_gate_up_kernel(const uint16
   p.kinv = ((1u << 24) + (uint32_t)k - 1u) / (uint32_t)k;
   p.e_codes = (size_t)2 * I * (H / 2);
   p.e_scales = (size_t)2 * I * (H / 32);
-  static_assert(GateUpPolicy::NS == 2, "scale slab size");
-  stream_items<GateUpPolicy, GU_SPS>(p, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
+  stream_items<P, GU_SPS>(p, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
 }
 
+template <int NS>
 __global__ void __launch_bounds__(WG_WAVES * 64) moe_down_kernel(const uint16_t* __restrict__ h,
                                                                  const uint8_t* __restrict__ wd,
                                                                  const uint8_t* __restrict__ sd, SortView sv,
                                                                  float* __restrict__ dpart, int H, int I, int gmax) {
   __shared__ __attribute__((aligned(16))) uint8_t xbufs[2 * XCHUNK_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t slabs[WG_WAVES][SLAB_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t sslabs[WG_WAVES][sslab_bytes<2>()];
+  __shared__ __attribute__((aligned(16))) uint8_t sslabs[WG_WAVES][sslab_bytes<NS>()];
   __shared__ uint32_t xctr[2];
   if (threadIdx.x < 2) xctr[threadIdx.x] = 0u;
   __syncthreads();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  DownPolicy p;
+  using P = DownPolicy<NS>;
+  P p;
   p.sv = sv;
   p.nseg = I / SEG_K;
-  p.nquad = H / (32 * WG_WAVES);
+  p.nquad = H / (P::TILE * WG_WAVES);
   p.na = ld_uniform(sv.num_active, 0);
   p.n_items = gmax * p.na * p.nquad;
   p.xact = h;
@@ -251,8 +279,7 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_down_kernel(const uint16_t*
   p.I = I;
   p.e_codes = (size_t)H * (I / 2);
   p.e_scales = (size_t)H * (I / 32);
-  static_assert(DownPolicy::NS == 2, "scale slab size");
-  stream_items<DownPolicy, DN_SPS>(p, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
+  stream_items<P, DN_SPS>(p, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
 }
 
 // One thread per (token, 4 consecutive outputs): fp32 sum of the gate-weighted slots, j ascending.
@@ -291,25 +318,49 @@ static int expert_grid(int64_t max_items, int wgs_per_cu) {
 static int64_t max_active(int T, int E, int k) { return (int64_t)T * k < E ? (int64_t)T * k : E; }
 static int row_groups(int T) { return (T + 15) / 16; }
 
+// Full-width tiles unless they would leave resident workgroup slots idle (few active
+// experts and row groups, i.e. small T) and half-width tiles, twice the items, still fit in
+// one round of the slots: then half-width tiles, twice the waves.
+template <class K2, class K1>
+static bool use_half_tiles(K2 k2, K1 k1, int64_t items_full, int& grid) {
+  static const int occ2 = resident_wgs_per_cu(k2, WG_WAVES * 64);
+  static const int occ1 = resident_wgs_per_cu(k1, WG_WAVES * 64);
+  if (2 * items_full > (int64_t)device_cu_count() * occ1) {
+    grid = expert_grid(items_full, occ2);
+    return false;
+  }
+  grid = expert_grid(2 * items_full, occ1);
+  return true;
+}
+
 int launch_gate_up(const uint16_t* x, const uint8_t* wgu, const uint8_t* sgu, const SortView& sv, uint16_t* h, int T,
                    int H, int I, int E, int k, hipStream_t stream) {
   if (H % (SEG_K * GU_SPS) != 0 || H % (SEG_K * SRUN) != 0 || I % (SUB_ROWS * WG_WAVES) != 0) return MX_ERR_SHAPE;
-  static const int occ = resident_wgs_per_cu(moe_gate_up_kernel, WG_WAVES * 64);
   const int gmax = row_groups(T);
-  const int grid = expert_grid((int64_t)gmax * max_active(T, E, k) * (I / (SUB_ROWS * WG_WAVES)), occ);
-  hipLaunchKernelGGL(moe_gate_up_kernel, dim3(grid), dim3(WG_WAVES * 64), 0, stream, x, wgu, sgu, sv, h, H, I, k,
-                     gmax);
+  const int64_t items_full = (int64_t)gmax * max_active(T, E, k) * (I / (GateUpPolicy<2>::TILE * WG_WAVES));
+  int grid = 0;
+  if (use_half_tiles(moe_gate_up_kernel<2>, moe_gate_up_kernel<1>, items_full, grid))
+    hipLaunchKernelGGL(moe_gate_up_kernel<1>, dim3(grid), dim3(WG_WAVES * 64), 0, stream, x, wgu, sgu, sv, h, H, I, k,
+                       gmax);
+  else
+    hipLaunchKernelGGL(moe_gate_up_kernel<2>, dim3(grid), dim3(WG_WAVES * 64), 0, stream, x, wgu, sgu, sv, h, H, I, k,
+                       gmax);
   return hip_status(hipGetLastError());
 }
 
 int launch_down(const uint16_t* h, const float* gates, const uint8_t* wd, const uint8_t* sd, const SortView& sv,
                 float* dpart, int T, int H, int I, int E, int k, hipStream_t stream) {
   (void)gates;  // applied by the combine
-  if (I % (SEG_K * DN_SPS) != 0 || I % (SEG_K * SRUN) != 0 || H % (32 * WG_WAVES) != 0) return MX_ERR_SHAPE;
-  static const int occ = resident_wgs_per_cu(moe_down_kernel, WG_WAVES * 64);
+  if (I % (SEG_K * DN_SPS) != 0 || I % (SEG_K * SRUN) != 0 || H % (2 * SUB_ROWS * WG_WAVES) != 0) return MX_ERR_SHAPE;
   const int gmax = row_groups(T);
-  const int grid = expert_grid((int64_t)gmax * max_active(T, E, k) * (H / (32 * WG_WAVES)), occ);
-  hipLaunchKernelGGL(moe_down_kernel, dim3(grid), dim3(WG_WAVES * 64), 0, stream, h, wd, sd, sv, dpart, H, I, gmax);
+  const int64_t items_full = (int64_t)gmax * max_active(T, E, k) * (H / (DownPolicy<2>::TILE * WG_WAVES));
+  int grid = 0;
+  if (use_half_tiles(moe_down_kernel<2>, moe_down_kernel<1>, items_full, grid))
+    hipLaunchKernelGGL(moe_down_kernel<1>, dim3(grid), dim3(WG_WAVES * 64), 0, stream, h, wd, sd, sv, dpart, H, I,
+                       gmax);
+  else
+    hipLaunchKernelGGL(moe_down_kernel<2>, dim3(grid), dim3(WG_WAVES * 64), 0, stream, h, wd, sd, sv, dpart, H, I,
+                       gmax);
   return hip_status(hipGetLastError());
 }
 

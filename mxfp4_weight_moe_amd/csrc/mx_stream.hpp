@@ -54,10 +54,12 @@ constexpr int SRUN = 4;
 constexpr int SRUN_ROW_BYTES = SRUN * SEG_SCALES;         // one row's scales of a run
 constexpr int SLANES_PER_ROW = SRUN_ROW_BYTES / 16;       // lanes loading one row
 constexpr int SROWS_PER_LOAD = 64 / SLANES_PER_ROW;       // rows one wave load covers
+// A wave's NS x 16 rows need scale_loads() loads; the last one may cover fewer rows than a
+// full load (16 rows: half the lanes), its other lanes repeat rows and do not store.
 template <int NS>
 constexpr int scale_loads() {
-  static_assert((NS * SUB_ROWS) % SROWS_PER_LOAD == 0, "whole scale loads per run");
-  return NS * SUB_ROWS / SROWS_PER_LOAD;
+  static_assert((NS * SUB_ROWS) % SROWS_PER_LOAD == 0 || NS * SUB_ROWS < SROWS_PER_LOAD, "whole scale loads");
+  return (NS * SUB_ROWS + SROWS_PER_LOAD - 1) / SROWS_PER_LOAD;
 }
 template <int NS>
 constexpr int sslab_bytes() {
@@ -109,7 +111,8 @@ __device__ __forceinline__ void srun_store(uint8_t* __restrict__ sslab, const u3
                                            int lane) {
 #pragma unroll
   for (int k = 0; k < scale_loads<NS>(); ++k)
-    *reinterpret_cast<u32x4*>(sslab + k * (64 * 16) + lane * 16) = sreg[k];
+    if (k * 64 + lane < NS * SUB_ROWS * SLANES_PER_ROW)
+      *reinterpret_cast<u32x4*>(sslab + k * (64 * 16) + lane * 16) = sreg[k];
 }
 
 // What the kernels need of an item; all fields are uniform across the workgroup.
@@ -300,7 +303,7 @@ __device__ __forceinline__ void stream_items(P& p, uint8_t* __restrict__ xbufs, 
     p.w_setup(f, wave, cw, lane);
 #pragma unroll
     for (int k = 0; k < SL; ++k) {
-      const int rho = k * SROWS_PER_LOAD + lane / SLANES_PER_ROW;
+      const int rho = (k * SROWS_PER_LOAD + lane / SLANES_PER_ROW) % (NS * SUB_ROWS);
       cw.sr[k] = p.scale_row(f, wave, rho / SUB_ROWS, rho % SUB_ROWS) + (lane % SLANES_PER_ROW) * 16;
     }
   };
@@ -333,6 +336,10 @@ __device__ __forceinline__ void stream_items(P& p, uint8_t* __restrict__ xbufs, 
     ok = false;
     return ch;
   };
+  // The first weight step and scale run are requested before anything else, so that the
+  // first compute waits for one memory round trip, not for the chunk hand-off as well.
+  wring_load(rw, cw);
+  srun_load<NS>(sreg, cw);
   u32x4 xv[XROUNDS];
   XChunk cur = chunk_of(first, 0);
   xchunk_load(p, cur, xv, tid);
@@ -340,17 +347,13 @@ __device__ __forceinline__ void stream_items(P& p, uint8_t* __restrict__ xbufs, 
   xready_publish(&xctr[0]);
   int xb = 0;                  // LDS buffer holding `cur`
   uint32_t gen[2] = {1u, 0u};  // chunks published so far into each buffer
-  xready_wait(&xctr[0], WG_THREADS);
-  srun_load<NS>(sreg, cw);  // the first run's scales
+  srun_store<NS>(sslab, sreg, lane);
+  advance_w();
+  if (cw.seg % SRUN == 0) srun_load<NS>(sreg, cw);
   bool have_next;
   XChunk nxt = next_chunk(cur, have_next);
   if (have_next) xchunk_load(p, nxt, xv, tid);
-  // The first weight step is requested after the next chunk's activation loads, so the
-  // wait before their LDS store never drains the weight stream.
-  wring_load(rw, cw);
-  advance_w();
-  srun_store<NS>(sslab, sreg, lane);
-  if (cw.seg % SRUN == 0) srun_load<NS>(sreg, cw);
+  xready_wait(&xctr[0], WG_THREADS);
 
   // ---- compute cursor
   int cseg = 0;
