@@ -69,12 +69,18 @@ constexpr int GU_SPS = 2;  // gate_up: 28 segments per item at H = 7168
 constexpr int DN_SPS = 2;  // down: 8 segments per item at I = 2048
 constexpr int CHUNK_ALIGN = GU_SPS > DN_SPS ? GU_SPS : DN_SPS;
 static_assert(CHUNK_ALIGN % GU_SPS == 0 && CHUNK_ALIGN % DN_SPS == 0, "chunks must end on steps");
-static_assert(SUB_ROWS * CHUNK_ALIGN <= XCHUNK_ROWSEGS, "a chunk must hold one step of a full row group");
+// Activation chunk buffers: gate_up keeps 2 workgroups per CU with 32 KB chunks; down's
+// items are short (I / 256 segments) and run 3 workgroups per CU with 16 KB chunks.
+constexpr int GU_XCHUNK = 32768;
+constexpr int DN_XCHUNK = 16384;
+static_assert(SUB_ROWS * CHUNK_ALIGN <= XGeom<GU_XCHUNK>::ROWSEGS && SUB_ROWS * CHUNK_ALIGN <= XGeom<DN_XCHUNK>::ROWSEGS,
+              "a chunk must hold one step of a full row group");
 
 // Fields shared by both expert GEMMs: the work list over (row group, expert, tile quad).
 struct ExpertItems {
   SortView sv;
   int nseg, n_items, nquad, na;
+  int xrowsegs;  // row-segments per activation chunk
 
   __device__ __forceinline__ bool valid(int it) const {
     const ItemIndex ix = item_decode(it, nquad, na);
@@ -87,7 +93,7 @@ struct ExpertItems {
     f.rows = min(16, ld_uniform(sv.counts, f.e) - ix.g * 16);
     f.row0 = ld_uniform(sv.offsets, f.e) + ix.g * 16;
     f.tile0 = ix.quad * WG_WAVES;
-    f.cs = chunk_segments(f.rows, nseg, CHUNK_ALIGN);
+    f.cs = chunk_segments(f.rows, nseg, CHUNK_ALIGN, xrowsegs);
     return f;
   }
 };
@@ -103,6 +109,7 @@ struct ExpertItems {
 template <int NS_>
 struct GateUpPolicy : ExpertItems {
   static constexpr int NS = NS_;
+  static constexpr int XCHUNK = GU_XCHUNK;
   static constexpr int TILE = NS == 2 ? SUB_ROWS : SUB_ROWS / 2;  // intermediate columns per wave
   struct EpiState {
     int hrow;  // h row of the group's first row
@@ -178,6 +185,7 @@ struct GateUpPolicy : ExpertItems {
 template <int NS_>
 struct DownPolicy : ExpertItems {
   static constexpr int NS = NS_;
+  static constexpr int XCHUNK = DN_XCHUNK;
   static constexpr int TILE = NS * SUB_ROWS;  // output columns per wave
   struct EpiState {
     int slot;  // flat slot of this lane's row, -1 if the row is past the group
@@ -224,7 +232,8 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_gate_up_kernel(const uint16
                                                                     const uint8_t* __restrict__ sgu, SortView sv,
                                                                     uint16_t* __restrict__ h, int H, int I, int k,
                                                                     int gmax) {
-  __shared__ __attribute__((aligned(16))) uint8_t xbufs[2 * XCHUNK_BYTES];
+  using P = GateUpPolicy<NS>;
+  __shared__ __attribute__((aligned(16))) uint8_t xbufs[2 * P::XCHUNK];
   __shared__ __attribute__((aligned(16))) uint8_t slabs[WG_WAVES][SLAB_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t sslabs[WG_WAVES][sslab_bytes<NS>()];
   __shared__ uint32_t xctr[2];
@@ -232,8 +241,8 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_gate_up_kernel(const uint16
   __syncthreads();
   // wave index as a scalar, so every per-item quantity derived from it stays uniform
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  using P = GateUpPolicy<NS>;
   P p;
+  p.xrowsegs = XGeom<P::XCHUNK>::ROWSEGS;
   p.sv = sv;
   p.nseg = H / SEG_K;
   p.nquad = I / (P::TILE * WG_WAVES);
@@ -257,15 +266,16 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_down_kernel(const uint16_t*
                                                                  const uint8_t* __restrict__ wd,
                                                                  const uint8_t* __restrict__ sd, SortView sv,
                                                                  float* __restrict__ dpart, int H, int I, int gmax) {
-  __shared__ __attribute__((aligned(16))) uint8_t xbufs[2 * XCHUNK_BYTES];
+  using P = DownPolicy<NS>;
+  __shared__ __attribute__((aligned(16))) uint8_t xbufs[2 * P::XCHUNK];
   __shared__ __attribute__((aligned(16))) uint8_t slabs[WG_WAVES][SLAB_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t sslabs[WG_WAVES][sslab_bytes<NS>()];
   __shared__ uint32_t xctr[2];
   if (threadIdx.x < 2) xctr[threadIdx.x] = 0u;
   __syncthreads();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  using P = DownPolicy<NS>;
   P p;
+  p.xrowsegs = XGeom<P::XCHUNK>::ROWSEGS;
   p.sv = sv;
   p.nseg = I / SEG_K;
   p.nquad = H / (P::TILE * WG_WAVES);

@@ -19,9 +19,9 @@
 //             a seventh of the kernel's time.
 //   acts      the activation rows of an item are staged in LDS, chunk by chunk, shared
 //             by the 4 waves.  A chunk holds CS segments of the item's R rows, with
-//             CS = XCHUNK_ROWSEGS / R rounded down to a multiple of SPS (at least SPS), so a
-//             chunk fits XCHUNK_BYTES, is loaded by XROUNDS rounds of 16-byte loads of
-//             the 256 threads, and ends on a step.  The loads of chunk i+1 are issued when
+//             CS = (row-segments per chunk) / R rounded down to a multiple of SPS (at least
+//             SPS), so a chunk fits the kernel's chunk buffer, is loaded by whole rounds of
+//             16-byte loads of the 256 threads, and ends on a step.  The loads of chunk i+1 are issued when
 //             chunk i starts and written to the other LDS buffer when it ends; LDS counters
 //             hand it over.
 //
@@ -37,16 +37,23 @@ constexpr int WG_WAVES = 4;
 // sched_barrier mask: ALU, VALU, SALU, MFMA, all DS and transcendental instructions may be
 // scheduled across; vector memory instructions may not
 constexpr int SCHED_ALL_BUT_VMEM = 0x1 | 0x2 | 0x4 | 0x8 | 0x80 | 0x100 | 0x200 | 0x400;
-constexpr int XCHUNK_BYTES = 32768;  // one activation chunk: R rows x CS segments x 512 B
-constexpr int XPIECES = XCHUNK_BYTES / 16;
-constexpr int XROUNDS = XPIECES / (WG_WAVES * 64);
-constexpr int XCHUNK_ROWSEGS = XCHUNK_BYTES / (SEG_K * 2);  // row-segments a chunk holds
+// Activation chunk geometry for a chunk buffer of BYTES (one of two per workgroup):
+// R rows x CS segments x 512 B, loaded in ROUNDS rounds of one 16-byte piece per thread.
+template <int BYTES>
+struct XGeom {
+  static constexpr int PIECES = BYTES / 16;
+  static constexpr int ROUNDS = PIECES / (WG_WAVES * 64);
+  static constexpr int ROWSEGS = BYTES / (SEG_K * 2);  // row-segments a chunk holds
+  static_assert(ROUNDS * WG_WAVES * 64 == PIECES, "whole rounds");
+  static_assert(ROWSEGS <= 64, "the reciprocal quotient below is exact only below 64 row-segments");
+};
 
-// Activation chunk length, in segments, for a group of `rows` rows: as many segments as fit,
-// a multiple of `align` (the weight step, so chunks end on steps), and at least one step.
-__host__ __device__ constexpr int chunk_segments(int rows, int nseg, int align) {
-  return (XCHUNK_ROWSEGS / rows / align * align) < align ? align
-         : ((XCHUNK_ROWSEGS / rows / align * align) < nseg ? XCHUNK_ROWSEGS / rows / align * align : nseg);
+// Activation chunk length, in segments, for a group of `rows` rows in a chunk of `rowsegs`
+// row-segments: as many segments as fit, a multiple of `align` (the weight step, so chunks
+// end on steps), and at least one step.
+__host__ __device__ constexpr int chunk_segments(int rows, int nseg, int align, int rowsegs) {
+  return (rowsegs / rows / align * align) < align ? align
+         : ((rowsegs / rows / align * align) < nseg ? rowsegs / rows / align * align : nseg);
 }
 
 // Scale staging: runs of SRUN segments (an item's segment count must be a multiple).
@@ -165,16 +172,15 @@ __device__ __forceinline__ void xready_wait(const uint32_t* ctr, uint32_t target
   __asm__ volatile("" ::: "memory");
 }
 
-// Row-segment rs (< XCHUNK_ROWSEGS) of a chunk with R rows is segment rs / R, row rs % R.
+// Row-segment rs (< 64) of a chunk with R rows is segment rs / R, row rs % R.
 // The quotient is (rs * ceil(2^16 / R)) >> 16, exact for rs < 64 and R <= 16.
-static_assert(XCHUNK_ROWSEGS <= 64, "the reciprocal quotient is exact only below 64 row-segments");
 __device__ __forceinline__ uint32_t rows_reciprocal(int R) { return (65536u + (uint32_t)R - 1u) / (uint32_t)R; }
 
 // Issue the activation loads of chunk `ch`: XROUNDS rounds of one 16-byte piece per thread
 // (threads past the chunk repeat its last piece; skipping the unneeded rounds costs more
 // registers than the loads it saves).  Lane m < 16 holds row m's element offset, and each
 // thread fetches its row's offset from there with one cross-lane read.
-template <class P>
+template <int XROUNDS, class P>
 __device__ __forceinline__ void xchunk_load(const P& p, const XChunk& ch, u32x4 (&xv)[XROUNDS], int tid) {
   const int R = ch.info.rows;
   const int npieces = R * ch.ns * 32;
@@ -195,6 +201,7 @@ __device__ __forceinline__ void xchunk_load(const P& p, const XChunk& ch, u32x4 
   }
 }
 
+template <int XROUNDS>
 __device__ __forceinline__ void xchunk_store(uint8_t* __restrict__ buf, const XChunk& ch, const u32x4 (&xv)[XROUNDS],
                                              int tid) {
   const int R = ch.info.rows;
@@ -269,7 +276,8 @@ __device__ __forceinline__ void segment_compute(u32x4 (&w)[NS][2], const uint8_t
 //   const uint8_t* scale_row(const ItemInfo&, int wave, int i, int r) -- scales of row r of subtile i
 //   EpiState;  void c_setup(const ItemInfo&, int wave, EpiState&, int lane)
 //   void epilogue(const EpiState&, const f32x4 (&acc)[NS], int lane)
-// `xbufs` is 2 * XCHUNK_BYTES of LDS, `xctr` 2 zeroed LDS counters, `slab` this wave's
+//   static constexpr int XCHUNK;                    -- bytes of one activation chunk buffer
+// `xbufs` is 2 * P::XCHUNK bytes of LDS, `xctr` 2 zeroed LDS counters, `slab` this wave's
 // SLAB_BYTES and `sslab` its sslab_bytes<NS>() of LDS.  nseg must be a multiple of SPS and
 // of SRUN (the launchers check it).
 template <class P, int SPS>
@@ -278,6 +286,8 @@ __device__ __forceinline__ void stream_items(P& p, uint8_t* __restrict__ xbufs, 
                                              int lane) {
   constexpr int NS = P::NS;
   constexpr int SL = scale_loads<NS>();
+  constexpr int XCHUNK_BYTES = P::XCHUNK;
+  constexpr int XROUNDS = XGeom<XCHUNK_BYTES>::ROUNDS;
   static_assert(SRUN % SPS == 0, "scale runs end on steps");
   const int tid = wave * 64 + lane;
   const int wg = blockIdx.x, n_wg = gridDim.x;
