@@ -312,3 +312,24 @@ def test_forward_maximum_sizes(dev, mx):
     y, sm = oracle_moe(cfg, x, logits, w_host, tokens=tok)
     worst = check_bound(got[tok], y, sm, MOE_REL, "maximum sizes")
     say(f"  worst ratio {worst:.3g}")
+
+
+@pytest.mark.parametrize("shape", [dict(T=3, H=1024, I=1024, E=8, k=2), dict(T=20, H=2048, I=1024, E=16, k=4)],
+                         ids=["T3", "T20"])
+def test_stage_hooks_match_forward(dev, mx, shape):
+    """The stage entry points (route_sort, gate_up_swiglu, down_combine) called one after another give
+    the forward's y bit for bit, and both match the oracle."""
+    cfg = synthetic.MoEConfig("hooks", routing="normal", e_lo=-8, e_hi=-2, seed=shape["T"] * 7, **shape)
+    host = synthetic.moe_inputs_host(cfg)
+    say("stage hooks vs forward", shape)
+    d, x, logits = moe_device_inputs(cfg, dev, host)
+    y_fwd = run_moe(mx, d, cfg.k)
+    ids, gates, srt = mx.moe_route_sort(d["logits"], cfg.k)
+    h = mx.moe_gate_up_swiglu(d["x"], d["wgu"], d["sgu"], srt, cfg.k)
+    y = mx.moe_down_combine(h, gates, d["wd"], d["sd"], srt, cfg.T, cfg.k)
+    torch.cuda.synchronize()
+    y_hooks = to_host_bits(y)
+    assert np.array_equal(y_hooks, y_fwd)
+    yo, sm = oracle_moe(cfg, x, logits, host)
+    worst = check_bound(y_hooks, yo, sm, MOE_REL, f"hooks {shape}")
+    say(f"  worst ratio {worst:.3g}")
