@@ -51,6 +51,8 @@ def parse():
                     help="moe_t4 | moe_t32_zipf | moe_t128 | moe_sweep_t<T>")
     ap.add_argument("--layers", type=int, default=4, help="distinct layers cycled by the steps")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replay")
+    ap.add_argument("--persistent", action="store_true",
+                    help="time the single-launch layer (moe_mxfp4_forward_persistent, T <= 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32, help="tokens of the oracle's timed sample")
     ap.add_argument("--stage-steps", type=int, default=None, help="steps of the per-kernel event pass (default K)")
@@ -121,6 +123,8 @@ def main():
     torch.cuda.set_device(dev)
     cfg = workload_config(args.workload)
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    if args.persistent and (T > 16 or T * k > 128):
+        raise SystemExit("--persistent takes T <= 16 and T * top_k <= 128")
     L = max(1, args.layers)
 
     def log(*a):
@@ -149,7 +153,7 @@ def main():
                active=torch.empty(E, dtype=torch.int32, device=dev),
                num_active=torch.empty(1, dtype=torch.int32, device=dev))
     h = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
-    names = ("route_sort", "gate_up", "down_combine")
+    names = ("layer",) if args.persistent else ("route_sort", "gate_up", "down_combine")
     n_active = []
     for lay in layers:
         mx.moe_route_sort(lay["logits"], k, ids=ids, gates=gates, out=srt)
@@ -158,11 +162,17 @@ def main():
 
     def forward(lay):
         w = lay["w"]
-        mx.moe_mxfp4_forward(lay["x"], lay["logits"], k, w["wgu"], w["sgu"], w["wd"], w["sd"], out=lay["y"], ws=ws)
+        mx.moe_mxfp4_forward(lay["x"], lay["logits"], k, w["wgu"], w["sgu"], w["wd"], w["sd"], out=lay["y"], ws=ws,
+                             persistent=args.persistent)
 
     def staged(i, e, stream):
         lay = layers[i % L]
         w = lay["w"]
+        if args.persistent:  # one kernel per layer
+            e[0].record(stream)
+            forward(lay)
+            e[1].record(stream)
+            return
         e[0].record(stream)
         mx.moe_route_sort(lay["logits"], k, ids=ids, gates=gates, out=srt)
         e[1].record(stream)
@@ -244,18 +254,23 @@ def main():
     mean_layer_bytes = float(np.mean([layer_bytes[i % L] for i in range(K)]))
     us_per_layer = ms_per_step * 1e3
     eff_gbps = mean_layer_bytes / (us_per_layer * 1e-6) / 1e9
-    # gate_up per launch: its experts' codes + scales, x read once, h written
-    gu_bytes = [n_active[i % L] * gu_expert + T * H * 2 + T * k * I * 2 for i in range(KS)]
-    gu_ms = stage_ms["gate_up"]
+    if args.persistent:
+        # the single kernel reads the whole layer's bytes
+        gu_bytes = [layer_bytes[i % L] for i in range(KS)]
+        gu_ms = stage_ms["layer"]
+    else:
+        # gate_up per launch: its experts' codes + scales, x read once, h written
+        gu_bytes = [n_active[i % L] * gu_expert + T * H * 2 + T * k * I * 2 for i in range(KS)]
+        gu_ms = stage_ms["gate_up"]
     gu_achieved = float(np.sum(gu_bytes) / (np.sum(gu_ms) * 1e-3) / 1e9)
     roofline = {
-        "kernel": "moe_gate_up_kernel",
+        "kernel": "moe_fused_kernel" if args.persistent else "moe_gate_up_kernel",
         "bound": "hbm",
         "achieved": round(gu_achieved, 1),
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
         "frac": round(gu_achieved / HBM_PEAK_GBPS, 4),
-        "traffic": measured_traffic(cfg.name),
+        "traffic": None if args.persistent else measured_traffic(cfg.name),
         "avg_launch_us": round(float(np.mean(gu_ms)) * 1e3, 2),
         "launches": len(gu_ms),
         "timing": "HIP events on the launch stream, one pair per launch, right after the timed region",
@@ -304,6 +319,7 @@ def main():
             "workload": cfg.name, "T": T, "H": H, "I": I, "E": E, "top_k": k, "routing": cfg.routing,
             "weights": "MXFP4 (E2M1 codes, E8M0 scale per 32)", "accumulate": "fp32",
             "layers_cycled": L, "timing": "eager launches" if args.eager else "HIP graph replay",
+            "path": "one persistent launch" if args.persistent else "route_sort, gate_up, down, combine launches",
         },
         "effective_GBps": round(eff_gbps, 1),
         "pct_of_8TBps": round(100 * eff_gbps / HBM_PEAK_GBPS, 2),

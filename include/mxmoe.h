@@ -142,6 +142,11 @@ MX_API int moe_down_combine(const uint16_t* h, const float* gates, const uint8_t
                             int64_t I, int64_t E, int64_t top_k, void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/* The first MX_WORKSPACE_CTL_BYTES bytes of a MoE workspace are control words (counters of
+ * moe_mxfp4_forward_persistent).  They must be zero before that call first uses the
+ * workspace, and every call leaves them zero again; the other calls do not touch them. */
+#define MX_WORKSPACE_CTL_BYTES 40960
+
 /* Bytes of device workspace moe_mxfp4_forward needs for these sizes. */
 MX_API size_t moe_mxfp4_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k);
 
@@ -164,7 +169,8 @@ MX_API size_t moe_mxfp4_workspace_size(int64_t T, int64_t H, int64_t I, int64_t 
  *   y             bf16 [T, H]   (written)
  *   workspace     device buffer of at least moe_mxfp4_workspace_size(T, H, I, E, top_k)
  *                 bytes, 256-byte aligned; contents need no initialization and are
- *                 overwritten.  Calls that share a workspace must not overlap in time.
+ *                 overwritten (the control words excepted, which this call does not
+ *                 touch).  Calls that share a workspace must not overlap in time.
  *   1 <= T <= MX_MAX_TOKENS; 1 <= top_k <= min(E, MX_MAX_TOPK); E <= MX_MAX_EXPERTS;
  *   H % 1024 == 0; I % 1024 == 0 (both GEMMs stream 1024 K values per step).
  */
@@ -172,6 +178,29 @@ MX_API int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, int6
                       const uint8_t* s_gate_up, const uint8_t* w_down, const uint8_t* s_down, uint16_t* y,
                       int64_t T, int64_t H, int64_t I, int64_t E, void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/*
+ * The same layer as moe_mxfp4_forward, as ONE persistent launch (the megakernels of the
+ * Lithos page, "Specialization unlocks engine performance", and of the AMD megakernel
+ * blog, "What Drives the Speedup": workgroups hand data to one another through memory
+ * instead of kernel boundaries).  Every workgroup routes and sorts all tokens itself; the
+ * gate_up and down phases hand h over through device counters in the workspace, and the
+ * workgroup that completes a column tile's down outputs combines it.  Results are bit-for-
+ * bit those of moe_mxfp4_forward.  Arguments as for moe_mxfp4_forward, plus:
+ *   - T <= 16 and T * top_k <= 128 (MX_ERR_SHAPE otherwise);
+ *   - the workspace's first MX_WORKSPACE_CTL_BYTES must be zero before its first use
+ *     (every call leaves them zero);
+ *   - no other work may occupy the GPU's compute units while it runs: its workgroups
+ *     wait for one another.  A wait that outlasts any layer by far gives up, leaving y
+ *     undefined and the int32 word at byte offset 8 of the workspace set to 1 (sticky;
+ *     the caller clears it).
+ * On MI355X it is not faster than moe_mxfp4_forward: kernel boundaries inside a HIP graph
+ * cost about a microsecond, and its in-kernel hand-offs cost as much.
+ */
+MX_API int moe_mxfp4_forward_persistent(const uint16_t* x, const float* router_logits, int64_t top_k,
+                                        const uint8_t* w_gate_up, const uint8_t* s_gate_up, const uint8_t* w_down,
+                                        const uint8_t* s_down, uint16_t* y, int64_t T, int64_t H, int64_t I,
+                                        int64_t E, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -45,13 +45,14 @@ _lib.moe_down_combine.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, 
 _lib.moe_mxfp4_workspace_size.restype = ctypes.c_size_t
 _lib.moe_mxfp4_workspace_size.argtypes = [_I64, _I64, _I64, _I64, _I64]
 _lib.moe_mxfp4_forward.argtypes = [_P, _P, _I64, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]
+_lib.moe_mxfp4_forward_persistent.argtypes = list(_lib.moe_mxfp4_forward.argtypes)
 for _n in ("mx_linear", "mxfp4_dequantize", "moe_route_topk", "moe_sort_by_expert", "moe_route_sort",
-           "moe_gate_up_swiglu", "moe_down_combine", "moe_mxfp4_forward"):
+           "moe_gate_up_swiglu", "moe_down_combine", "moe_mxfp4_forward", "moe_mxfp4_forward_persistent"):
     getattr(_lib, _n).restype = ctypes.c_int
 
 EXPORTED = ("mx_version", "mx_status_string", "mx_linear", "mxfp4_dequantize", "moe_route_topk",
             "moe_sort_by_expert", "moe_route_sort", "moe_gate_up_swiglu", "moe_down_combine",
-            "moe_mxfp4_workspace_size", "moe_mxfp4_forward")
+            "moe_mxfp4_workspace_size", "moe_mxfp4_forward", "moe_mxfp4_forward_persistent")
 
 
 class MxError(RuntimeError):
@@ -270,20 +271,23 @@ _ws_cache: dict = {}
 
 
 def workspace(T: int, H: int, I: int, E: int, top_k: int, device) -> torch.Tensor:
-    """A cached uint8 workspace tensor large enough for these sizes on `device`."""
+    """A cached uint8 workspace tensor large enough for these sizes on `device` (allocated
+    zero-filled: its leading control words must start at zero, and every call leaves them so)."""
     need = workspace_size(T, H, I, E, top_k)
     dev = torch.device(device)
     buf = _ws_cache.get(dev)
     if buf is None or buf.numel() < need:
-        buf = torch.empty(need, dtype=torch.uint8, device=dev)
+        buf = torch.zeros(need, dtype=torch.uint8, device=dev)
         _ws_cache[dev] = buf
     return buf
 
 
 def moe_mxfp4_forward(x: torch.Tensor, router_logits: torch.Tensor, top_k: int, W_gate_up: torch.Tensor,
                       S_gate_up: torch.Tensor, W_down: torch.Tensor, S_down: torch.Tensor,
-                      out: torch.Tensor | None = None, ws: torch.Tensor | None = None) -> torch.Tensor:
-    """y[T,H] of the MXFP4 SwiGLU MoE layer (see include/mxmoe.h for the definition)."""
+                      out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                      persistent: bool = False) -> torch.Tensor:
+    """y[T,H] of the MXFP4 SwiGLU MoE layer (see include/mxmoe.h for the definition).
+    persistent=True runs it as one persistent launch (moe_mxfp4_forward_persistent; T <= 16)."""
     _check(x, "x", torch.bfloat16, 2)
     dev = x.device
     _check(router_logits, "router_logits", torch.float32, 2, dev)
@@ -303,8 +307,9 @@ def moe_mxfp4_forward(x: torch.Tensor, router_logits: torch.Tensor, top_k: int, 
     if ws is None:
         ws = workspace(T, H, I, E, top_k, dev)
     _check(ws, "workspace", torch.uint8, 1, dev)
-    st = _lib.moe_mxfp4_forward(_ptr(x), _ptr(router_logits), top_k, _ptr(W_gate_up), _ptr(S_gate_up),
-                                _ptr(W_down), _ptr(S_down), _ptr(out), T, H, I, E, _ptr(ws), ws.numel(),
-                                _stream(dev))
-    _raise(st, "moe_mxfp4_forward")
+    name = "moe_mxfp4_forward_persistent" if persistent else "moe_mxfp4_forward"
+    st = getattr(_lib, name)(_ptr(x), _ptr(router_logits), top_k, _ptr(W_gate_up), _ptr(S_gate_up),
+                             _ptr(W_down), _ptr(S_down), _ptr(out), T, H, I, E, _ptr(ws), ws.numel(),
+                             _stream(dev))
+    _raise(st, name)
     return out

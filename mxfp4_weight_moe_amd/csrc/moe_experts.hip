@@ -1,228 +1,23 @@
-// The two expert GEMMs of the MXFP4 MoE layer and the combine.
+// The two expert GEMM kernels of the MXFP4 MoE layer (work lists and epilogues in
+// moe_policies.hpp) and the combine, for launches that follow the sort kernels.
 //
-// "Zyphra Inference Wave 2", section "Quantization": an MXFP4 expert runs two expert
-// GEMMs and combines the results, and a decode step reads only the routed experts; Kernel
-// Results: a kernel fusing both stages spilled registers and ran slower, and an atomic-add
-// combine was slower for the MX formats.  So: two GEMM kernels with fused epilogues, no
-// float atomics.
+// "Zyphra Inference Wave 2", Kernel Results: a kernel fusing both stages spilled registers
+// and ran slower, and an atomic-add combine was slower for the MX formats.  So: two GEMM
+// kernels with fused epilogues, no float atomics.
 //
-//   gate_up: item = (row group of an active expert, 4 tiles of intermediate columns).
-//            Each of the 4 wavefronts of a workgroup streams the gate rows and the matching
-//            up rows of its tile (16 + 16, or 8 + 8 for half-width tiles) over all H, then
-//            applies SwiGLU and rounds h to bf16.  h rows are stored in sorted-slot order.
-//   down:    item = (row group of an active expert, 4 tiles of 32 output columns, or 16
-//            for half-width tiles); stores the fp32 down outputs per flat slot.
 //   combine: y[t,:] = bf16(sum_j fl32(gate[t,j] * d[t*k + j,:])), j ascending.
 //
-// A row group is up to 16 of the expert's routed rows (one MFMA m-tile); experts with more
-// rows have several groups.  Items are ordered group-major, then expert, then column tile,
-// and dealt round-robin to a persistent grid of workgroups sized to the device, which
+// Items are dealt round-robin to a persistent grid of workgroups sized to the device, which
 // stream them back to back (mx_stream.hpp).  The number of active experts is read on the
 // device, so there is no host readback.
-#include "mx_internal.hpp"
-#include "mx_stream.hpp"
+#include "moe_policies.hpp"
 
 namespace mx {
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
-
-// Item metadata (sort outputs) is read through the scalar data path: the kernels never
-// write it, and scalar loads do not queue behind the wave's in-flight vector loads, so
-// setting up the next item does not drain the weight stream.
-typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
-
-__device__ __forceinline__ int ld_uniform(const int32_t* p, int i) { return ((cint_ptr)p)[i]; }
-
-// Flat slot of row `j` (< 16) of a group of `rows` rows starting at sorted position `base`,
-// as a per-lane value for lane row j = lane & 15 (-1 past the group).
-__device__ __forceinline__ int group_slot(const int32_t* sorted_slots, int base, int rows, int lane) {
-  const int j = lane & 15;
-  int v = -1;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    if (r < rows) {
-      const int s = ld_uniform(sorted_slots, base + r);
-      v = (j == r) ? s : v;
-    }
-  }
-  return v;
-}
-
-struct ItemIndex {
-  int a, quad, g;
-};
-
-// item = (g * na + a) * nquad + quad
-__device__ __forceinline__ ItemIndex item_decode(int it, int nquad, int na) {
-  ItemIndex r;
-  const int q = it / nquad;
-  r.quad = it - q * nquad;
-  r.g = q / na;
-  r.a = q - r.g * na;
-  return r;
-}
-
-// Segments per weight step: an item's segments (H / 256 for gate_up, I / 256 for down)
-// must be a multiple of these, which the launchers check.  Activation chunks are a
-// multiple of both, so they end on steps of either kernel.
-constexpr int GU_SPS = 2;  // gate_up: 28 segments per item at H = 7168
-constexpr int DN_SPS = 2;  // down: 8 segments per item at I = 2048
-constexpr int CHUNK_ALIGN = GU_SPS > DN_SPS ? GU_SPS : DN_SPS;
-static_assert(CHUNK_ALIGN % GU_SPS == 0 && CHUNK_ALIGN % DN_SPS == 0, "chunks must end on steps");
-// Activation chunk buffers: gate_up keeps 2 workgroups per CU with 32 KB chunks; down's
-// items are short (I / 256 segments) and run 3 workgroups per CU with 16 KB chunks.
-constexpr int GU_XCHUNK = 32768;
-constexpr int DN_XCHUNK = 16384;
-static_assert(SUB_ROWS * CHUNK_ALIGN <= XGeom<GU_XCHUNK>::ROWSEGS && SUB_ROWS * CHUNK_ALIGN <= XGeom<DN_XCHUNK>::ROWSEGS,
-              "a chunk must hold one step of a full row group");
-
-// Fields shared by both expert GEMMs: the work list over (row group, expert, tile quad).
-struct ExpertItems {
-  SortView sv;
-  int nseg, n_items, nquad, na;
-  int xrowsegs;  // row-segments per activation chunk
-
-  __device__ __forceinline__ bool valid(int it) const {
-    const ItemIndex ix = item_decode(it, nquad, na);
-    return ix.g * 16 < ld_uniform(sv.counts, ld_uniform(sv.active, ix.a));
-  }
-  __device__ __forceinline__ ItemInfo info(int it) const {
-    const ItemIndex ix = item_decode(it, nquad, na);
-    ItemInfo f;
-    f.e = ld_uniform(sv.active, ix.a);
-    f.rows = min(16, ld_uniform(sv.counts, f.e) - ix.g * 16);
-    f.row0 = ld_uniform(sv.offsets, f.e) + ix.g * 16;
-    f.tile0 = ix.quad * WG_WAVES;
-    f.cs = chunk_segments(f.rows, nseg, CHUNK_ALIGN, xrowsegs);
-    return f;
-  }
-};
-
-// ------------------------------------------------------------------ gate_up + SwiGLU
-
-// NS = 2: a wave's tile is 16 intermediate columns: subtile 0 = their 16 gate rows,
-//         subtile 1 = the 16 matching up rows.
-// NS = 1: a wave's tile is 8 intermediate columns: one subtile of their 8 gate rows
-//         (rows 0-7) and the 8 matching up rows (rows 8-15).  The MFMA result rows 8-15 sit
-//         in lanes 32-63, so one lane swap brings each up value beside its gate value.
-// Half-width tiles double the waves streaming a launch with few items (small T).
-template <int NS_>
-struct GateUpPolicy : ExpertItems {
-  static constexpr int NS = NS_;
-  static constexpr int XCHUNK = GU_XCHUNK;
-  static constexpr int TILE = NS == 2 ? SUB_ROWS : SUB_ROWS / 2;  // intermediate columns per wave
-  struct EpiState {
-    int hrow;  // h row of the group's first row
-    int rows;  // valid rows in the group
-    int n0;    // first intermediate column of this wave's tile
-  };
-  const uint16_t* xact;  // x [T, H]
-  const uint8_t* wgu;
-  const uint8_t* sgu;
-  uint16_t* h;
-  int H, I, k;
-  uint32_t kinv;  // ceil(2^24 / k)
-  size_t e_codes, e_scales;
-
-  // token = slot / k as (slot * ceil(2^24 / k)) >> 24, exact for slot < 8192 and k <= 32
-  static_assert(MX_MAX_TOKENS * MX_MAX_TOPK <= 8192 && MX_MAX_TOPK <= 32, "reciprocal range");
-  __device__ __forceinline__ int x_row_offset(const ItemInfo& f, int m) const {
-    const uint32_t slot = (uint32_t)ld_uniform(sv.sorted_slots, f.row0 + m);
-    return (int)(((uint64_t)slot * kinv) >> 24) * H;
-  }
-  // weight row of row r (0..15) of subtile i of this wave's tile
-  __device__ __forceinline__ int wrow(const ItemInfo& f, int wave, int i, int r) const {
-    const int n0 = (f.tile0 + wave) * TILE;
-    if (NS == 2) return (i ? I : 0) + n0 + r;
-    return (r < 8) ? n0 + r : I + n0 + r - 8;
-  }
-  __device__ __forceinline__ void w_setup(const ItemInfo& f, int wave, WCursor<NS>& c, int lane) const {
-    const uint8_t* we = wgu + (size_t)f.e * e_codes;
-    const size_t kb = (size_t)H >> 1;
-#pragma unroll
-    for (int i = 0; i < NS; ++i)
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-        c.w[i][q] = we + (size_t)wrow(f, wave, i, (lane >> 3) + 8 * q) * kb + (lane & 7) * 16;
-  }
-  __device__ __forceinline__ const uint8_t* scale_row(const ItemInfo& f, int wave, int i, int r) const {
-    return sgu + (size_t)f.e * e_scales + (size_t)wrow(f, wave, i, r) * (H >> 5);
-  }
-  __device__ __forceinline__ void c_setup(const ItemInfo& f, int wave, EpiState& s, int) const {
-    s.hrow = f.row0;
-    s.rows = f.rows;
-    s.n0 = (f.tile0 + wave) * TILE;
-  }
-  // MFMA result: lane l holds rows 4 (l >> 4) + 0..3 of the tile for token row l & 15.
-  __device__ __forceinline__ void epilogue(const EpiState& s, const f32x4 (&acc)[NS], int lane) const {
-    const int r = lane & 15;
-    float g[4], u[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      g[i] = acc[0][i];
-      if (NS == 2) {
-        u[i] = acc[1][i];
-      } else {
-        const uint32_t b = __float_as_uint(acc[0][i]);
-        u[i] = __uint_as_float(__builtin_amdgcn_permlane32_swap(b, b, false, false)[1]);  // lane l <- lane l + 32
-      }
-    }
-    if (r >= s.rows || (NS == 1 && lane >= 32)) return;
-    uint32_t o[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint16_t a = f32_to_bf16_rne(silu_mul(g[2 * j], u[2 * j]));
-      const uint16_t b = f32_to_bf16_rne(silu_mul(g[2 * j + 1], u[2 * j + 1]));
-      o[j] = (uint32_t)a | ((uint32_t)b << 16);
-    }
-    *reinterpret_cast<u32x2*>(h + (size_t)(s.hrow + r) * I + s.n0 + 4 * (lane >> 4)) = u32x2{o[0], o[1]};
-  }
-};
-
-// ------------------------------------------------------------------ down
-
-// A wave's tile is NS x 16 output columns (subtile i = columns n0 + 16 i ... + 15).
-template <int NS_>
-struct DownPolicy : ExpertItems {
-  static constexpr int NS = NS_;
-  static constexpr int XCHUNK = DN_XCHUNK;
-  static constexpr int TILE = NS * SUB_ROWS;  // output columns per wave
-  struct EpiState {
-    int slot;  // flat slot of this lane's row, -1 if the row is past the group
-    int n0;    // first output column of this wave's tile
-  };
-  const uint16_t* xact;  // h [T*k, I], rows in sorted order
-  const uint8_t* wd;
-  const uint8_t* sd;
-  float* dpart;
-  int H, I;
-  size_t e_codes, e_scales;
-
-  __device__ __forceinline__ int x_row_offset(const ItemInfo& f, int m) const { return (f.row0 + m) * I; }
-  __device__ __forceinline__ void w_setup(const ItemInfo& f, int wave, WCursor<NS>& c, int lane) const {
-    const uint8_t* we = wd + (size_t)f.e * e_codes;
-    const size_t kb = (size_t)I >> 1;
-    const int n0 = (f.tile0 + wave) * TILE;
-#pragma unroll
-    for (int i = 0; i < NS; ++i)
-#pragma unroll
-      for (int q = 0; q < 2; ++q) c.w[i][q] = we + (size_t)(n0 + 16 * i + (lane >> 3) + 8 * q) * kb + (lane & 7) * 16;
-  }
-  __device__ __forceinline__ const uint8_t* scale_row(const ItemInfo& f, int wave, int i, int r) const {
-    const int n = (f.tile0 + wave) * TILE + SUB_ROWS * i + r;
-    return sd + (size_t)f.e * e_scales + (size_t)n * (I >> 5);
-  }
-  __device__ __forceinline__ void c_setup(const ItemInfo& f, int wave, EpiState& s, int lane) const {
-    s.slot = group_slot(sv.sorted_slots, f.row0, f.rows, lane);
-    s.n0 = (f.tile0 + wave) * TILE;
-  }
-  __device__ __forceinline__ void epilogue(const EpiState& s, const f32x4 (&acc)[NS], int lane) const {
-    if (s.slot < 0) return;
-#pragma unroll
-    for (int i = 0; i < NS; ++i)
-      *reinterpret_cast<f32x4*>(dpart + (size_t)s.slot * H + s.n0 + 16 * i + 4 * (lane >> 4)) = acc[i];
-  }
-};
+template <int NS>
+using GateUpPlain = GateUpPolicy<NS, GlobalSort, GU_XCHUNK, false>;
+template <int NS>
+using DownPlain = DownPolicy<NS, GlobalSort, DN_XCHUNK, false>;
 
 // ------------------------------------------------------------------ kernels
 
@@ -232,7 +27,7 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_gate_up_kernel(const uint16
                                                                     const uint8_t* __restrict__ sgu, SortView sv,
                                                                     uint16_t* __restrict__ h, int H, int I, int k,
                                                                     int gmax) {
-  using P = GateUpPolicy<NS>;
+  using P = GateUpPlain<NS>;
   __shared__ __attribute__((aligned(16))) uint8_t xbufs[2 * P::XCHUNK];
   __shared__ __attribute__((aligned(16))) uint8_t slabs[WG_WAVES][SLAB_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t sslabs[WG_WAVES][sslab_bytes<NS>()];
@@ -243,10 +38,10 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_gate_up_kernel(const uint16
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   P p;
   p.xrowsegs = XGeom<P::XCHUNK>::ROWSEGS;
-  p.sv = sv;
+  p.m.sv = sv;
   p.nseg = H / SEG_K;
   p.nquad = I / (P::TILE * WG_WAVES);
-  p.na = ld_uniform(sv.num_active, 0);
+  p.na = p.m.num_active();
   p.n_items = gmax * p.na * p.nquad;
   p.xact = x;
   p.wgu = wgu;
@@ -266,7 +61,7 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_down_kernel(const uint16_t*
                                                                  const uint8_t* __restrict__ wd,
                                                                  const uint8_t* __restrict__ sd, SortView sv,
                                                                  float* __restrict__ dpart, int H, int I, int gmax) {
-  using P = DownPolicy<NS>;
+  using P = DownPlain<NS>;
   __shared__ __attribute__((aligned(16))) uint8_t xbufs[2 * P::XCHUNK];
   __shared__ __attribute__((aligned(16))) uint8_t slabs[WG_WAVES][SLAB_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t sslabs[WG_WAVES][sslab_bytes<NS>()];
@@ -276,10 +71,10 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_down_kernel(const uint16_t*
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   P p;
   p.xrowsegs = XGeom<P::XCHUNK>::ROWSEGS;
-  p.sv = sv;
+  p.m.sv = sv;
   p.nseg = I / SEG_K;
   p.nquad = H / (P::TILE * WG_WAVES);
-  p.na = ld_uniform(sv.num_active, 0);
+  p.na = p.m.num_active();
   p.n_items = gmax * p.na * p.nquad;
   p.xact = h;
   p.wd = wd;
@@ -347,7 +142,7 @@ int launch_gate_up(const uint16_t* x, const uint8_t* wgu, const uint8_t* sgu, co
                    int H, int I, int E, int k, hipStream_t stream) {
   if (H % (SEG_K * GU_SPS) != 0 || H % (SEG_K * SRUN) != 0 || I % (SUB_ROWS * WG_WAVES) != 0) return MX_ERR_SHAPE;
   const int gmax = row_groups(T);
-  const int64_t items_full = (int64_t)gmax * max_active(T, E, k) * (I / (GateUpPolicy<2>::TILE * WG_WAVES));
+  const int64_t items_full = (int64_t)gmax * max_active(T, E, k) * (I / (GateUpPlain<2>::TILE * WG_WAVES));
   int grid = 0;
   if (use_half_tiles(moe_gate_up_kernel<2>, moe_gate_up_kernel<1>, items_full, grid))
     hipLaunchKernelGGL(moe_gate_up_kernel<1>, dim3(grid), dim3(WG_WAVES * 64), 0, stream, x, wgu, sgu, sv, h, H, I, k,
@@ -363,7 +158,7 @@ int launch_down(const uint16_t* h, const float* gates, const uint8_t* wd, const 
   (void)gates;  // applied by the combine
   if (I % (SEG_K * DN_SPS) != 0 || I % (SEG_K * SRUN) != 0 || H % (2 * SUB_ROWS * WG_WAVES) != 0) return MX_ERR_SHAPE;
   const int gmax = row_groups(T);
-  const int64_t items_full = (int64_t)gmax * max_active(T, E, k) * (H / (DownPolicy<2>::TILE * WG_WAVES));
+  const int64_t items_full = (int64_t)gmax * max_active(T, E, k) * (H / (DownPlain<2>::TILE * WG_WAVES));
   int grid = 0;
   if (use_half_tiles(moe_down_kernel<2>, moe_down_kernel<1>, items_full, grid))
     hipLaunchKernelGGL(moe_down_kernel<1>, dim3(grid), dim3(WG_WAVES * 64), 0, stream, h, wd, sd, sv, dpart, H, I,

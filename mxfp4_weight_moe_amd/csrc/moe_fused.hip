@@ -1,0 +1,370 @@
+// The whole MoE layer in one launch for small T: routing, sort, gate_up + SwiGLU, down and
+// the gate-weighted combine.
+//
+// At small T a layer streams only tens of microseconds of weights, and each kernel
+// boundary (the GPU draining one kernel and starting the next) costs microseconds.  The
+// Lithos page ("Specialization unlocks engine performance", 1. Megakernels) and the AMD
+// megakernel blog ("What Drives the Speedup", 1. Megakernels) remove such boundaries with
+// persistent kernels whose workgroups hand data to one another through memory and
+// synchronize only where data is shared.  Here:
+//
+//   routing  every workgroup routes all T tokens and sorts the slots itself, into LDS
+//            (T <= 16: a few microseconds, and the same result everywhere).
+//   gate_up  the workgroups stream the gate_up items (moe_policies.hpp) and write h with
+//            device-coherent stores; each then adds its item count to a device counter,
+//            and the one that completes the count raises a ready flag, replicated on 64
+//            lines so that the polls of the workgroups spread over the memory channels.
+//   down     each wavefront requests its first weights, then waits for its replica of the
+//            flag before loading h.  The down outputs are written with device-coherent
+//            stores.
+//   combine  each workgroup adds one to the counter of every column quad it finished; the
+//            one that completes a quad (one item per active expert) has all of that quad's
+//            down outputs and combines those columns for every token, j ascending, exactly
+//            as the combine kernel of the multi-launch path does.
+//
+// No cache-wide write-back or invalidate is used: the data handed between workgroups
+// moves with sc1 accesses, and a wavefront's own stores are complete (s_waitcnt vmcnt(0))
+// before it publishes a count.  The last workgroup to finish (an exit counter) resets the
+// counters, so every call leaves the workspace control words zero, as it found them.
+//
+// The waits assume every workgroup of the grid is resident at once (the grid is sized to
+// the device's occupancy for this kernel).  A wait that would outlast any layer by far
+// gives up and raises the error word instead of hanging.
+#include "moe_policies.hpp"
+#include "moe_route.hpp"
+
+namespace mx {
+
+constexpr int FUSED_MAX_SLOTS = 128;  // T * k
+constexpr int FUSED_XCHUNK = GU_XCHUNK;
+static_assert(MX_FUSED_MAX_TOKENS <= 32, "a token mask per expert is one 32-bit word");
+static_assert(MX_FUSED_MAX_TOKENS <= 16, "one row group (16 rows) per expert");
+
+// The workgroup's routing and sort (LDS).  Active experts are numbered a = 0.. in
+// ascending expert order.
+struct FusedSort {
+  int32_t act[FUSED_MAX_SLOTS];    // expert id of active expert a
+  int32_t cnt[FUSED_MAX_SLOTS];    // its routed rows
+  int32_t off[FUSED_MAX_SLOTS];    // its first sorted position
+  int32_t slots[FUSED_MAX_SLOTS];  // flat slot at each sorted position
+  float gates[FUSED_MAX_SLOTS];    // gate of each flat slot t * k + j
+  int32_t na;                      // active experts
+  int32_t wave_sum[WG_WAVES];
+  int32_t ndone;                   // column quads this workgroup completed
+  int32_t last;                    // this workgroup finished last
+  int32_t h_ready;                 // the workgroup's poller saw every h row written
+};
+__shared__ FusedSort fsort;
+
+struct LdsSort {
+  __device__ __forceinline__ int num_active() const { return __builtin_amdgcn_readfirstlane(fsort.na); }
+  __device__ __forceinline__ int expert(int a) const { return __builtin_amdgcn_readfirstlane(fsort.act[a]); }
+  __device__ __forceinline__ int count(int a) const { return __builtin_amdgcn_readfirstlane(fsort.cnt[a]); }
+  __device__ __forceinline__ int offset(int a) const { return __builtin_amdgcn_readfirstlane(fsort.off[a]); }
+  __device__ __forceinline__ int slot(int i) const { return __builtin_amdgcn_readfirstlane(fsort.slots[i]); }
+};
+
+// Routing and counting sort of one workgroup into fsort; `tmp` is scratch LDS of at least
+// 9 KB (token masks, per-expert offsets, routed ids).  Wave w routes tokens w, w + 4, ...;
+// a slot (t, j) routed to expert e sets bit t of e's mask, and since a token's k experts
+// are distinct, the slot's rank among e's slots is the number of mask bits below t.
+// Counts, offsets and active positions come from one scan over the experts, 4 per thread.
+template <int PER>
+__device__ __forceinline__ void fused_route_sort(const float* __restrict__ logits, int T, int E, int k,
+                                                 uint8_t* __restrict__ tmp) {
+  uint32_t* bits = reinterpret_cast<uint32_t*>(tmp);             // [E]
+  int32_t* eoff = reinterpret_cast<int32_t*>(tmp + 4096);        // [E]
+  int32_t* sids = reinterpret_cast<int32_t*>(tmp + 8192);        // [T * k]
+  static_assert(MX_MAX_EXPERTS * 4 <= 4096 && FUSED_MAX_SLOTS * 4 <= 1024, "scratch layout");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float v[PER], vn[PER];
+  route_load<PER>(logits + (size_t)min(wave, T - 1) * E, E, lane, v);
+  for (int i = tid; i < E; i += WG_WAVES * 64) bits[i] = 0u;
+  __syncthreads();
+  for (int t = wave; t < T; t += WG_WAVES) {
+    // the next token of this wave (unconditional: the last row again past the end)
+    route_load<PER>(logits + (size_t)min(t + WG_WAVES, T - 1) * E, E, lane, vn);
+    int e;
+    float g;
+    route_select<PER>(v, E, k, lane, e, g);
+    if (lane < k) {
+      sids[t * k + lane] = e;
+      fsort.gates[t * k + lane] = g;
+      atomicOr(&bits[e], 1u << t);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) v[i] = vn[i];
+  }
+  __syncthreads();
+  // exclusive scan of (count | active << 16) over the experts
+  int c[4], packed[4], sum = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid * 4 + q;
+    c[q] = (e < E) ? __popc(bits[e]) : 0;
+    packed[q] = c[q] | (c[q] > 0 ? (1 << 16) : 0);
+    sum += packed[q];
+  }
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) fsort.wave_sum[wave] = incl;
+  __syncthreads();
+  int run = incl - sum;
+  for (int w = 0; w < wave; ++w) run += fsort.wave_sum[w];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid * 4 + q;
+    if (e < E) {
+      eoff[e] = run & 0xFFFF;
+      if (c[q] > 0) {
+        const int a = run >> 16;
+        fsort.act[a] = e;
+        fsort.cnt[a] = c[q];
+        fsort.off[a] = run & 0xFFFF;
+      }
+    }
+    run += packed[q];
+  }
+  if (tid == WG_WAVES * 64 - 1) fsort.na = run >> 16;
+  __syncthreads();
+  for (int f = tid; f < T * k; f += WG_WAVES * 64) {
+    const int e = sids[f];
+    const int t = f / k;
+    fsort.slots[eoff[e] + __popc(bits[e] & ((1u << t) - 1u))] = f;
+  }
+  __syncthreads();
+}
+
+// Items of workgroup wg among n dealt round-robin over g workgroups.
+__device__ __forceinline__ int items_of(int wg, int g, int n) { return wg < n ? (n - 1 - wg) / g + 1 : 0; }
+
+__device__ __forceinline__ void wait_own_stores() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores have completed
+}
+
+template <int PER, int NSG, int NSD>
+__global__ void __launch_bounds__(WG_WAVES * 64) moe_fused_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ logits, const uint8_t* __restrict__ wgu,
+    const uint8_t* __restrict__ sgu, const uint8_t* __restrict__ wd, const uint8_t* __restrict__ sd, uint16_t* hbuf,
+    float* dpart, uint16_t* __restrict__ y, int32_t* ctl, int T, int H, int I, int E, int k) {
+  __shared__ __attribute__((aligned(16))) uint8_t xbufs[2 * FUSED_XCHUNK];
+  __shared__ __attribute__((aligned(16))) uint8_t slabs[WG_WAVES][SLAB_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t sslabs[WG_WAVES][sslab_bytes<2>()];
+  __shared__ uint32_t xctr[2];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int wg = blockIdx.x, n_wg = gridDim.x;
+  if (tid < 2) xctr[tid] = 0u;
+  fused_route_sort<PER>(logits, T, E, k, xbufs);
+  const LdsSort meta;
+  const int na = meta.num_active();
+
+  // ---------------------------------------------------------------- gate_up + SwiGLU
+  using PG = GateUpPolicy<NSG, LdsSort, FUSED_XCHUNK, true>;
+  const int n_gu = na * (I / (PG::TILE * WG_WAVES));
+  {
+    PG p;
+    p.xrowsegs = XGeom<FUSED_XCHUNK>::ROWSEGS;
+    p.nseg = H / SEG_K;
+    p.nquad = I / (PG::TILE * WG_WAVES);
+    p.na = na;
+    p.n_items = n_gu;
+    p.xact = x;
+    p.wgu = wgu;
+    p.sgu = sgu;
+    p.h = hbuf;
+    p.H = H;
+    p.I = I;
+    p.k = k;
+    p.kinv = ((1u << 24) + (uint32_t)k - 1u) / (uint32_t)k;
+    p.e_codes = (size_t)2 * I * (H / 2);
+    p.e_scales = (size_t)2 * I * (H / 32);
+    stream_items<PG, GU_SPS>(p, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
+  }
+  // Publish: this workgroup's h stores are complete; add its item count.  The workgroup
+  // whose count completes the total raises every replica of the ready flag.
+  wait_own_stores();
+  __syncthreads();
+  if (tid == 0) {
+    const int mine = items_of(wg, n_wg, n_gu);
+    if (mine > 0) {
+      const int old = __hip_atomic_fetch_add(&ctl[CTL_GU_DONE], mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (old + mine == n_gu)
+        for (int r = 0; r < CTL_READY_REPLICAS; ++r)
+          __hip_atomic_store(&ctl[CTL_READY0 + r * CTL_READY_STRIDE], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    xctr[0] = 0u;  // fresh chunk hand-off for the down items
+    xctr[1] = 0u;
+    fsort.h_ready = 0;
+  }
+  __syncthreads();
+
+  // ---------------------------------------------------------------- down
+  using PD = DownPolicy<NSD, LdsSort, FUSED_XCHUNK, true>;
+  const int nquad_dn = H / (PD::TILE * WG_WAVES);
+  const int n_dn = na * nquad_dn;
+  {
+    PD p;
+    p.xrowsegs = XGeom<FUSED_XCHUNK>::ROWSEGS;
+    p.nseg = I / SEG_K;
+    p.nquad = nquad_dn;
+    p.na = na;
+    p.n_items = n_dn;
+    p.xact = hbuf;
+    p.wd = wd;
+    p.sd = sd;
+    p.dpart = dpart;
+    p.H = H;
+    p.I = I;
+    p.e_codes = (size_t)H * (I / 2);
+    p.e_scales = (size_t)H * (I / 32);
+    p.ready = ctl + CTL_READY0 + (wg % CTL_READY_REPLICAS) * CTL_READY_STRIDE;
+    p.err = ctl + CTL_ERR;
+    p.flag = (lds_i32*)&fsort.h_ready;
+    p.ready_target = 1;
+    p.wave = wave;
+    stream_items<PD, DN_SPS>(p, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
+  }
+  wait_own_stores();
+  __syncthreads();
+
+  // ---------------------------------------------------------------- combine
+  // Wave 0 counts this workgroup's items per column quad, 64 items per round; a quad is
+  // complete when its count reaches na (one item per active expert, all valid for T <= 16).
+  int32_t* done = reinterpret_cast<int32_t*>(xbufs);  // quads completed here (<= nquad_dn)
+  if (wave == 0) {
+    int nd = 0;
+    for (int base = wg; base < n_dn; base += 64 * n_wg) {
+      const int it = base + lane * n_wg;
+      bool fin = false;
+      int q = 0;
+      if (it < n_dn) {
+        q = it % nquad_dn;
+        fin = __hip_atomic_fetch_add(&ctl[CTL_QUAD0 + q], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == na - 1;
+      }
+      const uint64_t m = __ballot(fin);
+      if (fin) done[nd + __popcll(m & ((1ull << lane) - 1ull))] = q;
+      nd += __popcll(m);
+    }
+    if (lane == 0) fsort.ndone = nd;
+  }
+  __syncthreads();
+  constexpr int QV = PD::TILE * WG_WAVES / 4;  // 4-column groups per quad
+  const int nd = fsort.ndone;
+  for (int d = 0; d < nd; ++d) {
+    const int c0 = done[d] * (QV * 4);
+    for (int i = tid; i < T * QV; i += WG_WAVES * 64) {
+      const int t = i / QV;
+      const int n = c0 + (i - t * QV) * 4;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      // slots in batches of 8: all loads of a batch in flight at once, then the sum, j ascending
+      for (int j0 = 0; j0 < k; j0 += 8) {
+        u32x4 dv[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          dv[jj] = ld16_coherent(dpart + (size_t)(t * k + min(j0 + jj, k - 1)) * H + n);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          if (j0 + jj < k) {
+            const float g = fsort.gates[t * k + j0 + jj];
+            acc += f32x4{g * __uint_as_float(dv[jj][0]), g * __uint_as_float(dv[jj][1]),
+                         g * __uint_as_float(dv[jj][2]), g * __uint_as_float(dv[jj][3])};
+          }
+        }
+      }
+      const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
+      *reinterpret_cast<u32x2*>(y + (size_t)t * H + n) = u32x2{lo, hi};
+    }
+  }
+
+  // ---------------------------------------------------------------- exit
+  // Every workgroup's counter updates precede its exit count; the last one resets them.
+  __syncthreads();
+  if (tid == 0)
+    fsort.last = __hip_atomic_fetch_add(&ctl[CTL_EXIT], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_wg - 1;
+  __syncthreads();
+  if (fsort.last) {
+    for (int i = tid; i < nquad_dn; i += WG_WAVES * 64)
+      __hip_atomic_store(&ctl[CTL_QUAD0 + i], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid < CTL_READY_REPLICAS)
+      __hip_atomic_store(&ctl[CTL_READY0 + tid * CTL_READY_STRIDE], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+      __hip_atomic_store(&ctl[CTL_GU_DONE], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&ctl[CTL_EXIT], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launcher
+
+template <int PER, int NSG, int NSD>
+static int fused_launch_one(const uint16_t* x, const float* logits, const uint8_t* wgu, const uint8_t* sgu,
+                            const uint8_t* wd, const uint8_t* sd, uint16_t* hbuf, float* dpart, uint16_t* y,
+                            int32_t* ctl, int T, int H, int I, int E, int k, int64_t items, hipStream_t stream) {
+  static const int occ = [] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, moe_fused_kernel<PER, NSG, NSD>, WG_WAVES * 64, 0) !=
+            hipSuccess ||
+        n < 1)
+      n = 1;
+    return n;
+  }();
+  const int64_t cap = (int64_t)device_cu_count() * occ;
+  const int grid = (int)(items < cap ? items : cap);
+  hipLaunchKernelGGL((moe_fused_kernel<PER, NSG, NSD>), dim3(grid), dim3(WG_WAVES * 64), 0, stream, x, logits, wgu,
+                     sgu, wd, sd, hbuf, dpart, y, ctl, T, H, I, E, k);
+  return hip_status(hipGetLastError());
+}
+
+template <int PER>
+static int fused_launch_per(bool gu_half, bool dn_half, const uint16_t* x, const float* logits, const uint8_t* wgu,
+                            const uint8_t* sgu, const uint8_t* wd, const uint8_t* sd, uint16_t* hbuf, float* dpart,
+                            uint16_t* y, int32_t* ctl, int T, int H, int I, int E, int k, int64_t items,
+                            hipStream_t stream) {
+  if (gu_half)
+    return dn_half ? fused_launch_one<PER, 1, 1>(x, logits, wgu, sgu, wd, sd, hbuf, dpart, y, ctl, T, H, I, E, k, items, stream)
+                   : fused_launch_one<PER, 1, 2>(x, logits, wgu, sgu, wd, sd, hbuf, dpart, y, ctl, T, H, I, E, k, items, stream);
+  return dn_half ? fused_launch_one<PER, 2, 1>(x, logits, wgu, sgu, wd, sd, hbuf, dpart, y, ctl, T, H, I, E, k, items, stream)
+                 : fused_launch_one<PER, 2, 2>(x, logits, wgu, sgu, wd, sd, hbuf, dpart, y, ctl, T, H, I, E, k, items, stream);
+}
+
+bool fused_layer_fits(int T, int E, int k, int H, int I) {
+  (void)E;
+  return T <= MX_FUSED_MAX_TOKENS && T * k <= FUSED_MAX_SLOTS && H % (SEG_K * GU_SPS) == 0 &&
+         H % (SEG_K * SRUN) == 0 && I % (SEG_K * DN_SPS) == 0 && I % (SEG_K * SRUN) == 0 &&
+         I % (SUB_ROWS * WG_WAVES) == 0 && H % (2 * SUB_ROWS * WG_WAVES) == 0 && H / (SUB_ROWS * WG_WAVES) <= CTL_MAX_QUADS;
+}
+
+int launch_moe_fused(const uint16_t* x, const float* logits, const uint8_t* wgu, const uint8_t* sgu, const uint8_t* wd,
+                     const uint8_t* sd, uint16_t* hbuf, float* dpart, uint16_t* y, int32_t* ctl, int T, int H, int I,
+                     int E, int k, hipStream_t stream) {
+  if (!fused_layer_fits(T, E, k, H, I)) return MX_ERR_SHAPE;
+  // Half-width tiles when full-width ones would leave the device's workgroup slots idle
+  // (two resident workgroups per CU): the same rule as the multi-launch path.
+  const int64_t na_max = (int64_t)T * k < E ? (int64_t)T * k : E;
+  const int64_t slots = (int64_t)device_cu_count() * 2;
+  const int64_t gu_full = na_max * (I / (SUB_ROWS * WG_WAVES));
+  const int64_t dn_full = na_max * (H / (2 * SUB_ROWS * WG_WAVES));
+  const bool gu_half = 2 * gu_full <= slots, dn_half = 2 * dn_full <= slots;
+  const int64_t gu_items = gu_half ? 2 * gu_full : gu_full, dn_items = dn_half ? 2 * dn_full : dn_full;
+  const int64_t items = gu_items > dn_items ? gu_items : dn_items;
+  switch (route_per(E)) {
+    case 4:
+      return fused_launch_per<4>(gu_half, dn_half, x, logits, wgu, sgu, wd, sd, hbuf, dpart, y, ctl, T, H, I, E, k,
+                                 items, stream);
+    case 8:
+      return fused_launch_per<8>(gu_half, dn_half, x, logits, wgu, sgu, wd, sd, hbuf, dpart, y, ctl, T, H, I, E, k,
+                                 items, stream);
+    default:
+      return fused_launch_per<16>(gu_half, dn_half, x, logits, wgu, sgu, wd, sd, hbuf, dpart, y, ctl, T, H, I, E, k,
+                                  items, stream);
+  }
+}
+
+}  // namespace mx

@@ -20,6 +20,7 @@ MoeWorkspace moe_workspace_carve(void* base, int64_t T, int64_t H, int64_t I, in
     off += align_up(bytes);
     return p;
   };
+  w.ctl = reinterpret_cast<int32_t*>(take(MX_WORKSPACE_CTL_BYTES));
   w.ids = reinterpret_cast<int32_t*>(take(F * 4));
   w.gates = reinterpret_cast<float*>(take(F * 4));
   w.counts = reinterpret_cast<int32_t*>(take((size_t)E * 4));
@@ -211,6 +212,25 @@ int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, int64_t top
   if ((st = launch_gate_up(x, w_gate_up, s_gate_up, sv, ws.h, t, h, i, e, k, s)) != MX_OK) return st;
   if ((st = launch_down(ws.h, ws.gates, w_down, s_down, sv, ws.dpart, t, h, i, e, k, s)) != MX_OK) return st;
   return launch_combine(ws.dpart, ws.gates, y, t, h, k, s);
+}
+
+int moe_mxfp4_forward_persistent(const uint16_t* x, const float* router_logits, int64_t top_k,
+                                 const uint8_t* w_gate_up, const uint8_t* s_gate_up, const uint8_t* w_down,
+                                 const uint8_t* s_down, uint16_t* y, int64_t T, int64_t H, int64_t I, int64_t E,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !router_logits || !w_gate_up || !s_gate_up || !w_down || !s_down || !y) return MX_ERR_NULL;
+  int st = check_moe_sizes(T, E, top_k);
+  if (st != MX_OK) return st;
+  if ((st = check_expert_dims(H, I)) != MX_OK) return st;
+  if (!fused_layer_fits((int)T, (int)E, (int)top_k, (int)H, (int)I)) return MX_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(w_gate_up, 16) || !aligned(w_down, 16) || !aligned(s_gate_up, 16) ||
+      !aligned(s_down, 16) || !aligned(y, 8) || !aligned(router_logits, 4))
+    return MX_ERR_ALIGN;
+  if (!workspace || !aligned(workspace, 256)) return MX_ERR_WORKSPACE;
+  const MoeWorkspace ws = moe_workspace_carve(workspace, T, H, I, E, top_k);
+  if (workspace_bytes < ws.bytes) return MX_ERR_WORKSPACE;
+  return launch_moe_fused(x, router_logits, w_gate_up, s_gate_up, w_down, s_down, ws.h, ws.dpart, y, ws.ctl, (int)T,
+                          (int)H, (int)I, (int)E, (int)top_k, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -8,8 +8,27 @@
 
 namespace mx {
 
+// Control words at the start of the workspace (int32 indices): the single-launch layer's
+// counters, zero between calls.
+constexpr int CTL_GU_DONE = 0;  // gate_up items whose h rows are written
+constexpr int CTL_EXIT = 1;     // workgroups that have finished
+constexpr int CTL_ERR = 2;      // set to 1 by a wait that gave up (sticky)
+constexpr int CTL_QUAD0 = 64;   // per down column quad: items finished
+constexpr int CTL_MAX_QUADS = 1024;
+// Replicas of the "every h row written" flag, one 512-byte line apart, so that the
+// workgroups' polls spread over many memory channels instead of queueing on one.
+constexpr int CTL_READY0 = 2048;
+constexpr int CTL_READY_REPLICAS = 64;
+constexpr int CTL_READY_STRIDE = 128;
+static_assert(CTL_QUAD0 + CTL_MAX_QUADS <= CTL_READY0, "control block layout");
+static_assert((CTL_READY0 + CTL_READY_REPLICAS * CTL_READY_STRIDE) * 4 == MX_WORKSPACE_CTL_BYTES, "control block size");
+
+// Largest T the single-launch layer takes.
+constexpr int MX_FUSED_MAX_TOKENS = 16;
+
 // Layout of the moe_mxfp4_forward workspace, carved in this order, 256-byte aligned.
 struct MoeWorkspace {
+  int32_t* ctl;           // [MX_WORKSPACE_CTL_BYTES / 4] control words
   int32_t* ids;           // [T*k]
   float* gates;           // [T*k]
   int32_t* counts;        // [E]
@@ -55,5 +74,10 @@ int launch_gate_up(const uint16_t* x, const uint8_t* wgu, const uint8_t* sgu, co
 int launch_down(const uint16_t* h, const float* gates, const uint8_t* wd, const uint8_t* sd, const SortView& sv,
                 float* dpart, int T, int H, int I, int E, int k, hipStream_t stream);
 int launch_combine(const float* dpart, const float* gates, uint16_t* y, int T, int H, int k, hipStream_t stream);
+// The whole layer as one persistent launch (small T); fused_layer_fits says when it applies.
+bool fused_layer_fits(int T, int E, int k, int H, int I);
+int launch_moe_fused(const uint16_t* x, const float* logits, const uint8_t* wgu, const uint8_t* sgu, const uint8_t* wd,
+                     const uint8_t* sd, uint16_t* hbuf, float* dpart, uint16_t* y, int32_t* ctl, int T, int H, int I,
+                     int E, int k, hipStream_t stream);
 
 }  // namespace mx

@@ -197,7 +197,7 @@ __device__ __forceinline__ void xchunk_load(const P& p, const XChunk& ch, u32x4 
     const int rs = q >> 5, pc = q & 31;
     const int s = (int)(((uint32_t)rs * inv) >> 16), m = rs - s * R;
     const int ro = __builtin_amdgcn_ds_bpermute(m << 2, myoff);
-    xv[r] = ld16(p.xact + (size_t)ro + (size_t)(ch.c0 + s) * SEG_K + pc * 8);
+    xv[r] = p.xload(p.xact + (size_t)ro + (size_t)(ch.c0 + s) * SEG_K + pc * 8);
   }
 }
 
@@ -271,6 +271,8 @@ __device__ __forceinline__ void segment_compute(u32x4 (&w)[NS][2], const uint8_t
 // Drive one workgroup over its items.  Policy P provides:
 //   static constexpr int NS;   int nseg, n_items;   const uint16_t* xact;
 //   bool valid(int it);   ItemInfo info(int it);
+//   u32x4 xload(const uint16_t*)                    -- one 16-byte activation load
+//   void wait_inputs()                              -- before the first activation load
 //   int x_row_offset(const ItemInfo&, int m)        -- element offset of activation row m
 //   void w_setup(const ItemInfo&, int wave, WCursor<NS>&, int lane)   -- sets c.w
 //   const uint8_t* scale_row(const ItemInfo&, int wave, int i, int r) -- scales of row r of subtile i
@@ -350,6 +352,7 @@ __device__ __forceinline__ void stream_items(P& p, uint8_t* __restrict__ xbufs, 
   // first compute waits for one memory round trip, not for the chunk hand-off as well.
   wring_load(rw, cw);
   srun_load<NS>(sreg, cw);
+  p.wait_inputs();
   u32x4 xv[XROUNDS];
   XChunk cur = chunk_of(first, 0);
   xchunk_load(p, cur, xv, tid);

@@ -114,6 +114,24 @@ def test_forward_rejects():
     assert fwd(wb=ws - 1) == MX_ERR_WORKSPACE
 
 
+def test_persistent_forward_rejects():
+    L = m.raw()
+    ws = m.workspace_size(16, 1024, 1024, 64, 8)
+
+    def fwd(x=A, lg=A, k=2, wgu=A, sgu=A, wd=A, sd=A, y=A, T=4, H=1024, I=1024, E=8, w=A, wb=ws):
+        return L.moe_mxfp4_forward_persistent(x, lg, k, wgu, sgu, wd, sd, y, T, H, I, E, w, wb, None)
+
+    assert fwd(lg=None) == MX_ERR_NULL
+    assert fwd(T=0) == MX_ERR_SHAPE
+    assert fwd(T=17) == MX_ERR_SHAPE           # beyond the single-launch limit of 16 tokens
+    assert fwd(T=16, k=9, E=64) == MX_ERR_SHAPE  # 144 > 128 routed slots
+    assert fwd(T=4, k=33, E=64) == MX_ERR_SHAPE
+    assert fwd(H=1536) == MX_ERR_SHAPE
+    assert fwd(x=MIS) == MX_ERR_ALIGN
+    assert fwd(w=None) == MX_ERR_WORKSPACE
+    assert fwd(wb=m.workspace_size(4, 1024, 1024, 8, 2) - 1) == MX_ERR_WORKSPACE
+
+
 def test_workspace_size_grows_with_tokens():
     a = m.workspace_size(1, 7168, 2048, 256, 8)
     b = m.workspace_size(128, 7168, 2048, 384, 8)

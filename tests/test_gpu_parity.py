@@ -333,3 +333,112 @@ def test_stage_hooks_match_forward(dev, mx, shape):
     yo, sm = oracle_moe(cfg, x, logits, host)
     worst = check_bound(y_hooks, yo, sm, MOE_REL, f"hooks {shape}")
     say(f"  worst ratio {worst:.3g}")
+
+
+# ------------------------------------------------------------------ single-launch layer (T <= 16)
+
+CTL_BYTES = 40960  # MX_WORKSPACE_CTL_BYTES
+
+
+def run_hooks(mx, d, k, T):
+    """The layer as the stage entry points compute it (separate launches)."""
+    ids, gates, srt = mx.moe_route_sort(d["logits"], k)
+    h = mx.moe_gate_up_swiglu(d["x"], d["wgu"], d["sgu"], srt, k)
+    y = mx.moe_down_combine(h, gates, d["wd"], d["sd"], srt, T, k)
+    torch.cuda.synchronize()
+    return to_host_bits(y)
+
+
+FUSED_EDGES = [
+    dict(T=16, H=1024, I=1024, E=64, k=8),     # 128 slots: the largest single-launch step
+    dict(T=4, H=1024, I=1024, E=1024, k=32),   # 1024 experts (16 logits per lane), top-32
+    dict(T=16, H=1024, I=1024, E=512, k=8),    # 8 logits per lane, mostly one row per expert
+    dict(T=1, H=1024, I=1024, E=1, k=1),       # one expert, one row
+    dict(T=13, H=3072, I=1024, E=3, k=2),      # 13 rows on some experts
+    dict(T=16, H=1024, I=2048, E=2, k=1),      # 16 rows, a full row group, on some expert
+]
+
+
+@pytest.mark.parametrize("shape", FUSED_EDGES, ids=[f"T{s['T']}_H{s['H']}_I{s['I']}_E{s['E']}_k{s['k']}"
+                                                    for s in FUSED_EDGES])
+def test_single_launch_layer(dev, mx, shape):
+    """The persistent single-launch layer: within the oracle bound, bit-identical to the
+    stage entry points and to the default forward, and the workspace control words are zero
+    after the call (no wait gave up)."""
+    cfg = synthetic.MoEConfig("fused", routing="normal", e_lo=-8, e_hi=-2, seed=shape["T"] * 31 + shape["E"], **shape)
+    say("single-launch layer", shape)
+    small = cfg.E <= 64
+    host = synthetic.moe_inputs_host(cfg) if small else None
+    d, x, logits = moe_device_inputs(cfg, dev, host)
+    ws = mx.workspace(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, dev)
+    y = mx.moe_mxfp4_forward(d["x"], d["logits"], cfg.k, d["wgu"], d["sgu"], d["wd"], d["sd"], ws=ws,
+                             persistent=True)
+    torch.cuda.synchronize()
+    got = to_host_bits(y)
+    assert not ws[:CTL_BYTES].any().item(), "control words not reset"
+    assert np.array_equal(run_hooks(mx, d, cfg.k, cfg.T), got)
+    assert np.array_equal(run_moe(mx, d, cfg.k), got)
+    w_host = host if small else {key: d[key].cpu().numpy() for key in ("wgu", "sgu", "wd", "sd")}
+    tok = np.arange(cfg.T, dtype=np.int32) if small else np.array([0, cfg.T // 2, cfg.T - 1], np.int32)
+    yo, sm = oracle_moe(cfg, x, logits, w_host, tokens=tok)
+    worst = check_bound(got[tok], yo, sm, MOE_REL, f"single-launch {shape}")
+    say(f"  worst ratio {worst:.3g}")
+
+
+def test_single_launch_back_to_back_sizes(dev, mx):
+    """Persistent calls of different sizes on one workspace, back to back without
+    synchronizing and mixed with default forwards: each persistent call finds the control
+    words as the previous one left them."""
+    shapes = [dict(T=16, H=1024, I=1024, E=32, k=8), dict(T=2, H=1024, I=1024, E=32, k=8),
+              dict(T=7, H=1024, I=1024, E=32, k=4), dict(T=40, H=1024, I=1024, E=32, k=2),
+              dict(T=1, H=1024, I=1024, E=32, k=8)]
+    say("single-launch layer, back-to-back sizes")
+    ws = mx.workspace(40, 1024, 1024, 32, 8, dev)
+    runs = []
+    for i, s in enumerate(shapes):
+        cfg = synthetic.MoEConfig("b2b", routing="normal", e_lo=-8, e_hi=-2, seed=100 + i, **s)
+        host = synthetic.moe_inputs_host(cfg)
+        d, x, logits = moe_device_inputs(cfg, dev, host)
+        y = mx.moe_mxfp4_forward(d["x"], d["logits"], cfg.k, d["wgu"], d["sgu"], d["wd"], d["sd"], ws=ws,
+                                 persistent=cfg.T <= 16)
+        runs.append((cfg, host, x, logits, y))
+    torch.cuda.synchronize()
+    assert not ws[:CTL_BYTES].any().item()
+    for cfg, host, x, logits, y in runs:
+        yo, sm = oracle_moe(cfg, x, logits, host)
+        check_bound(to_host_bits(y), yo, sm, MOE_REL, f"back-to-back T={cfg.T}")
+
+
+@pytest.mark.parametrize("T,persistent", [(4, True), (4, False), (20, False)])
+def test_forward_graph_replays(dev, mx, T, persistent):
+    """The forward captured in a HIP graph: every replay, with eager work and
+    synchronizations between replays, gives the eager result bit for bit."""
+    cfg = synthetic.MoEConfig("graph", T=T, H=1024, I=1024, E=16, k=4, routing="normal", e_lo=-8, e_hi=-2, seed=T)
+    host = synthetic.moe_inputs_host(cfg)
+    say("forward graph replays, T =", T, "persistent =", persistent)
+    d, x, logits = moe_device_inputs(cfg, dev, host)
+    ws = mx.workspace(T, cfg.H, cfg.I, cfg.E, cfg.k, dev)
+    out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
+    fwd = lambda: mx.moe_mxfp4_forward(d["x"], d["logits"], cfg.k, d["wgu"], d["sgu"], d["wd"], d["sd"], out=out,
+                                       ws=ws, persistent=persistent)
+    fwd()
+    torch.cuda.synchronize()
+    ref = to_host_bits(out)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            fwd()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    for r in range(4):
+        out.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host_bits(out), ref), f"replay {r}"
+        fwd()  # eager work between replays
+        torch.cuda.synchronize()
+    assert not ws[:CTL_BYTES].any().item()
+    yo, sm = oracle_moe(cfg, x, logits, host)
+    check_bound(ref, yo, sm, MOE_REL, f"graph T={T}")
