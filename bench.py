@@ -38,7 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 # their hash, so measured traffic is only reported for the kernel it was measured on
 GATE_UP_SOURCES = ("mxfp4_weight_moe_amd/build.py", "mxfp4_weight_moe_amd/csrc/mx_device.hpp",
                    "mxfp4_weight_moe_amd/csrc/mx_internal.hpp", "mxfp4_weight_moe_amd/csrc/mx_stream.hpp",
-                   "mxfp4_weight_moe_amd/csrc/moe_experts.hip")
+                   "mxfp4_weight_moe_amd/csrc/moe_policies.hpp", "mxfp4_weight_moe_amd/csrc/moe_experts.hip")
 GATE_UP_COUNTERS = os.path.join(ROOT, "profiles", "moe_gate_up_kernel.moe_t32_zipf.hbm_counters.txt")
 
 
@@ -151,13 +151,13 @@ def main():
                offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
                sorted_slots=torch.empty(T * k, dtype=torch.int32, device=dev),
                active=torch.empty(E, dtype=torch.int32, device=dev),
-               num_active=torch.empty(1, dtype=torch.int32, device=dev))
+               num_active=torch.empty(2, dtype=torch.int32, device=dev))
     h = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
     names = ("layer",) if args.persistent else ("route_sort", "gate_up", "down_combine")
     n_active = []
     for lay in layers:
         mx.moe_route_sort(lay["logits"], k, ids=ids, gates=gates, out=srt)
-        n_active.append(int(srt["num_active"].item()))
+        n_active.append(int(srt["num_active"][0].item()))
     log(f"[bench] inputs resident: {torch.cuda.memory_allocated() / 2**30:.1f} GiB; active experts {n_active}")
 
     def forward(lay):
@@ -176,7 +176,7 @@ def main():
         e[0].record(stream)
         mx.moe_route_sort(lay["logits"], k, ids=ids, gates=gates, out=srt)
         e[1].record(stream)
-        mx.moe_gate_up_swiglu(lay["x"], w["wgu"], w["sgu"], srt, k, h=h)
+        mx.moe_gate_up_swiglu(lay["x"], w["wgu"], w["sgu"], srt, k, h=h, ws=ws)
         e[2].record(stream)
         mx.moe_down_combine(h, gates, w["wd"], w["sd"], srt, T, k, out=lay["y"], ws=ws)
         e[3].record(stream)

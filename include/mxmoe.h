@@ -102,7 +102,8 @@ MX_API int moe_route_topk(const float* logits, int64_t T, int64_t E, int64_t top
  *   offsets      int32 [E + 1]   exclusive prefix sum of counts
  *   sorted_slots int32 [T*top_k] flat slots in sorted order
  *   active       int32 [E]       experts with counts > 0, ascending; -1 after the last
- *   num_active   int32 [1]
+ *   num_active   int32 [2]       the number of active experts, then the largest count
+ *                                (the expert GEMMs use it to bound their row groups)
  */
 MX_API int moe_sort_by_expert(const int32_t* ids, int64_t T, int64_t top_k, int64_t E, int32_t* counts,
                        int32_t* offsets, int32_t* sorted_slots, int32_t* active, int32_t* num_active,
@@ -123,18 +124,21 @@ MX_API int moe_route_sort(const float* logits, int64_t T, int64_t E, int64_t top
  * slot f = sorted_slots[p] routed to expert e (offsets[e] <= p < offsets[e+1]) of token
  * t = f / top_k:  h[p, n] = bf16_rne( silu(g_n) * u_n ) with g, u as in moe_mxfp4_forward.
  *   h  bf16 [T*top_k, I] (written; rows in sorted-slot order).  Other arguments and limits
- *   as for moe_mxfp4_forward.  Each routed expert's gate_up weights are read once.
+ *   as for moe_mxfp4_forward, including the workspace, whose control words the call uses
+ *   (to deal out its work) and leaves zero.  Each routed expert's gate_up weights are read
+ *   once per 16 rows routed to it.
  */
 MX_API int moe_gate_up_swiglu(const uint16_t* x, const uint8_t* w_gate_up, const uint8_t* s_gate_up,
                               const int32_t* counts, const int32_t* offsets, const int32_t* sorted_slots,
                               const int32_t* active, const int32_t* num_active, uint16_t* h, int64_t T, int64_t H,
-                              int64_t I, int64_t E, int64_t top_k, void* stream);
+                              int64_t I, int64_t E, int64_t top_k, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 /*
  * Stage hook: the down GEMM with the gate-weighted combine, from gate_up's h and the sort
  * result:  y[t, n] = bf16_rne( sum_j gates[t, j] * sum_i h[p(t,j), i] * Wd[e][n, i] ), where
  * p(t, j) is the sorted position of slot t*top_k + j.  Uses `workspace` (at least
- * moe_mxfp4_workspace_size bytes, 256-byte aligned) as scratch.
+ * moe_mxfp4_workspace_size bytes, 256-byte aligned, control words zero) as scratch.
  */
 MX_API int moe_down_combine(const uint16_t* h, const float* gates, const uint8_t* w_down, const uint8_t* s_down,
                             const int32_t* counts, const int32_t* offsets, const int32_t* sorted_slots,
@@ -142,10 +146,10 @@ MX_API int moe_down_combine(const uint16_t* h, const float* gates, const uint8_t
                             int64_t I, int64_t E, int64_t top_k, void* workspace, size_t workspace_bytes,
                             void* stream);
 
-/* The first MX_WORKSPACE_CTL_BYTES bytes of a MoE workspace are control words (counters of
- * moe_mxfp4_forward_persistent).  They must be zero before that call first uses the
- * workspace, and every call leaves them zero again; the other calls do not touch them. */
-#define MX_WORKSPACE_CTL_BYTES 40960
+/* The first MX_WORKSPACE_CTL_BYTES bytes of a MoE workspace are control words: counters
+ * through which the workgroups of a launch deal out their work.  They must be zero before
+ * the workspace is first used, and every call leaves them zero again. */
+#define MX_WORKSPACE_CTL_BYTES 57344
 
 /* Bytes of device workspace moe_mxfp4_forward needs for these sizes. */
 MX_API size_t moe_mxfp4_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k);
@@ -168,9 +172,10 @@ MX_API size_t moe_mxfp4_workspace_size(int64_t T, int64_t H, int64_t I, int64_t 
  *   s_down        uint8 [E, H, I/32]
  *   y             bf16 [T, H]   (written)
  *   workspace     device buffer of at least moe_mxfp4_workspace_size(T, H, I, E, top_k)
- *                 bytes, 256-byte aligned; contents need no initialization and are
- *                 overwritten (the control words excepted, which this call does not
- *                 touch).  Calls that share a workspace must not overlap in time.
+ *                 bytes, 256-byte aligned.  Its first MX_WORKSPACE_CTL_BYTES must be zero
+ *                 before its first use (every call leaves them zero); the rest needs no
+ *                 initialization and is overwritten.  Calls that share a workspace must
+ *                 not overlap in time.
  *   1 <= T <= MX_MAX_TOKENS; 1 <= top_k <= min(E, MX_MAX_TOPK); E <= MX_MAX_EXPERTS;
  *   H % 1024 == 0; I % 1024 == 0 (both GEMMs stream 1024 K values per step).
  */
@@ -188,8 +193,6 @@ MX_API int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, int6
  * workgroup that completes a column tile's down outputs combines it.  Results are bit-for-
  * bit those of moe_mxfp4_forward.  Arguments as for moe_mxfp4_forward, plus:
  *   - T <= 16 and T * top_k <= 128 (MX_ERR_SHAPE otherwise);
- *   - the workspace's first MX_WORKSPACE_CTL_BYTES must be zero before its first use
- *     (every call leaves them zero);
  *   - no other work may occupy the GPU's compute units while it runs: its workgroups
  *     wait for one another.  A wait that outlasts any layer by far gives up, leaving y
  *     undefined and the int32 word at byte offset 8 of the workspace set to 1 (sticky;

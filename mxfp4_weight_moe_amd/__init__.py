@@ -39,7 +39,8 @@ _lib.mxfp4_dequantize.argtypes = [_P, _P, _I64, _I64, _P, _P]
 _lib.moe_route_topk.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P]
 _lib.moe_sort_by_expert.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P]
 _lib.moe_route_sort.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P]
-_lib.moe_gate_up_swiglu.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P]
+_lib.moe_gate_up_swiglu.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P,
+                                    ctypes.c_size_t, _P]
 _lib.moe_down_combine.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P,
                                   ctypes.c_size_t, _P]
 _lib.moe_mxfp4_workspace_size.restype = ctypes.c_size_t
@@ -172,7 +173,7 @@ def _sort_out(out: dict | None, T: int, k: int, E: int, dev) -> dict:
     if out is not None:
         _sort_ptrs(out, dev)
         if (out["counts"].numel() != E or out["offsets"].numel() != E + 1 or out["sorted_slots"].numel() != T * k
-                or out["active"].numel() != E or out["num_active"].numel() != 1):
+                or out["active"].numel() != E or out["num_active"].numel() != 2):
             raise ValueError("sort output tensors have the wrong sizes")
         return out
     return dict(
@@ -180,7 +181,7 @@ def _sort_out(out: dict | None, T: int, k: int, E: int, dev) -> dict:
         offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
         sorted_slots=torch.empty(T * k, dtype=torch.int32, device=dev),
         active=torch.empty(E, dtype=torch.int32, device=dev),
-        num_active=torch.empty(1, dtype=torch.int32, device=dev),
+        num_active=torch.empty(2, dtype=torch.int32, device=dev),
     )
 
 
@@ -220,7 +221,7 @@ def moe_route_sort(logits: torch.Tensor, top_k: int, ids: torch.Tensor | None = 
 
 
 def moe_gate_up_swiglu(x: torch.Tensor, W_gate_up: torch.Tensor, S_gate_up: torch.Tensor, sort: dict, top_k: int,
-                       h: torch.Tensor | None = None) -> torch.Tensor:
+                       h: torch.Tensor | None = None, ws: torch.Tensor | None = None) -> torch.Tensor:
     """Stage hook: h [T*k, I] bf16 (rows in sorted-slot order) from a moe_sort_by_expert result."""
     _check(x, "x", torch.bfloat16, 2)
     dev = x.device
@@ -234,8 +235,11 @@ def moe_gate_up_swiglu(x: torch.Tensor, W_gate_up: torch.Tensor, S_gate_up: torc
     if h is None:
         h = torch.empty((T * top_k, I), dtype=torch.bfloat16, device=dev)
     _check(h, "h", torch.bfloat16, 2, dev)
+    if ws is None:
+        ws = workspace(T, H, I, E, top_k, dev)
+    _check(ws, "workspace", torch.uint8, 1, dev)
     st = _lib.moe_gate_up_swiglu(_ptr(x), _ptr(W_gate_up), _ptr(S_gate_up), *_sort_ptrs(sort, dev), _ptr(h), T, H, I,
-                                 E, top_k, _stream(dev))
+                                 E, top_k, _ptr(ws), ws.numel(), _stream(dev))
     _raise(st, "moe_gate_up_swiglu")
     return h
 

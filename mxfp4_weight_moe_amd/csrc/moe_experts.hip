@@ -7,9 +7,12 @@
 //
 //   combine: y[t,:] = bf16(sum_j fl32(gate[t,j] * d[t*k + j,:])), j ascending.
 //
-// Items are dealt round-robin to a persistent grid of workgroups sized to the device, which
-// stream them back to back (mx_stream.hpp).  The number of active experts is read on the
-// device, so there is no host readback.
+// A persistent grid of workgroups sized to the device streams the items back to back
+// (mx_stream.hpp): extra row groups and three first-group items per workgroup dealt
+// statically, the rest claimed from a device counter in the workspace as workgroups become
+// free, so that workgroups finish together however unevenly the items' row counts and the
+// workgroups' memory speeds fall.  The
+// number of active experts is read on the device, so there is no host readback.
 #include "moe_policies.hpp"
 
 namespace mx {
@@ -26,12 +29,13 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_gate_up_kernel(const uint16
                                                                     const uint8_t* __restrict__ wgu,
                                                                     const uint8_t* __restrict__ sgu, SortView sv,
                                                                     uint16_t* __restrict__ h, int H, int I, int k,
-                                                                    int gmax) {
+                                                                    int32_t* claim) {
   using P = GateUpPlain<NS>;
   __shared__ __attribute__((aligned(16))) uint8_t xbufs[2 * P::XCHUNK];
   __shared__ __attribute__((aligned(16))) uint8_t slabs[WG_WAVES][SLAB_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t sslabs[WG_WAVES][sslab_bytes<NS>()];
   __shared__ uint32_t xctr[2];
+  __shared__ int32_t cq[4];
   if (threadIdx.x < 2) xctr[threadIdx.x] = 0u;
   __syncthreads();
   // wave index as a scalar, so every per-item quantity derived from it stays uniform
@@ -42,7 +46,8 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_gate_up_kernel(const uint16
   p.nseg = H / SEG_K;
   p.nquad = I / (P::TILE * WG_WAVES);
   p.na = p.m.num_active();
-  p.n_items = gmax * p.na * p.nquad;
+  p.n_items = ((p.m.max_rows() + 15) >> 4) * p.na * p.nquad;  // row-group levels that exist
+  ClaimedUnits seq{claim, (lds_i32*)cq, p.na * p.nquad, 0, false};
   p.xact = x;
   p.wgu = wgu;
   p.sgu = sgu;
@@ -53,19 +58,22 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_gate_up_kernel(const uint16
   p.kinv = ((1u << 24) + (uint32_t)k - 1u) / (uint32_t)k;
   p.e_codes = (size_t)2 * I * (H / 2);
   p.e_scales = (size_t)2 * I * (H / 32);
-  stream_items<P, GU_SPS>(p, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
+  stream_items<P, GU_SPS>(p, seq, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
+  seq.finish();
 }
 
 template <int NS>
 __global__ void __launch_bounds__(WG_WAVES * 64) moe_down_kernel(const uint16_t* __restrict__ h,
                                                                  const uint8_t* __restrict__ wd,
                                                                  const uint8_t* __restrict__ sd, SortView sv,
-                                                                 float* __restrict__ dpart, int H, int I, int gmax) {
+                                                                 float* __restrict__ dpart, int H, int I,
+                                                                 int32_t* claim) {
   using P = DownPlain<NS>;
   __shared__ __attribute__((aligned(16))) uint8_t xbufs[2 * P::XCHUNK];
   __shared__ __attribute__((aligned(16))) uint8_t slabs[WG_WAVES][SLAB_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t sslabs[WG_WAVES][sslab_bytes<NS>()];
   __shared__ uint32_t xctr[2];
+  __shared__ int32_t cq[4];
   if (threadIdx.x < 2) xctr[threadIdx.x] = 0u;
   __syncthreads();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -75,7 +83,8 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_down_kernel(const uint16_t*
   p.nseg = I / SEG_K;
   p.nquad = H / (P::TILE * WG_WAVES);
   p.na = p.m.num_active();
-  p.n_items = gmax * p.na * p.nquad;
+  p.n_items = ((p.m.max_rows() + 15) >> 4) * p.na * p.nquad;  // row-group levels that exist
+  ClaimedUnits seq{claim, (lds_i32*)cq, p.na * p.nquad, 0, false};
   p.xact = h;
   p.wd = wd;
   p.sd = sd;
@@ -84,7 +93,8 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_down_kernel(const uint16_t*
   p.I = I;
   p.e_codes = (size_t)H * (I / 2);
   p.e_scales = (size_t)H * (I / 32);
-  stream_items<P, DN_SPS>(p, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
+  stream_items<P, DN_SPS>(p, seq, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
+  seq.finish();
 }
 
 // One thread per (token, 4 consecutive outputs): fp32 sum of the gate-weighted slots, j ascending.
@@ -138,23 +148,23 @@ static bool use_half_tiles(K2 k2, K1 k1, int64_t items_full, int& grid) {
   return true;
 }
 
-int launch_gate_up(const uint16_t* x, const uint8_t* wgu, const uint8_t* sgu, const SortView& sv, uint16_t* h, int T,
-                   int H, int I, int E, int k, hipStream_t stream) {
+int launch_gate_up(const uint16_t* x, const uint8_t* wgu, const uint8_t* sgu, const SortView& sv, uint16_t* h,
+                   int32_t* ctl, int T, int H, int I, int E, int k, hipStream_t stream) {
   if (H % (SEG_K * GU_SPS) != 0 || H % (SEG_K * SRUN) != 0 || I % (SUB_ROWS * WG_WAVES) != 0) return MX_ERR_SHAPE;
   const int gmax = row_groups(T);
   const int64_t items_full = (int64_t)gmax * max_active(T, E, k) * (I / (GateUpPlain<2>::TILE * WG_WAVES));
   int grid = 0;
   if (use_half_tiles(moe_gate_up_kernel<2>, moe_gate_up_kernel<1>, items_full, grid))
     hipLaunchKernelGGL(moe_gate_up_kernel<1>, dim3(grid), dim3(WG_WAVES * 64), 0, stream, x, wgu, sgu, sv, h, H, I, k,
-                       gmax);
+                       ctl + CTL_CLAIM_GU);
   else
     hipLaunchKernelGGL(moe_gate_up_kernel<2>, dim3(grid), dim3(WG_WAVES * 64), 0, stream, x, wgu, sgu, sv, h, H, I, k,
-                       gmax);
+                       ctl + CTL_CLAIM_GU);
   return hip_status(hipGetLastError());
 }
 
 int launch_down(const uint16_t* h, const float* gates, const uint8_t* wd, const uint8_t* sd, const SortView& sv,
-                float* dpart, int T, int H, int I, int E, int k, hipStream_t stream) {
+                float* dpart, int32_t* ctl, int T, int H, int I, int E, int k, hipStream_t stream) {
   (void)gates;  // applied by the combine
   if (I % (SEG_K * DN_SPS) != 0 || I % (SEG_K * SRUN) != 0 || H % (2 * SUB_ROWS * WG_WAVES) != 0) return MX_ERR_SHAPE;
   const int gmax = row_groups(T);
@@ -162,10 +172,10 @@ int launch_down(const uint16_t* h, const float* gates, const uint8_t* wd, const 
   int grid = 0;
   if (use_half_tiles(moe_down_kernel<2>, moe_down_kernel<1>, items_full, grid))
     hipLaunchKernelGGL(moe_down_kernel<1>, dim3(grid), dim3(WG_WAVES * 64), 0, stream, h, wd, sd, sv, dpart, H, I,
-                       gmax);
+                       ctl + CTL_CLAIM_DN);
   else
     hipLaunchKernelGGL(moe_down_kernel<2>, dim3(grid), dim3(WG_WAVES * 64), 0, stream, h, wd, sd, sv, dpart, H, I,
-                       gmax);
+                       ctl + CTL_CLAIM_DN);
   return hip_status(hipGetLastError());
 }
 

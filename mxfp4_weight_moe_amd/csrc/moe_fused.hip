@@ -163,6 +163,8 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_fused_kernel(
   fused_route_sort<PER>(logits, T, E, k, xbufs);
   const LdsSort meta;
   const int na = meta.num_active();
+  // items dealt round-robin (T <= 16: one row group per expert, no extra groups)
+  StaticUnits units;
 
   // ---------------------------------------------------------------- gate_up + SwiGLU
   using PG = GateUpPolicy<NSG, LdsSort, FUSED_XCHUNK, true>;
@@ -184,7 +186,7 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_fused_kernel(
     p.kinv = ((1u << 24) + (uint32_t)k - 1u) / (uint32_t)k;
     p.e_codes = (size_t)2 * I * (H / 2);
     p.e_scales = (size_t)2 * I * (H / 32);
-    stream_items<PG, GU_SPS>(p, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
+    stream_items<PG, GU_SPS>(p, units, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
   }
   // Publish: this workgroup's h stores are complete; add its item count.  The workgroup
   // whose count completes the total raises every replica of the ready flag.
@@ -228,7 +230,7 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_fused_kernel(
     p.flag = (lds_i32*)&fsort.h_ready;
     p.ready_target = 1;
     p.wave = wave;
-    stream_items<PD, DN_SPS>(p, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
+    stream_items<PD, DN_SPS>(p, units, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
   }
   wait_own_stores();
   __syncthreads();

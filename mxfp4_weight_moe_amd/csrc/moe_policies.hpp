@@ -11,7 +11,10 @@
 //            for half-width tiles); stores the fp32 down outputs per flat slot.
 //
 // A row group is up to 16 of the expert's routed rows (one MFMA m-tile); experts with more
-// rows have several groups.  Items are ordered group-major, then expert, then column tile.
+// rows have several groups.  Items are numbered group-major, then expert, then column
+// tile quad: it = (g * na + a) * nquad + quad, so the first na * nquad items are the first
+// row groups of every active expert (all valid) and the rest are the extra groups of
+// experts with more than 16 rows (valid only where the expert has that many rows).
 //
 // Two parameters adapt the policies to where they run:
 //   Meta  where the sort outputs come from: GlobalSort (written by an earlier launch, read
@@ -40,6 +43,7 @@ __device__ __forceinline__ int ld_uniform(const int32_t* p, int i) { return ((ci
 struct GlobalSort {
   SortView sv;
   __device__ __forceinline__ int num_active() const { return ld_uniform(sv.num_active, 0); }
+  __device__ __forceinline__ int max_rows() const { return ld_uniform(sv.num_active, 1); }
   __device__ __forceinline__ int expert(int a) const { return ld_uniform(sv.active, a); }
   __device__ __forceinline__ int count(int a) const { return ld_uniform(sv.counts, expert(a)); }
   __device__ __forceinline__ int offset(int a) const { return ld_uniform(sv.offsets, expert(a)); }
@@ -66,7 +70,6 @@ __device__ __forceinline__ u32x4 ld16_coherent(const void* p) {
 // A wait that outlasts SPIN_LIMIT polls (far longer than any layer) raises *err and
 // returns, so a kernel never waits forever.
 constexpr uint32_t SPIN_LIMIT = 1u << 18;
-typedef __attribute__((address_space(3))) int32_t lds_i32;
 
 __device__ __forceinline__ void wait_counter(int32_t* ctr, int target, int32_t* err, lds_i32* flag, int wave) {
   if (wave == 0) {
@@ -104,20 +107,6 @@ __device__ __forceinline__ int group_slot(const Meta& m, int base, int rows, int
   return v;
 }
 
-struct ItemIndex {
-  int a, quad, g;
-};
-
-// item = (g * na + a) * nquad + quad
-__device__ __forceinline__ ItemIndex item_decode(int it, int nquad, int na) {
-  ItemIndex r;
-  const int q = it / nquad;
-  r.quad = it - q * nquad;
-  r.g = q / na;
-  r.a = q - r.g * na;
-  return r;
-}
-
 // Segments per weight step: an item's segments (H / 256 for gate_up, I / 256 for down)
 // must be a multiple of these, which the launchers check.  Activation chunks are a
 // multiple of both, so they end on steps of either kernel.
@@ -132,6 +121,19 @@ constexpr int DN_XCHUNK = 16384;
 static_assert(SUB_ROWS * CHUNK_ALIGN <= XGeom<GU_XCHUNK>::ROWSEGS && SUB_ROWS * CHUNK_ALIGN <= XGeom<DN_XCHUNK>::ROWSEGS,
               "a chunk must hold one step of a full row group");
 
+struct ItemIndex {
+  int a, quad, g;
+};
+
+__device__ __forceinline__ ItemIndex item_decode(int it, int nquad, int na) {
+  ItemIndex r;
+  const int q = it / nquad;
+  r.quad = it - q * nquad;
+  r.g = q / na;
+  r.a = q - r.g * na;
+  return r;
+}
+
 // Fields shared by both expert GEMMs: the work list over (row group, expert, tile quad).
 template <class Meta>
 struct ExpertItems {
@@ -139,6 +141,7 @@ struct ExpertItems {
   int nseg, n_items, nquad, na;
   int xrowsegs;  // row-segments per activation chunk
 
+  __device__ __forceinline__ int first_groups() const { return na * nquad; }
   __device__ __forceinline__ bool valid(int it) const {
     const ItemIndex ix = item_decode(it, nquad, na);
     return ix.g * 16 < m.count(ix.a);
@@ -220,7 +223,7 @@ struct GateUpPolicy : ExpertItems<Meta> {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       g[i] = acc[0][i];
-      if (NS == 2) {
+      if constexpr (NS == 2) {
         u[i] = acc[1][i];
       } else {
         const uint32_t b = __float_as_uint(acc[0][i]);

@@ -51,13 +51,15 @@ struct SortShared {
   uint32_t bits[SORT_WORDS];
   int32_t off[MX_MAX_EXPERTS];
   int32_t wave_sum[SORT_THREADS / 64];
+  int32_t wave_max[SORT_THREADS / 64];
 };
 
 // Counting sort from the token masks (bits must hold every routed (expert, token) pair).
 // A slot (t, j) routed to expert e sets bit t of expert e's mask; because a token's k
 // experts are distinct, the rank of the slot among expert e's slots is the number of set
 // bits below t, which fixes a stable order without any ordering of atomics.  Counts and
-// the active list come from one packed block-wide scan.  `ids` is read for the scatter
+// the active list come from one packed block-wide scan, the largest count from a block
+// maximum.  `ids` is read for the scatter
 // (global or LDS).  Must be called by all SORT_THREADS threads.
 __device__ __forceinline__ void sort_from_bits(SortShared& sh, const int32_t* ids, int T, int k, int E,
                                                int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
@@ -80,6 +82,10 @@ __device__ __forceinline__ void sort_from_bits(SortShared& sh, const int32_t* id
     if (lane >= off) incl += o;
   }
   if (lane == 63) sh.wave_sum[wave] = incl;
+  int most = cnt;  // largest count, over the wavefront
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) most = max(most, __shfl_xor(most, off));
+  if (lane == 0) sh.wave_max[wave] = most;
   __syncthreads();
   if (wave == 0) {
     int wv = (lane < SORT_THREADS / 64) ? sh.wave_sum[lane] : 0;
@@ -105,7 +111,10 @@ __device__ __forceinline__ void sort_from_bits(SortShared& sh, const int32_t* id
   if (e < E && e >= n_act) active[e] = -1;
   if (tid == 0) {
     offsets[E] = total & 0xFFFF;
-    *num_active = n_act;
+    num_active[0] = n_act;
+    int m = 0;
+    for (int w = 0; w < SORT_THREADS / 64; ++w) m = max(m, sh.wave_max[w]);
+    num_active[1] = m;
   }
   __syncthreads();
   for (int f = tid; f < F; f += SORT_THREADS) {

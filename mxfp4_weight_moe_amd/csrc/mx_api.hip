@@ -151,7 +151,7 @@ int moe_route_sort(const float* logits, int64_t T, int64_t E, int64_t top_k, int
 int moe_gate_up_swiglu(const uint16_t* x, const uint8_t* w_gate_up, const uint8_t* s_gate_up, const int32_t* counts,
                        const int32_t* offsets, const int32_t* sorted_slots, const int32_t* active,
                        const int32_t* num_active, uint16_t* h, int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k,
-                       void* stream) {
+                       void* workspace, size_t workspace_bytes, void* stream) {
   if (!x || !w_gate_up || !s_gate_up || !h || !sort_view_ok(counts, offsets, sorted_slots, active, num_active))
     return MX_ERR_NULL;
   int st = check_moe_sizes(T, E, top_k);
@@ -159,8 +159,11 @@ int moe_gate_up_swiglu(const uint16_t* x, const uint8_t* w_gate_up, const uint8_
   if (!aligned(x, 16) || !aligned(w_gate_up, 16) || !aligned(s_gate_up, 16) || !aligned(h, 8) ||
       !sort_view_aligned(counts, offsets, sorted_slots, active, num_active))
     return MX_ERR_ALIGN;
+  if (!workspace || !aligned(workspace, 256)) return MX_ERR_WORKSPACE;
+  const MoeWorkspace ws = moe_workspace_carve(workspace, T, H, I, E, top_k);
+  if (workspace_bytes < ws.bytes) return MX_ERR_WORKSPACE;
   const SortView sv{counts, offsets, sorted_slots, active, num_active};
-  return launch_gate_up(x, w_gate_up, s_gate_up, sv, h, (int)T, (int)H, (int)I, (int)E, (int)top_k,
+  return launch_gate_up(x, w_gate_up, s_gate_up, sv, h, ws.ctl, (int)T, (int)H, (int)I, (int)E, (int)top_k,
                         static_cast<hipStream_t>(stream));
 }
 
@@ -180,7 +183,8 @@ int moe_down_combine(const uint16_t* h, const float* gates, const uint8_t* w_dow
   if (workspace_bytes < ws.bytes) return MX_ERR_WORKSPACE;
   const SortView sv{counts, offsets, sorted_slots, active, num_active};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = launch_down(h, gates, w_down, s_down, sv, ws.dpart, (int)T, (int)H, (int)I, (int)E, (int)top_k, s)) != MX_OK)
+  if ((st = launch_down(h, gates, w_down, s_down, sv, ws.dpart, ws.ctl, (int)T, (int)H, (int)I, (int)E, (int)top_k,
+                        s)) != MX_OK)
     return st;
   return launch_combine(ws.dpart, gates, y, (int)T, (int)H, (int)top_k, s);
 }
@@ -209,8 +213,8 @@ int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, int64_t top
                               ws.active, ws.num_active, s)) != MX_OK)
     return st;
   const SortView sv{ws.counts, ws.offsets, ws.sorted_slots, ws.active, ws.num_active};
-  if ((st = launch_gate_up(x, w_gate_up, s_gate_up, sv, ws.h, t, h, i, e, k, s)) != MX_OK) return st;
-  if ((st = launch_down(ws.h, ws.gates, w_down, s_down, sv, ws.dpart, t, h, i, e, k, s)) != MX_OK) return st;
+  if ((st = launch_gate_up(x, w_gate_up, s_gate_up, sv, ws.h, ws.ctl, t, h, i, e, k, s)) != MX_OK) return st;
+  if ((st = launch_down(ws.h, ws.gates, w_down, s_down, sv, ws.dpart, ws.ctl, t, h, i, e, k, s)) != MX_OK) return st;
   return launch_combine(ws.dpart, ws.gates, y, t, h, k, s);
 }
 

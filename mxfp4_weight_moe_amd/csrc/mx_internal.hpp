@@ -8,18 +8,22 @@
 
 namespace mx {
 
-// Control words at the start of the workspace (int32 indices): the single-launch layer's
-// counters, zero between calls.
-constexpr int CTL_GU_DONE = 0;  // gate_up items whose h rows are written
-constexpr int CTL_EXIT = 1;     // workgroups that have finished
-constexpr int CTL_ERR = 2;      // set to 1 by a wait that gave up (sticky)
-constexpr int CTL_QUAD0 = 64;   // per down column quad: items finished
+// Control words at the start of the workspace (int32 indices), zero between calls: the
+// expert GEMMs' claim counters and the single-launch layer's counters and flags.  Words
+// that many workgroups update sit on lines of their own, 512 bytes apart, so that their
+// traffic spreads over memory channels instead of queueing on one.
+constexpr int CTL_GU_DONE = 0;      // single launch: gate_up items whose h rows are written
+constexpr int CTL_EXIT = 1;         // single launch: workgroups that have finished
+constexpr int CTL_ERR = 2;          // single launch: set to 1 by a wait that gave up (sticky)
+constexpr int CTL_CLAIM_GU = 256;   // gate_up claim classes (16 x 128 words)
+constexpr int CTL_CLAIM_DN = 2304;  // down claim classes (16 x 128 words)
+constexpr int CTL_QUAD0 = 4352;     // single launch: per down column quad, items finished
 constexpr int CTL_MAX_QUADS = 1024;
-// Replicas of the "every h row written" flag, one 512-byte line apart, so that the
-// workgroups' polls spread over many memory channels instead of queueing on one.
-constexpr int CTL_READY0 = 2048;
+// Replicas of the single launch's "every h row written" flag, one 512-byte line apart.
+constexpr int CTL_READY0 = 6144;
 constexpr int CTL_READY_REPLICAS = 64;
 constexpr int CTL_READY_STRIDE = 128;
+static_assert(CTL_CLAIM_DN - CTL_CLAIM_GU >= 16 * 128 && CTL_QUAD0 - CTL_CLAIM_DN >= 16 * 128, "claim classes");
 static_assert(CTL_QUAD0 + CTL_MAX_QUADS <= CTL_READY0, "control block layout");
 static_assert((CTL_READY0 + CTL_READY_REPLICAS * CTL_READY_STRIDE) * 4 == MX_WORKSPACE_CTL_BYTES, "control block size");
 
@@ -69,10 +73,11 @@ int launch_sort(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_
 int launch_route_sort(const float* logits, int T, int E, int k, int32_t* ids, float* gates, int32_t* counts,
                       int32_t* offsets, int32_t* sorted_slots, int32_t* active, int32_t* num_active,
                       hipStream_t stream);
-int launch_gate_up(const uint16_t* x, const uint8_t* wgu, const uint8_t* sgu, const SortView& sv, uint16_t* h, int T,
-                   int H, int I, int E, int k, hipStream_t stream);
+// ctl: the workspace's control words (the expert GEMMs claim their units there)
+int launch_gate_up(const uint16_t* x, const uint8_t* wgu, const uint8_t* sgu, const SortView& sv, uint16_t* h,
+                   int32_t* ctl, int T, int H, int I, int E, int k, hipStream_t stream);
 int launch_down(const uint16_t* h, const float* gates, const uint8_t* wd, const uint8_t* sd, const SortView& sv,
-                float* dpart, int T, int H, int I, int E, int k, hipStream_t stream);
+                float* dpart, int32_t* ctl, int T, int H, int I, int E, int k, hipStream_t stream);
 int launch_combine(const float* dpart, const float* gates, uint16_t* y, int T, int H, int k, hipStream_t stream);
 // The whole layer as one persistent launch (small T); fused_layer_fits says when it applies.
 bool fused_layer_fits(int T, int E, int k, int H, int I);

@@ -79,9 +79,15 @@ struct WRing {
   u32x4 w[SPS][NS][2];
 };
 
+// Position in a workgroup's work: the item `it`, and its ordinal n among the workgroup's
+// first-group items (-1 while it streams extra row groups, which come first).
+struct ItemPos {
+  int n, it;
+};
+
 template <int NS>
 struct WCursor {
-  int it;   // current item
+  ItemPos at;  // current item
   int seg;  // first segment of the step the ring is reloaded with
   const uint8_t* w[NS][2];                 // this lane's code bytes of segment 0 (2 rows)
   const uint8_t* sr[scale_loads<NS>()];    // this lane's scale bytes of segment 0, per load
@@ -133,7 +139,7 @@ struct ItemInfo {
 
 // Per-workgroup cursor over activation chunks.
 struct XChunk {
-  int it;  // item
+  ItemPos at;  // item
   int c0;  // first segment of the chunk within the item
   int ns;  // segments in the chunk
   ItemInfo info;
@@ -268,9 +274,100 @@ __device__ __forceinline__ void segment_compute(u32x4 (&w)[NS][2], const uint8_t
   }
 }
 
+// The items of a workgroup, in three phases:
+//   A  extra row groups (items it >= F, F = na * nquad, valid only for experts with more
+//      than 16 rows; few), dealt round-robin, first, because each is as long as any other
+//      item and leaving them to the end would lengthen the tail;
+//   B  first-group items wg, wg + G, wg + 2G (STATIC_UNITS of them; G workgroups);
+//   C  further first-group items: dealt round-robin too (StaticUnits), or claimed from a
+//      device counter as workgroups become free (ClaimedUnits), so that workgroups that
+//      stream faster, or drew lighter items, take more and all finish together.
+// unit(n) gives the n-th phase-B/C item; enter(n) is called when the chunk loader, which
+// reaches every item first, enters the n-th.
+constexpr int STATIC_UNITS = 3;
+struct StaticUnits {
+  __device__ __forceinline__ int unit(int n) const { return (int)blockIdx.x + n * (int)gridDim.x; }
+  __device__ __forceinline__ void enter(int) {}
+};
+
+// Claims: a launch with at most 5G first-group items claims nothing.  Otherwise workgroup
+// w belongs to claim class j = w mod K (K = 16 classes, or G if fewer), and class j owns
+// the dynamic items 3G + j, 3G + j + K, ...: its workgroups draw them in turn from the
+// class's own counter.  Classes keep each counter's claims few (simultaneous claims on
+// one word queue behind each other and slow every stream through its memory channel), and
+// interleaving keeps their work alike.  No claim is issued at the start: the claim for the
+// item at ordinal m + 2 is issued when the chunk loader enters ordinal m, and its result
+// is written to the LDS queue when the loader enters ordinal m + 1, by which time it has
+// long returned, so a claim never stalls the stream.  Claims are monotonic, so once a
+// workgroup draws an item past the end every later claim of its class is past it too, and
+// no item is lost.  `ctr` points at the class counters, CLAIM_STRIDE words apart; each
+// class has an exit counter CLAIM_EXIT words after its claim counter (zero between
+// launches; the class's last workgroup to finish resets both).
+constexpr int DYNAMIC_MIN = 5;
+static_assert(DYNAMIC_MIN >= STATIC_UNITS, "a dynamic launch has every static item");
+constexpr int CLAIM_CLASSES = 16;
+constexpr int CLAIM_STRIDE = 128;  // words between classes (512 bytes)
+constexpr int CLAIM_EXIT = 32;     // exit counter, one 128-byte line after the claim counter
+typedef __attribute__((address_space(3))) int32_t lds_i32;
+struct ClaimedUnits {
+  int32_t* ctr;
+  lds_i32* q;      // 4 LDS words: claim results for ordinals n & 3
+  int n_first;     // first-group items of the launch
+  int pending;     // thread 0: the last claim issued
+  bool claimed;    // thread 0: a claim was issued
+  // Claiming pays once workgroups average more than DYNAMIC_MIN items; below that the
+  // claims, issued in near lockstep, cost more than the balance gains.
+  __device__ __forceinline__ bool dynamic() const { return n_first > DYNAMIC_MIN * (int)gridDim.x; }
+  __device__ __forceinline__ int classes() const { return min(CLAIM_CLASSES, (int)gridDim.x); }
+  __device__ __forceinline__ int cls() const { return (int)blockIdx.x % classes(); }
+  __device__ __forceinline__ int32_t* class_ctr() const { return ctr + cls() * CLAIM_STRIDE; }
+  // An increment-with-wrap (at 2^32 - 1: never reached) rather than an add: the compiler's
+  // atomic optimizer turns a lone thread's add into a wave reduction that consumes the
+  // result at once, which would stall the stream on every claim.
+  __device__ __forceinline__ int claim() const {
+    typedef __attribute__((address_space(1))) uint32_t global_u32;
+    return (int)__builtin_amdgcn_atomic_inc32((volatile global_u32*)class_ctr(), 0xFFFFFFFFu, __ATOMIC_RELAXED,
+                                              "agent");
+  }
+  __device__ __forceinline__ int unit(int n) const {
+    // static launches deal every item round-robin: the 4th is past the end
+    if (n < STATIC_UNITS || !dynamic()) return (int)blockIdx.x + n * (int)gridDim.x;
+    return STATIC_UNITS * (int)gridDim.x + cls() + classes() * __builtin_amdgcn_readfirstlane(q[n & 3]);
+  }
+  // the chunk loader enters ordinal m (m >= 1): publish the claim for ordinal m + 1 (issued
+  // when it entered ordinal m - 1), then claim for ordinal m + 2
+  __device__ __forceinline__ void enter(int m) {
+    if (threadIdx.x == 0 && dynamic()) {
+      if (m + 1 >= STATIC_UNITS) q[(m + 1) & 3] = pending;
+      if (m + 2 >= STATIC_UNITS) {
+        pending = claim();
+        claimed = true;
+      }
+    }
+  }
+  // After the workgroup's last item: its outstanding claim has been performed before the
+  // exit count (its value is waited for), and the class's last workgroup resets the class.
+  __device__ __forceinline__ void finish() {
+    if (threadIdx.x == 0 && dynamic()) {
+      if (claimed) {
+        q[0] = pending;
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the claim has returned
+      }
+      const int K = classes();
+      const int members = ((int)gridDim.x - 1 - cls()) / K + 1;
+      int32_t* c = class_ctr();
+      if (__hip_atomic_fetch_add(c + CLAIM_EXIT, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == members - 1) {
+        __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(c + CLAIM_EXIT, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+};
+
 // Drive one workgroup over its items.  Policy P provides:
 //   static constexpr int NS;   int nseg, n_items;   const uint16_t* xact;
-//   bool valid(int it);   ItemInfo info(int it);
+//   int first_groups();   bool valid(int it);   ItemInfo info(int it);
 //   u32x4 xload(const uint16_t*)                    -- one 16-byte activation load
 //   void wait_inputs()                              -- before the first activation load
 //   int x_row_offset(const ItemInfo&, int m)        -- element offset of activation row m
@@ -282,8 +379,8 @@ __device__ __forceinline__ void segment_compute(u32x4 (&w)[NS][2], const uint8_t
 // `xbufs` is 2 * P::XCHUNK bytes of LDS, `xctr` 2 zeroed LDS counters, `slab` this wave's
 // SLAB_BYTES and `sslab` its sslab_bytes<NS>() of LDS.  nseg must be a multiple of SPS and
 // of SRUN (the launchers check it).
-template <class P, int SPS>
-__device__ __forceinline__ void stream_items(P& p, uint8_t* __restrict__ xbufs, uint32_t* xctr,
+template <class P, int SPS, class Seq>
+__device__ __forceinline__ void stream_items(P& p, Seq& seq, uint8_t* __restrict__ xbufs, uint32_t* xctr,
                                              uint8_t* __restrict__ slab, uint8_t* __restrict__ sslab, int wave,
                                              int lane) {
   constexpr int NS = P::NS;
@@ -292,25 +389,47 @@ __device__ __forceinline__ void stream_items(P& p, uint8_t* __restrict__ xbufs, 
   constexpr int XROUNDS = XGeom<XCHUNK_BYTES>::ROUNDS;
   static_assert(SRUN % SPS == 0, "scale runs end on steps");
   const int tid = wave * 64 + lane;
-  const int wg = blockIdx.x, n_wg = gridDim.x;
   uint32_t lds_wr[2], lds_rd[2];
   for (int q = 0; q < 2; ++q) lds_wr[q] = slab_off((uint32_t)(lane >> 3) + 8u * q, (uint32_t)(lane & 7));
   for (int h = 0; h < 2; ++h) lds_rd[h] = slab_off((uint32_t)(lane & 15), (uint32_t)(lane >> 4) + 4u * h);
   const uint32_t sshift = 8u * (uint32_t)(lane >> 4);
 
-  auto next_valid = [&](int it) {
+  const int n_first = p.first_groups();
+  const int wg = blockIdx.x, n_wg = gridDim.x;
+  // phase A: the next valid extra-group item at or after `it` in this workgroup's stride
+  auto next_extra = [&](int it) {
     while (it < p.n_items && !p.valid(it)) it += n_wg;
     return it;
   };
-  const int first = next_valid(wg);
-  if (first >= p.n_items) return;
+  // The next item after `c` (false past the end).  Only the chunk loader, which reaches
+  // every item first, tells the sequence that a phase-B/C item is entered.
+  auto pos_next = [&](const ItemPos& c, ItemPos& q, bool loader) {
+    if (c.n < 0) {
+      q.n = -1;
+      q.it = next_extra(c.it + n_wg);
+      if (q.it < p.n_items) return true;
+    }
+    q.n = c.n + 1;
+    q.it = seq.unit(q.n);
+    if (q.it >= n_first) return false;
+    if (loader && q.n > 0) seq.enter(q.n);
+    return true;
+  };
+  ItemPos first;
+  first.n = -1;
+  first.it = next_extra(n_first + wg);
+  if (first.it >= p.n_items) {
+    first.n = 0;
+    first.it = seq.unit(0);
+    if (first.it >= n_first) return;
+  }
 
   // ---- weight cursor (per wave): the step the ring is reloaded with.  Once the
   // workgroup's items are exhausted it stays on the last step (re-read, never used).
   WCursor<NS> cw;
-  auto cursor_setup = [&](int it) {
-    const ItemInfo f = p.info(it);
-    cw.it = it;
+  auto cursor_setup = [&](const ItemPos& at) {
+    const ItemInfo f = p.info(at.it);
+    cw.at = at;
     cw.seg = 0;
     p.w_setup(f, wave, cw, lane);
 #pragma unroll
@@ -324,27 +443,27 @@ __device__ __forceinline__ void stream_items(P& p, uint8_t* __restrict__ xbufs, 
     if (cw.seg + SPS < p.nseg) {
       cw.seg += SPS;
     } else {
-      const int nx = next_valid(cw.it + n_wg);
-      if (nx < p.n_items) cursor_setup(nx);
+      ItemPos nx;
+      if (pos_next(cw.at, nx, false)) cursor_setup(nx);
     }
   };
   WRing<NS, SPS> rw;
   u32x4 sreg[SL];  // scales of the next run, loaded one step ahead
 
   // ---- activation chunks (per workgroup): the first one is loaded before the loop
-  auto chunk_of = [&](int it, int c0) {
+  auto chunk_of = [&](const ItemPos& at, int c0) {
     XChunk ch;
-    ch.it = it;
+    ch.at = at;
     ch.c0 = c0;
-    ch.info = p.info(it);
+    ch.info = p.info(at.it);
     ch.ns = min(ch.info.cs, p.nseg - c0);
     return ch;
   };
   auto next_chunk = [&](const XChunk& ch, bool& ok) {
     ok = true;
-    if (ch.c0 + ch.ns < p.nseg) return chunk_of(ch.it, ch.c0 + ch.ns);
-    const int nx = next_valid(ch.it + n_wg);
-    if (nx < p.n_items) return chunk_of(nx, 0);
+    if (ch.c0 + ch.ns < p.nseg) return chunk_of(ch.at, ch.c0 + ch.ns);
+    ItemPos nx;
+    if (pos_next(ch.at, nx, true)) return chunk_of(nx, 0);
     ok = false;
     return ch;
   };

@@ -155,17 +155,18 @@ def route(logits: np.ndarray, k: int):
 
 
 def sort(ids: np.ndarray, E: int):
-    """Returns dict(counts [E], offsets [E+1], sorted_slots [T*k], active [E], num_active)."""
+    """Returns dict(counts [E], offsets [E+1], sorted_slots [T*k], active [E], num_active,
+    max_rows = the largest count)."""
     ids = _c(ids, np.int32)
     T, k = ids.shape
     counts = np.empty(E, np.int32)
     offsets = np.empty(E + 1, np.int32)
     sorted_slots = np.empty(T * k, np.int32)
     active = np.empty(E, np.int32)
-    na = np.zeros(1, np.int32)
+    na = np.zeros(2, np.int32)
     _load().ora_sort(_p(ids), T, k, E, _p(counts), _p(offsets), _p(sorted_slots), _p(active), _p(na))
     return dict(counts=counts, offsets=offsets, sorted_slots=sorted_slots, active=active,
-                num_active=int(na[0]))
+                num_active=int(na[0]), max_rows=int(na[1]))
 
 
 def moe_tokens(x_bits, logits, k, wgu, sgu, wd, sd, T, H, I, E, tokens=None, want_h=False,

@@ -203,7 +203,8 @@ void ora_route(const float* logits, int64_t T, int64_t E, int64_t k, int32_t* id
 /* Counting sort of the T*k flat slots f = t*k + j by expert id: experts
  * ascending, f ascending within an expert.  counts [E]; offsets [E+1]
  * (exclusive prefix sums); sorted_slots [T*k]; active [E] = experts with at
- * least one slot, ascending (entries past num_active are set to -1). */
+ * least one slot, ascending (entries past num_active are set to -1);
+ * num_active [2] = the number of active experts, then the largest count. */
 void ora_sort(const int32_t* ids, int64_t T, int64_t k, int64_t E, int32_t* counts, int32_t* offsets,
               int32_t* sorted_slots, int32_t* active, int32_t* num_active) {
   int64_t F = T * k;
@@ -222,7 +223,11 @@ void ora_sort(const int32_t* ids, int64_t T, int64_t k, int64_t E, int32_t* coun
   for (int64_t e = 0; e < E; ++e)
     if (counts[e] > 0) active[na++] = (int32_t)e;
   for (int64_t e = na; e < E; ++e) active[e] = -1;
-  *num_active = na;
+  int32_t most = 0;
+  for (int64_t e = 0; e < E; ++e)
+    if (counts[e] > most) most = counts[e];
+  num_active[0] = na;
+  num_active[1] = most;
 }
 
 /* ------------------------------------------------------------- MoE layer */

@@ -114,6 +114,31 @@ def test_forward_rejects():
     assert fwd(wb=ws - 1) == MX_ERR_WORKSPACE
 
 
+def test_stage_gemm_hooks_reject():
+    L = m.raw()
+    ws = m.workspace_size(4, 1024, 1024, 8, 2)
+
+    def gu(x=A, h=A, T=4, H=1024, I=1024, E=8, k=2, w=A, wb=ws):
+        return L.moe_gate_up_swiglu(x, A, A, A, A, A, A, A, h, T, H, I, E, k, w, wb, None)
+
+    assert gu(x=None) == MX_ERR_NULL
+    assert gu(h=None) == MX_ERR_NULL
+    assert gu(T=0) == MX_ERR_SHAPE
+    assert gu(H=1536) == MX_ERR_SHAPE
+    assert gu(x=MIS) == MX_ERR_ALIGN
+    assert gu(w=None) == MX_ERR_WORKSPACE
+    assert gu(w=P((1 << 20) + 128)) == MX_ERR_WORKSPACE
+    assert gu(wb=ws - 1) == MX_ERR_WORKSPACE
+
+    def dn(h=A, y=A, T=4, w=A, wb=ws):
+        return L.moe_down_combine(h, A, A, A, A, A, A, A, A, y, T, 1024, 1024, 8, 2, w, wb, None)
+
+    assert dn(y=None) == MX_ERR_NULL
+    assert dn(T=300) == MX_ERR_SHAPE
+    assert dn(w=None) == MX_ERR_WORKSPACE
+    assert dn(wb=ws - 1) == MX_ERR_WORKSPACE
+
+
 def test_persistent_forward_rejects():
     L = m.raw()
     ws = m.workspace_size(16, 1024, 1024, 64, 8)

@@ -74,6 +74,7 @@ def test_sort_matches_stable_argsort(T, E, k):
     assert np.array_equal(r["offsets"], np.concatenate([[0], np.cumsum(counts)]))
     act = np.nonzero(counts)[0]
     assert r["num_active"] == act.size
+    assert r["max_rows"] == counts.max()
     assert np.array_equal(r["active"][: act.size], act) and np.all(r["active"][act.size:] == -1)
 
 
