@@ -18,7 +18,7 @@ intermediate size of 2048.
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field
+from dataclasses import dataclass, replace
 
 import numpy as np
 
@@ -49,12 +49,13 @@ class MoEConfig:
     I: int
     E: int
     k: int
-    routing: str  # "normal" | "zipf" | "uniform"
+    routing: str  # "normal" | "zipf" | "uniform" | "spec"
     e_lo: int = -6
     e_hi: int = 0
     seed: int = 0
     zipf_s: float = 1.1
-    extra: dict = field(default_factory=dict)
+    positions: int = 1        # "spec": speculative positions per request (T = requests x positions)
+    spec_sigma: float = 1.2   # "spec": spread of the per-request expert preference
 
 
 LINEAR_CONFIGS = {
@@ -71,6 +72,10 @@ MOE_CONFIGS = {
     "moe_t32_zipf": MoEConfig("moe_t32_zipf", T=32, H=7168, I=2048, E=256, k=8, routing="zipf"),
     # 32 requests x 4 speculative positions, 384 experts, uniform-random logits
     "moe_t128": MoEConfig("moe_t128", T=128, H=7168, I=2048, E=384, k=8, routing="uniform"),
+    # the same step with the positions of each request routed alike (speculative verify)
+    "moe_spec_t128": MoEConfig("moe_spec_t128", T=128, H=7168, I=2048, E=384, k=8, routing="spec", positions=4),
+    # one request, 4 speculative positions
+    "moe_spec_t4": MoEConfig("moe_spec_t4", T=4, H=7168, I=2048, E=256, k=8, routing="spec", positions=4),
 }
 
 
@@ -81,8 +86,7 @@ def sweep_config(T: int, seed: int = 0) -> MoEConfig:
 
 def small_scale_variant(cfg: MoEConfig) -> MoEConfig:
     """Parity-only variant with scales 2^-12 .. 2^-6 so |g| is O(1) and SiLU is curved."""
-    return MoEConfig(cfg.name + "_smallscale", T=cfg.T, H=cfg.H, I=cfg.I, E=cfg.E, k=cfg.k,
-                     routing=cfg.routing, e_lo=-12, e_hi=-6, seed=cfg.seed, zipf_s=cfg.zipf_s)
+    return replace(cfg, name=cfg.name + "_smallscale", e_lo=-12, e_hi=-6)
 
 
 # --------------------------------------------------------------------------- host (numpy) draws
@@ -91,7 +95,7 @@ def _rng(seed: int, tag: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tag])))
 
 
-TAG_X, TAG_LOGITS, TAG_W, TAG_S, TAG_ZIPF = 1, 2, 3, 4, 5
+TAG_X, TAG_LOGITS, TAG_W, TAG_S, TAG_ZIPF, TAG_SPEC = 1, 2, 3, 4, 5, 6
 
 
 def bf16_bits_normal(shape, seed: int, tag: int = TAG_X) -> np.ndarray:
@@ -120,6 +124,13 @@ def router_logits(cfg: MoEConfig) -> np.ndarray:
              replacement, and gets N(0,1) logits plus 16 on the drawn experts
              (so the drawn set is the top-k, and the gates stay a softmax of
              N(0,1) values).
+    spec   : tokens t = r * positions + p are the speculative positions of request r;
+             each request draws an expert preference b_r ~ N(0, spec_sigma^2) per
+             expert, shared by its positions, and each token gets b_r + N(0,1).  The
+             positions of a request then route to overlapping experts: with
+             spec_sigma = 1.2, a request's 4 positions route to about 1.67 times the
+             distinct experts of its first 2 (11.7 against 7 on the AMD megakernel
+             blog, section "Data Locality"; independent tokens give about 1.95).
     """
     T, E, k = cfg.T, cfg.E, cfg.k
     g = _rng(cfg.seed, TAG_LOGITS)
@@ -138,6 +149,12 @@ def router_logits(cfg: MoEConfig) -> np.ndarray:
             drawn = z.choice(E, size=k, replace=False, p=p)
             base[t, drawn] += np.float32(16.0)
         return base
+    if cfg.routing == "spec":
+        P = cfg.positions
+        R = -(-T // P)
+        b = _rng(cfg.seed, TAG_SPEC).standard_normal(size=(R, E)) * cfg.spec_sigma
+        noise = g.standard_normal(size=(T, E))
+        return (b[np.arange(T) // P] + noise).astype(np.float32)
     raise ValueError(cfg.routing)
 
 
@@ -201,6 +218,5 @@ def moe_weights_device(cfg: MoEConfig, device, layer: int = 0):
 
 def moe_activations(cfg: MoEConfig, layer: int = 0):
     """(x bits [T,H] u16, logits [T,E] f32) on the host; per-layer seeds differ."""
-    c = cfg if layer == 0 else MoEConfig(cfg.name, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.routing,
-                                         cfg.e_lo, cfg.e_hi, cfg.seed + 7919 * layer, cfg.zipf_s)
+    c = cfg if layer == 0 else replace(cfg, seed=cfg.seed + 7919 * layer)
     return bf16_bits_normal((c.T, c.H), c.seed, TAG_X), router_logits(c)

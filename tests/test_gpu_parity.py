@@ -238,7 +238,8 @@ def test_moe_tiny_full_oracle(dev, mx, shape):
     say(f"  worst ratio {worst:.3g}")
 
 
-FULL = [("moe_t4", None), ("moe_t32_zipf", [0, 5, 13, 31]), ("moe_t128", [0, 1, 64, 127])]
+FULL = [("moe_t4", None), ("moe_t32_zipf", [0, 5, 13, 31]), ("moe_t128", [0, 1, 64, 127]),
+        ("moe_spec_t4", None), ("moe_spec_t128", [0, 1, 2, 3, 126])]
 
 
 @pytest.mark.parametrize("name,tokens", FULL, ids=[f[0] for f in FULL])
