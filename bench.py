@@ -123,8 +123,11 @@ def main():
     torch.cuda.set_device(dev)
     cfg = workload_config(args.workload)
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
-    if args.persistent and (T > 16 or T * k > 128):
-        raise SystemExit("--persistent takes T <= 16 and T * top_k <= 128")
+    ns = cfg.n_shared
+    if args.persistent and (T > 16 or T * k > 128 or ns):
+        raise SystemExit("--persistent takes T <= 16, T * top_k <= 128 and no shared experts")
+    # the event pass times each layer as a whole when the stage calls cannot reproduce it
+    whole_layer = args.persistent or ns > 0
     L = max(1, args.layers)
 
     def log(*a):
@@ -143,7 +146,7 @@ def main():
             y=torch.empty((T, H), dtype=torch.bfloat16, device=dev),
             x_bits=x_bits, logits_host=logits,
         ))
-    ws = mx.workspace(T, H, I, E, k, dev)
+    ws = mx.workspace(T, H, I, E + ns, k + ns, dev)
     # buffers of the stage-by-stage pass
     ids = torch.empty((T, k), dtype=torch.int32, device=dev)
     gates = torch.empty((T, k), dtype=torch.float32, device=dev)
@@ -153,22 +156,22 @@ def main():
                active=torch.empty(E, dtype=torch.int32, device=dev),
                num_active=torch.empty(2, dtype=torch.int32, device=dev))
     h = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
-    names = ("layer",) if args.persistent else ("route_sort", "gate_up", "down_combine")
+    names = ("layer",) if whole_layer else ("route_sort", "gate_up", "down_combine")
     n_active = []
     for lay in layers:
         mx.moe_route_sort(lay["logits"], k, ids=ids, gates=gates, out=srt)
-        n_active.append(int(srt["num_active"][0].item()))
+        n_active.append(int(srt["num_active"][0].item()) + ns)  # the shared experts are always read
     log(f"[bench] inputs resident: {torch.cuda.memory_allocated() / 2**30:.1f} GiB; active experts {n_active}")
 
     def forward(lay):
         w = lay["w"]
         mx.moe_mxfp4_forward(lay["x"], lay["logits"], k, w["wgu"], w["sgu"], w["wd"], w["sd"], out=lay["y"], ws=ws,
-                             persistent=args.persistent)
+                             persistent=args.persistent, n_shared=ns)
 
     def staged(i, e, stream):
         lay = layers[i % L]
         w = lay["w"]
-        if args.persistent:  # one kernel per layer
+        if whole_layer:  # one kernel per layer (persistent), or the whole layer's launches
             e[0].record(stream)
             forward(lay)
             e[1].record(stream)
@@ -254,8 +257,8 @@ def main():
     mean_layer_bytes = float(np.mean([layer_bytes[i % L] for i in range(K)]))
     us_per_layer = ms_per_step * 1e3
     eff_gbps = mean_layer_bytes / (us_per_layer * 1e-6) / 1e9
-    if args.persistent:
-        # the single kernel reads the whole layer's bytes
+    if whole_layer:
+        # the single kernel (or the layer's launches together) reads the whole layer's bytes
         gu_bytes = [layer_bytes[i % L] for i in range(KS)]
         gu_ms = stage_ms["layer"]
     else:
@@ -264,13 +267,14 @@ def main():
         gu_ms = stage_ms["gate_up"]
     gu_achieved = float(np.sum(gu_bytes) / (np.sum(gu_ms) * 1e-3) / 1e9)
     roofline = {
-        "kernel": "moe_fused_kernel" if args.persistent else "moe_gate_up_kernel",
+        "kernel": ("moe_fused_kernel" if args.persistent else "layer (all launches)") if whole_layer
+        else "moe_gate_up_kernel",
         "bound": "hbm",
         "achieved": round(gu_achieved, 1),
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
         "frac": round(gu_achieved / HBM_PEAK_GBPS, 4),
-        "traffic": None if args.persistent else measured_traffic(cfg.name),
+        "traffic": None if whole_layer else measured_traffic(cfg.name),
         "avg_launch_us": round(float(np.mean(gu_ms)) * 1e3, 2),
         "launches": len(gu_ms),
         "timing": "HIP events on the launch stream, one pair per launch, right after the timed region",
@@ -289,7 +293,7 @@ def main():
         log(f"[bench] oracle on {n} of {T} tokens, {threads} threads")
         c0 = time.perf_counter()
         oracle.moe_tokens(lay["x_bits"], lay["logits_host"], k, w_host["wgu"], w_host["sgu"], w_host["wd"],
-                          w_host["sd"], T, H, I, E, tokens=toks, nthreads=threads)
+                          w_host["sd"], T, H, I, E, tokens=toks, nthreads=threads, n_shared=ns)
         c1 = time.perf_counter()
         cpu = {
             "value": round((c1 - c0) * (T / n) * 1e6, 1),
@@ -316,7 +320,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": cfg.name, "T": T, "H": H, "I": I, "E": E, "top_k": k, "routing": cfg.routing,
+            "workload": cfg.name, "T": T, "H": H, "I": I, "E": E, "top_k": k, "n_shared": ns, "routing": cfg.routing,
             "weights": "MXFP4 (E2M1 codes, E8M0 scale per 32)", "accumulate": "fp32",
             "layers_cycled": L, "timing": "eager launches" if args.eager else "HIP graph replay",
             "path": "one persistent launch" if args.persistent else "route_sort, gate_up, down, combine launches",

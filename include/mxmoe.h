@@ -185,6 +185,24 @@ MX_API int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, int6
                       void* stream);
 
 /*
+ * The MoE layer with shared experts: every token reads its top_k routed experts (of E,
+ * chosen from router_logits [T, E]) and the n_shared shared experts, whose outputs add to
+ * the gate-weighted routed ones with weight 1 ("Zyphra Inference Wave 2", section
+ * "Quantization": a token uses its top-K routed experts plus the layer's shared experts;
+ * GLM-5.3 has 8 routed and 1 shared of 257).
+ *   y[t,n] = bf16_rne( sum_{j<top_k} gates[t,j] d_{t,j,n} + sum_{s<n_shared} d^S_{t,s,n} )
+ * summed in fp32 with j ascending and then s ascending; d^S is expert E + s's SwiGLU output.
+ * The weight tensors hold E + n_shared experts: [E + n_shared, 2I, H/2] etc., the shared
+ * ones last.  The workspace must hold moe_mxfp4_workspace_size(T, H, I, E + n_shared,
+ * top_k + n_shared) bytes.  0 <= n_shared; E + n_shared <= MX_MAX_EXPERTS;
+ * top_k + n_shared <= MX_MAX_TOPK; other arguments as for moe_mxfp4_forward.
+ */
+MX_API int moe_mxfp4_forward_shared(const uint16_t* x, const float* router_logits, int64_t top_k, int64_t n_shared,
+                                    const uint8_t* w_gate_up, const uint8_t* s_gate_up, const uint8_t* w_down,
+                                    const uint8_t* s_down, uint16_t* y, int64_t T, int64_t H, int64_t I, int64_t E,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The same layer as moe_mxfp4_forward, as ONE persistent launch (the megakernels of the
  * Lithos page, "Specialization unlocks engine performance", and of the AMD megakernel
  * blog, "What Drives the Speedup": workgroups hand data to one another through memory

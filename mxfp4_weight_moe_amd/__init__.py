@@ -47,13 +47,17 @@ _lib.moe_mxfp4_workspace_size.restype = ctypes.c_size_t
 _lib.moe_mxfp4_workspace_size.argtypes = [_I64, _I64, _I64, _I64, _I64]
 _lib.moe_mxfp4_forward.argtypes = [_P, _P, _I64, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]
 _lib.moe_mxfp4_forward_persistent.argtypes = list(_lib.moe_mxfp4_forward.argtypes)
+_lib.moe_mxfp4_forward_shared.argtypes = [_P, _P, _I64, _I64, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P,
+                                          ctypes.c_size_t, _P]
 for _n in ("mx_linear", "mxfp4_dequantize", "moe_route_topk", "moe_sort_by_expert", "moe_route_sort",
-           "moe_gate_up_swiglu", "moe_down_combine", "moe_mxfp4_forward", "moe_mxfp4_forward_persistent"):
+           "moe_gate_up_swiglu", "moe_down_combine", "moe_mxfp4_forward", "moe_mxfp4_forward_persistent",
+           "moe_mxfp4_forward_shared"):
     getattr(_lib, _n).restype = ctypes.c_int
 
 EXPORTED = ("mx_version", "mx_status_string", "mx_linear", "mxfp4_dequantize", "moe_route_topk",
             "moe_sort_by_expert", "moe_route_sort", "moe_gate_up_swiglu", "moe_down_combine",
-            "moe_mxfp4_workspace_size", "moe_mxfp4_forward", "moe_mxfp4_forward_persistent")
+            "moe_mxfp4_workspace_size", "moe_mxfp4_forward", "moe_mxfp4_forward_persistent",
+            "moe_mxfp4_forward_shared")
 
 
 class MxError(RuntimeError):
@@ -289,9 +293,11 @@ def workspace(T: int, H: int, I: int, E: int, top_k: int, device) -> torch.Tenso
 def moe_mxfp4_forward(x: torch.Tensor, router_logits: torch.Tensor, top_k: int, W_gate_up: torch.Tensor,
                       S_gate_up: torch.Tensor, W_down: torch.Tensor, S_down: torch.Tensor,
                       out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
-                      persistent: bool = False) -> torch.Tensor:
+                      persistent: bool = False, n_shared: int = 0) -> torch.Tensor:
     """y[T,H] of the MXFP4 SwiGLU MoE layer (see include/mxmoe.h for the definition).
-    persistent=True runs it as one persistent launch (moe_mxfp4_forward_persistent; T <= 16)."""
+    persistent=True runs it as one persistent launch (moe_mxfp4_forward_persistent; T <= 16).
+    n_shared > 0: the weights hold E routed + n_shared shared experts, router_logits [T, E]
+    (moe_mxfp4_forward_shared)."""
     _check(x, "x", torch.bfloat16, 2)
     dev = x.device
     _check(router_logits, "router_logits", torch.float32, 2, dev)
@@ -299,21 +305,31 @@ def moe_mxfp4_forward(x: torch.Tensor, router_logits: torch.Tensor, top_k: int, 
         _check(t, n, torch.uint8, 3, dev)
     T, H = x.shape
     E = router_logits.shape[1]
+    Ew = E + n_shared
     I = W_down.shape[2] * 2
     if router_logits.shape[0] != T:
         raise ValueError("router_logits must be [T, E]")
-    if (W_gate_up.shape != (E, 2 * I, H // 2) or S_gate_up.shape != (E, 2 * I, H // 32)
-            or W_down.shape != (E, H, I // 2) or S_down.shape != (E, H, I // 32)):
-        raise ValueError("expert weight shapes do not match [E, 2I, H/2], [E, 2I, H/32], [E, H, I/2], [E, H, I/32]")
+    if (W_gate_up.shape != (Ew, 2 * I, H // 2) or S_gate_up.shape != (Ew, 2 * I, H // 32)
+            or W_down.shape != (Ew, H, I // 2) or S_down.shape != (Ew, H, I // 32)):
+        raise ValueError("expert weight shapes do not match [E, 2I, H/2], [E, 2I, H/32], [E, H, I/2], [E, H, I/32] "
+                         "with E routed + n_shared shared experts")
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     _check(out, "out", torch.bfloat16, 2, dev)
     if ws is None:
-        ws = workspace(T, H, I, E, top_k, dev)
+        ws = workspace(T, H, I, Ew, top_k + n_shared, dev)
     _check(ws, "workspace", torch.uint8, 1, dev)
-    name = "moe_mxfp4_forward_persistent" if persistent else "moe_mxfp4_forward"
-    st = getattr(_lib, name)(_ptr(x), _ptr(router_logits), top_k, _ptr(W_gate_up), _ptr(S_gate_up),
-                             _ptr(W_down), _ptr(S_down), _ptr(out), T, H, I, E, _ptr(ws), ws.numel(),
-                             _stream(dev))
+    if n_shared:
+        if persistent:
+            raise ValueError("the single-launch layer has no shared experts")
+        name = "moe_mxfp4_forward_shared"
+        st = _lib.moe_mxfp4_forward_shared(_ptr(x), _ptr(router_logits), top_k, n_shared, _ptr(W_gate_up),
+                                           _ptr(S_gate_up), _ptr(W_down), _ptr(S_down), _ptr(out), T, H, I, E,
+                                           _ptr(ws), ws.numel(), _stream(dev))
+    else:
+        name = "moe_mxfp4_forward_persistent" if persistent else "moe_mxfp4_forward"
+        st = getattr(_lib, name)(_ptr(x), _ptr(router_logits), top_k, _ptr(W_gate_up), _ptr(S_gate_up),
+                                 _ptr(W_down), _ptr(S_down), _ptr(out), T, H, I, E, _ptr(ws), ws.numel(),
+                                 _stream(dev))
     _raise(st, name)
     return out

@@ -19,8 +19,8 @@ namespace mx {
 
 template <int NS>
 using GateUpPlain = GateUpPolicy<NS, GlobalSort, GU_XCHUNK, false>;
-template <int NS>
-using DownPlain = DownPolicy<NS, GlobalSort, DN_XCHUNK, false>;
+template <int NS, class SR>
+using DownPlain = DownPolicy<NS, GlobalSort, DN_XCHUNK, false, SR>;
 
 // ------------------------------------------------------------------ kernels
 
@@ -33,7 +33,7 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_gate_up_kernel(const uint16
   using P = GateUpPlain<NS>;
   __shared__ __attribute__((aligned(16))) uint8_t xbufs[2 * P::XCHUNK];
   __shared__ __attribute__((aligned(16))) uint8_t slabs[WG_WAVES][SLAB_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t sslabs[WG_WAVES][sslab_bytes<NS>()];
+  __shared__ __attribute__((aligned(16))) uint8_t sslabs[WG_WAVES][P::Scales::template slab_bytes<NS>()];
   __shared__ uint32_t xctr[2];
   __shared__ int32_t cq[4];
   if (threadIdx.x < 2) xctr[threadIdx.x] = 0u;
@@ -62,16 +62,17 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_gate_up_kernel(const uint16
   seq.finish();
 }
 
-template <int NS>
+// SR, SPS: scale run and weight step (ScaleRun4, DN_SPS when I % 1024 == 0, else 1 and 1)
+template <int NS, class SR, int SPS>
 __global__ void __launch_bounds__(WG_WAVES * 64) moe_down_kernel(const uint16_t* __restrict__ h,
                                                                  const uint8_t* __restrict__ wd,
                                                                  const uint8_t* __restrict__ sd, SortView sv,
                                                                  float* __restrict__ dpart, int H, int I,
                                                                  int32_t* claim) {
-  using P = DownPlain<NS>;
+  using P = DownPlain<NS, SR>;
   __shared__ __attribute__((aligned(16))) uint8_t xbufs[2 * P::XCHUNK];
   __shared__ __attribute__((aligned(16))) uint8_t slabs[WG_WAVES][SLAB_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t sslabs[WG_WAVES][sslab_bytes<NS>()];
+  __shared__ __attribute__((aligned(16))) uint8_t sslabs[WG_WAVES][P::Scales::template slab_bytes<NS>()];
   __shared__ uint32_t xctr[2];
   __shared__ int32_t cq[4];
   if (threadIdx.x < 2) xctr[threadIdx.x] = 0u;
@@ -93,7 +94,7 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_down_kernel(const uint16_t*
   p.I = I;
   p.e_codes = (size_t)H * (I / 2);
   p.e_scales = (size_t)H * (I / 32);
-  stream_items<P, DN_SPS>(p, seq, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
+  stream_items<P, SPS>(p, seq, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
   seq.finish();
 }
 
@@ -163,20 +164,31 @@ int launch_gate_up(const uint16_t* x, const uint8_t* wgu, const uint8_t* sgu, co
   return hip_status(hipGetLastError());
 }
 
+template <class SR, int SPS>
+static int launch_down_run(const uint16_t* h, const uint8_t* wd, const uint8_t* sd, const SortView& sv, float* dpart,
+                           int32_t* ctl, int T, int H, int I, int E, int k, hipStream_t stream) {
+  const int gmax = row_groups(T);
+  const int64_t items_full = (int64_t)gmax * max_active(T, E, k) * (H / (DownPlain<2, SR>::TILE * WG_WAVES));
+  int grid = 0;
+  if (use_half_tiles(moe_down_kernel<2, SR, SPS>, moe_down_kernel<1, SR, SPS>, items_full, grid))
+    hipLaunchKernelGGL((moe_down_kernel<1, SR, SPS>), dim3(grid), dim3(WG_WAVES * 64), 0, stream, h, wd, sd, sv, dpart,
+                       H, I, ctl + CTL_CLAIM_DN);
+  else
+    hipLaunchKernelGGL((moe_down_kernel<2, SR, SPS>), dim3(grid), dim3(WG_WAVES * 64), 0, stream, h, wd, sd, sv, dpart,
+                       H, I, ctl + CTL_CLAIM_DN);
+  return hip_status(hipGetLastError());
+}
+
 int launch_down(const uint16_t* h, const float* gates, const uint8_t* wd, const uint8_t* sd, const SortView& sv,
                 float* dpart, int32_t* ctl, int T, int H, int I, int E, int k, hipStream_t stream) {
   (void)gates;  // applied by the combine
-  if (I % (SEG_K * DN_SPS) != 0 || I % (SEG_K * SRUN) != 0 || H % (2 * SUB_ROWS * WG_WAVES) != 0) return MX_ERR_SHAPE;
-  const int gmax = row_groups(T);
-  const int64_t items_full = (int64_t)gmax * max_active(T, E, k) * (H / (DownPlain<2>::TILE * WG_WAVES));
-  int grid = 0;
-  if (use_half_tiles(moe_down_kernel<2>, moe_down_kernel<1>, items_full, grid))
-    hipLaunchKernelGGL(moe_down_kernel<1>, dim3(grid), dim3(WG_WAVES * 64), 0, stream, h, wd, sd, sv, dpart, H, I,
-                       ctl + CTL_CLAIM_DN);
-  else
-    hipLaunchKernelGGL(moe_down_kernel<2>, dim3(grid), dim3(WG_WAVES * 64), 0, stream, h, wd, sd, sv, dpart, H, I,
-                       ctl + CTL_CLAIM_DN);
-  return hip_status(hipGetLastError());
+  if (H % (2 * SUB_ROWS * WG_WAVES) != 0) return MX_ERR_SHAPE;
+  // down's reduction length is I: 4-segment scale runs and 2-segment steps when I % 1024 == 0,
+  // one-segment runs and steps for any other multiple of 256
+  if (I % (SEG_K * SRUN) == 0 && I % (SEG_K * DN_SPS) == 0)
+    return launch_down_run<ScaleRun4, DN_SPS>(h, wd, sd, sv, dpart, ctl, T, H, I, E, k, stream);
+  if (I % SEG_K == 0) return launch_down_run<ScaleRun<1>, 1>(h, wd, sd, sv, dpart, ctl, T, H, I, E, k, stream);
+  return MX_ERR_SHAPE;
 }
 
 int launch_combine(const float* dpart, const float* gates, uint16_t* y, int T, int H, int k, hipStream_t stream) {

@@ -154,7 +154,7 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_fused_kernel(
     float* dpart, uint16_t* __restrict__ y, int32_t* ctl, int T, int H, int I, int E, int k) {
   __shared__ __attribute__((aligned(16))) uint8_t xbufs[2 * FUSED_XCHUNK];
   __shared__ __attribute__((aligned(16))) uint8_t slabs[WG_WAVES][SLAB_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t sslabs[WG_WAVES][sslab_bytes<2>()];
+  __shared__ __attribute__((aligned(16))) uint8_t sslabs[WG_WAVES][ScaleRun4::slab_bytes<2>()];
   __shared__ uint32_t xctr[2];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;

@@ -172,6 +172,7 @@ template <int NS_, class Meta, int XCHUNK_, bool COH>
 struct GateUpPolicy : ExpertItems<Meta> {
   static constexpr int NS = NS_;
   static constexpr int XCHUNK = XCHUNK_;
+  typedef ScaleRun4 Scales;  // H % 1024 == 0
   static constexpr int TILE = NS == 2 ? SUB_ROWS : SUB_ROWS / 2;  // intermediate columns per wave
   struct EpiState {
     int hrow;  // h row of the group's first row
@@ -199,7 +200,7 @@ struct GateUpPolicy : ExpertItems<Meta> {
     if (NS == 2) return (i ? I : 0) + n0 + r;
     return (r < 8) ? n0 + r : I + n0 + r - 8;
   }
-  __device__ __forceinline__ void w_setup(const ItemInfo& f, int wave, WCursor<NS>& c, int lane) const {
+  __device__ __forceinline__ void w_setup(const ItemInfo& f, int wave, WCursor<NS, Scales>& c, int lane) const {
     const uint8_t* we = wgu + (size_t)f.e * e_codes;
     const size_t kb = (size_t)H >> 1;
 #pragma unroll
@@ -248,11 +249,14 @@ struct GateUpPolicy : ExpertItems<Meta> {
 
 // ------------------------------------------------------------------ down
 
-// A wave's tile is NS x 16 output columns (subtile i = columns n0 + 16 i ... + 15).
-template <int NS_, class Meta, int XCHUNK_, bool COH>
+// A wave's tile is NS x 16 output columns (subtile i = columns n0 + 16 i ... + 15).  The
+// scale run is 4 segments when I % 1024 == 0, else 1 (I a multiple of 256, e.g. one
+// tensor-parallel eighth of an expert).
+template <int NS_, class Meta, int XCHUNK_, bool COH, class SR = ScaleRun4>
 struct DownPolicy : ExpertItems<Meta> {
   static constexpr int NS = NS_;
   static constexpr int XCHUNK = XCHUNK_;
+  typedef SR Scales;
   static constexpr int TILE = NS * SUB_ROWS;  // output columns per wave
   struct EpiState {
     int slot;  // flat slot of this lane's row, -1 if the row is past the group
@@ -280,7 +284,7 @@ struct DownPolicy : ExpertItems<Meta> {
     if (COH) wait_counter(ready, ready_target, err, flag, wave);
   }
   __device__ __forceinline__ int x_row_offset(const ItemInfo& f, int m) const { return (f.row0 + m) * I; }
-  __device__ __forceinline__ void w_setup(const ItemInfo& f, int wave, WCursor<NS>& c, int lane) const {
+  __device__ __forceinline__ void w_setup(const ItemInfo& f, int wave, WCursor<NS, Scales>& c, int lane) const {
     const uint8_t* we = wd + (size_t)f.e * e_codes;
     const size_t kb = (size_t)I >> 1;
     const int n0 = (f.tile0 + wave) * TILE;

@@ -13,9 +13,14 @@
 
 namespace mx {
 
+// Slot j < k + ns of a token: the j-th routed expert and its gate for j < k, else the shared
+// expert E + j - k with gate 1 (a model's always-active experts follow its routed ones).
+__device__ __forceinline__ int slot_expert(int j, int k, int E, int routed) { return j < k ? routed : E + j - k; }
+__device__ __forceinline__ float slot_gate(int j, int k, float routed) { return j < k ? routed : 1.0f; }
+
 // One wavefront per token.
 template <int PER>
-__global__ void __launch_bounds__(256) moe_route_kernel(const float* __restrict__ logits, int T, int E, int k,
+__global__ void __launch_bounds__(256) moe_route_kernel(const float* __restrict__ logits, int T, int E, int k, int ns,
                                                         int32_t* __restrict__ ids, float* __restrict__ gates) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -25,18 +30,19 @@ __global__ void __launch_bounds__(256) moe_route_kernel(const float* __restrict_
   int e;
   float g;
   route_select<PER>(v, E, k, lane, e, g);
-  if (lane < k) {
-    ids[(size_t)t * k + lane] = e;
-    gates[(size_t)t * k + lane] = g;
+  const int kk = k + ns;
+  if (lane < kk) {
+    ids[(size_t)t * kk + lane] = slot_expert(lane, k, E, e);
+    gates[(size_t)t * kk + lane] = slot_gate(lane, k, g);
   }
 }
 
-int launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* gates, hipStream_t stream) {
+int launch_route(const float* logits, int T, int E, int k, int ns, int32_t* ids, float* gates, hipStream_t stream) {
   const dim3 grid((T + 3) / 4), block(256);
   switch (route_per(E)) {
-    case 4: hipLaunchKernelGGL(moe_route_kernel<4>, grid, block, 0, stream, logits, T, E, k, ids, gates); break;
-    case 8: hipLaunchKernelGGL(moe_route_kernel<8>, grid, block, 0, stream, logits, T, E, k, ids, gates); break;
-    default: hipLaunchKernelGGL(moe_route_kernel<16>, grid, block, 0, stream, logits, T, E, k, ids, gates); break;
+    case 4: hipLaunchKernelGGL(moe_route_kernel<4>, grid, block, 0, stream, logits, T, E, k, ns, ids, gates); break;
+    case 8: hipLaunchKernelGGL(moe_route_kernel<8>, grid, block, 0, stream, logits, T, E, k, ns, ids, gates); break;
+    default: hipLaunchKernelGGL(moe_route_kernel<16>, grid, block, 0, stream, logits, T, E, k, ns, ids, gates); break;
   }
   return hip_status(hipGetLastError());
 }
@@ -159,11 +165,12 @@ int launch_sort(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_
 // ------------------------------------------------------------------ route + sort, one launch
 
 // Single workgroup of SORT_THREADS: wave w routes tokens w, w + 16, ... (loading the next
-// token's logits before routing the current one), writing ids and gates and setting the
-// token masks directly; the routed ids stay in LDS for the sort.
+// token's logits before routing the current one), writing ids and gates (the ns shared
+// slots after the k routed ones) and setting the token masks directly; the ids stay in LDS
+// for the sort over the E + ns experts.
 template <int PER>
 __global__ void __launch_bounds__(SORT_THREADS) moe_route_sort_kernel(
-    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids, float* __restrict__ gates,
+    const float* __restrict__ logits, int T, int E, int k, int ns, int32_t* __restrict__ ids, float* __restrict__ gates,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slots,
     int32_t* __restrict__ active, int32_t* __restrict__ num_active) {
   __shared__ SortShared sh;
@@ -171,9 +178,10 @@ __global__ void __launch_bounds__(SORT_THREADS) moe_route_sort_kernel(
   constexpr int NW = SORT_THREADS / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int words = (T + 31) >> 5;
+  const int kk = k + ns;
   float v[PER], vn[PER];
   route_load<PER>(logits + (size_t)min(wave, T - 1) * E, E, lane, v);
-  for (int i = tid; i < E * words; i += SORT_THREADS) sh.bits[i] = 0u;
+  for (int i = tid; i < (E + ns) * words; i += SORT_THREADS) sh.bits[i] = 0u;
   __syncthreads();
   for (int t = wave; t < T; t += NW) {
     // unconditional (the last row again past the end), so the waits stay exact
@@ -181,17 +189,18 @@ __global__ void __launch_bounds__(SORT_THREADS) moe_route_sort_kernel(
     int e;
     float g;
     route_select<PER>(v, E, k, lane, e, g);
-    if (lane < k) {
-      ids[(size_t)t * k + lane] = e;
-      gates[(size_t)t * k + lane] = g;
-      s_ids[t * k + lane] = e;
-      atomicOr(&sh.bits[e * words + (t >> 5)], 1u << (t & 31));
+    if (lane < kk) {
+      const int ee = slot_expert(lane, k, E, e);
+      ids[(size_t)t * kk + lane] = ee;
+      gates[(size_t)t * kk + lane] = slot_gate(lane, k, g);
+      s_ids[t * kk + lane] = ee;
+      atomicOr(&sh.bits[ee * words + (t >> 5)], 1u << (t & 31));
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) v[i] = vn[i];
   }
   __syncthreads();
-  sort_from_bits(sh, s_ids, T, k, E, counts, offsets, sorted_slots, active, num_active);
+  sort_from_bits(sh, s_ids, T, kk, E + ns, counts, offsets, sorted_slots, active, num_active);
 }
 
 // Up to this many tokens (one per wavefront of the workgroup) route and sort run as one
@@ -199,26 +208,26 @@ __global__ void __launch_bounds__(SORT_THREADS) moe_route_sort_kernel(
 // kernel spread over T / 4 workgroups plus a separate sort launch.
 constexpr int ROUTE_SORT_FUSED_MAX_T = SORT_THREADS / 64;
 
-int launch_route_sort(const float* logits, int T, int E, int k, int32_t* ids, float* gates, int32_t* counts,
+int launch_route_sort(const float* logits, int T, int E, int k, int ns, int32_t* ids, float* gates, int32_t* counts,
                       int32_t* offsets, int32_t* sorted_slots, int32_t* active, int32_t* num_active,
                       hipStream_t stream) {
   if (T > ROUTE_SORT_FUSED_MAX_T) {
-    const int st = launch_route(logits, T, E, k, ids, gates, stream);
+    const int st = launch_route(logits, T, E, k, ns, ids, gates, stream);
     if (st != MX_OK) return st;
-    return launch_sort(ids, T, k, E, counts, offsets, sorted_slots, active, num_active, stream);
+    return launch_sort(ids, T, k + ns, E + ns, counts, offsets, sorted_slots, active, num_active, stream);
   }
   const dim3 grid(1), block(SORT_THREADS);
   switch (route_per(E)) {
     case 4:
-      hipLaunchKernelGGL(moe_route_sort_kernel<4>, grid, block, 0, stream, logits, T, E, k, ids, gates, counts,
+      hipLaunchKernelGGL(moe_route_sort_kernel<4>, grid, block, 0, stream, logits, T, E, k, ns, ids, gates, counts,
                          offsets, sorted_slots, active, num_active);
       break;
     case 8:
-      hipLaunchKernelGGL(moe_route_sort_kernel<8>, grid, block, 0, stream, logits, T, E, k, ids, gates, counts,
+      hipLaunchKernelGGL(moe_route_sort_kernel<8>, grid, block, 0, stream, logits, T, E, k, ns, ids, gates, counts,
                          offsets, sorted_slots, active, num_active);
       break;
     default:
-      hipLaunchKernelGGL(moe_route_sort_kernel<16>, grid, block, 0, stream, logits, T, E, k, ids, gates, counts,
+      hipLaunchKernelGGL(moe_route_sort_kernel<16>, grid, block, 0, stream, logits, T, E, k, ns, ids, gates, counts,
                          offsets, sorted_slots, active, num_active);
       break;
   }

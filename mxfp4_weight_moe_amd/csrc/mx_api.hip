@@ -57,10 +57,12 @@ static int check_moe_sizes(int64_t T, int64_t E, int64_t k) {
   return MX_OK;
 }
 
-// The expert kernels stage the weight scales 1024 K values (four 256-value segments) at a
-// time, so H and I must be multiples of 1024.
+// The gate_up GEMM (reduction length H) stages the weight scales 1024 K values (four
+// 256-value segments) at a time, so H must be a multiple of 1024; the down GEMM (reduction
+// length I) takes any multiple of 256, e.g. I = 256 for one tensor-parallel eighth of an
+// expert of 2048.
 static int check_expert_dims(int64_t H, int64_t I) {
-  if (H < 1024 || I < 1024 || H % 1024 != 0 || I % 1024 != 0 || H > 65536 || I > 65536) return MX_ERR_SHAPE;
+  if (H < 1024 || I < 256 || H % 1024 != 0 || I % 256 != 0 || H > 65536 || I > 65536) return MX_ERR_SHAPE;
   return MX_OK;
 }
 
@@ -120,7 +122,7 @@ int moe_route_topk(const float* logits, int64_t T, int64_t E, int64_t top_k, int
   const int st = check_moe_sizes(T, E, top_k);
   if (st != MX_OK) return st;
   if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(gates, 4)) return MX_ERR_ALIGN;
-  return launch_route(logits, (int)T, (int)E, (int)top_k, ids, gates, static_cast<hipStream_t>(stream));
+  return launch_route(logits, (int)T, (int)E, (int)top_k, 0, ids, gates, static_cast<hipStream_t>(stream));
 }
 
 int moe_sort_by_expert(const int32_t* ids, int64_t T, int64_t top_k, int64_t E, int32_t* counts, int32_t* offsets,
@@ -144,7 +146,7 @@ int moe_route_sort(const float* logits, int64_t T, int64_t E, int64_t top_k, int
   if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(gates, 4) || !aligned(counts, 4) || !aligned(offsets, 4) ||
       !aligned(sorted_slots, 4) || !aligned(active, 4) || !aligned(num_active, 4))
     return MX_ERR_ALIGN;
-  return launch_route_sort(logits, (int)T, (int)E, (int)top_k, ids, gates, counts, offsets, sorted_slots, active,
+  return launch_route_sort(logits, (int)T, (int)E, (int)top_k, 0, ids, gates, counts, offsets, sorted_slots, active,
                            num_active, static_cast<hipStream_t>(stream));
 }
 
@@ -194,28 +196,48 @@ size_t moe_mxfp4_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int6
   return moe_workspace_carve(nullptr, T, H, I, E, top_k).bytes;
 }
 
-int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, int64_t top_k, const uint8_t* w_gate_up,
-                      const uint8_t* s_gate_up, const uint8_t* w_down, const uint8_t* s_down, uint16_t* y, int64_t T,
-                      int64_t H, int64_t I, int64_t E, void* workspace, size_t workspace_bytes, void* stream) {
+// The layer over E routed experts (top_k of them per token) and ns shared experts after them.
+static int moe_forward_impl(const uint16_t* x, const float* router_logits, int64_t top_k, int64_t ns,
+                            const uint8_t* w_gate_up, const uint8_t* s_gate_up, const uint8_t* w_down,
+                            const uint8_t* s_down, uint16_t* y, int64_t T, int64_t H, int64_t I, int64_t E,
+                            void* workspace, size_t workspace_bytes, void* stream) {
   if (!x || !router_logits || !w_gate_up || !s_gate_up || !w_down || !s_down || !y) return MX_ERR_NULL;
   int st = check_moe_sizes(T, E, top_k);
   if (st != MX_OK) return st;
+  if (ns < 0 || E + ns > MX_MAX_EXPERTS || top_k + ns > MX_MAX_TOPK) return MX_ERR_SHAPE;
   if ((st = check_expert_dims(H, I)) != MX_OK) return st;
   if (!aligned(x, 16) || !aligned(w_gate_up, 16) || !aligned(w_down, 16) || !aligned(s_gate_up, 16) ||
       !aligned(s_down, 16) || !aligned(y, 8) || !aligned(router_logits, 4))
     return MX_ERR_ALIGN;
   if (!workspace || !aligned(workspace, 256)) return MX_ERR_WORKSPACE;
-  const MoeWorkspace ws = moe_workspace_carve(workspace, T, H, I, E, top_k);
+  // every slot, routed and shared, is one row of the expert GEMMs
+  const MoeWorkspace ws = moe_workspace_carve(workspace, T, H, I, E + ns, top_k + ns);
   if (workspace_bytes < ws.bytes) return MX_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int t = (int)T, h = (int)H, i = (int)I, e = (int)E, k = (int)top_k;
-  if ((st = launch_route_sort(router_logits, t, e, k, ws.ids, ws.gates, ws.counts, ws.offsets, ws.sorted_slots,
+  const int t = (int)T, h = (int)H, i = (int)I, e = (int)E, k = (int)top_k, n = (int)ns;
+  if ((st = launch_route_sort(router_logits, t, e, k, n, ws.ids, ws.gates, ws.counts, ws.offsets, ws.sorted_slots,
                               ws.active, ws.num_active, s)) != MX_OK)
     return st;
   const SortView sv{ws.counts, ws.offsets, ws.sorted_slots, ws.active, ws.num_active};
-  if ((st = launch_gate_up(x, w_gate_up, s_gate_up, sv, ws.h, ws.ctl, t, h, i, e, k, s)) != MX_OK) return st;
-  if ((st = launch_down(ws.h, ws.gates, w_down, s_down, sv, ws.dpart, ws.ctl, t, h, i, e, k, s)) != MX_OK) return st;
-  return launch_combine(ws.dpart, ws.gates, y, t, h, k, s);
+  if ((st = launch_gate_up(x, w_gate_up, s_gate_up, sv, ws.h, ws.ctl, t, h, i, e + n, k + n, s)) != MX_OK) return st;
+  if ((st = launch_down(ws.h, ws.gates, w_down, s_down, sv, ws.dpart, ws.ctl, t, h, i, e + n, k + n, s)) != MX_OK)
+    return st;
+  return launch_combine(ws.dpart, ws.gates, y, t, h, k + n, s);
+}
+
+int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, int64_t top_k, const uint8_t* w_gate_up,
+                      const uint8_t* s_gate_up, const uint8_t* w_down, const uint8_t* s_down, uint16_t* y, int64_t T,
+                      int64_t H, int64_t I, int64_t E, void* workspace, size_t workspace_bytes, void* stream) {
+  return moe_forward_impl(x, router_logits, top_k, 0, w_gate_up, s_gate_up, w_down, s_down, y, T, H, I, E, workspace,
+                          workspace_bytes, stream);
+}
+
+int moe_mxfp4_forward_shared(const uint16_t* x, const float* router_logits, int64_t top_k, int64_t n_shared,
+                             const uint8_t* w_gate_up, const uint8_t* s_gate_up, const uint8_t* w_down,
+                             const uint8_t* s_down, uint16_t* y, int64_t T, int64_t H, int64_t I, int64_t E,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return moe_forward_impl(x, router_logits, top_k, n_shared, w_gate_up, s_gate_up, w_down, s_down, y, T, H, I, E,
+                          workspace, workspace_bytes, stream);
 }
 
 int moe_mxfp4_forward_persistent(const uint16_t* x, const float* router_logits, int64_t top_k,

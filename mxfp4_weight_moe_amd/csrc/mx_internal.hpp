@@ -66,11 +66,13 @@ int device_cu_count();
 int launch_mx_linear(const uint16_t* x, const uint8_t* w, const uint8_t* s, uint16_t* y, int T, int K, int N,
                      hipStream_t stream);
 int launch_dequant(const uint8_t* w, const uint8_t* s, int64_t rows, int64_t K, uint16_t* out, hipStream_t stream);
-int launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* gates, hipStream_t stream);
+// ns: shared experts E .. E + ns - 1, routed by every token with gate 1 after its k routed
+// slots (ids and gates are [T, k + ns]; the sort then runs over E + ns experts)
+int launch_route(const float* logits, int T, int E, int k, int ns, int32_t* ids, float* gates, hipStream_t stream);
 int launch_sort(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* sorted_slots,
                 int32_t* active, int32_t* num_active, hipStream_t stream);
 // route + sort in one single-workgroup launch (the layer forward's path)
-int launch_route_sort(const float* logits, int T, int E, int k, int32_t* ids, float* gates, int32_t* counts,
+int launch_route_sort(const float* logits, int T, int E, int k, int ns, int32_t* ids, float* gates, int32_t* counts,
                       int32_t* offsets, int32_t* sorted_slots, int32_t* active, int32_t* num_active,
                       hipStream_t stream);
 // ctl: the workspace's control words (the expert GEMMs claim their units there)

@@ -12,8 +12,8 @@
 //             wave computes.  The ring runs across item boundaries, so there is no
 //             pipeline drain between items.
 //   scales    staged per wave in LDS, one run of SRUN segments at a time: one coalesced
-//             16-byte load per lane brings the run's scales of all NS x 16 rows (lanes
-//             SLANES_PER_ROW apart cover one row), one step ahead of use, and each segment
+//             16-byte load per lane brings the run's scales of all NS x 16 rows (the
+//             lanes of ScaleRun::LANES_PER_ROW cover one row), one step ahead of use, and each segment
 //             reads its row's 8 bytes back with one LDS load.  Loading 16 bytes of one row
 //             per lane and segment pair instead made the scale requests, not the bytes, cost
 //             a seventh of the kernel's time.
@@ -56,22 +56,40 @@ __host__ __device__ constexpr int chunk_segments(int rows, int nseg, int align, 
          : ((rowsegs / rows / align * align) < nseg ? rowsegs / rows / align * align : nseg);
 }
 
-// Scale staging: runs of SRUN segments (an item's segment count must be a multiple).
-constexpr int SRUN = 4;
-constexpr int SRUN_ROW_BYTES = SRUN * SEG_SCALES;         // one row's scales of a run
-constexpr int SLANES_PER_ROW = SRUN_ROW_BYTES / 16;       // lanes loading one row
-constexpr int SROWS_PER_LOAD = 64 / SLANES_PER_ROW;       // rows one wave load covers
-// A wave's NS x 16 rows need scale_loads() loads; the last one may cover fewer rows than a
-// full load (16 rows: half the lanes), its other lanes repeat rows and do not store.
-template <int NS>
-constexpr int scale_loads() {
-  static_assert((NS * SUB_ROWS) % SROWS_PER_LOAD == 0 || NS * SUB_ROWS < SROWS_PER_LOAD, "whole scale loads");
-  return (NS * SUB_ROWS + SROWS_PER_LOAD - 1) / SROWS_PER_LOAD;
-}
-template <int NS>
-constexpr int sslab_bytes() {
-  return NS * SUB_ROWS * SRUN_ROW_BYTES;
-}
+// Scale staging: runs of SRUN segments (an item's segment count must be a multiple).  A
+// run of one row is SRUN * 8 bytes; a lane loads LOAD of them (16, or 8 for one-segment
+// runs), so LANES_PER_ROW lanes cover a row and one wave load covers ROWS_PER_LOAD rows.
+// A wave's NS x 16 rows need loads<NS>() loads; the last one may cover fewer rows than a
+// full load, its other lanes repeat rows and do not store.
+template <bool C, class A, class B>
+struct pick_type {
+  typedef A type;
+};
+template <class A, class B>
+struct pick_type<false, A, B> {
+  typedef B type;
+};
+template <int SRUN_>
+struct ScaleRun {
+  static constexpr int SRUN = SRUN_;
+  static constexpr int ROW_BYTES = SRUN * SEG_SCALES;
+  static constexpr int LOAD = ROW_BYTES < 16 ? ROW_BYTES : 16;
+  static constexpr int LANES_PER_ROW = ROW_BYTES / LOAD;
+  static constexpr int ROWS_PER_LOAD = 64 / LANES_PER_ROW;
+  typedef typename pick_type<LOAD == 16, u32x4, u32x2>::type Reg;
+  static_assert(LOAD == 16 || LOAD == 8, "8- or 16-byte scale loads");
+  template <int NS>
+  static constexpr int loads() {
+    static_assert((NS * SUB_ROWS) % ROWS_PER_LOAD == 0 || NS * SUB_ROWS < ROWS_PER_LOAD, "whole scale loads");
+    return (NS * SUB_ROWS + ROWS_PER_LOAD - 1) / ROWS_PER_LOAD;
+  }
+  template <int NS>
+  static constexpr int slab_bytes() {
+    return NS * SUB_ROWS * ROW_BYTES;
+  }
+};
+constexpr int SRUN = 4;  // the run of the gate_up GEMM and of down when I % 1024 == 0
+typedef ScaleRun<SRUN> ScaleRun4;
 
 // One step of the weight ring: SPS consecutive segments of the wave's NS subtiles.
 template <int NS, int SPS>
@@ -85,18 +103,18 @@ struct ItemPos {
   int n, it;
 };
 
-template <int NS>
+template <int NS, class SR>
 struct WCursor {
   ItemPos at;  // current item
   int seg;  // first segment of the step the ring is reloaded with
-  const uint8_t* w[NS][2];                 // this lane's code bytes of segment 0 (2 rows)
-  const uint8_t* sr[scale_loads<NS>()];    // this lane's scale bytes of segment 0, per load
+  const uint8_t* w[NS][2];                      // this lane's code bytes of segment 0 (2 rows)
+  const uint8_t* sr[SR::template loads<NS>()];  // this lane's scale bytes of segment 0, per load
 };
 
 // Fill the ring with the step at cursor c, in the order the loop reloads it, so that the
 // compiler's waits on entry to the loop match its waits inside it.
-template <int NS, int SPS>
-__device__ __forceinline__ void wring_load(WRing<NS, SPS>& r, const WCursor<NS>& c) {
+template <int NS, int SPS, class SR>
+__device__ __forceinline__ void wring_load(WRing<NS, SPS>& r, const WCursor<NS, SR>& c) {
 #pragma unroll
   for (int j = 0; j < SPS; ++j) {
     const size_t wo = (size_t)(c.seg + j) * SEG_BYTES;
@@ -109,23 +127,24 @@ __device__ __forceinline__ void wring_load(WRing<NS, SPS>& r, const WCursor<NS>&
   }
 }
 
-// Scales of the run starting at c.seg (a multiple of SRUN), one 16-byte load per lane and load.
-template <int NS>
-__device__ __forceinline__ void srun_load(u32x4 (&sreg)[scale_loads<NS>()], const WCursor<NS>& c) {
+// Scales of the run starting at c.seg (a multiple of SRUN), one load per lane and load.
+template <int NS, class SR>
+__device__ __forceinline__ void srun_load(typename SR::Reg (&sreg)[SR::template loads<NS>()], const WCursor<NS, SR>& c) {
 #pragma unroll
-  for (int k = 0; k < scale_loads<NS>(); ++k) sreg[k] = ld16(c.sr[k] + (size_t)c.seg * SEG_SCALES);
+  for (int k = 0; k < SR::template loads<NS>(); ++k)
+    sreg[k] = *reinterpret_cast<const typename SR::Reg*>(c.sr[k] + (size_t)c.seg * SEG_SCALES);
   __builtin_amdgcn_sched_barrier(SCHED_ALL_BUT_VMEM);
 }
 
-// The slab holds row rho = i * 16 + r of the run at rho * SRUN_ROW_BYTES; a load's 64 lanes
-// cover SROWS_PER_LOAD consecutive rows, so lane l of load k lands at k * 1024 + l * 16.
-template <int NS>
-__device__ __forceinline__ void srun_store(uint8_t* __restrict__ sslab, const u32x4 (&sreg)[scale_loads<NS>()],
-                                           int lane) {
+// The slab holds row rho = i * 16 + r of the run at rho * ROW_BYTES; a load's 64 lanes cover
+// ROWS_PER_LOAD consecutive rows, so lane l of load k lands at (k * 64 + l) * LOAD.
+template <int NS, class SR>
+__device__ __forceinline__ void srun_store(uint8_t* __restrict__ sslab,
+                                           const typename SR::Reg (&sreg)[SR::template loads<NS>()], int lane) {
 #pragma unroll
-  for (int k = 0; k < scale_loads<NS>(); ++k)
-    if (k * 64 + lane < NS * SUB_ROWS * SLANES_PER_ROW)
-      *reinterpret_cast<u32x4*>(sslab + k * (64 * 16) + lane * 16) = sreg[k];
+  for (int k = 0; k < SR::template loads<NS>(); ++k)
+    if (k * 64 + lane < NS * SUB_ROWS * SR::LANES_PER_ROW)
+      *reinterpret_cast<typename SR::Reg*>(sslab + (k * 64 + lane) * SR::LOAD) = sreg[k];
 }
 
 // What the kernels need of an item; all fields are uniform across the workgroup.
@@ -227,9 +246,9 @@ __device__ __forceinline__ void xchunk_store(uint8_t* __restrict__ buf, const XC
 // products land in output columns that are not stored).  The scales come from the wave's
 // scale slab (segment u of the staged run).  Once the codes are in the slab, w is reloaded
 // with segment `nseg_next` of the cursor `c` (the same segment of the next step).
-template <int NS>
+template <int NS, class SR>
 __device__ __forceinline__ void segment_compute(u32x4 (&w)[NS][2], const uint8_t* __restrict__ sslab, int u,
-                                                const WCursor<NS>& c, int nseg_next,
+                                                const WCursor<NS, SR>& c, int nseg_next,
                                                 const uint8_t* __restrict__ xbuf, int sl, int R, int xrow,
                                                 uint8_t* __restrict__ slab, const uint32_t (&lds_wr)[2],
                                                 const uint32_t (&lds_rd)[2], uint32_t sshift, int lane,
@@ -257,7 +276,7 @@ __device__ __forceinline__ void segment_compute(u32x4 (&w)[NS][2], const uint8_t
   u32x2 sc2[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i)
-    sc2[i] = *reinterpret_cast<const u32x2*>(sslab + (i * SUB_ROWS + (lane & 15)) * SRUN_ROW_BYTES + u * SEG_SCALES);
+    sc2[i] = *reinterpret_cast<const u32x2*>(sslab + (i * SUB_ROWS + (lane & 15)) * SR::ROW_BYTES + u * SEG_SCALES);
   const int j = lane >> 4;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -376,18 +395,20 @@ struct ClaimedUnits {
 //   EpiState;  void c_setup(const ItemInfo&, int wave, EpiState&, int lane)
 //   void epilogue(const EpiState&, const f32x4 (&acc)[NS], int lane)
 //   static constexpr int XCHUNK;                    -- bytes of one activation chunk buffer
+//   typedef ScaleRun<...> Scales;                   -- scale staging run
 // `xbufs` is 2 * P::XCHUNK bytes of LDS, `xctr` 2 zeroed LDS counters, `slab` this wave's
-// SLAB_BYTES and `sslab` its sslab_bytes<NS>() of LDS.  nseg must be a multiple of SPS and
-// of SRUN (the launchers check it).
+// SLAB_BYTES and `sslab` its P::Scales::slab_bytes<NS>() of LDS.  nseg must be a multiple of
+// SPS and of the scale run (the launchers check it).
 template <class P, int SPS, class Seq>
 __device__ __forceinline__ void stream_items(P& p, Seq& seq, uint8_t* __restrict__ xbufs, uint32_t* xctr,
                                              uint8_t* __restrict__ slab, uint8_t* __restrict__ sslab, int wave,
                                              int lane) {
   constexpr int NS = P::NS;
-  constexpr int SL = scale_loads<NS>();
+  typedef typename P::Scales SR;
+  constexpr int SL = SR::template loads<NS>();
   constexpr int XCHUNK_BYTES = P::XCHUNK;
   constexpr int XROUNDS = XGeom<XCHUNK_BYTES>::ROUNDS;
-  static_assert(SRUN % SPS == 0, "scale runs end on steps");
+  static_assert(SR::SRUN % SPS == 0, "scale runs end on steps");
   const int tid = wave * 64 + lane;
   uint32_t lds_wr[2], lds_rd[2];
   for (int q = 0; q < 2; ++q) lds_wr[q] = slab_off((uint32_t)(lane >> 3) + 8u * q, (uint32_t)(lane & 7));
@@ -426,7 +447,7 @@ __device__ __forceinline__ void stream_items(P& p, Seq& seq, uint8_t* __restrict
 
   // ---- weight cursor (per wave): the step the ring is reloaded with.  Once the
   // workgroup's items are exhausted it stays on the last step (re-read, never used).
-  WCursor<NS> cw;
+  WCursor<NS, SR> cw;
   auto cursor_setup = [&](const ItemPos& at) {
     const ItemInfo f = p.info(at.it);
     cw.at = at;
@@ -434,8 +455,8 @@ __device__ __forceinline__ void stream_items(P& p, Seq& seq, uint8_t* __restrict
     p.w_setup(f, wave, cw, lane);
 #pragma unroll
     for (int k = 0; k < SL; ++k) {
-      const int rho = (k * SROWS_PER_LOAD + lane / SLANES_PER_ROW) % (NS * SUB_ROWS);
-      cw.sr[k] = p.scale_row(f, wave, rho / SUB_ROWS, rho % SUB_ROWS) + (lane % SLANES_PER_ROW) * 16;
+      const int rho = (k * SR::ROWS_PER_LOAD + lane / SR::LANES_PER_ROW) % (NS * SUB_ROWS);
+      cw.sr[k] = p.scale_row(f, wave, rho / SUB_ROWS, rho % SUB_ROWS) + (lane % SR::LANES_PER_ROW) * SR::LOAD;
     }
   };
   cursor_setup(first);
@@ -448,7 +469,7 @@ __device__ __forceinline__ void stream_items(P& p, Seq& seq, uint8_t* __restrict
     }
   };
   WRing<NS, SPS> rw;
-  u32x4 sreg[SL];  // scales of the next run, loaded one step ahead
+  typename SR::Reg sreg[SL];  // scales of the next run, loaded one step ahead
 
   // ---- activation chunks (per workgroup): the first one is loaded before the loop
   auto chunk_of = [&](const ItemPos& at, int c0) {
@@ -470,7 +491,7 @@ __device__ __forceinline__ void stream_items(P& p, Seq& seq, uint8_t* __restrict
   // The first weight step and scale run are requested before anything else, so that the
   // first compute waits for one memory round trip, not for the chunk hand-off as well.
   wring_load(rw, cw);
-  srun_load<NS>(sreg, cw);
+  srun_load<NS, SR>(sreg, cw);
   p.wait_inputs();
   u32x4 xv[XROUNDS];
   XChunk cur = chunk_of(first, 0);
@@ -479,9 +500,9 @@ __device__ __forceinline__ void stream_items(P& p, Seq& seq, uint8_t* __restrict
   xready_publish(&xctr[0]);
   int xb = 0;                  // LDS buffer holding `cur`
   uint32_t gen[2] = {1u, 0u};  // chunks published so far into each buffer
-  srun_store<NS>(sslab, sreg, lane);
+  srun_store<NS, SR>(sslab, sreg, lane);
   advance_w();
-  if (cw.seg % SRUN == 0) srun_load<NS>(sreg, cw);
+  if (cw.seg % SR::SRUN == 0) srun_load<NS, SR>(sreg, cw);
   bool have_next;
   XChunk nxt = next_chunk(cur, have_next);
   if (have_next) xchunk_load(p, nxt, xv, tid);
@@ -501,7 +522,7 @@ __device__ __forceinline__ void stream_items(P& p, Seq& seq, uint8_t* __restrict
     // one step: SPS segments; each segment's ring slot is reloaded with the next step
 #pragma unroll
     for (int jj = 0; jj < SPS; ++jj)
-      segment_compute<NS>(rw.w[jj], sslab, (cseg + jj) % SRUN, cw, cw.seg + jj, xbufs + xb * XCHUNK_BYTES,
+      segment_compute<NS, SR>(rw.w[jj], sslab, (cseg + jj) % SR::SRUN, cw, cw.seg + jj, xbufs + xb * XCHUNK_BYTES,
                           cseg + jj - cur.c0, cur.info.rows, xrow, slab, lds_wr, lds_rd, sshift, lane, acc);
     advance_w();
     // Chunks and items end on step boundaries (their lengths are multiples of SPS).
@@ -533,8 +554,8 @@ __device__ __forceinline__ void stream_items(P& p, Seq& seq, uint8_t* __restrict
     // Scales: the next step starting a run finds its run in sreg (loaded when the weight
     // cursor reached it, one step ago); the wave's own earlier slab reads precede this
     // store in LDS order.  Then prefetch the run the cursor has just reached, if any.
-    if (cseg % SRUN == 0) srun_store<NS>(sslab, sreg, lane);
-    if (cw.seg % SRUN == 0) srun_load<NS>(sreg, cw);
+    if (cseg % SR::SRUN == 0) srun_store<NS, SR>(sslab, sreg, lane);
+    if (cw.seg % SR::SRUN == 0) srun_load<NS, SR>(sreg, cw);
   }
 }
 

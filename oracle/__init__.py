@@ -64,7 +64,7 @@ def _load():
     lib.ora_mx_linear.argtypes = [P, P, P, I64, I64, I64, P, P, P, ctypes.c_int]
     lib.ora_route.argtypes = [P, I64, I64, I64, P, P]
     lib.ora_sort.argtypes = [P, I64, I64, I64, P, P, P, P, P]
-    lib.ora_moe_tokens.argtypes = [P, P, I64, P, P, P, P, I64, I64, I64, I64, P, I64, P, P, P, ctypes.c_int]
+    lib.ora_moe_tokens.argtypes = [P, P, I64, I64, P, P, P, P, I64, I64, I64, I64, P, I64, P, P, P, ctypes.c_int]
     for name in ("ora_pack_codes", "ora_unpack_codes", "ora_dequant_f64", "ora_mx_linear",
                  "ora_route", "ora_sort", "ora_moe_tokens"):
         getattr(lib, name).restype = None
@@ -170,17 +170,20 @@ def sort(ids: np.ndarray, E: int):
 
 
 def moe_tokens(x_bits, logits, k, wgu, sgu, wd, sd, T, H, I, E, tokens=None, want_h=False,
-               nthreads: int | None = None):
-    """MoE forward for the listed tokens (default: all).
+               nthreads: int | None = None, n_shared: int = 0):
+    """MoE forward for the listed tokens (default: all).  Each token routes to k of the E
+    routed experts (softmax gates over the selected logits) and to the n_shared shared
+    experts E .. E + n_shared - 1 with gate 1; the weight arrays hold E + n_shared experts.
 
-    Returns (y bf16 bits [ntok,H], scale_m fp64 [ntok,H], h bf16 bits [ntok*k, I] or None).
-    Weight arrays may be any contiguous uint8 arrays holding [E, ...] tensors.
+    Returns (y bf16 bits [ntok,H], scale_m fp64 [ntok,H], h bf16 bits [ntok*(k+n_shared), I]
+    or None).  Weight arrays may be any contiguous uint8 arrays holding [E+n_shared, ...] tensors.
     """
     x_bits = _c(x_bits, np.uint16)
     logits = _c(logits, np.float32)
     assert x_bits.size == T * H and logits.size == T * E
-    for a, n in ((wgu, E * 2 * I * H // 2), (sgu, E * 2 * I * H // 32), (wd, E * H * I // 2),
-                 (sd, E * H * I // 32)):
+    Ew = E + n_shared
+    for a, n in ((wgu, Ew * 2 * I * H // 2), (sgu, Ew * 2 * I * H // 32), (wd, Ew * H * I // 2),
+                 (sd, Ew * H * I // 32)):
         assert a.dtype == np.uint8 and a.flags.c_contiguous and a.size == n
     if tokens is None:
         tokens = np.arange(T, dtype=np.int32)
@@ -188,8 +191,8 @@ def moe_tokens(x_bits, logits, k, wgu, sgu, wd, sd, T, H, I, E, tokens=None, wan
     ntok = tokens.size
     y = np.empty((ntok, H), np.uint16)
     sm = np.empty((ntok, H), np.float64)
-    h = np.empty((ntok * k, I), np.uint16) if want_h else None
-    _load().ora_moe_tokens(_p(x_bits), _p(logits), k, _p(wgu), _p(sgu), _p(wd), _p(sd), T, H, I, E,
+    h = np.empty((ntok * (k + n_shared), I), np.uint16) if want_h else None
+    _load().ora_moe_tokens(_p(x_bits), _p(logits), k, n_shared, _p(wgu), _p(sgu), _p(wd), _p(sd), T, H, I, E,
                            _p(tokens), ntok, _p(y), _p(sm), _p(h) if want_h else None,
                            nthreads or default_threads())
     return y, sm, h

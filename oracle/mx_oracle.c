@@ -238,24 +238,34 @@ static double swiglu(float g, float u) {
   return gd / (1.0 + exp(-gd)) * (double)u;
 }
 
-/* MoE forward for the tokens listed in tok[0..ntok): for each token t and
- * slot j (expert e = ids[t,j], gate = gates[t,j]):
+/* MoE forward for the tokens listed in tok[0..ntok): each token routes to its
+ * k routed slots (ora_route over the E logits) and then to the n_shared shared
+ * experts E .. E + n_shared - 1 with gate 1 (a model's always-active experts);
+ * for each token t and slot j < k + n_shared (expert e = ids[t,j], gate = gates[t,j]):
  *   g_n = sum_K x[t,K] Wgu[e][n,K],  u_n = sum_K x[t,K] Wgu[e][I+n,K]   (fp32)
  *   h_n = bf16(silu(g_n) * u_n)                                         n < I
  *   d_n = sum_i h_i Wd[e][n,i]                                          (fp32)
  *   y[t,n] = bf16(sum_j fl32(gate_j * d_{j,n}))  j ascending, fp32.
- * Shapes: x bf16 [T,H]; logits f32 [T,E]; Wgu [E,2I,H/2], Sgu [E,2I,H/32];
- * Wd [E,H,I/2], Sd [E,H,I/32].  Outputs indexed by position in tok:
- * y [ntok,H] bf16 bits; scale_m [ntok,H] = sum_j gate_j sum_i |h_i Wd[e][n,i]|
- * (fp64, may be NULL); h [ntok*k, I] bf16 bits (may be NULL). */
-void ora_moe_tokens(const uint16_t* x, const float* logits, int64_t k, const uint8_t* wgu,
-                    const uint8_t* sgu, const uint8_t* wd, const uint8_t* sd, int64_t T, int64_t H,
-                    int64_t I, int64_t E, const int32_t* tok, int64_t ntok, uint16_t* y,
+ * Shapes: x bf16 [T,H]; logits f32 [T,E]; Wgu [E+n_shared,2I,H/2],
+ * Sgu [E+n_shared,2I,H/32]; Wd [E+n_shared,H,I/2], Sd [E+n_shared,H,I/32].
+ * Outputs indexed by position in tok: y [ntok,H] bf16 bits;
+ * scale_m [ntok,H] = sum_j gate_j sum_i |h_i Wd[e][n,i]| (fp64, may be NULL);
+ * h [ntok*(k+n_shared), I] bf16 bits (may be NULL). */
+void ora_moe_tokens(const uint16_t* x, const float* logits, int64_t k_routed, int64_t n_shared,
+                    const uint8_t* wgu, const uint8_t* sgu, const uint8_t* wd, const uint8_t* sd, int64_t T,
+                    int64_t H, int64_t I, int64_t E, const int32_t* tok, int64_t ntok, uint16_t* y,
                     double* scale_m, uint16_t* h_out, int nthreads) {
   (void)T;
+  const int64_t k = k_routed + n_shared;  /* slots per token */
   int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)(ntok * k));
   float* gates = (float*)malloc(sizeof(float) * (size_t)(ntok * k));
-  for (int64_t i = 0; i < ntok; ++i) ora_route(logits + (int64_t)tok[i] * E, 1, E, k, ids + i * k, gates + i * k);
+  for (int64_t i = 0; i < ntok; ++i) {
+    ora_route(logits + (int64_t)tok[i] * E, 1, E, k_routed, ids + i * k, gates + i * k);
+    for (int64_t s = 0; s < n_shared; ++s) {
+      ids[i * k + k_routed + s] = (int32_t)(E + s);
+      gates[i * k + k_routed + s] = 1.0f;
+    }
+  }
 
   uint16_t* h = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(ntok * k * I));
   const int64_t gu_rows = 2 * I;

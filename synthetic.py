@@ -56,6 +56,7 @@ class MoEConfig:
     zipf_s: float = 1.1
     positions: int = 1        # "spec": speculative positions per request (T = requests x positions)
     spec_sigma: float = 1.2   # "spec": spread of the per-request expert preference
+    n_shared: int = 0         # always-active shared experts, after the E routed ones
 
 
 LINEAR_CONFIGS = {
@@ -76,6 +77,14 @@ MOE_CONFIGS = {
     "moe_spec_t128": MoEConfig("moe_spec_t128", T=128, H=7168, I=2048, E=384, k=8, routing="spec", positions=4),
     # one request, 4 speculative positions
     "moe_spec_t4": MoEConfig("moe_spec_t4", T=4, H=7168, I=2048, E=256, k=8, routing="spec", positions=4),
+    # one GPU's share of a layer split 8 ways by tensor parallelism: each expert's
+    # intermediate width 2048 / 8 = 256 (the same routing as moe_t4 and moe_t32_zipf)
+    "moe_tp8_t4": MoEConfig("moe_tp8_t4", T=4, H=7168, I=256, E=256, k=8, routing="normal"),
+    "moe_tp8_t32": MoEConfig("moe_tp8_t32", T=32, H=7168, I=256, E=256, k=8, routing="zipf"),
+    # 256 routed experts (top-8) and one always-active shared expert, each token reading
+    # 9 experts (the GLM-5.3 layer of "Zyphra Inference Wave 2", section "Quantization")
+    "moe_shared_t1": MoEConfig("moe_shared_t1", T=1, H=7168, I=2048, E=256, k=8, routing="normal", n_shared=1),
+    "moe_shared_t32": MoEConfig("moe_shared_t32", T=32, H=7168, I=2048, E=256, k=8, routing="zipf", n_shared=1),
 }
 
 
@@ -169,10 +178,11 @@ def linear_inputs(cfg: LinearConfig):
 def moe_inputs_host(cfg: MoEConfig):
     """All MoE inputs on the host (small shapes only: every expert is drawn).
 
-    Returns dict(x [T,H] u16, logits [T,E] f32, wgu [E,2I,H/2], sgu [E,2I,H/32],
-    wd [E,H,I/2], sd [E,H,I/32]) as numpy arrays.
+    Returns dict(x [T,H] u16, logits [T,E] f32, wgu [Ew,2I,H/2], sgu [Ew,2I,H/32],
+    wd [Ew,H,I/2], sd [Ew,H,I/32]) as numpy arrays, Ew = E + n_shared (the shared experts
+    after the routed ones).
     """
-    T, H, I, E = cfg.T, cfg.H, cfg.I, cfg.E
+    T, H, I, E = cfg.T, cfg.H, cfg.I, cfg.E + cfg.n_shared
     x = bf16_bits_normal((T, H), cfg.seed, TAG_X)
     logits = router_logits(cfg)
     wgu = np.stack([random_codes(2 * I, H, cfg.seed, 1000 + 4 * e) for e in range(E)])
@@ -202,11 +212,11 @@ def device_scales(shape, e_lo: int, e_hi: int, seed: int, tag: int, device):
 
 
 def moe_weights_device(cfg: MoEConfig, device, layer: int = 0):
-    """Full [E, ...] MXFP4 weight tensors drawn on the device (fast for large E).
+    """Full [E + n_shared, ...] MXFP4 weight tensors drawn on the device (fast for large E).
 
     Returns dict(wgu, sgu, wd, sd) as uint8 torch tensors on `device`.
     """
-    T, H, I, E = cfg.T, cfg.H, cfg.I, cfg.E
+    T, H, I, E = cfg.T, cfg.H, cfg.I, cfg.E + cfg.n_shared
     base = 10_000 * (layer + 1)
     return dict(
         wgu=device_codes((E, 2 * I, H // 2), cfg.seed, base + 1, device),

@@ -105,7 +105,8 @@ def test_forward_rejects():
     assert fwd(H=320) == MX_ERR_SHAPE
     assert fwd(H=1536) == MX_ERR_SHAPE  # not a multiple of 1024
     assert fwd(I=96) == MX_ERR_SHAPE
-    assert fwd(I=512) == MX_ERR_SHAPE
+    assert fwd(I=128) == MX_ERR_SHAPE   # below 256
+    assert fwd(I=320) == MX_ERR_SHAPE   # not a multiple of 256
     assert fwd(wgu=MIS) == MX_ERR_ALIGN
     assert fwd(sgu=P((1 << 20) + 4)) == MX_ERR_ALIGN
     assert fwd(sd=P((1 << 20) + 8)) == MX_ERR_ALIGN
@@ -139,6 +140,21 @@ def test_stage_gemm_hooks_reject():
     assert dn(wb=ws - 1) == MX_ERR_WORKSPACE
 
 
+def test_shared_forward_rejects():
+    L = m.raw()
+    ws = m.workspace_size(4, 1024, 1024, 9, 3)  # E + n_shared experts, top_k + n_shared slots
+
+    def fwd(k=2, ns=1, T=4, E=8, w=A, wb=ws, x=A):
+        return L.moe_mxfp4_forward_shared(x, A, k, ns, A, A, A, A, A, T, 1024, 1024, E, w, wb, None)
+
+    assert fwd(x=None) == MX_ERR_NULL
+    assert fwd(ns=-1) == MX_ERR_SHAPE
+    assert fwd(E=1024) == MX_ERR_SHAPE        # 1025 experts with the shared one
+    assert fwd(k=32, E=64) == MX_ERR_SHAPE    # 33 slots per token
+    assert fwd(wb=ws - 1) == MX_ERR_WORKSPACE
+    assert fwd(wb=m.workspace_size(4, 1024, 1024, 8, 2)) == MX_ERR_WORKSPACE  # sized without the shared slots
+
+
 def test_persistent_forward_rejects():
     L = m.raw()
     ws = m.workspace_size(16, 1024, 1024, 64, 8)
@@ -152,6 +168,7 @@ def test_persistent_forward_rejects():
     assert fwd(T=16, k=9, E=64) == MX_ERR_SHAPE  # 144 > 128 routed slots
     assert fwd(T=4, k=33, E=64) == MX_ERR_SHAPE
     assert fwd(H=1536) == MX_ERR_SHAPE
+    assert fwd(I=256) == MX_ERR_SHAPE          # the single launch needs I % 1024 == 0
     assert fwd(x=MIS) == MX_ERR_ALIGN
     assert fwd(w=None) == MX_ERR_WORKSPACE
     assert fwd(wb=m.workspace_size(4, 1024, 1024, 8, 2) - 1) == MX_ERR_WORKSPACE

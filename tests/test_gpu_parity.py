@@ -201,15 +201,15 @@ def moe_device_inputs(cfg, dev, host=None):
     return d, x, logits
 
 
-def run_moe(mx, d, k):
-    y = mx.moe_mxfp4_forward(d["x"], d["logits"], k, d["wgu"], d["sgu"], d["wd"], d["sd"])
+def run_moe(mx, d, k, n_shared=0):
+    y = mx.moe_mxfp4_forward(d["x"], d["logits"], k, d["wgu"], d["sgu"], d["wd"], d["sd"], n_shared=n_shared)
     torch.cuda.synchronize()
     return to_host_bits(y)
 
 
 def oracle_moe(cfg, x, logits, w_host, tokens=None):
     y, sm, _ = oracle.moe_tokens(x, logits, cfg.k, w_host["wgu"], w_host["sgu"], w_host["wd"], w_host["sd"],
-                                 cfg.T, cfg.H, cfg.I, cfg.E, tokens=tokens)
+                                 cfg.T, cfg.H, cfg.I, cfg.E, tokens=tokens, n_shared=cfg.n_shared)
     return y, sm
 
 
@@ -239,7 +239,8 @@ def test_moe_tiny_full_oracle(dev, mx, shape):
 
 
 FULL = [("moe_t4", None), ("moe_t32_zipf", [0, 5, 13, 31]), ("moe_t128", [0, 1, 64, 127]),
-        ("moe_spec_t4", None), ("moe_spec_t128", [0, 1, 2, 3, 126])]
+        ("moe_spec_t4", None), ("moe_spec_t128", [0, 1, 2, 3, 126]),
+        ("moe_tp8_t4", None), ("moe_tp8_t32", None), ("moe_shared_t1", None), ("moe_shared_t32", [0, 9, 31])]
 
 
 @pytest.mark.parametrize("name,tokens", FULL, ids=[f[0] for f in FULL])
@@ -247,7 +248,7 @@ def test_moe_full_size(dev, mx, name, tokens):
     cfg = synthetic.MOE_CONFIGS[name]
     say("moe full", name, "tokens", tokens)
     d, x, logits = moe_device_inputs(cfg, dev)
-    got = run_moe(mx, d, cfg.k)
+    got = run_moe(mx, d, cfg.k, cfg.n_shared)
     w_host = {k: d[k].cpu().numpy() for k in ("wgu", "sgu", "wd", "sd")}
     tok = np.arange(cfg.T, dtype=np.int32) if tokens is None else np.array(tokens, np.int32)
     y, sm = oracle_moe(cfg, x, logits, w_host, tokens=tok)
@@ -348,6 +349,49 @@ def run_hooks(mx, d, k, T):
     y = mx.moe_down_combine(h, gates, d["wd"], d["sd"], srt, T, k)
     torch.cuda.synchronize()
     return to_host_bits(y)
+
+
+SHARED = [dict(T=1, H=1024, I=1024, E=4, k=1, n_shared=1), dict(T=5, H=1024, I=1024, E=8, k=2, n_shared=2),
+          dict(T=20, H=2048, I=1024, E=6, k=3, n_shared=1), dict(T=40, H=1024, I=256, E=4, k=2, n_shared=1)]
+
+
+@pytest.mark.parametrize("shape", SHARED, ids=[f"T{s['T']}_E{s['E']}_k{s['k']}_ns{s['n_shared']}" for s in SHARED])
+def test_moe_shared_experts(dev, mx, shape):
+    """Shared experts after the routed ones (every token reads them, gate 1), against the
+    oracle; at T = 40 the shared expert has three row groups."""
+    cfg = synthetic.MoEConfig("shared", routing="normal", e_lo=-8, e_hi=-2, seed=shape["T"] * 17 + shape["E"], **shape)
+    host = synthetic.moe_inputs_host(cfg)
+    say("moe shared experts", shape)
+    d, x, logits = moe_device_inputs(cfg, dev, host)
+    got = run_moe(mx, d, cfg.k, cfg.n_shared)
+    yo, sm = oracle_moe(cfg, x, logits, host)
+    worst = check_bound(got, yo, sm, MOE_REL, f"shared {shape}")
+    say(f"  worst ratio {worst:.3g}")
+    assert np.array_equal(run_moe(mx, d, cfg.k, cfg.n_shared), got)  # deterministic
+
+
+# down reductions that are not multiples of 1024 (one-segment scale runs): I = 256, 512, 768
+NARROW = [dict(T=5, H=1024, I=256, E=8, k=2), dict(T=20, H=2048, I=512, E=6, k=3), dict(T=3, H=1024, I=768, E=4, k=4),
+          dict(T=40, H=1024, I=256, E=4, k=2)]
+
+
+@pytest.mark.parametrize("shape", NARROW, ids=[f"T{s['T']}_H{s['H']}_I{s['I']}_E{s['E']}_k{s['k']}" for s in NARROW])
+def test_moe_narrow_intermediate(dev, mx, shape):
+    """Intermediate widths that are multiples of 256 but not of 1024, as one tensor-parallel
+    share of an expert: the oracle bound, bit-identical stage entry points, and the single
+    launch refusing them."""
+    cfg = synthetic.MoEConfig("narrow", routing="normal", e_lo=-8, e_hi=-2, seed=shape["T"] * 13 + shape["I"], **shape)
+    host = synthetic.moe_inputs_host(cfg)
+    say("moe narrow intermediate", shape)
+    d, x, logits = moe_device_inputs(cfg, dev, host)
+    got = run_moe(mx, d, cfg.k)
+    yo, sm = oracle_moe(cfg, x, logits, host)
+    worst = check_bound(got, yo, sm, MOE_REL, f"narrow {shape}")
+    say(f"  worst ratio {worst:.3g}")
+    assert np.array_equal(run_hooks(mx, d, cfg.k, cfg.T), got)
+    if cfg.T <= 16:
+        with pytest.raises(ValueError):
+            mx.moe_mxfp4_forward(d["x"], d["logits"], cfg.k, d["wgu"], d["sgu"], d["wd"], d["sd"], persistent=True)
 
 
 FUSED_EDGES = [

@@ -108,6 +108,57 @@ def test_single_expert_reduces_to_dense_mlp():
     assert np.array_equal(y, y_ref)  # gate = 1 exactly when k = 1
 
 
+def shared_cfg(seed, n_shared, E=3, k=2):
+    return synthetic.MoEConfig("tiny_shared", T=3, H=128, I=64, E=E, k=k, routing="normal", e_lo=-8, e_hi=-3,
+                               seed=seed, n_shared=n_shared)
+
+
+def dense_mlp_acc(x, wgu, sgu, wd, sd, T, H, I):
+    """The shared expert as a dense MLP from two mx_linear calls: (fp32 down outputs, h)."""
+    _, acc, _ = oracle.mx_linear(x, wgu, sgu, T, H, 2 * I)
+    g, u = acc[:, :I].astype(np.float64), acc[:, I:].astype(np.float64)
+    hv = g / (1 + np.exp(-g)) * u
+    h = np.array([[oracle.bf16_rne(v) for v in row] for row in hv], np.uint16)
+    _, dacc, _ = oracle.mx_linear(h, wd, sd, T, I, H)
+    return dacc, h
+
+
+@pytest.mark.parametrize("n_shared", [1, 2])
+def test_shared_experts_add_to_the_routed_ones(n_shared):
+    """With every routed expert's codes zero (its outputs are +0), the layer is the shared
+    experts' sum: one shared expert gives the dense MLP bit for bit, two identical ones
+    give exactly twice its fp32 down outputs before the bf16 rounding."""
+    cfg = shared_cfg(11, n_shared)
+    inp = synthetic.moe_inputs_host(cfg)
+    E = cfg.E
+    inp["wgu"][:E] = 0
+    inp["wd"][:E] = 0
+    for key in ("wgu", "sgu", "wd", "sd"):
+        inp[key][E + 1:] = inp[key][E]  # identical shared experts
+    y, _, h = oracle.moe_tokens(inp["x"], inp["logits"], cfg.k, inp["wgu"], inp["sgu"], inp["wd"], inp["sd"],
+                                cfg.T, cfg.H, cfg.I, E, want_h=True, n_shared=n_shared)
+    dacc, h_ref = dense_mlp_acc(inp["x"], inp["wgu"][E], inp["sgu"][E], inp["wd"][E], inp["sd"][E], cfg.T, cfg.H,
+                                cfg.I)
+    kk = cfg.k + n_shared
+    for s in range(n_shared):
+        assert np.array_equal(h.reshape(cfg.T, kk, cfg.I)[:, cfg.k + s], h_ref)
+    y_ref = np.array([[oracle.bf16_rne(n_shared * float(v)) for v in row] for row in dacc], np.uint16)
+    assert np.array_equal(y, y_ref)
+
+
+def test_shared_expert_slots_follow_the_routed_ones():
+    """Routed experts unchanged, one shared expert added: the routed slots' h rows are
+    the same as without the shared expert."""
+    cfg = shared_cfg(12, 1, E=5, k=2)
+    inp = synthetic.moe_inputs_host(cfg)
+    _, _, h1 = oracle.moe_tokens(inp["x"], inp["logits"], cfg.k, inp["wgu"], inp["sgu"], inp["wd"], inp["sd"],
+                                 cfg.T, cfg.H, cfg.I, cfg.E, want_h=True, n_shared=1)
+    routed = {k_: np.ascontiguousarray(v[:cfg.E]) for k_, v in inp.items() if k_ in ("wgu", "sgu", "wd", "sd")}
+    _, _, h0 = oracle.moe_tokens(inp["x"], inp["logits"], cfg.k, routed["wgu"], routed["sgu"], routed["wd"],
+                                 routed["sd"], cfg.T, cfg.H, cfg.I, cfg.E, want_h=True)
+    assert np.array_equal(h1.reshape(cfg.T, 3, cfg.I)[:, :2], h0.reshape(cfg.T, 2, cfg.I))
+
+
 def test_identical_experts_make_routing_irrelevant():
     cfg = tiny_cfg(6, T=4, H=64, I=32, E=6, k=3)
     inp = synthetic.moe_inputs_host(cfg)
