@@ -16,6 +16,12 @@ Functions pinned by ``tests/test_oracle_*.py``:
   moe_tokens               -> E = 1 reduction to the dense layer, identical-
                               expert invariance, a separately written fp64
                               brute-force MoE on tiny shapes
+  e4m3, mxfp8_quantize     -> torch's float8_e4m3fn decode and cast, nearest-
+                              value enumeration, scale/sign invariants
+  mx_linear_a8             -> one-hot extraction, reduction to mx_linear on
+                              MXFP8-representable activations, exact sums
+  moe_tokens(act8=True)    -> E = 1 reduction to two mx_linear_a8 calls,
+                              reduction to the bf16 layer, a brute force
 """
 from __future__ import annotations
 
@@ -65,8 +71,14 @@ def _load():
     lib.ora_route.argtypes = [P, I64, I64, I64, P, P]
     lib.ora_sort.argtypes = [P, I64, I64, I64, P, P, P, P, P]
     lib.ora_moe_tokens.argtypes = [P, P, I64, I64, P, P, P, P, I64, I64, I64, I64, P, I64, P, P, P, ctypes.c_int]
+    lib.ora_moe_tokens_a8.argtypes = lib.ora_moe_tokens.argtypes
+    lib.ora_e4m3.restype = ctypes.c_double
+    lib.ora_e4m3.argtypes = [ctypes.c_int]
+    lib.ora_mxfp8_quantize.argtypes = [P, I64, I64, P, P]
+    lib.ora_mx_linear_a8.argtypes = lib.ora_mx_linear.argtypes
     for name in ("ora_pack_codes", "ora_unpack_codes", "ora_dequant_f64", "ora_mx_linear",
-                 "ora_route", "ora_sort", "ora_moe_tokens"):
+                 "ora_route", "ora_sort", "ora_moe_tokens", "ora_moe_tokens_a8", "ora_mxfp8_quantize",
+                 "ora_mx_linear_a8"):
         getattr(lib, name).restype = None
     _lib = lib
     return lib
@@ -142,6 +154,37 @@ def mx_linear(x_bits: np.ndarray, w: np.ndarray, s: np.ndarray, T: int, K: int, 
     return y, acc, sd
 
 
+def e4m3(code: int) -> float:
+    """Value of an E4M3 byte (NaN for 0x7F and 0xFF)."""
+    return _load().ora_e4m3(int(code))
+
+
+def mxfp8_quantize(x_bits: np.ndarray, rows: int, K: int):
+    """MXFP8 quantization of bf16 rows: (codes uint8 [rows,K], scales uint8 [rows,K/32])."""
+    x_bits = _c(x_bits, np.uint16)
+    assert x_bits.size == rows * K and K % 32 == 0
+    codes = np.empty((rows, K), np.uint8)
+    scales = np.empty((rows, K // 32), np.uint8)
+    _load().ora_mxfp8_quantize(_p(x_bits), rows, K, _p(codes), _p(scales))
+    return codes, scales
+
+
+def mx_linear_a8(x_bits: np.ndarray, w: np.ndarray, s: np.ndarray, T: int, K: int, N: int,
+                 nthreads: int | None = None):
+    """The dense layer with MXFP8-quantized activations; returns as mx_linear, with
+    scale_d = sum_k |q(x) w|."""
+    x_bits = _c(x_bits, np.uint16)
+    w = _c(w, np.uint8)
+    s = _c(s, np.uint8)
+    assert x_bits.size == T * K and w.size == N * K // 2 and s.size == N * K // 32 and K % 32 == 0
+    y = np.empty((T, N), np.uint16)
+    acc = np.empty((T, N), np.float32)
+    sd = np.empty((T, N), np.float64)
+    _load().ora_mx_linear_a8(_p(x_bits), _p(w), _p(s), T, K, N, _p(y), _p(acc), _p(sd),
+                             nthreads or default_threads())
+    return y, acc, sd
+
+
 def route(logits: np.ndarray, k: int):
     """Returns (ids int32 [T,k], gates fp32 [T,k])."""
     logits = _c(logits, np.float32)
@@ -170,10 +213,13 @@ def sort(ids: np.ndarray, E: int):
 
 
 def moe_tokens(x_bits, logits, k, wgu, sgu, wd, sd, T, H, I, E, tokens=None, want_h=False,
-               nthreads: int | None = None, n_shared: int = 0):
+               nthreads: int | None = None, n_shared: int = 0, act8: bool = False):
     """MoE forward for the listed tokens (default: all).  Each token routes to k of the E
     routed experts (softmax gates over the selected logits) and to the n_shared shared
     experts E .. E + n_shared - 1 with gate 1; the weight arrays hold E + n_shared experts.
+
+    act8: quantize x before gate_up and h before down to MXFP8 (the GEMMs read the
+    quantized values; h is still returned in bf16, scale_m uses the quantized h).
 
     Returns (y bf16 bits [ntok,H], scale_m fp64 [ntok,H], h bf16 bits [ntok*(k+n_shared), I]
     or None).  Weight arrays may be any contiguous uint8 arrays holding [E+n_shared, ...] tensors.
@@ -192,7 +238,7 @@ def moe_tokens(x_bits, logits, k, wgu, sgu, wd, sd, T, H, I, E, tokens=None, wan
     y = np.empty((ntok, H), np.uint16)
     sm = np.empty((ntok, H), np.float64)
     h = np.empty((ntok * (k + n_shared), I), np.uint16) if want_h else None
-    _load().ora_moe_tokens(_p(x_bits), _p(logits), k, n_shared, _p(wgu), _p(sgu), _p(wd), _p(sd), T, H, I, E,
-                           _p(tokens), ntok, _p(y), _p(sm), _p(h) if want_h else None,
-                           nthreads or default_threads())
+    fn = _load().ora_moe_tokens_a8 if act8 else _load().ora_moe_tokens
+    fn(_p(x_bits), _p(logits), k, n_shared, _p(wgu), _p(sgu), _p(wd), _p(sd), T, H, I, E, _p(tokens), ntok,
+       _p(y), _p(sm), _p(h) if want_h else None, nthreads or default_threads())
     return y, sm, h

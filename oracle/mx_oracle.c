@@ -16,7 +16,8 @@
  *     needed weight once and applies it to every token of the step.
  *   - "Bringing Ultra-Fast, Interactive LLM Inference to AMD Instinct MI355X
  *     GPUs" (AMD ROCm blog), section "3. Low-Precision Data Types": 4-bit
- *     values with one shared scale per 32.
+ *     values with one shared scale per 32, fed to the matrix instructions
+ *     with MXFP8 activations (the *_a8 functions below).
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *   - E2M1 code c: sign = bit 3, bits 2..0 index the eight magnitudes in
@@ -35,6 +36,15 @@
  *   - Accumulation: fp32, K ascending, each product rounded to fp32 first;
  *     the combine sums the k gate-weighted fp32 down outputs in slot order and
  *     rounds once to bf16.
+ *   - MXFP8 activations (the *_a8 functions): the OCP MX format with E4M3
+ *     elements (bias 7, no infinities, S.1111.111 = NaN, largest 448).  Per
+ *     block of 32 consecutive K values of one activation row, the E8M0 scale
+ *     is 2^(floor(log2 amax) - 8) (8 = exponent of E4M3's largest value),
+ *     clamped to the E8M0 range, and each value divided by it is rounded to
+ *     the nearest E4M3 value (ties to even), saturating at +-448.  An all-zero
+ *     block gets scale byte 0; a block holding a NaN or an infinity gets
+ *     scale 0xFF (NaN) and codes 0x7F.  The MoE layer quantizes x before the
+ *     gate_up GEMM and the bf16 h before the down GEMM.
  *
  * Build: gcc -O2 -std=c11 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC
  * Contraction and fast-math are off so every fp32 operation is one IEEE
@@ -152,6 +162,21 @@ static float dot_row(const uint16_t* x, const uint8_t* w, const uint8_t* s, int6
   return acc;
 }
 
+/* The same dot product over activations given as exact fp64 values. */
+static float dot_vals(const double* a, const uint8_t* w, const uint8_t* s, int64_t K, int64_t r,
+                      double* abs_sum) {
+  float acc = 0.0f;
+  double as = 0.0;
+  for (int64_t k = 0; k < K; ++k) {
+    double p = a[k] * weight(w, s, K, r, k); /* exact in fp64 */
+    float pf = (float)p;
+    acc = acc + pf;
+    as += fabs(p);
+  }
+  if (abs_sum) *abs_sum = as;
+  return acc;
+}
+
 /* y[t,n] = bf16(sum_k x[t,k] * w[n,k]).  x: bf16 bits [T,K]; w: [N,K/2];
  * s: [N,K/32].  Outputs: y bf16 bits [T,N]; acc fp32 [T,N] (may be NULL);
  * scale_d fp64 [T,N] = sum_k |x*w| (may be NULL). */
@@ -169,6 +194,109 @@ void ora_mx_linear(const uint16_t* x, const uint8_t* w, const uint8_t* s, int64_
       if (acc) acc[t * N + n] = a;
       if (scale_d) scale_d[t * N + n] = as;
     }
+}
+
+/* ----------------------------------------------------- MXFP8 activations */
+
+/* E4M3 code -> value: sign bit 7, exponent bits 6..3 (bias 7), mantissa bits
+ * 2..0; exponent field 0 holds subnormals m * 2^-9; 0x7F / 0xFF are NaN. */
+double ora_e4m3(int code) {
+  code &= 0xFF;
+  int sg = code >> 7, e = (code >> 3) & 15, m = code & 7;
+  if (e == 15 && m == 7) return NAN;
+  double v = (e == 0) ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+  return sg ? -v : v;
+}
+
+/* Magnitude code (bits 6..0) of the E4M3 value nearest to a >= 0 (finite),
+ * ties to the even mantissa, saturating at 448. */
+static int e4m3_magnitude(double a) {
+  if (a >= 448.0) return 0x7E;
+  int e;
+  frexp(a, &e); /* a = f * 2^e, f in [0.5, 1): leading bit 2^(e-1) */
+  int lead = e - 1;
+  if (a == 0.0 || lead < -6) lead = -6; /* below 2^-6 the spacing is 2^-9 */
+  double q = ldexp(1.0, lead - 3);      /* 3 fraction bits */
+  double r = nearbyint(a / q) * q;      /* exact division; ties to even */
+  if (r < ldexp(1.0, -6)) return (int)(r / ldexp(1.0, -9)); /* subnormal */
+  int er;
+  double fr = frexp(r, &er); /* r < 448 before rounding, so r <= 448 here */
+  int ex = er - 1 + 7;
+  int m = (int)((fr * 2.0 - 1.0) * 8.0);
+  return (ex << 3) | m;
+}
+
+/* Quantize rows x K bf16 activations (K % 32 == 0) to MXFP8: codes [rows,K]
+ * (one E4M3 byte per value), scales [rows,K/32] (E8M0 bytes). */
+void ora_mxfp8_quantize(const uint16_t* x, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < K / 32; ++b) {
+      const uint16_t* blk = x + r * K + 32 * b;
+      uint8_t* cb = codes + r * K + 32 * b;
+      double amax = 0.0;
+      int finite = 1;
+      for (int i = 0; i < 32; ++i) {
+        double v = bf16_to_f64(blk[i]);
+        if (!isfinite(v)) finite = 0;
+        else if (fabs(v) > amax) amax = fabs(v);
+      }
+      if (!finite) {
+        scales[r * (K / 32) + b] = 0xFF;
+        for (int i = 0; i < 32; ++i) cb[i] = 0x7F;
+        continue;
+      }
+      int sbyte = 0;
+      if (amax > 0.0) {
+        int e;
+        frexp(amax, &e);
+        sbyte = (e - 1) - 8 + 127;
+        if (sbyte < 0) sbyte = 0;
+        if (sbyte > 254) sbyte = 254;
+      }
+      scales[r * (K / 32) + b] = (uint8_t)sbyte;
+      double scale = ldexp(1.0, sbyte - 127);
+      for (int i = 0; i < 32; ++i) {
+        double v = bf16_to_f64(blk[i]) / scale; /* exact: a power of two */
+        cb[i] = (uint8_t)((signbit(v) ? 0x80 : 0) | e4m3_magnitude(fabs(v)));
+      }
+    }
+}
+
+/* One activation row as the GEMM sees it: exact fp64 values of the row
+ * (bf16 as is, or quantized to MXFP8 and decoded when act8 is set). */
+static void activation_row(const uint16_t* x, int64_t K, int act8, double* out) {
+  if (!act8) {
+    for (int64_t k = 0; k < K; ++k) out[k] = bf16_to_f64(x[k]);
+    return;
+  }
+  uint8_t* c = (uint8_t*)malloc((size_t)K);
+  uint8_t* s = (uint8_t*)malloc((size_t)(K / 32));
+  ora_mxfp8_quantize(x, 1, K, c, s);
+  for (int64_t k = 0; k < K; ++k) out[k] = ora_e4m3(c[k]) * ora_e8m0(s[k / 32]);
+  free(c);
+  free(s);
+}
+
+/* The dense layer with MXFP8 activations: y[t,n] = bf16(sum_k q(x)[t,k] w[n,k]),
+ * q(x) the MXFP8-quantized x (K % 32 == 0).  Outputs as ora_mx_linear;
+ * scale_d = sum_k |q(x) * w|. */
+void ora_mx_linear_a8(const uint16_t* x, const uint8_t* w, const uint8_t* s, int64_t T, int64_t K,
+                      int64_t N, uint16_t* y, float* acc, double* scale_d, int nthreads) {
+  double* a = (double*)malloc(sizeof(double) * (size_t)(T * K));
+  for (int64_t t = 0; t < T; ++t) activation_row(x + t * K, K, 1, a + t * K);
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(static) collapse(2)
+#endif
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t n = 0; n < N; ++n) {
+      double as;
+      float v = dot_vals(a + t * K, w, s, K, n, &as);
+      if (y) y[t * N + n] = ora_bf16_rne((double)v);
+      if (acc) acc[t * N + n] = v;
+      if (scale_d) scale_d[t * N + n] = as;
+    }
+  free(a);
 }
 
 /* ---------------------------------------------------------------- routing */
@@ -250,12 +378,14 @@ static double swiglu(float g, float u) {
  * Sgu [E+n_shared,2I,H/32]; Wd [E+n_shared,H,I/2], Sd [E+n_shared,H,I/32].
  * Outputs indexed by position in tok: y [ntok,H] bf16 bits;
  * scale_m [ntok,H] = sum_j gate_j sum_i |h_i Wd[e][n,i]| (fp64, may be NULL);
- * h [ntok*(k+n_shared), I] bf16 bits (may be NULL). */
-void ora_moe_tokens(const uint16_t* x, const float* logits, int64_t k_routed, int64_t n_shared,
-                    const uint8_t* wgu, const uint8_t* sgu, const uint8_t* wd, const uint8_t* sd, int64_t T,
-                    int64_t H, int64_t I, int64_t E, const int32_t* tok, int64_t ntok, uint16_t* y,
-                    double* scale_m, uint16_t* h_out, int nthreads) {
-  (void)T;
+ * h [ntok*(k+n_shared), I] bf16 bits (may be NULL).
+ * With act8 set, x (before gate_up) and h (before down) are MXFP8-quantized
+ * per block of 32 (ora_mxfp8_quantize) and the GEMMs read the quantized
+ * values; h_out still returns the bf16 h and scale_m uses the quantized h. */
+static void moe_tokens_impl(const uint16_t* x, const float* logits, int64_t k_routed, int64_t n_shared,
+                            const uint8_t* wgu, const uint8_t* sgu, const uint8_t* wd, const uint8_t* sd,
+                            int64_t H, int64_t I, int64_t E, const int32_t* tok, int64_t ntok, uint16_t* y,
+                            double* scale_m, uint16_t* h_out, int nthreads, int act8) {
   const int64_t k = k_routed + n_shared;  /* slots per token */
   int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)(ntok * k));
   float* gates = (float*)malloc(sizeof(float) * (size_t)(ntok * k));
@@ -268,6 +398,9 @@ void ora_moe_tokens(const uint16_t* x, const float* logits, int64_t k_routed, in
   }
 
   uint16_t* h = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(ntok * k * I));
+  double* xa = (double*)malloc(sizeof(double) * (size_t)(ntok * H)); /* gate_up activations */
+  double* ha = (double*)malloc(sizeof(double) * (size_t)(ntok * k * I)); /* down activations */
+  for (int64_t i = 0; i < ntok; ++i) activation_row(x + (int64_t)tok[i] * H, H, act8, xa + i * H);
   const int64_t gu_rows = 2 * I;
   const size_t gu_w = (size_t)gu_rows * (size_t)(H / 2), gu_s = (size_t)gu_rows * (size_t)(H / 32);
   const size_t d_w = (size_t)H * (size_t)(I / 2), d_s = (size_t)H * (size_t)(I / 32);
@@ -277,14 +410,14 @@ void ora_moe_tokens(const uint16_t* x, const float* logits, int64_t k_routed, in
 #endif
   for (int64_t p = 0; p < ntok * k; ++p)
     for (int64_t n = 0; n < I; ++n) {
-      int64_t t = tok[p / k];
       int64_t e = ids[p];
       const uint8_t* W = wgu + (size_t)e * gu_w;
       const uint8_t* S = sgu + (size_t)e * gu_s;
-      float g = dot_row(x + t * H, W, S, H, n, NULL);
-      float u = dot_row(x + t * H, W, S, H, I + n, NULL);
+      float g = dot_vals(xa + (p / k) * H, W, S, H, n, NULL);
+      float u = dot_vals(xa + (p / k) * H, W, S, H, I + n, NULL);
       h[p * I + n] = ora_bf16_rne(swiglu(g, u));
     }
+  for (int64_t p = 0; p < ntok * k; ++p) activation_row(h + p * I, I, act8, ha + p * I);
 #ifdef _OPENMP
 #pragma omp parallel for schedule(static) collapse(2)
 #endif
@@ -296,7 +429,7 @@ void ora_moe_tokens(const uint16_t* x, const float* logits, int64_t k_routed, in
         int64_t p = i * k + j;
         int64_t e = ids[p];
         double as;
-        float d = dot_row(h + p * I, wd + (size_t)e * d_w, sd + (size_t)e * d_s, I, n, &as);
+        float d = dot_vals(ha + p * I, wd + (size_t)e * d_w, sd + (size_t)e * d_s, I, n, &as);
         float gd = (float)((double)gates[p] * (double)d);
         acc = acc + gd;
         sm += (double)gates[p] * as;
@@ -305,7 +438,28 @@ void ora_moe_tokens(const uint16_t* x, const float* logits, int64_t k_routed, in
       if (scale_m) scale_m[i * H + n] = sm;
     }
   if (h_out) memcpy(h_out, h, sizeof(uint16_t) * (size_t)(ntok * k * I));
+  free(ha);
+  free(xa);
   free(h);
   free(gates);
   free(ids);
+}
+
+void ora_moe_tokens(const uint16_t* x, const float* logits, int64_t k_routed, int64_t n_shared,
+                    const uint8_t* wgu, const uint8_t* sgu, const uint8_t* wd, const uint8_t* sd, int64_t T,
+                    int64_t H, int64_t I, int64_t E, const int32_t* tok, int64_t ntok, uint16_t* y,
+                    double* scale_m, uint16_t* h_out, int nthreads) {
+  (void)T;
+  moe_tokens_impl(x, logits, k_routed, n_shared, wgu, sgu, wd, sd, H, I, E, tok, ntok, y, scale_m, h_out,
+                  nthreads, 0);
+}
+
+/* The MoE layer with MXFP8 activations (see moe_tokens_impl). */
+void ora_moe_tokens_a8(const uint16_t* x, const float* logits, int64_t k_routed, int64_t n_shared,
+                       const uint8_t* wgu, const uint8_t* sgu, const uint8_t* wd, const uint8_t* sd, int64_t T,
+                       int64_t H, int64_t I, int64_t E, const int32_t* tok, int64_t ntok, uint16_t* y,
+                       double* scale_m, uint16_t* h_out, int nthreads) {
+  (void)T;
+  moe_tokens_impl(x, logits, k_routed, n_shared, wgu, sgu, wd, sd, H, I, E, tok, ntok, y, scale_m, h_out,
+                  nthreads, 1);
 }

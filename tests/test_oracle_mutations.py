@@ -11,6 +11,7 @@ import subprocess
 import pytest
 
 import oracle
+from tests import test_oracle_a8 as A8
 from tests import test_oracle_format as F
 from tests import test_oracle_linear as L
 from tests import test_oracle_moe as M
@@ -24,14 +25,19 @@ MUTATIONS = {
     "e8m0_bias": ("ldexp(1.0, (s & 0xFF) - 127)", "ldexp(1.0, (s & 0xFF) - 128)"),
     "magnitude_table": ("{0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0}", "{0.0, 0.5, 1.0, 1.5, 2.0, 2.5, 3.0, 4.0}"),
     "drop_up_projection": ("return gd / (1.0 + exp(-gd)) * (double)u;", "return gd / (1.0 + exp(-gd));"),
-    "swap_gate_up": ("float g = dot_row(x + t * H, W, S, H, n, NULL);\n      float u = dot_row(x + t * H, W, S, H, I + n, NULL);",
-                     "float u = dot_row(x + t * H, W, S, H, n, NULL);\n      float g = dot_row(x + t * H, W, S, H, I + n, NULL);"),
+    "swap_gate_up": ("float g = dot_vals(xa + (p / k) * H, W, S, H, n, NULL);\n      float u = dot_vals(xa + (p / k) * H, W, S, H, I + n, NULL);",
+                     "float u = dot_vals(xa + (p / k) * H, W, S, H, n, NULL);\n      float g = dot_vals(xa + (p / k) * H, W, S, H, I + n, NULL);"),
     "combine_wrong_gate": ("float gd = (float)((double)gates[p] * (double)d);", "float gd = (float)((double)gates[i * k] * (double)d);"),
     "tie_to_higher_id": ("if (best < 0 || l[e] > l[best]) best = e;", "if (best < 0 || l[e] >= l[best]) best = e;"),
     "unstable_sort": ("for (int64_t f = 0; f < F; ++f) {\n    int32_t e = ids[f];", "for (int64_t f = F - 1; f >= 0; --f) {\n    int32_t e = ids[f];"),
     "softmax_over_all": ("for (int64_t j = 0; j < k; ++j) den += exp((double)l[ids[t * k + j]] - m);",
                          "for (int64_t j = 0; j < E; ++j) den += exp((double)l[j] - m);"),
     "rounding_truncates": ("double n = nearbyint(a / q);", "double n = floor(a / q);"),
+    "e4m3_bias": ("ldexp((double)(8 + m), e - 10)", "ldexp((double)(8 + m), e - 11)"),
+    "mxfp8_scale_emax": ("sbyte = (e - 1) - 8 + 127;", "sbyte = (e - 1) - 7 + 127;"),
+    "e4m3_no_saturation": ("if (a >= 448.0) return 0x7E;", "if (a >= 480.0) return 0x7E;"),
+    "e4m3_subnormal_spacing": ("if (a == 0.0 || lead < -6) lead = -6;", "if (a == 0.0 || lead < -7) lead = -7;"),
+    "a8_h_not_quantized": ("activation_row(h + p * I, I, act8, ha + p * I);", "activation_row(h + p * I, I, 0, ha + p * I);"),
 }
 
 # pin tests expected to catch each mutation (each entry: callable(tmp_fixture_args) -> runs asserts)
@@ -57,6 +63,11 @@ CATCHERS = {
     "unstable_sort": [lambda: R.test_sort_matches_stable_argsort(4, 256, 8)],
     "softmax_over_all": [lambda: R.test_route_matches_lexsort_and_softmax(4, 256, 8)],
     "rounding_truncates": [lambda: F.test_bf16_rne_matches_torch_cast_on_floats()],
+    "e4m3_bias": [lambda: A8.test_e4m3_decode_matches_torch()],
+    "mxfp8_scale_emax": [lambda: A8.test_quantize_rounds_like_torch_over_all_bf16(0, 1.75)],
+    "e4m3_no_saturation": [lambda: A8.test_quantize_rounds_like_torch_over_all_bf16(0, 2 - 2.0 ** -7)],
+    "e4m3_subnormal_spacing": [lambda: A8.test_quantize_rounds_like_torch_over_all_bf16(0, 1.75)],
+    "a8_h_not_quantized": [lambda: A8.test_a8_moe_single_expert_reduces_to_a8_linear()],
 }
 
 
