@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replay")
     ap.add_argument("--persistent", action="store_true",
                     help="time the single-launch layer (moe_mxfp4_forward_persistent, T <= 16)")
+    ap.add_argument("--act8", action="store_true",
+                    help="MXFP8 activations for both expert GEMMs (moe_mxfp4_forward_a8, scaled MFMA)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32, help="tokens of the oracle's timed sample")
     ap.add_argument("--stage-steps", type=int, default=None, help="steps of the per-kernel event pass (default K)")
@@ -124,10 +126,10 @@ def main():
     cfg = workload_config(args.workload)
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
     ns = cfg.n_shared
-    if args.persistent and (T > 16 or T * k > 128 or ns):
-        raise SystemExit("--persistent takes T <= 16, T * top_k <= 128 and no shared experts")
+    if args.persistent and (T > 16 or T * k > 128 or ns or args.act8):
+        raise SystemExit("--persistent takes T <= 16, T * top_k <= 128, no shared experts and bf16 activations")
     # the event pass times each layer as a whole when the stage calls cannot reproduce it
-    whole_layer = args.persistent or ns > 0
+    whole_layer = args.persistent or ns > 0 or args.act8
     L = max(1, args.layers)
 
     def log(*a):
@@ -166,7 +168,7 @@ def main():
     def forward(lay):
         w = lay["w"]
         mx.moe_mxfp4_forward(lay["x"], lay["logits"], k, w["wgu"], w["sgu"], w["wd"], w["sd"], out=lay["y"], ws=ws,
-                             persistent=args.persistent, n_shared=ns)
+                             persistent=args.persistent, n_shared=ns, act8=args.act8)
 
     def staged(i, e, stream):
         lay = layers[i % L]
@@ -293,7 +295,7 @@ def main():
         log(f"[bench] oracle on {n} of {T} tokens, {threads} threads")
         c0 = time.perf_counter()
         oracle.moe_tokens(lay["x_bits"], lay["logits_host"], k, w_host["wgu"], w_host["sgu"], w_host["wd"],
-                          w_host["sd"], T, H, I, E, tokens=toks, nthreads=threads, n_shared=ns)
+                          w_host["sd"], T, H, I, E, tokens=toks, nthreads=threads, n_shared=ns, act8=args.act8)
         c1 = time.perf_counter()
         cpu = {
             "value": round((c1 - c0) * (T / n) * 1e6, 1),
@@ -317,11 +319,12 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8 (E4M3) x fp4 (E2M1), fp32 accumulate" if args.act8 else "bf16",
         "data": "synthetic",
         "config": {
             "workload": cfg.name, "T": T, "H": H, "I": I, "E": E, "top_k": k, "n_shared": ns, "routing": cfg.routing,
             "weights": "MXFP4 (E2M1 codes, E8M0 scale per 32)", "accumulate": "fp32",
+            "activations": "MXFP8 (E4M3, E8M0 scale per 32), quantized in the GEMM kernels" if args.act8 else "bf16",
             "layers_cycled": L, "timing": "eager launches" if args.eager else "HIP graph replay",
             "path": "one persistent launch" if args.persistent else "route_sort, gate_up, down, combine launches",
         },

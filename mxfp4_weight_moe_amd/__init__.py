@@ -49,15 +49,18 @@ _lib.moe_mxfp4_forward.argtypes = [_P, _P, _I64, _P, _P, _P, _P, _P, _I64, _I64,
 _lib.moe_mxfp4_forward_persistent.argtypes = list(_lib.moe_mxfp4_forward.argtypes)
 _lib.moe_mxfp4_forward_shared.argtypes = [_P, _P, _I64, _I64, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P,
                                           ctypes.c_size_t, _P]
+_lib.moe_mxfp4_forward_a8.argtypes = list(_lib.moe_mxfp4_forward_shared.argtypes)
+_lib.mx_linear_a8.argtypes = list(_lib.mx_linear.argtypes)
+_lib.mxfp8_quantize.argtypes = [_P, _I64, _I64, _P, _P, _P]
 for _n in ("mx_linear", "mxfp4_dequantize", "moe_route_topk", "moe_sort_by_expert", "moe_route_sort",
            "moe_gate_up_swiglu", "moe_down_combine", "moe_mxfp4_forward", "moe_mxfp4_forward_persistent",
-           "moe_mxfp4_forward_shared"):
+           "moe_mxfp4_forward_shared", "moe_mxfp4_forward_a8", "mx_linear_a8", "mxfp8_quantize"):
     getattr(_lib, _n).restype = ctypes.c_int
 
 EXPORTED = ("mx_version", "mx_status_string", "mx_linear", "mxfp4_dequantize", "moe_route_topk",
             "moe_sort_by_expert", "moe_route_sort", "moe_gate_up_swiglu", "moe_down_combine",
             "moe_mxfp4_workspace_size", "moe_mxfp4_forward", "moe_mxfp4_forward_persistent",
-            "moe_mxfp4_forward_shared")
+            "moe_mxfp4_forward_shared", "moe_mxfp4_forward_a8", "mx_linear_a8", "mxfp8_quantize")
 
 
 class MxError(RuntimeError):
@@ -110,8 +113,9 @@ def _raise(status: int, call: str):
 
 
 def mx_linear(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor,
-              out: torch.Tensor | None = None) -> torch.Tensor:
-    """y[T,N] = bf16(x[T,K] @ dequant(w)[N,K]^T), fp32 accumulation."""
+              out: torch.Tensor | None = None, act8: bool = False) -> torch.Tensor:
+    """y[T,N] = bf16(x[T,K] @ dequant(w)[N,K]^T), fp32 accumulation.
+    act8=True: x quantized to MXFP8 first, scaled MFMA (mx_linear_a8)."""
     _check(x, "x", torch.bfloat16, 2)
     dev = x.device
     _check(w_codes, "w_codes", torch.uint8, 2, dev)
@@ -125,9 +129,24 @@ def mx_linear(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor,
     _check(out, "out", torch.bfloat16, 2, dev)
     if out.shape != (T, N):
         raise ValueError("out has the wrong shape")
-    st = _lib.mx_linear(_ptr(x), _ptr(w_codes), _ptr(w_scales), _ptr(out), T, K, N, _stream(dev))
-    _raise(st, "mx_linear")
+    name = "mx_linear_a8" if act8 else "mx_linear"
+    st = getattr(_lib, name)(_ptr(x), _ptr(w_codes), _ptr(w_scales), _ptr(out), T, K, N, _stream(dev))
+    _raise(st, name)
     return out
+
+
+def mxfp8_quantize(x: torch.Tensor):
+    """MXFP8 (E4M3 codes, E8M0 scales per 32) of bf16 rows: (codes uint8 [R, K], scales uint8 [R, K/32])."""
+    _check(x, "x", torch.bfloat16, 2)
+    dev = x.device
+    R, K = x.shape
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    codes = torch.empty((R, K), dtype=torch.uint8, device=dev)
+    scales = torch.empty((R, K // 32), dtype=torch.uint8, device=dev)
+    st = _lib.mxfp8_quantize(_ptr(x), R, K, _ptr(codes), _ptr(scales), _stream(dev))
+    _raise(st, "mxfp8_quantize")
+    return codes, scales
 
 
 def mxfp4_dequantize(w_codes: torch.Tensor, w_scales: torch.Tensor) -> torch.Tensor:
@@ -293,11 +312,12 @@ def workspace(T: int, H: int, I: int, E: int, top_k: int, device) -> torch.Tenso
 def moe_mxfp4_forward(x: torch.Tensor, router_logits: torch.Tensor, top_k: int, W_gate_up: torch.Tensor,
                       S_gate_up: torch.Tensor, W_down: torch.Tensor, S_down: torch.Tensor,
                       out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
-                      persistent: bool = False, n_shared: int = 0) -> torch.Tensor:
+                      persistent: bool = False, n_shared: int = 0, act8: bool = False) -> torch.Tensor:
     """y[T,H] of the MXFP4 SwiGLU MoE layer (see include/mxmoe.h for the definition).
     persistent=True runs it as one persistent launch (moe_mxfp4_forward_persistent; T <= 16).
     n_shared > 0: the weights hold E routed + n_shared shared experts, router_logits [T, E]
-    (moe_mxfp4_forward_shared)."""
+    (moe_mxfp4_forward_shared).  act8=True: MXFP8 activations for both expert GEMMs
+    (moe_mxfp4_forward_a8, with or without shared experts)."""
     _check(x, "x", torch.bfloat16, 2)
     dev = x.device
     _check(router_logits, "router_logits", torch.float32, 2, dev)
@@ -319,13 +339,13 @@ def moe_mxfp4_forward(x: torch.Tensor, router_logits: torch.Tensor, top_k: int, 
     if ws is None:
         ws = workspace(T, H, I, Ew, top_k + n_shared, dev)
     _check(ws, "workspace", torch.uint8, 1, dev)
-    if n_shared:
-        if persistent:
-            raise ValueError("the single-launch layer has no shared experts")
-        name = "moe_mxfp4_forward_shared"
-        st = _lib.moe_mxfp4_forward_shared(_ptr(x), _ptr(router_logits), top_k, n_shared, _ptr(W_gate_up),
-                                           _ptr(S_gate_up), _ptr(W_down), _ptr(S_down), _ptr(out), T, H, I, E,
-                                           _ptr(ws), ws.numel(), _stream(dev))
+    if persistent and (n_shared or act8):
+        raise ValueError("the single-launch layer has neither shared experts nor MXFP8 activations")
+    if n_shared or act8:
+        name = "moe_mxfp4_forward_a8" if act8 else "moe_mxfp4_forward_shared"
+        st = getattr(_lib, name)(_ptr(x), _ptr(router_logits), top_k, n_shared, _ptr(W_gate_up), _ptr(S_gate_up),
+                                 _ptr(W_down), _ptr(S_down), _ptr(out), T, H, I, E, _ptr(ws), ws.numel(),
+                                 _stream(dev))
     else:
         name = "moe_mxfp4_forward_persistent" if persistent else "moe_mxfp4_forward"
         st = getattr(_lib, name)(_ptr(x), _ptr(router_logits), top_k, _ptr(W_gate_up), _ptr(S_gate_up),

@@ -17,20 +17,21 @@
 
 namespace mx {
 
-template <int NS>
-using GateUpPlain = GateUpPolicy<NS, GlobalSort, GU_XCHUNK, false>;
-template <int NS, class SR>
-using DownPlain = DownPolicy<NS, GlobalSort, DN_XCHUNK, false, SR>;
+// A8: MXFP8 activations (x for gate_up, h for down) and the scaled MFMA
+template <int NS, bool A8 = false>
+using GateUpPlain = GateUpPolicy<NS, GlobalSort, GU_XCHUNK, false, A8>;
+template <int NS, class SR, bool A8 = false>
+using DownPlain = DownPolicy<NS, GlobalSort, DN_XCHUNK, false, SR, A8>;
 
 // ------------------------------------------------------------------ kernels
 
-template <int NS>
+template <int NS, bool A8>
 __global__ void __launch_bounds__(WG_WAVES * 64) moe_gate_up_kernel(const uint16_t* __restrict__ x,
                                                                     const uint8_t* __restrict__ wgu,
                                                                     const uint8_t* __restrict__ sgu, SortView sv,
                                                                     uint16_t* __restrict__ h, int H, int I, int k,
                                                                     int32_t* claim) {
-  using P = GateUpPlain<NS>;
+  using P = GateUpPlain<NS, A8>;
   __shared__ __attribute__((aligned(16))) uint8_t xbufs[2 * P::XCHUNK];
   __shared__ __attribute__((aligned(16))) uint8_t slabs[WG_WAVES][SLAB_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t sslabs[WG_WAVES][P::Scales::template slab_bytes<NS>()];
@@ -63,13 +64,13 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_gate_up_kernel(const uint16
 }
 
 // SR, SPS: scale run and weight step (ScaleRun4, DN_SPS when I % 1024 == 0, else 1 and 1)
-template <int NS, class SR, int SPS>
+template <int NS, class SR, int SPS, bool A8>
 __global__ void __launch_bounds__(WG_WAVES * 64) moe_down_kernel(const uint16_t* __restrict__ h,
                                                                  const uint8_t* __restrict__ wd,
                                                                  const uint8_t* __restrict__ sd, SortView sv,
                                                                  float* __restrict__ dpart, int H, int I,
                                                                  int32_t* claim) {
-  using P = DownPlain<NS, SR>;
+  using P = DownPlain<NS, SR, A8>;
   __shared__ __attribute__((aligned(16))) uint8_t xbufs[2 * P::XCHUNK];
   __shared__ __attribute__((aligned(16))) uint8_t slabs[WG_WAVES][SLAB_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t sslabs[WG_WAVES][P::Scales::template slab_bytes<NS>()];
@@ -136,11 +137,12 @@ static int row_groups(int T) { return (T + 15) / 16; }
 
 // Full-width tiles unless they would leave resident workgroup slots idle (few active
 // experts and row groups, i.e. small T) and half-width tiles, twice the items, still fit in
-// one round of the slots: then half-width tiles, twice the waves.
-template <class K2, class K1>
-static bool use_half_tiles(K2 k2, K1 k1, int64_t items_full, int& grid) {
-  static const int occ2 = resident_wgs_per_cu(k2, WG_WAVES * 64);
-  static const int occ1 = resident_wgs_per_cu(k1, WG_WAVES * 64);
+// one round of the slots: then half-width tiles, twice the waves.  (The kernels are template
+// arguments, so each pair caches its own occupancy: kernels of one signature share a type.)
+template <auto K2, auto K1>
+static bool use_half_tiles(int64_t items_full, int& grid) {
+  static const int occ2 = resident_wgs_per_cu(K2, WG_WAVES * 64);
+  static const int occ1 = resident_wgs_per_cu(K1, WG_WAVES * 64);
   if (2 * items_full > (int64_t)device_cu_count() * occ1) {
     grid = expert_grid(items_full, occ2);
     return false;
@@ -149,46 +151,60 @@ static bool use_half_tiles(K2 k2, K1 k1, int64_t items_full, int& grid) {
   return true;
 }
 
-int launch_gate_up(const uint16_t* x, const uint8_t* wgu, const uint8_t* sgu, const SortView& sv, uint16_t* h,
-                   int32_t* ctl, int T, int H, int I, int E, int k, hipStream_t stream) {
-  if (H % (SEG_K * GU_SPS) != 0 || H % (SEG_K * SRUN) != 0 || I % (SUB_ROWS * WG_WAVES) != 0) return MX_ERR_SHAPE;
+template <bool A8>
+static int launch_gate_up_run(const uint16_t* x, const uint8_t* wgu, const uint8_t* sgu, const SortView& sv,
+                              uint16_t* h, int32_t* ctl, int T, int H, int I, int E, int k, hipStream_t stream) {
   const int gmax = row_groups(T);
   const int64_t items_full = (int64_t)gmax * max_active(T, E, k) * (I / (GateUpPlain<2>::TILE * WG_WAVES));
   int grid = 0;
-  if (use_half_tiles(moe_gate_up_kernel<2>, moe_gate_up_kernel<1>, items_full, grid))
-    hipLaunchKernelGGL(moe_gate_up_kernel<1>, dim3(grid), dim3(WG_WAVES * 64), 0, stream, x, wgu, sgu, sv, h, H, I, k,
-                       ctl + CTL_CLAIM_GU);
+  if (use_half_tiles<moe_gate_up_kernel<2, A8>, moe_gate_up_kernel<1, A8>>(items_full, grid))
+    hipLaunchKernelGGL((moe_gate_up_kernel<1, A8>), dim3(grid), dim3(WG_WAVES * 64), 0, stream, x, wgu, sgu, sv, h, H,
+                       I, k, ctl + CTL_CLAIM_GU);
   else
-    hipLaunchKernelGGL(moe_gate_up_kernel<2>, dim3(grid), dim3(WG_WAVES * 64), 0, stream, x, wgu, sgu, sv, h, H, I, k,
-                       ctl + CTL_CLAIM_GU);
+    hipLaunchKernelGGL((moe_gate_up_kernel<2, A8>), dim3(grid), dim3(WG_WAVES * 64), 0, stream, x, wgu, sgu, sv, h, H,
+                       I, k, ctl + CTL_CLAIM_GU);
   return hip_status(hipGetLastError());
 }
 
-template <class SR, int SPS>
+int launch_gate_up(const uint16_t* x, const uint8_t* wgu, const uint8_t* sgu, const SortView& sv, uint16_t* h,
+                   int32_t* ctl, int T, int H, int I, int E, int k, bool act8, hipStream_t stream) {
+  if (H % (SEG_K * GU_SPS) != 0 || H % (SEG_K * SRUN) != 0 || I % (SUB_ROWS * WG_WAVES) != 0) return MX_ERR_SHAPE;
+  if (act8) return launch_gate_up_run<true>(x, wgu, sgu, sv, h, ctl, T, H, I, E, k, stream);
+  return launch_gate_up_run<false>(x, wgu, sgu, sv, h, ctl, T, H, I, E, k, stream);
+}
+
+template <class SR, int SPS, bool A8>
 static int launch_down_run(const uint16_t* h, const uint8_t* wd, const uint8_t* sd, const SortView& sv, float* dpart,
                            int32_t* ctl, int T, int H, int I, int E, int k, hipStream_t stream) {
   const int gmax = row_groups(T);
   const int64_t items_full = (int64_t)gmax * max_active(T, E, k) * (H / (DownPlain<2, SR>::TILE * WG_WAVES));
   int grid = 0;
-  if (use_half_tiles(moe_down_kernel<2, SR, SPS>, moe_down_kernel<1, SR, SPS>, items_full, grid))
-    hipLaunchKernelGGL((moe_down_kernel<1, SR, SPS>), dim3(grid), dim3(WG_WAVES * 64), 0, stream, h, wd, sd, sv, dpart,
-                       H, I, ctl + CTL_CLAIM_DN);
+  if (use_half_tiles<moe_down_kernel<2, SR, SPS, A8>, moe_down_kernel<1, SR, SPS, A8>>(items_full, grid))
+    hipLaunchKernelGGL((moe_down_kernel<1, SR, SPS, A8>), dim3(grid), dim3(WG_WAVES * 64), 0, stream, h, wd, sd, sv,
+                       dpart, H, I, ctl + CTL_CLAIM_DN);
   else
-    hipLaunchKernelGGL((moe_down_kernel<2, SR, SPS>), dim3(grid), dim3(WG_WAVES * 64), 0, stream, h, wd, sd, sv, dpart,
-                       H, I, ctl + CTL_CLAIM_DN);
+    hipLaunchKernelGGL((moe_down_kernel<2, SR, SPS, A8>), dim3(grid), dim3(WG_WAVES * 64), 0, stream, h, wd, sd, sv,
+                       dpart, H, I, ctl + CTL_CLAIM_DN);
   return hip_status(hipGetLastError());
 }
 
-int launch_down(const uint16_t* h, const float* gates, const uint8_t* wd, const uint8_t* sd, const SortView& sv,
-                float* dpart, int32_t* ctl, int T, int H, int I, int E, int k, hipStream_t stream) {
-  (void)gates;  // applied by the combine
-  if (H % (2 * SUB_ROWS * WG_WAVES) != 0) return MX_ERR_SHAPE;
+template <bool A8>
+static int launch_down_mode(const uint16_t* h, const uint8_t* wd, const uint8_t* sd, const SortView& sv, float* dpart,
+                            int32_t* ctl, int T, int H, int I, int E, int k, hipStream_t stream) {
   // down's reduction length is I: 4-segment scale runs and 2-segment steps when I % 1024 == 0,
   // one-segment runs and steps for any other multiple of 256
   if (I % (SEG_K * SRUN) == 0 && I % (SEG_K * DN_SPS) == 0)
-    return launch_down_run<ScaleRun4, DN_SPS>(h, wd, sd, sv, dpart, ctl, T, H, I, E, k, stream);
-  if (I % SEG_K == 0) return launch_down_run<ScaleRun<1>, 1>(h, wd, sd, sv, dpart, ctl, T, H, I, E, k, stream);
+    return launch_down_run<ScaleRun4, DN_SPS, A8>(h, wd, sd, sv, dpart, ctl, T, H, I, E, k, stream);
+  if (I % SEG_K == 0) return launch_down_run<ScaleRun<1>, 1, A8>(h, wd, sd, sv, dpart, ctl, T, H, I, E, k, stream);
   return MX_ERR_SHAPE;
+}
+
+int launch_down(const uint16_t* h, const float* gates, const uint8_t* wd, const uint8_t* sd, const SortView& sv,
+                float* dpart, int32_t* ctl, int T, int H, int I, int E, int k, bool act8, hipStream_t stream) {
+  (void)gates;  // applied by the combine
+  if (H % (2 * SUB_ROWS * WG_WAVES) != 0) return MX_ERR_SHAPE;
+  if (act8) return launch_down_mode<true>(h, wd, sd, sv, dpart, ctl, T, H, I, E, k, stream);
+  return launch_down_mode<false>(h, wd, sd, sv, dpart, ctl, T, H, I, E, k, stream);
 }
 
 int launch_combine(const float* dpart, const float* gates, uint16_t* y, int T, int H, int k, hipStream_t stream) {

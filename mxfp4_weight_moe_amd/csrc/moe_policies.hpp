@@ -168,10 +168,11 @@ struct ExpertItems {
 //         (rows 0-7) and the 8 matching up rows (rows 8-15).  The MFMA result rows 8-15 sit
 //         in lanes 32-63, so one lane swap brings each up value beside its gate value.
 // Half-width tiles double the waves streaming a launch with few items (small T).
-template <int NS_, class Meta, int XCHUNK_, bool COH>
+template <int NS_, class Meta, int XCHUNK_, bool COH, bool A8 = false>
 struct GateUpPolicy : ExpertItems<Meta> {
   static constexpr int NS = NS_;
   static constexpr int XCHUNK = XCHUNK_;
+  static constexpr bool ACT8 = A8;  // x quantized to MXFP8 as it is staged
   typedef ScaleRun4 Scales;  // H % 1024 == 0
   static constexpr int TILE = NS == 2 ? SUB_ROWS : SUB_ROWS / 2;  // intermediate columns per wave
   struct EpiState {
@@ -252,10 +253,11 @@ struct GateUpPolicy : ExpertItems<Meta> {
 // A wave's tile is NS x 16 output columns (subtile i = columns n0 + 16 i ... + 15).  The
 // scale run is 4 segments when I % 1024 == 0, else 1 (I a multiple of 256, e.g. one
 // tensor-parallel eighth of an expert).
-template <int NS_, class Meta, int XCHUNK_, bool COH, class SR = ScaleRun4>
+template <int NS_, class Meta, int XCHUNK_, bool COH, class SR = ScaleRun4, bool A8 = false>
 struct DownPolicy : ExpertItems<Meta> {
   static constexpr int NS = NS_;
   static constexpr int XCHUNK = XCHUNK_;
+  static constexpr bool ACT8 = A8;  // h quantized to MXFP8 as it is staged
   typedef SR Scales;
   static constexpr int TILE = NS * SUB_ROWS;  // output columns per wave
   struct EpiState {

@@ -108,6 +108,24 @@ int mx_linear(const uint16_t* x, const uint8_t* w_codes, const uint8_t* w_scales
   return launch_mx_linear(x, w_codes, w_scales, y, (int)T, (int)K, (int)N, static_cast<hipStream_t>(stream));
 }
 
+int mx_linear_a8(const uint16_t* x, const uint8_t* w_codes, const uint8_t* w_scales, uint16_t* y, int64_t T,
+                 int64_t K, int64_t N, void* stream) {
+  if (!x || !w_codes || !w_scales || !y) return MX_ERR_NULL;
+  if (T < 1 || N < 1 || K < 32 || K % 32 != 0) return MX_ERR_SHAPE;
+  if (T > INT_LIM || K > INT_LIM || N > INT_LIM || T * K > (int64_t)1 << 40 || N * K > (int64_t)1 << 42)
+    return MX_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(w_codes, 16) || !aligned(y, 8)) return MX_ERR_ALIGN;
+  if (K % 256 == 0 && !aligned(w_scales, 8)) return MX_ERR_ALIGN;  // 8-byte scale loads
+  return launch_mx_linear_a8(x, w_codes, w_scales, y, (int)T, (int)K, (int)N, static_cast<hipStream_t>(stream));
+}
+
+int mxfp8_quantize(const uint16_t* x, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales, void* stream) {
+  if (!x || !codes || !scales) return MX_ERR_NULL;
+  if (rows < 1 || K < 32 || K % 32 != 0 || rows * (K / 32) > ((int64_t)1 << 38)) return MX_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(codes, 8)) return MX_ERR_ALIGN;
+  return launch_mxfp8_quantize(x, rows, K, codes, scales, static_cast<hipStream_t>(stream));
+}
+
 int mxfp4_dequantize(const uint8_t* w_codes, const uint8_t* w_scales, int64_t rows, int64_t K, uint16_t* out,
                      void* stream) {
   if (!w_codes || !w_scales || !out) return MX_ERR_NULL;
@@ -165,7 +183,7 @@ int moe_gate_up_swiglu(const uint16_t* x, const uint8_t* w_gate_up, const uint8_
   const MoeWorkspace ws = moe_workspace_carve(workspace, T, H, I, E, top_k);
   if (workspace_bytes < ws.bytes) return MX_ERR_WORKSPACE;
   const SortView sv{counts, offsets, sorted_slots, active, num_active};
-  return launch_gate_up(x, w_gate_up, s_gate_up, sv, h, ws.ctl, (int)T, (int)H, (int)I, (int)E, (int)top_k,
+  return launch_gate_up(x, w_gate_up, s_gate_up, sv, h, ws.ctl, (int)T, (int)H, (int)I, (int)E, (int)top_k, false,
                         static_cast<hipStream_t>(stream));
 }
 
@@ -186,7 +204,7 @@ int moe_down_combine(const uint16_t* h, const float* gates, const uint8_t* w_dow
   const SortView sv{counts, offsets, sorted_slots, active, num_active};
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = launch_down(h, gates, w_down, s_down, sv, ws.dpart, ws.ctl, (int)T, (int)H, (int)I, (int)E, (int)top_k,
-                        s)) != MX_OK)
+                        false, s)) != MX_OK)
     return st;
   return launch_combine(ws.dpart, gates, y, (int)T, (int)H, (int)top_k, s);
 }
@@ -196,11 +214,12 @@ size_t moe_mxfp4_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int6
   return moe_workspace_carve(nullptr, T, H, I, E, top_k).bytes;
 }
 
-// The layer over E routed experts (top_k of them per token) and ns shared experts after them.
+// The layer over E routed experts (top_k of them per token) and ns shared experts after them;
+// act8: MXFP8 activations for both expert GEMMs.
 static int moe_forward_impl(const uint16_t* x, const float* router_logits, int64_t top_k, int64_t ns,
                             const uint8_t* w_gate_up, const uint8_t* s_gate_up, const uint8_t* w_down,
                             const uint8_t* s_down, uint16_t* y, int64_t T, int64_t H, int64_t I, int64_t E,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+                            void* workspace, size_t workspace_bytes, bool act8, void* stream) {
   if (!x || !router_logits || !w_gate_up || !s_gate_up || !w_down || !s_down || !y) return MX_ERR_NULL;
   int st = check_moe_sizes(T, E, top_k);
   if (st != MX_OK) return st;
@@ -219,8 +238,10 @@ static int moe_forward_impl(const uint16_t* x, const float* router_logits, int64
                               ws.active, ws.num_active, s)) != MX_OK)
     return st;
   const SortView sv{ws.counts, ws.offsets, ws.sorted_slots, ws.active, ws.num_active};
-  if ((st = launch_gate_up(x, w_gate_up, s_gate_up, sv, ws.h, ws.ctl, t, h, i, e + n, k + n, s)) != MX_OK) return st;
-  if ((st = launch_down(ws.h, ws.gates, w_down, s_down, sv, ws.dpart, ws.ctl, t, h, i, e + n, k + n, s)) != MX_OK)
+  if ((st = launch_gate_up(x, w_gate_up, s_gate_up, sv, ws.h, ws.ctl, t, h, i, e + n, k + n, act8, s)) != MX_OK)
+    return st;
+  if ((st = launch_down(ws.h, ws.gates, w_down, s_down, sv, ws.dpart, ws.ctl, t, h, i, e + n, k + n, act8, s)) !=
+      MX_OK)
     return st;
   return launch_combine(ws.dpart, ws.gates, y, t, h, k + n, s);
 }
@@ -229,7 +250,7 @@ int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, int64_t top
                       const uint8_t* s_gate_up, const uint8_t* w_down, const uint8_t* s_down, uint16_t* y, int64_t T,
                       int64_t H, int64_t I, int64_t E, void* workspace, size_t workspace_bytes, void* stream) {
   return moe_forward_impl(x, router_logits, top_k, 0, w_gate_up, s_gate_up, w_down, s_down, y, T, H, I, E, workspace,
-                          workspace_bytes, stream);
+                          workspace_bytes, false, stream);
 }
 
 int moe_mxfp4_forward_shared(const uint16_t* x, const float* router_logits, int64_t top_k, int64_t n_shared,
@@ -237,7 +258,15 @@ int moe_mxfp4_forward_shared(const uint16_t* x, const float* router_logits, int6
                              const uint8_t* s_down, uint16_t* y, int64_t T, int64_t H, int64_t I, int64_t E,
                              void* workspace, size_t workspace_bytes, void* stream) {
   return moe_forward_impl(x, router_logits, top_k, n_shared, w_gate_up, s_gate_up, w_down, s_down, y, T, H, I, E,
-                          workspace, workspace_bytes, stream);
+                          workspace, workspace_bytes, false, stream);
+}
+
+int moe_mxfp4_forward_a8(const uint16_t* x, const float* router_logits, int64_t top_k, int64_t n_shared,
+                         const uint8_t* w_gate_up, const uint8_t* s_gate_up, const uint8_t* w_down,
+                         const uint8_t* s_down, uint16_t* y, int64_t T, int64_t H, int64_t I, int64_t E,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  return moe_forward_impl(x, router_logits, top_k, n_shared, w_gate_up, s_gate_up, w_down, s_down, y, T, H, I, E,
+                          workspace, workspace_bytes, true, stream);
 }
 
 int moe_mxfp4_forward_persistent(const uint16_t* x, const float* router_logits, int64_t top_k,

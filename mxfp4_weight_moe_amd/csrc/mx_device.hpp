@@ -117,8 +117,22 @@ __device__ __forceinline__ void stage_zero_x(Stage<NS, MT>& st) {
     for (int v = 0; v < 8; ++v) st.x[mt][v] = u32x4{0u, 0u, 0u, 0u};
 }
 
+// Activation pieces (8 values each) of half h of a segment: piece c of a lane in group g.
+// bf16 activations: the lane's row pointer is x + t * K + 32 * g, and pieces 0-3 are block
+// g + 4h.  A8 (MXFP8 activations for the scaled MFMA): the row pointer is
+// x + t * K + 32 * (g >> 1) + 16 * (g & 1); pieces 0, 1 are half (g & 1) of block 4h + (g >> 1)
+// and pieces 2, 3 the same half of block 4h + 2 + (g >> 1).
+template <bool A8>
+__device__ __forceinline__ int x_piece_off(int h, int c) {
+  return A8 ? h * 128 + (c >> 1) * 64 + (c & 1) * 8 : h * 128 + c * 8;
+}
+template <bool A8>
+__device__ __forceinline__ int x_piece_block(int g, int h, int c) {
+  return A8 ? 4 * h + 2 * (c >> 1) + (g >> 1) : g + 4 * h;
+}
+
 // Load segment `sg` (a full segment: all 8 blocks of the 256 K values exist).
-template <int NS, int MT>
+template <int NS, int MT, bool A8 = false>
 __device__ __forceinline__ void stage_load(Stage<NS, MT>& st, const StreamLanes<NS, MT>& L, int sg) {
   const size_t wo = (size_t)sg * SEG_BYTES;
 #pragma unroll
@@ -135,14 +149,14 @@ __device__ __forceinline__ void stage_load(Stage<NS, MT>& st, const StreamLanes<
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) st.x[mt][h * 4 + c] = ld16(xp + h * 128 + c * 8);
+        for (int c = 0; c < 4; ++c) st.x[mt][h * 4 + c] = ld16(xp + x_piece_off<A8>(h, c));
     }
   }
 }
 
 // Load a final partial segment with `nb` (< 8) valid MX blocks; missing blocks read as
 // zero codes and zero activations, so they add nothing.
-template <int NS, int MT>
+template <int NS, int MT, bool A8 = false>
 __device__ __forceinline__ void stage_load_tail(Stage<NS, MT>& st, const StreamLanes<NS, MT>& L, int sg, int nb,
                                                 int lane) {
   const size_t wo = (size_t)sg * SEG_BYTES;
@@ -165,10 +179,12 @@ __device__ __forceinline__ void stage_load_tail(Stage<NS, MT>& st, const StreamL
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const bool ok = (L.x[mt] != nullptr) && (b0 + 4 * h < nb);
       const uint16_t* xp = L.x[mt] + (size_t)sg * SEG_K;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) st.x[mt][h * 4 + c] = ok ? ld16(xp + h * 128 + c * 8) : u32x4{0u, 0u, 0u, 0u};
+      for (int c = 0; c < 4; ++c) {
+        const bool ok = (L.x[mt] != nullptr) && (x_piece_block<A8>(b0, h, c) < nb);
+        st.x[mt][h * 4 + c] = ok ? ld16(xp + x_piece_off<A8>(h, c)) : u32x4{0u, 0u, 0u, 0u};
+      }
     }
   }
 }
@@ -205,9 +221,22 @@ __device__ __forceinline__ void stage_compute(const Stage<NS, MT>& st, const Str
   }
 }
 
+template <int NS, int MT>
+__device__ void stage_compute_a8(const Stage<NS, MT>& st, const StreamLanes<NS, MT>& L, uint8_t* __restrict__ slab,
+                                 f32x4 (&acc)[MT][NS], int lane);  // mx_act8.hpp
+
+template <int NS, int MT, bool A8>
+__device__ __forceinline__ void stage_consume(const Stage<NS, MT>& st, const StreamLanes<NS, MT>& L,
+                                              uint8_t* __restrict__ slab, f32x4 (&acc)[MT][NS], int lane) {
+  if constexpr (A8)
+    stage_compute_a8(st, L, slab, acc, lane);
+  else
+    stage_compute(st, L, slab, acc);
+}
+
 // Stream segments [sg0, sg1) (+ an optional partial tail segment with nb_tail blocks at
 // index sg1) into acc with a D-deep register pipeline.
-template <int NS, int MT, int D>
+template <int NS, int MT, int D, bool A8 = false>
 __device__ __forceinline__ void stream_segments(const StreamLanes<NS, MT>& L, int sg0, int sg1, int nb_tail,
                                                 uint8_t* __restrict__ slab, f32x4 (&acc)[MT][NS], int lane) {
   Stage<NS, MT> st[D];
@@ -216,19 +245,19 @@ __device__ __forceinline__ void stream_segments(const StreamLanes<NS, MT>& L, in
   const int n = sg1 - sg0;
 #pragma unroll
   for (int d = 0; d < D; ++d)
-    if (d < n) stage_load(st[d], L, sg0 + d);
+    if (d < n) stage_load<NS, MT, A8>(st[d], L, sg0 + d);
   for (int b = 0; b < n; b += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       if (b + d < n) {
-        stage_compute(st[d], L, slab, acc);
-        if (b + d + D < n) stage_load(st[d], L, sg0 + b + d + D);
+        stage_consume<NS, MT, A8>(st[d], L, slab, acc, lane);
+        if (b + d + D < n) stage_load<NS, MT, A8>(st[d], L, sg0 + b + d + D);
       }
     }
   }
   if (nb_tail > 0) {
-    stage_load_tail(st[0], L, sg1, nb_tail, lane);
-    stage_compute(st[0], L, slab, acc);
+    stage_load_tail<NS, MT, A8>(st[0], L, sg1, nb_tail, lane);
+    stage_consume<NS, MT, A8>(st[0], L, slab, acc, lane);
   }
 }
 

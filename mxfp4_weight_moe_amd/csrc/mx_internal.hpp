@@ -66,6 +66,11 @@ int device_cu_count();
 int launch_mx_linear(const uint16_t* x, const uint8_t* w, const uint8_t* s, uint16_t* y, int T, int K, int N,
                      hipStream_t stream);
 int launch_dequant(const uint8_t* w, const uint8_t* s, int64_t rows, int64_t K, uint16_t* out, hipStream_t stream);
+// MXFP8 activations: the dense layer with x quantized in the lanes, and the quantizer alone
+int launch_mx_linear_a8(const uint16_t* x, const uint8_t* w, const uint8_t* s, uint16_t* y, int T, int K, int N,
+                        hipStream_t stream);
+int launch_mxfp8_quantize(const uint16_t* x, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales,
+                          hipStream_t stream);
 // ns: shared experts E .. E + ns - 1, routed by every token with gate 1 after its k routed
 // slots (ids and gates are [T, k + ns]; the sort then runs over E + ns experts)
 int launch_route(const float* logits, int T, int E, int k, int ns, int32_t* ids, float* gates, hipStream_t stream);
@@ -75,11 +80,12 @@ int launch_sort(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_
 int launch_route_sort(const float* logits, int T, int E, int k, int ns, int32_t* ids, float* gates, int32_t* counts,
                       int32_t* offsets, int32_t* sorted_slots, int32_t* active, int32_t* num_active,
                       hipStream_t stream);
-// ctl: the workspace's control words (the expert GEMMs claim their units there)
+// ctl: the workspace's control words (the expert GEMMs claim their units there);
+// act8: MXFP8 activations (x, resp. h, quantized as they are staged) and the scaled MFMA
 int launch_gate_up(const uint16_t* x, const uint8_t* wgu, const uint8_t* sgu, const SortView& sv, uint16_t* h,
-                   int32_t* ctl, int T, int H, int I, int E, int k, hipStream_t stream);
+                   int32_t* ctl, int T, int H, int I, int E, int k, bool act8, hipStream_t stream);
 int launch_down(const uint16_t* h, const float* gates, const uint8_t* wd, const uint8_t* sd, const SortView& sv,
-                float* dpart, int32_t* ctl, int T, int H, int I, int E, int k, hipStream_t stream);
+                float* dpart, int32_t* ctl, int T, int H, int I, int E, int k, bool act8, hipStream_t stream);
 int launch_combine(const float* dpart, const float* gates, uint16_t* y, int T, int H, int k, hipStream_t stream);
 // The whole layer as one persistent launch (small T); fused_layer_fits says when it applies.
 bool fused_layer_fits(int T, int E, int k, int H, int I);

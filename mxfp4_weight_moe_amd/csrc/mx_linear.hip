@@ -3,17 +3,20 @@
 //
 // The dense layer is the MXFP4 projection the AMD megakernel blog applies to attention
 // projections and the LM head ("Bringing Ultra-Fast, Interactive LLM Inference to AMD
-// Instinct MI355X GPUs", section "3. Low-Precision Data Types"); here activations stay bf16.
+// Instinct MI355X GPUs", section "3. Low-Precision Data Types").  Two activation modes:
+// bf16 (decode to bf16, bf16 MFMA), and MXFP8 as in that blog (activations quantized in the
+// lanes, scaled MFMA; mx_act8.hpp).
 //
 // Work split: one workgroup per 16 output rows of W; its W waves split the K segments and
 // sum their partial tiles through LDS in a fixed order.  Activation rows are processed in
 // passes of up to 32 (two MFMA m-tiles).
+#include "mx_act8.hpp"
 #include "mx_device.hpp"
 #include "mx_internal.hpp"
 
 namespace mx {
 
-template <int W, int MT, bool SBYTE>
+template <int W, int MT, bool SBYTE, bool A8>
 __device__ __forceinline__ void dense_pass(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
                                            const uint8_t* __restrict__ s, uint16_t* __restrict__ y, int T, int K,
                                            int N, int n0, int mp, uint8_t* slab, f32x4* red, int wave, int lane) {
@@ -29,7 +32,8 @@ __device__ __forceinline__ void dense_pass(const uint16_t* __restrict__ x, const
   L.s[0] = s + (size_t)min(n0 + (lane & 15), N - 1) * ks;
   for (int mt = 0; mt < MT; ++mt) {
     const int t = mp + mt * 16 + (lane & 15);
-    L.x[mt] = (t < T) ? x + (size_t)t * K + 32 * (lane >> 4) : nullptr;
+    const int xo = A8 ? 32 * (lane >> 5) + 16 * ((lane >> 4) & 1) : 32 * (lane >> 4);
+    L.x[mt] = (t < T) ? x + (size_t)t * K + xo : nullptr;
   }
   const int nseg = K / SEG_K;
   const int nb_tail = (K % SEG_K) / 32;
@@ -41,15 +45,15 @@ __device__ __forceinline__ void dense_pass(const uint16_t* __restrict__ x, const
     Stage<NS, MT> st;
     stage_zero_x(st);
     for (int sg = sg0; sg < sg1; ++sg) {
-      stage_load_tail(st, L, sg, 8, lane);
-      stage_compute(st, L, slab, acc);
+      stage_load_tail<NS, MT, A8>(st, L, sg, 8, lane);
+      stage_consume<NS, MT, A8>(st, L, slab, acc, lane);
     }
     if (wave == W - 1 && nb_tail > 0) {
-      stage_load_tail(st, L, nseg, nb_tail, lane);
-      stage_compute(st, L, slab, acc);
+      stage_load_tail<NS, MT, A8>(st, L, nseg, nb_tail, lane);
+      stage_consume<NS, MT, A8>(st, L, slab, acc, lane);
     }
   } else {
-    stream_segments<NS, MT, D>(L, sg0, sg1, (wave == W - 1) ? nb_tail : 0, slab, acc, lane);
+    stream_segments<NS, MT, D, A8>(L, sg0, sg1, (wave == W - 1) ? nb_tail : 0, slab, acc, lane);
   }
   wg_reduce<NS, MT, W>(acc, red, wave, lane);
   if (wave == 0) {
@@ -72,7 +76,7 @@ __device__ __forceinline__ void dense_pass(const uint16_t* __restrict__ x, const
   }
 }
 
-template <int W, bool SBYTE>
+template <int W, bool SBYTE, bool A8>
 __global__ void __launch_bounds__(W * 64) mx_linear_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
                                                            const uint8_t* __restrict__ s, uint16_t* __restrict__ y,
                                                            int T, int K, int N) {
@@ -82,37 +86,80 @@ __global__ void __launch_bounds__(W * 64) mx_linear_kernel(const uint16_t* __res
   const int n0 = blockIdx.x * SUB_ROWS;
   for (int mp = 0; mp < T; mp += 32) {
     if (T - mp > 16)
-      dense_pass<W, 2, SBYTE>(x, w, s, y, T, K, N, n0, mp, slabs[wave], red, wave, lane);
+      dense_pass<W, 2, SBYTE, A8>(x, w, s, y, T, K, N, n0, mp, slabs[wave], red, wave, lane);
     else
-      dense_pass<W, 1, SBYTE>(x, w, s, y, T, K, N, n0, mp, slabs[wave], red, wave, lane);
+      dense_pass<W, 1, SBYTE, A8>(x, w, s, y, T, K, N, n0, mp, slabs[wave], red, wave, lane);
   }
 }
 
-int launch_mx_linear(const uint16_t* x, const uint8_t* w, const uint8_t* s, uint16_t* y, int T, int K, int N,
-                     hipStream_t stream) {
+template <bool A8>
+static int launch_dense(const uint16_t* x, const uint8_t* w, const uint8_t* s, uint16_t* y, int T, int K, int N,
+                        hipStream_t stream) {
   const int items = (N + SUB_ROWS - 1) / SUB_ROWS;
   const int nseg = K / SEG_K;
+  // Up to 8 waves split K; with MXFP8 activations at most 4, whose registers then fit
+  // without spilling (8 waves of 64 lanes leave each lane half the register file).
+  constexpr int WMAX = A8 ? 4 : 8;
   int W = 1;
-  while (W < 8 && 2 * W <= nseg && items * W < 2048) W *= 2;
+  while (W < WMAX && 2 * W <= nseg && items * W < 2048) W *= 2;
   const bool sbyte = (K % SEG_K) != 0;
   dim3 grid(items), block(W * 64);
-#define MXL(WW, SB) hipLaunchKernelGGL((mx_linear_kernel<WW, SB>), grid, block, 0, stream, x, w, s, y, T, K, N)
+#define MXL(WW, SB) hipLaunchKernelGGL((mx_linear_kernel<WW, SB, A8>), grid, block, 0, stream, x, w, s, y, T, K, N)
   if (sbyte) {
     switch (W) {
       case 1: MXL(1, true); break;
       case 2: MXL(2, true); break;
       case 4: MXL(4, true); break;
-      default: MXL(8, true); break;
+      default:
+        if constexpr (WMAX == 8) MXL(8, true);
+        break;
     }
   } else {
     switch (W) {
       case 1: MXL(1, false); break;
       case 2: MXL(2, false); break;
       case 4: MXL(4, false); break;
-      default: MXL(8, false); break;
+      default:
+        if constexpr (WMAX == 8) MXL(8, false);
+        break;
     }
   }
 #undef MXL
+  return hip_status(hipGetLastError());
+}
+
+int launch_mx_linear(const uint16_t* x, const uint8_t* w, const uint8_t* s, uint16_t* y, int T, int K, int N,
+                     hipStream_t stream) {
+  return launch_dense<false>(x, w, s, y, T, K, N, stream);
+}
+
+int launch_mx_linear_a8(const uint16_t* x, const uint8_t* w, const uint8_t* s, uint16_t* y, int T, int K, int N,
+                        hipStream_t stream) {
+  return launch_dense<true>(x, w, s, y, T, K, N, stream);
+}
+
+// ------------------------------------------------------------------ MXFP8 quantization
+
+// One thread per 8-value piece; the 4 pieces of a block are 4 consecutive threads (rows are
+// contiguous and K % 32 == 0, so piece p belongs to block p / 4 of the flattened tensor).
+__global__ void __launch_bounds__(256) mxfp8_quantize_kernel(const uint16_t* __restrict__ x, int64_t npieces,
+                                                             uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool ok = p < npieces;  // npieces % 4 == 0: a block's 4 threads are all in or all out
+  const u32x4 v = ok ? ld16(x + p * 8) : u32x4{0u, 0u, 0u, 0u};
+  uint32_t sb;
+  const u32x2 c = act8_quant_quad(v, sb);
+  if (ok) {
+    *reinterpret_cast<u32x2*>(codes + p * 8) = c;
+    if ((p & 3) == 0) scales[p >> 2] = (uint8_t)sb;
+  }
+}
+
+int launch_mxfp8_quantize(const uint16_t* x, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales,
+                          hipStream_t stream) {
+  const int64_t npieces = rows * (K / 8);
+  const int64_t grid = (npieces + 255) / 256;
+  hipLaunchKernelGGL(mxfp8_quantize_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x, npieces, codes, scales);
   return hip_status(hipGetLastError());
 }
 

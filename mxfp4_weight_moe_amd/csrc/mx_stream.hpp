@@ -28,7 +28,13 @@
 // Loads retire in issue order and every step issues the same weight loads (an exhausted
 // cursor re-reads its last segment), so the compiler's waits stay exact: a segment waits
 // only for its own loads, issued one step earlier.
+//
+// MXFP8 activations (policies with ACT8): each thread quantizes its 16-byte piece of bf16
+// activations as it stores it into the chunk buffer (the 4 pieces of a 32-value block are
+// 4 consecutive threads), and segments go to the scaled MFMA with the weights' codes and
+// scales as they are (mx_act8.hpp).
 #pragma once
+#include "mx_act8.hpp"
 #include "mx_device.hpp"
 
 namespace mx {
@@ -241,6 +247,42 @@ __device__ __forceinline__ void xchunk_store(uint8_t* __restrict__ buf, const XC
   }
 }
 
+// MXFP8 chunk layout (ACT8): the 256 code bytes of row-segment (s, m) at (s * R + m) * 256,
+// as 16 pieces of 16 bytes XOR-swizzled by row (piece c at ((c ^ (m & 15)) << 4)), and its 8
+// scale bytes at XCHUNK / 2 + (s * R + m) * 8 (a chunk holds at most XCHUNK / 512
+// row-segments, so both halves fit).  Threads past the chunk quantize a repeat of its last
+// piece and store nothing: their block maximum would not be the block's.
+template <int XROUNDS, int XCHUNK>
+__device__ __forceinline__ void xchunk_store_a8(uint8_t* __restrict__ buf, const XChunk& ch,
+                                                const u32x4 (&xv)[XROUNDS], int tid) {
+  const int R = ch.info.rows;
+  const int npieces = R * ch.ns * 32;
+  const uint32_t inv = rows_reciprocal(R);
+#pragma unroll
+  for (int r = 0; r < XROUNDS; ++r) {
+    const int q0 = r * (WG_WAVES * 64) + tid;
+    const int q = min(q0, npieces - 1);
+    const int rs = q >> 5, pc = q & 31;
+    const int s = (int)(((uint32_t)rs * inv) >> 16), m = rs - s * R;
+    uint32_t sb;
+    const u32x2 c = act8_quant_quad(xv[r], sb);
+    if (q0 < npieces) {
+      const int row = s * R + m;
+      *reinterpret_cast<u32x2*>(buf + row * 256 + (((pc >> 1) ^ (m & 15)) << 4) + (pc & 1) * 8) = c;
+      if ((pc & 3) == 0) buf[XCHUNK / 2 + row * 8 + (pc >> 2)] = (uint8_t)sb;
+    }
+  }
+}
+
+template <int XROUNDS, int XCHUNK, bool A8>
+__device__ __forceinline__ void xchunk_put(uint8_t* __restrict__ buf, const XChunk& ch, const u32x4 (&xv)[XROUNDS],
+                                           int tid) {
+  if constexpr (A8)
+    xchunk_store_a8<XROUNDS, XCHUNK>(buf, ch, xv, tid);
+  else
+    xchunk_store<XROUNDS>(buf, ch, xv, tid);
+}
+
 // Consume one segment: LDS transpose of the codes, decode, MFMA with activations from the
 // chunk buffer (xrow: this lane's row within the chunk; rows past R read row 0, whose
 // products land in output columns that are not stored).  The scales come from the wave's
@@ -290,6 +332,51 @@ __device__ __forceinline__ void segment_compute(u32x4 (&w)[NS][2], const uint8_t
 #pragma unroll
       for (int i = 0; i < NS; ++i) acc[i] = mfma_bf16(decode8(wc[i][h][c4], sc[i]), xb, acc[i]);
     }
+  }
+}
+
+// The same with MXFP8 activations: the codes go to the scaled MFMA undecoded with their
+// scale bytes; the activation lane of group g reads pieces 8h + g and 8h + g + 4 of its row
+// (half g & 1 of blocks 4h + (g >> 1) and 4h + 2 + (g >> 1)) and the scale of block 4h + g.
+template <int NS, class SR, int XCHUNK>
+__device__ __forceinline__ void segment_compute_a8(u32x4 (&w)[NS][2], const uint8_t* __restrict__ sslab, int u,
+                                                   const WCursor<NS, SR>& c, int nseg_next,
+                                                   const uint8_t* __restrict__ xbuf, int sl, int R, int xrow,
+                                                   uint8_t* __restrict__ slab, const uint32_t (&lds_wr)[2],
+                                                   const uint32_t (&lds_rd)[2], uint32_t sshift, int lane,
+                                                   f32x4 (&acc)[NS]) {
+  u32x4 wc[NS][2];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    *reinterpret_cast<u32x4*>(slab + lds_wr[0]) = w[i][0];
+    *reinterpret_cast<u32x4*>(slab + lds_wr[1]) = w[i][1];
+    wc[i][0] = *reinterpret_cast<const u32x4*>(slab + lds_rd[0]);
+    wc[i][1] = *reinterpret_cast<const u32x4*>(slab + lds_rd[1]);
+  }
+  const size_t wo = (size_t)nseg_next * SEG_BYTES;
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    w[i][0] = ld_stream16(c.w[i][0] + wo);
+    w[i][1] = ld_stream16(c.w[i][1] + wo);
+  }
+  __builtin_amdgcn_sched_barrier(SCHED_ALL_BUT_VMEM);
+  u32x2 sc2[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i)
+    sc2[i] = *reinterpret_cast<const u32x2*>(sslab + (i * SUB_ROWS + (lane & 15)) * SR::ROW_BYTES + u * SEG_SCALES);
+  const int g = lane >> 4;
+  const int row = sl * R + xrow;
+  const uint8_t* xr = xbuf + row * 256;
+  const u32x2 xs2 = *reinterpret_cast<const u32x2*>(xbuf + XCHUNK / 2 + row * 8);
+  const int sw = xrow & 15;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const u32x4 xlo = *reinterpret_cast<const u32x4*>(xr + (((8 * h + g) ^ sw) << 4));
+    const u32x4 xhi = *reinterpret_cast<const u32x4*>(xr + (((8 * h + g + 4) ^ sw) << 4));
+    const int xs = (int)((xs2[h] >> sshift) & 0xFFu);
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+      acc[i] = mfma_scale_a8(wc[i][h], xlo, xhi, acc[i], (int)((sc2[i][h] >> sshift) & 0xFFu), xs);
   }
 }
 
@@ -395,6 +482,7 @@ struct ClaimedUnits {
 //   EpiState;  void c_setup(const ItemInfo&, int wave, EpiState&, int lane)
 //   void epilogue(const EpiState&, const f32x4 (&acc)[NS], int lane)
 //   static constexpr int XCHUNK;                    -- bytes of one activation chunk buffer
+//   static constexpr bool ACT8;                     -- MXFP8 activations, scaled MFMA
 //   typedef ScaleRun<...> Scales;                   -- scale staging run
 // `xbufs` is 2 * P::XCHUNK bytes of LDS, `xctr` 2 zeroed LDS counters, `slab` this wave's
 // SLAB_BYTES and `sslab` its P::Scales::slab_bytes<NS>() of LDS.  nseg must be a multiple of
@@ -496,7 +584,7 @@ __device__ __forceinline__ void stream_items(P& p, Seq& seq, uint8_t* __restrict
   u32x4 xv[XROUNDS];
   XChunk cur = chunk_of(first, 0);
   xchunk_load(p, cur, xv, tid);
-  xchunk_store(xbufs, cur, xv, tid);
+  xchunk_put<XROUNDS, XCHUNK_BYTES, P::ACT8>(xbufs, cur, xv, tid);
   xready_publish(&xctr[0]);
   int xb = 0;                  // LDS buffer holding `cur`
   uint32_t gen[2] = {1u, 0u};  // chunks published so far into each buffer
@@ -521,16 +609,22 @@ __device__ __forceinline__ void stream_items(P& p, Seq& seq, uint8_t* __restrict
   for (;;) {
     // one step: SPS segments; each segment's ring slot is reloaded with the next step
 #pragma unroll
-    for (int jj = 0; jj < SPS; ++jj)
-      segment_compute<NS, SR>(rw.w[jj], sslab, (cseg + jj) % SR::SRUN, cw, cw.seg + jj, xbufs + xb * XCHUNK_BYTES,
-                          cseg + jj - cur.c0, cur.info.rows, xrow, slab, lds_wr, lds_rd, sshift, lane, acc);
+    for (int jj = 0; jj < SPS; ++jj) {
+      if constexpr (P::ACT8)
+        segment_compute_a8<NS, SR, XCHUNK_BYTES>(rw.w[jj], sslab, (cseg + jj) % SR::SRUN, cw, cw.seg + jj,
+                                                 xbufs + xb * XCHUNK_BYTES, cseg + jj - cur.c0, cur.info.rows, xrow,
+                                                 slab, lds_wr, lds_rd, sshift, lane, acc);
+      else
+        segment_compute<NS, SR>(rw.w[jj], sslab, (cseg + jj) % SR::SRUN, cw, cw.seg + jj, xbufs + xb * XCHUNK_BYTES,
+                                cseg + jj - cur.c0, cur.info.rows, xrow, slab, lds_wr, lds_rd, sshift, lane, acc);
+    }
     advance_w();
     // Chunks and items end on step boundaries (their lengths are multiples of SPS).
     cseg += SPS;
     if (cseg >= cur.c0 + cur.ns) {
       // chunk done: publish this thread's pieces of the next chunk, wait for the rest
       if (have_next) {
-        xchunk_store(xbufs + (xb ^ 1) * XCHUNK_BYTES, nxt, xv, tid);
+        xchunk_put<XROUNDS, XCHUNK_BYTES, P::ACT8>(xbufs + (xb ^ 1) * XCHUNK_BYTES, nxt, xv, tid);
         xready_publish(&xctr[xb ^ 1]);
         gen[xb ^ 1] += 1u;
         xready_wait(&xctr[xb ^ 1], gen[xb ^ 1] * WG_THREADS);

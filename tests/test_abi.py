@@ -64,6 +64,31 @@ def test_mx_linear_rejects():
     assert L.mx_linear(A, A, A, P((1 << 20) + 2), 1, 64, 16, None) == MX_ERR_ALIGN
 
 
+def test_mxfp8_entry_points_reject():
+    L = m.raw()
+    assert L.mx_linear_a8(None, A, A, A, 1, 64, 16, None) == MX_ERR_NULL
+    assert L.mx_linear_a8(A, A, A, A, 1, 48, 16, None) == MX_ERR_SHAPE
+    assert L.mx_linear_a8(A, A, A, A, 0, 64, 16, None) == MX_ERR_SHAPE
+    assert L.mx_linear_a8(MIS, A, A, A, 1, 64, 16, None) == MX_ERR_ALIGN
+    assert L.mx_linear_a8(A, A, MIS, A, 1, 256, 16, None) == MX_ERR_ALIGN
+    assert L.mxfp8_quantize(None, 1, 32, A, A, None) == MX_ERR_NULL
+    assert L.mxfp8_quantize(A, 1, 48, A, A, None) == MX_ERR_SHAPE
+    assert L.mxfp8_quantize(A, 0, 32, A, A, None) == MX_ERR_SHAPE
+    assert L.mxfp8_quantize(MIS, 1, 32, A, A, None) == MX_ERR_ALIGN
+    assert L.mxfp8_quantize(A, 1, 32, MIS, A, None) == MX_ERR_ALIGN
+    ws = m.workspace_size(4, 1024, 1024, 9, 3)
+
+    def fwd(k=2, ns=1, T=4, E=8, H=1024, I=1024, w=A, wb=ws, x=A):
+        return L.moe_mxfp4_forward_a8(x, A, k, ns, A, A, A, A, A, T, H, I, E, w, wb, None)
+
+    assert fwd(x=None) == MX_ERR_NULL
+    assert fwd(T=0) == MX_ERR_SHAPE
+    assert fwd(ns=-1) == MX_ERR_SHAPE
+    assert fwd(I=320) == MX_ERR_SHAPE
+    assert fwd(x=MIS) == MX_ERR_ALIGN
+    assert fwd(wb=ws - 1) == MX_ERR_WORKSPACE
+
+
 def test_dequant_rejects():
     L = m.raw()
     assert L.mxfp4_dequantize(None, A, 1, 32, A, None) == MX_ERR_NULL
