@@ -38,7 +38,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 # their hash, so measured traffic is only reported for the kernel it was measured on
 GATE_UP_SOURCES = ("mxfp4_weight_moe_amd/build.py", "mxfp4_weight_moe_amd/csrc/mx_device.hpp",
                    "mxfp4_weight_moe_amd/csrc/mx_internal.hpp", "mxfp4_weight_moe_amd/csrc/mx_stream.hpp",
-                   "mxfp4_weight_moe_amd/csrc/moe_policies.hpp", "mxfp4_weight_moe_amd/csrc/moe_experts.hip")
+                   "mxfp4_weight_moe_amd/csrc/mx_act8.hpp", "mxfp4_weight_moe_amd/csrc/moe_policies.hpp",
+                   "mxfp4_weight_moe_amd/csrc/moe_experts.hip")
 GATE_UP_COUNTERS = os.path.join(ROOT, "profiles", "moe_gate_up_kernel.moe_t32_zipf.hbm_counters.txt")
 
 
