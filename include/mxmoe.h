@@ -129,7 +129,10 @@ MX_API int moe_route_topk(const float* logits, int64_t T, int64_t E, int64_t top
  *   counts       int32 [E]       slots per expert
  *   offsets      int32 [E + 1]   exclusive prefix sum of counts
  *   sorted_slots int32 [T*top_k] flat slots in sorted order
- *   active       int32 [E]       experts with counts > 0, ascending; -1 after the last
+ *   active       int32 [E]       experts with counts > 0, by row class descending (class 3:
+ *                                counts >= 8; 2: 4-7; 1: 2-3; 0: 1), then by expert id
+ *                                ascending; -1 after the last.  The expert GEMMs take their
+ *                                work in this order, so the items with the most rows go first
  *   num_active   int32 [2]       the number of active experts, then the largest count
  *                                (the expert GEMMs use it to bound their row groups)
  */

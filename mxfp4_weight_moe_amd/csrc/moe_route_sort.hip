@@ -58,14 +58,22 @@ struct SortShared {
   int32_t off[MX_MAX_EXPERTS];
   int32_t wave_sum[SORT_THREADS / 64];
   int32_t wave_max[SORT_THREADS / 64];
+  uint64_t wave_cls[SORT_THREADS / 64];
 };
+
+// Row class of an active expert: 3 for 8 or more routed rows, 2 for 4-7, 1 for 2-3, 0 for 1.
+// The active list runs heaviest class first, so the expert GEMMs deal and claim the items
+// with the most rows (the longest, since each stages its rows' activations) before the
+// lightest, and the last items claimed are short.
+__device__ __forceinline__ int row_class(int c) { return c >= 8 ? 3 : c >= 4 ? 2 : c >= 2 ? 1 : 0; }
 
 // Counting sort from the token masks (bits must hold every routed (expert, token) pair).
 // A slot (t, j) routed to expert e sets bit t of expert e's mask; because a token's k
 // experts are distinct, the rank of the slot among expert e's slots is the number of set
 // bits below t, which fixes a stable order without any ordering of atomics.  Counts and
-// the active list come from one packed block-wide scan, the largest count from a block
-// maximum.  `ids` is read for the scatter
+// offsets come from one packed block-wide scan, the active list's positions (row class
+// descending, then expert id) from a second one over four 16-bit class counters, and the
+// largest count from a block maximum.  `ids` is read for the scatter
 // (global or LDS).  Must be called by all SORT_THREADS threads.
 __device__ __forceinline__ void sort_from_bits(SortShared& sh, const int32_t* ids, int T, int k, int E,
                                                int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
@@ -88,6 +96,15 @@ __device__ __forceinline__ void sort_from_bits(SortShared& sh, const int32_t* id
     if (lane >= off) incl += o;
   }
   if (lane == 63) sh.wave_sum[wave] = incl;
+  // per-class active flags, one 16-bit field per class (at most 1024 experts per class)
+  const uint64_t cpk = (cnt > 0) ? (1ull << (16 * row_class(cnt))) : 0ull;
+  uint64_t cincl = cpk;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint64_t o = __shfl_up(cincl, off);
+    if (lane >= off) cincl += o;
+  }
+  if (lane == 63) sh.wave_cls[wave] = cincl;
   int most = cnt;  // largest count, over the wavefront
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) most = max(most, __shfl_xor(most, off));
@@ -101,16 +118,31 @@ __device__ __forceinline__ void sort_from_bits(SortShared& sh, const int32_t* id
       if (lane >= off) wv += o;
     }
     if (lane < SORT_THREADS / 64) sh.wave_sum[lane] = wv;  // inclusive over waves
+  } else if (wave == 1) {
+    uint64_t cv = (lane < SORT_THREADS / 64) ? sh.wave_cls[lane] : 0ull;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint64_t o = __shfl_up(cv, off);
+      if (lane >= off) cv += o;
+    }
+    if (lane < SORT_THREADS / 64) sh.wave_cls[lane] = cv;  // inclusive over waves
   }
   __syncthreads();
   const int excl = incl - packed + (wave > 0 ? sh.wave_sum[wave - 1] : 0);
   const int off_e = excl & 0xFFFF;
-  const int act_pos = excl >> 16;
+  const uint64_t cexcl = cincl - cpk + (wave > 0 ? sh.wave_cls[wave - 1] : 0ull);
+  const uint64_t ctot = sh.wave_cls[SORT_THREADS / 64 - 1];
   if (e < E) {
     sh.off[e] = off_e;
     counts[e] = cnt;
     offsets[e] = off_e;
-    if (cnt > 0) active[act_pos] = e;
+    if (cnt > 0) {
+      // heavier classes first: the totals of the classes above, then this class's rank
+      const int c = row_class(cnt);
+      int pos = (int)((cexcl >> (16 * c)) & 0xFFFFu);
+      for (int d = c + 1; d < 4; ++d) pos += (int)((ctot >> (16 * d)) & 0xFFFFu);
+      active[pos] = e;
+    }
   }
   const int total = sh.wave_sum[SORT_THREADS / 64 - 1];
   const int n_act = total >> 16;

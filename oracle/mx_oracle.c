@@ -328,13 +328,19 @@ void ora_route(const float* logits, int64_t T, int64_t E, int64_t k, int32_t* id
 
 /* ------------------------------------------------------------ expert sort */
 
+/* Row class of an active expert (its count of routed slots): 3 for 8 or more,
+ * 2 for 4-7, 1 for 2-3, 0 for 1. */
+static int row_class(int32_t c) { return c >= 8 ? 3 : c >= 4 ? 2 : c >= 2 ? 1 : 0; }
+
 /* Counting sort of the T*k flat slots f = t*k + j by expert id: experts
  * ascending, f ascending within an expert.  counts [E]; offsets [E+1]
  * (exclusive prefix sums); sorted_slots [T*k]; active [E] = experts with at
- * least one slot, ascending (entries past num_active are set to -1);
- * num_active [2] = the number of active experts, then the largest count. */
+ * least one slot, by row class descending, then by expert id ascending
+ * (entries past num_active are set to -1); num_active [2] = the number of
+ * active experts, then the largest count. */
 void ora_sort(const int32_t* ids, int64_t T, int64_t k, int64_t E, int32_t* counts, int32_t* offsets,
               int32_t* sorted_slots, int32_t* active, int32_t* num_active) {
+  if (E < 1) return;
   int64_t F = T * k;
   for (int64_t e = 0; e < E; ++e) counts[e] = 0;
   for (int64_t f = 0; f < F; ++f) counts[ids[f]] += 1;
@@ -348,8 +354,9 @@ void ora_sort(const int32_t* ids, int64_t T, int64_t k, int64_t E, int32_t* coun
   }
   free(fill);
   int32_t na = 0;
-  for (int64_t e = 0; e < E; ++e)
-    if (counts[e] > 0) active[na++] = (int32_t)e;
+  for (int cls = 3; cls >= 0; --cls)
+    for (int64_t e = 0; e < E; ++e)
+      if (counts[e] > 0 && row_class(counts[e]) == cls) active[na++] = (int32_t)e;
   for (int64_t e = na; e < E; ++e) active[e] = -1;
   int32_t most = 0;
   for (int64_t e = 0; e < E; ++e)

@@ -38,6 +38,7 @@ MUTATIONS = {
     "e4m3_no_saturation": ("if (a >= 448.0) return 0x7E;", "if (a >= 480.0) return 0x7E;"),
     "e4m3_subnormal_spacing": ("if (a == 0.0 || lead < -6) lead = -6;", "if (a == 0.0 || lead < -7) lead = -7;"),
     "a8_h_not_quantized": ("activation_row(h + p * I, I, act8, ha + p * I);", "activation_row(h + p * I, I, 0, ha + p * I);"),
+    "active_light_first": ("for (int cls = 3; cls >= 0; --cls)", "for (int cls = 0; cls <= 3; ++cls)"),
 }
 
 # pin tests expected to catch each mutation (each entry: callable(tmp_fixture_args) -> runs asserts)
@@ -68,6 +69,7 @@ CATCHERS = {
     "e4m3_no_saturation": [lambda: A8.test_quantize_rounds_like_torch_over_all_bf16(0, 2 - 2.0 ** -7)],
     "e4m3_subnormal_spacing": [lambda: A8.test_quantize_rounds_like_torch_over_all_bf16(0, 1.75)],
     "a8_h_not_quantized": [lambda: A8.test_a8_moe_single_expert_reduces_to_a8_linear()],
+    "active_light_first": [lambda: R.test_sort_matches_stable_argsort(32, 256, 8)],
 }
 
 

@@ -75,7 +75,10 @@ def test_sort_matches_stable_argsort(T, E, k):
     act = np.nonzero(counts)[0]
     assert r["num_active"] == act.size
     assert r["max_rows"] == counts.max()
-    assert np.array_equal(r["active"][: act.size], act) and np.all(r["active"][act.size:] == -1)
+    # heaviest row class first (>= 8, 4-7, 2-3, 1 rows), then expert id
+    cls = np.digitize(counts[act], [2, 4, 8])
+    order = act[np.lexsort((act, -cls))]
+    assert np.array_equal(r["active"][: act.size], order) and np.all(r["active"][act.size:] == -1)
 
 
 def test_expected_active_experts_uniform():
