@@ -112,7 +112,7 @@ def measured_traffic(workload: str):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this library has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
 
