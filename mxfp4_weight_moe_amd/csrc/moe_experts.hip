@@ -6,6 +6,11 @@
 // kernels with fused epilogues, no float atomics.
 //
 //   combine: y[t,:] = bf16(sum_j fl32(gate[t,j] * d[t*k + j,:])), j ascending.
+//            A kernel of its own, except at the smallest T (moe_down_kernel's FUSE variant,
+//            at most two items per workgroup): there every workgroup's items are dealt
+//            statically and each expert has one row group, so a workgroup can count, once
+//            its own items are done, the items finished per column quad; the one that
+//            completes a quad combines its columns.
 //
 // A persistent grid of workgroups sized to the device streams the items back to back
 // (mx_stream.hpp): extra row groups and three first-group items per workgroup dealt
@@ -20,8 +25,8 @@ namespace mx {
 // A8: MXFP8 activations (x for gate_up, h for down) and the scaled MFMA
 template <int NS, bool A8 = false>
 using GateUpPlain = GateUpPolicy<NS, GlobalSort, GU_XCHUNK, false, A8>;
-template <int NS, class SR, bool A8 = false>
-using DownPlain = DownPolicy<NS, GlobalSort, DN_XCHUNK, false, SR, A8>;
+template <int NS, class SR, bool A8 = false, bool FUSE = false>
+using DownPlain = DownPolicy<NS, GlobalSort, DN_XCHUNK, false, SR, A8, FUSE>;
 
 // ------------------------------------------------------------------ kernels
 
@@ -63,14 +68,76 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_gate_up_kernel(const uint16
   seq.finish();
 }
 
-// SR, SPS: scale run and weight step (ScaleRun4, DN_SPS when I % 1024 == 0, else 1 and 1)
-template <int NS, class SR, int SPS, bool A8>
+// The combine of the column quads this workgroup completes (FUSE launches).  Its items are
+// it = blockIdx.x + m * gridDim.x (no claims, one row group per expert), the down outputs
+// were written with device-coherent stores, and each wave's stores have completed
+// (vmcnt(0)) before the count.  A quad is complete when its count reaches na; the workgroup
+// that completes it resets the counter (nothing else touches it in this launch) and sums
+// the quad's columns for every token, j ascending, as moe_combine_kernel does.
+template <int TILE>
+__device__ __forceinline__ void combine_own_quads(int na, int nquad, int32_t* qctr, const float* __restrict__ gates,
+                                                  const float* dpart, uint16_t* __restrict__ y, int T, int k, int H,
+                                                  int32_t* done, uint32_t* ndone, int wave, int lane) {
+  wait_own_stores();
+  __syncthreads();
+  const int n_first = na * nquad;
+  if (wave == 0) {
+    int nd = 0;
+    for (int base = (int)blockIdx.x; base < n_first; base += 64 * (int)gridDim.x) {
+      const int it = base + lane * (int)gridDim.x;
+      bool fin = false;
+      int q = 0;
+      if (it < n_first) {
+        q = it % nquad;
+        fin = __hip_atomic_fetch_add(&qctr[q], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == na - 1;
+        if (fin) __hip_atomic_store(&qctr[q], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      const uint64_t m = __ballot(fin);
+      if (fin) done[nd + __popcll(m & ((1ull << lane) - 1ull))] = q;
+      nd += __popcll(m);
+    }
+    if (lane == 0) *ndone = (uint32_t)nd;
+  }
+  __syncthreads();
+  constexpr int QV = TILE * WG_WAVES / 4;  // 4-column groups per quad
+  const int nd = (int)*ndone;
+  const int tid = wave * 64 + lane;
+  for (int d = 0; d < nd; ++d) {
+    const int c0 = done[d] * (QV * 4);
+    for (int i = tid; i < T * QV; i += WG_WAVES * 64) {
+      const int t = i / QV;
+      const int n = c0 + (i - t * QV) * 4;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int j0 = 0; j0 < k; j0 += 8) {  // 8 loads in flight, then the sum, j ascending
+        u32x4 dv[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) dv[jj] = ld16_coherent(dpart + (size_t)(t * k + min(j0 + jj, k - 1)) * H + n);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          if (j0 + jj < k) {
+            const float g = gates[t * k + j0 + jj];
+            acc += f32x4{g * __uint_as_float(dv[jj][0]), g * __uint_as_float(dv[jj][1]),
+                         g * __uint_as_float(dv[jj][2]), g * __uint_as_float(dv[jj][3])};
+          }
+        }
+      }
+      const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
+      *reinterpret_cast<u32x2*>(y + (size_t)t * H + n) = u32x2{lo, hi};
+    }
+  }
+}
+
+// SR, SPS: scale run and weight step (ScaleRun4, DN_SPS when I % 1024 == 0, else 1 and 1).
+// FUSE: the launch also combines (small T; the launcher checks that no item is claimed).
+template <int NS, class SR, int SPS, bool A8, bool FUSE>
 __global__ void __launch_bounds__(WG_WAVES * 64) moe_down_kernel(const uint16_t* __restrict__ h,
                                                                  const uint8_t* __restrict__ wd,
                                                                  const uint8_t* __restrict__ sd, SortView sv,
                                                                  float* __restrict__ dpart, int H, int I,
-                                                                 int32_t* claim) {
-  using P = DownPlain<NS, SR, A8>;
+                                                                 int32_t* ctl, const float* __restrict__ gates,
+                                                                 uint16_t* __restrict__ y, int T, int k) {
+  using P = DownPlain<NS, SR, A8, FUSE>;
   __shared__ __attribute__((aligned(16))) uint8_t xbufs[2 * P::XCHUNK];
   __shared__ __attribute__((aligned(16))) uint8_t slabs[WG_WAVES][SLAB_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t sslabs[WG_WAVES][P::Scales::template slab_bytes<NS>()];
@@ -86,7 +153,7 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_down_kernel(const uint16_t*
   p.nquad = H / (P::TILE * WG_WAVES);
   p.na = p.m.num_active();
   p.n_items = ((p.m.max_rows() + 15) >> 4) * p.na * p.nquad;  // row-group levels that exist
-  ClaimedUnits seq{claim, (lds_i32*)cq, p.na * p.nquad, 0, false};
+  ClaimedUnits seq{ctl + CTL_CLAIM_DN, (lds_i32*)cq, p.na * p.nquad, 0, false};
   p.xact = h;
   p.wd = wd;
   p.sd = sd;
@@ -96,6 +163,9 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_down_kernel(const uint16_t*
   p.e_codes = (size_t)H * (I / 2);
   p.e_scales = (size_t)H * (I / 32);
   stream_items<P, SPS>(p, seq, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
+  if constexpr (FUSE)
+    combine_own_quads<P::TILE>(p.na, p.nquad, ctl + CTL_QUAD0, gates, dpart, y, T, k, H,
+                               reinterpret_cast<int32_t*>(xbufs), &xctr[0], wave, lane);
   seq.finish();
 }
 
@@ -173,38 +243,70 @@ int launch_gate_up(const uint16_t* x, const uint8_t* wgu, const uint8_t* sgu, co
   return launch_gate_up_run<false>(x, wgu, sgu, sv, h, ctl, T, H, I, E, k, stream);
 }
 
+// The combine goes into the down launch when every expert has one row group (T <= 16) and
+// no workgroup can get more than two items (min(T k, E) experts times the column quads):
+// then nothing is claimed, and the last workgroups' combine replaces a launch that costs
+// more.  With more items per workgroup the combine at the end of the last ones costs more
+// than the launch it saves (measured: slower at T = 8, and at T = 4 for I = 256).
+constexpr int FUSE_MAX_ITEMS = 2;
+static_assert(FUSE_MAX_ITEMS <= DYNAMIC_MIN, "a fused launch claims nothing");
+static bool fuse_combine(int T, int E, int k, int nquad, int grid) {
+  return T <= 16 && nquad <= CTL_MAX_QUADS && max_active(T, E, k) * nquad <= (int64_t)FUSE_MAX_ITEMS * grid;
+}
+
+template <int NS, class SR, int SPS, bool A8>
+static void launch_down_tiles(bool fuse, int grid, const uint16_t* h, const uint8_t* wd, const uint8_t* sd,
+                              const SortView& sv, float* dpart, int32_t* ctl, const float* gates, uint16_t* y, int T,
+                              int H, int I, int k, hipStream_t stream) {
+  if (fuse)
+    hipLaunchKernelGGL((moe_down_kernel<NS, SR, SPS, A8, true>), dim3(grid), dim3(WG_WAVES * 64), 0, stream, h, wd, sd,
+                       sv, dpart, H, I, ctl, gates, y, T, k);
+  else
+    hipLaunchKernelGGL((moe_down_kernel<NS, SR, SPS, A8, false>), dim3(grid), dim3(WG_WAVES * 64), 0, stream, h, wd,
+                       sd, sv, dpart, H, I, ctl, gates, y, T, k);
+}
+
 template <class SR, int SPS, bool A8>
-static int launch_down_run(const uint16_t* h, const uint8_t* wd, const uint8_t* sd, const SortView& sv, float* dpart,
-                           int32_t* ctl, int T, int H, int I, int E, int k, hipStream_t stream) {
+static int launch_down_run(const uint16_t* h, const float* gates, const uint8_t* wd, const uint8_t* sd,
+                           const SortView& sv, float* dpart, uint16_t* y, bool& combined, int32_t* ctl, int T, int H,
+                           int I, int E, int k, hipStream_t stream) {
   const int gmax = row_groups(T);
   const int64_t items_full = (int64_t)gmax * max_active(T, E, k) * (H / (DownPlain<2, SR>::TILE * WG_WAVES));
   int grid = 0;
-  if (use_half_tiles<moe_down_kernel<2, SR, SPS, A8>, moe_down_kernel<1, SR, SPS, A8>>(items_full, grid))
-    hipLaunchKernelGGL((moe_down_kernel<1, SR, SPS, A8>), dim3(grid), dim3(WG_WAVES * 64), 0, stream, h, wd, sd, sv,
-                       dpart, H, I, ctl + CTL_CLAIM_DN);
-  else
-    hipLaunchKernelGGL((moe_down_kernel<2, SR, SPS, A8>), dim3(grid), dim3(WG_WAVES * 64), 0, stream, h, wd, sd, sv,
-                       dpart, H, I, ctl + CTL_CLAIM_DN);
+  if (use_half_tiles<moe_down_kernel<2, SR, SPS, A8, false>, moe_down_kernel<1, SR, SPS, A8, false>>(items_full,
+                                                                                                    grid)) {
+    const int nquad = H / (DownPlain<1, SR>::TILE * WG_WAVES);
+    combined = fuse_combine(T, E, k, nquad, grid);
+    launch_down_tiles<1, SR, SPS, A8>(combined, grid, h, wd, sd, sv, dpart, ctl, gates, y, T, H, I, k, stream);
+  } else {
+    const int nquad = H / (DownPlain<2, SR>::TILE * WG_WAVES);
+    combined = fuse_combine(T, E, k, nquad, grid);
+    launch_down_tiles<2, SR, SPS, A8>(combined, grid, h, wd, sd, sv, dpart, ctl, gates, y, T, H, I, k, stream);
+  }
   return hip_status(hipGetLastError());
 }
 
 template <bool A8>
-static int launch_down_mode(const uint16_t* h, const uint8_t* wd, const uint8_t* sd, const SortView& sv, float* dpart,
-                            int32_t* ctl, int T, int H, int I, int E, int k, hipStream_t stream) {
+static int launch_down_mode(const uint16_t* h, const float* gates, const uint8_t* wd, const uint8_t* sd,
+                            const SortView& sv, float* dpart, uint16_t* y, bool& combined, int32_t* ctl, int T, int H,
+                            int I, int E, int k, hipStream_t stream) {
   // down's reduction length is I: 4-segment scale runs and 2-segment steps when I % 1024 == 0,
   // one-segment runs and steps for any other multiple of 256
   if (I % (SEG_K * SRUN) == 0 && I % (SEG_K * DN_SPS) == 0)
-    return launch_down_run<ScaleRun4, DN_SPS, A8>(h, wd, sd, sv, dpart, ctl, T, H, I, E, k, stream);
-  if (I % SEG_K == 0) return launch_down_run<ScaleRun<1>, 1, A8>(h, wd, sd, sv, dpart, ctl, T, H, I, E, k, stream);
+    return launch_down_run<ScaleRun4, DN_SPS, A8>(h, gates, wd, sd, sv, dpart, y, combined, ctl, T, H, I, E, k,
+                                                  stream);
+  if (I % SEG_K == 0)
+    return launch_down_run<ScaleRun<1>, 1, A8>(h, gates, wd, sd, sv, dpart, y, combined, ctl, T, H, I, E, k, stream);
   return MX_ERR_SHAPE;
 }
 
 int launch_down(const uint16_t* h, const float* gates, const uint8_t* wd, const uint8_t* sd, const SortView& sv,
-                float* dpart, int32_t* ctl, int T, int H, int I, int E, int k, bool act8, hipStream_t stream) {
-  (void)gates;  // applied by the combine
+                float* dpart, uint16_t* y, bool* combined, int32_t* ctl, int T, int H, int I, int E, int k, bool act8,
+                hipStream_t stream) {
+  *combined = false;
   if (H % (2 * SUB_ROWS * WG_WAVES) != 0) return MX_ERR_SHAPE;
-  if (act8) return launch_down_mode<true>(h, wd, sd, sv, dpart, ctl, T, H, I, E, k, stream);
-  return launch_down_mode<false>(h, wd, sd, sv, dpart, ctl, T, H, I, E, k, stream);
+  if (act8) return launch_down_mode<true>(h, gates, wd, sd, sv, dpart, y, *combined, ctl, T, H, I, E, k, stream);
+  return launch_down_mode<false>(h, gates, wd, sd, sv, dpart, y, *combined, ctl, T, H, I, E, k, stream);
 }
 
 int launch_combine(const float* dpart, const float* gates, uint16_t* y, int T, int H, int k, hipStream_t stream) {

@@ -142,11 +142,6 @@ __device__ __forceinline__ void fused_route_sort(const float* __restrict__ logit
 // Items of workgroup wg among n dealt round-robin over g workgroups.
 __device__ __forceinline__ int items_of(int wg, int g, int n) { return wg < n ? (n - 1 - wg) / g + 1 : 0; }
 
-__device__ __forceinline__ void wait_own_stores() {
-  __asm__ volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores have completed
-}
-
 template <int PER, int NSG, int NSD>
 __global__ void __launch_bounds__(WG_WAVES * 64) moe_fused_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ logits, const uint8_t* __restrict__ wgu,

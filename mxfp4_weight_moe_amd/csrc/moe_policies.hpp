@@ -107,6 +107,12 @@ __device__ __forceinline__ int group_slot(const Meta& m, int base, int rows, int
   return v;
 }
 
+// This wave's stores (and loads) have completed: s_waitcnt vmcnt(0).
+__device__ __forceinline__ void wait_own_stores() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
 // Segments per weight step: an item's segments (H / 256 for gate_up, I / 256 for down)
 // must be a multiple of these, which the launchers check.  Activation chunks are a
 // multiple of both, so they end on steps of either kernel.
@@ -252,8 +258,9 @@ struct GateUpPolicy : ExpertItems<Meta> {
 
 // A wave's tile is NS x 16 output columns (subtile i = columns n0 + 16 i ... + 15).  The
 // scale run is 4 segments when I % 1024 == 0, else 1 (I a multiple of 256, e.g. one
-// tensor-parallel eighth of an expert).
-template <int NS_, class Meta, int XCHUNK_, bool COH, class SR = ScaleRun4, bool A8 = false>
+// tensor-parallel eighth of an expert).  DCOH: the down outputs are written with
+// device-coherent stores (other workgroups of the launch combine them).
+template <int NS_, class Meta, int XCHUNK_, bool COH, class SR = ScaleRun4, bool A8 = false, bool DCOH = COH>
 struct DownPolicy : ExpertItems<Meta> {
   static constexpr int NS = NS_;
   static constexpr int XCHUNK = XCHUNK_;
@@ -308,7 +315,7 @@ struct DownPolicy : ExpertItems<Meta> {
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       float* dst = dpart + (size_t)s.slot * H + s.n0 + 16 * i + 4 * (lane >> 4);
-      if (COH) {
+      if (DCOH) {
         st8_coherent(dst, (uint64_t)__float_as_uint(acc[i][0]) | ((uint64_t)__float_as_uint(acc[i][1]) << 32));
         st8_coherent(dst + 2, (uint64_t)__float_as_uint(acc[i][2]) | ((uint64_t)__float_as_uint(acc[i][3]) << 32));
       } else {

@@ -203,10 +203,11 @@ int moe_down_combine(const uint16_t* h, const float* gates, const uint8_t* w_dow
   if (workspace_bytes < ws.bytes) return MX_ERR_WORKSPACE;
   const SortView sv{counts, offsets, sorted_slots, active, num_active};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = launch_down(h, gates, w_down, s_down, sv, ws.dpart, ws.ctl, (int)T, (int)H, (int)I, (int)E, (int)top_k,
-                        false, s)) != MX_OK)
+  bool combined = false;
+  if ((st = launch_down(h, gates, w_down, s_down, sv, ws.dpart, y, &combined, ws.ctl, (int)T, (int)H, (int)I, (int)E,
+                        (int)top_k, false, s)) != MX_OK)
     return st;
-  return launch_combine(ws.dpart, gates, y, (int)T, (int)H, (int)top_k, s);
+  return combined ? MX_OK : launch_combine(ws.dpart, gates, y, (int)T, (int)H, (int)top_k, s);
 }
 
 size_t moe_mxfp4_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k) {
@@ -240,10 +241,11 @@ static int moe_forward_impl(const uint16_t* x, const float* router_logits, int64
   const SortView sv{ws.counts, ws.offsets, ws.sorted_slots, ws.active, ws.num_active};
   if ((st = launch_gate_up(x, w_gate_up, s_gate_up, sv, ws.h, ws.ctl, t, h, i, e + n, k + n, act8, s)) != MX_OK)
     return st;
-  if ((st = launch_down(ws.h, ws.gates, w_down, s_down, sv, ws.dpart, ws.ctl, t, h, i, e + n, k + n, act8, s)) !=
-      MX_OK)
+  bool combined = false;
+  if ((st = launch_down(ws.h, ws.gates, w_down, s_down, sv, ws.dpart, y, &combined, ws.ctl, t, h, i, e + n, k + n,
+                        act8, s)) != MX_OK)
     return st;
-  return launch_combine(ws.dpart, ws.gates, y, t, h, k + n, s);
+  return combined ? MX_OK : launch_combine(ws.dpart, ws.gates, y, t, h, k + n, s);
 }
 
 int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, int64_t top_k, const uint8_t* w_gate_up,

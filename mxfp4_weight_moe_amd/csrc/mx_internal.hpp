@@ -84,8 +84,11 @@ int launch_route_sort(const float* logits, int T, int E, int k, int ns, int32_t*
 // act8: MXFP8 activations (x, resp. h, quantized as they are staged) and the scaled MFMA
 int launch_gate_up(const uint16_t* x, const uint8_t* wgu, const uint8_t* sgu, const SortView& sv, uint16_t* h,
                    int32_t* ctl, int T, int H, int I, int E, int k, bool act8, hipStream_t stream);
+// *combined is set when the down launch also wrote y (small T); otherwise the caller
+// launches the combine
 int launch_down(const uint16_t* h, const float* gates, const uint8_t* wd, const uint8_t* sd, const SortView& sv,
-                float* dpart, int32_t* ctl, int T, int H, int I, int E, int k, bool act8, hipStream_t stream);
+                float* dpart, uint16_t* y, bool* combined, int32_t* ctl, int T, int H, int I, int E, int k, bool act8,
+                hipStream_t stream);
 int launch_combine(const float* dpart, const float* gates, uint16_t* y, int T, int H, int k, hipStream_t stream);
 // The whole layer as one persistent launch (small T); fused_layer_fits says when it applies.
 bool fused_layer_fits(int T, int E, int k, int H, int I);

@@ -454,6 +454,34 @@ def test_single_launch_back_to_back_sizes(dev, mx):
         check_bound(to_host_bits(y), yo, sm, MOE_REL, f"back-to-back T={cfg.T}")
 
 
+def test_down_launch_combine_back_to_back(dev, mx):
+    """At small T the down launch also combines (the workgroup completing a column quad sums
+    it).  Calls of sizes on both sides of that rule, with shared experts and MXFP8
+    activations, back to back on one workspace without synchronizing: each must match the
+    oracle, and the control words must end zero."""
+    shapes = [dict(T=4, H=1024, I=1024, E=32, k=8), dict(T=1, H=2048, I=1024, E=8, k=2),
+              dict(T=40, H=1024, I=1024, E=16, k=2), dict(T=8, H=1024, I=512, E=64, k=8),
+              dict(T=2, H=1024, I=1024, E=6, k=2, n_shared=1), dict(T=16, H=1024, I=1024, E=64, k=8),
+              dict(T=3, H=1024, I=1024, E=32, k=4)]
+    say("down launch with its combine, back-to-back sizes")
+    ws = mx.workspace(40, 2048, 1024, 65, 9, dev)
+    runs = []
+    for i, s_ in enumerate(shapes):
+        cfg = synthetic.MoEConfig("b2b_comb", routing="normal", e_lo=-8, e_hi=-2, seed=200 + i, **s_)
+        host = synthetic.moe_inputs_host(cfg)
+        d, x, logits = moe_device_inputs(cfg, dev, host)
+        act8 = i % 3 == 1
+        y = mx.moe_mxfp4_forward(d["x"], d["logits"], cfg.k, d["wgu"], d["sgu"], d["wd"], d["sd"], ws=ws,
+                                 n_shared=cfg.n_shared, act8=act8)
+        runs.append((cfg, host, x, logits, y, act8))
+    torch.cuda.synchronize()
+    assert not ws[:CTL_BYTES].any().item()
+    for cfg, host, x, logits, y, act8 in runs:
+        yo, sm, _ = oracle.moe_tokens(x, logits, cfg.k, host["wgu"], host["sgu"], host["wd"], host["sd"], cfg.T,
+                                      cfg.H, cfg.I, cfg.E, n_shared=cfg.n_shared, act8=act8)
+        check_bound(to_host_bits(y), yo, sm, MOE_REL, f"back-to-back combine T={cfg.T} act8={act8}")
+
+
 @pytest.mark.parametrize("T,persistent", [(4, True), (4, False), (20, False)])
 def test_forward_graph_replays(dev, mx, T, persistent):
     """The forward captured in a HIP graph: every replay, with eager work and
