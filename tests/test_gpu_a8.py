@@ -203,3 +203,40 @@ def test_moe_a8_full_size(dev, mx, name, tokens):
     y, sm = oracle_moe_a8(cfg, x, logits, w, tokens=tok)
     worst = check_bound(got[tok], y, sm, MOE_REL, name)
     say(f"  worst ratio {worst:.3g}")
+
+
+@pytest.mark.parametrize("T", [2, 20])
+def test_moe_a8_graph_replays(dev, mx, T):
+    """The MXFP8 forward captured in a HIP graph (at T = 2 its down launch also combines):
+    every replay, with eager work and synchronizations between replays, gives the eager
+    result bit for bit, and the workspace control words end zero."""
+    cfg = synthetic.MoEConfig("graph_a8", T=T, H=1024, I=1024, E=16, k=4, routing="normal", e_lo=-8, e_hi=-2,
+                              seed=40 + T)
+    host = synthetic.moe_inputs_host(cfg)
+    say("a8 forward graph replays, T =", T)
+    d, x, logits = moe_inputs(cfg, dev, host)
+    ws = mx.workspace(T, cfg.H, cfg.I, cfg.E, cfg.k, dev)
+    out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
+    fwd = lambda: mx.moe_mxfp4_forward(d["x"], d["logits"], cfg.k, d["wgu"], d["sgu"], d["wd"], d["sd"], out=out,
+                                       ws=ws, act8=True)
+    fwd()
+    torch.cuda.synchronize()
+    ref = to_host_bits(out)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            fwd()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    for r in range(4):
+        out.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host_bits(out), ref), f"replay {r}"
+        fwd()
+        torch.cuda.synchronize()
+    assert not ws[:57344].any().item()
+    y, sm = oracle_moe_a8(cfg, x, logits, host)
+    check_bound(ref, y, sm, MOE_REL, f"a8 graph T={T}")
