@@ -383,7 +383,14 @@ __device__ __forceinline__ void segment_compute_a8(u32x4 (&w)[NS][2], const uint
 // The items of a workgroup, in three phases:
 //   A  extra row groups (items it >= F, F = na * nquad, valid only for experts with more
 //      than 16 rows; few), dealt round-robin, first, because each is as long as any other
-//      item and leaving them to the end would lengthen the tail;
+//      item and leaving them to the end would lengthen the tail.  The extra group of item
+//      j (the same expert and column quad as first-group item j) goes to workgroup
+//      (j + XOFF) mod G, with XOFF = F mod G rounded up to a multiple of 8.  Round-robin
+//      dealing leaves workgroups XOFF.. one first-group item short of the others (idle,
+//      when F < G), so the extra groups even out the rounds instead of adding one; and
+//      since workgroups are placed on the 8 XCDs round-robin, the extra group of item j
+//      runs on the XCD of first-group item j, where the two reads of the same weight rows
+//      can share that XCD's L2;
 //   B  first-group items wg, wg + G, wg + 2G (STATIC_UNITS of them; G workgroups);
 //   C  further first-group items: dealt round-robin too (StaticUnits), or claimed from a
 //      device counter as workgroups become free (ClaimedUnits), so that workgroups that
@@ -526,7 +533,8 @@ __device__ __forceinline__ void stream_items(P& p, Seq& seq, uint8_t* __restrict
   };
   ItemPos first;
   first.n = -1;
-  first.it = next_extra(n_first + wg);
+  const int xoff = ((n_first % n_wg + 7) & ~7) % n_wg;  // XOFF
+  first.it = next_extra(n_first + (wg + n_wg - xoff) % n_wg);
   if (first.it >= p.n_items) {
     first.n = 0;
     first.it = seq.unit(0);
