@@ -266,6 +266,16 @@ static void launch_down_tiles(bool fuse, int grid, const uint16_t* h, const uint
                        sd, sv, dpart, H, I, ctl, gates, y, T, k);
 }
 
+// Wide tiles (4 subtiles, 64 output columns per wave) for reductions of one 256-value
+// segment per scale run (I not a multiple of 1024, e.g. one tensor-parallel eighth of an
+// expert): such an item is a single step, so its fixed costs (item metadata, the activation
+// hand-off, the epilogue) outweigh its weight bytes, and the wider tile halves the items.
+// The launch runs 2 workgroups per CU instead of 3, and half the items balance less
+// evenly, so wide tiles pay only when the workgroups get at least WIDE_MIN_ITEMS items
+// (host bound: min(T k, E) active experts).  Measured on the TP8 share: down 43.1 ->
+// 37.9 us at T = 32, but 19.3 -> 20.7 us at T = 4 (under 2 items per workgroup).
+constexpr int WIDE_MIN_ITEMS = 4;
+
 template <class SR, int SPS, bool A8>
 static int launch_down_run(const uint16_t* h, const float* gates, const uint8_t* wd, const uint8_t* sd,
                            const SortView& sv, float* dpart, uint16_t* y, bool& combined, int32_t* ctl, int T, int H,
@@ -273,6 +283,18 @@ static int launch_down_run(const uint16_t* h, const float* gates, const uint8_t*
   const int gmax = row_groups(T);
   const int64_t items_full = (int64_t)gmax * max_active(T, E, k) * (H / (DownPlain<2, SR>::TILE * WG_WAVES));
   int grid = 0;
+  if constexpr (SR::SRUN == 1 && !A8) {
+    if (H % (DownPlain<4, SR>::TILE * WG_WAVES) == 0) {
+      static const int occ4 = resident_wgs_per_cu(moe_down_kernel<4, SR, SPS, A8, false>, WG_WAVES * 64);
+      if (items_full / 2 >= (int64_t)WIDE_MIN_ITEMS * device_cu_count() * occ4) {
+        grid = expert_grid(items_full / 2, occ4);
+        const int nquad = H / (DownPlain<4, SR>::TILE * WG_WAVES);
+        combined = fuse_combine(T, E, k, nquad, grid);
+        launch_down_tiles<4, SR, SPS, A8>(combined, grid, h, wd, sd, sv, dpart, ctl, gates, y, T, H, I, k, stream);
+        return hip_status(hipGetLastError());
+      }
+    }
+  }
   if (use_half_tiles<moe_down_kernel<2, SR, SPS, A8, false>, moe_down_kernel<1, SR, SPS, A8, false>>(items_full,
                                                                                                     grid)) {
     const int nquad = H / (DownPlain<1, SR>::TILE * WG_WAVES);

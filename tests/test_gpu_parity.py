@@ -370,9 +370,11 @@ def test_moe_shared_experts(dev, mx, shape):
     assert np.array_equal(run_moe(mx, d, cfg.k, cfg.n_shared), got)  # deterministic
 
 
-# down reductions that are not multiples of 1024 (one-segment scale runs): I = 256, 512, 768
+# down reductions that are not multiples of 1024 (one-segment scale runs): I = 256, 512, 768.
+# The last shape has enough items (5 row-group levels x 64 experts x 8 wide quads, at least
+# 4 per resident workgroup) for down's wide tiles, and experts with more than 16 rows.
 NARROW = [dict(T=5, H=1024, I=256, E=8, k=2), dict(T=20, H=2048, I=512, E=6, k=3), dict(T=3, H=1024, I=768, E=4, k=4),
-          dict(T=40, H=1024, I=256, E=4, k=2)]
+          dict(T=40, H=1024, I=256, E=4, k=2), dict(T=80, H=2048, I=256, E=64, k=8)]
 
 
 @pytest.mark.parametrize("shape", NARROW, ids=[f"T{s['T']}_H{s['H']}_I{s['I']}_E{s['E']}_k{s['k']}" for s in NARROW])
