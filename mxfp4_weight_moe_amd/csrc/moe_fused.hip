@@ -62,6 +62,7 @@ struct LdsSort {
   __device__ __forceinline__ int count(int a) const { return __builtin_amdgcn_readfirstlane(fsort.cnt[a]); }
   __device__ __forceinline__ int offset(int a) const { return __builtin_amdgcn_readfirstlane(fsort.off[a]); }
   __device__ __forceinline__ int slot(int i) const { return __builtin_amdgcn_readfirstlane(fsort.slots[i]); }
+  __device__ __forceinline__ int count_lane(int a) const { return fsort.cnt[a]; }
 };
 
 // Routing and counting sort of one workgroup into fsort; `tmp` is scratch LDS of at least

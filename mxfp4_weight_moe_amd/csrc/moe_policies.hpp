@@ -48,6 +48,8 @@ struct GlobalSort {
   __device__ __forceinline__ int count(int a) const { return ld_uniform(sv.counts, expert(a)); }
   __device__ __forceinline__ int offset(int a) const { return ld_uniform(sv.offsets, expert(a)); }
   __device__ __forceinline__ int slot(int i) const { return ld_uniform(sv.sorted_slots, i); }
+  // the rows of active expert a for a per-lane a (vector loads)
+  __device__ __forceinline__ int count_lane(int a) const { return sv.counts[sv.active[a]]; }
 };
 
 // Device-coherent 8- and 16-byte accesses (agent-scope relaxed atomics compile to plain
@@ -151,6 +153,11 @@ struct ExpertItems {
   __device__ __forceinline__ bool valid(int it) const {
     const ItemIndex ix = item_decode(it, nquad, na);
     return ix.g * 16 < m.count(ix.a);
+  }
+  // valid() for a per-lane item
+  __device__ __forceinline__ bool valid_lane(int it) const {
+    const ItemIndex ix = item_decode(it, nquad, na);
+    return ix.g * 16 < m.count_lane(ix.a);
   }
   __device__ __forceinline__ ItemInfo info(int it) const {
     const ItemIndex ix = item_decode(it, nquad, na);

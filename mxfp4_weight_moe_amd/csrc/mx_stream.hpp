@@ -480,7 +480,7 @@ struct ClaimedUnits {
 
 // Drive one workgroup over its items.  Policy P provides:
 //   static constexpr int NS;   int nseg, n_items;   const uint16_t* xact;
-//   int first_groups();   bool valid(int it);   ItemInfo info(int it);
+//   int first_groups();   bool valid_lane(int it) (per lane);   ItemInfo info(int it);
 //   u32x4 xload(const uint16_t*)                    -- one 16-byte activation load
 //   void wait_inputs()                              -- before the first activation load
 //   int x_row_offset(const ItemInfo&, int m)        -- element offset of activation row m
@@ -512,9 +512,19 @@ __device__ __forceinline__ void stream_items(P& p, Seq& seq, uint8_t* __restrict
 
   const int n_first = p.first_groups();
   const int wg = blockIdx.x, n_wg = gridDim.x;
-  // phase A: the next valid extra-group item at or after `it` in this workgroup's stride
+  // phase A: the next valid extra-group item at or after `it` in this workgroup's stride.
+  // Most candidates are invalid (only experts with more than 16 rows have extra groups),
+  // and each check reads the active list and then the expert's count, so the candidates
+  // are checked 64 at a time, one per lane: a scan costs two memory round trips per 64
+  // candidates instead of two per candidate, and the first weight loads, which wait for
+  // the scan, go out that much sooner.
   auto next_extra = [&](int it) {
-    while (it < p.n_items && !p.valid(it)) it += n_wg;
+    while (it < p.n_items) {
+      const int c = it + lane * n_wg;
+      const uint64_t ok = __ballot(c < p.n_items && p.valid_lane(c));
+      if (ok) return it + (int)__builtin_ctzll(ok) * n_wg;
+      it += 64 * n_wg;
+    }
     return it;
   };
   // The next item after `c` (false past the end).  Only the chunk loader, which reaches
