@@ -2,6 +2,7 @@
 """Benchmark of the MXFP4 weight-streaming MoE layer on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload moe_t32_zipf] [--layers L]
+    python bench.py --workload dense_t1|dense_t4 [--act8]      (the dense mx_linear)
 
 A step is one MoE layer forward (route + sort, gate_up + SwiGLU, down + combine) over one
 batch of T tokens.  Steps cycle over L distinct layers (own weights, own activations and
@@ -18,6 +19,11 @@ after the timed region, issued as the three stage calls with a HIP event between
 the stream the kernels run on.  roofline.traffic is the kernel's HBM bytes per launch as
 measured by the committed counter summary under profiles/, and null when the workload
 differs or the kernel's sources changed since the counters were taken.
+
+Dense workloads (dense_t1, dense_t4): a step is one mx_linear call.  The calls cycle over
+enough copies of the weights (own addresses) that their total exceeds the last-level cache
+by far; one HIP graph holds one call per copy.  The per-call time of the roofline entry
+comes from HIP events around each graph replay of the timed region.
 """
 from __future__ import annotations
 
@@ -32,6 +38,9 @@ import time
 import numpy as np
 
 METRIC = "µs per MXFP4 MoE layer and effective weight GB/s (% of 8 TB/s) at T=1..128"
+DENSE_METRIC = "µs per dense MXFP4 linear call (mx_linear) and effective weight GB/s (% of 8 TB/s)"
+# the dense calls cycle over weight copies totalling at least this many bytes
+DENSE_CYCLE_BYTES = 1 << 30
 HBM_PEAK_GBPS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 # sources (and build flags) the gate_up kernel is compiled from; the counter summary records
@@ -124,6 +133,8 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload in synthetic.LINEAR_CONFIGS:
+        return dense_main(args, synthetic.LINEAR_CONFIGS[args.workload], torch, mx, dev)
     cfg = workload_config(args.workload)
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
     ns = cfg.n_shared
@@ -336,6 +347,108 @@ def main():
         "stages_us": {n: round(float(np.mean(v)) * 1e3, 2) for n, v in stage_ms.items()},
         "staged_us_per_layer": round(staged_us_per_layer, 2),
         "roofline": roofline,
+        "cpu_baseline": cpu,
+        "env": {"GPU_MAX_HW_QUEUES": os.environ.get("GPU_MAX_HW_QUEUES"), "torch": torch.__version__,
+                "hip": getattr(torch.version, "hip", None)},
+    }
+    print(json.dumps(out), flush=True)
+
+
+def dense_main(args, cfg, torch, mx, dev):
+    """The dense layer: y[T,N] = bf16(x[T,K] @ W[N,K]^T) with MXFP4 W, one call per step."""
+    import synthetic
+
+    def log(*a):
+        print(*a, file=sys.stderr, flush=True)
+
+    T, K, N = cfg.T, cfg.K, cfg.N
+    x_bits, w, s = synthetic.linear_inputs(cfg)
+    w_bytes = w.nbytes + s.nbytes
+    copies = max(8, -(-DENSE_CYCLE_BYTES // w_bytes))
+    log(f"[bench] workload {cfg.name}: T={T} K={K} N={N}, {copies} weight copies of {w_bytes} B")
+    x = torch.from_numpy(x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    w0, s0 = torch.from_numpy(w).to(dev), torch.from_numpy(s).to(dev)
+    ws = [(w0.clone(), s0.clone()) for _ in range(copies)]
+    ys = [torch.empty((T, N), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
+    del w0, s0
+
+    def call(i):
+        mx.mx_linear(x, ws[i][0], ws[i][1], out=ys[i], act8=args.act8)
+
+    for i in range(copies):
+        call(i)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(copies):
+                call(i)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    for _ in range(max(1, -(-args.warmup // copies))):
+        graph.replay()
+    reps = max(1, -(-args.steps // copies))
+    nsteps = reps * copies
+    # HIP events on the replay stream bracket each replay of the graph: a call is shorter than
+    # its host-side submission, so eager event pairs would time the host, not the kernel
+    stream = torch.cuda.current_stream(dev)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for r in range(reps):
+        graph.replay()
+        evs[r + 1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    us_per_call = (t1 - t0) * 1e6 / nsteps
+    log(f"[bench] timed {nsteps} calls: {us_per_call:.2f} us/call")
+    call_ms = [evs[r].elapsed_time(evs[r + 1]) / copies for r in range(reps)]
+    call_bytes = w_bytes + T * K * 2 + T * N * 2  # weights, x, y
+    achieved = call_bytes / (float(np.mean(call_ms)) * 1e-3) / 1e9
+    eff_gbps = call_bytes / (us_per_call * 1e-6) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = oracle.default_threads()
+        fn = oracle.mx_linear_a8 if args.act8 else oracle.mx_linear
+        reps_cpu = 3
+        c0 = time.perf_counter()
+        for _ in range(reps_cpu):
+            fn(x_bits, w, s, T, K, N, nthreads=threads)
+        c1 = time.perf_counter()
+        cpu = {"value": round((c1 - c0) / reps_cpu * 1e6, 1), "unit": "us/call", "cores": threads, "kind": "oracle",
+               "sample": f"the whole call, {reps_cpu} repetitions averaged; CPU: {cpu_model()}",
+               "seconds": round(c1 - c0, 2)}
+
+    out = {
+        "metric": DENSE_METRIC,
+        "value": round(us_per_call, 3),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": nsteps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_per_call * 1e-3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8 (E4M3) x fp4 (E2M1), fp32 accumulate" if args.act8 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": T, "K": K, "N": N, "weights": "MXFP4 (E2M1 codes, E8M0 scale per 32)",
+                   "activations": "MXFP8, quantized in the kernel" if args.act8 else "bf16", "accumulate": "fp32",
+                   "weight_copies_cycled": copies, "timing": "HIP graph replay"},
+        "effective_GBps": round(eff_gbps, 1),
+        "pct_of_8TBps": round(100 * eff_gbps / HBM_PEAK_GBPS, 2),
+        "algorithmic_bytes_per_call": call_bytes,
+        "roofline": {"kernel": "mx_linear_kernel", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "avg_launch_us": round(float(np.mean(call_ms)) * 1e3, 3), "launches": nsteps,
+                     "timing": "HIP events on the replay stream around each graph replay of the timed region, "
+                               "per call (includes the graph's gaps between kernels)",
+                     "bytes_per_launch": call_bytes},
         "cpu_baseline": cpu,
         "env": {"GPU_MAX_HW_QUEUES": os.environ.get("GPU_MAX_HW_QUEUES"), "torch": torch.__version__,
                 "hip": getattr(torch.version, "hip", None)},
