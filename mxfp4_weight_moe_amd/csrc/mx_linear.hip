@@ -16,12 +16,15 @@
 
 namespace mx {
 
-template <int W, int MT, bool SBYTE, bool A8>
+// DEEP: a 4-deep load pipeline for one m-tile (every segment of a wave in flight when the
+// K split gives it at most 4), where the kernel's registers allow it; else 3 (one m-tile) or
+// 2 (two m-tiles).
+template <int W, int MT, bool SBYTE, bool A8, bool DEEP = false>
 __device__ __forceinline__ void dense_pass(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
                                            const uint8_t* __restrict__ s, uint16_t* __restrict__ y, int T, int K,
                                            int N, int n0, int mp, uint8_t* slab, f32x4* red, int wave, int lane) {
   constexpr int NS = 1;
-  constexpr int D = (MT == 1) ? 3 : 2;
+  constexpr int D = (MT == 1) ? (DEEP ? 4 : 3) : 2;
   StreamLanes<NS, MT> L;
   lanes_init_lds(L, lane);
   const int kb = K >> 1, ks = K >> 5;
@@ -76,7 +79,9 @@ __device__ __forceinline__ void dense_pass(const uint16_t* __restrict__ x, const
   }
 }
 
-template <int W, bool SBYTE, bool A8>
+// ONE_TILE: T <= 16, a single pass of one m-tile; the kernel then holds only that pass, whose
+// registers leave room (with bf16 activations) for the 4-deep pipeline.
+template <int W, bool SBYTE, bool A8, bool ONE_TILE>
 __global__ void __launch_bounds__(W * 64) mx_linear_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
                                                            const uint8_t* __restrict__ s, uint16_t* __restrict__ y,
                                                            int T, int K, int N) {
@@ -84,11 +89,15 @@ __global__ void __launch_bounds__(W * 64) mx_linear_kernel(const uint16_t* __res
   __shared__ f32x4 red[(W > 1) ? W * 2 * 64 : 1];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n0 = blockIdx.x * SUB_ROWS;
-  for (int mp = 0; mp < T; mp += 32) {
-    if (T - mp > 16)
-      dense_pass<W, 2, SBYTE, A8>(x, w, s, y, T, K, N, n0, mp, slabs[wave], red, wave, lane);
-    else
-      dense_pass<W, 1, SBYTE, A8>(x, w, s, y, T, K, N, n0, mp, slabs[wave], red, wave, lane);
+  if constexpr (ONE_TILE) {
+    dense_pass<W, 1, SBYTE, A8, !A8>(x, w, s, y, T, K, N, n0, 0, slabs[wave], red, wave, lane);
+  } else {
+    for (int mp = 0; mp < T; mp += 32) {
+      if (T - mp > 16)
+        dense_pass<W, 2, SBYTE, A8>(x, w, s, y, T, K, N, n0, mp, slabs[wave], red, wave, lane);
+      else
+        dense_pass<W, 1, SBYTE, A8>(x, w, s, y, T, K, N, n0, mp, slabs[wave], red, wave, lane);
+    }
   }
 }
 
@@ -104,7 +113,15 @@ static int launch_dense(const uint16_t* x, const uint8_t* w, const uint8_t* s, u
   while (W < WMAX && 2 * W <= nseg && items * W < 2048) W *= 2;
   const bool sbyte = (K % SEG_K) != 0;
   dim3 grid(items), block(W * 64);
-#define MXL(WW, SB) hipLaunchKernelGGL((mx_linear_kernel<WW, SB, A8>), grid, block, 0, stream, x, w, s, y, T, K, N)
+#define MXL1(WW, SB, OT) \
+  hipLaunchKernelGGL((mx_linear_kernel<WW, SB, A8, OT>), grid, block, 0, stream, x, w, s, y, T, K, N)
+#define MXL(WW, SB) \
+  do {                          \
+    if (T <= 16)                \
+      MXL1(WW, SB, true);       \
+    else                        \
+      MXL1(WW, SB, false);      \
+  } while (0)
   if (sbyte) {
     switch (W) {
       case 1: MXL(1, true); break;
@@ -125,6 +142,7 @@ static int launch_dense(const uint16_t* x, const uint8_t* w, const uint8_t* s, u
     }
   }
 #undef MXL
+#undef MXL1
   return hip_status(hipGetLastError());
 }
 
