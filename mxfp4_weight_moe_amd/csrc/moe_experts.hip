@@ -30,7 +30,9 @@ using DownPlain = DownPolicy<NS, GlobalSort, DN_XCHUNK, false, SR, A8, FUSE>;
 
 // ------------------------------------------------------------------ kernels
 
-template <int NS, bool A8>
+// SPS: segments per weight step (GU_SPS, or GU_SPS_DEEP for launches with fewer items than
+// resident workgroup slots)
+template <int NS, int SPS, bool A8>
 __global__ void __launch_bounds__(WG_WAVES * 64) moe_gate_up_kernel(const uint16_t* __restrict__ x,
                                                                     const uint8_t* __restrict__ wgu,
                                                                     const uint8_t* __restrict__ sgu, SortView sv,
@@ -48,6 +50,7 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_gate_up_kernel(const uint16
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   P p;
   p.xrowsegs = XGeom<P::XCHUNK>::ROWSEGS;
+  p.calign = SPS;
   p.m.sv = sv;
   p.nseg = H / SEG_K;
   p.nquad = I / (P::TILE * WG_WAVES);
@@ -64,7 +67,7 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_gate_up_kernel(const uint16
   p.kinv = ((1u << 24) + (uint32_t)k - 1u) / (uint32_t)k;
   p.e_codes = (size_t)2 * I * (H / 2);
   p.e_scales = (size_t)2 * I * (H / 32);
-  stream_items<P, GU_SPS>(p, seq, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
+  stream_items<P, SPS>(p, seq, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
   seq.finish();
 }
 
@@ -221,19 +224,33 @@ static bool use_half_tiles(int64_t items_full, int& grid) {
   return true;
 }
 
+template <bool A8, int SPS>
+static int launch_gate_up_sps(const uint16_t* x, const uint8_t* wgu, const uint8_t* sgu, const SortView& sv,
+                              uint16_t* h, int32_t* ctl, int T, int H, int I, int E, int k, bool half, int grid,
+                              hipStream_t stream) {
+  if (half)
+    hipLaunchKernelGGL((moe_gate_up_kernel<1, SPS, A8>), dim3(grid), dim3(WG_WAVES * 64), 0, stream, x, wgu, sgu, sv,
+                       h, H, I, k, ctl + CTL_CLAIM_GU);
+  else
+    hipLaunchKernelGGL((moe_gate_up_kernel<2, SPS, A8>), dim3(grid), dim3(WG_WAVES * 64), 0, stream, x, wgu, sgu, sv,
+                       h, H, I, k, ctl + CTL_CLAIM_GU);
+  return hip_status(hipGetLastError());
+}
+
 template <bool A8>
 static int launch_gate_up_run(const uint16_t* x, const uint8_t* wgu, const uint8_t* sgu, const SortView& sv,
                               uint16_t* h, int32_t* ctl, int T, int H, int I, int E, int k, hipStream_t stream) {
   const int gmax = row_groups(T);
   const int64_t items_full = (int64_t)gmax * max_active(T, E, k) * (I / (GateUpPlain<2>::TILE * WG_WAVES));
   int grid = 0;
-  if (use_half_tiles<moe_gate_up_kernel<2, A8>, moe_gate_up_kernel<1, A8>>(items_full, grid))
-    hipLaunchKernelGGL((moe_gate_up_kernel<1, A8>), dim3(grid), dim3(WG_WAVES * 64), 0, stream, x, wgu, sgu, sv, h, H,
-                       I, k, ctl + CTL_CLAIM_GU);
-  else
-    hipLaunchKernelGGL((moe_gate_up_kernel<2, A8>), dim3(grid), dim3(WG_WAVES * 64), 0, stream, x, wgu, sgu, sv, h, H,
-                       I, k, ctl + CTL_CLAIM_GU);
-  return hip_status(hipGetLastError());
+  const bool half = use_half_tiles<moe_gate_up_kernel<2, GU_SPS, A8>, moe_gate_up_kernel<1, GU_SPS, A8>>(items_full, grid);
+  static const int occ = resident_wgs_per_cu(moe_gate_up_kernel<2, GU_SPS, A8>, WG_WAVES * 64);
+  const int64_t items = half ? 2 * items_full : items_full;
+  if constexpr (!A8) {  // the MXFP8 kernel's registers leave no room for the deeper ring
+    if (half && H % (SEG_K * GU_SPS_DEEP) == 0 && items < (int64_t)device_cu_count() * occ)
+      return launch_gate_up_sps<A8, GU_SPS_DEEP>(x, wgu, sgu, sv, h, ctl, T, H, I, E, k, half, grid, stream);
+  }
+  return launch_gate_up_sps<A8, GU_SPS>(x, wgu, sgu, sv, h, ctl, T, H, I, E, k, half, grid, stream);
 }
 
 int launch_gate_up(const uint16_t* x, const uint8_t* wgu, const uint8_t* sgu, const SortView& sv, uint16_t* h,
