@@ -193,8 +193,9 @@ MX_API size_t moe_mxfp4_workspace_size(int64_t T, int64_t H, int64_t I, int64_t 
  *              h_n = bf16_rne( silu(g_n) * u_n ),  silu(g) = g / (1 + exp(-g))    n < I
  *   down:    d_n = sum_i h_i Wd[e][n,i]                                          (fp32)
  *   combine: y[t,n] = bf16_rne( sum_j gates[t,j] * d_{t,j,n} )                    (fp32)
- * Each routed expert's weights are read from HBM once per call, whatever the number of
- * tokens routed to it; experts no token routes to are not read.
+ * Each routed expert's weights are read from HBM once per 16 tokens routed to it (once per
+ * call for T <= 16, where no expert has more than 16 rows); experts no token routes to are
+ * not read.
  *   x             bf16 [T, H]
  *   router_logits fp32 [T, E] (finite)
  *   w_gate_up     uint8 [E, 2I, H/2]  (rows [0, I) gate, rows [I, 2I) up)

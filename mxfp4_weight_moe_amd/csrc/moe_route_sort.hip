@@ -3,8 +3,8 @@
 // Routing: one wavefront per token (moe_route.hpp).
 //
 // Sort: each expert receives a few token rows ("Zyphra Inference Wave 2", Kernel Results);
-// grouping the routed slots by expert lets each expert's weights be read once for all of
-// its rows.  The order is fixed (experts ascending, slot ascending), so the result is
+// grouping the routed slots by expert lets each expert's weights be read once for up to 16
+// of its rows (one MFMA row tile).  The order is fixed (experts ascending, slot ascending), so the result is
 // bit-exact and independent of thread timing.
 //
 // For up to 16 tokens the layer forward runs both in one single-workgroup launch
