@@ -299,6 +299,145 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_fused_kernel(
   }
 }
 
+// ------------------------------------------------------------------ gate_up with its own routing
+
+// The layer forward's gate_up launch for small T.  Every workgroup routes all T tokens and
+// sorts the slots into LDS itself (fused_route_sort, as the persistent layer does), so no
+// route + sort launch precedes it and the item metadata comes from LDS instead of a chain of
+// dependent loads.  Workgroup 0 also writes what the down launch needs to the workspace: the
+// counts and offsets of all E experts, the sorted slots, the gates, the active list and
+// {active experts, largest count}.  Its active list is in ascending expert order, not row
+// class order; the down launch accepts any order, since its items and outputs are indexed
+// by expert and sorted position.  h is identical to the default launches': the same rows at
+// the same sorted positions.  Nothing waits on another workgroup.
+struct SortOut {
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_slots;
+  int32_t* active;
+  int32_t* num_active;
+};
+
+template <int PER, int NS, int SPS>
+__global__ void __launch_bounds__(WG_WAVES * 64) moe_gate_up_routed_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ logits, const uint8_t* __restrict__ wgu,
+    const uint8_t* __restrict__ sgu, uint16_t* __restrict__ h, SortOut out, float* __restrict__ gates, int T, int H,
+    int I, int E, int k) {
+  __shared__ __attribute__((aligned(16))) uint8_t xbufs[2 * GU_XCHUNK];
+  __shared__ __attribute__((aligned(16))) uint8_t slabs[WG_WAVES][SLAB_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t sslabs[WG_WAVES][ScaleRun4::slab_bytes<NS>()];
+  __shared__ uint32_t xctr[2];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  if (tid < 2) xctr[tid] = 0u;
+  fused_route_sort<PER>(logits, T, E, k, xbufs);
+  const LdsSort meta;
+  const int na = meta.num_active();
+  if (blockIdx.x == 0) {
+    // the token masks and expert offsets are still in the routing scratch (xbufs)
+    const uint32_t* bits = reinterpret_cast<const uint32_t*>(xbufs);
+    const int32_t* eoff = reinterpret_cast<const int32_t*>(xbufs + 4096);
+    for (int e = tid; e < E; e += WG_WAVES * 64) {
+      out.counts[e] = __popc(bits[e]);
+      out.offsets[e] = eoff[e];
+    }
+    for (int i = tid; i < T * k; i += WG_WAVES * 64) {
+      out.sorted_slots[i] = fsort.slots[i];
+      gates[i] = fsort.gates[i];
+    }
+    for (int a = tid; a < na; a += WG_WAVES * 64) out.active[a] = fsort.act[a];
+    if (wave == 0) {
+      int m = 0;
+      for (int a = lane; a < na; a += 64) m = max(m, fsort.cnt[a]);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) m = max(m, __shfl_xor(m, o));
+      if (lane == 0) {
+        out.offsets[E] = T * k;
+        out.num_active[0] = na;
+        out.num_active[1] = m;
+      }
+    }
+  }
+  __syncthreads();  // the routing scratch has been read; the stream reuses xbufs
+  using PG = GateUpPolicy<NS, LdsSort, GU_XCHUNK, false>;
+  PG p;
+  p.xrowsegs = XGeom<GU_XCHUNK>::ROWSEGS;
+  p.calign = SPS;
+  p.nseg = H / SEG_K;
+  p.nquad = I / (PG::TILE * WG_WAVES);
+  p.na = na;
+  p.n_items = na * p.nquad;  // T <= 16: one row group per expert
+  p.xact = x;
+  p.wgu = wgu;
+  p.sgu = sgu;
+  p.h = h;
+  p.H = H;
+  p.I = I;
+  p.k = k;
+  p.kinv = ((1u << 24) + (uint32_t)k - 1u) / (uint32_t)k;
+  p.e_codes = (size_t)2 * I * (H / 2);
+  p.e_scales = (size_t)2 * I * (H / 32);
+  StaticUnits units;
+  stream_items<PG, SPS>(p, units, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
+}
+
+template <class K>
+static int routed_occupancy(K kernel) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, WG_WAVES * 64, 0) != hipSuccess || n < 1) n = 1;
+  return n;
+}
+
+// Tiles and grid as the gate_up launch chooses them: half-width tiles when full-width items
+// would leave resident slots idle and twice the items still fit in one round, and then
+// 4-segment steps while the items are fewer than the slots.
+template <int PER>
+static int launch_routed_per(const uint16_t* x, const float* logits, const uint8_t* wgu, const uint8_t* sgu,
+                             uint16_t* h, const SortOut& out, float* gates, int T, int H, int I, int E, int k,
+                             hipStream_t stream) {
+  static const int occ2 = routed_occupancy(moe_gate_up_routed_kernel<PER, 2, GU_SPS>);
+  static const int occ1 = routed_occupancy(moe_gate_up_routed_kernel<PER, 1, GU_SPS>);
+  const int64_t na_max = (int64_t)T * k < E ? (int64_t)T * k : E;
+  const int64_t items_full = na_max * (I / (SUB_ROWS * WG_WAVES));
+  const int64_t cus = device_cu_count();
+  const dim3 block(WG_WAVES * 64);
+  if (2 * items_full > cus * occ1) {
+    const dim3 grid((unsigned)(items_full < cus * occ2 ? items_full : cus * occ2));
+    hipLaunchKernelGGL((moe_gate_up_routed_kernel<PER, 2, GU_SPS>), grid, block, 0, stream, x, logits, wgu, sgu, h,
+                       out, gates, T, H, I, E, k);
+  } else {
+    const dim3 grid((unsigned)(2 * items_full));
+    if (H % (SEG_K * GU_SPS_DEEP) == 0 && 2 * items_full < cus * occ1)
+      hipLaunchKernelGGL((moe_gate_up_routed_kernel<PER, 1, GU_SPS_DEEP>), grid, block, 0, stream, x, logits, wgu,
+                         sgu, h, out, gates, T, H, I, E, k);
+    else
+      hipLaunchKernelGGL((moe_gate_up_routed_kernel<PER, 1, GU_SPS>), grid, block, 0, stream, x, logits, wgu, sgu, h,
+                         out, gates, T, H, I, E, k);
+  }
+  return hip_status(hipGetLastError());
+}
+
+// Measured against the route + sort launch followed by gate_up (graph replay, 4 layers):
+// T = 1 50.0 -> 46.7 us per layer, T = 2 81.4 -> 77.9, T = 4 132.0 -> 127.8, T = 8 226.8 ->
+// 223.1, T = 16 392.4 -> 391.2.
+bool gate_up_routed_fits(int T, int E, int k, int H, int I) {
+  (void)E;
+  return T <= MX_FUSED_MAX_TOKENS && T * k <= FUSED_MAX_SLOTS && H % (SEG_K * GU_SPS) == 0 &&
+         H % (SEG_K * SRUN) == 0 && I % (SUB_ROWS * WG_WAVES) == 0;
+}
+
+int launch_gate_up_routed(const uint16_t* x, const float* logits, const uint8_t* wgu, const uint8_t* sgu, uint16_t* h,
+                          int32_t* counts, int32_t* offsets, int32_t* sorted_slots, int32_t* active,
+                          int32_t* num_active, float* gates, int T, int H, int I, int E, int k, hipStream_t stream) {
+  if (!gate_up_routed_fits(T, E, k, H, I)) return MX_ERR_SHAPE;
+  const SortOut out{counts, offsets, sorted_slots, active, num_active};
+  switch (route_per(E)) {
+    case 4: return launch_routed_per<4>(x, logits, wgu, sgu, h, out, gates, T, H, I, E, k, stream);
+    case 8: return launch_routed_per<8>(x, logits, wgu, sgu, h, out, gates, T, H, I, E, k, stream);
+    default: return launch_routed_per<16>(x, logits, wgu, sgu, h, out, gates, T, H, I, E, k, stream);
+  }
+}
+
 // ------------------------------------------------------------------ launcher
 
 template <int PER, int NSG, int NSD>

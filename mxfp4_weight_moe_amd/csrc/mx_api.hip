@@ -235,12 +235,19 @@ static int moe_forward_impl(const uint16_t* x, const float* router_logits, int64
   if (workspace_bytes < ws.bytes) return MX_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int t = (int)T, h = (int)H, i = (int)I, e = (int)E, k = (int)top_k, n = (int)ns;
-  if ((st = launch_route_sort(router_logits, t, e, k, n, ws.ids, ws.gates, ws.counts, ws.offsets, ws.sorted_slots,
-                              ws.active, ws.num_active, s)) != MX_OK)
-    return st;
   const SortView sv{ws.counts, ws.offsets, ws.sorted_slots, ws.active, ws.num_active};
-  if ((st = launch_gate_up(x, w_gate_up, s_gate_up, sv, ws.h, ws.ctl, t, h, i, e + n, k + n, act8, s)) != MX_OK)
-    return st;
+  if (n == 0 && !act8 && gate_up_routed_fits(t, e, k, h, i)) {
+    // small T: gate_up routes and sorts in every workgroup and writes the sort for down
+    if ((st = launch_gate_up_routed(x, router_logits, w_gate_up, s_gate_up, ws.h, ws.counts, ws.offsets,
+                                    ws.sorted_slots, ws.active, ws.num_active, ws.gates, t, h, i, e, k, s)) != MX_OK)
+      return st;
+  } else {
+    if ((st = launch_route_sort(router_logits, t, e, k, n, ws.ids, ws.gates, ws.counts, ws.offsets, ws.sorted_slots,
+                                ws.active, ws.num_active, s)) != MX_OK)
+      return st;
+    if ((st = launch_gate_up(x, w_gate_up, s_gate_up, sv, ws.h, ws.ctl, t, h, i, e + n, k + n, act8, s)) != MX_OK)
+      return st;
+  }
   bool combined = false;
   if ((st = launch_down(ws.h, ws.gates, w_down, s_down, sv, ws.dpart, y, &combined, ws.ctl, t, h, i, e + n, k + n,
                         act8, s)) != MX_OK)
