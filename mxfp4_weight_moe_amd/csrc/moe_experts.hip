@@ -173,6 +173,8 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_down_kernel(const uint16_t*
 }
 
 // One thread per (token, 4 consecutive outputs): fp32 sum of the gate-weighted slots, j ascending.
+// The slots are loaded 8 at a time, all in flight together, and then summed in order: a loop
+// of one load per slot waited for each load in turn (k round trips per thread).
 __global__ void __launch_bounds__(256) moe_combine_kernel(const float* __restrict__ dpart, const float* __restrict__ gates,
                                                           uint16_t* __restrict__ y, int T, int H, int k) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -180,10 +182,18 @@ __global__ void __launch_bounds__(256) moe_combine_kernel(const float* __restric
   if (i >= (int64_t)T * per_t) return;
   const int64_t t = i / per_t, n = (i - t * per_t) * 4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const float g = gates[t * k + j];
-    const f32x4 d = *reinterpret_cast<const f32x4*>(dpart + (size_t)(t * k + j) * H + n);
-    acc += f32x4{g * d[0], g * d[1], g * d[2], g * d[3]};
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    f32x4 d[8];
+    float g[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int j = min(j0 + jj, k - 1);  // past k: the last slot again, not summed
+      d[jj] = *reinterpret_cast<const f32x4*>(dpart + (size_t)(t * k + j) * H + n);
+      g[jj] = gates[t * k + j];
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+      if (j0 + jj < k) acc += f32x4{g[jj] * d[jj][0], g[jj] * d[jj][1], g[jj] * d[jj][2], g[jj] * d[jj][3]};
   }
   const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
   const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
