@@ -30,8 +30,8 @@ using DownPlain = DownPolicy<NS, GlobalSort, DN_XCHUNK, false, SR, A8, FUSE>;
 
 // ------------------------------------------------------------------ kernels
 
-// SPS: segments per weight step (GU_SPS, or GU_SPS_DEEP for launches with fewer items than
-// resident workgroup slots)
+// SPS: segments per weight step (GU_SPS, or GU_SPS_DEEP for half-width launches with fewer
+// items than resident workgroup slots)
 template <int NS, int SPS, bool A8>
 __global__ void __launch_bounds__(WG_WAVES * 64) moe_gate_up_kernel(const uint16_t* __restrict__ x,
                                                                     const uint8_t* __restrict__ wgu,
@@ -173,8 +173,8 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_down_kernel(const uint16_t*
 }
 
 // One thread per (token, 4 consecutive outputs): fp32 sum of the gate-weighted slots, j ascending.
-// The slots are loaded 8 at a time, all in flight together, and then summed in order: a loop
-// of one load per slot waited for each load in turn (k round trips per thread).
+// The slots are loaded 8 at a time, all in flight together, and then summed in order, so a
+// thread's loads do not wait for one another (one round trip per 8 slots, not per slot).
 __global__ void __launch_bounds__(256) moe_combine_kernel(const float* __restrict__ dpart, const float* __restrict__ gates,
                                                           uint16_t* __restrict__ y, int T, int H, int k) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -253,7 +253,8 @@ static int launch_gate_up_run(const uint16_t* x, const uint8_t* wgu, const uint8
   const int gmax = row_groups(T);
   const int64_t items_full = (int64_t)gmax * max_active(T, E, k) * (I / (GateUpPlain<2>::TILE * WG_WAVES));
   int grid = 0;
-  const bool half = use_half_tiles<moe_gate_up_kernel<2, GU_SPS, A8>, moe_gate_up_kernel<1, GU_SPS, A8>>(items_full, grid);
+  const bool half =
+      use_half_tiles<moe_gate_up_kernel<2, GU_SPS, A8>, moe_gate_up_kernel<1, GU_SPS, A8>>(items_full, grid);
   static const int occ = resident_wgs_per_cu(moe_gate_up_kernel<2, GU_SPS, A8>, WG_WAVES * 64);
   const int64_t items = half ? 2 * items_full : items_full;
   if constexpr (!A8) {  // the MXFP8 kernel's registers leave no room for the deeper ring

@@ -160,11 +160,7 @@ struct ExpertItems {
   int calign = CHUNK_ALIGN;  // chunk lengths are multiples of this (the launch's weight step)
 
   __device__ __forceinline__ int first_groups() const { return na * nquad; }
-  __device__ __forceinline__ bool valid(int it) const {
-    const ItemIndex ix = item_decode(it, nquad, na);
-    return ix.g * 16 < m.count(ix.a);
-  }
-  // valid() for a per-lane item
+  // whether item `it` (per lane) exists: its row group starts below the expert's count
   __device__ __forceinline__ bool valid_lane(int it) const {
     const ItemIndex ix = item_decode(it, nquad, na);
     return ix.g * 16 < m.count_lane(ix.a);
