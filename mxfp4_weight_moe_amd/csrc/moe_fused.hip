@@ -1,5 +1,7 @@
 // The whole MoE layer in one launch for small T: routing, sort, gate_up + SwiGLU, down and
-// the gate-weighted combine.
+// the gate-weighted combine.  Also, at the end of this file, the layer forward's gate_up
+// launch for T <= 16, which does the routing and sort of this launch in each workgroup and
+// leaves down and the combine to their own launches.
 //
 // At small T a layer streams only tens of microseconds of weights, and each kernel
 // boundary (the GPU draining one kernel and starting the next) costs microseconds.  The
@@ -308,8 +310,9 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_fused_kernel(
 // counts and offsets of all E experts, the sorted slots, the gates, the active list and
 // {active experts, largest count}.  Its active list is in ascending expert order, not row
 // class order; the down launch accepts any order, since its items and outputs are indexed
-// by expert and sorted position.  h is identical to the default launches': the same rows at
-// the same sorted positions.  Nothing waits on another workgroup.
+// by expert and sorted position.  h is identical to that of the stage entry points
+// (moe_route_sort, then moe_gate_up_swiglu): the same rows at the same sorted positions.
+// Nothing waits on another workgroup.
 struct SortOut {
   int32_t* counts;
   int32_t* offsets;
