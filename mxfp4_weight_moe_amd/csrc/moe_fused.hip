@@ -321,7 +321,7 @@ struct SortOut {
   int32_t* num_active;
 };
 
-template <int PER, int NS, int SPS>
+template <int PER, int NS, int SPS, bool A8>
 __global__ void __launch_bounds__(WG_WAVES * 64) moe_gate_up_routed_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ logits, const uint8_t* __restrict__ wgu,
     const uint8_t* __restrict__ sgu, uint16_t* __restrict__ h, SortOut out, float* __restrict__ gates, int T, int H,
@@ -362,7 +362,7 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_gate_up_routed_kernel(
     }
   }
   __syncthreads();  // the routing scratch has been read; the stream reuses xbufs
-  using PG = GateUpPolicy<NS, LdsSort, GU_XCHUNK, false>;
+  using PG = GateUpPolicy<NS, LdsSort, GU_XCHUNK, false, A8>;
   PG p;
   p.xrowsegs = XGeom<GU_XCHUNK>::ROWSEGS;
   p.calign = SPS;
@@ -394,29 +394,33 @@ static int routed_occupancy(K kernel) {
 // Tiles and grid as the gate_up launch chooses them: half-width tiles when full-width items
 // would leave resident slots idle and twice the items still fit in one round, and then
 // 4-segment steps while the items are fewer than the slots.
-template <int PER>
+// A8: MXFP8 activations (the deeper ring's registers are not available there)
+template <int PER, bool A8>
 static int launch_routed_per(const uint16_t* x, const float* logits, const uint8_t* wgu, const uint8_t* sgu,
                              uint16_t* h, const SortOut& out, float* gates, int T, int H, int I, int E, int k,
                              hipStream_t stream) {
-  static const int occ2 = routed_occupancy(moe_gate_up_routed_kernel<PER, 2, GU_SPS>);
-  static const int occ1 = routed_occupancy(moe_gate_up_routed_kernel<PER, 1, GU_SPS>);
+  static const int occ2 = routed_occupancy(moe_gate_up_routed_kernel<PER, 2, GU_SPS, A8>);
+  static const int occ1 = routed_occupancy(moe_gate_up_routed_kernel<PER, 1, GU_SPS, A8>);
   const int64_t na_max = (int64_t)T * k < E ? (int64_t)T * k : E;
   const int64_t items_full = na_max * (I / (SUB_ROWS * WG_WAVES));
   const int64_t cus = device_cu_count();
   const dim3 block(WG_WAVES * 64);
   if (2 * items_full > cus * occ1) {
     const dim3 grid((unsigned)(items_full < cus * occ2 ? items_full : cus * occ2));
-    hipLaunchKernelGGL((moe_gate_up_routed_kernel<PER, 2, GU_SPS>), grid, block, 0, stream, x, logits, wgu, sgu, h,
-                       out, gates, T, H, I, E, k);
-  } else {
-    const dim3 grid((unsigned)(2 * items_full));
-    if (H % (SEG_K * GU_SPS_DEEP) == 0 && 2 * items_full < cus * occ1)
-      hipLaunchKernelGGL((moe_gate_up_routed_kernel<PER, 1, GU_SPS_DEEP>), grid, block, 0, stream, x, logits, wgu,
-                         sgu, h, out, gates, T, H, I, E, k);
-    else
-      hipLaunchKernelGGL((moe_gate_up_routed_kernel<PER, 1, GU_SPS>), grid, block, 0, stream, x, logits, wgu, sgu, h,
-                         out, gates, T, H, I, E, k);
+    hipLaunchKernelGGL((moe_gate_up_routed_kernel<PER, 2, GU_SPS, A8>), grid, block, 0, stream, x, logits, wgu, sgu,
+                       h, out, gates, T, H, I, E, k);
+    return hip_status(hipGetLastError());
   }
+  const dim3 grid((unsigned)(2 * items_full));
+  if constexpr (!A8) {
+    if (H % (SEG_K * GU_SPS_DEEP) == 0 && 2 * items_full < cus * occ1) {
+      hipLaunchKernelGGL((moe_gate_up_routed_kernel<PER, 1, GU_SPS_DEEP, A8>), grid, block, 0, stream, x, logits, wgu,
+                         sgu, h, out, gates, T, H, I, E, k);
+      return hip_status(hipGetLastError());
+    }
+  }
+  hipLaunchKernelGGL((moe_gate_up_routed_kernel<PER, 1, GU_SPS, A8>), grid, block, 0, stream, x, logits, wgu, sgu, h,
+                     out, gates, T, H, I, E, k);
   return hip_status(hipGetLastError());
 }
 
@@ -431,13 +435,21 @@ bool gate_up_routed_fits(int T, int E, int k, int H, int I) {
 
 int launch_gate_up_routed(const uint16_t* x, const float* logits, const uint8_t* wgu, const uint8_t* sgu, uint16_t* h,
                           int32_t* counts, int32_t* offsets, int32_t* sorted_slots, int32_t* active,
-                          int32_t* num_active, float* gates, int T, int H, int I, int E, int k, hipStream_t stream) {
+                          int32_t* num_active, float* gates, int T, int H, int I, int E, int k, bool act8,
+                          hipStream_t stream) {
   if (!gate_up_routed_fits(T, E, k, H, I)) return MX_ERR_SHAPE;
   const SortOut out{counts, offsets, sorted_slots, active, num_active};
+  if (act8) {
+    switch (route_per(E)) {
+      case 4: return launch_routed_per<4, true>(x, logits, wgu, sgu, h, out, gates, T, H, I, E, k, stream);
+      case 8: return launch_routed_per<8, true>(x, logits, wgu, sgu, h, out, gates, T, H, I, E, k, stream);
+      default: return launch_routed_per<16, true>(x, logits, wgu, sgu, h, out, gates, T, H, I, E, k, stream);
+    }
+  }
   switch (route_per(E)) {
-    case 4: return launch_routed_per<4>(x, logits, wgu, sgu, h, out, gates, T, H, I, E, k, stream);
-    case 8: return launch_routed_per<8>(x, logits, wgu, sgu, h, out, gates, T, H, I, E, k, stream);
-    default: return launch_routed_per<16>(x, logits, wgu, sgu, h, out, gates, T, H, I, E, k, stream);
+    case 4: return launch_routed_per<4, false>(x, logits, wgu, sgu, h, out, gates, T, H, I, E, k, stream);
+    case 8: return launch_routed_per<8, false>(x, logits, wgu, sgu, h, out, gates, T, H, I, E, k, stream);
+    default: return launch_routed_per<16, false>(x, logits, wgu, sgu, h, out, gates, T, H, I, E, k, stream);
   }
 }
 

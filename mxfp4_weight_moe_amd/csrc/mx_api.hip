@@ -236,10 +236,11 @@ static int moe_forward_impl(const uint16_t* x, const float* router_logits, int64
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int t = (int)T, h = (int)H, i = (int)I, e = (int)E, k = (int)top_k, n = (int)ns;
   const SortView sv{ws.counts, ws.offsets, ws.sorted_slots, ws.active, ws.num_active};
-  if (n == 0 && !act8 && gate_up_routed_fits(t, e, k, h, i)) {
+  if (n == 0 && gate_up_routed_fits(t, e, k, h, i)) {
     // small T: gate_up routes and sorts in every workgroup and writes the sort for down
     if ((st = launch_gate_up_routed(x, router_logits, w_gate_up, s_gate_up, ws.h, ws.counts, ws.offsets,
-                                    ws.sorted_slots, ws.active, ws.num_active, ws.gates, t, h, i, e, k, s)) != MX_OK)
+                                    ws.sorted_slots, ws.active, ws.num_active, ws.gates, t, h, i, e, k, act8, s)) !=
+        MX_OK)
       return st;
   } else {
     if ((st = launch_route_sort(router_logits, t, e, k, n, ws.ids, ws.gates, ws.counts, ws.offsets, ws.sorted_slots,

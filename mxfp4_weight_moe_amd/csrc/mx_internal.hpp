@@ -92,11 +92,13 @@ int launch_down(const uint16_t* h, const float* gates, const uint8_t* wd, const 
 int launch_combine(const float* dpart, const float* gates, uint16_t* y, int T, int H, int k, hipStream_t stream);
 // The forward's gate_up for small T with the routing and sort done in every workgroup (no
 // route + sort launch before it); it also writes the sort outputs and gates for the down
-// launch.  gate_up_routed_fits says when it applies (bf16 activations, no shared experts).
+// launch.  gate_up_routed_fits says when it applies (no shared experts); act8: MXFP8
+// activations, as launch_gate_up.
 bool gate_up_routed_fits(int T, int E, int k, int H, int I);
 int launch_gate_up_routed(const uint16_t* x, const float* logits, const uint8_t* wgu, const uint8_t* sgu, uint16_t* h,
                           int32_t* counts, int32_t* offsets, int32_t* sorted_slots, int32_t* active,
-                          int32_t* num_active, float* gates, int T, int H, int I, int E, int k, hipStream_t stream);
+                          int32_t* num_active, float* gates, int T, int H, int I, int E, int k, bool act8,
+                          hipStream_t stream);
 // The whole layer as one persistent launch (small T); fused_layer_fits says when it applies.
 bool fused_layer_fits(int T, int E, int k, int H, int I);
 int launch_moe_fused(const uint16_t* x, const float* logits, const uint8_t* wgu, const uint8_t* sgu, const uint8_t* wd,
