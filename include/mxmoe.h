@@ -143,8 +143,8 @@ MX_API int moe_sort_by_expert(const int32_t* ids, int64_t T, int64_t top_k, int6
 /*
  * moe_route_topk followed by moe_sort_by_expert of its ids: one launch for T <= 16, two
  * beyond.  moe_mxfp4_forward runs it as its first stage beyond 16 tokens (and with shared
- * experts or MXFP8 activations); up to 16 tokens its gate_up launch routes and sorts in
- * every workgroup instead, with the same result.  Arguments, outputs and limits
+ * experts); up to 16 tokens its gate_up launch routes and sorts in every workgroup instead,
+ * with the same result.  Arguments, outputs and limits
  * as for those two calls.
  */
 MX_API int moe_route_sort(const float* logits, int64_t T, int64_t E, int64_t top_k, int32_t* ids, float* gates,
