@@ -21,21 +21,13 @@ __device__ __forceinline__ float route_value(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
-// Router order as one unsigned 64-bit key: the value's key above the complement of the
-// expert id, so a larger value wins and, among equal values, the lower id.  0 (below every
-// valid key) marks an empty or already taken entry.
-__device__ __forceinline__ uint64_t route_key64(float v, int e) {
-  return ((uint64_t)route_key(v) << 32) | (uint64_t)(uint32_t)~e;
-}
-
 // a = max(a, a of the lane that DPP control CTRL selects); lanes of rows outside ROW_MASK
-// receive 0 and keep a.
+// receive 0 and keep a.  (Valid keys are never 0: route_key maps every finite value, -0 and
+// +0 included, above it; 0 marks an empty or already taken entry.)
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ void max64_dpp(uint64_t& a) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)a, CTRL, ROW_MASK, 0xF, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(a >> 32), CTRL, ROW_MASK, 0xF, false);
-  const uint64_t o = ((uint64_t)hi << 32) | lo;
-  if (o > a) a = o;
+__device__ __forceinline__ void max32_dpp(uint32_t& a) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, CTRL, ROW_MASK, 0xF, false);
+  a = o > a ? o : a;
 }
 
 // Sum over each row of 16 lanes (every lane of the row gets it).
@@ -53,16 +45,14 @@ constexpr int DPP_ROW_BCAST31 = 0x143;  // lane 31 to rows 2 and 3
 
 // Maximum over the wavefront, returned uniform: within each row of 16 lanes by four
 // exchanges, then rows 0+1 into row 1 and 2+3 into row 3, then row 1 into row 3.
-__device__ __forceinline__ uint64_t wave_max64(uint64_t a) {
-  max64_dpp<DPP_QUAD_XOR1, 0xF>(a);
-  max64_dpp<DPP_QUAD_XOR2, 0xF>(a);
-  max64_dpp<DPP_ROW_HALF_MIRROR, 0xF>(a);
-  max64_dpp<DPP_ROW_MIRROR, 0xF>(a);
-  max64_dpp<DPP_ROW_BCAST15, 0xA>(a);
-  max64_dpp<DPP_ROW_BCAST31, 0xC>(a);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)a, 63);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(a >> 32), 63);
-  return ((uint64_t)hi << 32) | lo;
+__device__ __forceinline__ uint32_t wave_max32(uint32_t a) {
+  max32_dpp<DPP_QUAD_XOR1, 0xF>(a);
+  max32_dpp<DPP_QUAD_XOR2, 0xF>(a);
+  max32_dpp<DPP_ROW_HALF_MIRROR, 0xF>(a);
+  max32_dpp<DPP_ROW_MIRROR, 0xF>(a);
+  max32_dpp<DPP_ROW_BCAST15, 0xA>(a);
+  max32_dpp<DPP_ROW_BCAST31, 0xC>(a);
+  return (uint32_t)__builtin_amdgcn_readlane((int)a, 63);
 }
 
 // One token's logits, lane l holding logits l, l + 64, ... (PER per lane, E <= 64 PER).
@@ -75,27 +65,38 @@ __device__ __forceinline__ void route_load(const float* __restrict__ l, int E, i
 }
 
 // Top-k of one token by one wavefront, from its loaded logits.  Each of the k rounds takes
-// every lane's largest untaken key, reduces it over the wavefront with DPP exchanges and
-// marks the winner taken (its key becomes 0).  Lane j < k returns the j-th winner (slots in
-// descending logit order) and its softmax gate over the k winners.
+// the wave's largest untaken value key (one 32-bit maximum per lane, then over the
+// wavefront with DPP exchanges); its winner is the lowest expert id holding that key, which
+// is the lowest lane of the first slot i whose ballot of key == maximum is not empty (ids
+// lane + 64 i: a lower slot always has the lower id), and its key becomes 0 (taken).  So a
+// larger value wins and equal values go to the lower expert id.  Lane j < k returns the
+// j-th winner (slots in descending logit order) and its softmax gate over the k winners.
 template <int PER>
 __device__ __forceinline__ void route_select(const float (&v)[PER], int E, int k, int lane, int& my_e,
                                              float& my_gate) {
-  uint64_t key[PER];
+  uint32_t key[PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) key[i] = (lane + 64 * i < E) ? route_key64(v[i], lane + 64 * i) : 0ull;
+  for (int i = 0; i < PER; ++i) key[i] = (lane + 64 * i < E) ? route_key(v[i]) : 0u;
   uint32_t my_key = 0u;
   my_e = 0;
   for (int j = 0; j < k; ++j) {
-    uint64_t b = key[0];
+    uint32_t b = key[0];
 #pragma unroll
     for (int i = 1; i < PER; ++i) b = key[i] > b ? key[i] : b;
-    const uint64_t w = wave_max64(b);
-    const int wi = (int)~(uint32_t)w;
+    const uint32_t w = wave_max32(b);
+    int wi = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) key[i] = (wi == lane + 64 * i) ? 0ull : key[i];
+    for (int i = 0; i < PER; ++i) {
+      const uint64_t m = __ballot(key[i] == w);
+      if (m) {
+        wi = 64 * i + (int)__builtin_ctzll(m);
+        break;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) key[i] = (wi == lane + 64 * i) ? 0u : key[i];
     if (lane == j) {
-      my_key = (uint32_t)(w >> 32);
+      my_key = w;
       my_e = wi;
     }
   }
