@@ -72,12 +72,14 @@ def _load():
     lib.ora_sort.argtypes = [P, I64, I64, I64, P, P, P, P, P]
     lib.ora_moe_tokens.argtypes = [P, P, I64, I64, P, P, P, P, I64, I64, I64, I64, P, I64, P, P, P, ctypes.c_int]
     lib.ora_moe_tokens_a8.argtypes = lib.ora_moe_tokens.argtypes
+    lib.ora_moe_tokens_terms.argtypes = lib.ora_moe_tokens.argtypes[:-1] + [P, P, P, P, ctypes.c_int]
     lib.ora_e4m3.restype = ctypes.c_double
     lib.ora_e4m3.argtypes = [ctypes.c_int]
     lib.ora_mxfp8_quantize.argtypes = [P, I64, I64, P, P]
     lib.ora_mx_linear_a8.argtypes = lib.ora_mx_linear.argtypes
     for name in ("ora_pack_codes", "ora_unpack_codes", "ora_dequant_f64", "ora_mx_linear",
-                 "ora_route", "ora_sort", "ora_moe_tokens", "ora_moe_tokens_a8", "ora_mxfp8_quantize",
+                 "ora_route", "ora_sort", "ora_moe_tokens", "ora_moe_tokens_a8", "ora_moe_tokens_terms",
+                 "ora_mxfp8_quantize",
                  "ora_mx_linear_a8"):
         getattr(lib, name).restype = None
     _lib = lib
@@ -198,18 +200,18 @@ def route(logits: np.ndarray, k: int):
 
 
 def sort(ids: np.ndarray, E: int):
-    """Returns dict(counts [E], offsets [E+1], sorted_slots [T*k], active [E], num_active,
-    max_rows = the largest count)."""
+    """Returns dict(counts [E], offsets [E+1], sorted_slots [T*k], active [E] (the active
+    experts ascending, then -1), num_active)."""
     ids = _c(ids, np.int32)
     T, k = ids.shape
     counts = np.empty(E, np.int32)
     offsets = np.empty(E + 1, np.int32)
     sorted_slots = np.empty(T * k, np.int32)
     active = np.empty(E, np.int32)
-    na = np.zeros(2, np.int32)
+    na = np.zeros(1, np.int32)
     _load().ora_sort(_p(ids), T, k, E, _p(counts), _p(offsets), _p(sorted_slots), _p(active), _p(na))
     return dict(counts=counts, offsets=offsets, sorted_slots=sorted_slots, active=active,
-                num_active=int(na[0]), max_rows=int(na[1]))
+                num_active=int(na[0]))
 
 
 def moe_tokens(x_bits, logits, k, wgu, sgu, wd, sd, T, H, I, E, tokens=None, want_h=False,
@@ -242,3 +244,37 @@ def moe_tokens(x_bits, logits, k, wgu, sgu, wd, sd, T, H, I, E, tokens=None, wan
     fn(_p(x_bits), _p(logits), k, n_shared, _p(wgu), _p(sgu), _p(wd), _p(sd), T, H, I, E, _p(tokens), ntok,
        _p(y), _p(sm), _p(h) if want_h else None, nthreads or default_threads())
     return y, sm, h
+
+
+def moe_gate_up_terms(x_bits, logits, k, wgu, sgu, wd, sd, T, H, I, E, tokens=None,
+                      nthreads: int | None = None, n_shared: int = 0):
+    """moe_tokens (bf16 activations) with the gate_up terms of every slot row.
+
+    Returns (y, scale_m, h, terms) as moe_tokens(want_h=True) does, with terms =
+    dict(g, u: fp32 [ntok*(k+n_shared), I], the dot products before SwiGLU; gabs, uabs:
+    fp64, sum_K |x w| of the gate and up rows).  Row i*(k+n_shared) + j is slot j of
+    token tokens[i].
+    """
+    x_bits = _c(x_bits, np.uint16)
+    logits = _c(logits, np.float32)
+    assert x_bits.size == T * H and logits.size == T * E
+    Ew = E + n_shared
+    for a, n in ((wgu, Ew * 2 * I * H // 2), (sgu, Ew * 2 * I * H // 32), (wd, Ew * H * I // 2),
+                 (sd, Ew * H * I // 32)):
+        assert a.dtype == np.uint8 and a.flags.c_contiguous and a.size == n
+    if tokens is None:
+        tokens = np.arange(T, dtype=np.int32)
+    tokens = _c(tokens, np.int32)
+    ntok = tokens.size
+    rows = ntok * (k + n_shared)
+    y = np.empty((ntok, H), np.uint16)
+    sm = np.empty((ntok, H), np.float64)
+    h = np.empty((rows, I), np.uint16)
+    g = np.empty((rows, I), np.float32)
+    u = np.empty((rows, I), np.float32)
+    ga = np.empty((rows, I), np.float64)
+    ua = np.empty((rows, I), np.float64)
+    _load().ora_moe_tokens_terms(_p(x_bits), _p(logits), k, n_shared, _p(wgu), _p(sgu), _p(wd), _p(sd), T, H, I, E,
+                                 _p(tokens), ntok, _p(y), _p(sm), _p(h), _p(g), _p(u), _p(ga), _p(ua),
+                                 nthreads or default_threads())
+    return y, sm, h, dict(g=g, u=u, gabs=ga, uabs=ua)

@@ -58,7 +58,7 @@
 #include <omp.h>
 #endif
 
-#define ORA_VERSION 1
+#define ORA_VERSION 2
 
 int ora_version(void) { return ORA_VERSION; }
 
@@ -328,16 +328,16 @@ void ora_route(const float* logits, int64_t T, int64_t E, int64_t k, int32_t* id
 
 /* ------------------------------------------------------------ expert sort */
 
-/* Row class of an active expert (its count of routed slots): 3 for 8 or more,
- * 2 for 4-7, 1 for 2-3, 0 for 1. */
-static int row_class(int32_t c) { return c >= 8 ? 3 : c >= 4 ? 2 : c >= 2 ? 1 : 0; }
-
 /* Counting sort of the T*k flat slots f = t*k + j by expert id: experts
- * ascending, f ascending within an expert.  counts [E]; offsets [E+1]
- * (exclusive prefix sums); sorted_slots [T*k]; active [E] = experts with at
- * least one slot, by row class descending, then by expert id ascending
- * (entries past num_active are set to -1); num_active [2] = the number of
- * active experts, then the largest count. */
+ * ascending, f ascending within an expert (a stable sort by expert).  The
+ * pages say only that a step's tokens are grouped by the expert they route to
+ * so that each routed expert's weights are read once ("Zyphra Inference Wave
+ * 2", sections "Speculative decoding." and "Quantization"); the stable order
+ * is the plainest reading.  Outputs: counts [E]; offsets [E+1] (exclusive
+ * prefix sums); sorted_slots [T*k]; active [E] = the experts with at least one
+ * slot, ascending (entries past the count are set to -1); *num_active = their
+ * number.  The order in which a GPU takes the active experts is its own
+ * scheduling choice and is not part of this definition. */
 void ora_sort(const int32_t* ids, int64_t T, int64_t k, int64_t E, int32_t* counts, int32_t* offsets,
               int32_t* sorted_slots, int32_t* active, int32_t* num_active) {
   if (E < 1) return;
@@ -354,15 +354,10 @@ void ora_sort(const int32_t* ids, int64_t T, int64_t k, int64_t E, int32_t* coun
   }
   free(fill);
   int32_t na = 0;
-  for (int cls = 3; cls >= 0; --cls)
-    for (int64_t e = 0; e < E; ++e)
-      if (counts[e] > 0 && row_class(counts[e]) == cls) active[na++] = (int32_t)e;
-  for (int64_t e = na; e < E; ++e) active[e] = -1;
-  int32_t most = 0;
   for (int64_t e = 0; e < E; ++e)
-    if (counts[e] > most) most = counts[e];
-  num_active[0] = na;
-  num_active[1] = most;
+    if (counts[e] > 0) active[na++] = (int32_t)e;
+  for (int64_t e = na; e < E; ++e) active[e] = -1;
+  *num_active = na;
 }
 
 /* ------------------------------------------------------------- MoE layer */
@@ -392,7 +387,8 @@ static double swiglu(float g, float u) {
 static void moe_tokens_impl(const uint16_t* x, const float* logits, int64_t k_routed, int64_t n_shared,
                             const uint8_t* wgu, const uint8_t* sgu, const uint8_t* wd, const uint8_t* sd,
                             int64_t H, int64_t I, int64_t E, const int32_t* tok, int64_t ntok, uint16_t* y,
-                            double* scale_m, uint16_t* h_out, int nthreads, int act8) {
+                            double* scale_m, uint16_t* h_out, float* g_out, float* u_out, double* gabs_out,
+                            double* uabs_out, int nthreads, int act8) {
   const int64_t k = k_routed + n_shared;  /* slots per token */
   int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)(ntok * k));
   float* gates = (float*)malloc(sizeof(float) * (size_t)(ntok * k));
@@ -420,9 +416,14 @@ static void moe_tokens_impl(const uint16_t* x, const float* logits, int64_t k_ro
       int64_t e = ids[p];
       const uint8_t* W = wgu + (size_t)e * gu_w;
       const uint8_t* S = sgu + (size_t)e * gu_s;
-      float g = dot_vals(xa + (p / k) * H, W, S, H, n, NULL);
-      float u = dot_vals(xa + (p / k) * H, W, S, H, I + n, NULL);
+      double ga, ua;
+      float g = dot_vals(xa + (p / k) * H, W, S, H, n, &ga);
+      float u = dot_vals(xa + (p / k) * H, W, S, H, I + n, &ua);
       h[p * I + n] = ora_bf16_rne(swiglu(g, u));
+      if (g_out) g_out[p * I + n] = g;
+      if (u_out) u_out[p * I + n] = u;
+      if (gabs_out) gabs_out[p * I + n] = ga;
+      if (uabs_out) uabs_out[p * I + n] = ua;
     }
   for (int64_t p = 0; p < ntok * k; ++p) activation_row(h + p * I, I, act8, ha + p * I);
 #ifdef _OPENMP
@@ -457,8 +458,8 @@ void ora_moe_tokens(const uint16_t* x, const float* logits, int64_t k_routed, in
                     int64_t H, int64_t I, int64_t E, const int32_t* tok, int64_t ntok, uint16_t* y,
                     double* scale_m, uint16_t* h_out, int nthreads) {
   (void)T;
-  moe_tokens_impl(x, logits, k_routed, n_shared, wgu, sgu, wd, sd, H, I, E, tok, ntok, y, scale_m, h_out,
-                  nthreads, 0);
+  moe_tokens_impl(x, logits, k_routed, n_shared, wgu, sgu, wd, sd, H, I, E, tok, ntok, y, scale_m, h_out, NULL,
+                  NULL, NULL, NULL, nthreads, 0);
 }
 
 /* The MoE layer with MXFP8 activations (see moe_tokens_impl). */
@@ -467,6 +468,21 @@ void ora_moe_tokens_a8(const uint16_t* x, const float* logits, int64_t k_routed,
                        int64_t H, int64_t I, int64_t E, const int32_t* tok, int64_t ntok, uint16_t* y,
                        double* scale_m, uint16_t* h_out, int nthreads) {
   (void)T;
-  moe_tokens_impl(x, logits, k_routed, n_shared, wgu, sgu, wd, sd, H, I, E, tok, ntok, y, scale_m, h_out,
-                  nthreads, 1);
+  moe_tokens_impl(x, logits, k_routed, n_shared, wgu, sgu, wd, sd, H, I, E, tok, ntok, y, scale_m, h_out, NULL,
+                  NULL, NULL, NULL, nthreads, 1);
+}
+
+/* The MoE layer (bf16 activations) with the gate_up terms of every slot row p
+ * (token tok[p / (k_routed + n_shared)], slot p % (k_routed + n_shared)) and
+ * column n < I: g_out, u_out = the fp32 g and u before SwiGLU, gabs_out,
+ * uabs_out = sum_K |x w| of the gate and up rows in fp64 (each [ntok*k, I],
+ * any may be NULL).  Other arguments and outputs as ora_moe_tokens. */
+void ora_moe_tokens_terms(const uint16_t* x, const float* logits, int64_t k_routed, int64_t n_shared,
+                          const uint8_t* wgu, const uint8_t* sgu, const uint8_t* wd, const uint8_t* sd, int64_t T,
+                          int64_t H, int64_t I, int64_t E, const int32_t* tok, int64_t ntok, uint16_t* y,
+                          double* scale_m, uint16_t* h_out, float* g_out, float* u_out, double* gabs_out,
+                          double* uabs_out, int nthreads) {
+  (void)T;
+  moe_tokens_impl(x, logits, k_routed, n_shared, wgu, sgu, wd, sd, H, I, E, tok, ntok, y, scale_m, h_out, g_out,
+                  u_out, gabs_out, uabs_out, nthreads, 0);
 }

@@ -108,6 +108,26 @@ def test_single_expert_reduces_to_dense_mlp():
     assert np.array_equal(y, y_ref)  # gate = 1 exactly when k = 1
 
 
+def test_gate_up_terms_are_the_dense_layer_dot_products():
+    """The gate_up terms the oracle reports (g, u before SwiGLU and their sums of |x w|)
+    are, slot by slot, the pinned dense layer's fp32 dot products and bound terms over the
+    routed expert's gate and up rows, and the h it returns with them is moe_tokens' h."""
+    cfg = tiny_cfg(7, T=4, H=128, I=64, E=5, k=2, e_lo=-8, e_hi=-3)
+    inp = synthetic.moe_inputs_host(cfg)
+    args = (inp["x"], inp["logits"], cfg.k, inp["wgu"], inp["sgu"], inp["wd"], inp["sd"], cfg.T, cfg.H, cfg.I, cfg.E)
+    y, sm, h, terms = oracle.moe_gate_up_terms(*args)
+    y2, sm2, h2 = oracle.moe_tokens(*args, want_h=True)
+    assert np.array_equal(y, y2) and np.array_equal(sm, sm2) and np.array_equal(h, h2)
+    ids, _ = oracle.route(inp["logits"], cfg.k)
+    for t in range(cfg.T):
+        for j in range(cfg.k):
+            e = ids[t, j]
+            _, acc, sd = oracle.mx_linear(inp["x"][t:t + 1], inp["wgu"][e], inp["sgu"][e], 1, cfg.H, 2 * cfg.I)
+            r = t * cfg.k + j
+            assert np.array_equal(terms["g"][r], acc[0, :cfg.I]) and np.array_equal(terms["u"][r], acc[0, cfg.I:])
+            assert np.array_equal(terms["gabs"][r], sd[0, :cfg.I]) and np.array_equal(terms["uabs"][r], sd[0, cfg.I:])
+
+
 def shared_cfg(seed, n_shared, E=3, k=2):
     return synthetic.MoEConfig("tiny_shared", T=3, H=128, I=64, E=E, k=k, routing="normal", e_lo=-8, e_hi=-3,
                                seed=seed, n_shared=n_shared)

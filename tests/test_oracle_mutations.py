@@ -25,8 +25,8 @@ MUTATIONS = {
     "e8m0_bias": ("ldexp(1.0, (s & 0xFF) - 127)", "ldexp(1.0, (s & 0xFF) - 128)"),
     "magnitude_table": ("{0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0}", "{0.0, 0.5, 1.0, 1.5, 2.0, 2.5, 3.0, 4.0}"),
     "drop_up_projection": ("return gd / (1.0 + exp(-gd)) * (double)u;", "return gd / (1.0 + exp(-gd));"),
-    "swap_gate_up": ("float g = dot_vals(xa + (p / k) * H, W, S, H, n, NULL);\n      float u = dot_vals(xa + (p / k) * H, W, S, H, I + n, NULL);",
-                     "float u = dot_vals(xa + (p / k) * H, W, S, H, n, NULL);\n      float g = dot_vals(xa + (p / k) * H, W, S, H, I + n, NULL);"),
+    "swap_gate_up": ("float g = dot_vals(xa + (p / k) * H, W, S, H, n, &ga);\n      float u = dot_vals(xa + (p / k) * H, W, S, H, I + n, &ua);",
+                     "float u = dot_vals(xa + (p / k) * H, W, S, H, n, &ga);\n      float g = dot_vals(xa + (p / k) * H, W, S, H, I + n, &ua);"),
     "combine_wrong_gate": ("float gd = (float)((double)gates[p] * (double)d);", "float gd = (float)((double)gates[i * k] * (double)d);"),
     "tie_to_higher_id": ("if (best < 0 || l[e] > l[best]) best = e;", "if (best < 0 || l[e] >= l[best]) best = e;"),
     "unstable_sort": ("for (int64_t f = 0; f < F; ++f) {\n    int32_t e = ids[f];", "for (int64_t f = F - 1; f >= 0; --f) {\n    int32_t e = ids[f];"),
@@ -38,7 +38,7 @@ MUTATIONS = {
     "e4m3_no_saturation": ("if (a >= 448.0) return 0x7E;", "if (a >= 480.0) return 0x7E;"),
     "e4m3_subnormal_spacing": ("if (a == 0.0 || lead < -6) lead = -6;", "if (a == 0.0 || lead < -7) lead = -7;"),
     "a8_h_not_quantized": ("activation_row(h + p * I, I, act8, ha + p * I);", "activation_row(h + p * I, I, 0, ha + p * I);"),
-    "active_light_first": ("for (int cls = 3; cls >= 0; --cls)", "for (int cls = 0; cls <= 3; ++cls)"),
+    "active_lists_idle_experts": ("if (counts[e] > 0) active[na++] = (int32_t)e;", "if (counts[e] >= 0) active[na++] = (int32_t)e;"),
 }
 
 # pin tests expected to catch each mutation (each entry: callable(tmp_fixture_args) -> runs asserts)
@@ -69,7 +69,7 @@ CATCHERS = {
     "e4m3_no_saturation": [lambda: A8.test_quantize_rounds_like_torch_over_all_bf16(0, 2 - 2.0 ** -7)],
     "e4m3_subnormal_spacing": [lambda: A8.test_quantize_rounds_like_torch_over_all_bf16(0, 1.75)],
     "a8_h_not_quantized": [lambda: A8.test_a8_moe_single_expert_reduces_to_a8_linear()],
-    "active_light_first": [lambda: R.test_sort_matches_stable_argsort(32, 256, 8)],
+    "active_lists_idle_experts": [lambda: R.test_sort_matches_stable_argsort(32, 256, 8)],
 }
 
 
