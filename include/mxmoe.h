@@ -65,7 +65,11 @@ MX_API const char* mx_status_string(int status);
 
 /*
  * Dense MXFP4 linear layer: y[t,n] = bf16_rne( sum_k x[t,k] * w[n,k] ), products exact,
- * fp32 accumulation.
+ * fp32 accumulation.  The MXFP4 projection the AMD megakernel blog ("Bringing Ultra-Fast,
+ * Interactive LLM Inference to AMD Instinct MI355X GPUs", section "3. Low-Precision Data
+ * Types") applies to attention projections and the LM head, here with bf16 activations;
+ * decode reads every weight on every pass, so a call's weight bytes set a floor on its
+ * time (same section).
  *   x       bf16 [T, K]
  *   w_codes uint8 [N, K/2], w_scales uint8 [N, K/32]
  *   y       bf16 [T, N]   (written)
@@ -112,9 +116,13 @@ MX_API int mxfp4_dequantize(const uint8_t* w_codes, const uint8_t* w_scales, int
                      void* stream);
 
 /*
- * Top-k routing with a softmax over the selected logits.  For each token t: the k
- * largest logits[t,:] (ties go to the lower expert id), in descending-logit order;
- * gates[t,j] = exp(l_j - l_0) / sum_i exp(l_i - l_0) in fp32.
+ * Top-k routing with a softmax over the selected logits ("Zyphra Inference Wave 2",
+ * Figure 10: top-8 routing over 256 and 384 experts; the AMD megakernel blog, section
+ * "4. Data Locality", profiles top-k expert routing as a phase of its own).  The pages fix
+ * neither tie order nor gate normalisation; the plainest reading is taken: for each token
+ * t, the k largest logits[t,:] (ties go to the lower expert id), in descending-logit order;
+ * gates[t,j] = exp(l_j - l_0) / sum_i exp(l_i - l_0) in fp32 (a softmax over the k
+ * selected logits).
  *   logits fp32 [T, E] (must be finite), ids int32 [T, top_k], gates fp32 [T, top_k].
  *   1 <= T <= MX_MAX_TOKENS, 1 <= top_k <= min(E, MX_MAX_TOPK), E <= MX_MAX_EXPERTS.
  */
@@ -123,7 +131,10 @@ MX_API int moe_route_topk(const float* logits, int64_t T, int64_t E, int64_t top
 
 /*
  * Counting sort of the T*top_k flat slots f = t*top_k + j by expert id ids[f]: experts
- * ascending, f ascending within an expert (bit-exact, deterministic).
+ * ascending, f ascending within an expert (bit-exact, deterministic).  "Zyphra Inference
+ * Wave 2" (sections "Speculative decoding." and "Quantization") has a step read each
+ * routed expert's weights once for all tokens routed to it; grouping the slots by expert
+ * is what lets the expert GEMMs do that.  The stable order is the plainest reading.
  *   ids          int32 [T, top_k]; each row must hold top_k DISTINCT ids in [0, E)
  *                (as moe_route_topk produces); other ids are skipped.
  *   counts       int32 [E]       slots per expert
@@ -143,9 +154,10 @@ MX_API int moe_sort_by_expert(const int32_t* ids, int64_t T, int64_t top_k, int6
 /*
  * moe_route_topk followed by moe_sort_by_expert of its ids: one launch for T <= 16, two
  * beyond.  moe_mxfp4_forward runs it as its first stage beyond 16 tokens (and with shared
- * experts); up to 16 tokens its gate_up launch routes and sorts in every workgroup instead,
- * with the same result.  Arguments, outputs and limits
- * as for those two calls.
+ * experts); up to 16 tokens its gate_up launch routes and sorts in every workgroup instead.
+ * That internal sort has the same counts, offsets and sorted slots, but keeps its active
+ * list in ascending expert order and leaves the entries past the last one unwritten (its
+ * down launch accepts any order).  Arguments, outputs and limits as for those two calls.
  */
 MX_API int moe_route_sort(const float* logits, int64_t T, int64_t E, int64_t top_k, int32_t* ids, float* gates,
                           int32_t* counts, int32_t* offsets, int32_t* sorted_slots, int32_t* active,
@@ -209,9 +221,12 @@ MX_API size_t moe_mxfp4_workspace_size(int64_t T, int64_t H, int64_t I, int64_t 
  *                 bytes, 256-byte aligned.  Its first MX_WORKSPACE_CTL_BYTES must be zero
  *                 before its first use (every call leaves them zero); the rest needs no
  *                 initialization and is overwritten.  Calls that share a workspace must
- *                 not overlap in time.
+ *                 not overlap in time (two streams need two workspaces).
  *   1 <= T <= MX_MAX_TOKENS; 1 <= top_k <= min(E, MX_MAX_TOPK); E <= MX_MAX_EXPERTS;
- *   H % 1024 == 0; I % 1024 == 0 (both GEMMs stream 1024 K values per step).
+ *   1024 <= H <= 65536 and H % 1024 == 0 (the gate_up GEMM stages its scales 1024 K
+ *   values at a time); 256 <= I <= 65536 and I % 256 == 0 (the down GEMM streams 256 K
+ *   values per segment; I = 256 is one tensor-parallel eighth of an expert of 2048).
+ *   MX_ERR_SHAPE otherwise.
  */
 MX_API int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, int64_t top_k, const uint8_t* w_gate_up,
                       const uint8_t* s_gate_up, const uint8_t* w_down, const uint8_t* s_down, uint16_t* y,
@@ -270,6 +285,22 @@ MX_API int moe_mxfp4_forward_persistent(const uint16_t* x, const float* router_l
                                         const uint8_t* w_gate_up, const uint8_t* s_gate_up, const uint8_t* w_down,
                                         const uint8_t* s_down, uint16_t* y, int64_t T, int64_t H, int64_t I,
                                         int64_t E, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * HBM reference kernels (measurement utilities, not steps of the layer).  "Zyphra
+ * Inference Wave 2" (footnote 6 of its roofline discussion) measures MI355X's HBM with a
+ * plain copy kernel, 6.07 of the nominal 8 TB/s; these give the same kind of yardstick on
+ * the GPU at hand.  Both stream the buffer once in 16-byte nontemporal pieces over the
+ * whole device.
+ *
+ * mx_hbm_read: reads `bytes` bytes at src and XORs them into xor_out: word c (c < 4)
+ *   receives the XOR of 32-bit word c of every 16-byte piece.  xor_out is 4 uint32 device
+ *   words that the CALLER zeroes before the call (the kernel XORs into them).
+ * mx_hbm_copy: copies `bytes` bytes from src to dst (the ranges must not overlap).
+ *   bytes >= 16 and bytes % 16 == 0; src and dst 16-byte aligned, xor_out 4-byte aligned.
+ */
+MX_API int mx_hbm_read(const void* src, size_t bytes, uint32_t* xor_out, void* stream);
+MX_API int mx_hbm_copy(void* dst, const void* src, size_t bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -52,15 +52,19 @@ _lib.moe_mxfp4_forward_shared.argtypes = [_P, _P, _I64, _I64, _P, _P, _P, _P, _P
 _lib.moe_mxfp4_forward_a8.argtypes = list(_lib.moe_mxfp4_forward_shared.argtypes)
 _lib.mx_linear_a8.argtypes = list(_lib.mx_linear.argtypes)
 _lib.mxfp8_quantize.argtypes = [_P, _I64, _I64, _P, _P, _P]
+_lib.mx_hbm_read.argtypes = [_P, ctypes.c_size_t, _P, _P]
+_lib.mx_hbm_copy.argtypes = [_P, _P, ctypes.c_size_t, _P]
 for _n in ("mx_linear", "mxfp4_dequantize", "moe_route_topk", "moe_sort_by_expert", "moe_route_sort",
            "moe_gate_up_swiglu", "moe_down_combine", "moe_mxfp4_forward", "moe_mxfp4_forward_persistent",
-           "moe_mxfp4_forward_shared", "moe_mxfp4_forward_a8", "mx_linear_a8", "mxfp8_quantize"):
+           "moe_mxfp4_forward_shared", "moe_mxfp4_forward_a8", "mx_linear_a8", "mxfp8_quantize", "mx_hbm_read",
+           "mx_hbm_copy"):
     getattr(_lib, _n).restype = ctypes.c_int
 
 EXPORTED = ("mx_version", "mx_status_string", "mx_linear", "mxfp4_dequantize", "moe_route_topk",
             "moe_sort_by_expert", "moe_route_sort", "moe_gate_up_swiglu", "moe_down_combine",
             "moe_mxfp4_workspace_size", "moe_mxfp4_forward", "moe_mxfp4_forward_persistent",
-            "moe_mxfp4_forward_shared", "moe_mxfp4_forward_a8", "mx_linear_a8", "mxfp8_quantize")
+            "moe_mxfp4_forward_shared", "moe_mxfp4_forward_a8", "mx_linear_a8", "mxfp8_quantize", "mx_hbm_read",
+            "mx_hbm_copy")
 
 
 class MxError(RuntimeError):
@@ -133,6 +137,36 @@ def mx_linear(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor,
     st = getattr(_lib, name)(_ptr(x), _ptr(w_codes), _ptr(w_scales), _ptr(out), T, K, N, _stream(dev))
     _raise(st, name)
     return out
+
+
+def hbm_read(src: torch.Tensor, xor_out: torch.Tensor | None = None) -> torch.Tensor:
+    """HBM reference read of a contiguous device tensor (size a multiple of 16 bytes):
+    returns int32 [4], word c = XOR of 32-bit word c of every 16-byte piece."""
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    dev = src.device
+    if xor_out is None:
+        xor_out = torch.zeros(4, dtype=torch.int32, device=dev)
+    else:
+        _check(xor_out, "xor_out", torch.int32, 1, dev)
+        xor_out.zero_()
+    nbytes = src.numel() * src.element_size()
+    st = _lib.mx_hbm_read(_ptr(src), nbytes, _ptr(xor_out), _stream(dev))
+    _raise(st, "mx_hbm_read")
+    return xor_out
+
+
+def hbm_copy(dst: torch.Tensor, src: torch.Tensor) -> torch.Tensor:
+    """HBM reference copy between two contiguous device tensors of the same byte size."""
+    for t, n in ((dst, "dst"), (src, "src")):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous device tensor")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes or dst.device != src.device:
+        raise ValueError("dst and src must have the same byte size and device")
+    st = _lib.mx_hbm_copy(_ptr(dst), _ptr(src), nbytes, _stream(src.device))
+    _raise(st, "mx_hbm_copy")
+    return dst
 
 
 def mxfp8_quantize(x: torch.Tensor):
@@ -297,24 +331,60 @@ def workspace_size(T: int, H: int, I: int, E: int, top_k: int) -> int:
 _ws_cache: dict = {}
 
 
-def workspace(T: int, H: int, I: int, E: int, top_k: int, device) -> torch.Tensor:
-    """A cached uint8 workspace tensor large enough for these sizes on `device` (allocated
-    zero-filled: its leading control words must start at zero, and every call leaves them so)."""
+def workspace(T: int, H: int, I: int, E: int, top_k: int, device, stream=None) -> torch.Tensor:
+    """A cached uint8 workspace tensor large enough for these sizes, one per (device,
+    stream) -- by default the device's current stream.  Calls that share a workspace must
+    not overlap in time: calls on one stream run one after another, and calls on two
+    streams get two workspaces.  Allocated zero-filled: its leading control words must start
+    at zero, and every call leaves them so."""
     need = workspace_size(T, H, I, E, top_k)
     dev = torch.device(device)
-    buf = _ws_cache.get(dev)
+    if dev.index is None:
+        dev = torch.device(dev.type, torch.cuda.current_device())
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    key = (dev, int(stream.cuda_stream))
+    buf = _ws_cache.get(key)
     if buf is None or buf.numel() < need:
         buf = torch.zeros(need, dtype=torch.uint8, device=dev)
-        _ws_cache[dev] = buf
+        _ws_cache[key] = buf
     return buf
+
+
+# moe_mxfp4_forward_persistent: byte offset of the int32 word its bounded waits set to 1
+# when they give up (sticky until cleared)
+PERSISTENT_ERROR_OFFSET = 8
+
+
+class MxWaitError(RuntimeError):
+    """A single-launch layer's cross-workgroup wait gave up; its output is undefined."""
+
+
+def take_persistent_error(ws: torch.Tensor) -> int:
+    """Read and clear the single-launch layer's sticky error word in `ws` (synchronizes
+    with the stream that used it)."""
+    word = ws[PERSISTENT_ERROR_OFFSET:PERSISTENT_ERROR_OFFSET + 4].view(torch.int32)
+    v = int(word.item())
+    if v:
+        word.zero_()
+    return v
+
+
+def raise_for_persistent_error(word: int) -> None:
+    if word:
+        raise MxWaitError("moe_mxfp4_forward_persistent: a cross-workgroup wait gave up (are other kernels "
+                          "occupying the GPU?); the output is undefined")
 
 
 def moe_mxfp4_forward(x: torch.Tensor, router_logits: torch.Tensor, top_k: int, W_gate_up: torch.Tensor,
                       S_gate_up: torch.Tensor, W_down: torch.Tensor, S_down: torch.Tensor,
                       out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
-                      persistent: bool = False, n_shared: int = 0, act8: bool = False) -> torch.Tensor:
+                      persistent: bool = False, n_shared: int = 0, act8: bool = False,
+                      check: bool = True) -> torch.Tensor:
     """y[T,H] of the MXFP4 SwiGLU MoE layer (see include/mxmoe.h for the definition).
-    persistent=True runs it as one persistent launch (moe_mxfp4_forward_persistent; T <= 16).
+    persistent=True runs it as one persistent launch (moe_mxfp4_forward_persistent; T <= 16);
+    with check=True (and outside graph capture) the call then waits for it, reads and clears
+    its sticky error word and raises MxWaitError when a wait gave up.
     n_shared > 0: the weights hold E routed + n_shared shared experts, router_logits [T, E]
     (moe_mxfp4_forward_shared).  act8=True: MXFP8 activations for both expert GEMMs
     (moe_mxfp4_forward_a8, with or without shared experts)."""
@@ -352,4 +422,6 @@ def moe_mxfp4_forward(x: torch.Tensor, router_logits: torch.Tensor, top_k: int, 
                                  _ptr(W_down), _ptr(S_down), _ptr(out), T, H, I, E, _ptr(ws), ws.numel(),
                                  _stream(dev))
     _raise(st, name)
+    if persistent and check and not torch.cuda.is_current_stream_capturing():
+        raise_for_persistent_error(take_persistent_error(ws))
     return out

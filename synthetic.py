@@ -6,7 +6,7 @@ no rounding).  Both the oracle side and the GPU side of the tests take their
 inputs from here, and nothing else is shared between them.
 
 Data formats produced:
-  x       bf16 bit patterns (uint16): the upper 16 bits of an fp32 N(0,1) draw
+  x       bf16 bit patterns (uint16): an fp32 N(0,1) draw rounded to nearest-even bf16
   codes   uint8, two 4-bit codes per byte, every byte uniform over 0..255
           (so every 4-bit code, -0 included, is uniform)
   scales  uint8 E8M0 bytes, 127 + e with e uniform over [e_lo, e_hi]
@@ -108,9 +108,10 @@ TAG_X, TAG_LOGITS, TAG_W, TAG_S, TAG_ZIPF, TAG_SPEC = 1, 2, 3, 4, 5, 6
 
 
 def bf16_bits_normal(shape, seed: int, tag: int = TAG_X) -> np.ndarray:
-    """bf16 bit patterns of an N(0,1) draw: the upper half of each fp32 sample."""
-    f = _rng(seed, tag).standard_normal(size=shape, dtype=np.float32)
-    return (f.view(np.uint32) >> 16).astype(np.uint16)
+    """bf16 bit patterns of an N(0,1) draw: each fp32 sample rounded to the nearest bf16,
+    ties to even (the samples are finite and far from the bf16 range's ends)."""
+    u = _rng(seed, tag).standard_normal(size=shape, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
 
 
 def random_codes(rows: int, K: int, seed: int, tag: int = TAG_W) -> np.ndarray:

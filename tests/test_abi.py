@@ -132,6 +132,12 @@ def test_forward_rejects():
     assert fwd(I=96) == MX_ERR_SHAPE
     assert fwd(I=128) == MX_ERR_SHAPE   # below 256
     assert fwd(I=320) == MX_ERR_SHAPE   # not a multiple of 256
+    # I = 256 and 768 pass the shape checks (the header's I % 256 == 0): they fail at the
+    # workspace check that follows, since the workspace below is sized for I = 1024
+    small = m.workspace_size(4, 1024, 256, 8, 2) - 1
+    assert fwd(I=256, wb=small) == MX_ERR_WORKSPACE
+    assert fwd(I=768, wb=m.workspace_size(4, 1024, 768, 8, 2) - 1) == MX_ERR_WORKSPACE
+    assert fwd(H=2048, I=256, wb=m.workspace_size(4, 2048, 256, 8, 2) - 1) == MX_ERR_WORKSPACE
     assert fwd(wgu=MIS) == MX_ERR_ALIGN
     assert fwd(sgu=P((1 << 20) + 4)) == MX_ERR_ALIGN
     assert fwd(sd=P((1 << 20) + 8)) == MX_ERR_ALIGN
@@ -204,3 +210,29 @@ def test_workspace_size_grows_with_tokens():
     b = m.workspace_size(128, 7168, 2048, 384, 8)
     assert 0 < a < b
     assert m.workspace_size(0, 7168, 2048, 256, 8) == 0
+
+
+def test_header_states_the_checked_limits():
+    """The header's stated MoE limits are the ones the library checks (above)."""
+    src = open(HEADER).read()
+    assert "I % 256 == 0" in src and "H % 1024 == 0" in src
+    assert "I % 1024 == 0 (both" not in src
+
+
+def test_hbm_reference_kernels_reject():
+    L = m.raw()
+    assert L.mx_hbm_read(None, 64, A, None) == MX_ERR_NULL
+    assert L.mx_hbm_read(A, 0, A, None) == MX_ERR_SHAPE
+    assert L.mx_hbm_read(A, 72, A, None) == MX_ERR_SHAPE
+    assert L.mx_hbm_read(MIS, 64, A, None) == MX_ERR_ALIGN
+    assert L.mx_hbm_copy(A, None, 64, None) == MX_ERR_NULL
+    assert L.mx_hbm_copy(A, A, 8, None) == MX_ERR_SHAPE
+    assert L.mx_hbm_copy(MIS, A, 64, None) == MX_ERR_ALIGN
+
+
+def test_persistent_error_word_raises():
+    """The binding turns the single-launch layer's sticky error word into an exception."""
+    m.raise_for_persistent_error(0)
+    with pytest.raises(m.MxWaitError):
+        m.raise_for_persistent_error(1)
+    assert m.PERSISTENT_ERROR_OFFSET == 8

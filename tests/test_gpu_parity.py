@@ -144,6 +144,24 @@ def test_route_edge_shapes_and_ties(dev, mx, T, E, k):
     assert np.max(np.abs(gates.cpu().numpy().astype(np.float64) - ogates)) <= 1e-6
 
 
+def check_sort(r, o):
+    """The library's sort against the oracle's: counts, offsets and sorted slots bit-exact;
+    the active list a permutation of the oracle's active set (ascending there) in the order
+    the library documents for its expert GEMMs (row class descending: 8 or more rows, 4-7,
+    2-3, 1; expert id ascending within a class), -1 after it; num_active = {the number of
+    active experts, the largest count}, the second computed here from the counts."""
+    for key in ("counts", "offsets", "sorted_slots"):
+        assert np.array_equal(r[key].cpu().numpy(), o[key]), key
+    counts, na = o["counts"], o["num_active"]
+    assert r["num_active"].cpu().tolist() == [na, int(counts.max())]
+    act = r["active"].cpu().numpy()
+    lib = act[:na]
+    assert np.array_equal(np.sort(lib), o["active"][:na]), "active list is not a permutation of the active set"
+    assert np.all(act[na:] == -1)
+    cls = np.digitize(counts[lib], [2, 4, 8])
+    assert np.array_equal(lib, lib[np.lexsort((lib, -cls))]), "active list not in row-class order"
+
+
 @pytest.mark.parametrize("T,E,k", [(1, 256, 8), (4, 256, 8), (32, 256, 8), (128, 384, 8), (256, 1024, 32),
                                    (3, 4, 4), (9, 7, 2), (256, 8, 1)])
 def test_sort_matches_oracle(dev, mx, T, E, k):
@@ -151,10 +169,7 @@ def test_sort_matches_oracle(dev, mx, T, E, k):
     ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
     say("sort", T, E, k)
     r = mx.moe_sort_by_expert(torch.from_numpy(ids).to(dev), E)
-    o = oracle.sort(ids, E)
-    for key in ("counts", "offsets", "sorted_slots", "active"):
-        assert np.array_equal(r[key].cpu().numpy(), o[key]), key
-    assert r["num_active"].cpu().tolist() == [o["num_active"], o["max_rows"]]
+    check_sort(r, oracle.sort(ids, E))
 
 
 # T <= 16 runs as one launch, larger T as the route and sort kernels: both paths, every
@@ -180,10 +195,7 @@ def test_route_sort_matches_oracle(dev, mx, name, variant):
     oids, ogates = oracle.route(logits, k)
     assert np.array_equal(ids.cpu().numpy(), oids)
     assert np.max(np.abs(gates.cpu().numpy().astype(np.float64) - ogates)) <= 1e-6
-    o = oracle.sort(oids, logits.shape[1])
-    for key in ("counts", "offsets", "sorted_slots", "active"):
-        assert np.array_equal(srt[key].cpu().numpy(), o[key]), key
-    assert srt["num_active"].cpu().tolist() == [o["num_active"], o["max_rows"]]
+    check_sort(srt, oracle.sort(oids, logits.shape[1]))
 
 
 # ------------------------------------------------------------------ MoE layer
@@ -201,9 +213,32 @@ def moe_device_inputs(cfg, dev, host=None):
     return d, x, logits
 
 
-def run_moe(mx, d, k, n_shared=0):
-    y = mx.moe_mxfp4_forward(d["x"], d["logits"], k, d["wgu"], d["sgu"], d["wd"], d["sd"], n_shared=n_shared)
+CTL_BYTES = 57344  # MX_WORKSPACE_CTL_BYTES
+
+
+def poisoned_workspace(mx, T, H, I, E, k, dev):
+    """A fresh workspace: control words zero (as the ABI requires), every other byte 0xFF,
+    so that any h, d or sort entry a kernel fails to write reads as NaN (or -1)."""
+    ws = torch.zeros(mx.workspace_size(T, H, I, E, k), dtype=torch.uint8, device=dev)
+    ws[CTL_BYTES:] = 0xFF
+    return ws
+
+
+def nan_like_out(shape, dev):
+    return torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
+
+
+def run_moe(mx, d, k, n_shared=0, act8=False):
+    """The layer forward on a NaN-poisoned workspace into a NaN-filled y."""
+    T, H = d["x"].shape
+    E = d["logits"].shape[1]
+    I = d["wd"].shape[2] * 2
+    dev = d["x"].device
+    ws = poisoned_workspace(mx, T, H, I, E + n_shared, k + n_shared, dev)
+    y = mx.moe_mxfp4_forward(d["x"], d["logits"], k, d["wgu"], d["sgu"], d["wd"], d["sd"], n_shared=n_shared,
+                             act8=act8, out=nan_like_out((T, H), dev), ws=ws)
     torch.cuda.synchronize()
+    assert not ws[:CTL_BYTES].any().item(), "control words not left zero"
     return to_host_bits(y)
 
 
@@ -238,8 +273,8 @@ def test_moe_tiny_full_oracle(dev, mx, shape):
     say(f"  worst ratio {worst:.3g}")
 
 
-FULL = [("moe_t4", None), ("moe_t32_zipf", [0, 5, 13, 31]), ("moe_t128", [0, 1, 64, 127]),
-        ("moe_spec_t4", None), ("moe_spec_t128", [0, 1, 2, 3, 126]),
+FULL = [("moe_t4", None), ("moe_t32_zipf", None), ("moe_t128", list(range(0, 128, 8))),
+        ("moe_spec_t4", None), ("moe_spec_t128", [0, 1, 2, 3, 40, 41, 126, 127]),
         ("moe_tp8_t4", None), ("moe_tp8_t32", None), ("moe_shared_t1", None), ("moe_shared_t32", [0, 9, 31])]
 
 
@@ -268,6 +303,8 @@ def test_moe_small_scale_variant(dev, mx):
 
 
 def test_moe_deterministic_and_inactive_experts_unread(dev, mx):
+    """Two runs on separately NaN-poisoned workspaces give the same y, and NaN scales planted
+    in every expert no token routes to change nothing."""
     cfg = synthetic.MoEConfig("det", T=8, H=1024, I=1024, E=32, k=4, routing="normal", e_lo=-8, e_hi=-2, seed=3)
     host = synthetic.moe_inputs_host(cfg)
     say("moe determinism / inactive NaN scales")
@@ -282,6 +319,153 @@ def test_moe_deterministic_and_inactive_experts_unread(dev, mx):
         d[key][unused] = 255
     y3 = run_moe(mx, d, cfg.k)
     assert np.array_equal(y1, y3)
+
+
+# ------------------------------------------------------------------ gate_up's h against the oracle's h
+
+H_REL = 1e-5  # the dense-output tolerance, applied to the fp32 dot products g and u
+
+
+def bf16_round_f64(v):
+    """Nearest bf16 (ties to even) of float64 values, as float64 (finite inputs)."""
+    m, e = np.frexp(v)                       # v = m * 2^e, 0.5 <= |m| < 1
+    q = np.ldexp(np.round(np.ldexp(m, 8)), e - 8)  # 8 significant bits; np.round ties to even
+    return np.where(v == 0, v, q)
+
+
+def check_h(got_bits, ora_bits, terms, what):
+    """gate_up's h against the oracle's, element by element.
+
+    g and u are dense MXFP4 dot products: the GPU's may differ from the oracle's fp32 sums
+    by the dense tolerance, H_REL * sum|x w| each.  With v = silu(g) u from the oracle's g
+    and u, that allows |h_exact - v| <= dh = 1.1 dg (|u| + du) + (|silu g| + 1.1 dg) du
+    plus 2^-20 |v| for the GPU's fp32 evaluation of silu (|silu'| <= 1.1).  The GPU's h
+    must be the bf16 rounding of some value within dh of v.  Where dh cannot move v across
+    a rounding boundary that means the oracle's h bit for bit, elsewhere one of the two
+    neighbours (a flip).  Returns (flips, elements)."""
+    go = bf16_to_f(got_bits).astype(np.float64)
+    ho = bf16_to_f(ora_bits).astype(np.float64)
+    g, u = terms["g"].astype(np.float64), terms["u"].astype(np.float64)
+    fin = np.isfinite(g) & np.isfinite(u)
+    assert np.array_equal(np.isnan(go[~fin]), np.isnan(ho[~fin])), f"{what}: NaN positions differ"
+    assert np.array_equal(go[~fin & ~np.isnan(ho)], ho[~fin & ~np.isnan(ho)]), f"{what}: non-finite h differ"
+    g, u, go, ho = g[fin], u[fin], go[fin], ho[fin]
+    dg, du = H_REL * terms["gabs"][fin], H_REL * terms["uabs"][fin]
+    silu = g / (1.0 + np.exp(-g))
+    v = silu * u
+    dh = 1.1 * dg * (np.abs(u) + du) + (np.abs(silu) + 1.1 * dg) * du + 2.0 ** -20 * np.abs(v)
+    lo, hi = bf16_round_f64(v - dh), bf16_round_f64(v + dh)
+    assert np.all(np.isfinite(go)), f"{what}: non-finite h where g and u are finite"
+    bad = (go < lo) | (go > hi)
+    if bad.any():
+        i = np.nonzero(bad)[0][0]
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} h values outside the bound; first gpu={go[i]!r} "
+                             f"oracle={ho[i]!r} v={v[i]!r} dh={dh[i]!r}")
+    flips = int((go != ho).sum())
+    one_value = lo == hi
+    assert np.array_equal(go[one_value], ho[one_value])  # implied above; stated for the reader
+    return flips, go.size, int((~one_value).sum())
+
+
+def gate_up_h_parity(mx, dev, cfg, d, x, logits, w_host, tokens=None):
+    """h from the gate_up stage entry point (after the route + sort entry point), on a
+    NaN-poisoned workspace into a NaN-filled h, against the oracle's h of the listed tokens."""
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    ids, gates, srt = mx.moe_route_sort(d["logits"], k)
+    ws = poisoned_workspace(mx, T, H, I, E, k, dev)
+    h = nan_like_out((T * k, I), dev)
+    mx.moe_gate_up_swiglu(d["x"], d["wgu"], d["sgu"], srt, k, h=h, ws=ws)
+    torch.cuda.synchronize()
+    hg = to_host_bits(h)                        # row p: the slot at sorted position p
+    slots = srt["sorted_slots"].cpu().numpy()
+    pos = np.empty_like(slots)
+    pos[slots] = np.arange(slots.size)          # sorted position of each flat slot
+    tok = np.arange(T, dtype=np.int32) if tokens is None else np.asarray(tokens, np.int32)
+    _, _, ho, terms = oracle.moe_gate_up_terms(x, logits, k, w_host["wgu"], w_host["sgu"], w_host["wd"],
+                                               w_host["sd"], T, H, I, E, tokens=tok)
+    flat = (tok[:, None] * k + np.arange(k)[None, :]).ravel()   # oracle row i*k + j is slot tok[i]*k + j
+    return check_h(hg[pos[flat]], ho, terms, cfg.name)
+
+
+H_TINY = [dict(T=1, H=1024, I=1024, E=4, k=1), dict(T=5, H=2048, I=1024, E=8, k=3),
+          dict(T=40, H=1024, I=1024, E=4, k=4), dict(T=64, H=3072, I=1024, E=16, k=8),
+          dict(T=20, H=2048, I=512, E=6, k=3), dict(T=2, H=1024, I=256, E=300, k=8)]
+
+
+@pytest.mark.parametrize("shape", H_TINY, ids=[f"T{s['T']}_H{s['H']}_I{s['I']}_E{s['E']}_k{s['k']}" for s in H_TINY])
+@pytest.mark.parametrize("scales", ["curved", "config"])
+def test_gate_up_h_matches_oracle_tiny(dev, mx, shape, scales):
+    """gate_up's h directly against the oracle's h: tiles of both widths, ragged and
+    repeated row groups, I = 256 and 512; SiLU in its curved region (scales 2^-12..2^-6)
+    and with the configs' scales."""
+    e_lo, e_hi = (-12, -6) if scales == "curved" else (-6, 0)
+    cfg = synthetic.MoEConfig("h_tiny", routing="normal", e_lo=e_lo, e_hi=e_hi, seed=shape["T"] * 5 + shape["E"],
+                              **shape)
+    host = synthetic.moe_inputs_host(cfg)
+    say("gate_up h, tiny", shape, scales)
+    d, x, logits = moe_device_inputs(cfg, dev, host)
+    flips, n, wide = gate_up_h_parity(mx, dev, cfg, d, x, logits, host)
+    say(f"  {flips} flips of {n} h values ({wide} within reach of a rounding boundary)")
+
+
+@pytest.mark.parametrize("name,tokens", [("moe_t4", None), ("moe_t32_zipf", None), ("moe_t128", list(range(0, 128, 16)))],
+                         ids=["moe_t4", "moe_t32_zipf", "moe_t128"])
+def test_gate_up_h_matches_oracle_full_size(dev, mx, name, tokens):
+    """The same at the full workload shapes, in the launch configuration the benchmark
+    times (every routed row at T = 4 and T = 32, where the hot experts have two row groups;
+    every slot of 8 tokens at T = 128)."""
+    cfg = synthetic.MOE_CONFIGS[name]
+    say("gate_up h, full size", name)
+    d, x, logits = moe_device_inputs(cfg, dev)
+    w_host = {key: d[key].cpu().numpy() for key in ("wgu", "sgu", "wd", "sd")}
+    flips, n, wide = gate_up_h_parity(mx, dev, cfg, d, x, logits, w_host, tokens)
+    say(f"  {flips} flips of {n} h values ({wide} within reach of a rounding boundary)")
+
+
+# ------------------------------------------------------------------ NaN and Inf through active experts
+
+@pytest.mark.parametrize("act8", [False, True], ids=["bf16", "mxfp8"])
+def test_moe_nan_scale_in_active_expert(dev, mx, act8):
+    """A NaN scale (0xFF) in one gate row block of a routed expert makes every output of
+    the tokens routed to it NaN (through h and the down sum); one in a down row block makes
+    that output column NaN for its tokens.  NaN positions must match the oracle's exactly,
+    every other output stays within the bound."""
+    cfg = synthetic.MoEConfig("nan_active", T=6, H=1024, I=1024, E=8, k=2, routing="normal", e_lo=-8, e_hi=-2,
+                              seed=21)
+    host = synthetic.moe_inputs_host(cfg)
+    ids, _ = oracle.route(host["logits"], cfg.k)
+    e1 = int(ids[0, 0])
+    e2 = next(int(e) for e in ids.ravel() if e != e1)
+    host["sgu"][e1, 5, 3] = 255
+    host["sd"][e2, 100, 0] = 255
+    say("moe NaN scale in active experts", e1, e2, "act8", act8)
+    d, x, logits = moe_device_inputs(cfg, dev, host)
+    got = run_moe(mx, d, cfg.k, act8=act8)
+    y, sm, _ = oracle.moe_tokens(x, logits, cfg.k, host["wgu"], host["sgu"], host["wd"], host["sd"], cfg.T, cfg.H,
+                                 cfg.I, cfg.E, act8=act8)
+    nan = np.isnan(bf16_to_f(y))
+    assert nan[0].all() and not nan.all()
+    check_bound(got, y, sm, MOE_REL, "NaN scale")
+
+
+@pytest.mark.parametrize("act8", [False, True], ids=["bf16", "mxfp8"])
+def test_moe_nan_and_inf_activation_rows(dev, mx, act8):
+    """A NaN, a +Inf and a -Inf activation in three tokens' rows: their outputs become
+    non-finite exactly where the oracle's do, the other tokens' outputs are unaffected."""
+    cfg = synthetic.MoEConfig("nan_x", T=7, H=1024, I=1024, E=8, k=2, routing="normal", e_lo=-8, e_hi=-2, seed=22)
+    host = synthetic.moe_inputs_host(cfg)
+    host["x"] = host["x"].copy()
+    host["x"][1, 17] = 0x7FC0   # NaN
+    host["x"][4, 300] = 0x7F80  # +Inf
+    host["x"][5, 3] = 0xFF80    # -Inf
+    say("moe NaN / Inf activation rows, act8", act8)
+    d, x, logits = moe_device_inputs(cfg, dev, host)
+    got = run_moe(mx, d, cfg.k, act8=act8)
+    y, sm, _ = oracle.moe_tokens(x, logits, cfg.k, host["wgu"], host["sgu"], host["wd"], host["sd"], cfg.T, cfg.H,
+                                 cfg.I, cfg.E, act8=act8)
+    fin = np.isfinite(bf16_to_f(y))
+    assert not fin[[1, 4, 5]].any() and fin[[0, 2, 3, 6]].all()
+    check_bound(got, y, sm, MOE_REL, "NaN/Inf x")
 
 
 def test_forward_with_tied_logits(dev, mx):
@@ -338,8 +522,6 @@ def test_stage_hooks_match_forward(dev, mx, shape):
 
 
 # ------------------------------------------------------------------ single-launch layer (T <= 16)
-
-CTL_BYTES = 57344  # MX_WORKSPACE_CTL_BYTES
 
 
 def run_hooks(mx, d, k, T):
@@ -447,7 +629,7 @@ def test_single_launch_back_to_back_sizes(dev, mx):
         host = synthetic.moe_inputs_host(cfg)
         d, x, logits = moe_device_inputs(cfg, dev, host)
         y = mx.moe_mxfp4_forward(d["x"], d["logits"], cfg.k, d["wgu"], d["sgu"], d["wd"], d["sd"], ws=ws,
-                                 persistent=cfg.T <= 16)
+                                 persistent=cfg.T <= 16, check=False)
         runs.append((cfg, host, x, logits, y))
     torch.cuda.synchronize()
     assert not ws[:CTL_BYTES].any().item()
@@ -517,3 +699,47 @@ def test_forward_graph_replays(dev, mx, T, persistent):
     assert not ws[:CTL_BYTES].any().item()
     yo, sm = oracle_moe(cfg, x, logits, host)
     check_bound(ref, yo, sm, MOE_REL, f"graph T={T}")
+
+
+# ------------------------------------------------------------------ HBM reference kernels, streams
+
+def test_hbm_reference_kernels(dev, mx):
+    """The bandwidth yardsticks compute what they claim: the read kernel's XOR of every
+    16-byte piece (bit-exact against numpy) and an exact copy, with a ragged tail."""
+    n = (64 << 20) + 48
+    host = np.random.default_rng(9).integers(0, 256, size=n, dtype=np.uint8)
+    src = torch.from_numpy(host).to(dev)
+    say("hbm read / copy", n)
+    got = mx.hbm_read(src).cpu().numpy().view(np.uint32)
+    want = np.bitwise_xor.reduce(host.view(np.uint32).reshape(-1, 4), axis=0)
+    assert np.array_equal(got, want)
+    dst = torch.full_like(src, 0xA5)
+    mx.hbm_copy(dst, src)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
+
+
+def test_workspace_cache_is_per_stream_and_streams_run_concurrently(dev, mx):
+    """The binding's cached workspaces are keyed by stream, so forwards issued on two
+    streams at once do not share control words: both give the single-stream result."""
+    cfg = synthetic.MoEConfig("streams", T=24, H=1024, I=1024, E=16, k=4, routing="normal", e_lo=-8, e_hi=-2, seed=4)
+    host = synthetic.moe_inputs_host(cfg)
+    say("two streams")
+    d, x, logits = moe_device_inputs(cfg, dev, host)
+    ref = run_moe(mx, d, cfg.k)
+    s1, s2 = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+    w1 = mx.workspace(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, dev, stream=s1)
+    w2 = mx.workspace(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, dev, stream=s2)
+    assert w1.data_ptr() != w2.data_ptr()
+    assert mx.workspace(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, dev, stream=s1).data_ptr() == w1.data_ptr()
+    outs = []
+    torch.cuda.synchronize()
+    for st in (s1, s2):
+        with torch.cuda.stream(st):
+            ys = [mx.moe_mxfp4_forward(d["x"], d["logits"], cfg.k, d["wgu"], d["sgu"], d["wd"], d["sd"])
+                  for _ in range(3)]
+        outs.extend(ys)
+    torch.cuda.synchronize()
+    for y in outs:
+        assert np.array_equal(to_host_bits(y), ref)
+    assert not w1[:CTL_BYTES].any().item() and not w2[:CTL_BYTES].any().item()

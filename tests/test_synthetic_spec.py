@@ -57,3 +57,12 @@ def test_spec_positions_share_a_request():
     same = np.corrcoef(lg[0], lg[1])[0, 1]
     diff = np.corrcoef(lg[0], lg[4])[0, 1]
     assert same > 0.4 and abs(diff) < 0.2
+
+
+def test_activations_are_the_nearest_bf16_of_a_normal_draw():
+    """x is bf16_rne(N(0,1)): the generator's rounding of each fp32 draw agrees with torch's
+    round-to-nearest-even cast."""
+    import torch
+    b = synthetic.bf16_bits_normal((4096,), 3)
+    f = synthetic._rng(3, synthetic.TAG_X).standard_normal(size=(4096,), dtype=np.float32)
+    assert np.array_equal(b, torch.from_numpy(f).bfloat16().view(torch.int16).numpy().view(np.uint16))
