@@ -8,17 +8,28 @@ A step is one MoE layer forward (route + sort, gate_up + SwiGLU, down + combine)
 batch of T tokens.  Steps cycle over L distinct layers (own weights, own activations and
 routing), as a decode step walks a stack of MoE layers, so no step finds its expert
 weights in a cache: the 256 MB last-level cache is smaller than the active bytes of L-1
-layers.  Inputs are resident in HBM before timing.  The timed region replays one HIP
-graph holding the L layer forwards (moe_mxfp4_forward) K/L times, between two device
-synchronizations; K is rounded up to a multiple of L.
+layers.  Inputs are resident in HBM before timing.  One HIP graph holds the L layer
+forwards (moe_mxfp4_forward); the timed region replays it K/L times between two device
+synchronizations (K rounded up to a multiple of L), with a HIP event between replays for
+the per-replay statistics.
 
-Printed: one JSON line with the layer time (us), effective weight GB/s, a roofline entry
-for the dominant kernel (gate_up) and the CPU oracle's time on a bounded sample of the same
-workload.  The kernel's launch time comes from a second pass over the same K steps right
-after the timed region, issued as the three stage calls with a HIP event between them on
-the stream the kernels run on.  roofline.traffic is the kernel's HBM bytes per launch as
-measured by the committed counter summary under profiles/, and null when the workload
-differs or the kernel's sources changed since the counters were taken.
+Before the W warm-up steps, a settle phase replays the same graph for --settle-ms of wall
+time.  After an idle spell the GPU's power management takes some 30 ms of sustained load
+to reach its steady state, and the first replays run up to a third slower; the settle
+phase is the pages' practice of warming the GPU before timed kernels ("Zyphra Inference
+Wave 2", Methodology and Limitations, Appendix B) with a length set in time rather than in
+steps.  The first replays of the settle phase are reported beside the result.
+
+Printed: one JSON line for the chosen workload -- layer time (us), effective weight GB/s
+and its share of 8 TB/s and of this GPU's measured copy and read bandwidth (the library's
+HBM reference kernels), a roofline entry for the dominant kernel (gate_up), the CPU
+oracle's time on a bounded sample of the same workload and the worst parity ratio of that
+sample against the GPU's output, and (by default) the other configurations of the
+benchmark under "configs".  The kernel's launch time comes from a pass over the same K
+steps right after the timed region, issued as the three stage calls with a HIP event
+between them on the stream the kernels run on.  roofline.traffic is the kernel's HBM bytes
+per launch as measured by the committed counter summary under profiles/, and null when the
+workload differs or the kernel's sources changed since the counters were taken.
 
 Dense workloads (dense_t1, dense_t4): a step is one mx_linear call.  The calls cycle over
 enough copies of the weights (own addresses) that their total exceeds the last-level cache
@@ -28,6 +39,7 @@ comes from HIP events around each graph replay of the timed region.
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
@@ -42,7 +54,10 @@ DENSE_METRIC = "µs per dense MXFP4 linear call (mx_linear) and effective weight
 # the dense calls cycle over weight copies totalling at least this many bytes
 DENSE_CYCLE_BYTES = 1 << 30
 HBM_PEAK_GBPS = 8000.0
+MOE_REL = 1e-2  # the MoE acceptance bound: |gpu - oracle| <= 1e-2 * sum_j g_j sum_i |h_i w_in| + 1 bf16 ulp
 ROOT = os.path.dirname(os.path.abspath(__file__))
+# the other configurations a default run reports beside its headline workload
+EXTRA_WORKLOADS = ("dense_t1", "dense_t4", "moe_t4", "moe_t128", "moe_sweep_t1")
 # sources (and build flags) the gate_up kernel is compiled from; the counter summary records
 # their hash, so measured traffic is only reported for the kernel it was measured on
 GATE_UP_SOURCES = ("mxfp4_weight_moe_amd/build.py", "mxfp4_weight_moe_amd/csrc/mx_device.hpp",
@@ -50,15 +65,18 @@ GATE_UP_SOURCES = ("mxfp4_weight_moe_amd/build.py", "mxfp4_weight_moe_amd/csrc/m
                    "mxfp4_weight_moe_amd/csrc/mx_act8.hpp", "mxfp4_weight_moe_amd/csrc/moe_policies.hpp",
                    "mxfp4_weight_moe_amd/csrc/moe_experts.hip")
 GATE_UP_COUNTERS = os.path.join(ROOT, "profiles", "moe_gate_up_kernel.moe_t32_zipf.hbm_counters.txt")
+MFMA_COUNTERS = os.path.join(ROOT, "profiles", "moe_t128.mfma_counters.txt")
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="wall time of graph replays before the warm-up steps (power-management settle)")
     ap.add_argument("--workload", default="moe_t32_zipf",
-                    help="moe_t4 | moe_t32_zipf | moe_t128 | moe_sweep_t<T>")
+                    help="moe_t4 | moe_t32_zipf | moe_t128 | moe_sweep_t<T> | dense_t1 | dense_t4 | ...")
     ap.add_argument("--layers", type=int, default=4, help="distinct layers cycled by the steps")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replay")
     ap.add_argument("--persistent", action="store_true",
@@ -68,6 +86,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32, help="tokens of the oracle's timed sample")
     ap.add_argument("--stage-steps", type=int, default=None, help="steps of the per-kernel event pass (default K)")
+    ap.add_argument("--no-extra", action="store_true", help="time only --workload (no other configurations)")
+    ap.add_argument("--extra-steps", type=int, default=80, help="timed steps of each other configuration")
+    ap.add_argument("--hbm-mib", type=int, default=4096, help="buffer of the HBM reference kernels (0: skip)")
     ap.add_argument("--copy-mib", type=int, default=1024,
                     help="size of the untimed reference copy (read + write) that calibrates HBM byte counters")
     return ap.parse_args()
@@ -93,24 +114,47 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
-def gate_up_source_hash() -> str:
+def gpu_clocks() -> dict:
+    """The active SCLK / MCLK levels the driver reports (sysfs), where readable."""
+    out = {}
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_[sm]clk")):
+        try:
+            with open(f) as fh:
+                cur = [line.split(":", 1)[1].strip(" *\n") for line in fh if "*" in line]
+            if cur:
+                out[os.path.basename(f)[len("pp_dpm_"):]] = cur[0]
+        except OSError:
+            pass
+    return out
+
+
+def source_hash(paths) -> str:
     h = hashlib.sha256()
-    for rel in GATE_UP_SOURCES:
+    for rel in paths:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per gate_up launch from the committed counter summary ("key: value" lines),
-    or None when the summary is absent, for another workload, or for other kernel sources."""
+def gate_up_source_hash() -> str:
+    return source_hash(GATE_UP_SOURCES)
+
+
+def read_summary(path):
+    """The "key: value" lines of a committed counter summary, or None."""
     try:
-        with open(GATE_UP_COUNTERS) as f:
+        with open(path) as f:
             kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith((" ", "#")))
     except OSError:
         return None
-    kv = {a.strip(): b.strip() for a, b in kv.items()}
-    if kv.get("workload") != workload or kv.get("kernel_sources_sha256") != gate_up_source_hash():
+    return {a.strip(): b.strip() for a, b in kv.items()}
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per gate_up launch from the committed counter summary, or None when the
+    summary is absent, for another workload, or for other kernel sources."""
+    kv = read_summary(GATE_UP_COUNTERS)
+    if not kv or kv.get("workload") != workload or kv.get("kernel_sources_sha256") != gate_up_source_hash():
         return None
     try:
         return int(kv["hbm_read_bytes_per_launch"]) + int(kv["hbm_write_bytes_per_launch"])
@@ -118,36 +162,79 @@ def measured_traffic(workload: str):
         return None
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this library has no multi-GPU path.",
-              file=sys.stderr)
-        sys.exit(2)
+def measured_mfma():
+    """MFMA utilisation of the expert GEMMs at T = 128 from the committed counter summary
+    (null when its kernel sources changed since)."""
+    kv = read_summary(MFMA_COUNTERS)
+    if not kv or kv.get("kernel_sources_sha256") != gate_up_source_hash():
+        return None
+    try:
+        return {"workload": kv["workload"], "gate_up_mfma_busy_pct": float(kv["gate_up_mfma_busy_pct"]),
+                "down_mfma_busy_pct": float(kv["down_mfma_busy_pct"]),
+                "gate_up_useful_tflops": float(kv["gate_up_useful_tflops"]),
+                "source": os.path.relpath(MFMA_COUNTERS, ROOT)}
+    except (KeyError, ValueError):
+        return None
 
-    import torch
-    if not torch.cuda.is_available():
-        raise SystemExit("bench.py needs a GPU")
-    import mxfp4_weight_moe_amd as mx  # raises if the HIP library is not built
+
+def stats_us(v):
+    a = np.asarray(v, np.float64)
+    return {"n": int(a.size), "mean": round(float(a.mean()), 2), "median": round(float(np.median(a)), 2),
+            "p10": round(float(np.percentile(a, 10)), 2), "p90": round(float(np.percentile(a, 90)), 2)}
+
+
+def moe_bound_ratio(gpu_bits, ora_bits, scale):
+    """Worst |gpu - oracle| / (1e-2 * scale + 1 bf16 ulp) over the finite outputs, and the
+    number of outputs whose NaN / Inf status differs."""
+    def f(b):
+        return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    g, o = f(gpu_bits), f(ora_bits)
+    fin = np.isfinite(g) & np.isfinite(o)
+    mismatch = int(((np.isnan(g) != np.isnan(o)) | ((np.isinf(g) | np.isinf(o)) & ~fin & (g != o))).sum())
+    m = np.maximum(np.abs(g[fin]), np.abs(o[fin]))
+    small = m < 2.0 ** -126
+    ulp = np.where(small, 2.0 ** -133, 2.0 ** (np.floor(np.log2(np.where(small, 1.0, m))) - 7))
+    ratio = np.abs(g[fin] - o[fin]) / (MOE_REL * np.asarray(scale, np.float64)[fin] + ulp)
+    return (float(ratio.max()) if ratio.size else 0.0), mismatch
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def settle(replay, stream, torch, settle_ms: float, units: int, record: int = 8):
+    """Replays back to back for settle_ms of wall time, at most two in flight (so the host
+    never queues more work than that); returns (replays, the first `record` replays' us per
+    unit: per layer, or per call)."""
+    timed = [torch.cuda.Event(enable_timing=True) for _ in range(record + 1)]
+    lag = [torch.cuda.Event(), torch.cuda.Event()]
+    timed[0].record(stream)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        if n >= 2:
+            lag[n % 2].synchronize()  # replay n - 2 has finished
+        replay()
+        lag[n % 2].record(stream)
+        n += 1
+        if n <= record:
+            timed[n].record(stream)
+        if n >= record and (time.perf_counter() - t0) * 1e3 >= settle_ms:
+            break
+    torch.cuda.synchronize()
+    first = [round(timed[i].elapsed_time(timed[i + 1]) * 1e3 / units, 2) for i in range(record)]
+    return n, first
+
+
+# ------------------------------------------------------------------------------ MoE workloads
+
+def moe_case(cfg, args, torch, mx, dev, *, steps: int, warmup: int, stage_pass: bool, cpu_leg: bool):
+    """Times one MoE workload; returns its result dict (the JSON line's fields)."""
     import synthetic
-
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    if args.workload in synthetic.LINEAR_CONFIGS:
-        return dense_main(args, synthetic.LINEAR_CONFIGS[args.workload], torch, mx, dev)
-    cfg = workload_config(args.workload)
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
     ns = cfg.n_shared
-    if args.persistent and (T > 16 or T * k > 128 or ns or args.act8):
-        raise SystemExit("--persistent takes T <= 16, T * top_k <= 128, no shared experts and bf16 activations")
-    # the event pass times each layer as a whole when the stage calls cannot reproduce it
     whole_layer = args.persistent or ns > 0 or args.act8
     L = max(1, args.layers)
-
-    def log(*a):
-        print(*a, file=sys.stderr, flush=True)
-
-    # ---------------------------------------------------------------- set-up (all before timing)
     log(f"[bench] workload {cfg.name}: T={T} H={H} I={I} E={E} k={k} routing={cfg.routing} layers={L}")
     layers = []
     for li in range(L):
@@ -161,7 +248,6 @@ def main():
             x_bits=x_bits, logits_host=logits,
         ))
     ws = mx.workspace(T, H, I, E + ns, k + ns, dev)
-    # buffers of the stage-by-stage pass
     ids = torch.empty((T, k), dtype=torch.int32, device=dev)
     gates = torch.empty((T, k), dtype=torch.float32, device=dev)
     srt = dict(counts=torch.empty(E, dtype=torch.int32, device=dev),
@@ -180,7 +266,7 @@ def main():
     def forward(lay):
         w = lay["w"]
         mx.moe_mxfp4_forward(lay["x"], lay["logits"], k, w["wgu"], w["sgu"], w["wd"], w["sd"], out=lay["y"], ws=ws,
-                             persistent=args.persistent, n_shared=ns, act8=args.act8)
+                             persistent=args.persistent, n_shared=ns, act8=args.act8, check=False)
 
     def staged(i, e, stream):
         lay = layers[i % L]
@@ -204,7 +290,7 @@ def main():
 
     # Untimed reference copy of a known size: under a counter profiler its FETCH_SIZE and
     # WRITE_SIZE give the scale between the counters and bytes actually moved.
-    if args.copy_mib > 0:
+    if stage_pass and args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 18, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
         dst.copy_(src)
@@ -224,46 +310,36 @@ def main():
         torch.cuda.current_stream(dev).wait_stream(side)
         torch.cuda.synchronize()
 
-    def run_steps(n):  # n is a multiple of L
-        for _ in range(n // L):
-            if graph is not None:
-                graph.replay()
-            else:
-                for lay in layers:
-                    forward(lay)
+    def replay():
+        if graph is not None:
+            graph.replay()
+        else:
+            for lay in layers:
+                forward(lay)
 
-    # ---------------------------------------------------------------- warm-up and timed region
-    # Warm-up long enough for the clocks to settle: kernel times drift down over the
-    # first tens of milliseconds of back-to-back work after an idle GPU.
-    run_steps(L * max(1, -(-args.warmup // L)))
-    reps = max(1, -(-args.steps // L))
+    stream = torch.cuda.current_stream(dev)
+    # ---------------------------------------------------------------- settle, warm-up, timed region
+    clocks_before = gpu_clocks()
+    n_settle, first = settle(replay, stream, torch, args.settle_ms, L)
+    for _ in range(max(0, -(-warmup // L))):
+        replay()
+    reps = max(1, -(-steps // L))
     K = reps * L
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    run_steps(K)
+    evs[0].record(stream)
+    for r in range(reps):
+        replay()
+        evs[r + 1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    clocks_after = gpu_clocks()
     ms_per_step = (t1 - t0) * 1e3 / K
-    log(f"[bench] timed {K} steps: {ms_per_step * 1e3:.1f} us/layer")
+    replay_us = [evs[r].elapsed_time(evs[r + 1]) * 1e3 / L for r in range(reps)]
+    log(f"[bench] {cfg.name}: settle {n_settle} replays (first {first}); timed {K} steps: "
+        f"{ms_per_step * 1e3:.1f} us/layer")
 
-    # ---------------------------------------------------------------- per-kernel pass (HIP events)
-    # Right after the timed region, the same K layer forwards issued as the three stage calls
-    # (the kernels the forward launches), with a HIP event between stages recorded on the
-    # stream the kernels are launched on.  Launches are queued far faster than the GPU
-    # drains them, so the stream never runs dry and each event pair brackets one kernel.
-    stream = torch.cuda.current_stream(dev)
-    KS = args.stage_steps or K
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(KS)]
-    for i in range(KS):
-        staged(i, evs[i], stream)
-    torch.cuda.synchronize()
-    stage_ms = {n: [] for n in names}
-    for e in evs:
-        for j, n in enumerate(names):
-            stage_ms[n].append(e[j].elapsed_time(e[j + 1]))
-    staged_us_per_layer = evs[0][0].elapsed_time(evs[-1][-1]) * 1e3 / KS
-
-    # ---------------------------------------------------------------- bytes and roofline
     gu_expert = 2 * I * H // 2 + 2 * I * H // 32          # gate_up codes + scales per expert
     dn_expert = H * I // 2 + H * I // 32                  # down codes + scales per expert
     act_bytes = T * H * 2 + T * E * 4 + T * H * 2         # x, router logits, y
@@ -271,68 +347,13 @@ def main():
     mean_layer_bytes = float(np.mean([layer_bytes[i % L] for i in range(K)]))
     us_per_layer = ms_per_step * 1e3
     eff_gbps = mean_layer_bytes / (us_per_layer * 1e-6) / 1e9
-    if whole_layer:
-        # the single kernel (or the layer's launches together) reads the whole layer's bytes
-        gu_bytes = [layer_bytes[i % L] for i in range(KS)]
-        gu_ms = stage_ms["layer"]
-    else:
-        # gate_up per launch: its experts' codes + scales, x read once, h written
-        gu_bytes = [n_active[i % L] * gu_expert + T * H * 2 + T * k * I * 2 for i in range(KS)]
-        gu_ms = stage_ms["gate_up"]
-    gu_achieved = float(np.sum(gu_bytes) / (np.sum(gu_ms) * 1e-3) / 1e9)
-    roofline = {
-        "kernel": ("moe_fused_kernel" if args.persistent else "layer (all launches)") if whole_layer
-        else "moe_gate_up_kernel",
-        "bound": "hbm",
-        "achieved": round(gu_achieved, 1),
-        "peak": HBM_PEAK_GBPS,
-        "unit": "GB/s",
-        "frac": round(gu_achieved / HBM_PEAK_GBPS, 4),
-        "traffic": None if whole_layer else measured_traffic(cfg.name),
-        "avg_launch_us": round(float(np.mean(gu_ms)) * 1e3, 2),
-        "launches": len(gu_ms),
-        "timing": "HIP events on the launch stream, one pair per launch, right after the timed region",
-        "bytes_per_launch": int(np.mean(gu_bytes)),
-    }
-
-    # ---------------------------------------------------------------- CPU oracle baseline
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-        lay = layers[0]
-        n = max(1, min(args.cpu_tokens, T))
-        toks = np.arange(n, dtype=np.int32)
-        w_host = {key: lay["w"][key].cpu().numpy() for key in ("wgu", "sgu", "wd", "sd")}
-        threads = oracle.default_threads()
-        log(f"[bench] oracle on {n} of {T} tokens, {threads} threads")
-        c0 = time.perf_counter()
-        oracle.moe_tokens(lay["x_bits"], lay["logits_host"], k, w_host["wgu"], w_host["sgu"], w_host["wd"],
-                          w_host["sd"], T, H, I, E, tokens=toks, nthreads=threads, n_shared=ns, act8=args.act8)
-        c1 = time.perf_counter()
-        cpu = {
-            "value": round((c1 - c0) * (T / n) * 1e6, 1),
-            "unit": "us/layer",
-            "cores": threads,
-            "kind": "oracle",
-            "sample": f"layer 0, tokens 0..{n - 1} of {T} (all {k} routed experts each), full route+gate_up+down+combine; "
-                      f"time scaled by {T}/{n}; CPU: {cpu_model()}",
-            "seconds": round(c1 - c0, 2),
-        }
-        del w_host
-
-    out = {
-        "metric": METRIC,
-        "value": round(us_per_layer, 2),
-        "unit": "us/layer",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": False,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp8 (E4M3) x fp4 (E2M1), fp32 accumulate" if args.act8 else "bf16",
-        "data": "synthetic",
+    res = {
+        "value": round(us_per_layer, 2), "K": K, "ms_per_step": round(ms_per_step, 5),
+        "effective_GBps": round(eff_gbps, 1), "pct_of_8TBps": round(100 * eff_gbps / HBM_PEAK_GBPS, 2),
+        "active_experts": n_active, "algorithmic_bytes_per_layer": int(mean_layer_bytes),
+        "replay_us_per_layer": stats_us(replay_us),
+        "settle": {"ms": args.settle_ms, "replays": n_settle, "first_replays_us_per_layer": first},
+        "clocks": {"before": clocks_before, "after": clocks_after},
         "config": {
             "workload": cfg.name, "T": T, "H": H, "I": I, "E": E, "top_k": k, "n_shared": ns, "routing": cfg.routing,
             "weights": "MXFP4 (E2M1 codes, E8M0 scale per 32)", "accumulate": "fp32",
@@ -340,27 +361,84 @@ def main():
             "layers_cycled": L, "timing": "eager launches" if args.eager else "HIP graph replay",
             "path": "one persistent launch" if args.persistent else "route_sort, gate_up, down, combine launches",
         },
-        "effective_GBps": round(eff_gbps, 1),
-        "pct_of_8TBps": round(100 * eff_gbps / HBM_PEAK_GBPS, 2),
-        "active_experts": n_active,
-        "algorithmic_bytes_per_layer": int(mean_layer_bytes),
-        "stages_us": {n: round(float(np.mean(v)) * 1e3, 2) for n, v in stage_ms.items()},
-        "staged_us_per_layer": round(staged_us_per_layer, 2),
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-        "env": {"GPU_MAX_HW_QUEUES": os.environ.get("GPU_MAX_HW_QUEUES"), "torch": torch.__version__,
-                "hip": getattr(torch.version, "hip", None)},
     }
-    print(json.dumps(out), flush=True)
+
+    # ---------------------------------------------------------------- per-kernel pass (HIP events)
+    # Right after the timed region, the same K layer forwards issued as the three stage calls
+    # (the kernels the forward launches), with a HIP event between stages recorded on the
+    # stream the kernels are launched on.  Launches are queued far faster than the GPU
+    # drains them, so the stream never runs dry and each event pair brackets one kernel.
+    if stage_pass:
+        KS = args.stage_steps or K
+        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(KS)]
+        for i in range(KS):
+            staged(i, sev[i], stream)
+        torch.cuda.synchronize()
+        stage_ms = {n: [] for n in names}
+        for e in sev:
+            for j, n in enumerate(names):
+                stage_ms[n].append(e[j].elapsed_time(e[j + 1]))
+        if whole_layer:
+            gu_bytes = [layer_bytes[i % L] for i in range(KS)]
+            gu_ms = stage_ms["layer"]
+        else:
+            # gate_up per launch: its experts' codes + scales, x read once, h written
+            gu_bytes = [n_active[i % L] * gu_expert + T * H * 2 + T * k * I * 2 for i in range(KS)]
+            gu_ms = stage_ms["gate_up"]
+        gu_achieved = float(np.sum(gu_bytes) / (np.sum(gu_ms) * 1e-3) / 1e9)
+        res["stages_us"] = {n: round(float(np.mean(v)) * 1e3, 2) for n, v in stage_ms.items()}
+        res["staged_us_per_layer"] = round(sev[0][0].elapsed_time(sev[-1][-1]) * 1e3 / KS, 2)
+        res["roofline"] = {
+            "kernel": ("moe_fused_kernel" if args.persistent else "layer (all launches)") if whole_layer
+            else "moe_gate_up_kernel",
+            "bound": "hbm", "achieved": round(gu_achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(gu_achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None if whole_layer else measured_traffic(cfg.name),
+            "avg_launch_us": round(float(np.mean(gu_ms)) * 1e3, 2), "launches": len(gu_ms),
+            "timing": "HIP events on the launch stream, one pair per launch, right after the timed region",
+            "bytes_per_launch": int(np.mean(gu_bytes)),
+        }
+
+    # ---------------------------------------------------------------- CPU oracle: baseline and parity
+    if cpu_leg:
+        import oracle
+        lay = layers[0]
+        lay["y"].fill_(float("nan"))
+        forward(lay)
+        torch.cuda.synchronize()
+        y_gpu = lay["y"].view(torch.int16).cpu().numpy().view(np.uint16)
+        n = max(1, min(args.cpu_tokens, T))
+        toks = np.arange(n, dtype=np.int32)
+        w_host = {key: lay["w"][key].cpu().numpy() for key in ("wgu", "sgu", "wd", "sd")}
+        threads = oracle.default_threads()
+        log(f"[bench] oracle on {n} of {T} tokens, {threads} threads")
+        c0 = time.perf_counter()
+        y_ora, scale, _ = oracle.moe_tokens(lay["x_bits"], lay["logits_host"], k, w_host["wgu"], w_host["sgu"],
+                                            w_host["wd"], w_host["sd"], T, H, I, E, tokens=toks, nthreads=threads,
+                                            n_shared=ns, act8=args.act8)
+        c1 = time.perf_counter()
+        worst, mismatch = moe_bound_ratio(y_gpu[:n], y_ora, scale)
+        res["cpu_baseline"] = {
+            "value": round((c1 - c0) * (T / n) * 1e6, 1), "unit": "us/layer", "cores": threads, "kind": "oracle",
+            "sample": f"layer 0, tokens 0..{n - 1} of {T} (all {k} routed experts each), full route+gate_up+down+"
+                      f"combine; time scaled by {T}/{n}; CPU: {cpu_model()}",
+            "seconds": round(c1 - c0, 2),
+        }
+        res["parity"] = {"tokens": n, "outputs": int(n * H), "worst_ratio": round(worst, 4),
+                         "nan_inf_mismatches": mismatch, "ok": bool(worst <= 1.0 and mismatch == 0),
+                         "bound": "|gpu - oracle| <= 1e-2 * sum_j gate_j sum_i |h_i w_in| + 1 bf16 ulp, per output; "
+                                  "worst_ratio = max |gpu - oracle| / bound over the sample"}
+        del w_host
+    del layers, ws, h
+    torch.cuda.empty_cache()
+    return res
 
 
-def dense_main(args, cfg, torch, mx, dev):
-    """The dense layer: y[T,N] = bf16(x[T,K] @ W[N,K]^T) with MXFP4 W, one call per step."""
+# ------------------------------------------------------------------------------ dense workloads
+
+def dense_case(cfg, args, torch, mx, dev, *, steps: int, warmup: int, cpu_leg: bool):
+    """y[T,N] = bf16(x[T,K] @ W[N,K]^T) with MXFP4 W, one call per step."""
     import synthetic
-
-    def log(*a):
-        print(*a, file=sys.stderr, flush=True)
-
     T, K, N = cfg.T, cfg.K, cfg.N
     x_bits, w, s = synthetic.linear_inputs(cfg)
     w_bytes = w.nbytes + s.nbytes
@@ -387,13 +465,15 @@ def dense_main(args, cfg, torch, mx, dev):
                 call(i)
     torch.cuda.current_stream(dev).wait_stream(side)
     torch.cuda.synchronize()
-    for _ in range(max(1, -(-args.warmup // copies))):
+    stream = torch.cuda.current_stream(dev)
+    clocks_before = gpu_clocks()
+    n_settle, first = settle(graph.replay, stream, torch, args.settle_ms, copies)
+    for _ in range(max(0, -(-warmup // copies))):
         graph.replay()
-    reps = max(1, -(-args.steps // copies))
+    reps = max(2, -(-steps // copies))
     nsteps = reps * copies
     # HIP events on the replay stream bracket each replay of the graph: a call is shorter than
     # its host-side submission, so eager event pairs would time the host, not the kernel
-    stream = torch.cuda.current_stream(dev)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -404,14 +484,28 @@ def dense_main(args, cfg, torch, mx, dev):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     us_per_call = (t1 - t0) * 1e6 / nsteps
-    log(f"[bench] timed {nsteps} calls: {us_per_call:.2f} us/call")
-    call_ms = [evs[r].elapsed_time(evs[r + 1]) / copies for r in range(reps)]
+    log(f"[bench] {cfg.name}: timed {nsteps} calls: {us_per_call:.2f} us/call")
+    call_us = [evs[r].elapsed_time(evs[r + 1]) * 1e3 / copies for r in range(reps)]
     call_bytes = w_bytes + T * K * 2 + T * N * 2  # weights, x, y
-    achieved = call_bytes / (float(np.mean(call_ms)) * 1e-3) / 1e9
+    achieved = call_bytes / (float(np.mean(call_us)) * 1e-6) / 1e9
     eff_gbps = call_bytes / (us_per_call * 1e-6) / 1e9
-
-    cpu = None
-    if not args.no_cpu_baseline:
+    res = {
+        "value": round(us_per_call, 3), "K": nsteps, "ms_per_step": round(us_per_call * 1e-3, 6),
+        "effective_GBps": round(eff_gbps, 1), "pct_of_8TBps": round(100 * eff_gbps / HBM_PEAK_GBPS, 2),
+        "algorithmic_bytes_per_call": call_bytes, "replay_us_per_call": stats_us(call_us),
+        "settle": {"ms": args.settle_ms, "replays": n_settle, "first_replays_us_per_call": first},
+        "clocks": {"before": clocks_before, "after": gpu_clocks()},
+        "config": {"workload": cfg.name, "T": T, "K": K, "N": N, "weights": "MXFP4 (E2M1 codes, E8M0 scale per 32)",
+                   "activations": "MXFP8, quantized in the kernel" if args.act8 else "bf16", "accumulate": "fp32",
+                   "weight_copies_cycled": copies, "timing": "HIP graph replay"},
+        "roofline": {"kernel": "mx_linear_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "avg_launch_us": round(float(np.mean(call_us)), 3), "launches": nsteps,
+                     "timing": "HIP events on the replay stream around each graph replay of the timed region, "
+                               "per call (includes the graph's gaps between kernels)",
+                     "bytes_per_launch": call_bytes},
+    }
+    if cpu_leg:
         import oracle
         threads = oracle.default_threads()
         fn = oracle.mx_linear_a8 if args.act8 else oracle.mx_linear
@@ -420,39 +514,132 @@ def dense_main(args, cfg, torch, mx, dev):
         for _ in range(reps_cpu):
             fn(x_bits, w, s, T, K, N, nthreads=threads)
         c1 = time.perf_counter()
-        cpu = {"value": round((c1 - c0) / reps_cpu * 1e6, 1), "unit": "us/call", "cores": threads, "kind": "oracle",
-               "sample": f"the whole call, {reps_cpu} repetitions averaged; CPU: {cpu_model()}",
-               "seconds": round(c1 - c0, 2)}
+        res["cpu_baseline"] = {"value": round((c1 - c0) / reps_cpu * 1e6, 1), "unit": "us/call", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"the whole call, {reps_cpu} repetitions averaged; CPU: {cpu_model()}",
+                               "seconds": round(c1 - c0, 2)}
+    del ws, ys, graph
+    torch.cuda.empty_cache()
+    return res
 
+
+# ------------------------------------------------------------------------------ HBM yardsticks
+
+def hbm_reference(args, torch, mx, dev, reps: int = 30):
+    """This GPU's streaming-read and copy bandwidth with the library's reference kernels
+    (mx_hbm_read, mx_hbm_copy) over --hbm-mib MiB, after their own settle; medians."""
+    nbytes = args.hbm_mib << 20
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    src.fill_(0x5A)
+    dst = torch.empty_like(src)
+    xor = torch.zeros(4, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    out = {"bytes": nbytes}
+    for name, fn, moved in (("read", lambda: mx.hbm_read(src, xor, clear=False), nbytes),
+                            ("copy", lambda: mx.hbm_copy(dst, src), 2 * nbytes)):
+        settle(fn, stream, torch, min(args.settle_ms, 200.0), 1, record=1)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        evs[0].record(stream)
+        for r in range(reps):
+            fn()
+            evs[r + 1].record(stream)
+        torch.cuda.synchronize()
+        us = [evs[r].elapsed_time(evs[r + 1]) * 1e3 for r in range(reps)]
+        med = float(np.median(us))
+        out[f"{name}_GBps"] = round(moved / (med * 1e-6) / 1e9, 1)
+        out[f"{name}_us_median"] = round(med, 2)
+    out["kernels"] = ("mx_hbm_read (16-byte nontemporal loads, XOR kept live), mx_hbm_copy (bytes read + written); "
+                      "timed right after the headline workload")
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this library has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    import mxfp4_weight_moe_amd as mx  # raises if the HIP library is not built
+    import synthetic
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dense = args.workload in synthetic.LINEAR_CONFIGS
+    if dense:
+        head = dense_case(synthetic.LINEAR_CONFIGS[args.workload], args, torch, mx, dev, steps=args.steps,
+                          warmup=args.warmup, cpu_leg=not args.no_cpu_baseline)
+    else:
+        if args.persistent:
+            c = workload_config(args.workload)
+            if c.T > 16 or c.T * c.k > 128 or c.n_shared or args.act8:
+                raise SystemExit("--persistent takes T <= 16, T * top_k <= 128, no shared experts and bf16 "
+                                 "activations")
+        head = moe_case(workload_config(args.workload), args, torch, mx, dev, steps=args.steps, warmup=args.warmup,
+                        stage_pass=True, cpu_leg=not args.no_cpu_baseline)
+
+    hbm = hbm_reference(args, torch, mx, dev) if args.hbm_mib > 0 else None
+
+    extras = {}
+    if not args.no_extra and not args.persistent:
+        for name in EXTRA_WORKLOADS:
+            if name == args.workload:
+                continue
+            if name in synthetic.LINEAR_CONFIGS:
+                r = dense_case(synthetic.LINEAR_CONFIGS[name], args, torch, mx, dev, steps=max(args.extra_steps, 1000),
+                               warmup=args.warmup, cpu_leg=False)
+                extras[name] = {"us_per_call": r["value"], "replay_us_per_call": r["replay_us_per_call"],
+                                "effective_GBps": r["effective_GBps"], "pct_of_8TBps": r["pct_of_8TBps"],
+                                "bytes": r["algorithmic_bytes_per_call"], "config": r["config"]}
+            else:
+                r = moe_case(workload_config(name), args, torch, mx, dev, steps=args.extra_steps, warmup=args.warmup,
+                             stage_pass=False, cpu_leg=False)
+                extras[name] = {"us_per_layer": r["value"], "replay_us_per_layer": r["replay_us_per_layer"],
+                                "effective_GBps": r["effective_GBps"], "pct_of_8TBps": r["pct_of_8TBps"],
+                                "active_experts": r["active_experts"], "bytes": r["algorithmic_bytes_per_layer"],
+                                "config": r["config"]}
+
+    unit = "us/call" if dense else "us/layer"
     out = {
-        "metric": DENSE_METRIC,
-        "value": round(us_per_call, 3),
-        "unit": "us/call",
+        "metric": DENSE_METRIC if dense else METRIC,
+        "value": head["value"],
+        "unit": unit,
         "n_gpus": 1,
-        "steps": nsteps,
+        "steps": head["K"],
         "warmup": args.warmup,
-        "ms_per_step": round(us_per_call * 1e-3, 6),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8 (E4M3) x fp4 (E2M1), fp32 accumulate" if args.act8 else "bf16",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "T": T, "K": K, "N": N, "weights": "MXFP4 (E2M1 codes, E8M0 scale per 32)",
-                   "activations": "MXFP8, quantized in the kernel" if args.act8 else "bf16", "accumulate": "fp32",
-                   "weight_copies_cycled": copies, "timing": "HIP graph replay"},
-        "effective_GBps": round(eff_gbps, 1),
-        "pct_of_8TBps": round(100 * eff_gbps / HBM_PEAK_GBPS, 2),
-        "algorithmic_bytes_per_call": call_bytes,
-        "roofline": {"kernel": "mx_linear_kernel", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "avg_launch_us": round(float(np.mean(call_ms)) * 1e3, 3), "launches": nsteps,
-                     "timing": "HIP events on the replay stream around each graph replay of the timed region, "
-                               "per call (includes the graph's gaps between kernels)",
-                     "bytes_per_launch": call_bytes},
-        "cpu_baseline": cpu,
-        "env": {"GPU_MAX_HW_QUEUES": os.environ.get("GPU_MAX_HW_QUEUES"), "torch": torch.__version__,
-                "hip": getattr(torch.version, "hip", None)},
+        "config": head["config"],
+        "effective_GBps": head["effective_GBps"],
+        "pct_of_8TBps": head["pct_of_8TBps"],
     }
+    if hbm:
+        out["pct_of_copy"] = round(100 * head["effective_GBps"] / hbm["copy_GBps"], 2)
+        out["pct_of_read"] = round(100 * head["effective_GBps"] / hbm["read_GBps"], 2)
+        out["copy_GBps"] = hbm["copy_GBps"]
+    for key in ("active_experts", "algorithmic_bytes_per_layer", "algorithmic_bytes_per_call", "stages_us",
+                "staged_us_per_layer", "replay_us_per_layer", "replay_us_per_call", "settle", "clocks"):
+        if key in head:
+            out[key] = head[key]
+    out["roofline"] = head["roofline"]
+    out["cpu_baseline"] = head.get("cpu_baseline")
+    if "parity" in head:
+        out["parity"] = head["parity"]
+    out["hbm_reference"] = hbm
+    if not dense:
+        out["mfma_t128"] = measured_mfma()
+    out["configs"] = extras
+    out["env"] = {"GPU_MAX_HW_QUEUES": os.environ.get("GPU_MAX_HW_QUEUES"), "torch": torch.__version__,
+                  "hip": getattr(torch.version, "hip", None), "device": torch.cuda.get_device_name(dev)}
     print(json.dumps(out), flush=True)
 
 

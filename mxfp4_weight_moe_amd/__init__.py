@@ -139,9 +139,10 @@ def mx_linear(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor,
     return out
 
 
-def hbm_read(src: torch.Tensor, xor_out: torch.Tensor | None = None) -> torch.Tensor:
+def hbm_read(src: torch.Tensor, xor_out: torch.Tensor | None = None, clear: bool = True) -> torch.Tensor:
     """HBM reference read of a contiguous device tensor (size a multiple of 16 bytes):
-    returns int32 [4], word c = XOR of 32-bit word c of every 16-byte piece."""
+    returns int32 [4], word c = XOR of 32-bit word c of every 16-byte piece (XORed into
+    xor_out, which is zeroed first unless clear=False)."""
     if not src.is_cuda or not src.is_contiguous():
         raise ValueError("src must be a contiguous device tensor")
     dev = src.device
@@ -149,7 +150,8 @@ def hbm_read(src: torch.Tensor, xor_out: torch.Tensor | None = None) -> torch.Te
         xor_out = torch.zeros(4, dtype=torch.int32, device=dev)
     else:
         _check(xor_out, "xor_out", torch.int32, 1, dev)
-        xor_out.zero_()
+        if clear:
+            xor_out.zero_()
     nbytes = src.numel() * src.element_size()
     st = _lib.mx_hbm_read(_ptr(src), nbytes, _ptr(xor_out), _stream(dev))
     _raise(st, "mx_hbm_read")
