@@ -49,7 +49,8 @@ enum mx_status {
   MX_ERR_SHAPE = -2,     /* a size is out of range or not a required multiple */
   MX_ERR_ALIGN = -3,     /* a pointer is not aligned as required */
   MX_ERR_WORKSPACE = -4, /* workspace missing or smaller than moe_mxfp4_workspace_size */
-  MX_ERR_HIP = -5        /* the HIP runtime reported an error while enqueueing */
+  MX_ERR_HIP = -5,       /* the HIP runtime reported an error while enqueueing */
+  MX_ERR_SCRATCH = -6    /* moe_mxfp4_forward_noalloc: the call needs more than its static scratch */
 };
 
 /* Limits checked by every call. */
@@ -232,6 +233,27 @@ MX_API int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, int6
                       const uint8_t* s_gate_up, const uint8_t* w_down, const uint8_t* s_down, uint16_t* y,
                       int64_t T, int64_t H, int64_t I, int64_t E, void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/*
+ * For callers that cannot allocate device memory -- code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation: moe_mxfp4_forward without a workspace
+ * argument.  Its scratch (the sort, h and the fp32 down outputs, as in the workspace) is a
+ * static device array of MX_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds
+ * until the process ends; the call allocates nothing.  Results are bit for bit those of
+ * moe_mxfp4_forward.  Arguments and limits as for moe_mxfp4_forward, and:
+ *   - MX_ERR_SCRATCH when moe_mxfp4_workspace_size(T, H, I, E, top_k) exceeds
+ *     MX_NOALLOC_SCRATCH_BYTES (it holds T = 128 tokens, top-8, H = 7168, I = 2048,
+ *     E = 384; not T * top_k much beyond 1024 slots at H = 7168);
+ *   - every call on one GPU shares that GPU's array: calls that overlap in time on one
+ *     GPU (two streams, or two host threads) race and give undefined results;
+ *   - the first call on a GPU also enqueues, on `stream`, a kernel that zeroes the
+ *     array's control words.
+ */
+#define MX_NOALLOC_SCRATCH_BYTES (40 << 20)
+MX_API int moe_mxfp4_forward_noalloc(const uint16_t* x, const float* router_logits, int64_t top_k,
+                                     const uint8_t* w_gate_up, const uint8_t* s_gate_up, const uint8_t* w_down,
+                                     const uint8_t* s_down, uint16_t* y, int64_t T, int64_t H, int64_t I, int64_t E,
+                                     void* stream);
 
 /*
  * The MoE layer with shared experts: every token reads its top_k routed experts (of E,

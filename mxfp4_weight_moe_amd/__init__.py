@@ -52,19 +52,22 @@ _lib.moe_mxfp4_forward_shared.argtypes = [_P, _P, _I64, _I64, _P, _P, _P, _P, _P
 _lib.moe_mxfp4_forward_a8.argtypes = list(_lib.moe_mxfp4_forward_shared.argtypes)
 _lib.mx_linear_a8.argtypes = list(_lib.mx_linear.argtypes)
 _lib.mxfp8_quantize.argtypes = [_P, _I64, _I64, _P, _P, _P]
+_lib.moe_mxfp4_forward_noalloc.argtypes = [_P, _P, _I64, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]
 _lib.mx_hbm_read.argtypes = [_P, ctypes.c_size_t, _P, _P]
 _lib.mx_hbm_copy.argtypes = [_P, _P, ctypes.c_size_t, _P]
 for _n in ("mx_linear", "mxfp4_dequantize", "moe_route_topk", "moe_sort_by_expert", "moe_route_sort",
            "moe_gate_up_swiglu", "moe_down_combine", "moe_mxfp4_forward", "moe_mxfp4_forward_persistent",
            "moe_mxfp4_forward_shared", "moe_mxfp4_forward_a8", "mx_linear_a8", "mxfp8_quantize", "mx_hbm_read",
-           "mx_hbm_copy"):
+           "mx_hbm_copy", "moe_mxfp4_forward_noalloc"):
     getattr(_lib, _n).restype = ctypes.c_int
 
 EXPORTED = ("mx_version", "mx_status_string", "mx_linear", "mxfp4_dequantize", "moe_route_topk",
             "moe_sort_by_expert", "moe_route_sort", "moe_gate_up_swiglu", "moe_down_combine",
             "moe_mxfp4_workspace_size", "moe_mxfp4_forward", "moe_mxfp4_forward_persistent",
             "moe_mxfp4_forward_shared", "moe_mxfp4_forward_a8", "mx_linear_a8", "mxfp8_quantize", "mx_hbm_read",
-            "mx_hbm_copy")
+            "mx_hbm_copy", "moe_mxfp4_forward_noalloc")
+MX_ERR_SCRATCH = -6
+MX_NOALLOC_SCRATCH_BYTES = 40 << 20
 
 
 class MxError(RuntimeError):

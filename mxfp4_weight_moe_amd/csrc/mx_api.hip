@@ -2,6 +2,7 @@
 // Every check runs before anything is enqueued; no call allocates or synchronizes.
 #include <atomic>
 #include <limits>
+#include <mutex>
 
 #include "mx_internal.hpp"
 
@@ -66,6 +67,47 @@ static int check_expert_dims(int64_t H, int64_t I) {
   return MX_OK;
 }
 
+// ------------------------------------------------------------------ static scratch
+
+// The scratch of moe_mxfp4_forward_noalloc, for callers that cannot allocate: one array
+// per GPU (each device that loads the library holds its own copy until the process ends).
+// Host code never uses this name as an address: it is a host-side stand-in for the device
+// symbol.  noalloc_scratch() looks the array's device address up once per device, with
+// hipGetSymbolAddress, and every later use goes through that address.
+static __device__ __align__(256) uint8_t scratch[MX_NOALLOC_SCRATCH_BYTES];
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+
+// Zeroes `words` int32 words (the workspace control words the expert GEMMs count in).
+__global__ void __launch_bounds__(256) zero_words_kernel(int32_t* __restrict__ p, int words) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < words) p[i] = 0;
+}
+
+// The current device's scratch address.  On a device's first call it also enqueues, on
+// `stream`, a kernel that zeroes the control words at the array's start (the array is
+// zero when the code object loads, and every forward leaves them zero; this makes the
+// first call independent of that).  A kernel rather than a memset, so that a first call
+// under graph capture records an ordinary kernel node.
+static int noalloc_scratch(void** out, hipStream_t stream) {
+  static std::mutex mu;
+  static void* addr[NOALLOC_MAX_DEVICES];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NOALLOC_MAX_DEVICES) return MX_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MX_ERR_HIP;
+    const int words = MX_WORKSPACE_CTL_BYTES / 4;
+    hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, stream, static_cast<int32_t*>(p),
+                       words);
+    if (hipGetLastError() != hipSuccess) return MX_ERR_HIP;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return MX_OK;
+}
+
 static bool sort_view_ok(const int32_t* counts, const int32_t* offsets, const int32_t* sorted_slots,
                          const int32_t* active, const int32_t* num_active) {
   return counts && offsets && sorted_slots && active && num_active;
@@ -93,6 +135,7 @@ const char* mx_status_string(int status) {
     case MX_ERR_ALIGN: return "a pointer is not aligned as required";
     case MX_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case MX_ERR_HIP: return "the HIP runtime reported an error while enqueueing";
+    case MX_ERR_SCRATCH: return "the call needs more scratch than the library's static array holds";
     default: return "unknown status";
   }
 }
@@ -217,10 +260,10 @@ size_t moe_mxfp4_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int6
 
 // The layer over E routed experts (top_k of them per token) and ns shared experts after them;
 // act8: MXFP8 activations for both expert GEMMs.
-static int moe_forward_impl(const uint16_t* x, const float* router_logits, int64_t top_k, int64_t ns,
+// The checks of the layer forward's arguments other than the workspace.
+static int moe_forward_args(const uint16_t* x, const float* router_logits, int64_t top_k, int64_t ns,
                             const uint8_t* w_gate_up, const uint8_t* s_gate_up, const uint8_t* w_down,
-                            const uint8_t* s_down, uint16_t* y, int64_t T, int64_t H, int64_t I, int64_t E,
-                            void* workspace, size_t workspace_bytes, bool act8, void* stream) {
+                            const uint8_t* s_down, const uint16_t* y, int64_t T, int64_t H, int64_t I, int64_t E) {
   if (!x || !router_logits || !w_gate_up || !s_gate_up || !w_down || !s_down || !y) return MX_ERR_NULL;
   int st = check_moe_sizes(T, E, top_k);
   if (st != MX_OK) return st;
@@ -229,6 +272,15 @@ static int moe_forward_impl(const uint16_t* x, const float* router_logits, int64
   if (!aligned(x, 16) || !aligned(w_gate_up, 16) || !aligned(w_down, 16) || !aligned(s_gate_up, 16) ||
       !aligned(s_down, 16) || !aligned(y, 8) || !aligned(router_logits, 4))
     return MX_ERR_ALIGN;
+  return MX_OK;
+}
+
+static int moe_forward_impl(const uint16_t* x, const float* router_logits, int64_t top_k, int64_t ns,
+                            const uint8_t* w_gate_up, const uint8_t* s_gate_up, const uint8_t* w_down,
+                            const uint8_t* s_down, uint16_t* y, int64_t T, int64_t H, int64_t I, int64_t E,
+                            void* workspace, size_t workspace_bytes, bool act8, void* stream) {
+  int st = moe_forward_args(x, router_logits, top_k, ns, w_gate_up, s_gate_up, w_down, s_down, y, T, H, I, E);
+  if (st != MX_OK) return st;
   if (!workspace || !aligned(workspace, 256)) return MX_ERR_WORKSPACE;
   // every slot, routed and shared, is one row of the expert GEMMs
   const MoeWorkspace ws = moe_workspace_carve(workspace, T, H, I, E + ns, top_k + ns);
@@ -261,6 +313,20 @@ int moe_mxfp4_forward(const uint16_t* x, const float* router_logits, int64_t top
                       int64_t H, int64_t I, int64_t E, void* workspace, size_t workspace_bytes, void* stream) {
   return moe_forward_impl(x, router_logits, top_k, 0, w_gate_up, s_gate_up, w_down, s_down, y, T, H, I, E, workspace,
                           workspace_bytes, false, stream);
+}
+
+int moe_mxfp4_forward_noalloc(const uint16_t* x, const float* router_logits, int64_t top_k, const uint8_t* w_gate_up,
+                              const uint8_t* s_gate_up, const uint8_t* w_down, const uint8_t* s_down, uint16_t* y,
+                              int64_t T, int64_t H, int64_t I, int64_t E, void* stream) {
+  int st = moe_forward_args(x, router_logits, top_k, 0, w_gate_up, s_gate_up, w_down, s_down, y, T, H, I, E);
+  if (st != MX_OK) return st;
+  const size_t need = moe_workspace_carve(nullptr, T, H, I, E, top_k).bytes;
+  if (need > (size_t)MX_NOALLOC_SCRATCH_BYTES) return MX_ERR_SCRATCH;
+  void* ws = nullptr;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = noalloc_scratch(&ws, s)) != MX_OK) return st;
+  return moe_forward_impl(x, router_logits, top_k, 0, w_gate_up, s_gate_up, w_down, s_down, y, T, H, I, E, ws,
+                          (size_t)MX_NOALLOC_SCRATCH_BYTES, false, stream);
 }
 
 int moe_mxfp4_forward_shared(const uint16_t* x, const float* router_logits, int64_t top_k, int64_t n_shared,

@@ -236,3 +236,20 @@ def test_persistent_error_word_raises():
     with pytest.raises(m.MxWaitError):
         m.raise_for_persistent_error(1)
     assert m.PERSISTENT_ERROR_OFFSET == 8
+
+
+def test_noalloc_forward_rejects():
+    """The static-scratch forward checks its arguments like moe_mxfp4_forward and refuses
+    sizes whose scratch exceeds its array, all before anything is enqueued."""
+    L = m.raw()
+
+    def fwd(x=A, k=2, T=4, H=1024, I=1024, E=8):
+        return L.moe_mxfp4_forward_noalloc(x, A, k, A, A, A, A, A, T, H, I, E, None)
+
+    assert fwd(x=None) == MX_ERR_NULL
+    assert fwd(T=0) == MX_ERR_SHAPE
+    assert fwd(I=320) == MX_ERR_SHAPE
+    assert fwd(x=MIS) == MX_ERR_ALIGN
+    assert fwd(T=256, k=32, E=1024, H=7168, I=2048) == m.MX_ERR_SCRATCH
+    assert m.workspace_size(256, 7168, 2048, 1024, 32) > m.MX_NOALLOC_SCRATCH_BYTES
+    assert m.status_string(m.MX_ERR_SCRATCH) != "unknown status"
