@@ -33,7 +33,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mx_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# MXMOE_ORACLE_LIB: load another build of mx_oracle.c (the sanitizer test's)
+_LIB_PATH = os.environ.get("MXMOE_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 CFLAGS = ["-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
