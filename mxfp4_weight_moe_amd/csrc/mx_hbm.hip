@@ -6,7 +6,7 @@
 // Both walk the buffer grid-stride in 16-byte pieces with nontemporal accesses, as the
 // expert GEMMs read their weights, each thread keeping several pieces in flight.  The read
 // kernel folds what it loads into an XOR (kept in registers, reduced across the wave and
-// added to four device words with vector atomics), so its loads are live and its result
+// XORed into four device words with vector atomics), so its loads are live and its result
 // can be checked bit for bit.
 #include "mx_device.hpp"
 #include "mx_internal.hpp"
@@ -45,9 +45,12 @@ __global__ void __launch_bounds__(HBM_BLOCK) hbm_read_kernel(const u32x4* __rest
     for (int off = 32; off > 0; off >>= 1) a ^= (uint32_t)__shfl_xor((int)a, off, 64);
     acc[c] = a;
   }
+  // XOR with zero changes nothing, so a wave whose fold is zero skips its atomic: a buffer
+  // of repeated words (the benchmark's) then adds no atomics to the timed read.
   if ((threadIdx.x & 63) == 0) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) atomicXor(xor_out + c, acc[c]);
+    for (int c = 0; c < 4; ++c)
+      if (acc[c] != 0u) atomicXor(xor_out + c, acc[c]);
   }
 }
 

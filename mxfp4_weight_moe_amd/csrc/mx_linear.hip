@@ -9,7 +9,8 @@
 //
 // Work split: one workgroup per 16 output rows of W; its W waves split the K segments and
 // sum their partial tiles through LDS in a fixed order.  Activation rows are processed in
-// passes of up to 32 (two MFMA m-tiles).
+// passes of up to 32 (two MFMA m-tiles).  One or two tokens with few output rows take a
+// path of their own (one row per wave, below).
 #include "mx_act8.hpp"
 #include "mx_device.hpp"
 #include "mx_internal.hpp"
@@ -101,10 +102,110 @@ __global__ void __launch_bounds__(W * 64) mx_linear_kernel(const uint16_t* __res
   }
 }
 
+// ------------------------------------------------------------------ one row per wave (T <= 2)
+
+// For one or two tokens and few output rows the MFMA tiles of 16 rows leave most CUs idle
+// (2048 rows are 128 tiles for 256 CUs), and a call is about one memory round trip:
+// measured on MI355X inside a HIP graph, a plain read of 2.2 MB takes 3.4 us spread over
+// 137 workgroups and 2.1 us over 546.  Here a workgroup of 4 waves owns 4 output rows, one
+// per wave, and each lane one MX block of its row at a time (16 code bytes, one scale
+// byte): the codes are decoded straight to fp32 with the scaled conversion
+// (v_cvt_scalef32_pk_f32_fp4, the E8M0 byte in the operand's exponent field, so 0xFF gives
+// NaN), the products x * w are exact in fp32 (at most 8 + 2 significant bits), each lane
+// sums its blocks in ascending K with fused multiply-adds (one rounding per term, as the
+// plain sum of exact products), and the 64 lane sums are added in a fixed butterfly order.
+// The activations (T * K <= 16384 values) are staged in LDS once per workgroup: read by
+// every wave from global memory instead, the same few KB were requested by all 2048 waves
+// of the 1-token layer and the call took 4.1 us; staged, 3.1 us (the MFMA path: 3.75 us).
+constexpr int ROWS_WG = 4;
+constexpr int ROWS_MAX_T = 2;
+constexpr int ROWS_MAX_TK = 16384;  // activations staged in LDS: T * K bf16 values
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+template <int TT>
+__global__ void __launch_bounds__(ROWS_WG * 64) mx_linear_rows_kernel(const uint16_t* __restrict__ x,
+                                                                      const uint8_t* __restrict__ w,
+                                                                      const uint8_t* __restrict__ s,
+                                                                      uint16_t* __restrict__ y, int T, int K, int N) {
+  __shared__ u32x4 xs[ROWS_MAX_TK / 8];
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * ROWS_WG + (threadIdx.x >> 6);
+  const int n = min(row, N - 1);  // rows past N compute row N - 1 again and store nothing
+  const int nb = K >> 5;
+  const uint8_t* wr = w + (size_t)n * (K >> 1);
+  const uint8_t* sr = s + (size_t)n * nb;
+  for (int i = threadIdx.x; i < T * K / 8; i += ROWS_WG * 64) xs[i] = ld16(x + (size_t)i * 8);
+  __syncthreads();
+  float acc[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) acc[t] = 0.f;
+  // blocks lane, lane + 64, ...: four at a time, their loads issued before any use
+  for (int b0 = 0; b0 < nb; b0 += 4 * 64) {
+    u32x4 c[4];
+    uint32_t sb[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int b = min(b0 + u * 64 + lane, nb - 1);  // past the row's end: its last block, not summed
+      c[u] = ld_stream16(wr + (size_t)b * 16);
+      sb[u] = sr[b];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int b = b0 + u * 64 + lane;
+      if (b >= nb) continue;
+      const float sc = e8m0_scale_operand(sb[u]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {  // code dword q: K values 8q .. 8q + 7 of the block
+        // byte p: values 8q + 2p (low nibble) and 8q + 2p + 1
+        const f32x2 wv[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[u][q], sc, 0),
+                             __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[u][q], sc, 1),
+                             __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[u][q], sc, 2),
+                             __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[u][q], sc, 3)};
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+          const u32x4 xw = xs[(min(t, T - 1) * K + b * 32) / 8 + q];
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            acc[t] = __builtin_fmaf(bf16_lo(xw[p]), wv[p][0], acc[t]);
+            acc[t] = __builtin_fmaf(bf16_hi(xw[p]), wv[p][1], acc[t]);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    float v = acc[t];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
+    acc[t] = v;
+  }
+  if (row < N && lane < TT && lane < T) {
+    float v = acc[0];
+#pragma unroll
+    for (int t = 1; t < TT; ++t) v = (lane == t) ? acc[t] : v;
+    y[(size_t)lane * N + n] = f32_to_bf16_rne(v);
+  }
+}
+
 template <bool A8>
 static int launch_dense(const uint16_t* x, const uint8_t* w, const uint8_t* s, uint16_t* y, int T, int K, int N,
                         hipStream_t stream) {
   const int items = (N + SUB_ROWS - 1) / SUB_ROWS;
+  if constexpr (!A8) {
+    // one or two tokens and fewer 16-row tiles than two per CU: one row per wave
+    if (T <= ROWS_MAX_T && T * K <= ROWS_MAX_TK && items < 2 * device_cu_count()) {
+      const dim3 grid((unsigned)((N + ROWS_WG - 1) / ROWS_WG)), block(ROWS_WG * 64);
+      if (T == 1)
+        hipLaunchKernelGGL((mx_linear_rows_kernel<1>), grid, block, 0, stream, x, w, s, y, T, K, N);
+      else
+        hipLaunchKernelGGL((mx_linear_rows_kernel<2>), grid, block, 0, stream, x, w, s, y, T, K, N);
+      return hip_status(hipGetLastError());
+    }
+  }
   const int nseg = K / SEG_K;
   // Up to 8 waves split K; with MXFP8 activations at most 4, whose registers then fit
   // without spilling (8 waves of 64 lanes leave each lane half the register file).

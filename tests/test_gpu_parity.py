@@ -112,6 +112,32 @@ def test_mx_linear_edge_values(dev, mx):
     assert np.array_equal(got[2][fin], y[2][fin])
 
 
+@pytest.mark.parametrize("T,K", [(1, 2048), (2, 2048), (1, 7200), (2, 96)])
+def test_mx_linear_edge_values_one_and_two_tokens(dev, mx, T, K):
+    """The one-row-per-wave path of one and two tokens: NaN scales (a whole output column,
+    one block), huge and tiny scales, and (T = 2) a one-hot row that must extract the weight
+    column exactly (nibble order, scale index); K = 7200 and 96 leave ragged blocks per lane."""
+    N = 48
+    cfg = synthetic.LinearConfig("edge12", T=T, K=K, N=N, e_lo=-6, e_hi=0, seed=K + T)
+    x, w, s = synthetic.linear_inputs(cfg)
+    s = s.copy()
+    s[3, :] = 255
+    s[4, min(2, K // 32 - 1)] = 255
+    s[5, :] = 235  # huge weights (6 * 2^108) whose sums stay finite: |x| < 4, K <= 7200 terms
+    s[6, :] = 30
+    x = x.copy()
+    if T == 2:
+        x[1, :] = 0
+        x[1, 7] = 0x3F80
+    say("mx_linear edge values, T =", T, "K =", K)
+    got = run_linear(dev, mx, x, w, s, T, K, N)
+    y, _, sd = oracle.mx_linear(x, w, s, T, K, N)
+    check_bound(got, y, sd, DENSE_REL, f"edge T={T} K={K}")
+    if T == 2:
+        fin = ~np.isnan(bf16_to_f(y[1]))
+        assert np.array_equal(got[1][fin], y[1][fin])
+
+
 # ------------------------------------------------------------------ routing and sort
 
 ROUTE_CASES = [("moe_t4", None), ("moe_t32_zipf", None), ("moe_t128", None)]
