@@ -25,9 +25,10 @@ and its share of 8 TB/s and of this GPU's measured copy and read bandwidth (the 
 HBM reference kernels), a roofline entry for the dominant kernel (gate_up), the CPU
 oracle's time on a bounded sample of the same workload and the worst parity ratio of that
 sample against the GPU's output, and (by default) the other configurations of the
-benchmark under "configs".  The kernel's launch time comes from a pass over the same K
-steps right after the timed region, issued as the three stage calls with a HIP event
-between them on the stream the kernels run on.  roofline.traffic is the kernel's HBM bytes
+benchmark under "configs".  The kernel's launch time comes from a pass of max(K, 200)
+steps right after the timed region (behind a few graph replays, so the GPU does not idle in
+between), issued as the three stage calls with a HIP event between them on the stream the
+kernels run on.  roofline.traffic is the kernel's HBM bytes
 per launch as measured by the committed counter summary under profiles/, and null when the
 workload differs or the kernel's sources changed since the counters were taken.
 
@@ -56,6 +57,8 @@ DENSE_CYCLE_BYTES = 1 << 30
 HBM_PEAK_GBPS = 8000.0
 MOE_REL = 1e-2  # the MoE acceptance bound: |gpu - oracle| <= 1e-2 * sum_j g_j sum_i |h_i w_in| + 1 bf16 ulp
 ROOT = os.path.dirname(os.path.abspath(__file__))
+STAGE_MIN = 200           # launches the per-kernel event pass times at least
+STAGE_LEAD_REPLAYS = 8    # graph replays queued right before it
 # the other configurations a default run reports beside its headline workload
 EXTRA_WORKLOADS = ("dense_t1", "dense_t4", "moe_t4", "moe_t128", "moe_sweep_t1")
 # sources (and build flags) the gate_up kernel is compiled from; the counter summary records
@@ -85,7 +88,8 @@ def parse():
                     help="MXFP8 activations for both expert GEMMs (moe_mxfp4_forward_a8, scaled MFMA)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32, help="tokens of the oracle's timed sample")
-    ap.add_argument("--stage-steps", type=int, default=None, help="steps of the per-kernel event pass (default K)")
+    ap.add_argument("--stage-steps", type=int, default=None,
+                    help="steps of the per-kernel event pass (default max(K, 200))")
     ap.add_argument("--no-extra", action="store_true", help="time only --workload (no other configurations)")
     ap.add_argument("--extra-steps", type=int, default=80, help="timed steps of each other configuration")
     ap.add_argument("--hbm-mib", type=int, default=4096, help="buffer of the HBM reference kernels (0: skip)")
@@ -364,13 +368,20 @@ def moe_case(cfg, args, torch, mx, dev, *, steps: int, warmup: int, stage_pass: 
     }
 
     # ---------------------------------------------------------------- per-kernel pass (HIP events)
-    # Right after the timed region, the same K layer forwards issued as the three stage calls
+    # Right after the timed region, the layer forwards issued as the three stage calls
     # (the kernels the forward launches), with a HIP event between stages recorded on the
     # stream the kernels are launched on.  Launches are queued far faster than the GPU
     # drains them, so the stream never runs dry and each event pair brackets one kernel.
     if stage_pass:
-        KS = args.stage_steps or K
+        # At least STAGE_MIN steps whatever --steps says, and the GPU kept loaded across the
+        # hand-over (replays queued with no host synchronization before the pass): after the
+        # timed region's synchronization an idle GPU would start the pass in the power
+        # manager's transient (measured: 20 launches right after a synchronization averaged
+        # 280 us against 254 us).
+        KS = args.stage_steps or max(K, STAGE_MIN)
         sev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(KS)]
+        for _ in range(STAGE_LEAD_REPLAYS):
+            replay()
         for i in range(KS):
             staged(i, sev[i], stream)
         torch.cuda.synchronize()
