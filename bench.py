@@ -87,7 +87,8 @@ def parse():
     ap.add_argument("--act8", action="store_true",
                     help="MXFP8 activations for both expert GEMMs (moe_mxfp4_forward_a8, scaled MFMA)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=32, help="tokens of the oracle's timed sample")
+    ap.add_argument("--cpu-tokens", type=int, default=32, help="tokens per layer of the oracle's timed sample")
+    ap.add_argument("--cpu-layers", type=int, default=2, help="layers of the oracle's timed sample")
     ap.add_argument("--stage-steps", type=int, default=None,
                     help="steps of the per-kernel event pass (default max(K, 200))")
     ap.add_argument("--no-extra", action="store_true", help="time only --workload (no other configurations)")
@@ -411,35 +412,41 @@ def moe_case(cfg, args, torch, mx, dev, *, steps: int, warmup: int, stage_pass: 
         }
 
     # ---------------------------------------------------------------- CPU oracle: baseline and parity
+    # The oracle on the first --cpu-tokens tokens of the first --cpu-layers layers (the whole
+    # layer at T <= 32): its time is the baseline, and its outputs are compared with the GPU's
+    # output of the same layers under the MoE bound.
     if cpu_leg:
         import oracle
-        lay = layers[0]
-        lay["y"].fill_(float("nan"))
-        forward(lay)
-        torch.cuda.synchronize()
-        y_gpu = lay["y"].view(torch.int16).cpu().numpy().view(np.uint16)
-        n = max(1, min(args.cpu_tokens, T))
-        toks = np.arange(n, dtype=np.int32)
-        w_host = {key: lay["w"][key].cpu().numpy() for key in ("wgu", "sgu", "wd", "sd")}
         threads = oracle.default_threads()
-        log(f"[bench] oracle on {n} of {T} tokens, {threads} threads")
-        c0 = time.perf_counter()
-        y_ora, scale, _ = oracle.moe_tokens(lay["x_bits"], lay["logits_host"], k, w_host["wgu"], w_host["sgu"],
-                                            w_host["wd"], w_host["sd"], T, H, I, E, tokens=toks, nthreads=threads,
-                                            n_shared=ns, act8=args.act8)
-        c1 = time.perf_counter()
-        worst, mismatch = moe_bound_ratio(y_gpu[:n], y_ora, scale)
+        n = max(1, min(args.cpu_tokens, T))
+        nl = max(1, min(args.cpu_layers, L))
+        toks = np.arange(n, dtype=np.int32)
+        log(f"[bench] oracle on {n} of {T} tokens of {nl} layer(s), {threads} threads")
+        secs, worst, mismatch = 0.0, 0.0, 0
+        for lay in layers[:nl]:
+            lay["y"].fill_(float("nan"))
+            forward(lay)
+            torch.cuda.synchronize()
+            y_gpu = lay["y"].view(torch.int16).cpu().numpy().view(np.uint16)
+            w_host = {key: lay["w"][key].cpu().numpy() for key in ("wgu", "sgu", "wd", "sd")}
+            c0 = time.perf_counter()
+            y_ora, scale, _ = oracle.moe_tokens(lay["x_bits"], lay["logits_host"], k, w_host["wgu"], w_host["sgu"],
+                                                w_host["wd"], w_host["sd"], T, H, I, E, tokens=toks, nthreads=threads,
+                                                n_shared=ns, act8=args.act8)
+            secs += time.perf_counter() - c0
+            wr, mm = moe_bound_ratio(y_gpu[:n], y_ora, scale)
+            worst, mismatch = max(worst, wr), mismatch + mm
+            del w_host
         res["cpu_baseline"] = {
-            "value": round((c1 - c0) * (T / n) * 1e6, 1), "unit": "us/layer", "cores": threads, "kind": "oracle",
-            "sample": f"layer 0, tokens 0..{n - 1} of {T} (all {k} routed experts each), full route+gate_up+down+"
-                      f"combine; time scaled by {T}/{n}; CPU: {cpu_model()}",
-            "seconds": round(c1 - c0, 2),
+            "value": round(secs / nl * (T / n) * 1e6, 1), "unit": "us/layer", "cores": threads, "kind": "oracle",
+            "sample": f"layers 0..{nl - 1}, tokens 0..{n - 1} of {T} each (all {k} routed experts per token), full "
+                      f"route+gate_up+down+combine; time per layer scaled by {T}/{n}; CPU: {cpu_model()}",
+            "seconds": round(secs, 2),
         }
-        res["parity"] = {"tokens": n, "outputs": int(n * H), "worst_ratio": round(worst, 4),
+        res["parity"] = {"layers": nl, "tokens": n, "outputs": int(nl * n * H), "worst_ratio": round(worst, 4),
                          "nan_inf_mismatches": mismatch, "ok": bool(worst <= 1.0 and mismatch == 0),
                          "bound": "|gpu - oracle| <= 1e-2 * sum_j gate_j sum_i |h_i w_in| + 1 bf16 ulp, per output; "
                                   "worst_ratio = max |gpu - oracle| / bound over the sample"}
-        del w_host
     del layers, ws, h
     torch.cuda.empty_cache()
     return res
