@@ -131,9 +131,14 @@ __device__ __forceinline__ int x_piece_block(int g, int h, int c) {
   return A8 ? 4 * h + 2 * (c >> 1) + (g >> 1) : g + 4 * h;
 }
 
-// Load segment `sg` (a full segment: all 8 blocks of the 256 K values exist).
-template <int NS, int MT, bool A8 = false>
-__device__ __forceinline__ void stage_load(Stage<NS, MT>& st, const StreamLanes<NS, MT>& L, int sg) {
+typedef __attribute__((address_space(3))) const uint16_t* lds_cu16_ptr;
+typedef __attribute__((address_space(3))) const u32x4* lds_cu32x4_ptr;
+
+// Load segment `sg` (a full segment: all 8 blocks of the 256 K values exist): its weight
+// codes and scales (stage_load_w), and its activation pieces (stage_load_x).  XL: the
+// activation rows L.x point into LDS (staged there by the caller), read with LDS loads.
+template <int NS, int MT>
+__device__ __forceinline__ void stage_load_w(Stage<NS, MT>& st, const StreamLanes<NS, MT>& L, int sg) {
   const size_t wo = (size_t)sg * SEG_BYTES;
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
@@ -142,16 +147,32 @@ __device__ __forceinline__ void stage_load(Stage<NS, MT>& st, const StreamLanes<
   }
 #pragma unroll
   for (int i = 0; i < NS; ++i) st.s[i] = ld8(L.s[i] + (size_t)sg * SEG_SCALES);
+}
+template <int NS, int MT, bool A8, bool XL>
+__device__ __forceinline__ void stage_load_x(Stage<NS, MT>& st, const StreamLanes<NS, MT>& L, int sg) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     if (L.x[mt]) {
-      const uint16_t* xp = L.x[mt] + (size_t)sg * SEG_K;
+      if constexpr (XL) {
+        const lds_cu16_ptr xp = (lds_cu16_ptr)L.x[mt] + sg * SEG_K;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) st.x[mt][h * 4 + c] = ld16(xp + x_piece_off<A8>(h, c));
+          for (int c = 0; c < 4; ++c) st.x[mt][h * 4 + c] = *(lds_cu32x4_ptr)(xp + x_piece_off<A8>(h, c));
+      } else {
+        const uint16_t* xp = L.x[mt] + (size_t)sg * SEG_K;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) st.x[mt][h * 4 + c] = ld16(xp + x_piece_off<A8>(h, c));
+      }
     }
   }
+}
+template <int NS, int MT, bool A8 = false, bool XL = false>
+__device__ __forceinline__ void stage_load(Stage<NS, MT>& st, const StreamLanes<NS, MT>& L, int sg) {
+  stage_load_w(st, L, sg);
+  stage_load_x<NS, MT, A8, XL>(st, L, sg);
 }
 
 // Load a final partial segment with `nb` (< 8) valid MX blocks; missing blocks read as
@@ -235,8 +256,9 @@ __device__ __forceinline__ void stage_consume(const Stage<NS, MT>& st, const Str
 }
 
 // Stream segments [sg0, sg1) (+ an optional partial tail segment with nb_tail blocks at
-// index sg1) into acc with a D-deep register pipeline.
-template <int NS, int MT, int D, bool A8 = false>
+// index sg1, not with XL) into acc with a D-deep register pipeline.  XL: the activation
+// rows are in LDS.
+template <int NS, int MT, int D, bool A8 = false, bool XL = false>
 __device__ __forceinline__ void stream_segments(const StreamLanes<NS, MT>& L, int sg0, int sg1, int nb_tail,
                                                 uint8_t* __restrict__ slab, f32x4 (&acc)[MT][NS], int lane) {
   Stage<NS, MT> st[D];
@@ -245,17 +267,17 @@ __device__ __forceinline__ void stream_segments(const StreamLanes<NS, MT>& L, in
   const int n = sg1 - sg0;
 #pragma unroll
   for (int d = 0; d < D; ++d)
-    if (d < n) stage_load<NS, MT, A8>(st[d], L, sg0 + d);
+    if (d < n) stage_load<NS, MT, A8, XL>(st[d], L, sg0 + d);
   for (int b = 0; b < n; b += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       if (b + d < n) {
         stage_consume<NS, MT, A8>(st[d], L, slab, acc, lane);
-        if (b + d + D < n) stage_load<NS, MT, A8>(st[d], L, sg0 + b + d + D);
+        if (b + d + D < n) stage_load<NS, MT, A8, XL>(st[d], L, sg0 + b + d + D);
       }
     }
   }
-  if (nb_tail > 0) {
+  if (!XL && nb_tail > 0) {
     stage_load_tail<NS, MT, A8>(st[0], L, sg1, nb_tail, lane);
     stage_consume<NS, MT, A8>(st[0], L, slab, acc, lane);
   }

@@ -19,8 +19,8 @@ namespace mx {
 
 // DEEP: a 4-deep load pipeline for one m-tile (every segment of a wave in flight when the
 // K split gives it at most 4), where the kernel's registers allow it; else 3 (one m-tile) or
-// 2 (two m-tiles).
-template <int W, int MT, bool SBYTE, bool A8, bool DEEP = false>
+// 2 (two m-tiles).  XL: x is the workgroup's LDS copy of the activations (same layout).
+template <int W, int MT, bool SBYTE, bool A8, bool DEEP = false, bool XL = false>
 __device__ __forceinline__ void dense_pass(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
                                            const uint8_t* __restrict__ s, uint16_t* __restrict__ y, int T, int K,
                                            int N, int n0, int mp, uint8_t* slab, f32x4* red, int wave, int lane) {
@@ -57,7 +57,7 @@ __device__ __forceinline__ void dense_pass(const uint16_t* __restrict__ x, const
       stage_consume<NS, MT, A8>(st, L, slab, acc, lane);
     }
   } else {
-    stream_segments<NS, MT, D, A8>(L, sg0, sg1, (wave == W - 1) ? nb_tail : 0, slab, acc, lane);
+    stream_segments<NS, MT, D, A8, XL>(L, sg0, sg1, (wave == W - 1) ? nb_tail : 0, slab, acc, lane);
   }
   wg_reduce<NS, MT, W>(acc, red, wave, lane);
   if (wave == 0) {
@@ -82,15 +82,38 @@ __device__ __forceinline__ void dense_pass(const uint16_t* __restrict__ x, const
 
 // ONE_TILE: T <= 16, a single pass of one m-tile; the kernel then holds only that pass, whose
 // registers leave room (with bf16 activations) for the 4-deep pipeline.
-template <int W, bool SBYTE, bool A8, bool ONE_TILE>
+// XL (one tile, K % 256 == 0, T * K <= DENSE_XL_MAX): the workgroup first copies x into LDS
+// (dynamic shared memory of T * K bf16) with full-width 16-byte loads, and the waves read
+// their MFMA activation fragments from there.  Read from global memory, each fragment load
+// has only T of every 16 lanes active, so at T = 4 the activation loads were 8 of the 11
+// load instructions per segment and a fifth of the call's time.
+constexpr int DENSE_XL_MAX = 32768;  // activation values staged in LDS (64 KB)
+template <int W, bool SBYTE, bool A8, bool ONE_TILE, bool XL = false>
 __global__ void __launch_bounds__(W * 64) mx_linear_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
                                                            const uint8_t* __restrict__ s, uint16_t* __restrict__ y,
                                                            int T, int K, int N) {
   __shared__ __attribute__((aligned(16))) uint8_t slabs[W][SLAB_BYTES];
   __shared__ f32x4 red[(W > 1) ? W * 2 * 64 : 1];
+  extern __shared__ u32x4 xdyn[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n0 = blockIdx.x * SUB_ROWS;
-  if constexpr (ONE_TILE) {
+  if constexpr (XL) {
+    static_assert(ONE_TILE && !SBYTE, "LDS activations: one tile, whole segments");
+    // 8 loads of a thread in flight at once, then their stores (no branch around the
+    // first 8: a piece past the end is the last piece again, stored with the same value)
+    const int n16 = T * K / 8, nt = W * 64, t = threadIdx.x;
+    const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+    for (int i0 = t; i0 < n16; i0 += 8 * nt) {
+      u32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = xv[min(i0 + u * nt, n16 - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) xdyn[min(i0 + u * nt, n16 - 1)] = v[u];
+    }
+    __syncthreads();
+    dense_pass<W, 1, SBYTE, A8, !A8, true>(reinterpret_cast<const uint16_t*>(xdyn), w, s, y, T, K, N, n0, 0,
+                                           slabs[wave], red, wave, lane);
+  } else if constexpr (ONE_TILE) {
     dense_pass<W, 1, SBYTE, A8, !A8>(x, w, s, y, T, K, N, n0, 0, slabs[wave], red, wave, lane);
   } else {
     for (int mp = 0; mp < T; mp += 32) {
@@ -213,15 +236,19 @@ static int launch_dense(const uint16_t* x, const uint8_t* w, const uint8_t* s, u
   int W = 1;
   while (W < WMAX && 2 * W <= nseg && items * W < 2048) W *= 2;
   const bool sbyte = (K % SEG_K) != 0;
+  const bool xl = T <= 16 && !sbyte && T * K <= DENSE_XL_MAX;
+  const unsigned xl_bytes = xl ? (unsigned)(T * K * 2) : 0u;
   dim3 grid(items), block(W * 64);
-#define MXL1(WW, SB, OT) \
-  hipLaunchKernelGGL((mx_linear_kernel<WW, SB, A8, OT>), grid, block, 0, stream, x, w, s, y, T, K, N)
-#define MXL(WW, SB) \
-  do {                          \
-    if (T <= 16)                \
-      MXL1(WW, SB, true);       \
-    else                        \
-      MXL1(WW, SB, false);      \
+#define MXL1(WW, SB, OT, XX) \
+  hipLaunchKernelGGL((mx_linear_kernel<WW, SB, A8, OT, XX>), grid, block, xl_bytes, stream, x, w, s, y, T, K, N)
+#define MXL(WW, SB)                           \
+  do {                                        \
+    if (T <= 16 && !(SB) && xl)               \
+      MXL1(WW, false, true, true);            \
+    else if (T <= 16)                         \
+      MXL1(WW, SB, true, false);              \
+    else                                      \
+      MXL1(WW, SB, false, false);             \
   } while (0)
   if (sbyte) {
     switch (W) {

@@ -100,7 +100,7 @@ def test_mx_linear_a8_configs(dev, mx, name):
 
 
 ODD = [(1, 32, 16), (3, 64, 17), (2, 96, 40), (5, 288, 33), (16, 256, 16), (17, 512, 48), (31, 1024, 64),
-       (32, 800, 80), (33, 256, 32), (64, 2048, 128), (7, 7168, 100), (4, 7200, 64)]
+       (32, 800, 80), (33, 256, 32), (64, 2048, 128), (7, 7168, 100), (4, 7200, 64), (9, 2048, 48), (2, 16384, 24)]
 
 
 @pytest.mark.parametrize("T,K,N", ODD)
