@@ -220,18 +220,22 @@ static int row_groups(int T) { return (T + 15) / 16; }
 
 // Full-width tiles unless they would leave resident workgroup slots idle (few active
 // experts and row groups, i.e. small T) and half-width tiles, twice the items, still fit in
-// one round of the slots: then half-width tiles, twice the waves.  (The kernels are template
-// arguments, so each pair caches its own occupancy: kernels of one signature share a type.)
+// one round of the slots: then half-width tiles, twice the waves.  second_round: also
+// half-width tiles when the full-width items need more than one round of the slots but
+// less than two, where the second round would be run by a fraction of the workgroups while
+// the others idle (down at T = 2 and 3: 1.15 and 1.7 rounds, 77.4 -> 76.6 and 105.1 ->
+// 102.8 us per layer; from 2.2 rounds at T = 4 on, and at T = 1, half-width was slower).
+// (The kernels are template arguments, so each pair caches its own occupancy: kernels of
+// one signature share a type.)
 template <auto K2, auto K1>
-static bool use_half_tiles(int64_t items_full, int& grid) {
+static bool use_half_tiles(int64_t items_full, int& grid, bool second_round = false) {
   static const int occ2 = resident_wgs_per_cu(K2, WG_WAVES * 64);
   static const int occ1 = resident_wgs_per_cu(K1, WG_WAVES * 64);
-  if (2 * items_full > (int64_t)device_cu_count() * occ1) {
-    grid = expert_grid(items_full, occ2);
-    return false;
-  }
-  grid = expert_grid(2 * items_full, occ1);
-  return true;
+  const int64_t slots2 = (int64_t)device_cu_count() * occ2;
+  const bool half = 2 * items_full <= (int64_t)device_cu_count() * occ1 ||
+                    (second_round && items_full > slots2 && items_full < 2 * slots2);
+  grid = half ? expert_grid(2 * items_full, occ1) : expert_grid(items_full, occ2);
+  return half;
 }
 
 template <bool A8, int SPS>
@@ -324,7 +328,7 @@ static int launch_down_run(const uint16_t* h, const float* gates, const uint8_t*
     }
   }
   if (use_half_tiles<moe_down_kernel<2, SR, SPS, A8, false>, moe_down_kernel<1, SR, SPS, A8, false>>(items_full,
-                                                                                                    grid)) {
+                                                                                                    grid, true)) {
     const int nquad = H / (DownPlain<1, SR>::TILE * WG_WAVES);
     combined = fuse_combine(T, E, k, nquad, grid);
     launch_down_tiles<1, SR, SPS, A8>(combined, grid, h, wd, sd, sv, dpart, ctl, gates, y, T, H, I, k, stream);
