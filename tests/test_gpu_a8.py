@@ -188,13 +188,15 @@ def test_moe_a8_tiny(dev, mx, shape):
     assert np.array_equal(run_moe_a8(mx, d, cfg.k, cfg.n_shared), got)  # deterministic
 
 
+# moe_sweep_t1: in-gate_up routing with the combine inside down; moe_sweep_t2: half-width down
 FULL = [("moe_t4", None), ("moe_t32_zipf", [0, 7, 31]), ("moe_t128", [0, 100]), ("moe_tp8_t32", [0, 3, 30]),
-        ("moe_shared_t1", None)]
+        ("moe_shared_t1", None), ("moe_sweep_t1", None), ("moe_sweep_t2", None)]
 
 
 @pytest.mark.parametrize("name,tokens", FULL, ids=[f[0] for f in FULL])
 def test_moe_a8_full_size(dev, mx, name, tokens):
-    cfg = synthetic.MOE_CONFIGS[name]
+    cfg = (synthetic.MOE_CONFIGS[name] if name in synthetic.MOE_CONFIGS
+           else synthetic.sweep_config(int(name[len("moe_sweep_t"):])))
     say("moe a8 full", name, "tokens", tokens)
     d, x, logits = moe_inputs(cfg, dev)
     got = run_moe_a8(mx, d, cfg.k, cfg.n_shared)

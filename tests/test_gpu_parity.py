@@ -300,14 +300,25 @@ def test_moe_tiny_full_oracle(dev, mx, shape):
     say(f"  worst ratio {worst:.3g}")
 
 
+# the sweep points cover the launch shapes of the smallest T: T = 1 (gate_up that routes in
+# every workgroup, down with the combine inside), T = 2 and 3 (half-width down because
+# full-width items would need between one and two rounds of the slots), T = 16 (the largest
+# in-gate_up routing)
 FULL = [("moe_t4", None), ("moe_t32_zipf", None), ("moe_t128", list(range(0, 128, 8))),
         ("moe_spec_t4", None), ("moe_spec_t128", [0, 1, 2, 3, 40, 41, 126, 127]),
-        ("moe_tp8_t4", None), ("moe_tp8_t32", None), ("moe_shared_t1", None), ("moe_shared_t32", [0, 9, 31])]
+        ("moe_tp8_t4", None), ("moe_tp8_t32", None), ("moe_shared_t1", None), ("moe_shared_t32", [0, 9, 31]),
+        ("moe_sweep_t1", None), ("moe_sweep_t2", None), ("moe_sweep_t3", None), ("moe_sweep_t16", None)]
+
+
+def full_config(name):
+    if name in synthetic.MOE_CONFIGS:
+        return synthetic.MOE_CONFIGS[name]
+    return synthetic.sweep_config(int(name[len("moe_sweep_t"):]))
 
 
 @pytest.mark.parametrize("name,tokens", FULL, ids=[f[0] for f in FULL])
 def test_moe_full_size(dev, mx, name, tokens):
-    cfg = synthetic.MOE_CONFIGS[name]
+    cfg = full_config(name)
     say("moe full", name, "tokens", tokens)
     d, x, logits = moe_device_inputs(cfg, dev)
     got = run_moe(mx, d, cfg.k, cfg.n_shared)
