@@ -134,11 +134,10 @@ __device__ __forceinline__ int x_piece_block(int g, int h, int c) {
 typedef __attribute__((address_space(3))) const uint16_t* lds_cu16_ptr;
 typedef __attribute__((address_space(3))) const u32x4* lds_cu32x4_ptr;
 
-// Load segment `sg` (a full segment: all 8 blocks of the 256 K values exist): its weight
-// codes and scales (stage_load_w), and its activation pieces (stage_load_x).  XL: the
+// Load segment `sg` (a full segment: all 8 blocks of the 256 K values exist).  XL: the
 // activation rows L.x point into LDS (staged there by the caller), read with LDS loads.
-template <int NS, int MT>
-__device__ __forceinline__ void stage_load_w(Stage<NS, MT>& st, const StreamLanes<NS, MT>& L, int sg) {
+template <int NS, int MT, bool A8 = false, bool XL = false>
+__device__ __forceinline__ void stage_load(Stage<NS, MT>& st, const StreamLanes<NS, MT>& L, int sg) {
   const size_t wo = (size_t)sg * SEG_BYTES;
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
@@ -147,9 +146,6 @@ __device__ __forceinline__ void stage_load_w(Stage<NS, MT>& st, const StreamLane
   }
 #pragma unroll
   for (int i = 0; i < NS; ++i) st.s[i] = ld8(L.s[i] + (size_t)sg * SEG_SCALES);
-}
-template <int NS, int MT, bool A8, bool XL>
-__device__ __forceinline__ void stage_load_x(Stage<NS, MT>& st, const StreamLanes<NS, MT>& L, int sg) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     if (L.x[mt]) {
@@ -168,11 +164,6 @@ __device__ __forceinline__ void stage_load_x(Stage<NS, MT>& st, const StreamLane
       }
     }
   }
-}
-template <int NS, int MT, bool A8 = false, bool XL = false>
-__device__ __forceinline__ void stage_load(Stage<NS, MT>& st, const StreamLanes<NS, MT>& L, int sg) {
-  stage_load_w(st, L, sg);
-  stage_load_x<NS, MT, A8, XL>(st, L, sg);
 }
 
 // Load a final partial segment with `nb` (< 8) valid MX blocks; missing blocks read as

@@ -99,8 +99,8 @@ __global__ void __launch_bounds__(W * 64) mx_linear_kernel(const uint16_t* __res
   const int n0 = blockIdx.x * SUB_ROWS;
   if constexpr (XL) {
     static_assert(ONE_TILE && !SBYTE, "LDS activations: one tile, whole segments");
-    // 8 loads of a thread in flight at once, then their stores (no branch around the
-    // first 8: a piece past the end is the last piece again, stored with the same value)
+    // 8 loads of a thread in flight at once, then their stores; no branches (a piece past
+    // the end is the last piece again, stored with the same value)
     const int n16 = T * K / 8, nt = W * 64, t = threadIdx.x;
     const u32x4* xv = reinterpret_cast<const u32x4*>(x);
     for (int i0 = t; i0 < n16; i0 += 8 * nt) {
