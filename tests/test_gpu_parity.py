@@ -329,6 +329,27 @@ def test_moe_full_size(dev, mx, name, tokens):
     say(f"  worst ratio {worst:.3g}")
 
 
+@pytest.mark.parametrize("T,E,k,hot", [(256, 8, 1, [3]), (256, 2, 2, [0, 1]), (200, 64, 4, [5, 6, 7, 60]),
+                                        (256, 512, 8, [0, 1, 2, 3, 4, 5, 6, 7])],
+                         ids=["T256_one_expert", "T256_two_experts_k2", "T200_four_hot", "T256_E512_eight_hot"])
+def test_moe_all_tokens_on_few_experts(dev, mx, T, E, k, hot):
+    """Routing skewed to the extreme: every token picks the same experts, so each of them has
+    T rows (up to 16 row groups) and almost every work item is an extra row group."""
+    cfg = synthetic.MoEConfig("skew", T=T, H=1024, I=1024, E=E, k=k, routing="normal", e_lo=-8, e_hi=-2,
+                              seed=T + E + k)
+    host = synthetic.moe_inputs_host(cfg)
+    logits = host["logits"].copy()
+    logits[:, hot] += 40.0  # the hot experts win every token's top-k
+    host["logits"] = logits
+    say("moe skewed routing", T, E, k, hot)
+    d, x, logits = moe_device_inputs(cfg, dev, host=host)
+    got = run_moe(mx, d, cfg.k)
+    y, sm = oracle_moe(cfg, x, logits, host)
+    worst = check_bound(got, y, sm, MOE_REL, f"skewed {T},{E},{k}")
+    say(f"  worst ratio {worst:.3g}")
+    assert np.array_equal(run_moe(mx, d, cfg.k), got)  # deterministic
+
+
 def test_moe_small_scale_variant(dev, mx):
     cfg = synthetic.small_scale_variant(synthetic.MOE_CONFIGS["moe_t4"])
     say("moe small-scale variant")
