@@ -350,6 +350,47 @@ def test_moe_all_tokens_on_few_experts(dev, mx, T, E, k, hot):
     assert np.array_equal(run_moe(mx, d, cfg.k), got)  # deterministic
 
 
+def random_moe_cases(n=16, seed=20261203):
+    """Seeded random layer shapes over the ranges the launchers choose between: T from 1 to
+    256, 1 to 1024 experts, top-1 to top-32, H and I over several multiples of 1024 and
+    256, and three routing distributions (host weights kept under ~400 MB)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        H = int(rng.choice([1024, 2048, 3072]))
+        I = int(rng.choice([256, 512, 768, 1024, 2048]))
+        E = int(rng.choice([1, 3, 8, 16, 64, 200, 256, 384, 1024]))
+        k = int(min(E, rng.choice([1, 2, 4, 6, 8, 16, 32])))
+        T = int(rng.choice([1, 2, 3, 4, 5, 8, 16, 17, 24, 32, 33, 64, 100, 128, 200, 256]))
+        routing = str(rng.choice(["normal", "uniform", "zipf"]))
+        if E * 1.6 * H * I > 4e8:
+            continue
+        cases.append(dict(T=T, H=H, I=I, E=E, k=k, routing=routing, seed=len(cases)))
+    return cases
+
+
+RANDOM_MOE = random_moe_cases()
+
+
+@pytest.mark.parametrize("shape", RANDOM_MOE,
+                         ids=[f"T{c['T']}_H{c['H']}_I{c['I']}_E{c['E']}_k{c['k']}_{c['routing']}" for c in RANDOM_MOE])
+def test_moe_random_shapes(dev, mx, shape):
+    cfg = synthetic.MoEConfig("random", e_lo=-8, e_hi=-2, **shape)
+    host = synthetic.moe_inputs_host(cfg)
+    say("moe random shape", shape)
+    d, x, logits = moe_device_inputs(cfg, dev, host)
+    got = run_moe(mx, d, cfg.k)
+    T = cfg.T
+    tok = None
+    if T * cfg.k * cfg.H * cfg.I * 3 > 3e9:  # sampled tokens where the whole layer would be slow
+        tok = np.unique(np.array([0, T // 3, T // 2, T - 1], np.int32))
+    y, sm = oracle_moe(cfg, x, logits, host) if tok is None else \
+        oracle.moe_tokens(x, logits, cfg.k, host["wgu"], host["sgu"], host["wd"], host["sd"], T, cfg.H, cfg.I, cfg.E,
+                          tokens=tok)[:2]
+    worst = check_bound(got if tok is None else got[tok], y, sm, MOE_REL, f"random {shape}")
+    say(f"  worst ratio {worst:.3g}")
+
+
 def test_moe_small_scale_variant(dev, mx):
     cfg = synthetic.small_scale_variant(synthetic.MOE_CONFIGS["moe_t4"])
     say("moe small-scale variant")
