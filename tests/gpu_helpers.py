@@ -57,3 +57,17 @@ def check_bound(gpu_bits, ora_bits, scale, rel, what=""):
         raise AssertionError(f"{what}: {bad.size} of {ratio.size} outputs out of bound; worst ratio {worst:.3g}; "
                              f"first bad gpu={g[fin][bad[0]]!r} oracle={o[fin][bad[0]]!r} tol={tol[bad[0]]!r}")
     return worst
+
+
+def random_linear_shapes(n=16, seed=20261204):
+    """Seeded random dense-layer shapes (T, K, N): T from 1 to 64, K any multiple of 32 up to
+    8192 (so partial segments and odd scale-row alignments occur), N from 1 to 3000."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        T = int(rng.choice([1, 2, 3, 4, 5, 8, 12, 16, 17, 24, 32, 33, 48, 64]))
+        K = 32 * int(rng.integers(1, 257))
+        N = int(rng.integers(1, 3001))
+        out.append((T, K, N))
+    return out
+

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import synthetic
-from tests.gpu_helpers import MOE_REL, bf16_to_f, check_bound, say, to_dev_bf16, to_host_bits
+from tests.gpu_helpers import MOE_REL, bf16_to_f, check_bound, random_linear_shapes, say, to_dev_bf16, to_host_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -111,6 +111,19 @@ def test_mx_linear_a8_odd_shapes(dev, mx, T, K, N):
     got = run_linear_a8(dev, mx, x, w, s)
     y, _, sd = oracle.mx_linear_a8(x, w, s, T, K, N)
     check_bound(got, y, sd, A8_DENSE_REL, f"a8 odd {T},{K},{N}")
+
+
+RANDOM_LINEAR = random_linear_shapes(seed=20261205)
+
+
+@pytest.mark.parametrize("T,K,N", RANDOM_LINEAR)
+def test_mx_linear_a8_random_shapes(dev, mx, T, K, N):
+    cfg = synthetic.LinearConfig("random", T=T, K=K, N=N, e_lo=-6, e_hi=2, seed=T * 3 + K + N)
+    x, w, s = synthetic.linear_inputs(cfg)
+    say("mx_linear_a8 random", T, K, N)
+    got = run_linear_a8(dev, mx, x, w, s)
+    y, _, sd = oracle.mx_linear_a8(x, w, s, T, K, N)
+    check_bound(got, y, sd, A8_DENSE_REL, f"a8 random {T},{K},{N}")
 
 
 def test_mx_linear_a8_sparse_and_one_hot(dev, mx):

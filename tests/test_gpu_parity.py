@@ -10,8 +10,8 @@ import torch
 
 import oracle
 import synthetic
-from tests.gpu_helpers import (DENSE_REL, MOE_REL, bf16_to_f, check_bound, say, to_dev_bf16,
-                               to_host_bits)
+from tests.gpu_helpers import (DENSE_REL, MOE_REL, bf16_to_f, check_bound, random_linear_shapes, say,
+                               to_dev_bf16, to_host_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -89,6 +89,19 @@ def test_mx_linear_odd_shapes(dev, mx, T, K, N):
     got = run_linear(dev, mx, x, w, s, T, K, N)
     y, _, sd = oracle.mx_linear(x, w, s, T, K, N)
     check_bound(got, y, sd, DENSE_REL, f"odd {T},{K},{N}")
+
+
+RANDOM_LINEAR = random_linear_shapes()
+
+
+@pytest.mark.parametrize("T,K,N", RANDOM_LINEAR)
+def test_mx_linear_random_shapes(dev, mx, T, K, N):
+    cfg = synthetic.LinearConfig("random", T=T, K=K, N=N, e_lo=-6, e_hi=2, seed=T * 5 + K + N)
+    x, w, s = synthetic.linear_inputs(cfg)
+    say("mx_linear random", T, K, N)
+    got = run_linear(dev, mx, x, w, s, T, K, N)
+    y, _, sd = oracle.mx_linear(x, w, s, T, K, N)
+    check_bound(got, y, sd, DENSE_REL, f"random {T},{K},{N}")
 
 
 def test_mx_linear_edge_values(dev, mx):
