@@ -39,6 +39,18 @@ MUTATIONS = {
     "e4m3_subnormal_spacing": ("if (a == 0.0 || lead < -6) lead = -6;", "if (a == 0.0 || lead < -7) lead = -7;"),
     "a8_h_not_quantized": ("activation_row(h + p * I, I, act8, ha + p * I);", "activation_row(h + p * I, I, 0, ha + p * I);"),
     "active_lists_idle_experts": ("if (counts[e] > 0) active[na++] = (int32_t)e;", "if (counts[e] >= 0) active[na++] = (int32_t)e;"),
+    "silu_sign": ("return gd / (1.0 + exp(-gd)) * (double)u;", "return gd / (1.0 + exp(gd)) * (double)u;"),
+    "combine_drops_last_slot": ("      for (int64_t j = 0; j < k; ++j) {\n        int64_t p = i * k + j;",
+                                "      for (int64_t j = 0; j < k - 1; ++j) {\n        int64_t p = i * k + j;"),
+    "down_uses_first_slot_expert": ("        int64_t p = i * k + j;\n        int64_t e = ids[p];",
+                                    "        int64_t p = i * k + j;\n        int64_t e = ids[i * k];"),
+    "gate_up_wrong_token": ("float g = dot_vals(xa + (p / k) * H, W, S, H, n, &ga);",
+                            "float g = dot_vals(xa + (p % k) * H, W, S, H, n, &ga);"),
+    "bound_term_ungated": ("        sm += (double)gates[p] * as;", "        sm += as;"),
+    "gates_not_normalized": ("gates[t * k + j] = (float)(exp((double)l[ids[t * k + j]] - m) / den);",
+                             "gates[t * k + j] = (float)(exp((double)l[ids[t * k + j]] - m));"),
+    "offsets_missing_last": ("for (int64_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];",
+                             "for (int64_t e = 0; e + 1 < E; ++e) offsets[e + 1] = offsets[e] + counts[e];"),
 }
 
 # pin tests expected to catch each mutation (each entry: callable(tmp_fixture_args) -> runs asserts)
@@ -70,6 +82,13 @@ CATCHERS = {
     "e4m3_subnormal_spacing": [lambda: A8.test_quantize_rounds_like_torch_over_all_bf16(0, 1.75)],
     "a8_h_not_quantized": [lambda: A8.test_a8_moe_single_expert_reduces_to_a8_linear()],
     "active_lists_idle_experts": [lambda: R.test_sort_matches_stable_argsort(32, 256, 8)],
+    "silu_sign": [lambda: M.test_brute_force_tiny_moe(0, _mags())],
+    "combine_drops_last_slot": [lambda: M.test_brute_force_tiny_moe(0, _mags())],
+    "down_uses_first_slot_expert": [lambda: M.test_brute_force_tiny_moe(0, _mags())],
+    "gate_up_wrong_token": [lambda: M.test_brute_force_tiny_moe(0, _mags())],
+    "bound_term_ungated": [lambda: M.test_brute_force_tiny_moe(0, _mags())],
+    "gates_not_normalized": [lambda: R.test_route_matches_lexsort_and_softmax(4, 256, 8)],
+    "offsets_missing_last": [lambda: R.test_sort_matches_stable_argsort(4, 256, 8)],
 }
 
 
