@@ -66,7 +66,7 @@ EXTRA_WORKLOADS = ("dense_t1", "dense_t4", "moe_t4", "moe_t128", "moe_sweep_t1")
 GATE_UP_SOURCES = ("mxfp4_weight_moe_amd/build.py", "mxfp4_weight_moe_amd/csrc/mx_device.hpp",
                    "mxfp4_weight_moe_amd/csrc/mx_internal.hpp", "mxfp4_weight_moe_amd/csrc/mx_stream.hpp",
                    "mxfp4_weight_moe_amd/csrc/mx_act8.hpp", "mxfp4_weight_moe_amd/csrc/moe_policies.hpp",
-                   "mxfp4_weight_moe_amd/csrc/moe_experts.hip")
+                   "mxfp4_weight_moe_amd/csrc/moe_experts.hip", "mxfp4_weight_moe_amd/csrc/moe_fused.hip")
 GATE_UP_COUNTERS = os.path.join(ROOT, "profiles", "moe_gate_up_kernel.moe_t32_zipf.hbm_counters.txt")
 MFMA_COUNTERS = os.path.join(ROOT, "profiles", "moe_t128.mfma_counters.txt")
 
@@ -131,6 +131,15 @@ def gpu_clocks() -> dict:
         except OSError:
             pass
     return out
+
+
+def forward_path(T: int, k: int, E: int, ns: int) -> str:
+    """The launches moe_mxfp4_forward makes for these sizes (its dispatch)."""
+    if ns == 0 and T <= 16 and T * k <= 128:
+        return "gate_up (routing and sorting in every workgroup), down, combine launches (combine inside down at the smallest T)"
+    if ns == 0 and T <= 32 and T * k <= 256 and E <= 1024:
+        return "route, gate_up (sorting in every workgroup), down, combine launches"
+    return "route_sort, gate_up, down, combine launches"
 
 
 def source_hash(paths) -> str:
@@ -261,7 +270,11 @@ def moe_case(cfg, args, torch, mx, dev, *, steps: int, warmup: int, stage_pass: 
                active=torch.empty(E, dtype=torch.int32, device=dev),
                num_active=torch.empty(2, dtype=torch.int32, device=dev))
     h = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
-    names = ("layer",) if whole_layer else ("route_sort", "gate_up", "down_combine")
+    # From 17 to 32 tokens (no shared experts) the forward routes in a launch of its own and
+    # gate_up sorts the slots in every workgroup; the per-kernel pass issues the same calls.
+    sorted_path = ns == 0 and 16 < T <= 32 and T * k <= 256 and E <= 1024
+    names = ("layer",) if whole_layer else (("route", "gate_up", "down_combine") if sorted_path
+                                           else ("route_sort", "gate_up", "down_combine"))
     n_active = []
     for lay in layers:
         mx.moe_route_sort(lay["logits"], k, ids=ids, gates=gates, out=srt)
@@ -282,9 +295,14 @@ def moe_case(cfg, args, torch, mx, dev, *, steps: int, warmup: int, stage_pass: 
             e[1].record(stream)
             return
         e[0].record(stream)
-        mx.moe_route_sort(lay["logits"], k, ids=ids, gates=gates, out=srt)
-        e[1].record(stream)
-        mx.moe_gate_up_swiglu(lay["x"], w["wgu"], w["sgu"], srt, k, h=h, ws=ws)
+        if sorted_path:
+            mx.moe_route_topk(lay["logits"], k, ids=ids, gates=gates)
+            e[1].record(stream)
+            mx.moe_gate_up_swiglu_from_ids(lay["x"], ids, w["wgu"], w["sgu"], h=h, sort=srt, ws=ws)
+        else:
+            mx.moe_route_sort(lay["logits"], k, ids=ids, gates=gates, out=srt)
+            e[1].record(stream)
+            mx.moe_gate_up_swiglu(lay["x"], w["wgu"], w["sgu"], srt, k, h=h, ws=ws)
         e[2].record(stream)
         mx.moe_down_combine(h, gates, w["wd"], w["sd"], srt, T, k, out=lay["y"], ws=ws)
         e[3].record(stream)
@@ -364,7 +382,7 @@ def moe_case(cfg, args, torch, mx, dev, *, steps: int, warmup: int, stage_pass: 
             "weights": "MXFP4 (E2M1 codes, E8M0 scale per 32)", "accumulate": "fp32",
             "activations": "MXFP8 (E4M3, E8M0 scale per 32), quantized in the GEMM kernels" if args.act8 else "bf16",
             "layers_cycled": L, "timing": "eager launches" if args.eager else "HIP graph replay",
-            "path": "one persistent launch" if args.persistent else "route_sort, gate_up, down, combine launches",
+            "path": "one persistent launch" if args.persistent else forward_path(T, k, E, ns),
         },
     }
 
@@ -402,7 +420,7 @@ def moe_case(cfg, args, torch, mx, dev, *, steps: int, warmup: int, stage_pass: 
         res["staged_us_per_layer"] = round(sev[0][0].elapsed_time(sev[-1][-1]) * 1e3 / KS, 2)
         res["roofline"] = {
             "kernel": ("moe_fused_kernel" if args.persistent else "layer (all launches)") if whole_layer
-            else "moe_gate_up_kernel",
+            else ("moe_gate_up_sorted_kernel" if sorted_path else "moe_gate_up_kernel"),
             "bound": "hbm", "achieved": round(gu_achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(gu_achieved / HBM_PEAK_GBPS, 4),
             "traffic": None if whole_layer else measured_traffic(cfg.name),

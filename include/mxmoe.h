@@ -154,8 +154,9 @@ MX_API int moe_sort_by_expert(const int32_t* ids, int64_t T, int64_t top_k, int6
 
 /*
  * moe_route_topk followed by moe_sort_by_expert of its ids: one launch for T <= 16, two
- * beyond.  moe_mxfp4_forward runs it as its first stage beyond 16 tokens (and with shared
- * experts); up to 16 tokens its gate_up launch routes and sorts in every workgroup instead.
+ * beyond.  moe_mxfp4_forward runs it as its first stage beyond 32 tokens (and with shared
+ * experts); up to 16 tokens its gate_up launch routes and sorts in every workgroup instead,
+ * and from 17 to 32 it routes alone and gate_up sorts (moe_gate_up_swiglu_from_ids).
  * That internal sort has the same counts, offsets and sorted slots, but keeps its active
  * list in ascending expert order and leaves the entries past the last one unwritten (its
  * down launch accepts any order).  Arguments, outputs and limits as for those two calls.
@@ -179,6 +180,27 @@ MX_API int moe_gate_up_swiglu(const uint16_t* x, const uint8_t* w_gate_up, const
                               const int32_t* active, const int32_t* num_active, uint16_t* h, int64_t T, int64_t H,
                               int64_t I, int64_t E, int64_t top_k, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/*
+ * Stage hook: gate_up with SwiGLU straight from the routed ids (moe_route_topk's output),
+ * sorting the slots inside the launch: every workgroup sorts the T*top_k slots itself, and
+ * the launch also writes the sort (counts, offsets, sorted_slots, active, num_active), equal
+ * to moe_sort_by_expert's on the same ids.  moe_mxfp4_forward runs it for 16 < T <= 32
+ * without shared experts, in place of the sort launch: a token's routed expert GEMMs read
+ * each routed expert's weights once ("Zyphra Inference Wave 2", section "Quantization"),
+ * and a launch boundary costs microseconds at this size (the AMD megakernel blog, "What
+ * Drives the Speedup", 1. Megakernels).
+ *   ids     int32 [T, top_k], each in [0, E)
+ *   outputs h as for moe_gate_up_swiglu (identical values), and the sort arrays as for
+ *           moe_sort_by_expert (written).
+ *   T <= 32, T*top_k <= 256, E <= 1024 (MX_ERR_SHAPE otherwise); other arguments, limits
+ *   and the workspace as for moe_gate_up_swiglu.
+ */
+MX_API int moe_gate_up_swiglu_from_ids(const uint16_t* x, const int32_t* ids, const uint8_t* w_gate_up,
+                                       const uint8_t* s_gate_up, int32_t* counts, int32_t* offsets,
+                                       int32_t* sorted_slots, int32_t* active, int32_t* num_active, uint16_t* h,
+                                       int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k, void* workspace,
+                                       size_t workspace_bytes, void* stream);
 
 /*
  * Stage hook: the down GEMM with the gate-weighted combine, from gate_up's h and the sort

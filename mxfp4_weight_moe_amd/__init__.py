@@ -41,6 +41,8 @@ _lib.moe_sort_by_expert.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P
 _lib.moe_route_sort.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.moe_gate_up_swiglu.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P,
                                     ctypes.c_size_t, _P]
+_lib.moe_gate_up_swiglu_from_ids.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P,
+                                             ctypes.c_size_t, _P]
 _lib.moe_down_combine.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P,
                                   ctypes.c_size_t, _P]
 _lib.moe_mxfp4_workspace_size.restype = ctypes.c_size_t
@@ -58,14 +60,14 @@ _lib.mx_hbm_copy.argtypes = [_P, _P, ctypes.c_size_t, _P]
 for _n in ("mx_linear", "mxfp4_dequantize", "moe_route_topk", "moe_sort_by_expert", "moe_route_sort",
            "moe_gate_up_swiglu", "moe_down_combine", "moe_mxfp4_forward", "moe_mxfp4_forward_persistent",
            "moe_mxfp4_forward_shared", "moe_mxfp4_forward_a8", "mx_linear_a8", "mxfp8_quantize", "mx_hbm_read",
-           "mx_hbm_copy", "moe_mxfp4_forward_noalloc"):
+           "mx_hbm_copy", "moe_mxfp4_forward_noalloc", "moe_gate_up_swiglu_from_ids"):
     getattr(_lib, _n).restype = ctypes.c_int
 
 EXPORTED = ("mx_version", "mx_status_string", "mx_linear", "mxfp4_dequantize", "moe_route_topk",
             "moe_sort_by_expert", "moe_route_sort", "moe_gate_up_swiglu", "moe_down_combine",
             "moe_mxfp4_workspace_size", "moe_mxfp4_forward", "moe_mxfp4_forward_persistent",
             "moe_mxfp4_forward_shared", "moe_mxfp4_forward_a8", "mx_linear_a8", "mxfp8_quantize", "mx_hbm_read",
-            "mx_hbm_copy", "moe_mxfp4_forward_noalloc")
+            "mx_hbm_copy", "moe_mxfp4_forward_noalloc", "moe_gate_up_swiglu_from_ids")
 MX_ERR_SCRATCH = -6
 MX_NOALLOC_SCRATCH_BYTES = 40 << 20
 
@@ -304,6 +306,38 @@ def moe_gate_up_swiglu(x: torch.Tensor, W_gate_up: torch.Tensor, S_gate_up: torc
                                  E, top_k, _ptr(ws), ws.numel(), _stream(dev))
     _raise(st, "moe_gate_up_swiglu")
     return h
+
+
+def moe_gate_up_swiglu_from_ids(x: torch.Tensor, ids: torch.Tensor, W_gate_up: torch.Tensor, S_gate_up: torch.Tensor,
+                                h: torch.Tensor | None = None, sort: dict | None = None,
+                                ws: torch.Tensor | None = None):
+    """Stage hook for T <= 32: (h [T*k, I] bf16, sort dict) from the routed ids, the slots
+    sorted inside the gate_up launch (the sort equals moe_sort_by_expert's)."""
+    _check(x, "x", torch.bfloat16, 2)
+    dev = x.device
+    _check(ids, "ids", torch.int32, 2, dev)
+    _check(W_gate_up, "W_gate_up", torch.uint8, 3, dev)
+    _check(S_gate_up, "S_gate_up", torch.uint8, 3, dev)
+    T, H = x.shape
+    top_k = ids.shape[1]
+    E, two_i, _ = W_gate_up.shape
+    I = two_i // 2
+    if ids.shape[0] != T:
+        raise ValueError("ids must be [T, top_k]")
+    if W_gate_up.shape != (E, 2 * I, H // 2) or S_gate_up.shape != (E, 2 * I, H // 32):
+        raise ValueError("W_gate_up / S_gate_up shapes do not match [E, 2I, H/2] / [E, 2I, H/32]")
+    sort = _sort_out(sort, T, top_k, E, dev)
+    if h is None:
+        h = torch.empty((T * top_k, I), dtype=torch.bfloat16, device=dev)
+    _check(h, "h", torch.bfloat16, 2, dev)
+    if ws is None:
+        ws = workspace(T, H, I, E, top_k, dev)
+    _check(ws, "workspace", torch.uint8, 1, dev)
+    st = _lib.moe_gate_up_swiglu_from_ids(_ptr(x), _ptr(ids), _ptr(W_gate_up), _ptr(S_gate_up),
+                                          *[_ptr(sort[key]) for key in _SORT_KEYS], _ptr(h), T, H, I, E, top_k,
+                                          _ptr(ws), ws.numel(), _stream(dev))
+    _raise(st, "moe_gate_up_swiglu_from_ids")
+    return h, sort
 
 
 def moe_down_combine(h: torch.Tensor, gates: torch.Tensor, W_down: torch.Tensor, S_down: torch.Tensor, sort: dict,

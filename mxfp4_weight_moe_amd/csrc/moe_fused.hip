@@ -1,7 +1,8 @@
 // The whole MoE layer in one launch for small T: routing, sort, gate_up + SwiGLU, down and
 // the gate-weighted combine.  Also, at the end of this file, the layer forward's gate_up
-// launch for T <= 16, which does the routing and sort of this launch in each workgroup and
-// leaves down and the combine to their own launches.
+// launches for T <= 16, which does the routing and sort of this launch in each workgroup and
+// leaves down and the combine to their own launches, and for 16 < T <= 32, which sorts the
+// routed slots in each workgroup.
 //
 // At small T a layer streams only tens of microseconds of weights, and each kernel
 // boundary (the GPU draining one kernel and starting the next) costs microseconds.  The
@@ -422,6 +423,231 @@ static int launch_routed_per(const uint16_t* x, const float* logits, const uint8
   hipLaunchKernelGGL((moe_gate_up_routed_kernel<PER, 1, GU_SPS, A8>), grid, block, 0, stream, x, logits, wgu, sgu, h,
                      out, gates, T, H, I, E, k);
   return hip_status(hipGetLastError());
+}
+
+// ------------------------------------------------------------------ gate_up with its own sort
+
+// For 16 < T <= 32 the forward launches the routing alone (moe_route_kernel writes the ids
+// and gates), and every gate_up workgroup sorts the T k slots into LDS itself, replacing
+// the sort launch and the chain of dependent metadata loads at each item.  (Routing in
+// every workgroup, as the T <= 16 launch does, costs more than a launch at 32 tokens: each
+// wave would route 8 tokens one after another.)  The sort is the sort kernel's: counts and
+// offsets in expert order, slots stable by flat slot, the active list by row class
+// (heaviest first) and then expert id (-1 after the last); workgroup 0 writes it for the
+// down launch, equal to moe_sort_by_expert's on the same ids.
+constexpr int SORTED_MAX_T = 32;        // one 32-bit token mask per expert
+constexpr int SORTED_MAX_SLOTS = 256;   // T * k
+
+struct WgSort {
+  int32_t act[SORTED_MAX_SLOTS];      // expert of active expert a
+  int32_t cnt_off[SORTED_MAX_SLOTS];  // its count | its first sorted position << 16
+  int32_t slots[SORTED_MAX_SLOTS];    // flat slot at each sorted position
+  int32_t na;                         // active experts
+  int32_t max_rows;                   // largest count
+  int32_t wave_sum[WG_WAVES];
+  int32_t wave_max[WG_WAVES];
+  uint64_t wave_cls[WG_WAVES];
+};
+typedef __attribute__((address_space(3))) WgSort lds_wgsort;
+
+struct LdsSortW {
+  lds_wgsort* s;
+  __device__ __forceinline__ int num_active() const { return __builtin_amdgcn_readfirstlane(s->na); }
+  __device__ __forceinline__ int max_rows() const { return __builtin_amdgcn_readfirstlane(s->max_rows); }
+  __device__ __forceinline__ int expert(int a) const { return __builtin_amdgcn_readfirstlane(s->act[a]); }
+  __device__ __forceinline__ int count(int a) const { return __builtin_amdgcn_readfirstlane(s->cnt_off[a] & 0xFFFF); }
+  __device__ __forceinline__ int offset(int a) const { return __builtin_amdgcn_readfirstlane(s->cnt_off[a] >> 16); }
+  __device__ __forceinline__ int slot(int i) const { return __builtin_amdgcn_readfirstlane(s->slots[i]); }
+  __device__ __forceinline__ int count_lane(int a) const { return s->cnt_off[a] & 0xFFFF; }
+};
+
+// Row class as the sort kernel ranks it: 3 for 8 or more rows, 2 for 4-7, 1 for 2-3, 0 for 1.
+__device__ __forceinline__ int wg_row_class(int c) { return c >= 8 ? 3 : c >= 4 ? 2 : c >= 2 ? 1 : 0; }
+
+// Inclusive scan over the workgroup's threads (4 wavefronts) of a per-thread value, with
+// the wavefront totals in `ws`; returns the exclusive prefix and the total.
+template <class V, class WS>
+__device__ __forceinline__ V wg_exclusive_scan(V v, WS ws, V& total, int lane, int wave) {
+  V incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const V o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) ws[wave] = incl;
+  __syncthreads();
+  V before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < WG_WAVES; ++w) {
+    if (w < wave) before += ws[w];
+    total += ws[w];
+  }
+  return incl - v + before;
+}
+
+// The workgroup's sort of the T * k routed slots (ids: [T, k], T <= 32, E <= 1024) into
+// *ws, with `tmp` as 8 KB of scratch (token masks and expert offsets).  Each thread takes
+// 4 consecutive experts.  Must be called by all threads.
+__device__ __forceinline__ void wg_sort_slots(const int32_t* __restrict__ ids, int T, int E, int k, lds_wgsort* ws,
+                                              uint8_t* __restrict__ tmp) {
+  uint32_t* bits = reinterpret_cast<uint32_t*>(tmp);       // [E] token masks
+  int32_t* eoff = reinterpret_cast<int32_t*>(tmp + 4096);  // [E] first sorted position
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int F = T * k;
+  for (int i = tid; i < E; i += WG_WAVES * 64) bits[i] = 0u;
+  __syncthreads();
+  const int my_e = (tid < F) ? ids[tid] : -1;  // F <= 256 = one slot per thread
+  if (my_e >= 0 && my_e < E) atomicOr(&bits[my_e], 1u << (tid / k));
+  __syncthreads();
+  int c[4];
+  int packed = 0, most = 0;
+  uint64_t cls = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid * 4 + q;
+    c[q] = (e < E) ? __popc(bits[e]) : 0;
+    packed += c[q] | (c[q] > 0 ? (1 << 16) : 0);
+    if (c[q] > 0) cls += 1ull << (16 * wg_row_class(c[q]));
+    most = max(most, c[q]);
+  }
+  int ptot;
+  int run = wg_exclusive_scan(packed, ws->wave_sum, ptot, lane, wave);
+  uint64_t ctot;
+  uint64_t crun = wg_exclusive_scan(cls, ws->wave_cls, ctot, lane, wave);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) most = max(most, __shfl_xor(most, off));
+  if (lane == 0) ws->wave_max[wave] = most;
+  // the active list: heavier classes first (the totals of the classes above), then by id
+  int base[4];
+#pragma unroll
+  for (int cl = 0; cl < 4; ++cl) {
+    base[cl] = 0;
+    for (int d = cl + 1; d < 4; ++d) base[cl] += (int)((ctot >> (16 * d)) & 0xFFFFu);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid * 4 + q;
+    if (e < E) {
+      eoff[e] = run & 0xFFFF;
+      if (c[q] > 0) {
+        const int cl = wg_row_class(c[q]);
+        const int a = base[cl] + (int)((crun >> (16 * cl)) & 0xFFFFu);
+        ws->act[a] = e;
+        ws->cnt_off[a] = c[q] | ((run & 0xFFFF) << 16);
+        crun += 1ull << (16 * cl);
+      }
+    }
+    run += c[q] | (c[q] > 0 ? (1 << 16) : 0);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    ws->na = ptot >> 16;
+    int m = 0;
+    for (int w = 0; w < WG_WAVES; ++w) m = max(m, ws->wave_max[w]);
+    ws->max_rows = m;
+  }
+  if (my_e >= 0 && my_e < E) {
+    const int t = tid / k;
+    ws->slots[eoff[my_e] + __popc(bits[my_e] & ((1u << t) - 1u))] = tid;
+  }
+  __syncthreads();
+}
+
+template <int NS, int SPS, bool A8>
+__global__ void __launch_bounds__(WG_WAVES * 64) moe_gate_up_sorted_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, const uint8_t* __restrict__ wgu,
+    const uint8_t* __restrict__ sgu, uint16_t* __restrict__ h, SortOut out, int T, int H, int I, int E, int k,
+    int32_t* claim) {
+  __shared__ __attribute__((aligned(16))) uint8_t xbufs[2 * GU_XCHUNK];
+  __shared__ __attribute__((aligned(16))) uint8_t slabs[WG_WAVES][SLAB_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t sslabs[WG_WAVES][ScaleRun4::slab_bytes<NS>()];
+  __shared__ uint32_t xctr[2];
+  __shared__ int32_t cq[4];
+  __shared__ WgSort wsort;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  if (tid < 2) xctr[tid] = 0u;
+  lds_wgsort* ws = (lds_wgsort*)&wsort;
+  wg_sort_slots(ids, T, E, k, ws, xbufs);
+  const LdsSortW meta{ws};
+  const int na = meta.num_active();
+  if (blockIdx.x == 0) {
+    // the token masks and expert offsets are still in the sort scratch (xbufs)
+    const uint32_t* bits = reinterpret_cast<const uint32_t*>(xbufs);
+    const int32_t* eoff = reinterpret_cast<const int32_t*>(xbufs + 4096);
+    for (int e = tid; e < E; e += WG_WAVES * 64) {
+      out.counts[e] = __popc(bits[e]);
+      out.offsets[e] = eoff[e];
+    }
+    for (int i = tid; i < T * k; i += WG_WAVES * 64) out.sorted_slots[i] = ws->slots[i];
+    for (int a = tid; a < E; a += WG_WAVES * 64) out.active[a] = a < na ? ws->act[a] : -1;
+    if (tid == 0) {
+      out.offsets[E] = T * k;
+      out.num_active[0] = na;
+      out.num_active[1] = ws->max_rows;
+    }
+  }
+  __syncthreads();  // the sort scratch has been read; the stream reuses xbufs
+  using PG = GateUpPolicy<NS, LdsSortW, GU_XCHUNK, false, A8>;
+  PG p;
+  p.m = meta;
+  p.xrowsegs = XGeom<GU_XCHUNK>::ROWSEGS;
+  p.calign = SPS;
+  p.nseg = H / SEG_K;
+  p.nquad = I / (PG::TILE * WG_WAVES);
+  p.na = na;
+  p.n_items = ((meta.max_rows() + 15) >> 4) * na * p.nquad;  // row-group levels that exist
+  p.xact = x;
+  p.wgu = wgu;
+  p.sgu = sgu;
+  p.h = h;
+  p.H = H;
+  p.I = I;
+  p.k = k;
+  p.kinv = ((1u << 24) + (uint32_t)k - 1u) / (uint32_t)k;
+  p.e_codes = (size_t)2 * I * (H / 2);
+  p.e_scales = (size_t)2 * I * (H / 32);
+  ClaimedUnits seq{claim, (lds_i32*)cq, na * p.nquad, 0, false};
+  stream_items<PG, SPS>(p, seq, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
+  seq.finish();
+}
+
+template <bool A8>
+static int launch_sorted_run(const uint16_t* x, const int32_t* ids, const uint8_t* wgu, const uint8_t* sgu,
+                             uint16_t* h, const SortOut& out, int32_t* claim, int T, int H, int I, int E, int k,
+                             hipStream_t stream) {
+  static const int occ2 = routed_occupancy(moe_gate_up_sorted_kernel<2, GU_SPS, A8>);
+  static const int occ1 = routed_occupancy(moe_gate_up_sorted_kernel<1, GU_SPS, A8>);
+  const int64_t na_max = (int64_t)T * k < E ? (int64_t)T * k : E;
+  const int64_t items_full = ((T + 15) / 16) * na_max * (I / (SUB_ROWS * WG_WAVES));
+  const int64_t cus = device_cu_count();
+  const dim3 block(WG_WAVES * 64);
+  if (2 * items_full > cus * occ1) {
+    const dim3 grid((unsigned)(items_full < cus * occ2 ? items_full : cus * occ2));
+    hipLaunchKernelGGL((moe_gate_up_sorted_kernel<2, GU_SPS, A8>), grid, block, 0, stream, x, ids, wgu, sgu, h, out,
+                       T, H, I, E, k, claim);
+  } else {
+    const dim3 grid((unsigned)(2 * items_full));
+    hipLaunchKernelGGL((moe_gate_up_sorted_kernel<1, GU_SPS, A8>), grid, block, 0, stream, x, ids, wgu, sgu, h, out,
+                       T, H, I, E, k, claim);
+  }
+  return hip_status(hipGetLastError());
+}
+
+bool gate_up_sorted_fits(int T, int E, int k, int H, int I) {
+  return T <= SORTED_MAX_T && T * k <= SORTED_MAX_SLOTS && E <= 1024 && H % (SEG_K * GU_SPS) == 0 &&
+         H % (SEG_K * SRUN) == 0 && I % (SUB_ROWS * WG_WAVES) == 0;
+}
+
+int launch_gate_up_sorted(const uint16_t* x, const int32_t* ids, const uint8_t* wgu, const uint8_t* sgu, uint16_t* h,
+                          int32_t* counts, int32_t* offsets, int32_t* sorted_slots, int32_t* active,
+                          int32_t* num_active, int32_t* ctl, int T, int H, int I, int E, int k, bool act8,
+                          hipStream_t stream) {
+  if (!gate_up_sorted_fits(T, E, k, H, I)) return MX_ERR_SHAPE;
+  const SortOut out{counts, offsets, sorted_slots, active, num_active};
+  if (act8) return launch_sorted_run<true>(x, ids, wgu, sgu, h, out, ctl + CTL_CLAIM_GU, T, H, I, E, k, stream);
+  return launch_sorted_run<false>(x, ids, wgu, sgu, h, out, ctl + CTL_CLAIM_GU, T, H, I, E, k, stream);
 }
 
 // Measured against the route + sort launch followed by gate_up (graph replay, 4 layers):

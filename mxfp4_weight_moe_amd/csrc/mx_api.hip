@@ -230,6 +230,26 @@ int moe_gate_up_swiglu(const uint16_t* x, const uint8_t* w_gate_up, const uint8_
                         static_cast<hipStream_t>(stream));
 }
 
+int moe_gate_up_swiglu_from_ids(const uint16_t* x, const int32_t* ids, const uint8_t* w_gate_up,
+                                const uint8_t* s_gate_up, int32_t* counts, int32_t* offsets, int32_t* sorted_slots,
+                                int32_t* active, int32_t* num_active, uint16_t* h, int64_t T, int64_t H, int64_t I,
+                                int64_t E, int64_t top_k, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !ids || !w_gate_up || !s_gate_up || !h || !sort_view_ok(counts, offsets, sorted_slots, active, num_active))
+    return MX_ERR_NULL;
+  int st = check_moe_sizes(T, E, top_k);
+  if (st != MX_OK || (st = check_expert_dims(H, I)) != MX_OK) return st;
+  if (!gate_up_sorted_fits((int)T, (int)E, (int)top_k, (int)H, (int)I)) return MX_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(ids, 4) || !aligned(w_gate_up, 16) || !aligned(s_gate_up, 16) || !aligned(h, 8) ||
+      !sort_view_aligned(counts, offsets, sorted_slots, active, num_active))
+    return MX_ERR_ALIGN;
+  if (!workspace || !aligned(workspace, 256)) return MX_ERR_WORKSPACE;
+  const MoeWorkspace ws = moe_workspace_carve(workspace, T, H, I, E, top_k);
+  if (workspace_bytes < ws.bytes) return MX_ERR_WORKSPACE;
+  return launch_gate_up_sorted(x, ids, w_gate_up, s_gate_up, h, counts, offsets, sorted_slots, active, num_active,
+                               ws.ctl, (int)T, (int)H, (int)I, (int)E, (int)top_k, false,
+                               static_cast<hipStream_t>(stream));
+}
+
 int moe_down_combine(const uint16_t* h, const float* gates, const uint8_t* w_down, const uint8_t* s_down,
                      const int32_t* counts, const int32_t* offsets, const int32_t* sorted_slots, const int32_t* active,
                      const int32_t* num_active, uint16_t* y, int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k,
@@ -293,6 +313,12 @@ static int moe_forward_impl(const uint16_t* x, const float* router_logits, int64
     if ((st = launch_gate_up_routed(x, router_logits, w_gate_up, s_gate_up, ws.h, ws.counts, ws.offsets,
                                     ws.sorted_slots, ws.active, ws.num_active, ws.gates, t, h, i, e, k, act8, s)) !=
         MX_OK)
+      return st;
+  } else if (n == 0 && gate_up_sorted_fits(t, e, k, h, i)) {
+    // up to 32 tokens: the routing launch, then gate_up sorts the slots in every workgroup
+    if ((st = launch_route(router_logits, t, e, k, 0, ws.ids, ws.gates, s)) != MX_OK) return st;
+    if ((st = launch_gate_up_sorted(x, ws.ids, w_gate_up, s_gate_up, ws.h, ws.counts, ws.offsets, ws.sorted_slots,
+                                    ws.active, ws.num_active, ws.ctl, t, h, i, e, k, act8, s)) != MX_OK)
       return st;
   } else {
     if ((st = launch_route_sort(router_logits, t, e, k, n, ws.ids, ws.gates, ws.counts, ws.offsets, ws.sorted_slots,

@@ -94,6 +94,13 @@ int launch_combine(const float* dpart, const float* gates, uint16_t* y, int T, i
 // route + sort launch before it); it also writes the sort outputs and gates for the down
 // launch.  gate_up_routed_fits says when it applies (no shared experts); act8: MXFP8
 // activations, as launch_gate_up.
+// The forward's gate_up for 16 < T <= 32: sorts the routed ids (moe_route_kernel's output)
+// in every workgroup and writes the sort for the down launch.
+bool gate_up_sorted_fits(int T, int E, int k, int H, int I);
+int launch_gate_up_sorted(const uint16_t* x, const int32_t* ids, const uint8_t* wgu, const uint8_t* sgu, uint16_t* h,
+                          int32_t* counts, int32_t* offsets, int32_t* sorted_slots, int32_t* active,
+                          int32_t* num_active, int32_t* ctl, int T, int H, int I, int E, int k, bool act8,
+                          hipStream_t stream);
 bool gate_up_routed_fits(int T, int E, int k, int H, int I);
 int launch_gate_up_routed(const uint16_t* x, const float* logits, const uint8_t* wgu, const uint8_t* sgu, uint16_t* h,
                           int32_t* counts, int32_t* offsets, int32_t* sorted_slots, int32_t* active,

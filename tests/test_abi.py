@@ -162,6 +162,20 @@ def test_stage_gemm_hooks_reject():
     assert gu(w=P((1 << 20) + 128)) == MX_ERR_WORKSPACE
     assert gu(wb=ws - 1) == MX_ERR_WORKSPACE
 
+    def gi(x=A, ids=A, h=A, T=4, H=1024, I=1024, E=8, k=2, w=A, wb=ws):
+        return L.moe_gate_up_swiglu_from_ids(x, ids, A, A, A, A, A, A, A, h, T, H, I, E, k, w, wb, None)
+
+    assert gi(ids=None) == MX_ERR_NULL
+    assert gi(h=None) == MX_ERR_NULL
+    assert gi(T=0) == MX_ERR_SHAPE
+    assert gi(T=33, E=64) == MX_ERR_SHAPE  # the in-launch sort holds one 32-bit token mask per expert
+    assert gi(T=32, k=9, E=64) == MX_ERR_SHAPE  # at most 256 slots
+    assert gi(H=1536) == MX_ERR_SHAPE
+    assert gi(ids=P((1 << 20) + 2)) == MX_ERR_ALIGN
+    assert gi(x=MIS) == MX_ERR_ALIGN
+    assert gi(w=None) == MX_ERR_WORKSPACE
+    assert gi(wb=ws - 1) == MX_ERR_WORKSPACE
+
     def dn(h=A, y=A, T=4, w=A, wb=ws):
         return L.moe_down_combine(h, A, A, A, A, A, A, A, A, y, T, 1024, 1024, 8, 2, w, wb, None)
 

@@ -480,14 +480,30 @@ def check_h(got_bits, ora_bits, terms, what):
     return flips, go.size, int((~one_value).sum())
 
 
-def gate_up_h_parity(mx, dev, cfg, d, x, logits, w_host, tokens=None):
-    """h from the gate_up stage entry point (after the route + sort entry point), on a
-    NaN-poisoned workspace into a NaN-filled h, against the oracle's h of the listed tokens."""
+def poisoned_sort(T, k, E, dev):
+    """Sort output tensors filled with a value no entry point writes (every entry must be written)."""
+    return {key: torch.full((n,), -7, dtype=torch.int32, device=dev)
+            for key, n in (("counts", E), ("offsets", E + 1), ("sorted_slots", T * k), ("active", E),
+                           ("num_active", 2))}
+
+
+def gate_up_h_parity(mx, dev, cfg, d, x, logits, w_host, tokens=None, from_ids=False):
+    """h from a gate_up stage entry point, on a NaN-poisoned workspace into a NaN-filled h,
+    against the oracle's h of the listed tokens: moe_gate_up_swiglu after the route + sort
+    entry point, or (from_ids) moe_gate_up_swiglu_from_ids after the route entry point, whose
+    sort, written into poisoned tensors, must equal the oracle's."""
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
-    ids, gates, srt = mx.moe_route_sort(d["logits"], k)
     ws = poisoned_workspace(mx, T, H, I, E, k, dev)
     h = nan_like_out((T * k, I), dev)
-    mx.moe_gate_up_swiglu(d["x"], d["wgu"], d["sgu"], srt, k, h=h, ws=ws)
+    if from_ids:
+        ids, gates = mx.moe_route_topk(d["logits"], k)
+        _, srt = mx.moe_gate_up_swiglu_from_ids(d["x"], ids, d["wgu"], d["sgu"], h=h, sort=poisoned_sort(T, k, E, dev),
+                                                ws=ws)
+        torch.cuda.synchronize()
+        check_sort(srt, oracle.sort(ids.cpu().numpy(), E))
+    else:
+        ids, gates, srt = mx.moe_route_sort(d["logits"], k)
+        mx.moe_gate_up_swiglu(d["x"], d["wgu"], d["sgu"], srt, k, h=h, ws=ws)
     torch.cuda.synchronize()
     hg = to_host_bits(h)                        # row p: the slot at sorted position p
     slots = srt["sorted_slots"].cpu().numpy()
@@ -532,6 +548,47 @@ def test_gate_up_h_matches_oracle_full_size(dev, mx, name, tokens):
     d, x, logits = moe_device_inputs(cfg, dev)
     w_host = {key: d[key].cpu().numpy() for key in ("wgu", "sgu", "wd", "sd")}
     flips, n, wide = gate_up_h_parity(mx, dev, cfg, d, x, logits, w_host, tokens)
+    say(f"  {flips} flips of {n} h values ({wide} within reach of a rounding boundary)")
+
+
+# gate_up that sorts the slots itself (T <= 32, T k <= 256, E <= 1024): experts with two row
+# groups (17 and 32 rows), I = 256 and 512, E = 1024 (four experts per thread in its count
+# scan), a small T the entry point also accepts, and every expert routed by every token
+FROM_IDS = [dict(T=17, H=1024, I=1024, E=4, k=4), dict(T=20, H=2048, I=512, E=6, k=3),
+            dict(T=32, H=1024, I=256, E=300, k=8), dict(T=32, H=1024, I=1024, E=1024, k=8),
+            dict(T=3, H=1024, I=1024, E=8, k=2), dict(T=32, H=3072, I=1024, E=2, k=2),
+            dict(T=25, H=2048, I=1024, E=64, k=1)]
+
+
+@pytest.mark.parametrize("shape", FROM_IDS, ids=[f"T{s['T']}_H{s['H']}_I{s['I']}_E{s['E']}_k{s['k']}" for s in FROM_IDS])
+def test_gate_up_from_ids_matches_oracle(dev, mx, shape):
+    """moe_gate_up_swiglu_from_ids: its sort bit-exact against the oracle's (active list in
+    row-class order, -1 after it), its h against the oracle's h, and the same h bit for bit as
+    moe_gate_up_swiglu after the route + sort entry point."""
+    cfg = synthetic.MoEConfig("from_ids", routing="normal", e_lo=-8, e_hi=-2, seed=shape["T"] * 11 + shape["E"],
+                              **shape)
+    host = synthetic.moe_inputs_host(cfg)
+    say("gate_up from ids, tiny", shape)
+    d, x, logits = moe_device_inputs(cfg, dev, host)
+    flips, n, wide = gate_up_h_parity(mx, dev, cfg, d, x, logits, host, from_ids=True)
+    say(f"  {flips} flips of {n} h values ({wide} within reach of a rounding boundary)")
+    ids, _, srt = mx.moe_route_sort(d["logits"], cfg.k)
+    h_sep = mx.moe_gate_up_swiglu(d["x"], d["wgu"], d["sgu"], srt, cfg.k)
+    h_ids, srt2 = mx.moe_gate_up_swiglu_from_ids(d["x"], ids, d["wgu"], d["sgu"])
+    torch.cuda.synchronize()
+    for key in ("counts", "offsets", "sorted_slots", "active", "num_active"):
+        assert torch.equal(srt[key], srt2[key]), key
+    assert np.array_equal(to_host_bits(h_ids), to_host_bits(h_sep))
+
+
+def test_gate_up_from_ids_full_size(dev, mx):
+    """The same at T = 32, H = 7168, I = 2048, E = 256, top-8 with Zipf routing (the hot experts
+    have two row groups), the launch the layer forward makes at that size: every routed row."""
+    cfg = synthetic.MOE_CONFIGS["moe_t32_zipf"]
+    say("gate_up from ids, full size", cfg.name)
+    d, x, logits = moe_device_inputs(cfg, dev)
+    w_host = {key: d[key].cpu().numpy() for key in ("wgu", "sgu", "wd", "sd")}
+    flips, n, wide = gate_up_h_parity(mx, dev, cfg, d, x, logits, w_host, from_ids=True)
     say(f"  {flips} flips of {n} h values ({wide} within reach of a rounding boundary)")
 
 
