@@ -133,11 +133,13 @@ def gpu_clocks() -> dict:
     return out
 
 
-def forward_path(T: int, k: int, E: int, ns: int) -> str:
+def forward_path(T: int, k: int, E: int, ns: int, I: int, H: int, act8: bool = False) -> str:
     """The launches moe_mxfp4_forward makes for these sizes (its dispatch)."""
     if ns == 0 and T <= 16 and T * k <= 128:
         return "gate_up (routing and sorting in every workgroup), down, combine launches (combine inside down at the smallest T)"
     if ns == 0 and T <= 32 and T * k <= 256 and E <= 1024:
+        if not act8 and I % 1024 == 0 and H % 128 == 0 and min(T * k, E) * (I // 64) >= 512:
+            return "route, gate_up + down (one launch, sorting in every workgroup), combine launches"
         return "route, gate_up (sorting in every workgroup), down, combine launches"
     return "route_sort, gate_up, down, combine launches"
 
@@ -270,10 +272,15 @@ def moe_case(cfg, args, torch, mx, dev, *, steps: int, warmup: int, stage_pass: 
                active=torch.empty(E, dtype=torch.int32, device=dev),
                num_active=torch.empty(2, dtype=torch.int32, device=dev))
     h = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
-    # From 17 to 32 tokens (no shared experts) the forward routes in a launch of its own and
-    # gate_up sorts the slots in every workgroup; the per-kernel pass issues the same calls.
-    sorted_path = ns == 0 and 16 < T <= 32 and T * k <= 256 and E <= 1024
-    names = ("layer",) if whole_layer else (("route", "gate_up", "down_combine") if sorted_path
+    d = torch.empty((T * k, H), dtype=torch.float32, device=dev)
+    # From 17 to 32 tokens (no shared experts) the forward routes in a launch of its own, then
+    # runs both expert GEMMs in one launch (or, where that does not apply, a gate_up that
+    # sorts the slots in every workgroup); the per-kernel pass issues the same calls.
+    path = forward_path(T, k, E, ns, I, H)
+    single_path = not whole_layer and path.startswith("route, gate_up + down")
+    sorted_path = not whole_layer and path.startswith("route, gate_up (")
+    names = ("layer",) if whole_layer else (("route", "gate_up_down", "combine") if single_path else
+                                           ("route", "gate_up", "down_combine") if sorted_path
                                            else ("route_sort", "gate_up", "down_combine"))
     n_active = []
     for lay in layers:
@@ -293,6 +300,17 @@ def moe_case(cfg, args, torch, mx, dev, *, steps: int, warmup: int, stage_pass: 
             e[0].record(stream)
             forward(lay)
             e[1].record(stream)
+            return
+        if single_path:
+            h.view(torch.int16).fill_(-1)  # the expert launch's "not yet written" pattern
+            e[0].record(stream)
+            mx.moe_route_topk(lay["logits"], k, ids=ids, gates=gates)
+            e[1].record(stream)
+            mx.moe_expert_gemms_from_ids(lay["x"], ids, w["wgu"], w["sgu"], w["wd"], w["sd"], h=h, d=d, ws=ws,
+                                         fill_h=False)
+            e[2].record(stream)
+            mx.moe_combine(d, gates, out=lay["y"])
+            e[3].record(stream)
             return
         e[0].record(stream)
         if sorted_path:
@@ -382,7 +400,8 @@ def moe_case(cfg, args, torch, mx, dev, *, steps: int, warmup: int, stage_pass: 
             "weights": "MXFP4 (E2M1 codes, E8M0 scale per 32)", "accumulate": "fp32",
             "activations": "MXFP8 (E4M3, E8M0 scale per 32), quantized in the GEMM kernels" if args.act8 else "bf16",
             "layers_cycled": L, "timing": "eager launches" if args.eager else "HIP graph replay",
-            "path": "one persistent launch" if args.persistent else forward_path(T, k, E, ns),
+            "path": "one persistent launch" if args.persistent else
+            forward_path(T, k, E, ns, I, H, act8=args.act8),
         },
     }
 
@@ -411,6 +430,11 @@ def moe_case(cfg, args, torch, mx, dev, *, steps: int, warmup: int, stage_pass: 
         if whole_layer:
             gu_bytes = [layer_bytes[i % L] for i in range(KS)]
             gu_ms = stage_ms["layer"]
+        elif single_path:
+            # both expert GEMMs: their experts' codes + scales, x read, h written and read, d written
+            gu_bytes = [n_active[i % L] * (gu_expert + dn_expert) + T * H * 2 + 2 * T * k * I * 2 + T * k * H * 4
+                        for i in range(KS)]
+            gu_ms = stage_ms["gate_up_down"]
         else:
             # gate_up per launch: its experts' codes + scales, x read once, h written
             gu_bytes = [n_active[i % L] * gu_expert + T * H * 2 + T * k * I * 2 for i in range(KS)]
@@ -420,7 +444,8 @@ def moe_case(cfg, args, torch, mx, dev, *, steps: int, warmup: int, stage_pass: 
         res["staged_us_per_layer"] = round(sev[0][0].elapsed_time(sev[-1][-1]) * 1e3 / KS, 2)
         res["roofline"] = {
             "kernel": ("moe_fused_kernel" if args.persistent else "layer (all launches)") if whole_layer
-            else ("moe_gate_up_sorted_kernel" if sorted_path else "moe_gate_up_kernel"),
+            else ("moe_experts_sorted_kernel" if single_path else
+                  "moe_gate_up_sorted_kernel" if sorted_path else "moe_gate_up_kernel"),
             "bound": "hbm", "achieved": round(gu_achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(gu_achieved / HBM_PEAK_GBPS, 4),
             "traffic": None if whole_layer else measured_traffic(cfg.name),

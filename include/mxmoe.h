@@ -156,7 +156,8 @@ MX_API int moe_sort_by_expert(const int32_t* ids, int64_t T, int64_t top_k, int6
  * moe_route_topk followed by moe_sort_by_expert of its ids: one launch for T <= 16, two
  * beyond.  moe_mxfp4_forward runs it as its first stage beyond 32 tokens (and with shared
  * experts); up to 16 tokens its gate_up launch routes and sorts in every workgroup instead,
- * and from 17 to 32 it routes alone and gate_up sorts (moe_gate_up_swiglu_from_ids).
+ * and from 17 to 32 it routes alone and its expert launch sorts (moe_expert_gemms_from_ids,
+ * or moe_gate_up_swiglu_from_ids where that one does not apply).
  * That internal sort has the same counts, offsets and sorted slots, but keeps its active
  * list in ascending expert order and leaves the entries past the last one unwritten (its
  * down launch accepts any order).  Arguments, outputs and limits as for those two calls.
@@ -186,7 +187,8 @@ MX_API int moe_gate_up_swiglu(const uint16_t* x, const uint8_t* w_gate_up, const
  * sorting the slots inside the launch: every workgroup sorts the T*top_k slots itself, and
  * the launch also writes the sort (counts, offsets, sorted_slots, active, num_active), equal
  * to moe_sort_by_expert's on the same ids.  moe_mxfp4_forward runs it for 16 < T <= 32
- * without shared experts, in place of the sort launch: a token's routed expert GEMMs read
+ * without shared experts where moe_expert_gemms_from_ids does not apply (MXFP8 activations,
+ * I % 1024 != 0, or too few items to fill the grid), in place of the sort launch: a token's routed expert GEMMs read
  * each routed expert's weights once ("Zyphra Inference Wave 2", section "Quantization"),
  * and a launch boundary costs microseconds at this size (the AMD megakernel blog, "What
  * Drives the Speedup", 1. Megakernels).
@@ -201,6 +203,44 @@ MX_API int moe_gate_up_swiglu_from_ids(const uint16_t* x, const int32_t* ids, co
                                        int32_t* sorted_slots, int32_t* active, int32_t* num_active, uint16_t* h,
                                        int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k, void* workspace,
                                        size_t workspace_bytes, void* stream);
+
+/*
+ * Stage hook: both expert GEMMs in one launch, straight from the routed ids, as
+ * moe_mxfp4_forward runs them for 16 < T <= 32 without shared experts: every workgroup sorts
+ * the T*top_k slots itself, streams its share of the gate_up items and then its share of the
+ * down items, so that down work fills the end of the gate_up work ("Zyphra Inference Wave 2",
+ * Kernel Results, for the two GEMMs of an MXFP4 expert; the AMD megakernel blog, "What Drives
+ * the Speedup", 1. Megakernels, for removing the boundary between dependent kernels).
+ *   ids  int32 [T, top_k], each row top_k distinct ids in [0, E) (moe_route_topk's output)
+ *   h    bf16 [T*top_k, I].  In: every element 0xFFFF.  The down items recognise rows that
+ *        gate_up has not written yet by that pattern (0xFFFF is a NaN that SwiGLU produces
+ *        only from NaN inputs; if it does, the launch only waits longer).  Out: h as
+ *        moe_gate_up_swiglu writes it (identical values; rows in sorted-slot order).
+ *   d    fp32 [T*top_k, H] (written): d[t*top_k + j, n] = sum_i h[p(t,j), i] * Wd[e][n, i]
+ *        (fp32), the slot's down output before its gate; moe_combine makes y from it.
+ * The launch's workgroups may wait for one another: a down item that finds an unwritten h
+ * row waits until every workgroup has finished its gate_up items.  The grid is sized to what
+ * the device holds at once, so all of them run; a wait that outlasts any layer by far gives
+ * up, leaves d undefined and sets the int32 at byte offset 8 of the workspace to 1 (sticky,
+ * as for moe_mxfp4_forward_persistent).  It applies when T <= 32, T*top_k <= 256,
+ * E <= 1024, I % 1024 == 0 and the gate_up items fill the grid (min(T*top_k, E) * I / 64 at
+ * least the device's resident workgroups, 512 on MI355X); MX_ERR_SHAPE otherwise.  Other
+ * arguments, limits and the workspace as for moe_gate_up_swiglu.
+ */
+MX_API int moe_expert_gemms_from_ids(const uint16_t* x, const int32_t* ids, const uint8_t* w_gate_up,
+                                     const uint8_t* s_gate_up, const uint8_t* w_down, const uint8_t* s_down,
+                                     uint16_t* h, float* d, int64_t T, int64_t H, int64_t I, int64_t E,
+                                     int64_t top_k, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Stage hook: the gate-weighted combine, y[t, n] = bf16_rne( sum_j gates[t, j] * d[t*top_k + j, n] )
+ * in fp32, j ascending (the last step of moe_mxfp4_forward; "Zyphra Inference Wave 2",
+ * section "Quantization": the routed experts' outputs are combined with their router weights).
+ *   d      fp32 [T*top_k, H]   gates  fp32 [T, top_k]   y  bf16 [T, H] (written)
+ *   1 <= T <= MX_MAX_TOKENS, 1 <= top_k <= MX_MAX_TOPK, 4 <= H <= 65536, H % 4 == 0.
+ */
+MX_API int moe_combine(const float* d, const float* gates, uint16_t* y, int64_t T, int64_t H, int64_t top_k,
+                       void* stream);
 
 /*
  * Stage hook: the down GEMM with the gate-weighted combine, from gate_up's h and the sort

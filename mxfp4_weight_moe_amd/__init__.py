@@ -45,6 +45,9 @@ _lib.moe_gate_up_swiglu_from_ids.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P,
                                              ctypes.c_size_t, _P]
 _lib.moe_down_combine.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P,
                                   ctypes.c_size_t, _P]
+_lib.moe_expert_gemms_from_ids.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P,
+                                           ctypes.c_size_t, _P]
+_lib.moe_combine.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P]
 _lib.moe_mxfp4_workspace_size.restype = ctypes.c_size_t
 _lib.moe_mxfp4_workspace_size.argtypes = [_I64, _I64, _I64, _I64, _I64]
 _lib.moe_mxfp4_forward.argtypes = [_P, _P, _I64, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]
@@ -60,14 +63,16 @@ _lib.mx_hbm_copy.argtypes = [_P, _P, ctypes.c_size_t, _P]
 for _n in ("mx_linear", "mxfp4_dequantize", "moe_route_topk", "moe_sort_by_expert", "moe_route_sort",
            "moe_gate_up_swiglu", "moe_down_combine", "moe_mxfp4_forward", "moe_mxfp4_forward_persistent",
            "moe_mxfp4_forward_shared", "moe_mxfp4_forward_a8", "mx_linear_a8", "mxfp8_quantize", "mx_hbm_read",
-           "mx_hbm_copy", "moe_mxfp4_forward_noalloc", "moe_gate_up_swiglu_from_ids"):
+           "mx_hbm_copy", "moe_mxfp4_forward_noalloc", "moe_gate_up_swiglu_from_ids", "moe_expert_gemms_from_ids",
+           "moe_combine"):
     getattr(_lib, _n).restype = ctypes.c_int
 
 EXPORTED = ("mx_version", "mx_status_string", "mx_linear", "mxfp4_dequantize", "moe_route_topk",
             "moe_sort_by_expert", "moe_route_sort", "moe_gate_up_swiglu", "moe_down_combine",
             "moe_mxfp4_workspace_size", "moe_mxfp4_forward", "moe_mxfp4_forward_persistent",
             "moe_mxfp4_forward_shared", "moe_mxfp4_forward_a8", "mx_linear_a8", "mxfp8_quantize", "mx_hbm_read",
-            "mx_hbm_copy", "moe_mxfp4_forward_noalloc", "moe_gate_up_swiglu_from_ids")
+            "mx_hbm_copy", "moe_mxfp4_forward_noalloc", "moe_gate_up_swiglu_from_ids", "moe_expert_gemms_from_ids",
+            "moe_combine")
 MX_ERR_SCRATCH = -6
 MX_NOALLOC_SCRATCH_BYTES = 40 << 20
 
@@ -338,6 +343,65 @@ def moe_gate_up_swiglu_from_ids(x: torch.Tensor, ids: torch.Tensor, W_gate_up: t
                                           _ptr(ws), ws.numel(), _stream(dev))
     _raise(st, "moe_gate_up_swiglu_from_ids")
     return h, sort
+
+
+def moe_expert_gemms_from_ids(x: torch.Tensor, ids: torch.Tensor, W_gate_up: torch.Tensor, S_gate_up: torch.Tensor,
+                              W_down: torch.Tensor, S_down: torch.Tensor, h: torch.Tensor | None = None,
+                              d: torch.Tensor | None = None, ws: torch.Tensor | None = None, fill_h: bool = True):
+    """Stage hook for 16 < T <= 32: both expert GEMMs in one launch from the routed ids:
+    (h [T*k, I] bf16 in sorted-slot order, d [T*k, H] fp32 down outputs by flat slot).
+    The launch needs every element of h at 0xFFFF when it starts: fill_h=True fills it here
+    (on the current stream); with fill_h=False the caller has done so."""
+    _check(x, "x", torch.bfloat16, 2)
+    dev = x.device
+    _check(ids, "ids", torch.int32, 2, dev)
+    for t, n in ((W_gate_up, "W_gate_up"), (S_gate_up, "S_gate_up"), (W_down, "W_down"), (S_down, "S_down")):
+        _check(t, n, torch.uint8, 3, dev)
+    T, H = x.shape
+    top_k = ids.shape[1]
+    E = W_gate_up.shape[0]
+    I = W_down.shape[2] * 2
+    if ids.shape[0] != T:
+        raise ValueError("ids must be [T, top_k]")
+    if (W_gate_up.shape != (E, 2 * I, H // 2) or S_gate_up.shape != (E, 2 * I, H // 32)
+            or W_down.shape != (E, H, I // 2) or S_down.shape != (E, H, I // 32)):
+        raise ValueError("expert weight shapes do not match [E, 2I, H/2], [E, 2I, H/32], [E, H, I/2], [E, H, I/32]")
+    if h is None:
+        h = torch.empty((T * top_k, I), dtype=torch.bfloat16, device=dev)
+    if d is None:
+        d = torch.empty((T * top_k, H), dtype=torch.float32, device=dev)
+    _check(h, "h", torch.bfloat16, 2, dev)
+    _check(d, "d", torch.float32, 2, dev)
+    if h.shape != (T * top_k, I) or d.shape != (T * top_k, H):
+        raise ValueError("h must be [T*top_k, I] and d [T*top_k, H]")
+    if fill_h:
+        h.view(torch.int16).fill_(-1)
+    if ws is None:
+        ws = workspace(T, H, I, E, top_k, dev)
+    _check(ws, "workspace", torch.uint8, 1, dev)
+    st = _lib.moe_expert_gemms_from_ids(_ptr(x), _ptr(ids), _ptr(W_gate_up), _ptr(S_gate_up), _ptr(W_down),
+                                        _ptr(S_down), _ptr(h), _ptr(d), T, H, I, E, top_k, _ptr(ws), ws.numel(),
+                                        _stream(dev))
+    _raise(st, "moe_expert_gemms_from_ids")
+    return h, d
+
+
+def moe_combine(d: torch.Tensor, gates: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Stage hook: y [T, H] bf16 = sum_j gates[t, j] d[t*k + j] (fp32, j ascending)."""
+    _check(d, "d", torch.float32, 2)
+    dev = d.device
+    _check(gates, "gates", torch.float32, 2, dev)
+    T, top_k = gates.shape
+    H = d.shape[1]
+    if d.shape[0] != T * top_k:
+        raise ValueError("d must be [T*top_k, H] for gates [T, top_k]")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, 2, dev)
+    if out.shape != (T, H):
+        raise ValueError("out must be [T, H]")
+    _raise(_lib.moe_combine(_ptr(d), _ptr(gates), _ptr(out), T, H, top_k, _stream(dev)), "moe_combine")
+    return out
 
 
 def moe_down_combine(h: torch.Tensor, gates: torch.Tensor, W_down: torch.Tensor, S_down: torch.Tensor, sort: dict,

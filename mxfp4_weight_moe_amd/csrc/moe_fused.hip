@@ -650,6 +650,169 @@ int launch_gate_up_sorted(const uint16_t* x, const int32_t* ids, const uint8_t* 
   return launch_sorted_run<false>(x, ids, wgu, sgu, h, out, ctl + CTL_CLAIM_GU, T, H, I, E, k, stream);
 }
 
+// ------------------------------------------------------------------ gate_up and down in one launch
+
+// From 17 to 32 tokens the forward runs both expert GEMMs in one launch, so that down's items
+// fill the end of gate_up's: a workgroup whose gate_up claims run out starts on down items
+// at once, instead of idling until the slowest workgroup of a gate_up launch finishes (13 us
+// of idle per workgroup on average at 32 tokens, Zipf routing) and then paying a launch
+// boundary and down's start-up.  The pages' own step ("Zyphra Inference Wave 2", Kernel
+// Results) fused both GEMMs into one kernel body and spilled registers; here the two phases
+// share the launch, not the body: each workgroup streams its gate_up items to the end
+// (stream_items), then its down items, through the same LDS.
+//
+// Hand-off of h without flags: h is filled with 0xFFFF before the launch (by the routing
+// launch), gate_up writes each element once with device-coherent stores, and a down wave
+// that loads an 0xFFFF (not yet written, or a NaN with that bit pattern) waits until every
+// workgroup has finished its gate_up phase and loads again (xchunk_settle).  Items are
+// taken in the same expert order in both phases, so down reaches an expert long after its
+// gate_up items finished and the wait is practically never taken; a per-item flag written
+// by gate_up was measured instead and cost 3-40 us at 32 tokens (stores and atomics from
+// many workgroups into a few cache lines queue behind one another).
+//
+// Workgroups wait for one another only in that rare case, and only for workgroups of the
+// launch to finish their gate_up items, which need nothing from anyone: the grid is sized to
+// what the device holds at once at this kernel's occupancy, so every workgroup runs.  A wait
+// that outlasts SPIN_LIMIT polls sets the error word and goes on.  The last workgroup to
+// exit resets the counters, so the control words are zero again after the launch.
+template <int NS, class SR>
+struct DownAfterGateUp : DownPolicy<NS, LdsSortW, GU_XCHUNK, false, SR, false, false> {
+  static constexpr bool SENTINEL = true;
+  // (ready: workgroups past their gate_up items; ready_target: the grid; err: the error word)
+  __device__ __forceinline__ void wait_all_written() const {
+    for (uint32_t n = 0;; ++n) {
+      const int v =
+          __builtin_amdgcn_readfirstlane(__hip_atomic_load(this->ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      if (v >= this->ready_target) break;
+      if (n == SPIN_LIMIT) {
+        __hip_atomic_store(this->err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+  }
+};
+
+__global__ void __launch_bounds__(WG_WAVES * 64) moe_experts_sorted_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, const uint8_t* __restrict__ wgu,
+    const uint8_t* __restrict__ sgu, const uint8_t* __restrict__ wd, const uint8_t* __restrict__ sd, uint16_t* h,
+    float* __restrict__ dpart, int32_t* ctl, int T, int H, int I, int E, int k) {
+  __shared__ __attribute__((aligned(16))) uint8_t xbufs[2 * GU_XCHUNK];
+  __shared__ __attribute__((aligned(16))) uint8_t slabs[WG_WAVES][SLAB_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t sslabs[WG_WAVES][ScaleRun4::slab_bytes<2>()];
+  __shared__ uint32_t xctr[2];
+  __shared__ int32_t cq[4];
+  __shared__ int32_t last;
+  __shared__ WgSort wsort;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  if (tid < 2) xctr[tid] = 0u;
+  lds_wgsort* ws = (lds_wgsort*)&wsort;
+  wg_sort_slots(ids, T, E, k, ws, xbufs);
+  const LdsSortW meta{ws};
+  const int na = meta.num_active();
+  const int levels = (meta.max_rows() + 15) >> 4;  // row-group levels that exist
+
+  // ---------------------------------------------------------------- gate_up + SwiGLU
+  {
+    using PG = GateUpPolicy<2, LdsSortW, GU_XCHUNK, true>;
+    PG p;
+    p.m = meta;
+    p.xrowsegs = XGeom<GU_XCHUNK>::ROWSEGS;
+    p.calign = GU_SPS;
+    p.nseg = H / SEG_K;
+    p.nquad = I / (PG::TILE * WG_WAVES);
+    p.na = na;
+    p.n_items = levels * na * p.nquad;
+    p.xact = x;
+    p.wgu = wgu;
+    p.sgu = sgu;
+    p.h = h;
+    p.H = H;
+    p.I = I;
+    p.k = k;
+    p.kinv = ((1u << 24) + (uint32_t)k - 1u) / (uint32_t)k;
+    p.e_codes = (size_t)2 * I * (H / 2);
+    p.e_scales = (size_t)2 * I * (H / 32);
+    ClaimedUnits seq{ctl + CTL_CLAIM_GU, (lds_i32*)cq, na * p.nquad, 0, false};
+    stream_items<PG, GU_SPS>(p, seq, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
+    seq.finish();
+  }
+  // this workgroup's h stores are complete; count it, and start a fresh chunk hand-off
+  wait_own_stores();
+  __syncthreads();
+  if (tid == 0) {
+    __hip_atomic_fetch_add(&ctl[CTL_GU_DONE], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    xctr[0] = 0u;
+    xctr[1] = 0u;
+  }
+  __syncthreads();
+
+  // ---------------------------------------------------------------- down
+  {
+    using PD = DownAfterGateUp<2, ScaleRun4>;
+    PD p;
+    p.m = meta;
+    p.xrowsegs = XGeom<GU_XCHUNK>::ROWSEGS;
+    p.calign = DN_SPS;
+    p.nseg = I / SEG_K;
+    p.nquad = H / (PD::TILE * WG_WAVES);
+    p.na = na;
+    p.n_items = levels * na * p.nquad;
+    p.xact = h;
+    p.wd = wd;
+    p.sd = sd;
+    p.dpart = dpart;
+    p.H = H;
+    p.I = I;
+    p.e_codes = (size_t)H * (I / 2);
+    p.e_scales = (size_t)H * (I / 32);
+    p.ready = ctl + CTL_GU_DONE;
+    p.ready_target = (int)gridDim.x;
+    p.err = ctl + CTL_ERR;
+    p.flag = nullptr;
+    p.wave = wave;
+    ClaimedUnits seq{ctl + CTL_CLAIM_DN, (lds_i32*)cq, na * p.nquad, 0, false};
+    stream_items<PD, DN_SPS>(p, seq, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
+    seq.finish();
+  }
+
+  // ---------------------------------------------------------------- exit
+  __syncthreads();
+  if (tid == 0)
+    last = __hip_atomic_fetch_add(&ctl[CTL_EXIT], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1;
+  __syncthreads();
+  if (last && tid == 0) {
+    __hip_atomic_store(&ctl[CTL_GU_DONE], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&ctl[CTL_EXIT], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// The sort fits one workgroup, I and H take 4-segment scale runs and 2-segment steps in both
+// reductions, and the gate_up items (full-width tiles) can fill the grid: at least
+// EXPERTS_MIN_ITEMS of them when every slot routes to its own expert (the resident
+// workgroups of MI355X, 256 CUs x 2; with fewer items the separate launches choose
+// half-width tiles).
+constexpr int64_t EXPERTS_MIN_ITEMS = 512;
+bool experts_sorted_fits(int T, int E, int k, int H, int I) {
+  if (!gate_up_sorted_fits(T, E, k, H, I) || I % (SEG_K * SRUN) != 0 || I % (SEG_K * DN_SPS) != 0 ||
+      H % (2 * SUB_ROWS * WG_WAVES) != 0)
+    return false;
+  const int64_t na_max = (int64_t)T * k < E ? (int64_t)T * k : E;
+  return na_max * (I / (SUB_ROWS * WG_WAVES)) >= EXPERTS_MIN_ITEMS;
+}
+
+int launch_experts_sorted(const uint16_t* x, const int32_t* ids, const uint8_t* wgu, const uint8_t* sgu,
+                          const uint8_t* wd, const uint8_t* sd, uint16_t* h, float* dpart, int32_t* ctl, int T, int H,
+                          int I, int E, int k, hipStream_t stream) {
+  if (!experts_sorted_fits(T, E, k, H, I)) return MX_ERR_SHAPE;
+  static const int occ = routed_occupancy(moe_experts_sorted_kernel);
+  const dim3 grid((unsigned)(device_cu_count() * occ)), block(WG_WAVES * 64);
+  hipLaunchKernelGGL(moe_experts_sorted_kernel, grid, block, 0, stream, x, ids, wgu, sgu, wd, sd, h, dpart, ctl, T, H,
+                     I, E, k);
+  return hip_status(hipGetLastError());
+}
+
 // Measured against the route + sort launch followed by gate_up (graph replay, 4 layers):
 // T = 1 50.0 -> 46.7 us per layer, T = 2 81.4 -> 77.9, T = 4 132.0 -> 127.8, T = 8 226.8 ->
 // 223.1, T = 16 392.4 -> 391.2.

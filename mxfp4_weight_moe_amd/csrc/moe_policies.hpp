@@ -52,20 +52,6 @@ struct GlobalSort {
   __device__ __forceinline__ int count_lane(int a) const { return sv.counts[sv.active[a]]; }
 };
 
-// Device-coherent 8- and 16-byte accesses (agent-scope relaxed atomics compile to plain
-// loads and stores with the sc1 bit).
-__device__ __forceinline__ void st8_coherent(void* p, uint64_t v) {
-  __hip_atomic_store(static_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t ld8_coherent(const void* p) {
-  return __hip_atomic_load(static_cast<uint64_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ u32x4 ld16_coherent(const void* p) {
-  const uint64_t a = ld8_coherent(p);
-  const uint64_t b = ld8_coherent(static_cast<const uint8_t*>(p) + 8);
-  return u32x4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
-}
-
 // Bounded wait for a device-wide counter to reach `target`.  One wavefront of the
 // workgroup polls (polls of every wavefront on one address queue behind each other and
 // behind the counter's own updates) and raises the LDS flag; the others wait on the flag.
@@ -156,6 +142,7 @@ template <class Meta>
 struct ExpertItems {
   Meta m;
   int nseg, n_items, nquad, na;
+  static constexpr bool SENTINEL = false;  // activations are complete when the launch starts
   int xrowsegs;  // row-segments per activation chunk
   int calign = CHUNK_ALIGN;  // chunk lengths are multiples of this (the launch's weight step)
 

@@ -18,10 +18,20 @@ namespace mx {
 __device__ __forceinline__ int slot_expert(int j, int k, int E, int routed) { return j < k ? routed : E + j - k; }
 __device__ __forceinline__ float slot_gate(int j, int k, float routed) { return j < k ? routed : 1.0f; }
 
-// One wavefront per token.
+// One wavefront per token.  Workgroups past the routing ones fill `fill` (n16 16-byte units)
+// with all ones: the h rows of a launch whose down items read them while gate_up writes them
+// start out as 0xFFFF (the expert launch's "not yet written" pattern).
 template <int PER>
 __global__ void __launch_bounds__(256) moe_route_kernel(const float* __restrict__ logits, int T, int E, int k, int ns,
-                                                        int32_t* __restrict__ ids, float* __restrict__ gates) {
+                                                        int32_t* __restrict__ ids, float* __restrict__ gates,
+                                                        u32x4* __restrict__ fill, int64_t n16) {
+  const int route_wgs = (T + 3) / 4;
+  if ((int)blockIdx.x >= route_wgs) {
+    const int64_t stride = (int64_t)(gridDim.x - route_wgs) * 256;
+    for (int64_t i = (int64_t)(blockIdx.x - route_wgs) * 256 + threadIdx.x; i < n16; i += stride)
+      fill[i] = u32x4{~0u, ~0u, ~0u, ~0u};
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -37,12 +47,18 @@ __global__ void __launch_bounds__(256) moe_route_kernel(const float* __restrict_
   }
 }
 
-int launch_route(const float* logits, int T, int E, int k, int ns, int32_t* ids, float* gates, hipStream_t stream) {
-  const dim3 grid((T + 3) / 4), block(256);
+int launch_route(const float* logits, int T, int E, int k, int ns, int32_t* ids, float* gates, hipStream_t stream,
+                 void* fill, size_t fill_bytes) {
+  const int64_t n16 = fill ? (int64_t)(fill_bytes / 16) : 0;
+  const int64_t fill_wgs = (n16 + 1023) / 1024 < 256 ? (n16 + 1023) / 1024 : 256;  // 4 stores per thread up to 4 MB
+  const dim3 grid((unsigned)((T + 3) / 4 + fill_wgs)), block(256);
+  u32x4* f = static_cast<u32x4*>(fill);
   switch (route_per(E)) {
-    case 4: hipLaunchKernelGGL(moe_route_kernel<4>, grid, block, 0, stream, logits, T, E, k, ns, ids, gates); break;
-    case 8: hipLaunchKernelGGL(moe_route_kernel<8>, grid, block, 0, stream, logits, T, E, k, ns, ids, gates); break;
-    default: hipLaunchKernelGGL(moe_route_kernel<16>, grid, block, 0, stream, logits, T, E, k, ns, ids, gates); break;
+    case 4: hipLaunchKernelGGL(moe_route_kernel<4>, grid, block, 0, stream, logits, T, E, k, ns, ids, gates, f, n16); break;
+    case 8: hipLaunchKernelGGL(moe_route_kernel<8>, grid, block, 0, stream, logits, T, E, k, ns, ids, gates, f, n16); break;
+    default:
+      hipLaunchKernelGGL(moe_route_kernel<16>, grid, block, 0, stream, logits, T, E, k, ns, ids, gates, f, n16);
+      break;
   }
   return hip_status(hipGetLastError());
 }

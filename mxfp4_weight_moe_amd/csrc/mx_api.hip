@@ -28,7 +28,7 @@ MoeWorkspace moe_workspace_carve(void* base, int64_t T, int64_t H, int64_t I, in
   w.offsets = reinterpret_cast<int32_t*>(take((size_t)(E + 1) * 4));
   w.sorted_slots = reinterpret_cast<int32_t*>(take(F * 4));
   w.active = reinterpret_cast<int32_t*>(take((size_t)E * 4));
-  w.num_active = reinterpret_cast<int32_t*>(take(4));
+  w.num_active = reinterpret_cast<int32_t*>(take(8));
   w.h = reinterpret_cast<uint16_t*>(take(F * (size_t)I * 2));
   w.dpart = reinterpret_cast<float*>(take(F * (size_t)H * 4));
   w.bytes = off;
@@ -273,6 +273,32 @@ int moe_down_combine(const uint16_t* h, const float* gates, const uint8_t* w_dow
   return combined ? MX_OK : launch_combine(ws.dpart, gates, y, (int)T, (int)H, (int)top_k, s);
 }
 
+int moe_expert_gemms_from_ids(const uint16_t* x, const int32_t* ids, const uint8_t* w_gate_up,
+                              const uint8_t* s_gate_up, const uint8_t* w_down, const uint8_t* s_down, uint16_t* h,
+                              float* d, int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (!x || !ids || !w_gate_up || !s_gate_up || !w_down || !s_down || !h || !d) return MX_ERR_NULL;
+  int st = check_moe_sizes(T, E, top_k);
+  if (st != MX_OK || (st = check_expert_dims(H, I)) != MX_OK) return st;
+  if (!experts_sorted_fits((int)T, (int)E, (int)top_k, (int)H, (int)I)) return MX_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(ids, 4) || !aligned(w_gate_up, 16) || !aligned(s_gate_up, 16) ||
+      !aligned(w_down, 16) || !aligned(s_down, 16) || !aligned(h, 16) || !aligned(d, 16))
+    return MX_ERR_ALIGN;
+  if (!workspace || !aligned(workspace, 256)) return MX_ERR_WORKSPACE;
+  const MoeWorkspace ws = moe_workspace_carve(workspace, T, H, I, E, top_k);
+  if (workspace_bytes < ws.bytes) return MX_ERR_WORKSPACE;
+  return launch_experts_sorted(x, ids, w_gate_up, s_gate_up, w_down, s_down, h, d, ws.ctl, (int)T, (int)H, (int)I,
+                               (int)E, (int)top_k, static_cast<hipStream_t>(stream));
+}
+
+int moe_combine(const float* d, const float* gates, uint16_t* y, int64_t T, int64_t H, int64_t top_k, void* stream) {
+  if (!d || !gates || !y) return MX_ERR_NULL;
+  if (T < 1 || T > MX_MAX_TOKENS || top_k < 1 || top_k > MX_MAX_TOPK || H < 4 || H > 65536 || H % 4 != 0)
+    return MX_ERR_SHAPE;
+  if (!aligned(d, 16) || !aligned(gates, 4) || !aligned(y, 8)) return MX_ERR_ALIGN;
+  return launch_combine(d, gates, y, (int)T, (int)H, (int)top_k, static_cast<hipStream_t>(stream));
+}
+
 size_t moe_mxfp4_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k) {
   if (T < 1 || H < 1 || I < 1 || E < 1 || top_k < 1) return 0;
   return moe_workspace_carve(nullptr, T, H, I, E, top_k).bytes;
@@ -314,6 +340,15 @@ static int moe_forward_impl(const uint16_t* x, const float* router_logits, int64
                                     ws.sorted_slots, ws.active, ws.num_active, ws.gates, t, h, i, e, k, act8, s)) !=
         MX_OK)
       return st;
+  } else if (n == 0 && !act8 && experts_sorted_fits(t, e, k, h, i)) {
+    // up to 32 tokens: the routing launch (which also fills h with 0xFFFF), then one launch
+    // for both expert GEMMs, then the combine
+    if ((st = launch_route(router_logits, t, e, k, 0, ws.ids, ws.gates, s, ws.h, (size_t)t * k * i * 2)) != MX_OK)
+      return st;
+    if ((st = launch_experts_sorted(x, ws.ids, w_gate_up, s_gate_up, w_down, s_down, ws.h, ws.dpart, ws.ctl, t, h, i, e,
+                                    k, s)) != MX_OK)
+      return st;
+    return launch_combine(ws.dpart, ws.gates, y, t, h, k, s);
   } else if (n == 0 && gate_up_sorted_fits(t, e, k, h, i)) {
     // up to 32 tokens: the routing launch, then gate_up sorts the slots in every workgroup
     if ((st = launch_route(router_logits, t, e, k, 0, ws.ids, ws.gates, s)) != MX_OK) return st;

@@ -49,6 +49,20 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Device-coherent 8- and 16-byte accesses (agent-scope relaxed atomics compile to plain
+// loads and stores with the sc1 bit).
+__device__ __forceinline__ void st8_coherent(void* p, uint64_t v) {
+  __hip_atomic_store(static_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld8_coherent(const void* p) {
+  return __hip_atomic_load(static_cast<uint64_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u32x4 ld16_coherent(const void* p) {
+  const uint64_t a = ld8_coherent(p);
+  const uint64_t b = ld8_coherent(static_cast<const uint8_t*>(p) + 8);
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
 // The conversion instruction reads the E8M0 scale from the exponent field of an fp32.

@@ -39,7 +39,7 @@ struct MoeWorkspace {
   int32_t* offsets;       // [E+1]
   int32_t* sorted_slots;  // [T*k]
   int32_t* active;        // [E]
-  int32_t* num_active;    // [1]
+  int32_t* num_active;    // [2]: active experts, largest count
   uint16_t* h;            // [T*k, I] bf16, rows in sorted-slot order
   float* dpart;           // [T*k, H] fp32 down outputs, rows by flat slot
   size_t bytes;
@@ -73,7 +73,9 @@ int launch_mxfp8_quantize(const uint16_t* x, int64_t rows, int64_t K, uint8_t* c
                           hipStream_t stream);
 // ns: shared experts E .. E + ns - 1, routed by every token with gate 1 after its k routed
 // slots (ids and gates are [T, k + ns]; the sort then runs over E + ns experts)
-int launch_route(const float* logits, int T, int E, int k, int ns, int32_t* ids, float* gates, hipStream_t stream);
+// fill: optionally, fill_bytes (a multiple of 16) of device memory set to all ones in the same launch
+int launch_route(const float* logits, int T, int E, int k, int ns, int32_t* ids, float* gates, hipStream_t stream,
+                 void* fill = nullptr, size_t fill_bytes = 0);
 int launch_sort(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* sorted_slots,
                 int32_t* active, int32_t* num_active, hipStream_t stream);
 // route + sort in one single-workgroup launch (the layer forward's path)
@@ -90,17 +92,25 @@ int launch_down(const uint16_t* h, const float* gates, const uint8_t* wd, const 
                 float* dpart, uint16_t* y, bool* combined, int32_t* ctl, int T, int H, int I, int E, int k, bool act8,
                 hipStream_t stream);
 int launch_combine(const float* dpart, const float* gates, uint16_t* y, int T, int H, int k, hipStream_t stream);
-// The forward's gate_up for small T with the routing and sort done in every workgroup (no
-// route + sort launch before it); it also writes the sort outputs and gates for the down
-// launch.  gate_up_routed_fits says when it applies (no shared experts); act8: MXFP8
-// activations, as launch_gate_up.
-// The forward's gate_up for 16 < T <= 32: sorts the routed ids (moe_route_kernel's output)
-// in every workgroup and writes the sort for the down launch.
+// gate_up for 16 < T <= 32: sorts the routed ids (moe_route_kernel's output) in every
+// workgroup and writes the sort for a down launch (the stage entry point, and the forward
+// with MXFP8 activations or where the single expert launch below does not apply).
 bool gate_up_sorted_fits(int T, int E, int k, int H, int I);
 int launch_gate_up_sorted(const uint16_t* x, const int32_t* ids, const uint8_t* wgu, const uint8_t* sgu, uint16_t* h,
                           int32_t* counts, int32_t* offsets, int32_t* sorted_slots, int32_t* active,
                           int32_t* num_active, int32_t* ctl, int T, int H, int I, int E, int k, bool act8,
                           hipStream_t stream);
+// The forward's expert GEMMs for 16 < T <= 32 (bf16 activations) in one launch: every
+// workgroup sorts the routed ids, streams its gate_up items, then its down items.  h must
+// hold 0xFFFF in every element when it starts (launch_route's fill); the combine follows.
+bool experts_sorted_fits(int T, int E, int k, int H, int I);
+int launch_experts_sorted(const uint16_t* x, const int32_t* ids, const uint8_t* wgu, const uint8_t* sgu,
+                          const uint8_t* wd, const uint8_t* sd, uint16_t* h, float* dpart, int32_t* ctl, int T, int H,
+                          int I, int E, int k, hipStream_t stream);
+// The forward's gate_up for small T with the routing and sort done in every workgroup (no
+// route + sort launch before it); it also writes the sort outputs and gates for the down
+// launch.  gate_up_routed_fits says when it applies (no shared experts); act8: MXFP8
+// activations, as launch_gate_up.
 bool gate_up_routed_fits(int T, int E, int k, int H, int I);
 int launch_gate_up_routed(const uint16_t* x, const float* logits, const uint8_t* wgu, const uint8_t* sgu, uint16_t* h,
                           int32_t* counts, int32_t* offsets, int32_t* sorted_slots, int32_t* active,

@@ -211,7 +211,9 @@ __device__ __forceinline__ uint32_t rows_reciprocal(int R) { return (65536u + (u
 // (threads past the chunk repeat its last piece; skipping the unneeded rounds costs more
 // registers than the loads it saves).  Lane m < 16 holds row m's element offset, and each
 // thread fetches its row's offset from there with one cross-lane read.
-template <int XROUNDS, class P>
+// COHERENT: device-coherent loads instead of the policy's (the reload of a chunk that another
+// workgroup of the launch may have written since a cached copy was fetched)
+template <bool COHERENT = false, int XROUNDS, class P>
 __device__ __forceinline__ void xchunk_load(const P& p, const XChunk& ch, u32x4 (&xv)[XROUNDS], int tid) {
   const int R = ch.info.rows;
   const int npieces = R * ch.ns * 32;
@@ -228,7 +230,8 @@ __device__ __forceinline__ void xchunk_load(const P& p, const XChunk& ch, u32x4 
     const int rs = q >> 5, pc = q & 31;
     const int s = (int)(((uint32_t)rs * inv) >> 16), m = rs - s * R;
     const int ro = __builtin_amdgcn_ds_bpermute(m << 2, myoff);
-    xv[r] = p.xload(p.xact + (size_t)ro + (size_t)(ch.c0 + s) * SEG_K + pc * 8);
+    const uint16_t* a = p.xact + (size_t)ro + (size_t)(ch.c0 + s) * SEG_K + pc * 8;
+    xv[r] = COHERENT ? ld16_coherent(a) : p.xload(a);
   }
 }
 
@@ -281,6 +284,33 @@ __device__ __forceinline__ void xchunk_put(uint8_t* __restrict__ buf, const XChu
     xchunk_store_a8<XROUNDS, XCHUNK>(buf, ch, xv, tid);
   else
     xchunk_store<XROUNDS>(buf, ch, xv, tid);
+}
+
+// Activations written earlier in the same launch (policies with SENTINEL, down after gate_up
+// in one launch): every h element holds 0xFFFF until gate_up writes it, with a device-coherent
+// store, and gate_up writes each element once.  So any other value a load returns, from
+// memory or from a cached copy, is the element's final value, and the chunk's loads can be
+// ordinary cached ones.  A wave that finds an 0xFFFF in its pieces (not yet written when the
+// copy was fetched, or a NaN that happens to have that pattern) waits until every workgroup
+// has finished its gate_up items (p.wait_all_written) and loads its pieces again with
+// device-coherent loads, which do not return a stale cached copy.  The branch is
+// wave-uniform, and ends with all of the wave's loads complete, so the waits the compiler
+// counts on the common path stay exact.
+template <class P, int XROUNDS>
+__device__ __forceinline__ void xchunk_settle(const P& p, const XChunk& ch, u32x4 (&xv)[XROUNDS], int tid) {
+  if constexpr (P::SENTINEL) {
+    bool unwritten = false;
+#pragma unroll
+    for (int r = 0; r < XROUNDS; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) unwritten |= (xv[r][c] & 0xFFFFu) == 0xFFFFu || (xv[r][c] >> 16) == 0xFFFFu;
+    if (__ballot(unwritten) != 0ull) {
+      p.wait_all_written();
+      xchunk_load<true>(p, ch, xv, tid);
+      __asm__ volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    }
+  }
 }
 
 // Consume one segment: LDS transpose of the codes, decode, MFMA with activations from the
@@ -602,6 +632,7 @@ __device__ __forceinline__ void stream_items(P& p, Seq& seq, uint8_t* __restrict
   u32x4 xv[XROUNDS];
   XChunk cur = chunk_of(first, 0);
   xchunk_load(p, cur, xv, tid);
+  xchunk_settle(p, cur, xv, tid);
   xchunk_put<XROUNDS, XCHUNK_BYTES, P::ACT8>(xbufs, cur, xv, tid);
   xready_publish(&xctr[0]);
   int xb = 0;                  // LDS buffer holding `cur`
@@ -642,6 +673,7 @@ __device__ __forceinline__ void stream_items(P& p, Seq& seq, uint8_t* __restrict
     if (cseg >= cur.c0 + cur.ns) {
       // chunk done: publish this thread's pieces of the next chunk, wait for the rest
       if (have_next) {
+        xchunk_settle(p, nxt, xv, tid);
         xchunk_put<XROUNDS, XCHUNK_BYTES, P::ACT8>(xbufs + (xb ^ 1) * XCHUNK_BYTES, nxt, xv, tid);
         xready_publish(&xctr[xb ^ 1]);
         gen[xb ^ 1] += 1u;

@@ -176,6 +176,40 @@ def test_stage_gemm_hooks_reject():
     assert gi(w=None) == MX_ERR_WORKSPACE
     assert gi(wb=ws - 1) == MX_ERR_WORKSPACE
 
+    ws32 = m.workspace_size(32, 1024, 1024, 64, 8)
+
+    def eg(x=A, ids=A, h=A, d=A, T=32, H=1024, I=1024, E=64, k=8, w=A, wb=ws32):
+        return L.moe_expert_gemms_from_ids(x, ids, A, A, A, A, h, d, T, H, I, E, k, w, wb, None)
+
+    assert eg(ids=None) == MX_ERR_NULL
+    assert eg(h=None) == MX_ERR_NULL
+    assert eg(d=None) == MX_ERR_NULL
+    assert eg(T=0) == MX_ERR_SHAPE
+    assert eg(T=33) == MX_ERR_SHAPE          # the in-launch sort holds one 32-bit token mask per expert
+    assert eg(k=9) == MX_ERR_SHAPE           # at most 256 slots
+    assert eg(I=768) == MX_ERR_SHAPE         # down's reduction in 4-segment scale runs
+    assert eg(E=8, k=2, T=4, wb=ws) == MX_ERR_SHAPE  # 8 experts x 16 tile quads cannot fill the grid
+    assert eg(E=31, k=8) == MX_ERR_SHAPE     # 31 x 16 = 496 < 512 items
+    assert eg(H=1536) == MX_ERR_SHAPE
+    assert eg(h=P((1 << 20) + 8)) == MX_ERR_ALIGN
+    assert eg(d=P((1 << 20) + 4)) == MX_ERR_ALIGN
+    assert eg(ids=P((1 << 20) + 2)) == MX_ERR_ALIGN
+    assert eg(w=None) == MX_ERR_WORKSPACE
+    assert eg(w=P((1 << 20) + 128)) == MX_ERR_WORKSPACE
+    assert eg(wb=ws32 - 1) == MX_ERR_WORKSPACE
+
+    def cb(d=A, g=A, y=A, T=4, H=1024, k=2):
+        return L.moe_combine(d, g, y, T, H, k, None)
+
+    assert cb(d=None) == MX_ERR_NULL
+    assert cb(g=None) == MX_ERR_NULL
+    assert cb(T=0) == MX_ERR_SHAPE
+    assert cb(T=257) == MX_ERR_SHAPE
+    assert cb(k=33) == MX_ERR_SHAPE
+    assert cb(H=1026) == MX_ERR_SHAPE
+    assert cb(d=P((1 << 20) + 8)) == MX_ERR_ALIGN
+    assert cb(y=P((1 << 20) + 4)) == MX_ERR_ALIGN
+
     def dn(h=A, y=A, T=4, w=A, wb=ws):
         return L.moe_down_combine(h, A, A, A, A, A, A, A, A, y, T, 1024, 1024, 8, 2, w, wb, None)
 

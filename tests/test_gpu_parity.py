@@ -404,6 +404,70 @@ def test_moe_random_shapes(dev, mx, shape):
     say(f"  worst ratio {worst:.3g}")
 
 
+def expert_gemm_hooks_match(mx, d, cfg, y_fwd, dev):
+    """The forward's launches as stage calls (moe_route_topk, moe_expert_gemms_from_ids on a
+    poisoned workspace, moe_combine) give the forward's y bit for bit, and the launch's h
+    equals moe_gate_up_swiglu's h bit for bit."""
+    ids, gates = mx.moe_route_topk(d["logits"], cfg.k)
+    ws = poisoned_workspace(mx, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, dev)
+    dd = torch.full((cfg.T * cfg.k, cfg.H), float("nan"), dtype=torch.float32, device=dev)
+    h1, dd = mx.moe_expert_gemms_from_ids(d["x"], ids, d["wgu"], d["sgu"], d["wd"], d["sd"], d=dd, ws=ws)
+    y1 = mx.moe_combine(dd, gates, out=nan_like_out((cfg.T, cfg.H), dev))
+    _, _, srt = mx.moe_route_sort(d["logits"], cfg.k)
+    h2 = mx.moe_gate_up_swiglu(d["x"], d["wgu"], d["sgu"], srt, cfg.k)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host_bits(y1), y_fwd)
+    assert np.array_equal(to_host_bits(h1), to_host_bits(h2))
+    assert int(ws[:CTL_BYTES].count_nonzero()) == 0
+
+
+# From 17 to 32 tokens the forward runs both expert GEMMs in one launch whenever their items
+# fill the grid.  E = 32 with I = 1024 gives exactly one gate_up item per workgroup, so many
+# down items start before their expert's h is complete and take the wait-and-reload path;
+# Zipf routing gives experts with two row groups; E = 200 and 256 give many light experts.
+SINGLE_EXPERT_LAUNCH = [dict(T=32, H=1024, I=1024, E=32, k=8, routing="normal"),
+                        dict(T=32, H=1024, I=1024, E=64, k=8, routing="zipf"),
+                        dict(T=17, H=2048, I=1024, E=256, k=8, routing="normal"),
+                        dict(T=24, H=1024, I=2048, E=32, k=6, routing="uniform"),
+                        dict(T=32, H=1024, I=1024, E=200, k=8, routing="zipf")]
+
+
+@pytest.mark.parametrize("shape", SINGLE_EXPERT_LAUNCH,
+                         ids=[f"T{s['T']}_H{s['H']}_I{s['I']}_E{s['E']}_k{s['k']}_{s['routing']}"
+                              for s in SINGLE_EXPERT_LAUNCH])
+def test_moe_single_expert_launch(dev, mx, shape):
+    """The forward's single launch of both expert GEMMs: every token against the oracle, and
+    y bit-identical to the stage entry points' (separate gate_up and down launches), twice in
+    a row on the same workspace (the launch leaves its control words zero)."""
+    cfg = synthetic.MoEConfig("one_launch", e_lo=-8, e_hi=-2, seed=shape["T"] * 3 + shape["E"], **shape)
+    host = synthetic.moe_inputs_host(cfg)
+    say("moe single expert launch", shape)
+    d, x, logits = moe_device_inputs(cfg, dev, host)
+    got = run_moe(mx, d, cfg.k)
+    y, sm = oracle_moe(cfg, x, logits, host)
+    worst = check_bound(got, y, sm, MOE_REL, f"single expert launch {shape}")
+    say(f"  worst ratio {worst:.3g}")
+    assert np.array_equal(run_hooks(mx, d, cfg.k, cfg.T), got)
+    expert_gemm_hooks_match(mx, d, cfg, got, dev)
+    ws = poisoned_workspace(mx, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, dev)
+    for _ in range(2):
+        out = nan_like_out((cfg.T, cfg.H), dev)
+        mx.moe_mxfp4_forward(d["x"], d["logits"], cfg.k, d["wgu"], d["sgu"], d["wd"], d["sd"], out=out, ws=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host_bits(out), got)
+    assert int(ws[:CTL_BYTES].count_nonzero()) == 0
+
+
+def test_expert_gemm_hooks_full_size(dev, mx):
+    """The single expert launch at T = 32, H = 7168, I = 2048, E = 256, top-8, Zipf routing
+    (the launch configuration the benchmark times): the stage calls give the forward's y bit
+    for bit, with h identical to the separate gate_up's."""
+    cfg = synthetic.MOE_CONFIGS["moe_t32_zipf"]
+    say("expert gemm hooks, full size", cfg.name)
+    d, x, logits = moe_device_inputs(cfg, dev)
+    expert_gemm_hooks_match(mx, d, cfg, run_moe(mx, d, cfg.k), dev)
+
+
 def test_moe_small_scale_variant(dev, mx):
     cfg = synthetic.small_scale_variant(synthetic.MOE_CONFIGS["moe_t4"])
     say("moe small-scale variant")
