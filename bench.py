@@ -135,11 +135,12 @@ def gpu_clocks() -> dict:
 
 def forward_path(T: int, k: int, E: int, ns: int, I: int, H: int, act8: bool = False) -> str:
     """The launches moe_mxfp4_forward makes for these sizes (its dispatch)."""
+    if (ns == 0 and not act8 and T <= 32 and T * k <= 256 and E <= 1024 and I % 1024 == 0 and H % 128 == 0
+            and min(T * k, E) * (I // 64) >= 1536):
+        return "route, gate_up + down (one launch, sorting in every workgroup), combine launches"
     if ns == 0 and T <= 16 and T * k <= 128:
         return "gate_up (routing and sorting in every workgroup), down, combine launches (combine inside down at the smallest T)"
     if ns == 0 and T <= 32 and T * k <= 256 and E <= 1024:
-        if not act8 and I % 1024 == 0 and H % 128 == 0 and min(T * k, E) * (I // 64) >= 512:
-            return "route, gate_up + down (one launch, sorting in every workgroup), combine launches"
         return "route, gate_up (sorting in every workgroup), down, combine launches"
     return "route_sort, gate_up, down, combine launches"
 

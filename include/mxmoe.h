@@ -155,9 +155,10 @@ MX_API int moe_sort_by_expert(const int32_t* ids, int64_t T, int64_t top_k, int6
 /*
  * moe_route_topk followed by moe_sort_by_expert of its ids: one launch for T <= 16, two
  * beyond.  moe_mxfp4_forward runs it as its first stage beyond 32 tokens (and with shared
- * experts); up to 16 tokens its gate_up launch routes and sorts in every workgroup instead,
- * and from 17 to 32 it routes alone and its expert launch sorts (moe_expert_gemms_from_ids,
- * or moe_gate_up_swiglu_from_ids where that one does not apply).
+ * experts).  Up to 32 tokens it routes alone and its expert launch sorts where
+ * moe_expert_gemms_from_ids pays; otherwise, up to 16 tokens its gate_up launch routes and
+ * sorts in every workgroup, and from 17 to 32 it routes alone and gate_up sorts
+ * (moe_gate_up_swiglu_from_ids).
  * That internal sort has the same counts, offsets and sorted slots, but keeps its active
  * list in ascending expert order and leaves the entries past the last one unwritten (its
  * down launch accepts any order).  Arguments, outputs and limits as for those two calls.
@@ -188,7 +189,7 @@ MX_API int moe_gate_up_swiglu(const uint16_t* x, const uint8_t* w_gate_up, const
  * the launch also writes the sort (counts, offsets, sorted_slots, active, num_active), equal
  * to moe_sort_by_expert's on the same ids.  moe_mxfp4_forward runs it for 16 < T <= 32
  * without shared experts where moe_expert_gemms_from_ids does not apply (MXFP8 activations,
- * I % 1024 != 0, or too few items to fill the grid), in place of the sort launch: a token's routed expert GEMMs read
+ * I % 1024 != 0, or too few items), in place of the sort launch: a token's routed expert GEMMs read
  * each routed expert's weights once ("Zyphra Inference Wave 2", section "Quantization"),
  * and a launch boundary costs microseconds at this size (the AMD megakernel blog, "What
  * Drives the Speedup", 1. Megakernels).
@@ -206,7 +207,9 @@ MX_API int moe_gate_up_swiglu_from_ids(const uint16_t* x, const int32_t* ids, co
 
 /*
  * Stage hook: both expert GEMMs in one launch, straight from the routed ids, as
- * moe_mxfp4_forward runs them for 16 < T <= 32 without shared experts: every workgroup sorts
+ * moe_mxfp4_forward runs them without shared experts for T <= 32 whenever the gate_up items
+ * can be 3 or more per resident workgroup (min(T*top_k, E) * I / 64 >= 1536; from 6 tokens
+ * at top-8 and I = 2048): every workgroup sorts
  * the T*top_k slots itself, streams its share of the gate_up items and then its share of the
  * down items, so that down work fills the end of the gate_up work ("Zyphra Inference Wave 2",
  * Kernel Results, for the two GEMMs of an MXFP4 expert; the AMD megakernel blog, "What Drives
@@ -222,10 +225,10 @@ MX_API int moe_gate_up_swiglu_from_ids(const uint16_t* x, const int32_t* ids, co
  * row waits until every workgroup has finished its gate_up items.  The grid is sized to what
  * the device holds at once, so all of them run; a wait that outlasts any layer by far gives
  * up, leaves d undefined and sets the int32 at byte offset 8 of the workspace to 1 (sticky,
- * as for moe_mxfp4_forward_persistent).  It applies when T <= 32, T*top_k <= 256,
- * E <= 1024, I % 1024 == 0 and the gate_up items fill the grid (min(T*top_k, E) * I / 64 at
- * least the device's resident workgroups, 512 on MI355X); MX_ERR_SHAPE otherwise.  Other
- * arguments, limits and the workspace as for moe_gate_up_swiglu.
+ * as for moe_mxfp4_forward_persistent).  T <= 32, T*top_k <= 256, E <= 1024 and
+ * I % 1024 == 0 (MX_ERR_SHAPE otherwise); with fewer items than that bound the results are
+ * the same, only slower than separate launches.  Other arguments, limits and the workspace
+ * as for moe_gate_up_swiglu.
  */
 MX_API int moe_expert_gemms_from_ids(const uint16_t* x, const int32_t* ids, const uint8_t* w_gate_up,
                                      const uint8_t* s_gate_up, const uint8_t* w_down, const uint8_t* s_down,

@@ -675,6 +675,12 @@ int launch_gate_up_sorted(const uint16_t* x, const int32_t* ids, const uint8_t* 
 // what the device holds at once at this kernel's occupancy, so every workgroup runs.  A wait
 // that outlasts SPIN_LIMIT polls sets the error word and goes on.  The last workgroup to
 // exit resets the counters, so the control words are zero again after the launch.
+// The down phase runs at gate_up's occupancy (2 workgroups per CU, not down's 3), so its
+// waves keep two steps of 2 segments in flight instead of one; the registers are there (205).
+// Measured: T = 32 Zipf 380.4 -> 379.7 us per layer, uniform T = 32 587.6 -> 585.6.
+constexpr int DN_SPS_DEEP = 4;
+static_assert(SRUN % DN_SPS_DEEP == 0, "scale runs end on steps");
+
 template <int NS, class SR>
 struct DownAfterGateUp : DownPolicy<NS, LdsSortW, GU_XCHUNK, false, SR, false, false> {
   static constexpr bool SENTINEL = true;
@@ -754,7 +760,7 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_experts_sorted_kernel(
     PD p;
     p.m = meta;
     p.xrowsegs = XGeom<GU_XCHUNK>::ROWSEGS;
-    p.calign = DN_SPS;
+    p.calign = DN_SPS_DEEP;
     p.nseg = I / SEG_K;
     p.nquad = H / (PD::TILE * WG_WAVES);
     p.na = na;
@@ -773,7 +779,7 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_experts_sorted_kernel(
     p.flag = nullptr;
     p.wave = wave;
     ClaimedUnits seq{ctl + CTL_CLAIM_DN, (lds_i32*)cq, na * p.nquad, 0, false};
-    stream_items<PD, DN_SPS>(p, seq, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
+    stream_items<PD, DN_SPS_DEEP>(p, seq, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
     seq.finish();
   }
 
@@ -788,16 +794,22 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_experts_sorted_kernel(
   }
 }
 
-// The sort fits one workgroup, I and H take 4-segment scale runs and 2-segment steps in both
-// reductions, and the gate_up items (full-width tiles) can fill the grid: at least
-// EXPERTS_MIN_ITEMS of them when every slot routes to its own expert (the resident
-// workgroups of MI355X, 256 CUs x 2; with fewer items the separate launches choose
-// half-width tiles).
-constexpr int64_t EXPERTS_MIN_ITEMS = 512;
+// The sort fits one workgroup and I and H take 4-segment scale runs and 4- and 2-segment
+// steps.  The launch is correct for any number of items (workgroups without any pass
+// through); whether it pays is experts_sorted_pays.
 bool experts_sorted_fits(int T, int E, int k, int H, int I) {
-  if (!gate_up_sorted_fits(T, E, k, H, I) || I % (SEG_K * SRUN) != 0 || I % (SEG_K * DN_SPS) != 0 ||
-      H % (2 * SUB_ROWS * WG_WAVES) != 0)
-    return false;
+  return gate_up_sorted_fits(T, E, k, H, I) && I % (SEG_K * SRUN) == 0 && I % (SEG_K * DN_SPS_DEEP) == 0 &&
+         H % (2 * SUB_ROWS * WG_WAVES) == 0;
+}
+
+// The single launch pays once the gate_up items are at least 3 per resident workgroup
+// (512 on MI355X) when every slot routes to its own expert.  With fewer, down items reach
+// experts whose h is still being written and wait for the whole gate_up phase, and cached
+// copies of h lines fetched before they were written send later chunks to the slow reload:
+// measured against the separate launches, T = 2 75.7 -> 82.1 and T = 4 125.2 -> 154.8 us per
+// layer (1 and 2 items per workgroup), but T = 8 220.3 -> 217.4 and T = 16 392.1 -> 387.4.
+constexpr int64_t EXPERTS_MIN_ITEMS = 3 * 512;
+bool experts_sorted_pays(int T, int E, int k, int I) {
   const int64_t na_max = (int64_t)T * k < E ? (int64_t)T * k : E;
   return na_max * (I / (SUB_ROWS * WG_WAVES)) >= EXPERTS_MIN_ITEMS;
 }

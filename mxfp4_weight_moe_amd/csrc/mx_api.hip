@@ -334,21 +334,21 @@ static int moe_forward_impl(const uint16_t* x, const float* router_logits, int64
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int t = (int)T, h = (int)H, i = (int)I, e = (int)E, k = (int)top_k, n = (int)ns;
   const SortView sv{ws.counts, ws.offsets, ws.sorted_slots, ws.active, ws.num_active};
-  if (n == 0 && gate_up_routed_fits(t, e, k, h, i)) {
-    // small T: gate_up routes and sorts in every workgroup and writes the sort for down
-    if ((st = launch_gate_up_routed(x, router_logits, w_gate_up, s_gate_up, ws.h, ws.counts, ws.offsets,
-                                    ws.sorted_slots, ws.active, ws.num_active, ws.gates, t, h, i, e, k, act8, s)) !=
-        MX_OK)
-      return st;
-  } else if (n == 0 && !act8 && experts_sorted_fits(t, e, k, h, i)) {
-    // up to 32 tokens: the routing launch (which also fills h with 0xFFFF), then one launch
-    // for both expert GEMMs, then the combine
+  if (n == 0 && !act8 && experts_sorted_fits(t, e, k, h, i) && experts_sorted_pays(t, e, k, i)) {
+    // the routing launch (which also fills h with 0xFFFF), one launch for both expert
+    // GEMMs, then the combine
     if ((st = launch_route(router_logits, t, e, k, 0, ws.ids, ws.gates, s, ws.h, (size_t)t * k * i * 2)) != MX_OK)
       return st;
     if ((st = launch_experts_sorted(x, ws.ids, w_gate_up, s_gate_up, w_down, s_down, ws.h, ws.dpart, ws.ctl, t, h, i, e,
                                     k, s)) != MX_OK)
       return st;
     return launch_combine(ws.dpart, ws.gates, y, t, h, k, s);
+  } else if (n == 0 && gate_up_routed_fits(t, e, k, h, i)) {
+    // small T: gate_up routes and sorts in every workgroup and writes the sort for down
+    if ((st = launch_gate_up_routed(x, router_logits, w_gate_up, s_gate_up, ws.h, ws.counts, ws.offsets,
+                                    ws.sorted_slots, ws.active, ws.num_active, ws.gates, t, h, i, e, k, act8, s)) !=
+        MX_OK)
+      return st;
   } else if (n == 0 && gate_up_sorted_fits(t, e, k, h, i)) {
     // up to 32 tokens: the routing launch, then gate_up sorts the slots in every workgroup
     if ((st = launch_route(router_logits, t, e, k, 0, ws.ids, ws.gates, s)) != MX_OK) return st;

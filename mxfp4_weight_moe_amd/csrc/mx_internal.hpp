@@ -100,10 +100,12 @@ int launch_gate_up_sorted(const uint16_t* x, const int32_t* ids, const uint8_t* 
                           int32_t* counts, int32_t* offsets, int32_t* sorted_slots, int32_t* active,
                           int32_t* num_active, int32_t* ctl, int T, int H, int I, int E, int k, bool act8,
                           hipStream_t stream);
-// The forward's expert GEMMs for 16 < T <= 32 (bf16 activations) in one launch: every
-// workgroup sorts the routed ids, streams its gate_up items, then its down items.  h must
-// hold 0xFFFF in every element when it starts (launch_route's fill); the combine follows.
+// Both expert GEMMs in one launch (bf16 activations, T <= 32): every workgroup sorts the
+// routed ids, streams its gate_up items, then its down items.  h must hold 0xFFFF in every
+// element when it starts (launch_route's fill); the combine follows.  The forward uses it
+// where experts_sorted_pays.
 bool experts_sorted_fits(int T, int E, int k, int H, int I);
+bool experts_sorted_pays(int T, int E, int k, int I);
 int launch_experts_sorted(const uint16_t* x, const int32_t* ids, const uint8_t* wgu, const uint8_t* sgu,
                           const uint8_t* wd, const uint8_t* sd, uint16_t* h, float* dpart, int32_t* ctl, int T, int H,
                           int I, int E, int k, hipStream_t stream);

@@ -188,8 +188,7 @@ def test_stage_gemm_hooks_reject():
     assert eg(T=33) == MX_ERR_SHAPE          # the in-launch sort holds one 32-bit token mask per expert
     assert eg(k=9) == MX_ERR_SHAPE           # at most 256 slots
     assert eg(I=768) == MX_ERR_SHAPE         # down's reduction in 4-segment scale runs
-    assert eg(E=8, k=2, T=4, wb=ws) == MX_ERR_SHAPE  # 8 experts x 16 tile quads cannot fill the grid
-    assert eg(E=31, k=8) == MX_ERR_SHAPE     # 31 x 16 = 496 < 512 items
+    assert eg(E=1025) == MX_ERR_SHAPE
     assert eg(H=1536) == MX_ERR_SHAPE
     assert eg(h=P((1 << 20) + 8)) == MX_ERR_ALIGN
     assert eg(d=P((1 << 20) + 4)) == MX_ERR_ALIGN

@@ -421,24 +421,28 @@ def expert_gemm_hooks_match(mx, d, cfg, y_fwd, dev):
     assert int(ws[:CTL_BYTES].count_nonzero()) == 0
 
 
-# From 17 to 32 tokens the forward runs both expert GEMMs in one launch whenever their items
-# fill the grid.  E = 32 with I = 1024 gives exactly one gate_up item per workgroup, so many
-# down items start before their expert's h is complete and take the wait-and-reload path;
-# Zipf routing gives experts with two row groups; E = 200 and 256 give many light experts.
+# Both expert GEMMs in one launch (moe_expert_gemms_from_ids), which the forward runs up to
+# 32 tokens once min(T k, E) I / 64 >= 1536.  Shapes below that bound exercise the stage entry
+# point against the forward's separate launches: E = 32 with I = 1024 gives one gate_up item
+# per workgroup, so many down items start before their expert's h is complete and take the
+# wait-and-reload path.  Zipf routing gives experts with two row groups; T = 6 and 12 sit on
+# the bound; E = 200 and 256 give many light experts.
 SINGLE_EXPERT_LAUNCH = [dict(T=32, H=1024, I=1024, E=32, k=8, routing="normal"),
                         dict(T=32, H=1024, I=1024, E=64, k=8, routing="zipf"),
                         dict(T=17, H=2048, I=1024, E=256, k=8, routing="normal"),
                         dict(T=24, H=1024, I=2048, E=32, k=6, routing="uniform"),
-                        dict(T=32, H=1024, I=1024, E=200, k=8, routing="zipf")]
+                        dict(T=32, H=1024, I=1024, E=200, k=8, routing="zipf"),
+                        dict(T=6, H=1024, I=2048, E=128, k=8, routing="normal"),
+                        dict(T=12, H=2048, I=1024, E=256, k=8, routing="zipf")]
 
 
 @pytest.mark.parametrize("shape", SINGLE_EXPERT_LAUNCH,
                          ids=[f"T{s['T']}_H{s['H']}_I{s['I']}_E{s['E']}_k{s['k']}_{s['routing']}"
                               for s in SINGLE_EXPERT_LAUNCH])
 def test_moe_single_expert_launch(dev, mx, shape):
-    """The forward's single launch of both expert GEMMs: every token against the oracle, and
-    y bit-identical to the stage entry points' (separate gate_up and down launches), twice in
-    a row on the same workspace (the launch leaves its control words zero)."""
+    """The forward against the oracle (every token), bit-identical to the separate stage
+    launches and to the single expert launch's stage calls, and again twice in a row on one
+    workspace (every path leaves its control words zero)."""
     cfg = synthetic.MoEConfig("one_launch", e_lo=-8, e_hi=-2, seed=shape["T"] * 3 + shape["E"], **shape)
     host = synthetic.moe_inputs_host(cfg)
     say("moe single expert launch", shape)
