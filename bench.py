@@ -142,6 +142,9 @@ def forward_path(T: int, k: int, E: int, ns: int, I: int, H: int, act8: bool = F
         return "gate_up (routing and sorting in every workgroup), down, combine launches (combine inside down at the smallest T)"
     if ns == 0 and T <= 32 and T * k <= 256 and E <= 1024:
         return "route, gate_up (sorting in every workgroup), down, combine launches"
+    if (not act8 and 16 < T <= 32 and I % 1024 == 0 and H % 128 == 0
+            and min(T * (k + ns), E + ns) * (I // 64) >= 1536):
+        return "route, sort, gate_up + down (one launch), combine launches"
     return "route_sort, gate_up, down, combine launches"
 
 

@@ -681,8 +681,8 @@ int launch_gate_up_sorted(const uint16_t* x, const int32_t* ids, const uint8_t* 
 constexpr int DN_SPS_DEEP = 4;
 static_assert(SRUN % DN_SPS_DEEP == 0, "scale runs end on steps");
 
-template <int NS, class SR>
-struct DownAfterGateUp : DownPolicy<NS, LdsSortW, GU_XCHUNK, false, SR, false, false> {
+template <int NS, class Meta, class SR>
+struct DownAfterGateUp : DownPolicy<NS, Meta, GU_XCHUNK, false, SR, false, false> {
   static constexpr bool SENTINEL = true;
   // (ready: workgroups past their gate_up items; ready_target: the grid; err: the error word)
   __device__ __forceinline__ void wait_all_written() const {
@@ -699,29 +699,33 @@ struct DownAfterGateUp : DownPolicy<NS, LdsSortW, GU_XCHUNK, false, SR, false, f
   }
 };
 
-__global__ void __launch_bounds__(WG_WAVES * 64) moe_experts_sorted_kernel(
-    const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, const uint8_t* __restrict__ wgu,
-    const uint8_t* __restrict__ sgu, const uint8_t* __restrict__ wd, const uint8_t* __restrict__ sd, uint16_t* h,
-    float* __restrict__ dpart, int32_t* ctl, int T, int H, int I, int E, int k) {
-  __shared__ __attribute__((aligned(16))) uint8_t xbufs[2 * GU_XCHUNK];
-  __shared__ __attribute__((aligned(16))) uint8_t slabs[WG_WAVES][SLAB_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t sslabs[WG_WAVES][ScaleRun4::slab_bytes<2>()];
-  __shared__ uint32_t xctr[2];
-  __shared__ int32_t cq[4];
-  __shared__ int32_t last;
-  __shared__ WgSort wsort;
+// LDS of the single expert launch (besides the sort it may hold)
+struct ExpertsLds {
+  uint8_t* xbufs;    // 2 * GU_XCHUNK
+  uint8_t* slabs;    // WG_WAVES * SLAB_BYTES
+  uint8_t* sslabs;   // WG_WAVES * ScaleRun4::slab_bytes<2>()
+  uint32_t* xctr;    // 2
+  int32_t* cq;       // 4
+  int32_t* last;     // 1
+};
+
+// Both phases and the exit, for the sort in `meta` (the workgroup's own in LDS, or the sort
+// launches' in global memory).
+template <class Meta>
+__device__ __forceinline__ void experts_phases(const Meta& meta, const ExpertsLds& L, const uint16_t* __restrict__ x,
+                                               const uint8_t* __restrict__ wgu, const uint8_t* __restrict__ sgu,
+                                               const uint8_t* __restrict__ wd, const uint8_t* __restrict__ sd,
+                                               uint16_t* h, float* __restrict__ dpart, int32_t* ctl, int H, int I,
+                                               int k) {
+  constexpr int SSLAB = ScaleRun4::slab_bytes<2>();
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  if (tid < 2) xctr[tid] = 0u;
-  lds_wgsort* ws = (lds_wgsort*)&wsort;
-  wg_sort_slots(ids, T, E, k, ws, xbufs);
-  const LdsSortW meta{ws};
   const int na = meta.num_active();
   const int levels = (meta.max_rows() + 15) >> 4;  // row-group levels that exist
 
   // ---------------------------------------------------------------- gate_up + SwiGLU
   {
-    using PG = GateUpPolicy<2, LdsSortW, GU_XCHUNK, true>;
+    using PG = GateUpPolicy<2, Meta, GU_XCHUNK, true>;
     PG p;
     p.m = meta;
     p.xrowsegs = XGeom<GU_XCHUNK>::ROWSEGS;
@@ -740,8 +744,9 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_experts_sorted_kernel(
     p.kinv = ((1u << 24) + (uint32_t)k - 1u) / (uint32_t)k;
     p.e_codes = (size_t)2 * I * (H / 2);
     p.e_scales = (size_t)2 * I * (H / 32);
-    ClaimedUnits seq{ctl + CTL_CLAIM_GU, (lds_i32*)cq, na * p.nquad, 0, false};
-    stream_items<PG, GU_SPS>(p, seq, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
+    ClaimedUnits seq{ctl + CTL_CLAIM_GU, (lds_i32*)L.cq, na * p.nquad, 0, false};
+    stream_items<PG, GU_SPS>(p, seq, L.xbufs, L.xctr, L.slabs + wave * SLAB_BYTES, L.sslabs + wave * SSLAB, wave,
+                             lane);
     seq.finish();
   }
   // this workgroup's h stores are complete; count it, and start a fresh chunk hand-off
@@ -749,14 +754,14 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_experts_sorted_kernel(
   __syncthreads();
   if (tid == 0) {
     __hip_atomic_fetch_add(&ctl[CTL_GU_DONE], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    xctr[0] = 0u;
-    xctr[1] = 0u;
+    L.xctr[0] = 0u;
+    L.xctr[1] = 0u;
   }
   __syncthreads();
 
   // ---------------------------------------------------------------- down
   {
-    using PD = DownAfterGateUp<2, ScaleRun4>;
+    using PD = DownAfterGateUp<2, Meta, ScaleRun4>;
     PD p;
     p.m = meta;
     p.xrowsegs = XGeom<GU_XCHUNK>::ROWSEGS;
@@ -778,21 +783,56 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_experts_sorted_kernel(
     p.err = ctl + CTL_ERR;
     p.flag = nullptr;
     p.wave = wave;
-    ClaimedUnits seq{ctl + CTL_CLAIM_DN, (lds_i32*)cq, na * p.nquad, 0, false};
-    stream_items<PD, DN_SPS_DEEP>(p, seq, xbufs, xctr, slabs[wave], sslabs[wave], wave, lane);
+    ClaimedUnits seq{ctl + CTL_CLAIM_DN, (lds_i32*)L.cq, na * p.nquad, 0, false};
+    stream_items<PD, DN_SPS_DEEP>(p, seq, L.xbufs, L.xctr, L.slabs + wave * SLAB_BYTES, L.sslabs + wave * SSLAB, wave,
+                                  lane);
     seq.finish();
   }
 
   // ---------------------------------------------------------------- exit
   __syncthreads();
   if (tid == 0)
-    last = __hip_atomic_fetch_add(&ctl[CTL_EXIT], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1;
+    *L.last = __hip_atomic_fetch_add(&ctl[CTL_EXIT], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              (int)gridDim.x - 1;
   __syncthreads();
-  if (last && tid == 0) {
+  if (*L.last && tid == 0) {
     __hip_atomic_store(&ctl[CTL_GU_DONE], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&ctl[CTL_EXIT], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
+
+#define MX_EXPERTS_LDS                                                                   \
+  __shared__ __attribute__((aligned(16))) uint8_t xbufs[2 * GU_XCHUNK];                   \
+  __shared__ __attribute__((aligned(16))) uint8_t slabs[WG_WAVES * SLAB_BYTES];           \
+  __shared__ __attribute__((aligned(16))) uint8_t sslabs[WG_WAVES * ScaleRun4::slab_bytes<2>()]; \
+  __shared__ uint32_t xctr[2];                                                            \
+  __shared__ int32_t cq[4];                                                               \
+  __shared__ int32_t last;                                                                \
+  const ExpertsLds lds{xbufs, slabs, sslabs, xctr, cq, &last};                            \
+  if (threadIdx.x < 2) xctr[threadIdx.x] = 0u
+
+// T <= 32: every workgroup sorts the routed ids itself.
+__global__ void __launch_bounds__(WG_WAVES * 64) moe_experts_sorted_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, const uint8_t* __restrict__ wgu,
+    const uint8_t* __restrict__ sgu, const uint8_t* __restrict__ wd, const uint8_t* __restrict__ sd, uint16_t* h,
+    float* __restrict__ dpart, int32_t* ctl, int T, int H, int I, int E, int k) {
+  MX_EXPERTS_LDS;
+  __shared__ WgSort wsort;
+  lds_wgsort* ws = (lds_wgsort*)&wsort;
+  wg_sort_slots(ids, T, E, k, ws, xbufs);  // ends with a barrier: xbufs is free again
+  experts_phases(LdsSortW{ws}, lds, x, wgu, sgu, wd, sd, h, dpart, ctl, H, I, k);
+}
+
+// Any T: the sort launches' result in global memory.
+__global__ void __launch_bounds__(WG_WAVES * 64) moe_experts_kernel(
+    const uint16_t* __restrict__ x, SortView sv, const uint8_t* __restrict__ wgu, const uint8_t* __restrict__ sgu,
+    const uint8_t* __restrict__ wd, const uint8_t* __restrict__ sd, uint16_t* h, float* __restrict__ dpart,
+    int32_t* ctl, int H, int I, int k) {
+  MX_EXPERTS_LDS;
+  __syncthreads();
+  experts_phases(GlobalSort{sv}, lds, x, wgu, sgu, wd, sd, h, dpart, ctl, H, I, k);
+}
+#undef MX_EXPERTS_LDS
 
 // The sort fits one workgroup and I and H take 4-segment scale runs and 4- and 2-segment
 // steps.  The launch is correct for any number of items (workgroups without any pass
@@ -822,6 +862,21 @@ int launch_experts_sorted(const uint16_t* x, const int32_t* ids, const uint8_t* 
   const dim3 grid((unsigned)(device_cu_count() * occ)), block(WG_WAVES * 64);
   hipLaunchKernelGGL(moe_experts_sorted_kernel, grid, block, 0, stream, x, ids, wgu, sgu, wd, sd, h, dpart, ctl, T, H,
                      I, E, k);
+  return hip_status(hipGetLastError());
+}
+
+bool experts_fits(int H, int I) {
+  return H % (SEG_K * GU_SPS) == 0 && H % (SEG_K * SRUN) == 0 && I % (SEG_K * SRUN) == 0 &&
+         I % (SEG_K * DN_SPS_DEEP) == 0 && H % (2 * SUB_ROWS * WG_WAVES) == 0;
+}
+
+int launch_experts(const uint16_t* x, const SortView& sv, const uint8_t* wgu, const uint8_t* sgu, const uint8_t* wd,
+                   const uint8_t* sd, uint16_t* h, float* dpart, int32_t* ctl, int H, int I, int k,
+                   hipStream_t stream) {
+  if (!experts_fits(H, I)) return MX_ERR_SHAPE;
+  static const int occ = routed_occupancy(moe_experts_kernel);
+  const dim3 grid((unsigned)(device_cu_count() * occ)), block(WG_WAVES * 64);
+  hipLaunchKernelGGL(moe_experts_kernel, grid, block, 0, stream, x, sv, wgu, sgu, wd, sd, h, dpart, ctl, H, I, k);
   return hip_status(hipGetLastError());
 }
 

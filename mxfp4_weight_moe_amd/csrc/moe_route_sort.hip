@@ -258,9 +258,10 @@ constexpr int ROUTE_SORT_FUSED_MAX_T = SORT_THREADS / 64;
 
 int launch_route_sort(const float* logits, int T, int E, int k, int ns, int32_t* ids, float* gates, int32_t* counts,
                       int32_t* offsets, int32_t* sorted_slots, int32_t* active, int32_t* num_active,
-                      hipStream_t stream) {
+                      hipStream_t stream, void* fill, size_t fill_bytes) {
+  if (fill && T <= ROUTE_SORT_FUSED_MAX_T) return MX_ERR_SHAPE;  // the single-workgroup launch does not fill
   if (T > ROUTE_SORT_FUSED_MAX_T) {
-    const int st = launch_route(logits, T, E, k, ns, ids, gates, stream);
+    const int st = launch_route(logits, T, E, k, ns, ids, gates, stream, fill, fill_bytes);
     if (st != MX_OK) return st;
     return launch_sort(ids, T, k + ns, E + ns, counts, offsets, sorted_slots, active, num_active, stream);
   }

@@ -355,6 +355,16 @@ static int moe_forward_impl(const uint16_t* x, const float* router_logits, int64
     if ((st = launch_gate_up_sorted(x, ws.ids, w_gate_up, s_gate_up, ws.h, ws.counts, ws.offsets, ws.sorted_slots,
                                     ws.active, ws.num_active, ws.ctl, t, h, i, e, k, act8, s)) != MX_OK)
       return st;
+  } else if (!act8 && t > 16 && t <= EXPERTS_MAX_T && experts_fits(h, i) && experts_sorted_pays(t, e + n, k + n, i)) {
+    // shared experts, or more than 256 slots: the route and sort launches (the route launch
+    // also fills h with 0xFFFF), one launch for both expert GEMMs, then the combine
+    if ((st = launch_route_sort(router_logits, t, e, k, n, ws.ids, ws.gates, ws.counts, ws.offsets, ws.sorted_slots,
+                                ws.active, ws.num_active, s, ws.h, (size_t)t * (k + n) * i * 2)) != MX_OK)
+      return st;
+    if ((st = launch_experts(x, sv, w_gate_up, s_gate_up, w_down, s_down, ws.h, ws.dpart, ws.ctl, h, i, k + n, s)) !=
+        MX_OK)
+      return st;
+    return launch_combine(ws.dpart, ws.gates, y, t, h, k + n, s);
   } else {
     if ((st = launch_route_sort(router_logits, t, e, k, n, ws.ids, ws.gates, ws.counts, ws.offsets, ws.sorted_slots,
                                 ws.active, ws.num_active, s)) != MX_OK)

@@ -78,10 +78,11 @@ int launch_route(const float* logits, int T, int E, int k, int ns, int32_t* ids,
                  void* fill = nullptr, size_t fill_bytes = 0);
 int launch_sort(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* sorted_slots,
                 int32_t* active, int32_t* num_active, hipStream_t stream);
-// route + sort in one single-workgroup launch (the layer forward's path)
+// route + sort: one single-workgroup launch up to 16 tokens, the route and sort launches
+// beyond (fill: as launch_route's, beyond 16 tokens only)
 int launch_route_sort(const float* logits, int T, int E, int k, int ns, int32_t* ids, float* gates, int32_t* counts,
                       int32_t* offsets, int32_t* sorted_slots, int32_t* active, int32_t* num_active,
-                      hipStream_t stream);
+                      hipStream_t stream, void* fill = nullptr, size_t fill_bytes = 0);
 // ctl: the workspace's control words (the expert GEMMs claim their units there);
 // act8: MXFP8 activations (x, resp. h, quantized as they are staged) and the scaled MFMA
 int launch_gate_up(const uint16_t* x, const uint8_t* wgu, const uint8_t* sgu, const SortView& sv, uint16_t* h,
@@ -106,6 +107,16 @@ int launch_gate_up_sorted(const uint16_t* x, const int32_t* ids, const uint8_t* 
 // where experts_sorted_pays.
 bool experts_sorted_fits(int T, int E, int k, int H, int I);
 bool experts_sorted_pays(int T, int E, int k, int I);
+// The same launch from a sort in global memory (moe_sort_by_expert's outputs).  The forward
+// uses it up to EXPERTS_MAX_T tokens: beyond, the down phase at gate_up's occupancy (2
+// workgroups per CU instead of 3) costs more than the ends of the launches it saves
+// (measured with the route and sort launches before it: T = 64 816.5 us per layer either
+// way, T = 128 with E = 384 1,330.5 -> 1,340.6; shared expert at T = 32 405.6 -> 398.4).
+constexpr int EXPERTS_MAX_T = 32;
+bool experts_fits(int H, int I);
+int launch_experts(const uint16_t* x, const SortView& sv, const uint8_t* wgu, const uint8_t* sgu, const uint8_t* wd,
+                   const uint8_t* sd, uint16_t* h, float* dpart, int32_t* ctl, int H, int I, int k,
+                   hipStream_t stream);
 int launch_experts_sorted(const uint16_t* x, const int32_t* ids, const uint8_t* wgu, const uint8_t* sgu,
                           const uint8_t* wd, const uint8_t* sd, uint16_t* h, float* dpart, int32_t* ctl, int T, int H,
                           int I, int E, int k, hipStream_t stream);
