@@ -5,7 +5,7 @@
     python bench.py --workload dense_t1|dense_t4 [--act8]      (the dense mx_linear)
 
 A step is one MoE layer forward (route + sort, gate_up + SwiGLU, down + combine) over one
-batch of T tokens.  Steps cycle over L distinct layers (own weights, own activations and
+batch of T tokens, in the launches moe_mxfp4_forward makes for that size (config.path).  Steps cycle over L distinct layers (own weights, own activations and
 routing), as a decode step walks a stack of MoE layers, so no step finds its expert
 weights in a cache: the 256 MB last-level cache is smaller than the active bytes of L-1
 layers.  Inputs are resident in HBM before timing.  One HIP graph holds the L layer
@@ -22,13 +22,14 @@ steps.  The first replays of the settle phase are reported beside the result.
 
 Printed: one JSON line for the chosen workload -- layer time (us), effective weight GB/s
 and its share of 8 TB/s and of this GPU's measured copy and read bandwidth (the library's
-HBM reference kernels), a roofline entry for the dominant kernel (gate_up), the CPU
+HBM reference kernels), a roofline entry for the dominant kernel (the launch of both
+expert GEMMs from 6 to 32 tokens where the forward runs them in one, gate_up otherwise), the CPU
 oracle's time on a bounded sample of the same workload and the worst parity ratio of that
 sample against the GPU's output, and (by default) the other configurations of the
 benchmark under "configs".  The kernel's launch time comes from a pass of max(K, 200)
 steps right after the timed region (behind a few graph replays, so the GPU does not idle in
-between), issued as the three stage calls with a HIP event between them on the stream the
-kernels run on.  roofline.traffic is the kernel's HBM bytes
+between), issued as the stage calls that make the forward's launches, with a HIP event
+between them on the stream the kernels run on.  roofline.traffic is the kernel's HBM bytes
 per launch as measured by the committed counter summary under profiles/, and null when the
 workload differs or the kernel's sources changed since the counters were taken.
 
@@ -61,13 +62,13 @@ STAGE_MIN = 200           # launches the per-kernel event pass times at least
 STAGE_LEAD_REPLAYS = 8    # graph replays queued right before it
 # the other configurations a default run reports beside its headline workload
 EXTRA_WORKLOADS = ("dense_t1", "dense_t4", "moe_t4", "moe_t128", "moe_sweep_t1")
-# sources (and build flags) the gate_up kernel is compiled from; the counter summary records
-# their hash, so measured traffic is only reported for the kernel it was measured on
-GATE_UP_SOURCES = ("mxfp4_weight_moe_amd/build.py", "mxfp4_weight_moe_amd/csrc/mx_device.hpp",
+# sources (and build flags) the expert GEMM kernels are compiled from; the counter summaries
+# record their hash, so measured traffic is only reported for the kernel it was measured on
+EXPERT_SOURCES = ("mxfp4_weight_moe_amd/build.py", "mxfp4_weight_moe_amd/csrc/mx_device.hpp",
                    "mxfp4_weight_moe_amd/csrc/mx_internal.hpp", "mxfp4_weight_moe_amd/csrc/mx_stream.hpp",
                    "mxfp4_weight_moe_amd/csrc/mx_act8.hpp", "mxfp4_weight_moe_amd/csrc/moe_policies.hpp",
                    "mxfp4_weight_moe_amd/csrc/moe_experts.hip", "mxfp4_weight_moe_amd/csrc/moe_fused.hip")
-GATE_UP_COUNTERS = os.path.join(ROOT, "profiles", "moe_gate_up_kernel.moe_t32_zipf.hbm_counters.txt")
+HEADLINE_COUNTERS = os.path.join(ROOT, "profiles", "moe_experts_sorted_kernel.moe_t32_zipf.hbm_counters.txt")
 MFMA_COUNTERS = os.path.join(ROOT, "profiles", "moe_t128.mfma_counters.txt")
 
 
@@ -156,8 +157,8 @@ def source_hash(paths) -> str:
     return h.hexdigest()[:16]
 
 
-def gate_up_source_hash() -> str:
-    return source_hash(GATE_UP_SOURCES)
+def expert_source_hash() -> str:
+    return source_hash(EXPERT_SOURCES)
 
 
 def read_summary(path):
@@ -170,11 +171,12 @@ def read_summary(path):
     return {a.strip(): b.strip() for a, b in kv.items()}
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per gate_up launch from the committed counter summary, or None when the
-    summary is absent, for another workload, or for other kernel sources."""
-    kv = read_summary(GATE_UP_COUNTERS)
-    if not kv or kv.get("workload") != workload or kv.get("kernel_sources_sha256") != gate_up_source_hash():
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None when the
+    summary is absent, for another workload or kernel, or for other kernel sources."""
+    kv = read_summary(HEADLINE_COUNTERS)
+    if (not kv or kv.get("workload") != workload or kv.get("kernel") != kernel
+            or kv.get("kernel_sources_sha256") != expert_source_hash()):
         return None
     try:
         return int(kv["hbm_read_bytes_per_launch"]) + int(kv["hbm_write_bytes_per_launch"])
@@ -186,7 +188,7 @@ def measured_mfma():
     """MFMA utilisation of the expert GEMMs at T = 128 from the committed counter summary
     (null when its kernel sources changed since)."""
     kv = read_summary(MFMA_COUNTERS)
-    if not kv or kv.get("kernel_sources_sha256") != gate_up_source_hash():
+    if not kv or kv.get("kernel_sources_sha256") != expert_source_hash():
         return None
     try:
         return {"workload": kv["workload"], "gate_up_mfma_busy_pct": float(kv["gate_up_mfma_busy_pct"]),
@@ -446,13 +448,14 @@ def moe_case(cfg, args, torch, mx, dev, *, steps: int, warmup: int, stage_pass: 
         gu_achieved = float(np.sum(gu_bytes) / (np.sum(gu_ms) * 1e-3) / 1e9)
         res["stages_us"] = {n: round(float(np.mean(v)) * 1e3, 2) for n, v in stage_ms.items()}
         res["staged_us_per_layer"] = round(sev[0][0].elapsed_time(sev[-1][-1]) * 1e3 / KS, 2)
+        kname = (("moe_fused_kernel" if args.persistent else "layer (all launches)") if whole_layer
+                 else ("moe_experts_sorted_kernel" if single_path else
+                       "moe_gate_up_sorted_kernel" if sorted_path else "moe_gate_up_kernel"))
         res["roofline"] = {
-            "kernel": ("moe_fused_kernel" if args.persistent else "layer (all launches)") if whole_layer
-            else ("moe_experts_sorted_kernel" if single_path else
-                  "moe_gate_up_sorted_kernel" if sorted_path else "moe_gate_up_kernel"),
+            "kernel": kname,
             "bound": "hbm", "achieved": round(gu_achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(gu_achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None if whole_layer else measured_traffic(cfg.name),
+            "traffic": None if whole_layer else measured_traffic(cfg.name, kname),
             "avg_launch_us": round(float(np.mean(gu_ms)) * 1e3, 2), "launches": len(gu_ms),
             "timing": "HIP events on the launch stream, one pair per launch, right after the timed region",
             "bytes_per_launch": int(np.mean(gu_bytes)),
