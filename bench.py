@@ -134,16 +134,16 @@ def gpu_clocks() -> dict:
     return out
 
 
-def forward_path(T: int, k: int, E: int, ns: int, I: int, H: int, act8: bool = False) -> str:
+def forward_path(T: int, k: int, E: int, ns: int, I: int, H: int) -> str:
     """The launches moe_mxfp4_forward makes for these sizes (its dispatch)."""
-    if (ns == 0 and not act8 and T <= 32 and T * k <= 256 and E <= 1024 and I % 1024 == 0 and H % 128 == 0
+    if (ns == 0 and T <= 32 and T * k <= 256 and E <= 1024 and I % 1024 == 0 and H % 128 == 0
             and min(T * k, E) * (I // 64) >= 1536):
         return "route, gate_up + down (one launch, sorting in every workgroup), combine launches"
     if ns == 0 and T <= 16 and T * k <= 128:
         return "gate_up (routing and sorting in every workgroup), down, combine launches (combine inside down at the smallest T)"
     if ns == 0 and T <= 32 and T * k <= 256 and E <= 1024:
         return "route, gate_up (sorting in every workgroup), down, combine launches"
-    if (not act8 and 16 < T <= 32 and I % 1024 == 0 and H % 128 == 0
+    if (16 < T <= 32 and I % 1024 == 0 and H % 128 == 0
             and min(T * (k + ns), E + ns) * (I // 64) >= 1536):
         return "route, sort, gate_up + down (one launch), combine launches"
     return "route_sort, gate_up, down, combine launches"
@@ -407,7 +407,7 @@ def moe_case(cfg, args, torch, mx, dev, *, steps: int, warmup: int, stage_pass: 
             "activations": "MXFP8 (E4M3, E8M0 scale per 32), quantized in the GEMM kernels" if args.act8 else "bf16",
             "layers_cycled": L, "timing": "eager launches" if args.eager else "HIP graph replay",
             "path": "one persistent launch" if args.persistent else
-            forward_path(T, k, E, ns, I, H, act8=args.act8),
+            forward_path(T, k, E, ns, I, H),
         },
     }
 

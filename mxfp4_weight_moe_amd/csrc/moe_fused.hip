@@ -681,8 +681,8 @@ int launch_gate_up_sorted(const uint16_t* x, const int32_t* ids, const uint8_t* 
 constexpr int DN_SPS_DEEP = 4;
 static_assert(SRUN % DN_SPS_DEEP == 0, "scale runs end on steps");
 
-template <int NS, class Meta, class SR>
-struct DownAfterGateUp : DownPolicy<NS, Meta, GU_XCHUNK, false, SR, false, false> {
+template <int NS, class Meta, class SR, bool A8>
+struct DownAfterGateUp : DownPolicy<NS, Meta, GU_XCHUNK, false, SR, A8, false> {
   static constexpr bool SENTINEL = true;
   // (ready: workgroups past their gate_up items; ready_target: the grid; err: the error word)
   __device__ __forceinline__ void wait_all_written() const {
@@ -710,8 +710,8 @@ struct ExpertsLds {
 };
 
 // Both phases and the exit, for the sort in `meta` (the workgroup's own in LDS, or the sort
-// launches' in global memory).
-template <class Meta>
+// launches' in global memory); A8: MXFP8 activations (x and h quantized as they are staged).
+template <bool A8, class Meta>
 __device__ __forceinline__ void experts_phases(const Meta& meta, const ExpertsLds& L, const uint16_t* __restrict__ x,
                                                const uint8_t* __restrict__ wgu, const uint8_t* __restrict__ sgu,
                                                const uint8_t* __restrict__ wd, const uint8_t* __restrict__ sd,
@@ -725,7 +725,7 @@ __device__ __forceinline__ void experts_phases(const Meta& meta, const ExpertsLd
 
   // ---------------------------------------------------------------- gate_up + SwiGLU
   {
-    using PG = GateUpPolicy<2, Meta, GU_XCHUNK, true>;
+    using PG = GateUpPolicy<2, Meta, GU_XCHUNK, true, A8>;
     PG p;
     p.m = meta;
     p.xrowsegs = XGeom<GU_XCHUNK>::ROWSEGS;
@@ -761,11 +761,12 @@ __device__ __forceinline__ void experts_phases(const Meta& meta, const ExpertsLd
 
   // ---------------------------------------------------------------- down
   {
-    using PD = DownAfterGateUp<2, Meta, ScaleRun4>;
+    using PD = DownAfterGateUp<2, Meta, ScaleRun4, A8>;
+    constexpr int SPS = A8 ? DN_SPS : DN_SPS_DEEP;  // the MXFP8 phase has no registers for the deeper ring
     PD p;
     p.m = meta;
     p.xrowsegs = XGeom<GU_XCHUNK>::ROWSEGS;
-    p.calign = DN_SPS_DEEP;
+    p.calign = SPS;
     p.nseg = I / SEG_K;
     p.nquad = H / (PD::TILE * WG_WAVES);
     p.na = na;
@@ -784,7 +785,7 @@ __device__ __forceinline__ void experts_phases(const Meta& meta, const ExpertsLd
     p.flag = nullptr;
     p.wave = wave;
     ClaimedUnits seq{ctl + CTL_CLAIM_DN, (lds_i32*)L.cq, na * p.nquad, 0, false};
-    stream_items<PD, DN_SPS_DEEP>(p, seq, L.xbufs, L.xctr, L.slabs + wave * SLAB_BYTES, L.sslabs + wave * SSLAB, wave,
+    stream_items<PD, SPS>(p, seq, L.xbufs, L.xctr, L.slabs + wave * SLAB_BYTES, L.sslabs + wave * SSLAB, wave,
                                   lane);
     seq.finish();
   }
@@ -812,6 +813,7 @@ __device__ __forceinline__ void experts_phases(const Meta& meta, const ExpertsLd
   if (threadIdx.x < 2) xctr[threadIdx.x] = 0u
 
 // T <= 32: every workgroup sorts the routed ids itself.
+template <bool A8>
 __global__ void __launch_bounds__(WG_WAVES * 64) moe_experts_sorted_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, const uint8_t* __restrict__ wgu,
     const uint8_t* __restrict__ sgu, const uint8_t* __restrict__ wd, const uint8_t* __restrict__ sd, uint16_t* h,
@@ -820,17 +822,18 @@ __global__ void __launch_bounds__(WG_WAVES * 64) moe_experts_sorted_kernel(
   __shared__ WgSort wsort;
   lds_wgsort* ws = (lds_wgsort*)&wsort;
   wg_sort_slots(ids, T, E, k, ws, xbufs);  // ends with a barrier: xbufs is free again
-  experts_phases(LdsSortW{ws}, lds, x, wgu, sgu, wd, sd, h, dpart, ctl, H, I, k);
+  experts_phases<A8>(LdsSortW{ws}, lds, x, wgu, sgu, wd, sd, h, dpart, ctl, H, I, k);
 }
 
 // Any T: the sort launches' result in global memory.
+template <bool A8>
 __global__ void __launch_bounds__(WG_WAVES * 64) moe_experts_kernel(
     const uint16_t* __restrict__ x, SortView sv, const uint8_t* __restrict__ wgu, const uint8_t* __restrict__ sgu,
     const uint8_t* __restrict__ wd, const uint8_t* __restrict__ sd, uint16_t* h, float* __restrict__ dpart,
     int32_t* ctl, int H, int I, int k) {
   MX_EXPERTS_LDS;
   __syncthreads();
-  experts_phases(GlobalSort{sv}, lds, x, wgu, sgu, wd, sd, h, dpart, ctl, H, I, k);
+  experts_phases<A8>(GlobalSort{sv}, lds, x, wgu, sgu, wd, sd, h, dpart, ctl, H, I, k);
 }
 #undef MX_EXPERTS_LDS
 
@@ -854,15 +857,23 @@ bool experts_sorted_pays(int T, int E, int k, int I) {
   return na_max * (I / (SUB_ROWS * WG_WAVES)) >= EXPERTS_MIN_ITEMS;
 }
 
+template <bool A8>
+static int launch_experts_sorted_run(const uint16_t* x, const int32_t* ids, const uint8_t* wgu, const uint8_t* sgu,
+                                     const uint8_t* wd, const uint8_t* sd, uint16_t* h, float* dpart, int32_t* ctl,
+                                     int T, int H, int I, int E, int k, hipStream_t stream) {
+  static const int occ = routed_occupancy(moe_experts_sorted_kernel<A8>);
+  const dim3 grid((unsigned)(device_cu_count() * occ)), block(WG_WAVES * 64);
+  hipLaunchKernelGGL(moe_experts_sorted_kernel<A8>, grid, block, 0, stream, x, ids, wgu, sgu, wd, sd, h, dpart, ctl, T,
+                     H, I, E, k);
+  return hip_status(hipGetLastError());
+}
+
 int launch_experts_sorted(const uint16_t* x, const int32_t* ids, const uint8_t* wgu, const uint8_t* sgu,
                           const uint8_t* wd, const uint8_t* sd, uint16_t* h, float* dpart, int32_t* ctl, int T, int H,
-                          int I, int E, int k, hipStream_t stream) {
+                          int I, int E, int k, bool act8, hipStream_t stream) {
   if (!experts_sorted_fits(T, E, k, H, I)) return MX_ERR_SHAPE;
-  static const int occ = routed_occupancy(moe_experts_sorted_kernel);
-  const dim3 grid((unsigned)(device_cu_count() * occ)), block(WG_WAVES * 64);
-  hipLaunchKernelGGL(moe_experts_sorted_kernel, grid, block, 0, stream, x, ids, wgu, sgu, wd, sd, h, dpart, ctl, T, H,
-                     I, E, k);
-  return hip_status(hipGetLastError());
+  if (act8) return launch_experts_sorted_run<true>(x, ids, wgu, sgu, wd, sd, h, dpart, ctl, T, H, I, E, k, stream);
+  return launch_experts_sorted_run<false>(x, ids, wgu, sgu, wd, sd, h, dpart, ctl, T, H, I, E, k, stream);
 }
 
 bool experts_fits(int H, int I) {
@@ -870,14 +881,22 @@ bool experts_fits(int H, int I) {
          I % (SEG_K * DN_SPS_DEEP) == 0 && H % (2 * SUB_ROWS * WG_WAVES) == 0;
 }
 
+template <bool A8>
+static int launch_experts_run(const uint16_t* x, const SortView& sv, const uint8_t* wgu, const uint8_t* sgu,
+                              const uint8_t* wd, const uint8_t* sd, uint16_t* h, float* dpart, int32_t* ctl, int H,
+                              int I, int k, hipStream_t stream) {
+  static const int occ = routed_occupancy(moe_experts_kernel<A8>);
+  const dim3 grid((unsigned)(device_cu_count() * occ)), block(WG_WAVES * 64);
+  hipLaunchKernelGGL(moe_experts_kernel<A8>, grid, block, 0, stream, x, sv, wgu, sgu, wd, sd, h, dpart, ctl, H, I, k);
+  return hip_status(hipGetLastError());
+}
+
 int launch_experts(const uint16_t* x, const SortView& sv, const uint8_t* wgu, const uint8_t* sgu, const uint8_t* wd,
-                   const uint8_t* sd, uint16_t* h, float* dpart, int32_t* ctl, int H, int I, int k,
+                   const uint8_t* sd, uint16_t* h, float* dpart, int32_t* ctl, int H, int I, int k, bool act8,
                    hipStream_t stream) {
   if (!experts_fits(H, I)) return MX_ERR_SHAPE;
-  static const int occ = routed_occupancy(moe_experts_kernel);
-  const dim3 grid((unsigned)(device_cu_count() * occ)), block(WG_WAVES * 64);
-  hipLaunchKernelGGL(moe_experts_kernel, grid, block, 0, stream, x, sv, wgu, sgu, wd, sd, h, dpart, ctl, H, I, k);
-  return hip_status(hipGetLastError());
+  if (act8) return launch_experts_run<true>(x, sv, wgu, sgu, wd, sd, h, dpart, ctl, H, I, k, stream);
+  return launch_experts_run<false>(x, sv, wgu, sgu, wd, sd, h, dpart, ctl, H, I, k, stream);
 }
 
 // Measured against the route + sort launch followed by gate_up (graph replay, 4 layers):

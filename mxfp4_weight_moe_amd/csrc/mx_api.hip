@@ -288,7 +288,7 @@ int moe_expert_gemms_from_ids(const uint16_t* x, const int32_t* ids, const uint8
   const MoeWorkspace ws = moe_workspace_carve(workspace, T, H, I, E, top_k);
   if (workspace_bytes < ws.bytes) return MX_ERR_WORKSPACE;
   return launch_experts_sorted(x, ids, w_gate_up, s_gate_up, w_down, s_down, h, d, ws.ctl, (int)T, (int)H, (int)I,
-                               (int)E, (int)top_k, static_cast<hipStream_t>(stream));
+                               (int)E, (int)top_k, false, static_cast<hipStream_t>(stream));
 }
 
 int moe_combine(const float* d, const float* gates, uint16_t* y, int64_t T, int64_t H, int64_t top_k, void* stream) {
@@ -334,13 +334,13 @@ static int moe_forward_impl(const uint16_t* x, const float* router_logits, int64
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int t = (int)T, h = (int)H, i = (int)I, e = (int)E, k = (int)top_k, n = (int)ns;
   const SortView sv{ws.counts, ws.offsets, ws.sorted_slots, ws.active, ws.num_active};
-  if (n == 0 && !act8 && experts_sorted_fits(t, e, k, h, i) && experts_sorted_pays(t, e, k, i)) {
+  if (n == 0 && experts_sorted_fits(t, e, k, h, i) && experts_sorted_pays(t, e, k, i)) {
     // the routing launch (which also fills h with 0xFFFF), one launch for both expert
     // GEMMs, then the combine
     if ((st = launch_route(router_logits, t, e, k, 0, ws.ids, ws.gates, s, ws.h, (size_t)t * k * i * 2)) != MX_OK)
       return st;
     if ((st = launch_experts_sorted(x, ws.ids, w_gate_up, s_gate_up, w_down, s_down, ws.h, ws.dpart, ws.ctl, t, h, i, e,
-                                    k, s)) != MX_OK)
+                                    k, act8, s)) != MX_OK)
       return st;
     return launch_combine(ws.dpart, ws.gates, y, t, h, k, s);
   } else if (n == 0 && gate_up_routed_fits(t, e, k, h, i)) {
@@ -355,14 +355,14 @@ static int moe_forward_impl(const uint16_t* x, const float* router_logits, int64
     if ((st = launch_gate_up_sorted(x, ws.ids, w_gate_up, s_gate_up, ws.h, ws.counts, ws.offsets, ws.sorted_slots,
                                     ws.active, ws.num_active, ws.ctl, t, h, i, e, k, act8, s)) != MX_OK)
       return st;
-  } else if (!act8 && t > 16 && t <= EXPERTS_MAX_T && experts_fits(h, i) && experts_sorted_pays(t, e + n, k + n, i)) {
+  } else if (t > 16 && t <= EXPERTS_MAX_T && experts_fits(h, i) && experts_sorted_pays(t, e + n, k + n, i)) {
     // shared experts, or more than 256 slots: the route and sort launches (the route launch
     // also fills h with 0xFFFF), one launch for both expert GEMMs, then the combine
     if ((st = launch_route_sort(router_logits, t, e, k, n, ws.ids, ws.gates, ws.counts, ws.offsets, ws.sorted_slots,
                                 ws.active, ws.num_active, s, ws.h, (size_t)t * (k + n) * i * 2)) != MX_OK)
       return st;
-    if ((st = launch_experts(x, sv, w_gate_up, s_gate_up, w_down, s_down, ws.h, ws.dpart, ws.ctl, h, i, k + n, s)) !=
-        MX_OK)
+    if ((st = launch_experts(x, sv, w_gate_up, s_gate_up, w_down, s_down, ws.h, ws.dpart, ws.ctl, h, i, k + n, act8,
+                             s)) != MX_OK)
       return st;
     return launch_combine(ws.dpart, ws.gates, y, t, h, k + n, s);
   } else {

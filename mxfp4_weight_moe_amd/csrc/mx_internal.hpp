@@ -115,11 +115,11 @@ bool experts_sorted_pays(int T, int E, int k, int I);
 constexpr int EXPERTS_MAX_T = 32;
 bool experts_fits(int H, int I);
 int launch_experts(const uint16_t* x, const SortView& sv, const uint8_t* wgu, const uint8_t* sgu, const uint8_t* wd,
-                   const uint8_t* sd, uint16_t* h, float* dpart, int32_t* ctl, int H, int I, int k,
+                   const uint8_t* sd, uint16_t* h, float* dpart, int32_t* ctl, int H, int I, int k, bool act8,
                    hipStream_t stream);
 int launch_experts_sorted(const uint16_t* x, const int32_t* ids, const uint8_t* wgu, const uint8_t* sgu,
                           const uint8_t* wd, const uint8_t* sd, uint16_t* h, float* dpart, int32_t* ctl, int T, int H,
-                          int I, int E, int k, hipStream_t stream);
+                          int I, int E, int k, bool act8, hipStream_t stream);
 // The forward's gate_up for small T with the routing and sort done in every workgroup (no
 // route + sort launch before it); it also writes the sort outputs and gates for the down
 // launch.  gate_up_routed_fits says when it applies (no shared experts); act8: MXFP8

@@ -184,6 +184,11 @@ TINY = [
     dict(T=9, H=1024, I=256, E=3, k=2),     # one-segment down reductions
     dict(T=20, H=2048, I=768, E=6, k=3),
     dict(T=4, H=1024, I=1024, E=6, k=2, n_shared=1),
+    # both expert GEMMs in one launch: the workgroup's own sort (T = 8, 32), and the sort
+    # launches' result (a shared expert at T = 24)
+    dict(T=8, H=1024, I=2048, E=64, k=8),
+    dict(T=32, H=1024, I=1024, E=128, k=8),
+    dict(T=24, H=1024, I=1024, E=128, k=6, n_shared=1),
 ]
 
 
@@ -203,7 +208,7 @@ def test_moe_a8_tiny(dev, mx, shape):
 
 # moe_sweep_t1: in-gate_up routing with the combine inside down; moe_sweep_t2: half-width down
 FULL = [("moe_t4", None), ("moe_t32_zipf", [0, 7, 31]), ("moe_t128", [0, 100]), ("moe_tp8_t32", [0, 3, 30]),
-        ("moe_shared_t1", None), ("moe_sweep_t1", None), ("moe_sweep_t2", None)]
+        ("moe_shared_t1", None), ("moe_shared_t32", [0, 9, 31]), ("moe_sweep_t1", None), ("moe_sweep_t2", None)]
 
 
 @pytest.mark.parametrize("name,tokens", FULL, ids=[f[0] for f in FULL])
@@ -220,12 +225,13 @@ def test_moe_a8_full_size(dev, mx, name, tokens):
     say(f"  worst ratio {worst:.3g}")
 
 
-@pytest.mark.parametrize("T", [2, 20])
-def test_moe_a8_graph_replays(dev, mx, T):
-    """The MXFP8 forward captured in a HIP graph (at T = 2 its down launch also combines):
-    every replay, with eager work and synchronizations between replays, gives the eager
-    result bit for bit, and the workspace control words end zero."""
-    cfg = synthetic.MoEConfig("graph_a8", T=T, H=1024, I=1024, E=16, k=4, routing="normal", e_lo=-8, e_hi=-2,
+@pytest.mark.parametrize("T,E,k", [(2, 16, 4), (20, 16, 4), (24, 128, 8)])
+def test_moe_a8_graph_replays(dev, mx, T, E, k):
+    """The MXFP8 forward captured in a HIP graph (at T = 2 its down launch also combines; at
+    T = 24 over 128 experts both expert GEMMs run in one launch): every replay, with eager
+    work and synchronizations between replays, gives the eager result bit for bit, and the
+    workspace control words end zero."""
+    cfg = synthetic.MoEConfig("graph_a8", T=T, H=1024, I=1024, E=E, k=k, routing="normal", e_lo=-8, e_hi=-2,
                               seed=40 + T)
     host = synthetic.moe_inputs_host(cfg)
     say("a8 forward graph replays, T =", T)

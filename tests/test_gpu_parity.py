@@ -909,11 +909,13 @@ def test_down_launch_combine_back_to_back(dev, mx):
         check_bound(to_host_bits(y), yo, sm, MOE_REL, f"back-to-back combine T={cfg.T} act8={act8}")
 
 
-@pytest.mark.parametrize("T,persistent", [(4, True), (4, False), (20, False)])
-def test_forward_graph_replays(dev, mx, T, persistent):
+@pytest.mark.parametrize("T,persistent,E,k", [(4, True, 16, 4), (4, False, 16, 4), (20, False, 16, 4),
+                                               (24, False, 128, 8)])
+def test_forward_graph_replays(dev, mx, T, persistent, E, k):
     """The forward captured in a HIP graph: every replay, with eager work and
-    synchronizations between replays, gives the eager result bit for bit."""
-    cfg = synthetic.MoEConfig("graph", T=T, H=1024, I=1024, E=16, k=4, routing="normal", e_lo=-8, e_hi=-2, seed=T)
+    synchronizations between replays, gives the eager result bit for bit (at T = 24 over 128
+    experts: the routing launch that fills h, both expert GEMMs in one launch, the combine)."""
+    cfg = synthetic.MoEConfig("graph", T=T, H=1024, I=1024, E=E, k=k, routing="normal", e_lo=-8, e_hi=-2, seed=T)
     host = synthetic.moe_inputs_host(cfg)
     say("forward graph replays, T =", T, "persistent =", persistent)
     d, x, logits = moe_device_inputs(cfg, dev, host)
