@@ -652,7 +652,8 @@ int launch_gate_up_sorted(const uint16_t* x, const int32_t* ids, const uint8_t* 
 
 // ------------------------------------------------------------------ gate_up and down in one launch
 
-// From 17 to 32 tokens the forward runs both expert GEMMs in one launch, so that down's items
+// Up to 32 tokens, wherever the gate_up items can be 3 or more per resident workgroup (from 6
+// tokens at top-8), the forward runs both expert GEMMs in one launch, so that down's items
 // fill the end of gate_up's: a workgroup whose gate_up claims run out starts on down items
 // at once, instead of idling until the slowest workgroup of a gate_up launch finishes (13 us
 // of idle per workgroup on average at 32 tokens, Zipf routing) and then paying a launch
@@ -662,9 +663,10 @@ int launch_gate_up_sorted(const uint16_t* x, const int32_t* ids, const uint8_t* 
 // (stream_items), then its down items, through the same LDS.
 //
 // Hand-off of h without flags: h is filled with 0xFFFF before the launch (by the routing
-// launch), gate_up writes each element once with device-coherent stores, and a down wave
-// that loads an 0xFFFF (not yet written, or a NaN with that bit pattern) waits until every
-// workgroup has finished its gate_up phase and loads again (xchunk_settle).  Items are
+// launch; the kernel boundary leaves no older copy of it in any cache), gate_up writes each
+// element once with device-coherent stores, and a down wave that loads an 0xFFFF (not yet
+// written, or a NaN with that bit pattern) waits until every workgroup has finished its
+// gate_up phase and loads again, coherently (xchunk_settle).  Items are
 // taken in the same expert order in both phases, so down reaches an expert long after its
 // gate_up items finished and the wait is practically never taken; a per-item flag written
 // by gate_up was measured instead and cost 3-40 us at 32 tokens (stores and atomics from
