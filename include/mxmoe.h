@@ -215,10 +215,14 @@ MX_API int moe_gate_up_swiglu_from_ids(const uint16_t* x, const int32_t* ids, co
  * Kernel Results, for the two GEMMs of an MXFP4 expert; the AMD megakernel blog, "What Drives
  * the Speedup", 1. Megakernels, for removing the boundary between dependent kernels).
  *   ids  int32 [T, top_k], each row top_k distinct ids in [0, E) (moe_route_topk's output)
- *   h    bf16 [T*top_k, I].  In: every element 0xFFFF.  The down items recognise rows that
- *        gate_up has not written yet by that pattern (0xFFFF is a NaN that SwiGLU produces
- *        only from NaN inputs; if it does, the launch only waits longer).  Out: h as
- *        moe_gate_up_swiglu writes it (identical values; rows in sorted-slot order).
+ *   h    bf16 [T*top_k, I] (written): h as moe_gate_up_swiglu writes it (identical values;
+ *        rows in sorted-slot order).  It is also the hand-off between the two GEMMs: the
+ *        down items recognise rows that gate_up has not written yet by the pattern 0xFFFF
+ *        in every element (a NaN that SwiGLU produces only from NaN inputs; if it does, the
+ *        launch only waits longer), so h must hold 0xFFFF throughout when the launch starts.
+ *   h_prefilled  0: the call first fills h with 0xFFFF (one more launch, as moe_mxfp4_forward
+ *        does inside its routing launch); 1: the caller has done so on this stream.  With 1
+ *        and any other content in h the results are undefined.
  *   d    fp32 [T*top_k, H] (written): d[t*top_k + j, n] = sum_i h[p(t,j), i] * Wd[e][n, i]
  *        (fp32), the slot's down output before its gate; moe_combine makes y from it.
  * The launch's workgroups may wait for one another: a down item that finds an unwritten h
@@ -232,8 +236,9 @@ MX_API int moe_gate_up_swiglu_from_ids(const uint16_t* x, const int32_t* ids, co
  */
 MX_API int moe_expert_gemms_from_ids(const uint16_t* x, const int32_t* ids, const uint8_t* w_gate_up,
                                      const uint8_t* s_gate_up, const uint8_t* w_down, const uint8_t* s_down,
-                                     uint16_t* h, float* d, int64_t T, int64_t H, int64_t I, int64_t E,
-                                     int64_t top_k, void* workspace, size_t workspace_bytes, void* stream);
+                                     uint16_t* h, int h_prefilled, float* d, int64_t T, int64_t H, int64_t I,
+                                     int64_t E, int64_t top_k, void* workspace, size_t workspace_bytes,
+                                     void* stream);
 
 /*
  * Stage hook: the gate-weighted combine, y[t, n] = bf16_rne( sum_j gates[t, j] * d[t*top_k + j, n] )

@@ -45,8 +45,8 @@ _lib.moe_gate_up_swiglu_from_ids.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P,
                                              ctypes.c_size_t, _P]
 _lib.moe_down_combine.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P,
                                   ctypes.c_size_t, _P]
-_lib.moe_expert_gemms_from_ids.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P,
-                                           ctypes.c_size_t, _P]
+_lib.moe_expert_gemms_from_ids.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _P, _I64, _I64, _I64, _I64,
+                                           _I64, _P, ctypes.c_size_t, _P]
 _lib.moe_combine.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P]
 _lib.moe_mxfp4_workspace_size.restype = ctypes.c_size_t
 _lib.moe_mxfp4_workspace_size.argtypes = [_I64, _I64, _I64, _I64, _I64]
@@ -348,10 +348,10 @@ def moe_gate_up_swiglu_from_ids(x: torch.Tensor, ids: torch.Tensor, W_gate_up: t
 def moe_expert_gemms_from_ids(x: torch.Tensor, ids: torch.Tensor, W_gate_up: torch.Tensor, S_gate_up: torch.Tensor,
                               W_down: torch.Tensor, S_down: torch.Tensor, h: torch.Tensor | None = None,
                               d: torch.Tensor | None = None, ws: torch.Tensor | None = None, fill_h: bool = True):
-    """Stage hook for 16 < T <= 32: both expert GEMMs in one launch from the routed ids:
+    """Stage hook for T <= 32: both expert GEMMs in one launch from the routed ids:
     (h [T*k, I] bf16 in sorted-slot order, d [T*k, H] fp32 down outputs by flat slot).
-    The launch needs every element of h at 0xFFFF when it starts: fill_h=True fills it here
-    (on the current stream); with fill_h=False the caller has done so."""
+    The launch needs every element of h at 0xFFFF when it starts: fill_h=True has the call
+    fill it first (one more launch); with fill_h=False the caller has done so on this stream."""
     _check(x, "x", torch.bfloat16, 2)
     dev = x.device
     _check(ids, "ids", torch.int32, 2, dev)
@@ -374,14 +374,12 @@ def moe_expert_gemms_from_ids(x: torch.Tensor, ids: torch.Tensor, W_gate_up: tor
     _check(d, "d", torch.float32, 2, dev)
     if h.shape != (T * top_k, I) or d.shape != (T * top_k, H):
         raise ValueError("h must be [T*top_k, I] and d [T*top_k, H]")
-    if fill_h:
-        h.view(torch.int16).fill_(-1)
     if ws is None:
         ws = workspace(T, H, I, E, top_k, dev)
     _check(ws, "workspace", torch.uint8, 1, dev)
     st = _lib.moe_expert_gemms_from_ids(_ptr(x), _ptr(ids), _ptr(W_gate_up), _ptr(S_gate_up), _ptr(W_down),
-                                        _ptr(S_down), _ptr(h), _ptr(d), T, H, I, E, top_k, _ptr(ws), ws.numel(),
-                                        _stream(dev))
+                                        _ptr(S_down), _ptr(h), 0 if fill_h else 1, _ptr(d), T, H, I, E, top_k,
+                                        _ptr(ws), ws.numel(), _stream(dev))
     _raise(st, "moe_expert_gemms_from_ids")
     return h, d
 

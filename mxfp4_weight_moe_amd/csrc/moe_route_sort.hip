@@ -63,6 +63,21 @@ int launch_route(const float* logits, int T, int E, int k, int ns, int32_t* ids,
   return hip_status(hipGetLastError());
 }
 
+// All ones over n16 16-byte units (the single expert launch's "not yet written" h, when no
+// routing launch fills it).
+__global__ void __launch_bounds__(256) mx_fill_ones_kernel(u32x4* __restrict__ p, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
+    p[i] = u32x4{~0u, ~0u, ~0u, ~0u};
+}
+
+int launch_fill_ones(void* p, size_t bytes, hipStream_t stream) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 == 0) return MX_OK;
+  const int64_t wgs = (n16 + 1023) / 1024 < 1024 ? (n16 + 1023) / 1024 : 1024;
+  hipLaunchKernelGGL(mx_fill_ones_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, static_cast<u32x4*>(p), n16);
+  return hip_status(hipGetLastError());
+}
+
 // ------------------------------------------------------------------ sort
 
 constexpr int SORT_THREADS = 1024;

@@ -275,8 +275,8 @@ int moe_down_combine(const uint16_t* h, const float* gates, const uint8_t* w_dow
 
 int moe_expert_gemms_from_ids(const uint16_t* x, const int32_t* ids, const uint8_t* w_gate_up,
                               const uint8_t* s_gate_up, const uint8_t* w_down, const uint8_t* s_down, uint16_t* h,
-                              float* d, int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+                              int h_prefilled, float* d, int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k,
+                              void* workspace, size_t workspace_bytes, void* stream) {
   if (!x || !ids || !w_gate_up || !s_gate_up || !w_down || !s_down || !h || !d) return MX_ERR_NULL;
   int st = check_moe_sizes(T, E, top_k);
   if (st != MX_OK || (st = check_expert_dims(H, I)) != MX_OK) return st;
@@ -287,8 +287,10 @@ int moe_expert_gemms_from_ids(const uint16_t* x, const int32_t* ids, const uint8
   if (!workspace || !aligned(workspace, 256)) return MX_ERR_WORKSPACE;
   const MoeWorkspace ws = moe_workspace_carve(workspace, T, H, I, E, top_k);
   if (workspace_bytes < ws.bytes) return MX_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!h_prefilled && (st = launch_fill_ones(h, (size_t)(T * top_k * I * 2), s)) != MX_OK) return st;
   return launch_experts_sorted(x, ids, w_gate_up, s_gate_up, w_down, s_down, h, d, ws.ctl, (int)T, (int)H, (int)I,
-                               (int)E, (int)top_k, false, static_cast<hipStream_t>(stream));
+                               (int)E, (int)top_k, false, s);
 }
 
 int moe_combine(const float* d, const float* gates, uint16_t* y, int64_t T, int64_t H, int64_t top_k, void* stream) {

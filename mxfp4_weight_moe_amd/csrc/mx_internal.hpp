@@ -76,6 +76,8 @@ int launch_mxfp8_quantize(const uint16_t* x, int64_t rows, int64_t K, uint8_t* c
 // fill: optionally, fill_bytes (a multiple of 16) of device memory set to all ones in the same launch
 int launch_route(const float* logits, int T, int E, int k, int ns, int32_t* ids, float* gates, hipStream_t stream,
                  void* fill = nullptr, size_t fill_bytes = 0);
+// bytes (a multiple of 16) of device memory set to all ones
+int launch_fill_ones(void* p, size_t bytes, hipStream_t stream);
 int launch_sort(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* sorted_slots,
                 int32_t* active, int32_t* num_active, hipStream_t stream);
 // route + sort: one single-workgroup launch up to 16 tokens, the route and sort launches

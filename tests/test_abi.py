@@ -179,7 +179,7 @@ def test_stage_gemm_hooks_reject():
     ws32 = m.workspace_size(32, 1024, 1024, 64, 8)
 
     def eg(x=A, ids=A, h=A, d=A, T=32, H=1024, I=1024, E=64, k=8, w=A, wb=ws32):
-        return L.moe_expert_gemms_from_ids(x, ids, A, A, A, A, h, d, T, H, I, E, k, w, wb, None)
+        return L.moe_expert_gemms_from_ids(x, ids, A, A, A, A, h, 0, d, T, H, I, E, k, w, wb, None)
 
     assert eg(ids=None) == MX_ERR_NULL
     assert eg(h=None) == MX_ERR_NULL
