@@ -848,9 +848,9 @@ bool experts_sorted_fits(int T, int E, int k, int H, int I) {
 }
 
 // The single launch pays once the gate_up items are at least 3 per resident workgroup
-// (512 on MI355X) when every slot routes to its own expert.  With fewer, down items reach
-// experts whose h is still being written and wait for the whole gate_up phase, and cached
-// copies of h lines fetched before they were written send later chunks to the slow reload:
+// (512 on MI355X) when every slot routes to its own expert.  With fewer, every expert's
+// gate_up items finish in the last round, so down waits for the whole gate_up phase while
+// the early workgroups' down weight loads take bandwidth from gate_up's last items:
 // measured against the separate launches, T = 2 75.7 -> 82.1 and T = 4 125.2 -> 154.8 us per
 // layer (1 and 2 items per workgroup), but T = 8 220.3 -> 217.4 and T = 16 392.1 -> 387.4.
 constexpr int64_t EXPERTS_MIN_ITEMS = 3 * 512;
