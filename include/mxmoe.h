@@ -280,10 +280,10 @@ MX_API size_t moe_mxfp4_workspace_size(int64_t T, int64_t H, int64_t I, int64_t 
  *   combine: y[t,n] = bf16_rne( sum_j gates[t,j] * d_{t,j,n} )                    (fp32)
  * Each routed expert's weights are read from HBM once per 16 tokens routed to it (once per
  * call for T <= 16, where no expert has more than 16 rows); experts no token routes to are
- * not read.  Up to 32 tokens, where the gate_up items can be 3 or more per resident
- * workgroup (min(T*(top_k + shared), E + shared) * I / 64 >= 1536 with I % 1024 == 0; from
- * 6 tokens at top-8), both expert GEMMs run in one launch whose workgroups may wait for one
- * another (moe_expert_gemms_from_ids).  Such a wait is bounded: if one ever gave up, y is
+ * not read.  Up to 32 tokens (from 17 with shared experts), where the gate_up items can be
+ * 3 or more per resident workgroup (min(T * slots per token, experts) * I / 64 >= 1536 with
+ * I % 1024 == 0; from 6 tokens at top-8), both expert GEMMs run in one launch whose
+ * workgroups may wait for one another (moe_expert_gemms_from_ids).  Such a wait is bounded: if one ever gave up, y is
  * undefined and the int32 at byte offset 8 of the workspace reads 1 (sticky, as for
  * moe_mxfp4_forward_persistent).
  *   x             bf16 [T, H]
